@@ -1,0 +1,226 @@
+"""Throughput of the Gated DeltaNet mixer forward on one MI355X.
+
+A step is one chunkwise forward (the prefill hot path) over the scalar-gate
+workload B=8, H=12, T=8192, d_k=d_v=128, chunk 64, bf16 q/k/v/o with fp32
+g/beta/state, synthetic seeded inputs resident in HBM.  ``value`` is tokens/s
+of that step (B*T tokens per step) in millions.  The same run also times the
+fused recurrent decode step (256 sequences x 48 heads of 128x128 fp32 state, 64
+chained in-place steps) and reports its HBM bandwidth, and times the fp64 CPU
+oracle on a bounded sample of the prefill workload.
+
+Prints one JSON line.  Options: --gpus (1 only), --steps, --warmup,
+--no-cpu (skip the CPU baseline), --only {all,chunk,decode}.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+CHUNK = 64
+
+
+def chunk_bytes(B, T, H, K, V, es, channel, s0, so):
+    """Algorithmic HBM bytes of one chunkwise forward: every input read once,
+    every output written once."""
+    per_ht = 2 * K * es + V * es + V * es + (K if channel else 1) * 4 + 4
+    state = B * H * K * V * 4 * ((1 if s0 else 0) + (1 if so else 0))
+    return B * T * H * per_ht + state
+
+
+def chunk_flops(B, T, H, K, V, C=CHUNK):
+    """Flops per head-token of the formulation the kernel runs, lower-triangular
+    C x C blocks counted at half ("useful") or whole ("dense"):
+    Gram K K^T and Q K^T (2 C K), K+ S, Q+ S and K-^T D (6 K V), Tm X and P D (2 C V),
+    the triangular inverse (C^2 / 3)."""
+    useful = C * (2 * K + 2 * V) + 6 * K * V + C * C / 3
+    dense = 2 * C * (2 * K + 2 * V) + 6 * K * V + C * C / 3
+    n = B * T * H
+    return n * useful, n * dense
+
+
+def decode_bytes(N, H, K, V, es, channel):
+    per = 2 * K * V * 4 + 2 * K * es + V * es + V * es + (K if channel else 1) * 4 + 4
+    return N * H * per
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def bench_chunk(torch, gdn, steps, warmup):
+    from gdn_inputs import CHUNK_CONFIGS, chunk_inputs
+    cfg = CHUNK_CONFIGS["scalar_bf16"]
+    d = chunk_inputs(cfg, device="cuda")
+    B, T, H, K, V = cfg.B, cfg.T, cfg.H, cfg.K, cfg.V
+    o = torch.empty(B, T, H, V, dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty(B, H, K, V, dtype=torch.float32, device="cuda")
+    run = lambda: gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o, S_T)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = chunk_bytes(B, T, H, K, V, 2, False, d["S0"] is not None, True)
+    useful, dense = chunk_flops(B, T, H, K, V)
+    s = ms / 1e3
+    return dict(cfg=cfg, ms=ms, tokens=B * T, head_tokens=B * T * H, bytes=nbytes,
+                gbs=nbytes / s / 1e9, useful_tflops=useful / s / 1e12,
+                dense_tflops=dense / s / 1e12, inputs=d)
+
+
+def bench_decode(torch, gdn, reps):
+    from gdn_inputs import DECODE_CONFIG, decode_inputs
+    cfg = DECODE_CONFIG
+    d = decode_inputs(cfg, device="cuda")
+    N, H, K, V = cfg.N, cfg.H, cfg.K, cfg.V
+    S = d["S0"].clone()
+    o = torch.empty(cfg.steps, N, H, V, dtype=torch.bfloat16, device="cuda")
+
+    def chain():
+        for s in range(cfg.steps):
+            gdn.gdn_recurrent_step(d["q"][s], d["k"][s], d["v"][s], d["g"][s], d["beta"][s], S, o[s])
+
+    chain()  # warm-up
+    times = []
+    for _ in range(reps):
+        S.copy_(d["S0"])                      # restore the state (not timed)
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch)
+        e0.record()
+        chain()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / cfg.steps)
+    ms = sorted(times)[len(times) // 2]
+    nbytes = decode_bytes(N, H, K, V, 2, True)
+    return dict(cfg=cfg, ms_per_step=ms, bytes=nbytes, gbs=nbytes / (ms / 1e3) / 1e9)
+
+
+def cpu_baseline(chunk_inputs_dev, cfg, target_s=15.0):
+    """fp64 oracle on a bounded sample of the prefill workload: whole sequences of
+    some (b, h) slices, one OpenMP thread per slice."""
+    import oracle
+    threads = oracle.max_threads()
+    d = chunk_inputs_dev
+    # time one slice alone to size the sample (target_s of CPU thread-time)
+    one = [t[:1, :, :1].cpu().contiguous() for t in (d["q"], d["k"], d["v"], d["g"], d["beta"])]
+    t0 = time.perf_counter()
+    oracle.forward(*one, None, want_o=True, nthreads=1)
+    t_one = time.perf_counter() - t0
+    nb = int(round(target_s / max(t_one, 1e-3) / cfg.H))
+    nb = max(1, min(cfg.B, nb))
+    args = [t[:nb].cpu().contiguous() for t in (d["q"], d["k"], d["v"], d["g"], d["beta"])]
+    nsl = nb * cfg.H
+    t0 = time.perf_counter()
+    oracle.forward(*args, None, want_o=True)
+    wall = time.perf_counter() - t0
+    head_tokens = nsl * cfg.T
+    used = min(threads, nsl)
+    return dict(value=head_tokens / cfg.H / wall / 1e6, unit="Mtok/s", cores=used,
+                kind="oracle",
+                sample=(f"fp64 oracle on {nsl} of {cfg.B * cfg.H} (b,h) slices (batch rows "
+                        f"0..{nb - 1}), T={cfg.T}, same inputs: {head_tokens} head-tokens in "
+                        f"{wall:.2f} s wall on {used} threads; Mtok/s = head-tokens/s / H"),
+                wall_s=wall, head_tokens_per_s=head_tokens / wall,
+                host_cpus=len(os.sched_getaffinity(0)))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["all", "chunk", "decode"], default="all")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_layer_amd as gdn
+    if not os.path.exists(gdn.LIB_PATH):
+        from gated_deltanet_layer_amd import build
+        build.build()
+    gdn.lib()
+    torch.manual_seed(0)
+
+    out = {
+        "metric": "GDN chunk fwd Mtok/s + %bf16 MFMA peak; decode step GB/s + %HBM peak",
+        "value": None, "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; q,k unit-norm, v~N(0,1), beta=sigmoid(N(0,1)), g=-softplus(N(0,1)))",
+    }
+    ch = None
+    if args.only in ("all", "chunk"):
+        ch = bench_chunk(torch, gdn, args.steps, args.warmup)
+        cfg = ch["cfg"]
+        out["value"] = ch["tokens"] / (ch["ms"] / 1e3) / 1e6
+        out["ms_per_step"] = ch["ms"]
+        out["config"] = {
+            "workload": f"scalar-gate GDN chunkwise forward, B={cfg.B} H={cfg.H} T={cfg.T} "
+                        f"d_k=d_v={cfg.K} chunk={cfg.chunk}, bf16 q/k/v/o, fp32 g/beta/state, S0=0",
+            "global_batch": cfg.B, "seq_len": cfg.T, "heads": cfg.H, "d_k": cfg.K, "d_v": cfg.V,
+            "parallelism": "single GPU"}
+        out["roofline"] = {
+            "bound": "hbm", "achieved": ch["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": ch["gbs"] / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "chunk_fwd_kernel<bf16,128,scalar>",
+            "algorithmic_bytes_per_launch": ch["bytes"]}
+        out["mfma"] = {
+            "useful_tflops": ch["useful_tflops"], "dense_tile_tflops": ch["dense_tflops"],
+            "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac_useful": ch["useful_tflops"] / BF16_PEAK_TFLOPS}
+        out["head_tokens_per_s"] = ch["head_tokens"] / (ch["ms"] / 1e3)
+    if args.only in ("all", "decode"):
+        dc = bench_decode(torch, gdn, reps=max(3, min(args.steps, 10)))
+        c = dc["cfg"]
+        dec = {"workload": f"fused recurrent decode, N={c.N} H={c.H} d_k=d_v={c.K}, per-channel "
+                           f"gate, bf16 q/k/v/o, fp32 state in place, {c.steps} chained steps",
+               "ms_per_step": dc["ms_per_step"], "gbs": dc["gbs"],
+               "frac_hbm": dc["gbs"] / HBM_PEAK_GBS, "bytes_per_step": dc["bytes"]}
+        out["decode"] = dec
+        if ch is None:
+            out["value"] = dc["gbs"]
+            out["unit"] = "GB/s"
+            out["ms_per_step"] = dc["ms_per_step"]
+            out["config"] = {"workload": dec["workload"]}
+            out["roofline"] = {"bound": "hbm", "achieved": dc["gbs"], "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": dc["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                               "kernel": "recurrent_step_kernel<bf16,128,128,channel>"}
+    if ch is not None and not args.no_cpu:
+        torch.cuda.synchronize()
+        cb = cpu_baseline(ch["inputs"], ch["cfg"])
+        cb["cpu_model"] = platform.processor() or _cpu_model()
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+"""Gated DeltaNet mixer forward on MI355X (gfx950): Python binding of libgdn.so.
+
+The work runs in the HIP kernels behind the C ABI declared in ``include/gdn.h``;
+this module only checks tensors, marshals pointers and sizes, and passes the
+current torch stream.  PyTorch provides device memory and streams.  There is no
+fallback: if ``libgdn.so`` has not been built, every call raises.
+
+Entry points (same names as the C ABI):
+    gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk=64)
+    gdn_recurrent_step(q, k, v, g, beta, S, o)
+Conveniences that allocate the outputs:
+    chunk_fwd(q, k, v, g, beta, S0=None, want_o=True) -> (o, S_T)
+    recurrent_step_(q, k, v, g, beta, S) -> o      (S updated in place)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK, GDN_EINVAL, GDN_ENOTSUP, GDN_EHIP = 0, 1, 2, 3
+GDN_F32, GDN_BF16 = 0, 1
+GDN_GATE_HEAD, GDN_GATE_CHANNEL = 0, 1
+SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_status_str", "gdn_abi_version")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgdn.so, with argument types set.  Raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m gated_deltanet_layer_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, fp, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+        L.gdn_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp,
+                                    i, i, i, i, i, i, i, i, vp]
+        L.gdn_chunk_fwd.restype = i
+        L.gdn_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp,
+                                         i, i, i, i, i, i, vp]
+        L.gdn_recurrent_step.restype = i
+        L.gdn_status_str.argtypes = [i]
+        L.gdn_status_str.restype = ctypes.c_char_p
+        L.gdn_abi_version.argtypes = []
+        L.gdn_abi_version.restype = i
+        _lib = L
+        return L
+
+
+def status_str(s: int) -> str:
+    return lib().gdn_status_str(int(s)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().gdn_abi_version())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"q/k/v/o must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check(t, name, shape=None, dtype=None, device=None):
+    if t is None:
+        return
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk: int = 64, stream=None) -> None:
+    """Chunkwise forward; writes o [B,T,H,V] and/or S_T [B,H,K,V] (either may be None).
+
+    q, k [B,T,H,K] and v [B,T,H,V] share a dtype (fp32 or bf16); g is [B,T,H] (scalar
+    gate) or [B,T,H,K] (per key channel), fp32; beta [B,T,H] fp32; S0 [B,H,K,V] fp32
+    or None.  S_T may be S0 (in place).  Enqueued on the current torch stream.
+    """
+    import torch
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, D]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    dt = q.dtype
+    _check(q, "q", dtype=dt)
+    _check(k, "k", (B, T, H, K), dt, dev)
+    _check(v, "v", (B, T, H, V), dt, dev)
+    if g.dim() == 4:
+        gate = GDN_GATE_CHANNEL
+        _check(g, "g", (B, T, H, K), torch.float32, dev)
+    else:
+        gate = GDN_GATE_HEAD
+        _check(g, "g", (B, T, H), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    _check(S0, "S0", (B, H, K, V), torch.float32, dev)
+    _check(o, "o", (B, T, H, V), dt, dev)
+    _check(S_T, "S_T", (B, H, K, V), torch.float32, dev)
+    rc = lib().gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                             _ptr(o), _ptr(S_T), B, T, H, K, V, int(chunk),
+                             _dtype_code(q), gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd")
+
+
+def gdn_recurrent_step(q, k, v, g, beta, S, o, stream=None) -> None:
+    """One decode step for N sequences: S [N,H,K,V] fp32 updated in place, o [N,H,V].
+
+    q, k [N,H,K], v [N,H,V] (fp32 or bf16), g [N,H] or [N,H,K] fp32, beta [N,H] fp32.
+    """
+    import torch
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [N, H, D]")
+    N, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    dt = q.dtype
+    _check(q, "q", dtype=dt)
+    _check(k, "k", (N, H, K), dt, dev)
+    _check(v, "v", (N, H, V), dt, dev)
+    if g.dim() == 3:
+        gate = GDN_GATE_CHANNEL
+        _check(g, "g", (N, H, K), torch.float32, dev)
+    else:
+        gate = GDN_GATE_HEAD
+        _check(g, "g", (N, H), torch.float32, dev)
+    _check(beta, "beta", (N, H), torch.float32, dev)
+    _check(S, "S", (N, H, K, V), torch.float32, dev)
+    _check(o, "o", (N, H, V), dt, dev)
+    rc = lib().gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S),
+                                  _ptr(o), N, H, K, V, _dtype_code(q), gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_recurrent_step")
+
+
+def chunk_fwd(q, k, v, g, beta, S0=None, want_o: bool = True, chunk: int = 64, stream=None):
+    """Allocate o (if wanted) and S_T, run gdn_chunk_fwd, return (o, S_T)."""
+    import torch
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device) if want_o else None
+    S_T = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
+    gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk=chunk, stream=stream)
+    return o, S_T
+
+
+def recurrent_step_(q, k, v, g, beta, S, o=None, stream=None):
+    """One decode step; S is updated in place.  Returns o [N,H,V]."""
+    import torch
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    gdn_recurrent_step(q, k, v, g, beta, S, o, stream=stream)
+    return o

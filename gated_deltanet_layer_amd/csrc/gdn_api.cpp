@@ -1,0 +1,151 @@
+// gdn_api.cpp -- C ABI of libgdn: argument checks on the host, then dispatch.
+//
+// Every check runs before any HIP call; a call that fails a check enqueues
+// nothing.  Kernel selection is by (dtype, gate, K); V picks the number of
+// 64-column blocks.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+hipError_t chunk_fwd_launch(bool bf16, bool channel, int K, const void *q, const void *k,
+                            const void *v, const float *g, const float *beta, const float *S0,
+                            void *o, float *S_T, int B, int T, int H, int V, hipStream_t st);
+hipError_t recurrent_step_launch(bool bf16, bool channel, int K, int V, const void *q,
+                                 const void *k, const void *v, const float *g,
+                                 const float *beta, float *S, void *o, long nslices,
+                                 hipStream_t st);
+} // namespace gdn
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool aligned(const void *p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1u)) == 0; }
+bool aligned16(const void *p) { return aligned(p, 16); }
+
+Range range(const void *p, unsigned long long bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + (uintptr_t)bytes};
+}
+
+bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool kv_supported(int x) { return x == 64 || x == 128; }
+
+// n = a * b * c * d without overflow past 2^62, or -1.
+long long prod(long long a, long long b, long long c = 1, long long d = 1) {
+    const long long lim = 1LL << 62;
+    long long n = a;
+    for (long long f : {b, c, d}) {
+        if (f != 0 && n > lim / f) return -1;
+        n *= f;
+    }
+    return n;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *gdn_status_str(gdn_status s) {
+    switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_EINVAL: return "invalid argument";
+    case GDN_ENOTSUP: return "unsupported shape or type";
+    case GDN_EHIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *S0, void *o, float *S_T,
+                         int B, int T, int H, int K, int V, int chunk,
+                         gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EINVAL;
+    if (gate != GDN_GATE_HEAD && gate != GDN_GATE_CHANNEL) return GDN_EINVAL;
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0 || chunk <= 0) return GDN_EINVAL;
+    if (!o && !S_T) return GDN_EINVAL;
+    const long long es = dtype == GDN_BF16 ? 2 : 4;
+    const long long ntok = prod(B, T, H);
+    const long long nqk = prod(B, T, H, K), nv = prod(B, T, H, V), nst = prod(B, H, K, V);
+    if (ntok < 0 || nqk < 0 || nv < 0 || nst < 0) return GDN_EINVAL;
+    const long long ng = gate == GDN_GATE_CHANNEL ? nqk : ntok;
+    if (ntok > 0 && (!q || !k || !v || !g || !beta)) return GDN_EINVAL;
+    // q, k, v (and a per-channel g) are read as 16-byte vectors from row starts;
+    // the rest is accessed element by element.
+    for (const void *p : {q, k, v})
+        if (p && !aligned16(p)) return GDN_EINVAL;
+    if (g && !aligned(g, gate == GDN_GATE_CHANNEL ? 16 : 4)) return GDN_EINVAL;
+    for (const void *p : {(const void *)beta, (const void *)S0, (const void *)S_T})
+        if (p && !aligned(p, 4)) return GDN_EINVAL;
+    if (o && !aligned(o, (unsigned)es)) return GDN_EINVAL;
+    // o must not touch any input or the state; S_T may be S0 exactly.
+    const Range rq = range(q, nqk * es), rk = range(k, nqk * es), rv = range(v, nv * es);
+    const Range rg = range(g, ng * 4), rb = range(beta, ntok * 4);
+    const Range rs0 = range(S0, S0 ? nst * 4 : 0), rst = range(S_T, S_T ? nst * 4 : 0);
+    const Range ro = range(o, o ? nv * es : 0);
+    for (Range r : {rq, rk, rv, rg, rb, rs0, rst})
+        if (overlap(ro, r)) return GDN_EINVAL;
+    for (Range r : {rq, rk, rv, rg, rb})
+        if (overlap(rst, r)) return GDN_EINVAL;
+    if (S0 && S_T && (const void *)S0 != (const void *)S_T && overlap(rs0, rst)) return GDN_EINVAL;
+
+    if (!kv_supported(K) || !kv_supported(V) || chunk != 64) return GDN_ENOTSUP;
+    if (dtype == GDN_F32 && K != 64) return GDN_ENOTSUP;
+    if (prod(B, H, V / 64) > 0x7fffffffLL) return GDN_ENOTSUP;
+    if (B == 0 || H == 0) return GDN_OK;
+    if (!S_T && T == 0) return GDN_OK;  // nothing to write
+
+    const hipError_t e = gdn::chunk_fwd_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL, K,
+                                               q, k, v, g, beta, S0, o, S_T, B, T, H, V,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, float *S, void *o, int N, int H, int K,
+                              int V, gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EINVAL;
+    if (gate != GDN_GATE_HEAD && gate != GDN_GATE_CHANNEL) return GDN_EINVAL;
+    if (N < 0 || H < 0 || K <= 0 || V <= 0) return GDN_EINVAL;
+    const long long es = dtype == GDN_BF16 ? 2 : 4;
+    const long long ns = prod(N, H), nqk = prod(N, H, K), nv = prod(N, H, V), nst = prod(N, H, K, V);
+    if (ns < 0 || nqk < 0 || nv < 0 || nst < 0) return GDN_EINVAL;
+    const long long ng = gate == GDN_GATE_CHANNEL ? nqk : ns;
+    if (ns > 0 && (!q || !k || !v || !g || !beta || !S)) return GDN_EINVAL;
+    // The state is streamed as 16-byte vectors; the vectors are read per element.
+    if (S && !aligned16(S)) return GDN_EINVAL;
+    for (const void *p : {q, k, v, (const void *)o})
+        if (p && !aligned(p, (unsigned)es)) return GDN_EINVAL;
+    for (const void *p : {(const void *)g, (const void *)beta})
+        if (p && !aligned(p, 4)) return GDN_EINVAL;
+    const Range rq = range(q, nqk * es), rk = range(k, nqk * es), rv = range(v, nv * es);
+    const Range rg = range(g, ng * 4), rb = range(beta, ns * 4), rs = range(S, nst * 4);
+    const Range ro = range(o, o ? nv * es : 0);
+    for (Range r : {rq, rk, rv, rg, rb, rs})
+        if (overlap(ro, r)) return GDN_EINVAL;
+    for (Range r : {rq, rk, rv, rg, rb})
+        if (overlap(rs, r)) return GDN_EINVAL;
+
+    if (!kv_supported(K) || !kv_supported(V)) return GDN_ENOTSUP;
+    if (ns > 0x7fffffffLL) return GDN_ENOTSUP;
+    if (ns == 0) return GDN_OK;
+
+    const hipError_t e = gdn::recurrent_step_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL,
+                                                    K, V, q, k, v, g, beta, S, o, ns,
+                                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+} // extern "C"

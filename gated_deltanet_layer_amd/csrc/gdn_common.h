@@ -1,0 +1,64 @@
+// gdn_common.h -- small device helpers shared by the gfx950 kernels.
+//
+// MFMA operand layout used throughout (CDNA3/CDNA4 matrix cores, wave64):
+//   lane l = 16 * gq + r  (gq = l / 16 in 0..3, r = l % 16)
+//   C/D tile 16x16 fp32:  lane holds rows 4*gq + {0,1,2,3} of column r.
+//   A operand:            lane holds row r, a run of k-slots chosen by gq.
+//   B operand:            lane holds column r, the same run of k-slots.
+// Because A and B use the same k-slots per lane group, any fixed bijection
+// between k-slots and the contraction index works, provided A and B agree.
+// We use the one that lets a C tile feed the next product as its B operand
+// without moving data between lanes: for a 32-wide k block made of two
+// 16-row slabs s0, s1, lane group gq supplies rows
+//   {16*s0 + 4*gq + i, 16*s1 + 4*gq + i : i = 0..3}
+// (bf16 16x16x32), and for fp32 16x16x4 the k-step j uses row 4*gq + j of the
+// slab.  An A operand read from LDS must then take, for its row r, the four
+// contiguous columns 16*s + 4*gq .. +3 of each slab.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ bf16x4 cvt4(f32x4 v) {
+    bf16x4 r;
+    r[0] = (__bf16)v[0];
+    r[1] = (__bf16)v[1];
+    r[2] = (__bf16)v[2];
+    r[3] = (__bf16)v[3];
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// acc += A(16x32) * B(32x16), bf16 operands, fp32 accumulate.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+// acc += A(16x4) * B(4x16), fp32 operands.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+} // namespace gdn

@@ -1,0 +1,118 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet mixer forward.
+ *
+ * The operation (Atomic-GDN2 model card, section 2.1 "Gated DeltaNet-2"), for
+ * every batch row b and head h independently, token by token:
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = S_t^T q_t                              (read after the write)
+ *   alpha_t = exp(g_t)
+ *
+ * S_t is a K x V fp32 matrix (keys on the rows, values on the columns).  The
+ * library receives the log-decay g and exponentiates it itself (same section).
+ * g is either one value per head-token (GDN_GATE_HEAD: the scalar retention
+ * gate) or one value per key channel (GDN_GATE_CHANNEL: the per-key-channel
+ * gate of GDN-2 / KDA).  No 1/sqrt(K) scale is applied to q; the caller
+ * normalises q and k, applies the sigmoid to beta and the clamp to g.
+ *
+ * The two entry points are the two execution modes that compute this same
+ * mathematics (MindPattern "Gated DeltaNet" page, finding of 2026-07-29):
+ * a chunkwise mode for prefill/training and a fused recurrent mode for decode.
+ * The recurrent state is the fixed-size fp32 S (the state-memory accounting of
+ * "Hybrid layouts: three DeltaNet, one attention", 01 Concept), and the initial
+ * state is a first-class input (the S0-tuning finding on the MindPattern page).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, owned by the caller, contiguous
+ *    row-major in the layouts given, aligned to their element size.  The
+ *    streamed operands need 16 bytes: q, k, v and a per-channel g of
+ *    gdn_chunk_fwd, and S of gdn_recurrent_step.  The library allocates nothing
+ *    and keeps no state between calls.
+ *  - q, k, v and o share one storage type (gdn_dtype).  g, beta and every state
+ *    tensor are fp32.  Arithmetic is fp32 with fp32 accumulation; for
+ *    GDN_BF16 the matrix products take bf16 operands on the MFMA units.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *    the call returns without waiting.  Faults inside a kernel surface at the
+ *    caller's next synchronisation of that stream.
+ *  - Arguments are checked on the host before anything is enqueued.  A call that
+ *    returns an error has enqueued nothing and written nothing.
+ *  - Preconditions that are NOT checked per element: g <= 0; for
+ *    GDN_GATE_CHANNEL, g in [-5, 0] (the configured domain of the card's
+ *    section 2.1); finite inputs.  Outside them results are unspecified.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define GDN_API __attribute__((visibility("default")))
+#else
+#define GDN_API
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_EINVAL = 1,   /* null / misaligned / aliasing pointer, negative size, bad enum */
+    GDN_ENOTSUP = 2,  /* valid request this build has no kernel for (K, V, chunk) */
+    GDN_EHIP = 3      /* the HIP runtime rejected a launch */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+typedef enum { GDN_GATE_HEAD = 0, GDN_GATE_CHANNEL = 1 } gdn_gate;
+
+/*
+ * Chunkwise forward over a whole sequence batch.
+ *
+ *   q, k  [B, T, H, K]   dtype        v  [B, T, H, V]   dtype
+ *   g     [B, T, H] (GDN_GATE_HEAD) or [B, T, H, K] (GDN_GATE_CHANNEL), fp32 log-decay
+ *   beta  [B, T, H]      fp32
+ *   S0    [B, H, K, V]   fp32 initial state, or NULL for zeros
+ *   o     [B, T, H, V]   dtype output, or NULL to compute the final state only
+ *   S_T   [B, H, K, V]   fp32 final state, or NULL.  May equal S0 (updated in
+ *                        place); must not partially overlap any other buffer.
+ *
+ * K and V: 64 or 128 (GDN_F32: K = 64).  chunk: 64 (tokens per chunk).  Any
+ * T >= 0: a partial last chunk behaves as if padded with identity tokens
+ * (beta = 0, g = 0), whose outputs are not written.  B, T or H equal to 0 is a
+ * valid call: with T = 0, S_T receives S0 (or zeros).  At least one of o, S_T
+ * must be non-NULL.  o must not alias any input.
+ */
+GDN_API gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *S0,
+                         void *o, float *S_T,
+                         int B, int T, int H, int K, int V, int chunk,
+                         gdn_dtype dtype, gdn_gate gate, void *stream);
+
+/*
+ * One fused recurrent (decode) step for N sequences, updating S in place.
+ *
+ *   q, k  [N, H, K]   dtype          v  [N, H, V]   dtype
+ *   g     [N, H] or [N, H, K] fp32   beta [N, H]    fp32
+ *   S     [N, H, K, V] fp32, read and overwritten with S' (in place)
+ *   o     [N, H, V]   dtype output, or NULL
+ *
+ * K and V: 64 or 128.  N or H equal to 0 is a valid empty call.  Each (n, h)
+ * slice is owned by one workgroup, so the in-place update is race-free.
+ */
+GDN_API gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v,
+                              const float *g, const float *beta,
+                              float *S, void *o,
+                              int N, int H, int K, int V,
+                              gdn_dtype dtype, gdn_gate gate, void *stream);
+
+/* Static English text for a status code (never NULL). */
+GDN_API const char *gdn_status_str(gdn_status s);
+
+/* GDN_ABI_VERSION of the library that is loaded. */
+GDN_API int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

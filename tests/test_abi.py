@@ -1,0 +1,150 @@
+"""C-ABI library: loads, exports every declared symbol, rejects bad arguments on
+the host before touching the GPU (CPU only: every call here fails validation or
+is an empty no-op, so no kernel is launched)."""
+import os
+import re
+
+import pytest
+
+import gated_deltanet_layer_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gdn.LIB_PATH):
+        from gated_deltanet_layer_amd import build
+        build.build()
+    return gdn.lib()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert set(names) == set(gdn.SYMBOLS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_only_declared_symbols_are_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert {s for s in exported if s.startswith("gdn_")} == set(gdn.SYMBOLS)
+
+
+def test_version_and_status_strings(L):
+    assert gdn.abi_version() == 1
+    assert gdn.status_str(0) == "ok"
+    assert "invalid" in gdn.status_str(1)
+    assert "unsupported" in gdn.status_str(2)
+    assert "HIP" in gdn.status_str(3)
+    assert gdn.status_str(99) == "unknown status"
+
+
+# Fake, well-separated, 16-byte aligned device addresses: validation only looks
+# at their values, and every call below returns before any HIP call.
+BASE = 1 << 44
+SEP = 1 << 36
+
+
+def _ptrs(n=8):
+    return [BASE + i * SEP for i in range(n)]
+
+
+def _chunk(L, **kw):
+    q, k, v, g, beta, S0, o, S_T = _ptrs()
+    a = dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, o=o, S_T=S_T,
+             B=2, T=100, H=3, K=128, V=128, chunk=64, dtype=1, gate=0)
+    a.update(kw)
+    return L.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["o"],
+                           a["S_T"], a["B"], a["T"], a["H"], a["K"], a["V"], a["chunk"],
+                           a["dtype"], a["gate"], None)
+
+
+def _step(L, **kw):
+    q, k, v, g, beta, S, o = _ptrs(7)
+    a = dict(q=q, k=k, v=v, g=g, beta=beta, S=S, o=o, N=4, H=3, K=128, V=128,
+             dtype=1, gate=1)
+    a.update(kw)
+    return L.gdn_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], a["o"],
+                                a["N"], a["H"], a["K"], a["V"], a["dtype"], a["gate"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=2), dict(dtype=-1), dict(gate=2), dict(B=-1), dict(T=-1), dict(H=-1),
+    dict(K=0), dict(V=-5), dict(chunk=0), dict(q=None), dict(g=None), dict(beta=None),
+    dict(o=None, S_T=None), dict(q=BASE + 8), dict(v=BASE + 2 * SEP + 4),
+    dict(g=BASE + 3 * SEP + 4, gate=1), dict(g=BASE + 3 * SEP + 2),
+    dict(beta=BASE + 4 * SEP + 2), dict(S_T=BASE + 7 * SEP + 2), dict(o=BASE + 6 * SEP + 1),
+    dict(o=BASE),                       # o aliases q
+    dict(o=BASE + 2 * SEP + 64),        # o overlaps v
+    dict(S_T=BASE + 3 * SEP),           # S_T aliases g
+    dict(S_T=BASE + 5 * SEP + 16),      # S_T partially overlaps S0
+    dict(B=1 << 30, T=1 << 30, H=1 << 30),  # size overflow
+])
+def test_chunk_rejects_invalid(L, kw):
+    assert _chunk(L, **kw) == gdn.GDN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(K=96), dict(V=32), dict(K=256), dict(chunk=32), dict(chunk=128),
+    dict(dtype=0, K=128),               # fp32 chunk path: K = 64 only
+])
+def test_chunk_unsupported(L, kw):
+    assert _chunk(L, **kw) == gdn.GDN_ENOTSUP
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=0, S_T=None)])
+def test_chunk_empty_is_a_noop(L, kw):
+    assert _chunk(L, **kw) == gdn.GDN_OK
+
+
+def test_chunk_empty_batch_needs_no_pointers(L):
+    assert _chunk(L, B=0, q=None, k=None, v=None, g=None, beta=None) == gdn.GDN_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=3), dict(gate=-1), dict(N=-1), dict(H=-2), dict(K=0), dict(S=None),
+    dict(q=None), dict(o=BASE + 5 * SEP), dict(o=BASE), dict(S=BASE + 1 * SEP),
+    dict(v=BASE + 2 * SEP + 1), dict(S=BASE + 5 * SEP + 8), dict(beta=BASE + 4 * SEP + 2),
+    dict(q=BASE + 1), dict(g=BASE + 3 * SEP + 2),
+])
+def test_step_rejects_invalid(L, kw):
+    assert _step(L, **kw) == gdn.GDN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(K=32), dict(V=256), dict(K=100)])
+def test_step_unsupported(L, kw):
+    assert _step(L, **kw) == gdn.GDN_ENOTSUP
+
+
+def test_step_empty_is_a_noop(L):
+    assert _step(L, N=0) == gdn.GDN_OK
+
+
+def test_element_aligned_vectors_are_accepted_by_validation(L):
+    # per-step slices of [steps, N, H] beta / scalar g are 4-byte aligned only;
+    # validation must pass them (the call then fails later only for lack of a GPU,
+    # so this uses an unsupported K to stop right after the pointer checks)
+    assert _step(L, beta=BASE + 4 * SEP + 4, g=BASE + 3 * SEP + 4, gate=0, K=32) == gdn.GDN_ENOTSUP
+    assert _chunk(L, beta=BASE + 4 * SEP + 4, S0=BASE + 5 * SEP + 4, K=32) == gdn.GDN_ENOTSUP
+
+
+def test_python_binding_rejects_cpu_tensors(L):
+    import torch
+    q = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError):
+        gdn.gdn_chunk_fwd(q, q, q, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1), None, q, None)
+
+
+def test_status_error_carries_code(L):
+    e = gdn.GDNError(2, "gdn_chunk_fwd")
+    assert e.status == 2 and "unsupported" in str(e)
