@@ -9,20 +9,24 @@
 // the chunk (per key channel; a scalar gate is broadcast):
 //   A_ts = beta_t sum_c k_tc k_sc e^{gamma_tc - gamma_sc}   (s < t, else 0)
 //   P_ts =        sum_c q_tc k_sc e^{gamma_tc - gamma_sc}   (s <= t, else 0)
-//   Tm   = (I + A)^{-1}                                     (unit lower triangular)
-//   D    = Tm diag(beta) (V - K+ S),    K+_t = e^{gamma_t} k_t
-//   O    = Q+ S + P D,                  Q+_t = e^{gamma_t} q_t
-//   S'   = Diag(e^{gamma_n}) S + K-^T D, K-_t = e^{gamma_n - gamma_t} k_t
+//   (I + A) D = diag(beta) (V - K+ S),  K+_t = e^{gamma_t} k_t
+//   O  = Q+ S + P D,                    Q+_t = e^{gamma_t} q_t
+//   S' = Diag(e^{gamma_n}) S + K-^T D,  K-_t = e^{gamma_n - gamma_t} k_t
+// I + A is unit lower triangular.  D is found by block forward substitution
+// over 16-token blocks: D_i = T_ii (X_i - sum_{j<i} A_ij D_j), with T_ii the
+// inverse of the 16 x 16 diagonal block of I + A.
 //
 // Work split.  One workgroup of 4 waves owns one (b, h, 64-column block of V)
 // and walks the chunks of that sequence in order; every column of S evolves on
 // its own, so column blocks need no communication.  Wave w owns value columns
-// 16w..16w+15 of the block and keeps that 128 x 16 (K x 16) slice of S in
-// registers, in the MFMA accumulator layout, for the whole sequence; the state
-// products chain through registers (see gdn_common.h for the operand layout).
-// The K-only work of a chunk (Gram matrices, triangular inverse) is shared by
-// the 4 waves through LDS.  The next chunk's q/k/v/g/beta are loaded into
-// registers while the current chunk computes.
+// 16w..16w+15 of the block and keeps that K x 16 slice of S in registers, in
+// the MFMA accumulator layout, for the whole sequence; the state products
+// chain through registers (operand layout: gdn_common.h).  The K-only work of a
+// chunk (Gram blocks, diagonal inverses) is split over the 4 waves on a static
+// schedule; each wave inverts the diagonal block it computed, so no barrier
+// separates the two.  The next chunk's q/k/v/g/beta are loaded into registers
+// while the current chunk computes.  Three workgroup barriers per chunk
+// (five with the per-channel gate).
 //
 // Per-key-channel gate: the decay sits inside the contractions of A and P.  It
 // is split at 16-token block boundaries: with lambda the running sum of g from
@@ -33,7 +37,7 @@
 // so e^{-lambda} stays below 5.6e34, inside the fp32/bf16 range; the middle
 // factor is <= 1.  This is why the gate domain is bounded (the card's
 // section 2.1 says the bound comes from the kernel, not from the model).
-#include "gdn_common.h"
+#include "mfma_frag.h"
 
 namespace gdn {
 
@@ -42,100 +46,46 @@ constexpr int VBLK = 64;   // value columns per workgroup
 constexpr int NTHR = 256;
 
 // ---------------------------------------------------------------------------
-// Operand fragments (one 16 x 32 operand slice per lane; see gdn_common.h).
-template <typename OT> struct Frag;
-template <> struct Frag<__bf16> { bf16x8 v; };
-template <> struct Frag<float> { f32x4 lo, hi; };
-
-// Row-major matrix M in LDS; fragment rows row0 .. row0+15, k columns
-// k0 + 4*gq .. +3 and k0 + 16 + 4*gq .. +3 for lane group gq.
-__device__ __forceinline__ Frag<__bf16> lds_frag(const __bf16 *M, int ld, int row0, int k0) {
-    const int lane = threadIdx.x & 63;
-    const __bf16 *p = M + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
-    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(p);
-    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p + 16);
-    return {cat8(a, b)};
-}
-__device__ __forceinline__ Frag<float> lds_frag(const float *M, int ld, int row0, int k0) {
-    const int lane = threadIdx.x & 63;
-    const float *p = M + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
-    return {*reinterpret_cast<const f32x4 *>(p), *reinterpret_cast<const f32x4 *>(p + 16)};
-}
-
-// B operand from two accumulator tiles holding rows k0..k0+15 and k0+16..k0+31.
-template <typename OT> __device__ __forceinline__ Frag<OT> reg_frag(f32x4 c0, f32x4 c1);
-template <> __device__ __forceinline__ Frag<__bf16> reg_frag<__bf16>(f32x4 c0, f32x4 c1) {
-    return {cat8(cvt4(c0), cvt4(c1))};
-}
-template <> __device__ __forceinline__ Frag<float> reg_frag<float>(f32x4 c0, f32x4 c1) {
-    return {c0, c1};
-}
-
-__device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
-    return mfma_bf16(a.v, b.v, acc);
-}
-__device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<float> &a, const Frag<float> &b) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = mfma_f32(a.lo[e], b.lo[e], acc);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = mfma_f32(a.hi[e], b.hi[e], acc);
-    return acc;
-}
-
-// Multiply the k-slots of a fragment by per-column factors f[k] (f in LDS).
-__device__ __forceinline__ Frag<__bf16> scale_frag(Frag<__bf16> x, const float *f, int k0) {
-    const int gq = (threadIdx.x & 63) >> 4;
-    const f32x4 f0 = *reinterpret_cast<const f32x4 *>(f + k0 + 4 * gq);
-    const f32x4 f1 = *reinterpret_cast<const f32x4 *>(f + k0 + 16 + 4 * gq);
-    f32x4 a, b;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        a[e] = (float)x.v[e] * f0[e];
-        b[e] = (float)x.v[4 + e] * f1[e];
-    }
-    return {cat8(cvt4(a), cvt4(b))};
-}
-__device__ __forceinline__ Frag<float> scale_frag(Frag<float> x, const float *f, int k0) {
-    const int gq = (threadIdx.x & 63) >> 4;
-    const f32x4 f0 = *reinterpret_cast<const f32x4 *>(f + k0 + 4 * gq);
-    const f32x4 f1 = *reinterpret_cast<const f32x4 *>(f + k0 + 16 + 4 * gq);
-    return {x.lo * f0, x.hi * f1};
-}
-
-// ---------------------------------------------------------------------------
 // LDS layout (bytes).  Operand arrays carry a 16-byte row pad.
 template <typename OT, int K, bool CH> struct Smem {
     static constexpr int PAD = 16 / (int)sizeof(OT);
     static constexpr int LDK = K + PAD;          // [64][K] operand arrays
     static constexpr int LDC = CH_T + PAD;       // [*][64] operand arrays
-    static constexpr int LDF = CH_T + 4;         // [64][64] fp32 arrays
-    static constexpr bool SEP_TM = sizeof(OT) != 4;  // bf16 copy of Tm
+    static constexpr int LDD = 16 + PAD;         // [64][16] diagonal inverses
+    static constexpr int LDA = 20;               // [16][16] fp32 scratch (+4 pad)
+    static constexpr int E = (int)sizeof(OT);
     static constexpr int align(int x) { return (x + 255) & ~255; }
     static constexpr int kK = 0;
-    static constexpr int kQ = align(kK + CH_T * LDK * (int)sizeof(OT));
-    static constexpr int kKI = align(kQ + CH_T * LDK * (int)sizeof(OT));
-    static constexpr int kKmT = align(kKI + (CH ? CH_T * LDK * (int)sizeof(OT) : 0));
-    static constexpr int kV = align(kKmT + K * LDC * (int)sizeof(OT));
-    static constexpr int kA = align(kV + CH_T * LDC * (int)sizeof(OT));
-    static constexpr int kT = kA + CH_T * LDF * 4;        // contiguous with kA
-    static constexpr int kTm = align(kT + CH_T * LDF * 4);
-    static constexpr int kP = align(kTm + (SEP_TM ? CH_T * LDC * (int)sizeof(OT) : 0));
-    static constexpr int kBeta = align(kP + CH_T * LDC * (int)sizeof(OT));
-    static constexpr int kGs = kBeta + CH_T * 4;           // scalar gate g
-    static constexpr int kGam = kGs + CH_T * 4;            // scalar gate vectors
-    static constexpr int kEg = kGam + CH_T * 4;
-    static constexpr int kEgn = kEg + CH_T * 4;
-    static constexpr int kEgN = kEgn + CH_T * 4;
-    static constexpr int kLam = align(kEgN + 16);          // channel gate: [4][K]
-    static constexpr int kER = kLam + (CH ? 4 * K * 4 : 0);  // [5][K] e^{R_b}
-    static constexpr int kFP = kER + (CH ? 5 * K * 4 : 0);   // [6][K] e^{R_i - R_j}
+    static constexpr int kQ = align(kK + CH_T * LDK * E);
+    static constexpr int kKI = align(kQ + CH_T * LDK * E);
+    static constexpr int kKmT = align(kKI + (CH ? CH_T * LDK * E : 0));
+    static constexpr int kV = align(kKmT + K * LDC * E);
+    static constexpr int kO = align(kV + CH_T * LDC * E);
+    static constexpr int kAn = align(kO + CH_T * LDC * E);
+    static constexpr int kP = align(kAn + CH_T * LDC * E);
+    static constexpr int kTd = align(kP + CH_T * LDC * E);
+    static constexpr int kAd = align(kTd + CH_T * LDD * E);      // [4 waves][16][LDA] fp32
+    static constexpr int kBeta = align(kAd + 4 * 16 * LDA * 4);
+    static constexpr int kG = kBeta + CH_T * 4;                   // scalar g [64]
+    static constexpr int kW = kG + CH_T * 4;                      // [4 waves][3][64]
+    static constexpr int kLam = align(kW + 4 * 3 * CH_T * 4);     // channel: [4][K]
+    static constexpr int kER = kLam + (CH ? 4 * K * 4 : 0);       // [5][K] e^{R_b}
+    static constexpr int kFP = kER + (CH ? 5 * K * 4 : 0);        // [6][K] e^{R_i - R_j}
     static constexpr int bytes = align(kFP + (CH ? 6 * K * 4 : 0));
-    static_assert(CH_T * K * 4 <= 2 * CH_T * LDF * 4, "g staging must fit in A+T");
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
 // Off-diagonal 16-token block pair (i, j), j < i -> index of its factor row.
 __device__ __forceinline__ int pair_idx(int i, int j) { return i * (i - 1) / 2 + j; }
+
+// Gram blocks (i, j), j <= i, per wave: rows grouped so a wave reuses its
+// left-hand fragments, 2-3 blocks per wave, exactly one diagonal block each.
+__constant__ const signed char kGramSched[4][3][2] = {
+    {{3, 0}, {3, 1}, {0, 0}},
+    {{3, 2}, {3, 3}, {-1, -1}},
+    {{2, 0}, {2, 1}, {2, 2}},
+    {{1, 0}, {1, 1}, {-1, -1}},
+};
 
 struct ChunkArgs {
     const void *q, *k, *v;
@@ -153,15 +103,16 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
     using L = Smem<OT, K, CH>;
     constexpr int NT = K / 16;             // 16-row tiles of S
     constexpr int NKB = K / 32;            // 32-wide k blocks over the key dim
-    constexpr int VPR = K * (int)sizeof(DT) / 16;       // 16-B vectors per q/k row
-    constexpr int NVK = CH_T * VPR / NTHR;               // per thread
-    constexpr int EPV = 16 / (int)sizeof(DT);            // elements per vector
-    constexpr int VPRV = VBLK * (int)sizeof(DT) / 16;    // 16-B vectors per v row
-    constexpr int NVV = CH_T * VPRV / NTHR;
-    constexpr int GPR = K / 4;                           // f32x4 per g row (channel)
-    constexpr int NVG = CH ? CH_T * GPR / NTHR : 1;
+    constexpr int EPV = 16 / (int)sizeof(DT);            // elements per 16-B vector
+    constexpr int CG = K / EPV;                          // vectors per q/k row
+    constexpr int RG = NTHR / CG;                        // row groups
+    constexpr int RPT = CH_T / RG;                       // rows per thread (q/k)
+    constexpr int VPRV = VBLK / EPV;                     // vectors per v/o row
+    constexpr int NVV = CH_T * VPRV / NTHR;              // v/o vectors per thread
+    constexpr int CPT = K / 64;                          // channel-gate prep: channels per thread
     using vec_t = f32x4;                                 // 16-byte transport type
-    static_assert(NVK >= 1 && NVV >= 1 && NVG >= 1, "layout");
+    using pack_t = typename Pack<DT, RPT>::type;
+    static_assert(RPT * RG == CH_T && NVV >= 1, "layout");
 
     extern __shared__ __attribute__((aligned(256))) char smem[];
     OT *sK = reinterpret_cast<OT *>(smem + L::kK);
@@ -169,18 +120,12 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
     OT *sKI = reinterpret_cast<OT *>(smem + L::kKI);
     OT *sKmT = reinterpret_cast<OT *>(smem + L::kKmT);
     OT *sV = reinterpret_cast<OT *>(smem + L::kV);
-    float *sA = reinterpret_cast<float *>(smem + L::kA);
-    float *sT = reinterpret_cast<float *>(smem + L::kT);
-    float *sG = sA;  // channel gate staging [64][K], dead before A is written
-    OT *sTm = L::SEP_TM ? reinterpret_cast<OT *>(smem + L::kTm) : reinterpret_cast<OT *>(sT);
-    constexpr int LDTM = L::SEP_TM ? L::LDC : L::LDF;
+    DT *sO = reinterpret_cast<DT *>(smem + L::kO);
+    OT *sAn = reinterpret_cast<OT *>(smem + L::kAn);
     OT *sP = reinterpret_cast<OT *>(smem + L::kP);
+    OT *sTd = reinterpret_cast<OT *>(smem + L::kTd);
     float *sBeta = reinterpret_cast<float *>(smem + L::kBeta);
-    float *sGs = reinterpret_cast<float *>(smem + L::kGs);
-    float *sGam = reinterpret_cast<float *>(smem + L::kGam);
-    float *sEg = reinterpret_cast<float *>(smem + L::kEg);
-    float *sEgn = reinterpret_cast<float *>(smem + L::kEgn);
-    float *sEgN = reinterpret_cast<float *>(smem + L::kEgN);
+    float *sG = reinterpret_cast<float *>(smem + L::kG);
     float *sLam = reinterpret_cast<float *>(smem + L::kLam);
     float *sER = reinterpret_cast<float *>(smem + L::kER);
     float *sFP = reinterpret_cast<float *>(smem + L::kFP);
@@ -190,6 +135,9 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
     const int wave = tid >> 6;
     const int r16 = lane & 15;
     const int gq = lane >> 4;
+    float *sAd = reinterpret_cast<float *>(smem + L::kAd) + wave * 16 * L::LDA;  // wave-private
+    float *sW = reinterpret_cast<float *>(smem + L::kW) + wave * 3 * CH_T;       // wave-private
+    float *wGam = sW, *wEg = sW + CH_T, *wEgn = sW + 2 * CH_T;
 
     // workgroup -> (b*H + h, column block)
     const int T = args.T, H = args.H, V = args.V, nvb = args.nvb;
@@ -213,18 +161,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
     const DT *kg = static_cast<const DT *>(args.k);
     const DT *vg = static_cast<const DT *>(args.v);
     DT *og = static_cast<DT *>(args.o);
-    const long HK = (long)H * K, HV = (long)H * V;
     const long row_base = (long)b * T * H + h;   // row of token 0 in [B*T*H]
-
-    // Blocks of Tm and P above the diagonal that the 32-wide k steps touch
-    // are never written: clear them once.
-    for (int i = tid; i < 2 * 16 * 16; i += NTHR) {
-        const int blk = i >> 8, rr = (i >> 4) & 15, cc = i & 15;
-        const int r0 = blk ? 32 : 0, c0 = blk ? 48 : 16;
-        sP[(r0 + rr) * L::LDC + c0 + cc] = from_f32<OT>(0.f);
-        sTm[(r0 + rr) * LDTM + c0 + cc] = from_f32<OT>(0.f);
-        if (L::SEP_TM) sT[(r0 + rr) * L::LDF + c0 + cc] = 0.f;
-    }
 
     // State slice in accumulator layout: S_acc[ct][e] = S[16ct + 4gq + e][v0 + vcol].
     f32x4 S_acc[NT];
@@ -238,21 +175,25 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
     }
 
     // ---- prefetch registers for one chunk ----
-    vec_t pk[NVK], pq[NVK], pv[NVV], pg[NVG];
+    // q/k: thread (cg = tid % CG, rg = tid / CG) loads rows RPT*rg .. +RPT-1,
+    // 16 bytes at column cg*EPV; v: NVV 16-byte vectors; channel g: thread
+    // (blk = tid / 64, cp = tid % 64) loads CPT channels of its 16 tokens.
+    const int cg = tid % CG, rg = tid / CG;
+    vec_t pk[RPT], pq[RPT], pv[NVV];
+    float pgc[CH ? 16 : 1][CH ? CPT : 1];
     float pb = 0.f, pgs = 0.f;
     auto load_chunk = [&](int t0) {
 #pragma unroll
-        for (int j = 0; j < NVK; ++j) {
-            const int idx = tid + NTHR * j, row = idx / VPR, cv = idx % VPR;
-            const int t = t0 + row;
+        for (int i = 0; i < RPT; ++i) {
+            const int t = t0 + RPT * rg + i;
             vec_t zk = {0.f, 0.f, 0.f, 0.f}, zq = zk;
             if (t < T) {
-                const long off = (row_base + (long)t * H) * K + cv * EPV;
+                const long off = (row_base + (long)t * H) * K + cg * EPV;
                 zk = *reinterpret_cast<const vec_t *>(kg + off);
                 zq = *reinterpret_cast<const vec_t *>(qg + off);
             }
-            pk[j] = zk;
-            pq[j] = zq;
+            pk[i] = zk;
+            pq[i] = zq;
         }
 #pragma unroll
         for (int j = 0; j < NVV; ++j) {
@@ -263,40 +204,61 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
                 z = *reinterpret_cast<const vec_t *>(vg + (row_base + (long)t * H) * V + v0 + cv * EPV);
             pv[j] = z;
         }
-        if constexpr (CH) {
-#pragma unroll
-            for (int j = 0; j < NVG; ++j) {
-                const int idx = tid + NTHR * j, row = idx / GPR, cv = idx % GPR;
-                const int t = t0 + row;
-                vec_t z = {0.f, 0.f, 0.f, 0.f};
-                if (t < T)
-                    z = *reinterpret_cast<const vec_t *>(args.g + (row_base + (long)t * H) * K + cv * 4);
-                pg[j] = z;
-            }
-        } else {
+        if constexpr (!CH)
             pgs = (tid < CH_T && t0 + tid < T) ? args.g[row_base + (long)(t0 + tid) * H] : 0.f;
-        }
         pb = (tid < CH_T && t0 + tid < T) ? args.beta[row_base + (long)(t0 + tid) * H] : 0.f;
+    };
+    auto load_gate = [&](int t0) {  // per-channel gate, in the prep mapping
+        if constexpr (CH) {
+            const int blk = tid >> 6, cp = tid & 63;
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) {
+                const int t = t0 + 16 * blk + tt;
+#pragma unroll
+                for (int ci = 0; ci < CPT; ++ci)
+                    pgc[tt][ci] = (t < T) ? args.g[(row_base + (long)t * H) * K + cp * CPT + ci] : 0.f;
+            }
+        }
     };
 
     const int nchunks = (T + CH_T - 1) / CH_T;
-    if (nchunks > 0) load_chunk(0);
+    if (nchunks > 0) {
+        load_chunk(0);
+        load_gate(0);
+    }
+
+    // Write the staged outputs of the chunk at t0 (rows < nvalid) from sO to o.
+    auto flush_o = [&](int t0, int nvalid) {
+        if (!og) return;
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+            const int idx = tid + NTHR * j, row = idx / VPRV, cv = idx % VPRV;
+            if (row < nvalid)
+                *reinterpret_cast<vec_t *>(og + (row_base + (long)(t0 + row) * H) * V + v0 + cv * EPV) =
+                    *reinterpret_cast<const vec_t *>(sO + row * L::LDC + cv * EPV);
+        }
+    };
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * CH_T;
-        const int nvalid = min(CH_T, T - t0);
 
-        // ---- stage the prefetched chunk into LDS ----
+        // ---- stage the prefetched chunk into LDS (and flush the last outputs) ----
+        if (c > 0) flush_o(t0 - CH_T, CH_T);
 #pragma unroll
-        for (int j = 0; j < NVK; ++j) {
-            const int idx = tid + NTHR * j, row = idx / VPR, cv = idx % VPR;
-            *reinterpret_cast<vec_t *>(sK + row * L::LDK + cv * EPV) = pk[j];
-            *reinterpret_cast<vec_t *>(sQ + row * L::LDK + cv * EPV) = pq[j];
-            if constexpr (!CH) {
-                // K^T for the state update (the scalar decay is applied to D).
-                const DT *ke = reinterpret_cast<const DT *>(&pk[j]);
+        for (int i = 0; i < RPT; ++i) {
+            *reinterpret_cast<vec_t *>(sK + (RPT * rg + i) * L::LDK + cg * EPV) = pk[i];
+            *reinterpret_cast<vec_t *>(sQ + (RPT * rg + i) * L::LDK + cg * EPV) = pq[i];
+        }
+        if constexpr (!CH) {
+            // K^T (the scalar decay is applied to D instead): for each channel of
+            // this thread's vector, RPT consecutive tokens in one packed write.
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) sKmT[(cv * EPV + e) * L::LDC + row] = ke[e];
+            for (int e = 0; e < EPV; ++e) {
+                const int ch = cg * EPV + e;
+                pack_t pk_t;
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) pk_t[i] = reinterpret_cast<const DT *>(&pk[i])[e];
+                *reinterpret_cast<pack_t *>(sKmT + ch * L::LDC + ((RPT * rg) ^ kmt_swz<EPV>(ch))) = pk_t;
             }
         }
 #pragma unroll
@@ -304,40 +266,25 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
             const int idx = tid + NTHR * j, row = idx / VPRV, cv = idx % VPRV;
             *reinterpret_cast<vec_t *>(sV + row * L::LDC + cv * EPV) = pv[j];
         }
-        if constexpr (CH) {
-#pragma unroll
-            for (int j = 0; j < NVG; ++j) {
-                const int idx = tid + NTHR * j, row = idx / GPR, cv = idx % GPR;
-                *reinterpret_cast<vec_t *>(sG + row * K + cv * 4) = pg[j];
-            }
-        }
         if (tid < CH_T) {
             sBeta[tid] = pb;
-            if (!CH) sGs[tid] = pgs;
+            if (!CH) sG[tid] = pgs;
         }
-        __syncthreads();
-
-        if (c + 1 < nchunks) load_chunk(t0 + CH_T);
+        lds_barrier();
 
         // ---- gate preparation ----
+        float egN = 1.f;       // scalar gate: e^{gamma_n}
         if constexpr (!CH) {
-            if (wave == 0) {
-                // inclusive running sum of g over the chunk (lane = token)
-                float x = sGs[lane];
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float y = __shfl_up(x, off, 64);
-                    if (lane >= off) x += y;
-                }
-                const float gn = __shfl(x, 63, 64);
-                sGam[lane] = x;
-                sEg[lane] = __expf(x);
-                sEgn[lane] = __expf(gn - x);
-                if (lane == 0) sEgN[0] = __expf(gn);
-            }
+            if (c + 1 < nchunks) load_chunk(t0 + CH_T);
+            // every wave scans g itself (lane = token) into its private vectors
+            const float x = wave_inclusive_sum(sG[lane]);
+            const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+            wGam[lane] = x;
+            wEg[lane] = __expf(x);
+            wEgn[lane] = __expf(gn - x);
+            egN = __expf(gn);
         } else {
             // thread -> 16-token block blk, channels cp*CPT .. +CPT-1
-            constexpr int CPT = K / 64;
             const int blk = tid >> 6, cp = tid & 63;
             float kraw[16][CPT], lamv[16][CPT];
 #pragma unroll
@@ -347,7 +294,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
 #pragma unroll
                 for (int tt = 0; tt < 16; ++tt) {
                     const int t = 16 * blk + tt;
-                    lam += sG[t * K + ch];
+                    lam += pgc[tt][ci];
                     const float el = __expf(lam);
                     const float eil = __expf(-lam);
                     const float kv = to_f32(sK[t * L::LDK + ch]);
@@ -360,7 +307,11 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
                 }
                 sLam[blk * K + ch] = lam;
             }
-            __syncthreads();
+            if (c + 1 < nchunks) {
+                load_chunk(t0 + CH_T);
+                load_gate(t0 + CH_T);
+            }
+            lds_barrier();
 #pragma unroll
             for (int ci = 0; ci < CPT; ++ci) {
                 const int ch = cp * CPT + ci;
@@ -369,9 +320,10 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Rb[i + 1] = Rb[i] + sLam[i * K + ch];
                 const float base = Rb[4] - Rb[blk];
+                const int swz = kmt_swz<EPV>(ch);
 #pragma unroll
                 for (int tt = 0; tt < 16; ++tt)
-                    sKmT[ch * L::LDC + 16 * blk + tt] =
+                    sKmT[ch * L::LDC + ((16 * blk + tt) ^ swz)] =
                         from_f32<OT>(kraw[tt][ci] * __expf(base - lamv[tt][ci]));
                 if (blk == 0) {
 #pragma unroll
@@ -383,179 +335,168 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
                             sFP[pair_idx(i, j) * K + ch] = __expf(Rb[i] - Rb[j]);
                 }
             }
+            lds_barrier();
         }
-        __syncthreads();
 
-        // ---- Gram blocks: A (strictly lower) and P (lower incl. diagonal) ----
+        // ---- Gram blocks and diagonal inverses (static per-wave schedule) ----
         {
             const OT *rhs = CH ? sKI : sK;
-            for (int p = wave; p < 10; p += 4) {
-                // p -> (i, j), j <= i, enumerated row by row
-                const int i = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
-                const int j = p - i * (i + 1) / 2;
-                f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
+            Frag<OT> aK[NKB], aQ[NKB];
+            int cur_i = -1;
+#pragma unroll
+            for (int pp = 0; pp < 3; ++pp) {
+                const int i = kGramSched[wave][pp][0], j = kGramSched[wave][pp][1];
+                if (i < 0) break;
+                if (i != cur_i) {
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) {
+                        aK[kb] = lds_frag(sK, L::LDK, 16 * i, 32 * kb);
+                        aQ[kb] = lds_frag(sQ, L::LDK, 16 * i, 32 * kb);
+                    }
+                    cur_i = i;
+                }
+                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
                     Frag<OT> fr = lds_frag(rhs, L::LDK, 16 * j, 32 * kb);
                     if (CH && j < i) fr = scale_frag(fr, sFP + pair_idx(i, j) * K, 32 * kb);
-                    aA = mma(aA, lds_frag(sK, L::LDK, 16 * i, 32 * kb), fr);
-                    aP = mma(aP, lds_frag(sQ, L::LDK, 16 * i, 32 * kb), fr);
+                    accA = mma(accA, aK[kb], fr);
+                    accP = mma(accP, aQ[kb], fr);
                 }
+                // rows t = 16i + 4gq + e, column s = 16j + r16
                 const int s = 16 * j + r16;
+                const f32x4 bt = *reinterpret_cast<const f32x4 *>(sBeta + 16 * i + 4 * gq);
+                f32x4 a, p;
+                f32x4 gt = {0.f, 0.f, 0.f, 0.f};
+                float gs = 0.f;
+                if constexpr (!CH) {
+                    gt = *reinterpret_cast<const f32x4 *>(wGam + 16 * i + 4 * gq);
+                    gs = wGam[s];
+                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * i + 4 * gq + e;
-                    float dec = 1.f;
-                    if (!CH) dec = (s <= t) ? __expf(sGam[t] - sGam[s]) : 0.f;
-                    sA[t * L::LDF + s] = (s < t) ? sBeta[t] * aA[e] * dec : 0.f;
-                    sP[t * L::LDC + s] = from_f32<OT>((s <= t) ? aP[e] * dec : 0.f);
+                    const float dec = CH ? 1.f : ((s <= t) ? __expf(gt[e] - gs) : 0.f);
+                    a[e] = (s < t) ? bt[e] * accA[e] * dec : 0.f;
+                    p[e] = (s <= t) ? accP[e] * dec : 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * i + 4 * gq + e;
+                    sP[t * L::LDC + s] = from_f32<OT>(p[e]);
+                    if (j < i) sAn[t * L::LDC + s] = from_f32<OT>(-a[e]);
+                }
+                if (j == i) {
+                    // Column r16 of T_ii = (I + A_ii)^{-1} by forward substitution:
+                    // once x_r is final, subtract A[r'][r] x_r from every later
+                    // row.  A[r'][r] sits in lane 16*(r'/4) + r, element r'%4, of
+                    // this wave's accumulator and is broadcast with readlane.
+                    float x[16];
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == r16) ? 1.f : 0.f;
+#pragma unroll
+                    for (int r = 0; r < 15; ++r) {
+#pragma unroll
+                        for (int r2 = r + 1; r2 < 16; ++r2)
+                            x[r2] -= __int_as_float(__builtin_amdgcn_readlane(
+                                         __float_as_int(a[r2 & 3]), 16 * (r2 >> 2) + r)) * x[r];
+                    }
+                    if (gq == 0) {
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr)
+                            sTd[(16 * i + rr) * L::LDD + r16] = from_f32<OT>(x[rr]);
+                    }
                 }
             }
         }
-        __syncthreads();
 
-        // ---- Tm = (I + A)^{-1}: 16x16 diagonal blocks by substitution ----
-        if constexpr (!L::SEP_TM && CH) {
-            // fp32 Tm shares its rows with the g staging area: clear the two
-            // blocks above the diagonal that the 32-wide k steps read.
-            for (int i = tid; i < 2 * 16 * 16; i += NTHR) {
-                const int blk = i >> 8, rr = (i >> 4) & 15, cc = i & 15;
-                sT[((blk ? 32 : 0) + rr) * L::LDF + (blk ? 48 : 16) + cc] = 0.f;
-            }
-        }
-        if (lane < 16) {
-            const int d0 = 16 * wave, jcol = lane;
-            float x[16];
+        // ---- K+ S and Q+ S (registers only; independent of the Gram work) ----
+        f32x4 KS[4], QS[4];
+        if constexpr (!CH) {
+            Frag<OT> Sb[NKB];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float *arow = sA + (d0 + r) * L::LDF + d0;
-                float acc = (r == jcol) ? 1.f : 0.f;
+            for (int kb = 0; kb < NKB; ++kb) Sb[kb] = reg_frag<OT>(S_acc[2 * kb], S_acc[2 * kb + 1]);
 #pragma unroll
-                for (int s = 0; s < r; ++s) acc -= arow[s] * x[s];
-                x[r] = acc;
-            }
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sT[(d0 + r) * L::LDF + d0 + jcol] = x[r];
-        }
-        __syncthreads();
-        // off-diagonal blocks, one block diagonal at a time:
-        //   Tm_ij = -Tm_ii * sum_{k=j}^{i-1} A_ik Tm_kj
-#pragma unroll
-        for (int d = 1; d < 4; ++d) {
-            if (wave < 4 - d) {
-                const int jb = wave, ib = wave + d;
-                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-                for (int kbk = jb; kbk < ib; ++kbk) {
-                    const f32x4 a = *reinterpret_cast<const f32x4 *>(
-                        sA + (16 * ib + r16) * L::LDF + 16 * kbk + 4 * gq);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        Y = mfma_f32(a[e], sT[(16 * kbk + 4 * gq + e) * L::LDF + 16 * jb + r16], Y);
+                for (int kb = 0; kb < NKB; ++kb) {
+                    ak = mma(ak, lds_frag(sK, L::LDK, 16 * rt, 32 * kb), Sb[kb]);
+                    aq = mma(aq, lds_frag(sQ, L::LDK, 16 * rt, 32 * kb), Sb[kb]);
                 }
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(
-                    sT + (16 * ib + r16) * L::LDF + 16 * ib + 4 * gq);
-                f32x4 Z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Z = mfma_f32(a[e], Y[e], Z);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sT[(16 * ib + 4 * gq + e) * L::LDF + 16 * jb + r16] = -Z[e];
+                const f32x4 eg = *reinterpret_cast<const f32x4 *>(wEg + 16 * rt + 4 * gq);
+                KS[rt] = ak * eg;
+                QS[rt] = aq * eg;
             }
-            __syncthreads();
-        }
-        if constexpr (L::SEP_TM) {
-            // operand copy of the lower block triangle
-            for (int i = tid; i < 10 * 256; i += NTHR) {
-                const int p = i >> 8, rr = (i >> 4) & 15, cc = i & 15;
-                const int ib = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
-                const int jb = p - ib * (ib + 1) / 2;
-                const int t = 16 * ib + rr, s = 16 * jb + cc;
-                sTm[t * L::LDC + s] = from_f32<OT>(sT[t * L::LDF + s]);
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                // rows of block rt read S scaled by e^{R_rt} per key channel
+                f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const f32x4 e0 = *reinterpret_cast<const f32x4 *>(sER + rt * K + 32 * kb + 4 * gq);
+                    const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sER + rt * K + 32 * kb + 16 + 4 * gq);
+                    const Frag<OT> sb = reg_frag<OT>(S_acc[2 * kb] * e0, S_acc[2 * kb + 1] * e1);
+                    ak = mma(ak, lds_frag(sK, L::LDK, 16 * rt, 32 * kb), sb);
+                    aq = mma(aq, lds_frag(sQ, L::LDK, 16 * rt, 32 * kb), sb);
+                }
+                KS[rt] = ak;
+                QS[rt] = aq;
             }
-            __syncthreads();
         }
+        lds_barrier();   // -A blocks, P and T_ii of all waves are visible
 
         // ---- state chain (per wave, its 16 value columns) ----
         {
-            f32x4 KS[4], QS[4];
-            if constexpr (!CH) {
-                Frag<OT> Sb[NKB];
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) Sb[kb] = reg_frag<OT>(S_acc[2 * kb], S_acc[2 * kb + 1]);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) {
-                        ak = mma(ak, lds_frag(sK, L::LDK, 16 * rt, 32 * kb), Sb[kb]);
-                        aq = mma(aq, lds_frag(sQ, L::LDK, 16 * rt, 32 * kb), Sb[kb]);
-                    }
-                    const f32x4 eg = *reinterpret_cast<const f32x4 *>(sEg + 16 * rt + 4 * gq);
-                    KS[rt] = ak * eg;
-                    QS[rt] = aq * eg;
-                }
-            } else {
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    // rows of block rt read S scaled by e^{R_rt} per key channel
-                    f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) {
-                        const f32x4 e0 = *reinterpret_cast<const f32x4 *>(sER + rt * K + 32 * kb + 4 * gq);
-                        const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sER + rt * K + 32 * kb + 16 + 4 * gq);
-                        const Frag<OT> sb = reg_frag<OT>(S_acc[2 * kb] * e0, S_acc[2 * kb + 1] * e1);
-                        ak = mma(ak, lds_frag(sK, L::LDK, 16 * rt, 32 * kb), sb);
-                        aq = mma(aq, lds_frag(sQ, L::LDK, 16 * rt, 32 * kb), sb);
-                    }
-                    KS[rt] = ak;
-                    QS[rt] = aq;
-                }
-            }
             // X = diag(beta) (V - K+ S)
             f32x4 X[4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+            for (int rt = 0; rt < 4; ++rt) {
+                const f32x4 bt = *reinterpret_cast<const f32x4 *>(sBeta + 16 * rt + 4 * gq);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * rt + 4 * gq + e;
-                    X[rt][e] = sBeta[t] * (to_f32(sV[t * L::LDC + vcol]) - KS[rt][e]);
+                    X[rt][e] = bt[e] * (to_f32(sV[t * L::LDC + vcol]) - KS[rt][e]);
                 }
-            // D = Tm X (Tm lower triangular: row block rt needs k blocks 0..rt/2)
-            const Frag<OT> Xf0 = reg_frag<OT>(X[0], X[1]), Xf1 = reg_frag<OT>(X[2], X[3]);
+            }
+            // (I + A) D = X by block forward substitution (sAn holds -A)
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             f32x4 D[4];
+            D[0] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 0, 0), reg_frag<OT>(X[0], z));
+            f32x4 Y = mma_lo(X[1], lds_frag_lo(sAn, L::LDC, 16, 0), reg_frag<OT>(D[0], z));
+            D[1] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 16, 0), reg_frag<OT>(Y, z));
+            const Frag<OT> Df0 = reg_frag<OT>(D[0], D[1]);
+            Y = mma(X[2], lds_frag(sAn, L::LDC, 32, 0), Df0);
+            f32x4 Y3 = mma(X[3], lds_frag(sAn, L::LDC, 48, 0), Df0);
+            D[2] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 32, 0), reg_frag<OT>(Y, z));
+            Y3 = mma_lo(Y3, lds_frag_lo(sAn, L::LDC, 48, 32), reg_frag<OT>(D[2], z));
+            D[3] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 48, 0), reg_frag<OT>(Y3, z));
+            const Frag<OT> Df1 = reg_frag<OT>(D[2], D[3]);
+
+            // O = Q+ S + P D, staged in sO for 16-byte stores
+            f32x4 O[4];
+            O[0] = mma_lo(QS[0], lds_frag_lo(sP, L::LDC, 0, 0), Df0);
+            O[1] = mma(QS[1], lds_frag(sP, L::LDC, 16, 0), Df0);
+            O[2] = mma(QS[2], lds_frag(sP, L::LDC, 32, 0), Df0);
+            O[2] = mma_lo(O[2], lds_frag_lo(sP, L::LDC, 32, 32), Df1);
+            O[3] = mma(QS[3], lds_frag(sP, L::LDC, 48, 0), Df0);
+            O[3] = mma(O[3], lds_frag(sP, L::LDC, 48, 32), Df1);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma(acc, lds_frag(sTm, LDTM, 16 * rt, 0), Xf0);
-                if (rt >= 2) acc = mma(acc, lds_frag(sTm, LDTM, 16 * rt, 32), Xf1);
-                D[rt] = acc;
-            }
-            const Frag<OT> Df0 = reg_frag<OT>(D[0], D[1]), Df1 = reg_frag<OT>(D[2], D[3]);
-            // O = Q+ S + P D
-            if (og) {
+            for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    f32x4 acc = QS[rt];
-                    acc = mma(acc, lds_frag(sP, L::LDC, 16 * rt, 0), Df0);
-                    if (rt >= 2) acc = mma(acc, lds_frag(sP, L::LDC, 16 * rt, 32), Df1);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * rt + 4 * gq + e;
-                        if (t < nvalid)
-                            og[(row_base + (long)(t0 + t) * H) * V + v0 + vcol] = from_f32<DT>(acc[e]);
-                    }
-                }
-            }
+                for (int e = 0; e < 4; ++e)
+                    sO[(16 * rt + 4 * gq + e) * L::LDC + vcol] = from_f32<DT>(O[rt][e]);
+
             // S' = Diag(e^{gamma_n}) S + K-^T D
             Frag<OT> Ef0, Ef1;
             if constexpr (!CH) {
                 f32x4 Dt[4];
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
-                    Dt[rt] = D[rt] * *reinterpret_cast<const f32x4 *>(sEgn + 16 * rt + 4 * gq);
+                    Dt[rt] = D[rt] * *reinterpret_cast<const f32x4 *>(wEgn + 16 * rt + 4 * gq);
                 Ef0 = reg_frag<OT>(Dt[0], Dt[1]);
                 Ef1 = reg_frag<OT>(Dt[2], Dt[3]);
-                const float egN = sEgN[0];
 #pragma unroll
                 for (int ct = 0; ct < NT; ++ct) S_acc[ct] *= egN;
             } else {
@@ -567,12 +508,13 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
             }
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
-                S_acc[ct] = mma(S_acc[ct], lds_frag(sKmT, L::LDC, 16 * ct, 0), Ef0);
-                S_acc[ct] = mma(S_acc[ct], lds_frag(sKmT, L::LDC, 16 * ct, 32), Ef1);
+                S_acc[ct] = mma(S_acc[ct], lds_frag_kmt<EPV>(sKmT, L::LDC, 16 * ct, 0), Ef0);
+                S_acc[ct] = mma(S_acc[ct], lds_frag_kmt<EPV>(sKmT, L::LDC, 16 * ct, 32), Ef1);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
+    if (nchunks > 0) flush_o((nchunks - 1) * CH_T, T - (nchunks - 1) * CH_T);
 
     if (args.S_T) {
         float *ST = args.S_T + (long)bh * K * V;
@@ -600,11 +542,18 @@ static hipError_t launch_chunk(const ChunkArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Host entry used by the C ABI after validation.
+hipError_t chunk_fwd_ws_launch(int K, const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *S0, void *o, float *S_T, int B,
+                               int T, int H, int V, hipStream_t st);
+
+// Host entry used by the C ABI after validation.  bf16 operands with the
+// scalar gate take the warp-specialised kernel (chunk_fwd_ws.hip).
 hipError_t chunk_fwd_launch(bool bf16, bool channel, int K, const void *q, const void *k,
                             const void *v, const float *g, const float *beta, const float *S0,
                             void *o, float *S_T, int B, int T, int H, int V, hipStream_t st)
 {
+    if (bf16 && !channel)
+        return chunk_fwd_ws_launch(K, q, k, v, g, beta, S0, o, S_T, B, T, H, V, st);
     ChunkArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = S0; a.o = o; a.S_T = S_T;
     a.B = B; a.T = T; a.H = H; a.V = V;

@@ -88,7 +88,7 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const floa
     if (g && !aligned(g, gate == GDN_GATE_CHANNEL ? 16 : 4)) return GDN_EINVAL;
     for (const void *p : {(const void *)beta, (const void *)S0, (const void *)S_T})
         if (p && !aligned(p, 4)) return GDN_EINVAL;
-    if (o && !aligned(o, (unsigned)es)) return GDN_EINVAL;
+    if (o && !aligned16(o)) return GDN_EINVAL;   // written as 16-byte row pieces
     // o must not touch any input or the state; S_T may be S0 exactly.
     const Range rq = range(q, nqk * es), rk = range(k, nqk * es), rv = range(v, nv * es);
     const Range rg = range(g, ng * 4), rb = range(beta, ntok * 4);

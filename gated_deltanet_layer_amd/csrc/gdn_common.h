@@ -56,6 +56,34 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
+// Workgroup barrier for LDS traffic only.  __syncthreads() also fences global
+// memory, which waits for every outstanding global load and store of the wave;
+// the kernels keep prefetches and output stores in flight across barriers, so
+// they wait only for LDS operations (lgkmcnt) before s_barrier.  The memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: DPP shifts within each
+// row of 16 lanes, then the row totals are added with readlane.
+template <int CTRL> __device__ __forceinline__ float dpp_shr(float x) {
+    // row_shr:n with bound_ctrl: lanes without a source read 0
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x += dpp_shr<0x111>(x);   // row_shr:1
+    x += dpp_shr<0x112>(x);   // row_shr:2
+    x += dpp_shr<0x114>(x);   // row_shr:4
+    x += dpp_shr<0x118>(x);   // row_shr:8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+    const int row = (threadIdx.x & 63) >> 4;
+    const float off = row == 0 ? 0.f : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2;
+    return x + off;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
     return x;

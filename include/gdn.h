@@ -25,7 +25,7 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers, owned by the caller, contiguous
  *    row-major in the layouts given, aligned to their element size.  The
- *    streamed operands need 16 bytes: q, k, v and a per-channel g of
+ *    streamed operands need 16 bytes: q, k, v, o and a per-channel g of
  *    gdn_chunk_fwd, and S of gdn_recurrent_step.  The library allocates nothing
  *    and keeps no state between calls.
  *  - q, k, v and o share one storage type (gdn_dtype).  g, beta and every state
