@@ -78,15 +78,6 @@ template <typename OT, int K, bool CH> struct Smem {
 // Off-diagonal 16-token block pair (i, j), j < i -> index of its factor row.
 __device__ __forceinline__ int pair_idx(int i, int j) { return i * (i - 1) / 2 + j; }
 
-// Gram blocks (i, j), j <= i, per wave: rows grouped so a wave reuses its
-// left-hand fragments, 2-3 blocks per wave, exactly one diagonal block each.
-__constant__ const signed char kGramSched[4][3][2] = {
-    {{3, 0}, {3, 1}, {0, 0}},
-    {{3, 2}, {3, 3}, {-1, -1}},
-    {{2, 0}, {2, 1}, {2, 2}},
-    {{1, 0}, {1, 1}, {-1, -1}},
-};
-
 struct ChunkArgs {
     const void *q, *k, *v;
     const float *g, *beta, *S0;
@@ -133,9 +124,9 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform copy
     const int r16 = lane & 15;
     const int gq = lane >> 4;
-    float *sAd = reinterpret_cast<float *>(smem + L::kAd) + wave * 16 * L::LDA;  // wave-private
     float *sW = reinterpret_cast<float *>(smem + L::kW) + wave * 3 * CH_T;       // wave-private
     float *wGam = sW, *wEg = sW + CH_T, *wEgn = sW + 2 * CH_T;
 
@@ -345,7 +336,8 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
             int cur_i = -1;
 #pragma unroll
             for (int pp = 0; pp < 3; ++pp) {
-                const int i = kGramSched[wave][pp][0], j = kGramSched[wave][pp][1];
+                int i, j;
+                gram_block(wave_u, pp, i, j);
                 if (i < 0) break;
                 if (i != cur_i) {
 #pragma unroll
@@ -387,25 +379,11 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
                     if (j < i) sAn[t * L::LDC + s] = from_f32<OT>(-a[e]);
                 }
                 if (j == i) {
-                    // Column r16 of T_ii = (I + A_ii)^{-1} by forward substitution:
-                    // once x_r is final, subtract A[r'][r] x_r from every later
-                    // row.  A[r'][r] sits in lane 16*(r'/4) + r, element r'%4, of
-                    // this wave's accumulator and is broadcast with readlane.
-                    float x[16];
+                    // T_ii = (I + A_ii)^{-1}, in registers (accumulator layout)
+                    const f32x4 tinv = unit_lower_inverse16(a);
 #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == r16) ? 1.f : 0.f;
-#pragma unroll
-                    for (int r = 0; r < 15; ++r) {
-#pragma unroll
-                        for (int r2 = r + 1; r2 < 16; ++r2)
-                            x[r2] -= __int_as_float(__builtin_amdgcn_readlane(
-                                         __float_as_int(a[r2 & 3]), 16 * (r2 >> 2) + r)) * x[r];
-                    }
-                    if (gq == 0) {
-#pragma unroll
-                        for (int rr = 0; rr < 16; ++rr)
-                            sTd[(16 * i + rr) * L::LDD + r16] = from_f32<OT>(x[rr]);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        sTd[(16 * i + 4 * gq + e) * L::LDD + r16] = from_f32<OT>(tinv[e]);
                 }
             }
         }

@@ -36,6 +36,7 @@ template <int K> struct WsSmem {
     static constexpr int LDC = WS_T + PAD;        // [*][64] v, -A, P
     static constexpr int LDT = WS_T;              // [K][64] k^T (swizzled, unpadded)
     static constexpr int LDD = 16 + PAD;          // [64][16] T_ii
+    static constexpr int LDN = 48 + PAD;          // [48][48] -A: rows 16..63, cols 0..47
     static constexpr int al(int x) { return (x + 255) & ~255; }
     // one buffer
     static constexpr int oK = 0;
@@ -43,15 +44,19 @@ template <int K> struct WsSmem {
     static constexpr int oKT = oQ + WS_T * LDK * 2;
     static constexpr int oV = oKT + K * LDT * 2;
     static constexpr int oAn = oV + WS_T * LDC * 2;           // rows 16..63 of -A
-    static constexpr int oP = oAn + (WS_T - 16) * LDC * 2;
+    static constexpr int oP = oAn + (WS_T - 16) * LDN * 2;
     static constexpr int oTd = oP + WS_T * LDC * 2;
     static constexpr int oBeta = oTd + WS_T * LDD * 2;
     static constexpr int oEg = oBeta + WS_T * 4;               // e^{gamma_t}
     static constexpr int oEgn = oEg + WS_T * 4;                // e^{gamma_n - gamma_t}
     static constexpr int oEgN = oEgn + WS_T * 4;               // e^{gamma_n}
     static constexpr int BUF = al(oEgN + 16);
-    static constexpr int kGam = 2 * BUF;                       // prep-private gamma [64]
-    static constexpr int kCtr = kGam + WS_T * 4;               // prep arrival counter
+    // prep-private tables of the chunk being prepared (see ws_gram_tile)
+    static constexpr int kGam = 2 * BUF;                       // gamma_t [64]
+    static constexpr int kRowf = kGam + WS_T * 4;              // [3][64] e^{gamma_t - gamma_{16j+15}}
+    static constexpr int kBrowf = kRowf + 3 * WS_T * 4;        // [3][64] beta_t * rowf
+    static constexpr int kColf = kBrowf + 3 * WS_T * 4;        // [64] e^{gamma_{16b+15} - gamma_s}
+    static constexpr int kCtr = kColf + WS_T * 4;              // prep arrival counter
     static constexpr int bytes = al(kCtr + 16);
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
@@ -72,14 +77,88 @@ __device__ __forceinline__ void prep_barrier(unsigned *ctr, unsigned target) {
     asm volatile("" ::: "memory");
 }
 
-// Gram blocks (i, j), j <= i, per prep wave (same schedule as chunk_fwd.hip):
-// one diagonal block each, left-hand fragments reused within a row.
-__constant__ const signed char kWsGram[4][3][2] = {
-    {{3, 0}, {3, 1}, {0, 0}},
-    {{3, 2}, {3, 3}, {-1, -1}},
-    {{2, 0}, {2, 1}, {2, 2}},
-    {{1, 0}, {1, 1}, {-1, -1}},
-};
+// One Gram tile pair of the chunk: rows s of block J against columns t of block
+// I (J <= I), computed transposed (k_s . k_t and k_s . q_t) so that each lane
+// ends with four consecutive columns s of one row t of A and P and writes them
+// as one 8-byte piece.  bK/bQ hold the B fragments of k and q rows of block I.
+//   off-diagonal (J < I): the decay e^{gamma_t - gamma_s} is the product of
+//     the two table factors e^{gamma_t - gamma_r} (row) and e^{gamma_r - gamma_s}
+//     (column), r the last token of block J; both are <= 1, so no overflow.
+//   diagonal (J == I): masked, with one exponential per element; returns the
+//     tile of A^T in the accumulator layout (for the diagonal inverse).
+template <int I, int J, int NKB, int LDK, int LDC, int LDN>
+__device__ __forceinline__ f32x4 ws_gram_tile(const Frag<__bf16> (&bK)[NKB], const Frag<__bf16> (&bQ)[NKB],
+                                              const __bf16 *sK, __bf16 *sAn, __bf16 *sP,
+                                              const float *gam, const float *rowf, const float *browf,
+                                              const float *colf, const float *beta)
+{
+    const int gq = lane_gq(), r16 = lane_r16();
+    f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        const Frag<__bf16> fa = lds_frag(sK, LDK, 16 * J, 32 * kb);
+        aA = mma(aA, fa, bK[kb]);
+        aP = mma(aP, fa, bQ[kb]);
+    }
+    const int t = 16 * I + r16;            // row of A and P held by this lane
+    const int s0 = 16 * J + 4 * gq;        // its four columns s0 .. s0+3
+    if constexpr (J < I) {
+        const f32x4 cf = *reinterpret_cast<const f32x4 *>(colf + s0);
+        const f32x4 a = aA * cf * browf[J * WS_T + t];
+        const f32x4 p = aP * cf * rowf[J * WS_T + t];
+        *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * LDN + s0) = cvt4(-a);
+        *reinterpret_cast<bf16x4 *>(sP + t * LDC + s0) = cvt4(p);
+        return f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+        const float gt = gam[t], bt = beta[t];
+        const f32x4 gs = *reinterpret_cast<const f32x4 *>(gam + s0);
+        f32x4 a, p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = s0 + e;
+            const float dec = (s <= t) ? __expf(gt - gs[e]) : 0.f;
+            a[e] = (s < t) ? bt * aA[e] * dec : 0.f;
+            p[e] = aP[e] * dec;
+        }
+        *reinterpret_cast<bf16x4 *>(sP + t * LDC + s0) = cvt4(p);
+        return a;
+    }
+}
+
+// Gram work of prep wave PW (rows grouped so B fragments are loaded once per
+// row, one diagonal tile each):
+//   PW0: (3,0) (3,1) (0,0)   PW1: (3,2) (3,3)   PW2: (2,0) (2,1) (2,2)   PW3: (1,0) (1,1)
+// Returns A_dd^T of its diagonal tile d in the accumulator layout.
+template <int PW, int NKB, int LDK, int LDC, int LDN>
+__device__ __forceinline__ f32x4 ws_gram_wave(const __bf16 *sK, const __bf16 *sQ, __bf16 *sAn,
+                                              __bf16 *sP, const float *gam, const float *rowf,
+                                              const float *browf, const float *colf,
+                                              const float *beta, int &diag)
+{
+    Frag<__bf16> bK[NKB], bQ[NKB];
+    auto row = [&](int i) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            bK[kb] = lds_frag(sK, LDK, 16 * i, 32 * kb);
+            bQ[kb] = lds_frag(sQ, LDK, 16 * i, 32 * kb);
+        }
+    };
+#define GDN_TILE(I, J) ws_gram_tile<I, J, NKB, LDK, LDC, LDN>(bK, bQ, sK, sAn, sP, gam, rowf, browf, colf, beta)
+    if constexpr (PW == 0) {
+        row(3); GDN_TILE(3, 0); GDN_TILE(3, 1);
+        row(0); diag = 0; return GDN_TILE(0, 0);
+    } else if constexpr (PW == 1) {
+        row(3); GDN_TILE(3, 2);
+        diag = 3; return GDN_TILE(3, 3);
+    } else if constexpr (PW == 2) {
+        row(2); GDN_TILE(2, 0); GDN_TILE(2, 1);
+        diag = 2; return GDN_TILE(2, 2);
+    } else {
+        row(1); GDN_TILE(1, 0);
+        diag = 1; return GDN_TILE(1, 1);
+    }
+#undef GDN_TILE
+}
 
 struct WsArgs {
     const __bf16 *q, *k, *v;
@@ -136,12 +215,44 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
 
     if (wave >= 4) {
         // ============================ prep waves ============================
-        const int ptid = tid - 256, pw = wave - 4;
+        const int ptid = tid - 256;
+        const int pw = __builtin_amdgcn_readfirstlane(wave - 4);   // wave-uniform
         const int cg = ptid % CG, rg = ptid / CG;
         float *gam = reinterpret_cast<float *>(smem + L::kGam);
+        float *rowf = reinterpret_cast<float *>(smem + L::kRowf);
+        float *browf = reinterpret_cast<float *>(smem + L::kBrowf);
+        float *colf = reinterpret_cast<float *>(smem + L::kColf);
         f32x4 pk[RPT], pq[RPT], pv[NVV];
         float pb = 0.f, pg = 0.f;
+        // Full chunks: uniform chunk base pointers plus 32-bit per-lane offsets
+        // (a chunk spans 64 token rows, well inside 2^31 elements).
+        int koff[RPT], voff[NVV];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) koff[i] = (RPT * rg + i) * H * K + cg * EPV;
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+            const int idx = ptid + 256 * j;
+            voff[j] = (idx / (WS_VB / EPV)) * H * V + (idx % (WS_VB / EPV)) * EPV;
+        }
+        const int goff = ptid * H;
         auto load = [&](int t0) {
+            if (t0 + WS_T <= T) {
+                const long tok = row_base + (long)t0 * H;   // row of the chunk's first token
+                const __bf16 *kb = args.k + tok * K, *qb = args.q + tok * K;
+                const __bf16 *vb = args.v + tok * V + v0;
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    pk[i] = *reinterpret_cast<const f32x4 *>(kb + koff[i]);
+                    pq[i] = *reinterpret_cast<const f32x4 *>(qb + koff[i]);
+                }
+#pragma unroll
+                for (int j = 0; j < NVV; ++j) pv[j] = *reinterpret_cast<const f32x4 *>(vb + voff[j]);
+                if (ptid < WS_T) {
+                    pg = args.g[tok + goff];
+                    pb = args.beta[tok + goff];
+                }
+                return;
+            }
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int t = t0 + RPT * rg + i;
@@ -199,79 +310,47 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 *reinterpret_cast<f32x4 *>(sV + row * L::LDC + cv * EPV) = pv[j];
             }
             if (pw == 0) {
-                // running sum of g over the chunk (lane = token) and its decays
+                // running sum of g over the chunk (lane = token), its decays, and
+                // the factor tables of the Gram tiles (block ends r_j = gamma_{16j+15})
                 const float x = wave_inclusive_sum(pg);
                 const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+                const float e0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+                const float e1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+                const float e2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
                 gam[lane] = x;
                 reinterpret_cast<float *>(B + L::oEg)[lane] = __expf(x);
                 reinterpret_cast<float *>(B + L::oEgn)[lane] = __expf(gn - x);
                 if (lane == 0) reinterpret_cast<float *>(B + L::oEgN)[0] = __expf(gn);
                 sBeta[lane] = pb;
+                const float ends[3] = {e0, e1, e2};
+#pragma unroll
+                for (int jb = 0; jb < 3; ++jb) {
+                    const float f = lane > 16 * jb + 15 ? __expf(x - ends[jb]) : 0.f;
+                    rowf[jb * WS_T + lane] = f;
+                    browf[jb * WS_T + lane] = pb * f;
+                }
+                const int blk = lane >> 4;
+                const float end = blk == 0 ? e0 : blk == 1 ? e1 : blk == 2 ? e2 : gn;
+                colf[lane] = __expf(end - x);
             }
             if (n + 1 < nchunks) load((n + 1) * WS_T);
             arrivals += 4;
             prep_barrier(ctr, arrivals);
 
-            // Gram blocks on the static schedule
-            Frag<__bf16> aK[NKB], aQ[NKB];
-            int cur_i = -1;
-#pragma unroll
-            for (int pp = 0; pp < 3; ++pp) {
-                const int i = kWsGram[pw][pp][0], j = kWsGram[pw][pp][1];
-                if (i < 0) break;
-                if (i != cur_i) {
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) {
-                        aK[kb] = lds_frag(sK, L::LDK, 16 * i, 32 * kb);
-                        aQ[kb] = lds_frag(sQ, L::LDK, 16 * i, 32 * kb);
-                    }
-                    cur_i = i;
-                }
-                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const Frag<__bf16> fr = lds_frag(sK, L::LDK, 16 * j, 32 * kb);
-                    accA = mma(accA, aK[kb], fr);
-                    accP = mma(accP, aQ[kb], fr);
-                }
-                // rows t = 16i + 4gq + e, column s = 16j + r16
-                const int s = 16 * j + r16;
-                const f32x4 bt = *reinterpret_cast<const f32x4 *>(sBeta + 16 * i + 4 * gq);
-                const f32x4 gt = *reinterpret_cast<const f32x4 *>(gam + 16 * i + 4 * gq);
-                const float gs = gam[s];
-                f32x4 a, p;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * i + 4 * gq + e;
-                    const float dec = (s <= t) ? __expf(gt[e] - gs) : 0.f;
-                    a[e] = (s < t) ? bt[e] * accA[e] * dec : 0.f;
-                    p[e] = accP[e] * dec;
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * i + 4 * gq + e;
-                    sP[t * L::LDC + s] = (__bf16)p[e];
-                    if (j < i) sAn[(t - 16) * L::LDC + s] = (__bf16)(-a[e]);
-                }
-                if (j == i) {
-                    // column r16 of T_ii = (I + A_ii)^{-1} by forward substitution;
-                    // A[r'][r] is in lane 16*(r'/4) + r, element r'%4 (readlane)
-                    float x[16];
-#pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == r16) ? 1.f : 0.f;
-#pragma unroll
-                    for (int r = 0; r < 15; ++r)
-#pragma unroll
-                        for (int r2 = r + 1; r2 < 16; ++r2)
-                            x[r2] -= __int_as_float(__builtin_amdgcn_readlane(
-                                         __float_as_int(a[r2 & 3]), 16 * (r2 >> 2) + r)) * x[r];
-                    if (gq == 0) {
-#pragma unroll
-                        for (int rr = 0; rr < 16; ++rr)
-                            sTd[(16 * i + rr) * L::LDD + r16] = (__bf16)x[rr];
-                    }
-                }
-            }
+            // Gram tiles and the diagonal inverse (static per-wave schedule)
+            int diag = 0;
+            f32x4 aT;
+            if (pw == 0)
+                aT = ws_gram_wave<0, NKB, L::LDK, L::LDC, L::LDN>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
+            else if (pw == 1)
+                aT = ws_gram_wave<1, NKB, L::LDK, L::LDC, L::LDN>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
+            else if (pw == 2)
+                aT = ws_gram_wave<2, NKB, L::LDK, L::LDC, L::LDN>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
+            else
+                aT = ws_gram_wave<3, NKB, L::LDK, L::LDC, L::LDN>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
+            // T_dd^T = (I + A_dd^T)^{-1}: lane (gq, j) gets T_dd[j][4gq .. 4gq+3]
+            const f32x4 tT = unit_upper_inverse16(aT);
+            *reinterpret_cast<bf16x4 *>(sTd + (16 * diag + r16) * L::LDD + 4 * gq) = cvt4(tT);
         };
 
         if (nchunks > 0) {
@@ -345,13 +424,13 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 D[4];
         D[0] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 0, 0), reg_frag<__bf16>(X[0], z));
-        f32x4 Y = mma_lo(X[1], lds_frag_lo(sAn, L::LDC, 0, 0), reg_frag<__bf16>(D[0], z));
+        f32x4 Y = mma_lo(X[1], lds_frag_lo(sAn, L::LDN, 0, 0), reg_frag<__bf16>(D[0], z));
         D[1] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 16, 0), reg_frag<__bf16>(Y, z));
         const Frag<__bf16> Df0 = reg_frag<__bf16>(D[0], D[1]);
-        Y = mma(X[2], lds_frag(sAn, L::LDC, 16, 0), Df0);
-        f32x4 Y3 = mma(X[3], lds_frag(sAn, L::LDC, 32, 0), Df0);
+        Y = mma(X[2], lds_frag(sAn, L::LDN, 16, 0), Df0);
+        f32x4 Y3 = mma(X[3], lds_frag(sAn, L::LDN, 32, 0), Df0);
         D[2] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 32, 0), reg_frag<__bf16>(Y, z));
-        Y3 = mma_lo(Y3, lds_frag_lo(sAn, L::LDC, 32, 32), reg_frag<__bf16>(D[2], z));
+        Y3 = mma_lo(Y3, lds_frag_lo(sAn, L::LDN, 32, 32), reg_frag<__bf16>(D[2], z));
         D[3] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 48, 0), reg_frag<__bf16>(Y3, z));
         const Frag<__bf16> Df1 = reg_frag<__bf16>(D[2], D[3]);
 

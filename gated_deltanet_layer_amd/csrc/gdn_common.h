@@ -84,6 +84,72 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
     return x + off;
 }
 
+// Broadcast 16-lane row R of x to all four rows of the wave (gfx950 permlane
+// swaps: the 16-lane swap exchanges odd rows of one operand with even rows of
+// the other, the 32-lane swap the upper half of one with the lower half of the
+// other).
+template <int R> __device__ __forceinline__ float row_broadcast(float x) {
+    const int xi = __float_as_int(x);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+    const int a = (R & 1) ? (int)s16[1] : (int)s16[0];      // rows {R%2, R%2, R%2+2, R%2+2}
+    const auto s32 = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    return __int_as_float((R & 2) ? (int)s32[1] : (int)s32[0]);
+}
+
+// Broadcast lane N of each 16-lane row to the whole row (DPP row_newbcast).
+template <int N> __device__ __forceinline__ float lane_in_row(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, false));
+}
+
+// Inverse of a unit lower triangular 16 x 16 matrix I + A held in the MFMA
+// accumulator layout (lane 16*gq + j holds A[4gq + e][j], e = 0..3; A strictly
+// lower).  Returns T = (I + A)^{-1} in the same layout.  Column j is built by
+// forward substitution, right-looking: once row r is final, every later row
+// subtracts A[row][r] * T[r][j].  The pivot row comes from one lane group
+// (row_broadcast), the column of A from one lane of each row (lane_in_row);
+// A's zeros on and above the diagonal make the update a no-op where it must be.
+__device__ __forceinline__ f32x4 unit_lower_inverse16(f32x4 a) {
+    const int lane = threadIdx.x & 63, gq = lane >> 4, j = lane & 15;
+    f32x4 t;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = (4 * gq + e == j) ? 1.f : 0.f;
+#define GDN_INV_STEP(r)                                                   \
+    {                                                                     \
+        const float piv = row_broadcast<(r) / 4>(t[(r) % 4]);             \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e)                     \
+            t[e] -= lane_in_row<(r)>(a[e]) * piv;                         \
+    }
+    GDN_INV_STEP(0) GDN_INV_STEP(1) GDN_INV_STEP(2) GDN_INV_STEP(3)
+    GDN_INV_STEP(4) GDN_INV_STEP(5) GDN_INV_STEP(6) GDN_INV_STEP(7)
+    GDN_INV_STEP(8) GDN_INV_STEP(9) GDN_INV_STEP(10) GDN_INV_STEP(11)
+    GDN_INV_STEP(12) GDN_INV_STEP(13) GDN_INV_STEP(14)
+#undef GDN_INV_STEP
+    return t;
+}
+
+// Inverse of a unit upper triangular 16 x 16 matrix I + U held in the MFMA
+// accumulator layout (lane 16*gq + j holds U[4gq + e][j]; U strictly upper).
+// Returns (I + U)^{-1} in the same layout, by backward substitution:
+// once row r is final, every earlier row subtracts U[row][r] * X[r][j].
+__device__ __forceinline__ f32x4 unit_upper_inverse16(f32x4 u) {
+    const int lane = threadIdx.x & 63, gq = lane >> 4, j = lane & 15;
+    f32x4 t;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = (4 * gq + e == j) ? 1.f : 0.f;
+#define GDN_INVU_STEP(r)                                                  \
+    {                                                                     \
+        const float piv = row_broadcast<(r) / 4>(t[(r) % 4]);             \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e)                     \
+            t[e] -= lane_in_row<(r)>(u[e]) * piv;                         \
+    }
+    GDN_INVU_STEP(15) GDN_INVU_STEP(14) GDN_INVU_STEP(13) GDN_INVU_STEP(12)
+    GDN_INVU_STEP(11) GDN_INVU_STEP(10) GDN_INVU_STEP(9) GDN_INVU_STEP(8)
+    GDN_INVU_STEP(7) GDN_INVU_STEP(6) GDN_INVU_STEP(5) GDN_INVU_STEP(4)
+    GDN_INVU_STEP(3) GDN_INVU_STEP(2) GDN_INVU_STEP(1)
+#undef GDN_INVU_STEP
+    return t;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
     return x;

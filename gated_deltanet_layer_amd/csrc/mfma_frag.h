@@ -116,4 +116,17 @@ template <> struct Pack<__bf16, 4> { typedef bf16x4 type; };
 template <> struct Pack<__bf16, 2> { typedef bf16x2 type; };
 template <> struct Pack<float, 4> { typedef f32x4 type; };
 
+
+// Gram blocks (i, j), j <= i, handled by wave w (0..3) in step pp (0..2):
+//   w0: (3,0) (3,1) (0,0)   w1: (3,2) (3,3)   w2: (2,0) (2,1) (2,2)   w3: (1,0) (1,1)
+// Rows are grouped so a wave reuses its left-hand fragments, and every wave owns
+// exactly one diagonal block.  i < 0 marks an empty step.  w must be
+// wave-uniform; the selection compiles to scalar instructions.
+__device__ __forceinline__ void gram_block(int w, int pp, int &i, int &j) {
+    if (w == 0) { i = pp < 2 ? 3 : 0; j = pp < 2 ? pp : 0; }
+    else if (w == 1) { i = pp < 2 ? 3 : -1; j = pp + 2; }
+    else if (w == 2) { i = 2; j = pp; }
+    else { i = pp < 2 ? 1 : -1; j = pp; }
+}
+
 } // namespace gdn
