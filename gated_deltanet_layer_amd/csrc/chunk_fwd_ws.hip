@@ -32,11 +32,16 @@ constexpr int WS_NTHR = 512;   // 4 chain waves + 4 prep waves
 
 template <int K> struct WsSmem {
     static constexpr int PAD = 8;                 // bf16 elements = 16 bytes
-    static constexpr int LDK = K + PAD;           // [64][K] q and k
+    // q, k, k^T, -A and P are stored in fragment order (frag_col), so every
+    // fragment is one 16-byte read.  -A and P rows carry a 16-byte pad, q, k
+    // and k^T rows an XOR swizzle of their 16-byte chunks (qk_swz, kt_swz);
+    // either keeps the 16 rows of a fragment read on distinct banks.  v and
+    // T_ii are stored plainly.
+    static constexpr int LDK = K;                 // [64][K] q and k (chunk-swizzled)
     static constexpr int LDC = WS_T + PAD;        // [*][64] v, -A, P
-    static constexpr int LDT = WS_T;              // [K][64] k^T (swizzled, unpadded)
+    static constexpr int LDT = WS_T;              // [K][64] k^T (chunk-swizzled)
     static constexpr int LDD = 16 + PAD;          // [64][16] T_ii
-    static constexpr int LDN = 48 + PAD;          // [48][48] -A: rows 16..63, cols 0..47
+    static constexpr int LDN = LDC;               // [48][64] -A: rows 16..63
     static constexpr int al(int x) { return (x + 255) & ~255; }
     // one buffer
     static constexpr int oK = 0;
@@ -60,6 +65,10 @@ template <int K> struct WsSmem {
     static constexpr int bytes = al(kCtr + 16);
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
+
+// Chunk swizzles (in 16-byte chunks): q/k row t has K/8 chunks; k^T row c has 8.
+template <int K> __device__ __forceinline__ int qk_swz(int t) { return t & (K / 8 - 1); }
+__device__ __forceinline__ int kt_swz(int c) { return ((c >> 1) ^ (c >> 4)) & 7; }
 
 // Barrier among the four prep waves: each wave adds one arrival to an LDS
 // counter and waits until the counter reaches `target` (4 per use).  All four
@@ -94,9 +103,10 @@ __device__ __forceinline__ f32x4 ws_gram_tile(const Frag<__bf16> (&bK)[NKB], con
 {
     const int gq = lane_gq(), r16 = lane_r16();
     f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
+    static_assert(LDK % 64 == 0, "q/k rows are unpadded");
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-        const Frag<__bf16> fa = lds_frag(sK, LDK, 16 * J, 32 * kb);
+        const Frag<__bf16> fa = lds_frag_fos(sK, LDK, 16 * J, 32 * kb, qk_swz<LDK>(16 * J + r16));
         aA = mma(aA, fa, bK[kb]);
         aP = mma(aP, fa, bQ[kb]);
     }
@@ -106,8 +116,8 @@ __device__ __forceinline__ f32x4 ws_gram_tile(const Frag<__bf16> (&bK)[NKB], con
         const f32x4 cf = *reinterpret_cast<const f32x4 *>(colf + s0);
         const f32x4 a = aA * cf * browf[J * WS_T + t];
         const f32x4 p = aP * cf * rowf[J * WS_T + t];
-        *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * LDN + s0) = cvt4(-a);
-        *reinterpret_cast<bf16x4 *>(sP + t * LDC + s0) = cvt4(p);
+        *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * LDN + frag_col(s0)) = cvt4(-a);
+        *reinterpret_cast<bf16x4 *>(sP + t * LDC + frag_col(s0)) = cvt4(p);
         return f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
         const float gt = gam[t], bt = beta[t];
@@ -120,7 +130,7 @@ __device__ __forceinline__ f32x4 ws_gram_tile(const Frag<__bf16> (&bK)[NKB], con
             a[e] = (s < t) ? bt * aA[e] * dec : 0.f;
             p[e] = aP[e] * dec;
         }
-        *reinterpret_cast<bf16x4 *>(sP + t * LDC + s0) = cvt4(p);
+        *reinterpret_cast<bf16x4 *>(sP + t * LDC + frag_col(s0)) = cvt4(p);
         return a;
     }
 }
@@ -139,8 +149,8 @@ __device__ __forceinline__ f32x4 ws_gram_wave(const __bf16 *sK, const __bf16 *sQ
     auto row = [&](int i) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            bK[kb] = lds_frag(sK, LDK, 16 * i, 32 * kb);
-            bQ[kb] = lds_frag(sQ, LDK, 16 * i, 32 * kb);
+            bK[kb] = lds_frag_fos(sK, LDK, 16 * i, 32 * kb, qk_swz<LDK>(16 * i + lane_r16()));
+            bQ[kb] = lds_frag_fos(sQ, LDK, 16 * i, 32 * kb, qk_swz<LDK>(16 * i + lane_r16()));
         }
     };
 #define GDN_TILE(I, J) ws_gram_tile<I, J, NKB, LDK, LDC, LDN>(bK, bQ, sK, sAn, sP, gam, rowf, browf, colf, beta)
@@ -293,8 +303,14 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
             float *sBeta = reinterpret_cast<float *>(B + L::oBeta);
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                *reinterpret_cast<f32x4 *>(sK + (RPT * rg + i) * L::LDK + cg * EPV) = pk[i];
-                *reinterpret_cast<f32x4 *>(sQ + (RPT * rg + i) * L::LDK + cg * EPV) = pq[i];
+                // 8 logical columns = two groups of 4 in fragment order
+                const int row = RPT * rg + i, sw = qk_swz<K>(row) << 3;
+                __bf16 *kr = sK + row * L::LDK, *qr = sQ + row * L::LDK;
+                const int c0 = frag_col(cg * EPV) ^ sw, c1 = frag_col(cg * EPV + 4) ^ sw;
+                *reinterpret_cast<f32x2 *>(kr + c0) = f32x2{pk[i][0], pk[i][1]};
+                *reinterpret_cast<f32x2 *>(kr + c1) = f32x2{pk[i][2], pk[i][3]};
+                *reinterpret_cast<f32x2 *>(qr + c0) = f32x2{pq[i][0], pq[i][1]};
+                *reinterpret_cast<f32x2 *>(qr + c1) = f32x2{pq[i][2], pq[i][3]};
             }
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
@@ -302,7 +318,7 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 pack_t pt;
 #pragma unroll
                 for (int i = 0; i < RPT; ++i) pt[i] = reinterpret_cast<const __bf16 *>(&pk[i])[e];
-                *reinterpret_cast<pack_t *>(sKT + ch * L::LDT + ((RPT * rg) ^ kmt_swz<EPV>(ch))) = pt;
+                *reinterpret_cast<pack_t *>(sKT + ch * L::LDT + (frag_col(RPT * rg) ^ (kt_swz(ch) << 3))) = pt;
             }
 #pragma unroll
             for (int j = 0; j < NVV; ++j) {
@@ -403,8 +419,9 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    ak = mma(ak, lds_frag(sK, L::LDK, 16 * rt, 32 * kb), Sb[kb]);
-                    aq = mma(aq, lds_frag(sQ, L::LDK, 16 * rt, 32 * kb), Sb[kb]);
+                    const int sw = qk_swz<K>(16 * rt + r16);
+                    ak = mma(ak, lds_frag_fos(sK, L::LDK, 16 * rt, 32 * kb, sw), Sb[kb]);
+                    aq = mma(aq, lds_frag_fos(sQ, L::LDK, 16 * rt, 32 * kb, sw), Sb[kb]);
                 }
                 const f32x4 eg = *reinterpret_cast<const f32x4 *>(sEg + 16 * rt + 4 * gq);
                 KS[rt] = ak * eg;
@@ -424,24 +441,24 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 D[4];
         D[0] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 0, 0), reg_frag<__bf16>(X[0], z));
-        f32x4 Y = mma_lo(X[1], lds_frag_lo(sAn, L::LDN, 0, 0), reg_frag<__bf16>(D[0], z));
+        f32x4 Y = mma_lo(X[1], lds_frag_fo_lo(sAn, L::LDN, 0, 0), reg_frag<__bf16>(D[0], z));
         D[1] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 16, 0), reg_frag<__bf16>(Y, z));
         const Frag<__bf16> Df0 = reg_frag<__bf16>(D[0], D[1]);
-        Y = mma(X[2], lds_frag(sAn, L::LDN, 16, 0), Df0);
-        f32x4 Y3 = mma(X[3], lds_frag(sAn, L::LDN, 32, 0), Df0);
+        Y = mma(X[2], lds_frag_fo(sAn, L::LDN, 16, 0), Df0);
+        f32x4 Y3 = mma(X[3], lds_frag_fo(sAn, L::LDN, 32, 0), Df0);
         D[2] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 32, 0), reg_frag<__bf16>(Y, z));
-        Y3 = mma_lo(Y3, lds_frag_lo(sAn, L::LDN, 32, 32), reg_frag<__bf16>(D[2], z));
+        Y3 = mma_lo(Y3, lds_frag_fo_lo(sAn, L::LDN, 32, 32), reg_frag<__bf16>(D[2], z));
         D[3] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 48, 0), reg_frag<__bf16>(Y3, z));
         const Frag<__bf16> Df1 = reg_frag<__bf16>(D[2], D[3]);
 
         // O = Q+ S + P D
         f32x4 O[4];
-        O[0] = mma_lo(QS[0], lds_frag_lo(sP, L::LDC, 0, 0), Df0);
-        O[1] = mma(QS[1], lds_frag(sP, L::LDC, 16, 0), Df0);
-        O[2] = mma(QS[2], lds_frag(sP, L::LDC, 32, 0), Df0);
-        O[2] = mma_lo(O[2], lds_frag_lo(sP, L::LDC, 32, 32), Df1);
-        O[3] = mma(QS[3], lds_frag(sP, L::LDC, 48, 0), Df0);
-        O[3] = mma(O[3], lds_frag(sP, L::LDC, 48, 32), Df1);
+        O[0] = mma_lo(QS[0], lds_frag_fo_lo(sP, L::LDC, 0, 0), Df0);
+        O[1] = mma(QS[1], lds_frag_fo(sP, L::LDC, 16, 0), Df0);
+        O[2] = mma(QS[2], lds_frag_fo(sP, L::LDC, 32, 0), Df0);
+        O[2] = mma_lo(O[2], lds_frag_fo_lo(sP, L::LDC, 32, 32), Df1);
+        O[3] = mma(QS[3], lds_frag_fo(sP, L::LDC, 48, 0), Df0);
+        O[3] = mma(O[3], lds_frag_fo(sP, L::LDC, 48, 32), Df1);
         if (args.o) {
             // through this wave's own v columns (already consumed) for row stores
 #pragma unroll
@@ -468,8 +485,8 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             S_acc[ct] *= egN;
-            S_acc[ct] = mma(S_acc[ct], lds_frag_kmt<EPV>(sKT, L::LDT, 16 * ct, 0), Ef0);
-            S_acc[ct] = mma(S_acc[ct], lds_frag_kmt<EPV>(sKT, L::LDT, 16 * ct, 32), Ef1);
+            S_acc[ct] = mma(S_acc[ct], lds_frag_fos(sKT, L::LDT, 16 * ct, 0, kt_swz(16 * ct + r16)), Ef0);
+            S_acc[ct] = mma(S_acc[ct], lds_frag_fos(sKT, L::LDT, 16 * ct, 32, kt_swz(16 * ct + r16)), Ef1);
         }
         lds_barrier();
     }

@@ -61,6 +61,33 @@ __device__ __forceinline__ Frag<float> lds_frag_kmt(const float *M, int ld, int 
             *reinterpret_cast<const f32x4 *>(p + ((col + 16) ^ s))};
 }
 
+// Fragment-ordered storage ("frag order"): inside each block of 32 columns the
+// columns are stored in the order lane group gq reads them, so one lane's
+// fragment (logical columns k0 + 4gq .. +3 and k0 + 16 + 4gq .. +3) is 16
+// contiguous bytes and loads with one 16-byte LDS read.  Groups of 4
+// consecutive logical columns stay contiguous.
+__device__ __forceinline__ constexpr int frag_col(int c) {
+    return (c & ~31) | (((c & 15) >> 2) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+__device__ __forceinline__ Frag<__bf16> lds_frag_fo(const __bf16 *M, int ld, int row0, int k0) {
+    return {*reinterpret_cast<const bf16x8 *>(M + (row0 + lane_r16()) * ld + k0 + 8 * lane_gq())};
+}
+// First 16 logical columns only (the other half zero).
+__device__ __forceinline__ Frag<__bf16> lds_frag_fo_lo(const __bf16 *M, int ld, int row0, int k0) {
+    const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+    return {cat8(*reinterpret_cast<const bf16x4 *>(M + (row0 + lane_r16()) * ld + k0 + 8 * lane_gq()), z)};
+}
+
+// Unpadded fragment-order rows with their 16-byte chunks XOR-swizzled per row
+// (chunk ^ swz), so the 16 rows of a fragment read fall on distinct banks.
+// swz is a chunk count below the number of chunks in a row; groups of 4
+// columns stay contiguous.
+__device__ __forceinline__ Frag<__bf16> lds_frag_fos(const __bf16 *M, int ld, int row0, int k0,
+                                                    int swz) {
+    return {*reinterpret_cast<const bf16x8 *>(M + (row0 + lane_r16()) * ld +
+                                              ((k0 + 8 * lane_gq()) ^ (swz << 3)))};
+}
+
 // B operand from two accumulator tiles holding rows k0..k0+15 and k0+16..k0+31.
 template <typename OT> __device__ __forceinline__ Frag<OT> reg_frag(f32x4 c0, f32x4 c1);
 template <> __device__ __forceinline__ Frag<__bf16> reg_frag<__bf16>(f32x4 c0, f32x4 c1) {
