@@ -1,0 +1,289 @@
+"""GPU checks beyond plain parity: special cases with known answers, the two
+execution modes against each other, state passing, the gate forms against each
+other, run-to-run determinism, aliasing and the state-only call, stress inputs
+that keep the state alive across chunks, and the long 48-head prefill.
+
+Each case compares the HIP path (through the C ABI) with the fp64 oracle to the
+bound of tests/parity.py, and where two HIP calls must agree, compares them too.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_layer_amd as gdn
+import oracle
+from gdn_inputs import CHUNK_CONFIGS, ChunkConfig, chunk_inputs
+from tests.parity import TOL_BF16, TOL_FP32, slice_rel, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(d):
+    return {k: (None if v is None else v.to(DEV)) for k, v in d.items()}
+
+
+def _tol(dtype):
+    return TOL_FP32 if dtype == "fp32" else TOL_BF16
+
+
+def _chunk(d, S0="from_inputs", want_o=True):
+    S0 = d["S0"] if isinstance(S0, str) else S0
+    o, S = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0, want_o=want_o)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def _oracle(d):
+    return oracle.forward(d["q"].cpu(), d["k"].cpu(), d["v"].cpu(), d["g"].cpu(),
+                          d["beta"].cpu(), None if d["S0"] is None else d["S0"].cpu())
+
+
+def _assert_vs_oracle(o, S, ro, rS, tol, label):
+    eo = slice_rel(to_np(o), ro, (0, 2)) if o is not None else 0.0
+    eS = slice_rel(to_np(S), rS, (0, 1))
+    _say(f"[modes] {label}: err_o={eo:.3e} err_S={eS:.3e} tol={tol:.0e}")
+    assert np.isfinite(to_np(S)).all()
+    assert eo <= tol and eS <= tol
+
+
+# ------------------------------------------------------------- special cases
+@pytest.mark.parametrize("K,dtype,gate", [(64, "fp32", "head"), (64, "fp32", "channel"),
+                                          (128, "bf16", "head"), (128, "bf16", "channel")])
+def test_no_write_no_decay_keeps_state(K, dtype, gate):
+    """beta = 0 and g = 0 make every step the identity on the state: S_T = S0 and
+    o_t = S0^T q_t (Atomic-GDN2 card, section 2.1, with alpha = 1, beta = 0)."""
+    cfg = ChunkConfig("p1", B=2, H=3, T=150, K=K, V=K, dtype=dtype, gate=gate, s0_sigma=0.5,
+                      g_scale=0.0, g_cap=5.0 if gate == "channel" else None)
+    d = _dev(chunk_inputs(cfg))
+    d["beta"] = torch.zeros_like(d["beta"])
+    _say(f"[modes] identity K{K} {dtype} {gate}")
+    o, S = _chunk(d)
+    S0 = d["S0"]
+    assert torch.equal(S, S0) or (S - S0).abs().max().item() <= 1e-6 * S0.abs().max().item()
+    ref_o = torch.einsum("bthk,bhkv->bthv", d["q"].double().cpu(), S0.double().cpu())
+    eo = slice_rel(to_np(o), ref_o.numpy(), (0, 2))
+    _say(f"[modes] identity: err_o={eo:.3e}")
+    assert eo <= _tol(dtype)
+
+
+def _orthonormal_keys(T, K, gen):
+    """T <= K orthonormal rows from the QR factorisation of a Gaussian matrix."""
+    a = torch.randn(K, K, generator=gen, dtype=torch.float64)
+    qm, _ = torch.linalg.qr(a)
+    return qm[:T].float()
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_orthonormal_keys_exact_recall(gate):
+    """Delta rule with beta = 1, no decay and orthonormal keys: each write replaces
+    what the key held, so reading with q_t = k_t returns v_t exactly, and the final
+    state maps every key to its value (MindPattern 'Gated DeltaNet' page, the
+    delta rule writes the error)."""
+    B, H, T, K, V = 1, 2, 64, 64, 64
+    gen = torch.Generator().manual_seed(7)
+    k = torch.stack([torch.stack([_orthonormal_keys(T, K, gen) for _ in range(H)], 1)
+                     for _ in range(B)])                          # [B,T,H,K]
+    v = torch.randn(B, T, H, V, generator=gen)
+    S0 = torch.randn(B, H, K, V, generator=gen)
+    g = torch.zeros(B, T, H, K) if gate == "channel" else torch.zeros(B, T, H)
+    d = _dev(dict(q=k.clone(), k=k, v=v, g=g, beta=torch.ones(B, T, H), S0=S0))
+    _say(f"[modes] exact recall {gate}")
+    o, S = _chunk(d)
+    err_o = (o - d["v"]).abs().max().item() / d["v"].abs().max().item()
+    recall = torch.einsum("bhkv,bthk->bthv", S.double(), d["k"].double())
+    err_S = (recall - d["v"].double()).abs().max().item() / d["v"].abs().max().item()
+    _say(f"[modes] exact recall: err_o={err_o:.3e} err_recall={err_S:.3e}")
+    assert err_o <= TOL_FP32 and err_S <= TOL_FP32
+
+
+# ------------------------------------------------------------- mode agreement
+@pytest.mark.parametrize("K,dtype,gate", [(64, "fp32", "head"), (64, "fp32", "channel"),
+                                          (128, "bf16", "head"), (128, "bf16", "channel"),
+                                          (64, "bf16", "head"), (64, "bf16", "channel")])
+def test_chunkwise_equals_token_steps(K, dtype, gate):
+    """The chunkwise prefill and T chained fused decode steps compute the same
+    recurrence (MindPattern 'Gated DeltaNet' page, the two execution modes)."""
+    cfg = ChunkConfig("p6", B=2, H=3, T=100, K=K, V=K, dtype=dtype, gate=gate, s0_sigma=0.1,
+                      g_sigma=2.0 if gate == "channel" else 1.0,
+                      g_cap=5.0 if gate == "channel" else None)
+    d = _dev(chunk_inputs(cfg))
+    _say(f"[modes] chunk vs steps K{K} {dtype} {gate}")
+    o_c, S_c = _chunk(d)
+    S = d["S0"].clone()
+    outs = []
+    for t in range(cfg.T):
+        sl = lambda x: x[:, t].contiguous()
+        outs.append(gdn.recurrent_step_(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]),
+                                        sl(d["beta"]), S))
+    torch.cuda.synchronize()
+    o_s = torch.stack(outs, 1)
+    ro, rS = _oracle(d)
+    tol = _tol(dtype)
+    _assert_vs_oracle(o_c, S_c, ro, rS, tol, "chunkwise")
+    _assert_vs_oracle(o_s, S, ro, rS, tol, "token steps")
+    e = slice_rel(to_np(o_c), to_np(o_s), (0, 2))
+    eS = slice_rel(to_np(S_c), to_np(S), (0, 1))
+    _say(f"[modes] chunk vs steps: o {e:.3e} S {eS:.3e}")
+    assert e <= tol and eS <= tol
+
+
+@pytest.mark.parametrize("K,dtype,gate,T1", [(64, "fp32", "head", 64), (64, "fp32", "channel", 100),
+                                             (128, "bf16", "head", 100), (128, "bf16", "head", 128),
+                                             (128, "bf16", "channel", 37)])
+def test_split_sequence_state_passing(K, dtype, gate, T1):
+    """Running tokens [0, T1) and then [T1, T) from the carried state equals one
+    call over [0, T): the fixed-size state is the whole memory (Hybrid layouts,
+    lesson 4.16, 01 Concept)."""
+    cfg = ChunkConfig("p7", B=2, H=2, T=300, K=K, V=K, dtype=dtype, gate=gate, s0_sigma=0.1,
+                      g_scale=0.05, g_sigma=2.0 if gate == "channel" else 1.0,
+                      g_cap=5.0 if gate == "channel" else None)
+    d = _dev(chunk_inputs(cfg))
+    _say(f"[modes] split at {T1}: K{K} {dtype} {gate}")
+    o, S = _chunk(d)
+    part = lambda lo, hi: {n: (x[:, lo:hi].contiguous() if n != "S0" else x) for n, x in d.items()}
+    d1, d2 = part(0, T1), part(T1, cfg.T)
+    o1, S1 = _chunk(d1)
+    o2, S2 = _chunk(d2, S0=S1)
+    o12 = torch.cat([o1, o2], 1)
+    tol = _tol(dtype)
+    e = slice_rel(to_np(o12), to_np(o), (0, 2))
+    eS = slice_rel(to_np(S2), to_np(S), (0, 1))
+    _say(f"[modes] split vs whole: o {e:.3e} S {eS:.3e}")
+    assert e <= tol and eS <= tol
+    ro, rS = _oracle(d)
+    _assert_vs_oracle(o12, S2, ro, rS, tol, "split")
+
+
+@pytest.mark.parametrize("K,dtype", [(64, "fp32"), (128, "bf16"), (64, "bf16")])
+def test_replicated_channel_gate_equals_scalar_gate(K, dtype):
+    """A per-key-channel gate that repeats one value over the K channels is the
+    scalar-per-head gate (The 388-Million-Parameter Laboratory, the scalar to
+    channel-wise identity check)."""
+    cfg = ChunkConfig("p3", B=2, H=3, T=200, K=K, V=K, dtype=dtype, gate="head", s0_sigma=0.1)
+    d = _dev(chunk_inputs(cfg))
+    _say(f"[modes] replicated gate K{K} {dtype}")
+    o_h, S_h = _chunk(d)
+    dc = dict(d)
+    dc["g"] = d["g"].unsqueeze(-1).expand(*d["g"].shape, K).contiguous()
+    o_c, S_c = _chunk(dc)
+    ro, rS = _oracle(d)
+    tol = _tol(dtype)
+    _assert_vs_oracle(o_h, S_h, ro, rS, tol, "scalar gate")
+    _assert_vs_oracle(o_c, S_c, ro, rS, tol, "replicated channel gate")
+    e = slice_rel(to_np(o_c), to_np(o_h), (0, 2))
+    eS = slice_rel(to_np(S_c), to_np(S_h), (0, 1))
+    _say(f"[modes] replicated vs scalar: o {e:.3e} S {eS:.3e}")
+    agree = 1e-5 if dtype == "fp32" else tol
+    assert e <= agree and eS <= agree
+
+
+# ------------------------------------------------------------- call forms
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_deterministic(gate):
+    cfg = ChunkConfig("det", B=2, H=4, T=1000, K=128, V=128, dtype="bf16", gate=gate,
+                      s0_sigma=0.05, g_sigma=2.0 if gate == "channel" else 1.0,
+                      g_cap=5.0 if gate == "channel" else None)
+    d = _dev(chunk_inputs(cfg))
+    _say(f"[modes] determinism {gate}")
+    o1, S1 = _chunk(d)
+    o2, S2 = _chunk(d)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("K,dtype,gate", [(64, "fp32", "head"), (128, "bf16", "head"),
+                                          (128, "bf16", "channel")])
+def test_in_place_state_and_state_only(K, dtype, gate):
+    """S_T may alias S0, and o may be omitted; neither changes the state."""
+    cfg = ChunkConfig("alias", B=2, H=3, T=130, K=K, V=K, dtype=dtype, gate=gate, s0_sigma=0.1,
+                      g_cap=5.0 if gate == "channel" else None)
+    d = _dev(chunk_inputs(cfg))
+    _say(f"[modes] aliasing K{K} {dtype} {gate}")
+    o, S = _chunk(d)
+    _, S_only = _chunk(d, want_o=False)
+    assert torch.equal(S_only, S)
+    B, T, H = cfg.B, cfg.T, cfg.H
+    S_io = d["S0"].clone()
+    o2 = torch.empty(B, T, H, K, dtype=DT[dtype], device=DEV)
+    gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S_io, o2, S_io)
+    torch.cuda.synchronize()
+    assert torch.equal(S_io, S) and torch.equal(o2, o)
+
+
+# ------------------------------------------------------------- stress inputs
+def test_stress_no_decay_fp32():
+    """Small fp32 case with g = 0: the state carries everything across chunks."""
+    cfg = CHUNK_CONFIGS["scalar_fp32_small"].with_(g_scale=0.0, s0_sigma=0.1)
+    d = _dev(chunk_inputs(cfg))
+    _say("[modes] stress g=0 fp32")
+    o, S = _chunk(d)
+    _assert_vs_oracle(o, S, *_oracle(d), TOL_FP32, "g=0 fp32")
+
+
+@pytest.mark.parametrize("K,gate", [(128, "head"), (64, "head"), (128, "channel")])
+def test_stress_slow_decay_bf16(K, gate):
+    """Slow decay (g scaled by 0.01) over long sequences: the inter-chunk path
+    carries the result."""
+    cfg = ChunkConfig("p2", B=1, H=4, T=4096, K=K, V=K, dtype="bf16", gate=gate, g_scale=0.01,
+                      s0_sigma=0.02, g_sigma=2.0 if gate == "channel" else 1.0,
+                      g_cap=5.0 if gate == "channel" else None)
+    d = _dev(chunk_inputs(cfg))
+    _say(f"[modes] stress slow decay K{K} {gate}")
+    o, S = _chunk(d)
+    _assert_vs_oracle(o, S, *_oracle(d), TOL_BF16, "slow decay")
+
+
+@pytest.mark.parametrize("dtype,K", [("fp32", 64), ("bf16", 128), ("bf16", 64)])
+def test_stress_channel_gate_extremes(dtype, K):
+    """Half the key channels never decay (g = 0), the other half take the largest
+    decay the clamp allows (g = -5), the two ends of the gate's domain
+    (Atomic-GDN2 card, section 2.1)."""
+    cfg = ChunkConfig("p3x", B=2, H=2, T=300, K=K, V=K, dtype=dtype, gate="channel",
+                      g_cap=5.0, s0_sigma=0.1)
+    d = _dev(chunk_inputs(cfg))
+    g = torch.zeros_like(d["g"])
+    g[..., 1::2] = -5.0
+    d["g"] = g
+    _say(f"[modes] channel extremes {dtype} K{K}")
+    o, S = _chunk(d)
+    _assert_vs_oracle(o, S, *_oracle(d), _tol(dtype), "g in {0,-5}")
+
+
+@pytest.mark.parametrize("T", [1, 63, 65, 100])
+@pytest.mark.parametrize("K,gate", [(64, "head"), (128, "head"), (64, "channel"), (128, "channel")])
+def test_ragged_bf16(T, K, gate):
+    cfg = ChunkConfig("p4", B=3, H=2, T=T, K=K, V=K, dtype="bf16", gate=gate, s0_sigma=0.1,
+                      g_sigma=2.0 if gate == "channel" else 1.0,
+                      g_cap=5.0 if gate == "channel" else None)
+    d = _dev(chunk_inputs(cfg))
+    _say(f"[modes] ragged T{T} K{K} {gate}")
+    o, S = _chunk(d)
+    _assert_vs_oracle(o, S, *_oracle(d), TOL_BF16, f"ragged T{T}")
+
+
+# ------------------------------------------------------------- long prefill
+@pytest.mark.timeout(600)
+def test_long_prefill_48_heads_sampled():
+    """T = 262144 with 48 heads of 128 x 128 fp32 state and a given S0: the GPU
+    runs the whole batch; the oracle follows three heads over the whole sequence."""
+    cfg = CHUNK_CONFIGS["channel_long"]
+    _say(f"[modes] long prefill B{cfg.B} H{cfg.H} T{cfg.T}")
+    d = chunk_inputs(cfg, device=DEV)
+    o, S = _chunk(d)
+    heads = [0, 23, cfg.H - 1]
+    sel = lambda x: x[:, :, heads].cpu().contiguous()
+    _say("[modes] long prefill: GPU done, oracle on 3 heads")
+    ro, rS = oracle.forward(sel(d["q"]), sel(d["k"]), sel(d["v"]), sel(d["g"]), sel(d["beta"]),
+                            d["S0"][:, heads].cpu().contiguous(), nthreads=3)
+    eo = slice_rel(to_np(o[:, :, heads]), ro, (0, 2))
+    eS = slice_rel(to_np(S[:, heads]), rS, (0, 1))
+    _say(f"[modes] long prefill: err_o={eo:.3e} err_S={eS:.3e}")
+    assert eo <= TOL_BF16 and eS <= TOL_BF16
