@@ -10,19 +10,28 @@
 //                    run chunk c: K+S, Q+S, X = diag(beta)(V - K+S), the block
 //                    forward substitution for D, O = Q+S + P D, and
 //                    S' = e^{gamma_n} S + K^T (e^{gamma_n - gamma} D).
-//   prep waves 4-7   get chunk c+1 ready: stage q, k, k^T, v and the decay
-//                    vectors into the other half of a double-buffered LDS set,
-//                    then compute the Gram blocks -A (strictly lower), P (lower)
-//                    and the 16 x 16 diagonal inverses T_ii, and load chunk c+2
-//                    from HBM into registers.
+//   prep waves 4-7   get chunk c+1 ready: the running sum of g and its
+//                    exponentials, the Gram blocks -A (strictly lower) and P
+//                    (lower), and the 16 x 16 diagonal inverses T_ii; and they
+//                    keep the copies from HBM in flight: q and k of chunk c+2
+//                    and v of chunk c+1 go straight from global memory into LDS
+//                    (global_load_lds, 16 bytes per lane), so no wave stages
+//                    them through registers.
+//
+// q, k and v stay row-major in LDS (16-byte chunks XOR-swizzled per row).  Each
+// operand is read in the layout its MFMA needs: 16-byte reads for the q and k
+// fragments of K+S, Q+S and the Gram blocks, and the gfx950 transposing read
+// (ds_read_b64_tr_b16) for the k^T fragments of the state update and for v in
+// the accumulator layout.  To make the q/k fragments single 16-byte reads, the
+// rows of the state are kept in a fixed order of the key index: accumulator row
+// 32b + 16h + 4g + e holds key 32b + 8g + 4h + e.
 //
 // A single workgroup barrier per chunk hands the buffers over.  The prep waves
-// also need one barrier among themselves per chunk (staging before Gram); it
-// is an LDS arrival counter that only those four waves use, so the chain waves
-// never wait for it.  Each SIMD runs one chain wave and one prep wave, so the
-// latency-bound prep work (substitution, exponentials, staging) overlaps the
-// chain's matrix-core work.
+// also need one barrier among themselves per chunk (all of q and k landed
+// before the Gram blocks); it is an LDS arrival counter that only those four
+// waves use.
 #include "mfma_frag.h"
+#include <stdint.h>
 
 namespace gdn {
 
@@ -31,44 +40,100 @@ constexpr int WS_VB = 64;      // value columns per workgroup
 constexpr int WS_NTHR = 512;   // 4 chain waves + 4 prep waves
 
 template <int K> struct WsSmem {
-    static constexpr int PAD = 8;                 // bf16 elements = 16 bytes
-    // q, k, k^T, -A and P are stored in fragment order (frag_col), so every
-    // fragment is one 16-byte read.  -A and P rows carry a 16-byte pad, q, k
-    // and k^T rows an XOR swizzle of their 16-byte chunks (qk_swz, kt_swz);
-    // either keeps the 16 rows of a fragment read on distinct banks.  v and
-    // T_ii are stored plainly.
-    static constexpr int LDK = K;                 // [64][K] q and k (chunk-swizzled)
-    static constexpr int LDC = WS_T + PAD;        // [*][64] v, -A, P
-    static constexpr int LDT = WS_T;              // [K][64] k^T (chunk-swizzled)
-    static constexpr int LDD = 16 + PAD;          // [64][16] T_ii
-    static constexpr int LDN = LDC;               // [48][64] -A: rows 16..63
     static constexpr int al(int x) { return (x + 255) & ~255; }
-    // one buffer
-    static constexpr int oK = 0;
-    static constexpr int oQ = oK + WS_T * LDK * 2;
-    static constexpr int oKT = oQ + WS_T * LDK * 2;
-    static constexpr int oV = oKT + K * LDT * 2;
-    static constexpr int oAn = oV + WS_T * LDC * 2;           // rows 16..63 of -A
-    static constexpr int oP = oAn + (WS_T - 16) * LDN * 2;
-    static constexpr int oTd = oP + WS_T * LDC * 2;
-    static constexpr int oBeta = oTd + WS_T * LDD * 2;
-    static constexpr int oEg = oBeta + WS_T * 4;               // e^{gamma_t}
-    static constexpr int oEgn = oEg + WS_T * 4;                // e^{gamma_n - gamma_t}
-    static constexpr int oEgN = oEgn + WS_T * 4;               // e^{gamma_n}
-    static constexpr int BUF = al(oEgN + 16);
+    static constexpr int RB = K * 2;              // bytes per q/k row
+    static constexpr int CPR = RB / 16;           // 16-byte chunks per q/k row
+    static constexpr int TILE = WS_T * RB;        // one q or k tile
+    static constexpr int VRB = WS_VB * 2;         // bytes per v row (8 chunks)
+    static constexpr int VTILE = WS_T * VRB;
+    static constexpr int PAD = 8;                 // bf16 elements = 16 bytes
+    static constexpr int LDC = WS_T + PAD;        // rows of -A and P (fragment order)
+    static constexpr int LDD = 16;                // rows of T_ii
+    // q/k: a ring of three stages (k at +0, q at +TILE); v: a ring of two
+    static constexpr int oKQ = 0;
+    static constexpr int oV = oKQ + 3 * 2 * TILE;
+    static constexpr int oD = oV + 2 * VTILE;
+    // derived buffer (two of them): what the prep waves compute for one chunk
+    static constexpr int dAn = 0;                           // [48][LDC] rows 16..63 of -A
+    static constexpr int dP = dAn + (WS_T - 16) * LDC * 2;  // [64][LDC] P
+    static constexpr int dTd = dP + WS_T * LDC * 2;         // [64][16] T_ii
+    static constexpr int dBeta = dTd + WS_T * LDD * 2;      // beta_t
+    static constexpr int dBeg = dBeta + WS_T * 4;           // beta_t e^{gamma_t}
+    static constexpr int dEg = dBeg + WS_T * 4;             // e^{gamma_t}
+    static constexpr int dEgn = dEg + WS_T * 4;             // e^{gamma_n - gamma_t}
+    static constexpr int dEgN = dEgn + WS_T * 4;            // e^{gamma_n}
+    static constexpr int DBUF = al(dEgN + 16);
     // prep-private tables of the chunk being prepared (see ws_gram_tile)
-    static constexpr int kGam = 2 * BUF;                       // gamma_t [64]
+    static constexpr int kGam = oD + 2 * DBUF;                 // gamma_t [64]
     static constexpr int kRowf = kGam + WS_T * 4;              // [3][64] e^{gamma_t - gamma_{16j+15}}
     static constexpr int kBrowf = kRowf + 3 * WS_T * 4;        // [3][64] beta_t * rowf
     static constexpr int kColf = kBrowf + 3 * WS_T * 4;        // [64] e^{gamma_{16b+15} - gamma_s}
-    static constexpr int kCtr = kColf + WS_T * 4;              // prep arrival counter
+    static constexpr int kAd = kColf + WS_T * 4;               // [4][16][16] fp32 -A of diagonal blocks
+    static constexpr int kGB = kAd + 4 * 16 * 16 * 4;          // [2][2][64] g and beta of a chunk
+    static constexpr int kCtr = kGB + 2 * 2 * WS_T * 4;        // prep arrival counter
     static constexpr int bytes = al(kCtr + 16);
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-// Chunk swizzles (in 16-byte chunks): q/k row t has K/8 chunks; k^T row c has 8.
-template <int K> __device__ __forceinline__ int qk_swz(int t) { return t & (K / 8 - 1); }
-__device__ __forceinline__ int kt_swz(int c) { return ((c >> 1) ^ (c >> 4)) & 7; }
+// Byte offset of the 16-byte chunk `ch` of q/k row `row` (rows of CPR chunks,
+// chunk index XOR-swizzled by the row).
+template <int CPR> __device__ __forceinline__ int qk_off(int row, int ch) {
+    return row * CPR * 16 + ((ch ^ (row & (CPR - 1))) << 4);
+}
+// Byte offset of the 16-byte chunk `ch` of v row `row` (8 chunks per row).
+__device__ __forceinline__ int v_off(int row, int ch) { return row * 128 + ((ch ^ (row & 7)) << 4); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// gfx950 transposing LDS read: inside each 16-lane group, lane 4a+b receives
+// element b of the 8-byte pieces addressed by lanes a, 4+a, 8+a and 12+a.
+// `addr` is an LDS byte address; a constant added to it folds into the
+// instruction's offset field.
+__device__ __forceinline__ bf16x4 lds_read_tr(unsigned addr) {
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(uintptr_t)addr);
+    return __builtin_bit_cast(bf16x4, r);
+}
+// 32-bit LDS address of a pointer into shared memory.
+__device__ __forceinline__ unsigned lds_u32(const char *p) {
+    return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char *)p;
+}
+// Keeps the compiler from merging constant offsets into x (so that they stay
+// foldable into the LDS instructions that use x).
+__device__ __forceinline__ unsigned opaque(unsigned x) {
+    asm("" : "+v"(x));
+    return x;
+}
+
+// q/k fragment: rows row0 + r16, keys 32 kb + 8 gq .. +7 (one 16-byte read).
+template <int CPR> __device__ __forceinline__ Frag<__bf16> qk_frag(const char *M, int row0, int kb) {
+    return {*reinterpret_cast<const bf16x8 *>(M + qk_off<CPR>(row0 + lane_r16(), 4 * kb + lane_gq()))};
+}
+
+// Copies from global memory straight into LDS (global_load_lds): lane l of
+// the wave writes its 16 (or 4) bytes from `src` (per lane) at lds + 16 l (or
+// + 4 l); `lds` is wave-uniform and goes through M0.  Written as inline asm so
+// that the compiler's own wait-count tracking, which would otherwise wait for
+// every copy in flight before any LDS access, leaves them alone: the kernel
+// waits for them explicitly (wait_vm) before their data is read.  They have no
+// register results.
+__device__ __forceinline__ unsigned lds_addr(const char *lds) {
+    return (unsigned)__builtin_amdgcn_readfirstlane(
+        (int)(uintptr_t)(__attribute__((address_space(3))) const char *)lds);
+}
+__device__ __forceinline__ void g2lds16(const void *src, char *lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 ::"v"(src), "s"(lds_addr(lds)) : "memory", "m0");
+}
+__device__ __forceinline__ void g2lds4(const void *src, char *lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 ::"v"(src), "s"(lds_addr(lds)) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (they complete in issue order).
+template <int N> __device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Barrier among the four prep waves: each wave adds one arrival to an LDS
 // counter and waits until the counter reaches `target` (4 per use).  All four
@@ -86,27 +151,62 @@ __device__ __forceinline__ void prep_barrier(unsigned *ctr, unsigned target) {
     asm volatile("" ::: "memory");
 }
 
+// Broadcast lane Q of each group of four lanes to the group (DPP quad_perm).
+template <int Q> __device__ __forceinline__ float quad_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), Q * 0x55, 0xf, 0xf, false));
+}
+
+// Rows of T = (I + A)^{-1} for a strictly lower 16 x 16 block A, given -A
+// row-major in LDS.  Lane 4j + p returns T[j][4p .. 4p+3].  Row j of T solves
+// (I + A^T) y = e_j, upper triangular: once y_s is final (s from 15 down), every
+// y_r with r < s takes -A[s][r] y_s.  The coefficients of a step are the same
+// for every row j, so each lane reads them with one broadcast 16-byte read, and
+// y_s comes from the lane of its quad that holds it.
+__device__ __forceinline__ f32x4 unit_lower_inverse16_rows(const float *negA) {
+    const int lane = threadIdx.x & 63, j = lane >> 2, p = lane & 3;
+    // all coefficient rows first, so the 15 dependent steps do not each wait
+    // for an LDS round trip
+    f32x4 c[16];
+#pragma unroll
+    for (int s = 1; s < 16; ++s) c[s] = *reinterpret_cast<const f32x4 *>(negA + s * 16 + 4 * p);
+    asm volatile("" ::: "memory");
+    f32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = (4 * p + e == j) ? 1.f : 0.f;
+#define GDN_ROWINV_STEP(s)                                                          \
+    {                                                                               \
+        const float ys = quad_bcast<(s) / 4>(y[(s) % 4]);                           \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf(ys, c[s][e], y[e]); \
+    }
+    GDN_ROWINV_STEP(15) GDN_ROWINV_STEP(14) GDN_ROWINV_STEP(13) GDN_ROWINV_STEP(12)
+    GDN_ROWINV_STEP(11) GDN_ROWINV_STEP(10) GDN_ROWINV_STEP(9) GDN_ROWINV_STEP(8)
+    GDN_ROWINV_STEP(7) GDN_ROWINV_STEP(6) GDN_ROWINV_STEP(5) GDN_ROWINV_STEP(4)
+    GDN_ROWINV_STEP(3) GDN_ROWINV_STEP(2) GDN_ROWINV_STEP(1)
+#undef GDN_ROWINV_STEP
+    return y;
+}
+
 // One Gram tile pair of the chunk: rows s of block J against columns t of block
 // I (J <= I), computed transposed (k_s . k_t and k_s . q_t) so that each lane
 // ends with four consecutive columns s of one row t of A and P and writes them
-// as one 8-byte piece.  bK/bQ hold the B fragments of k and q rows of block I.
+// as one 8-byte piece in fragment order.  bK/bQ hold the B fragments of the k
+// and q rows of block I.
 //   off-diagonal (J < I): the decay e^{gamma_t - gamma_s} is the product of
 //     the two table factors e^{gamma_t - gamma_r} (row) and e^{gamma_r - gamma_s}
 //     (column), r the last token of block J; both are <= 1, so no overflow.
-//   diagonal (J == I): masked, with one exponential per element; returns the
-//     tile of A^T in the accumulator layout (for the diagonal inverse).
-template <int I, int J, int NKB, int LDK, int LDC, int LDN>
+//   diagonal (J == I): masked, with one exponential per element; returns A's
+//     tile (lane (gq, r16) holds A[t][s0 .. s0+3]).
+template <int I, int J, int NKB, int CPR, int LDC>
 __device__ __forceinline__ f32x4 ws_gram_tile(const Frag<__bf16> (&bK)[NKB], const Frag<__bf16> (&bQ)[NKB],
-                                              const __bf16 *sK, __bf16 *sAn, __bf16 *sP,
+                                              const char *sK, __bf16 *sAn, __bf16 *sP,
                                               const float *gam, const float *rowf, const float *browf,
                                               const float *colf, const float *beta)
 {
     const int gq = lane_gq(), r16 = lane_r16();
     f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
-    static_assert(LDK % 64 == 0, "q/k rows are unpadded");
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-        const Frag<__bf16> fa = lds_frag_fos(sK, LDK, 16 * J, 32 * kb, qk_swz<LDK>(16 * J + r16));
+        const Frag<__bf16> fa = qk_frag<CPR>(sK, 16 * J, kb);
         aA = mma(aA, fa, bK[kb]);
         aP = mma(aP, fa, bQ[kb]);
     }
@@ -116,7 +216,7 @@ __device__ __forceinline__ f32x4 ws_gram_tile(const Frag<__bf16> (&bK)[NKB], con
         const f32x4 cf = *reinterpret_cast<const f32x4 *>(colf + s0);
         const f32x4 a = aA * cf * browf[J * WS_T + t];
         const f32x4 p = aP * cf * rowf[J * WS_T + t];
-        *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * LDN + frag_col(s0)) = cvt4(-a);
+        *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * LDC + frag_col(s0)) = cvt4(-a);
         *reinterpret_cast<bf16x4 *>(sP + t * LDC + frag_col(s0)) = cvt4(p);
         return f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
@@ -138,9 +238,9 @@ __device__ __forceinline__ f32x4 ws_gram_tile(const Frag<__bf16> (&bK)[NKB], con
 // Gram work of prep wave PW (rows grouped so B fragments are loaded once per
 // row, one diagonal tile each):
 //   PW0: (3,0) (3,1) (0,0)   PW1: (3,2) (3,3)   PW2: (2,0) (2,1) (2,2)   PW3: (1,0) (1,1)
-// Returns A_dd^T of its diagonal tile d in the accumulator layout.
-template <int PW, int NKB, int LDK, int LDC, int LDN>
-__device__ __forceinline__ f32x4 ws_gram_wave(const __bf16 *sK, const __bf16 *sQ, __bf16 *sAn,
+// Returns A of its diagonal tile d (see ws_gram_tile).
+template <int PW, int NKB, int CPR, int LDC>
+__device__ __forceinline__ f32x4 ws_gram_wave(const char *sK, const char *sQ, __bf16 *sAn,
                                               __bf16 *sP, const float *gam, const float *rowf,
                                               const float *browf, const float *colf,
                                               const float *beta, int &diag)
@@ -149,11 +249,11 @@ __device__ __forceinline__ f32x4 ws_gram_wave(const __bf16 *sK, const __bf16 *sQ
     auto row = [&](int i) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            bK[kb] = lds_frag_fos(sK, LDK, 16 * i, 32 * kb, qk_swz<LDK>(16 * i + lane_r16()));
-            bQ[kb] = lds_frag_fos(sQ, LDK, 16 * i, 32 * kb, qk_swz<LDK>(16 * i + lane_r16()));
+            bK[kb] = qk_frag<CPR>(sK, 16 * i, kb);
+            bQ[kb] = qk_frag<CPR>(sQ, 16 * i, kb);
         }
     };
-#define GDN_TILE(I, J) ws_gram_tile<I, J, NKB, LDK, LDC, LDN>(bK, bQ, sK, sAn, sP, gam, rowf, browf, colf, beta)
+#define GDN_TILE(I, J) ws_gram_tile<I, J, NKB, CPR, LDC>(bK, bQ, sK, sAn, sP, gam, rowf, browf, colf, beta)
     if constexpr (PW == 0) {
         row(3); GDN_TILE(3, 0); GDN_TILE(3, 1);
         row(0); diag = 0; return GDN_TILE(0, 0);
@@ -184,14 +284,11 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
 {
     using L = WsSmem<K>;
     constexpr int NT = K / 16;          // 16-row tiles of S
-    constexpr int NKB = K / 32;         // 32-wide k blocks over the key dim
-    constexpr int EPV = 8;              // bf16 per 16-byte vector
-    constexpr int CG = K / EPV;         // vectors per q/k row
-    constexpr int RG = 256 / CG;        // row groups over the 256 prep threads
-    constexpr int RPT = WS_T / RG;      // rows per prep thread
-    constexpr int NVV = WS_T * (WS_VB / EPV) / 256;   // v vectors per prep thread
-    using pack_t = typename Pack<__bf16, RPT>::type;
-    static_assert(RPT * RG == WS_T, "layout");
+    constexpr int NKB = K / 32;         // 32-key blocks
+    constexpr int CPR = L::CPR;
+    constexpr int RPI = 64 / CPR;       // q/k rows per 1 KB copy instruction
+    constexpr int NQK = 16 / RPI;       // copy instructions per wave for its 16 rows of q (or k)
+    constexpr int NVL = 2;              // v copy instructions per wave (16 rows of 8 chunks)
 
     extern __shared__ __attribute__((aligned(256))) char smem[];
     const int tid = threadIdx.x;
@@ -218,125 +315,121 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
     const long row_base = (long)b * T * H + h;   // row of token 0 in [B*T*H]
     const int nchunks = (T + WS_T - 1) / WS_T;
 
-    auto buf = [&](int c) { return smem + (c & 1) * L::BUF; };
+    auto kq_stage = [&](int c) { return smem + L::oKQ + (c % 3) * 2 * L::TILE; };
+    auto v_stage = [&](int c) { return smem + L::oV + (c & 1) * L::VTILE; };
+    auto dbuf = [&](int c) { return smem + L::oD + (c & 1) * L::DBUF; };
     unsigned *ctr = reinterpret_cast<unsigned *>(smem + L::kCtr);
     if (tid == 0) *ctr = 0u;
     lds_barrier();
 
     if (wave >= 4) {
         // ============================ prep waves ============================
-        const int ptid = tid - 256;
         const int pw = __builtin_amdgcn_readfirstlane(wave - 4);   // wave-uniform
-        const int cg = ptid % CG, rg = ptid / CG;
         float *gam = reinterpret_cast<float *>(smem + L::kGam);
         float *rowf = reinterpret_cast<float *>(smem + L::kRowf);
         float *browf = reinterpret_cast<float *>(smem + L::kBrowf);
         float *colf = reinterpret_cast<float *>(smem + L::kColf);
-        f32x4 pk[RPT], pq[RPT], pv[NVV];
-        float pb = 0.f, pg = 0.f;
-        // Full chunks: uniform chunk base pointers plus 32-bit per-lane offsets
-        // (a chunk spans 64 token rows, well inside 2^31 elements).
-        int koff[RPT], voff[NVV];
+        float *sAd = reinterpret_cast<float *>(smem + L::kAd) + pw * 256;
+
+        // This wave copies rows [16 pw, 16 pw + 16) of q, k and v of a chunk.
+        // Lane l of copy instruction i fills LDS row rq = 16 pw + i RPI + l / CPR,
+        // slot l % CPR, with logical chunk slot ^ (rq & (CPR-1)) of that row.
+        int qk_src[NQK], v_src[NVL];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) koff[i] = (RPT * rg + i) * H * K + cg * EPV;
-#pragma unroll
-        for (int j = 0; j < NVV; ++j) {
-            const int idx = ptid + 256 * j;
-            voff[j] = (idx / (WS_VB / EPV)) * H * V + (idx % (WS_VB / EPV)) * EPV;
+        for (int i = 0; i < NQK; ++i) {
+            const int rq = 16 * pw + i * RPI + lane / CPR, slot = lane % CPR;
+            qk_src[i] = rq * H * K + 8 * (slot ^ (rq & (CPR - 1)));
         }
-        const int goff = ptid * H;
-        auto load = [&](int t0) {
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int rv = 16 * pw + i * 8 + lane / 8, slot = lane % 8;
+            v_src[i] = rv * H * V + 8 * (slot ^ (rv & 7));
+        }
+        // q and k of chunk n into its stage.  Rows past T repeat row T-1 (their
+        // beta and g are zero, so they never contribute); n = nchunks copies
+        // only such rows into a free stage, which keeps the wait counts fixed.
+        auto copy_qk = [&](int n) {
+            char *st = kq_stage(n);
+            const int t0 = n * WS_T;
             if (t0 + WS_T <= T) {
-                const long tok = row_base + (long)t0 * H;   // row of the chunk's first token
+                const long tok = row_base + (long)t0 * H;
                 const __bf16 *kb = args.k + tok * K, *qb = args.q + tok * K;
-                const __bf16 *vb = args.v + tok * V + v0;
 #pragma unroll
-                for (int i = 0; i < RPT; ++i) {
-                    pk[i] = *reinterpret_cast<const f32x4 *>(kb + koff[i]);
-                    pq[i] = *reinterpret_cast<const f32x4 *>(qb + koff[i]);
+                for (int i = 0; i < NQK; ++i) g2lds16(kb + qk_src[i], st + (16 * pw + i * RPI) * L::RB);
+#pragma unroll
+                for (int i = 0; i < NQK; ++i) g2lds16(qb + qk_src[i], st + L::TILE + (16 * pw + i * RPI) * L::RB);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NQK; ++i) {
+                    const int rq = 16 * pw + i * RPI + lane / CPR, slot = lane % CPR;
+                    const int t = min(t0 + rq, T - 1);
+                    const long off = (row_base + (long)t * H) * K + 8 * (slot ^ (rq & (CPR - 1)));
+                    g2lds16(args.k + off, st + (16 * pw + i * RPI) * L::RB);
                 }
 #pragma unroll
-                for (int j = 0; j < NVV; ++j) pv[j] = *reinterpret_cast<const f32x4 *>(vb + voff[j]);
-                if (ptid < WS_T) {
-                    pg = args.g[tok + goff];
-                    pb = args.beta[tok + goff];
+                for (int i = 0; i < NQK; ++i) {
+                    const int rq = 16 * pw + i * RPI + lane / CPR, slot = lane % CPR;
+                    const int t = min(t0 + rq, T - 1);
+                    const long off = (row_base + (long)t * H) * K + 8 * (slot ^ (rq & (CPR - 1)));
+                    g2lds16(args.q + off, st + L::TILE + (16 * pw + i * RPI) * L::RB);
                 }
-                return;
             }
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const int t = t0 + RPT * rg + i;
-                f32x4 zk = {0.f, 0.f, 0.f, 0.f}, zq = zk;
-                if (t < T) {
-                    const long off = (row_base + (long)t * H) * K + cg * EPV;
-                    zk = *reinterpret_cast<const f32x4 *>(args.k + off);
-                    zq = *reinterpret_cast<const f32x4 *>(args.q + off);
-                }
-                pk[i] = zk;
-                pq[i] = zq;
-            }
-#pragma unroll
-            for (int j = 0; j < NVV; ++j) {
-                const int idx = ptid + 256 * j, row = idx / (WS_VB / EPV), cv = idx % (WS_VB / EPV);
-                const int t = t0 + row;
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                if (t < T)
-                    z = *reinterpret_cast<const f32x4 *>(args.v + (row_base + (long)t * H) * V + v0 + cv * EPV);
-                pv[j] = z;
-            }
-            const bool ok = ptid < WS_T && t0 + ptid < T;
-            pg = ok ? args.g[row_base + (long)(t0 + ptid) * H] : 0.f;
-            pb = ok ? args.beta[row_base + (long)(t0 + ptid) * H] : 0.f;
         };
+        auto copy_v = [&](int n) {
+            char *st = v_stage(n);
+            const int t0 = n * WS_T;
+            if (t0 + WS_T <= T) {
+                const __bf16 *vbase = args.v + (row_base + (long)t0 * H) * V + v0;
+#pragma unroll
+                for (int i = 0; i < NVL; ++i) g2lds16(vbase + v_src[i], st + (16 * pw + i * 8) * L::VRB);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NVL; ++i) {
+                    const int rv = 16 * pw + i * 8 + lane / 8, slot = lane % 8;
+                    const int t = min(t0 + rv, T - 1);
+                    const long off = (row_base + (long)t * H) * V + v0 + 8 * (slot ^ (rv & 7));
+                    g2lds16(args.v + off, st + (16 * pw + i * 8) * L::VRB);
+                }
+            }
+        };
+        // g and beta of chunk n into LDS (prep wave 0, lane = token), from a
+        // clamped row; the scan zeroes tokens past T.
+        auto copy_gb = [&](int n) {
+            char *st = smem + L::kGB + (n & 1) * 2 * WS_T * 4;
+            const long r = row_base + (long)min(n * WS_T + lane, T - 1) * H;
+            g2lds4(args.g + r, st);
+            g2lds4(args.beta + r, st + WS_T * 4);
+        };
+
         unsigned arrivals = 0;
-        // Stage the registers (chunk n) into buffer n&1, load chunk n+1, then
-        // compute the Gram blocks and diagonal inverses of chunk n.
+        // Chunk n: copy v(n) and q/k(n+1), scan g(n), then (once q/k(n) have
+        // landed in every prep wave) the Gram blocks and diagonal inverses.
         auto prepare = [&](int n) {
-            char *B = buf(n);
-            __bf16 *sK = reinterpret_cast<__bf16 *>(B + L::oK);
-            __bf16 *sQ = reinterpret_cast<__bf16 *>(B + L::oQ);
-            __bf16 *sKT = reinterpret_cast<__bf16 *>(B + L::oKT);
-            __bf16 *sV = reinterpret_cast<__bf16 *>(B + L::oV);
-            __bf16 *sAn = reinterpret_cast<__bf16 *>(B + L::oAn);
-            __bf16 *sP = reinterpret_cast<__bf16 *>(B + L::oP);
-            __bf16 *sTd = reinterpret_cast<__bf16 *>(B + L::oTd);
-            float *sBeta = reinterpret_cast<float *>(B + L::oBeta);
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                // 8 logical columns = two groups of 4 in fragment order
-                const int row = RPT * rg + i, sw = qk_swz<K>(row) << 3;
-                __bf16 *kr = sK + row * L::LDK, *qr = sQ + row * L::LDK;
-                const int c0 = frag_col(cg * EPV) ^ sw, c1 = frag_col(cg * EPV + 4) ^ sw;
-                *reinterpret_cast<f32x2 *>(kr + c0) = f32x2{pk[i][0], pk[i][1]};
-                *reinterpret_cast<f32x2 *>(kr + c1) = f32x2{pk[i][2], pk[i][3]};
-                *reinterpret_cast<f32x2 *>(qr + c0) = f32x2{pq[i][0], pq[i][1]};
-                *reinterpret_cast<f32x2 *>(qr + c1) = f32x2{pq[i][2], pq[i][3]};
-            }
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                const int ch = cg * EPV + e;
-                pack_t pt;
-#pragma unroll
-                for (int i = 0; i < RPT; ++i) pt[i] = reinterpret_cast<const __bf16 *>(&pk[i])[e];
-                *reinterpret_cast<pack_t *>(sKT + ch * L::LDT + (frag_col(RPT * rg) ^ (kt_swz(ch) << 3))) = pt;
-            }
-#pragma unroll
-            for (int j = 0; j < NVV; ++j) {
-                const int idx = ptid + 256 * j, row = idx / (WS_VB / EPV), cv = idx % (WS_VB / EPV);
-                *reinterpret_cast<f32x4 *>(sV + row * L::LDC + cv * EPV) = pv[j];
-            }
+            char *D = dbuf(n);
+            __bf16 *sAn = reinterpret_cast<__bf16 *>(D + L::dAn);
+            __bf16 *sP = reinterpret_cast<__bf16 *>(D + L::dP);
+            __bf16 *sTd = reinterpret_cast<__bf16 *>(D + L::dTd);
+            float *sBeta = reinterpret_cast<float *>(D + L::dBeta);
+            copy_v(n);
+            copy_qk(n + 1);
             if (pw == 0) {
+                wait_vm<NVL + 2 * NQK>();           // q/k(n), g/beta(n) landed (v(n), q/k(n+1) may fly)
                 // running sum of g over the chunk (lane = token), its decays, and
                 // the factor tables of the Gram tiles (block ends r_j = gamma_{16j+15})
+                const float *gb = reinterpret_cast<const float *>(smem + L::kGB + (n & 1) * 2 * WS_T * 4);
+                const bool live = n * WS_T + lane < T;
+                const float pg = live ? gb[lane] : 0.f, pb = live ? gb[WS_T + lane] : 0.f;
                 const float x = wave_inclusive_sum(pg);
                 const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
                 const float e0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
                 const float e1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
                 const float e2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+                const float eg = __expf(x);
                 gam[lane] = x;
-                reinterpret_cast<float *>(B + L::oEg)[lane] = __expf(x);
-                reinterpret_cast<float *>(B + L::oEgn)[lane] = __expf(gn - x);
-                if (lane == 0) reinterpret_cast<float *>(B + L::oEgN)[0] = __expf(gn);
+                reinterpret_cast<float *>(D + L::dEg)[lane] = eg;
+                reinterpret_cast<float *>(D + L::dBeg)[lane] = pb * eg;
+                reinterpret_cast<float *>(D + L::dEgn)[lane] = __expf(gn - x);
+                if (lane == 0) reinterpret_cast<float *>(D + L::dEgN)[0] = __expf(gn);
                 sBeta[lane] = pb;
                 const float ends[3] = {e0, e1, e2};
 #pragma unroll
@@ -348,29 +441,40 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 const int blk = lane >> 4;
                 const float end = blk == 0 ? e0 : blk == 1 ? e1 : blk == 2 ? e2 : gn;
                 colf[lane] = __expf(end - x);
+                // the g/beta slot read above is rewritten two chunks later, after
+                // this wave's reads of it have completed (prep_barrier waits for them)
+                copy_gb(n + 1);
+            } else {
+                wait_vm<NVL + 2 * NQK>();           // q/k(n) landed (v(n), q/k(n+1) may fly)
             }
-            if (n + 1 < nchunks) load((n + 1) * WS_T);
             arrivals += 4;
             prep_barrier(ctr, arrivals);
 
             // Gram tiles and the diagonal inverse (static per-wave schedule)
+            const char *sK = kq_stage(n), *sQ = kq_stage(n) + L::TILE;
             int diag = 0;
-            f32x4 aT;
+            f32x4 a;
             if (pw == 0)
-                aT = ws_gram_wave<0, NKB, L::LDK, L::LDC, L::LDN>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
+                a = ws_gram_wave<0, NKB, CPR, L::LDC>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
             else if (pw == 1)
-                aT = ws_gram_wave<1, NKB, L::LDK, L::LDC, L::LDN>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
+                a = ws_gram_wave<1, NKB, CPR, L::LDC>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
             else if (pw == 2)
-                aT = ws_gram_wave<2, NKB, L::LDK, L::LDC, L::LDN>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
+                a = ws_gram_wave<2, NKB, CPR, L::LDC>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
             else
-                aT = ws_gram_wave<3, NKB, L::LDK, L::LDC, L::LDN>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
-            // T_dd^T = (I + A_dd^T)^{-1}: lane (gq, j) gets T_dd[j][4gq .. 4gq+3]
-            const f32x4 tT = unit_upper_inverse16(aT);
-            *reinterpret_cast<bf16x4 *>(sTd + (16 * diag + r16) * L::LDD + 4 * gq) = cvt4(tT);
+                a = ws_gram_wave<3, NKB, CPR, L::LDC>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
+            // -A_dd row-major (lane (gq, r16) holds row r16, columns 4gq..4gq+3);
+            // the same wave reads it back, in order, for the row-wise inverse.
+            *reinterpret_cast<f32x4 *>(sAd + r16 * 16 + 4 * gq) = -a;
+            const f32x4 tr = unit_lower_inverse16_rows(sAd);
+            *reinterpret_cast<bf16x4 *>(sTd + (16 * diag + (lane >> 2)) * L::LDD + 4 * (lane & 3)) = cvt4(tr);
+            // v(n) landed before the hand-over barrier
+            if (pw == 0) wait_vm<2 * NQK + 2>();
+            else wait_vm<2 * NQK>();
         };
 
         if (nchunks > 0) {
-            load(0);
+            copy_qk(0);
+            if (pw == 0) copy_gb(0);
             prepare(0);
             lds_barrier();
         }
@@ -378,11 +482,15 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
             if (c + 1 < nchunks) prepare(c + 1);
             lds_barrier();
         }
+        wait_vm<0>();   // no copy may still be in flight at exit
         return;
     }
 
     // ============================= chain waves =============================
+    // Accumulator tile ct = 2kb + hh, lane (gq, r16), element e holds S[key][col]
+    // with key = 32kb + 8gq + 4hh + e and col = v0 + 16 wave + r16.
     const int vcol = 16 * wave + r16;   // this lane's column inside the block
+    auto key_of = [&](int ct, int e) { return 32 * (ct >> 1) + 8 * gq + 4 * (ct & 1) + e; };
     f32x4 S_acc[NT];
     {
         const float *S0 = args.S0 ? args.S0 + (long)bh * K * V : nullptr;
@@ -390,25 +498,38 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
         for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                S_acc[ct][e] = S0 ? S0[(16 * ct + 4 * gq + e) * V + v0 + vcol] : 0.f;
+                S_acc[ct][e] = S0 ? S0[key_of(ct, e) * V + v0 + vcol] : 0.f;
     }
     if (nchunks > 0) lds_barrier();     // chunk 0 is ready
 
+    // Transposing reads: lane (gq, j) addresses row 4gq + j/4 of a 16-row slab
+    // and the 8-byte piece j % 4 of the four it covers (keys for k^T, value
+    // columns 16 wave .. +15 for v).
+    // Per-lane LDS byte offsets that do not change from chunk to chunk: rows
+    // 16 apart differ by a constant (the swizzles depend on the row mod 16).
+    const int trow = 4 * gq + (r16 >> 2), tq = r16 & 3;
+    const int v_tr = v_off(trow, 2 * wave + (tq >> 1)) + 8 * (tq & 1);    // + 2048 rt
+    int v_st[4];                                                         // + 2048 rt
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v_st[e] = v_off(4 * gq + e, 2 * wave + (r16 >> 3)) + 2 * (r16 & 7);
+    const int v_rd0 = v_off(lane, 2 * wave), v_rd1 = v_off(lane, 2 * wave + 1);
+    int k_tr[NKB];                         // + 8 hh + RB (32 kb2 + 16 s)
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) k_tr[kk] = qk_off<CPR>(trow, 4 * kk + tq);
     for (int c = 0; c < nchunks; ++c) {
-        char *B = buf(c);
-        const __bf16 *sK = reinterpret_cast<const __bf16 *>(B + L::oK);
-        const __bf16 *sQ = reinterpret_cast<const __bf16 *>(B + L::oQ);
-        const __bf16 *sKT = reinterpret_cast<const __bf16 *>(B + L::oKT);
-        __bf16 *sV = reinterpret_cast<__bf16 *>(B + L::oV);
-        const __bf16 *sAn = reinterpret_cast<const __bf16 *>(B + L::oAn);
-        const __bf16 *sP = reinterpret_cast<const __bf16 *>(B + L::oP);
-        const __bf16 *sTd = reinterpret_cast<const __bf16 *>(B + L::oTd);
-        const float *sBeta = reinterpret_cast<const float *>(B + L::oBeta);
-        const float *sEg = reinterpret_cast<const float *>(B + L::oEg);
-        const float *sEgn = reinterpret_cast<const float *>(B + L::oEgn);
-        const float egN = reinterpret_cast<const float *>(B + L::oEgN)[0];
+        const char *sK = kq_stage(c), *sQ = kq_stage(c) + L::TILE;
+        char *sV = v_stage(c);
+        const char *D = dbuf(c);
+        const __bf16 *sAn = reinterpret_cast<const __bf16 *>(D + L::dAn);
+        const __bf16 *sP = reinterpret_cast<const __bf16 *>(D + L::dP);
+        const __bf16 *sTd = reinterpret_cast<const __bf16 *>(D + L::dTd);
+        const float *sBeta = reinterpret_cast<const float *>(D + L::dBeta);
+        const float *sBeg = reinterpret_cast<const float *>(D + L::dBeg);
+        const float *sEg = reinterpret_cast<const float *>(D + L::dEg);
+        const float *sEgn = reinterpret_cast<const float *>(D + L::dEgn);
+        const float egN = reinterpret_cast<const float *>(D + L::dEgN)[0];
 
-        // K+ S and Q+ S
+        // K S and Q S (the e^{gamma} row factors are applied below)
         f32x4 KS[4], QS[4];
         {
             Frag<__bf16> Sb[NKB];
@@ -419,37 +540,37 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    const int sw = qk_swz<K>(16 * rt + r16);
-                    ak = mma(ak, lds_frag_fos(sK, L::LDK, 16 * rt, 32 * kb, sw), Sb[kb]);
-                    aq = mma(aq, lds_frag_fos(sQ, L::LDK, 16 * rt, 32 * kb, sw), Sb[kb]);
+                    ak = mma(ak, qk_frag<CPR>(sK, 16 * rt, kb), Sb[kb]);
+                    aq = mma(aq, qk_frag<CPR>(sQ, 16 * rt, kb), Sb[kb]);
                 }
-                const f32x4 eg = *reinterpret_cast<const f32x4 *>(sEg + 16 * rt + 4 * gq);
-                KS[rt] = ak * eg;
-                QS[rt] = aq * eg;
+                KS[rt] = ak;
+                QS[rt] = aq * *reinterpret_cast<const f32x4 *>(sEg + 16 * rt + 4 * gq);
             }
         }
-        // X = diag(beta) (V - K+ S)
+        // X = diag(beta) V - diag(beta e^{gamma}) K S, v read in accumulator layout
+        const unsigned vtr_addr = opaque(lds_u32(sV) + v_tr);
         f32x4 X[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
+            const bf16x4 vv = lds_read_tr(vtr_addr + 2048 * rt);
             const f32x4 bt = *reinterpret_cast<const f32x4 *>(sBeta + 16 * rt + 4 * gq);
+            const f32x4 be = *reinterpret_cast<const f32x4 *>(sBeg + 16 * rt + 4 * gq);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                X[rt][e] = bt[e] * ((float)sV[(16 * rt + 4 * gq + e) * L::LDC + vcol] - KS[rt][e]);
+            for (int e = 0; e < 4; ++e) X[rt][e] = __builtin_fmaf(-be[e], KS[rt][e], bt[e] * (float)vv[e]);
         }
         // (I + A) D = X by block forward substitution (sAn holds -A, rows from 16)
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 D[4];
-        D[0] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 0, 0), reg_frag<__bf16>(X[0], z));
-        f32x4 Y = mma_lo(X[1], lds_frag_fo_lo(sAn, L::LDN, 0, 0), reg_frag<__bf16>(D[0], z));
-        D[1] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 16, 0), reg_frag<__bf16>(Y, z));
-        const Frag<__bf16> Df0 = reg_frag<__bf16>(D[0], D[1]);
-        Y = mma(X[2], lds_frag_fo(sAn, L::LDN, 16, 0), Df0);
-        f32x4 Y3 = mma(X[3], lds_frag_fo(sAn, L::LDN, 32, 0), Df0);
-        D[2] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 32, 0), reg_frag<__bf16>(Y, z));
-        Y3 = mma_lo(Y3, lds_frag_fo_lo(sAn, L::LDN, 32, 32), reg_frag<__bf16>(D[2], z));
-        D[3] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 48, 0), reg_frag<__bf16>(Y3, z));
-        const Frag<__bf16> Df1 = reg_frag<__bf16>(D[2], D[3]);
+        f32x4 Dd[4];
+        Dd[0] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 0, 0), reg_frag<__bf16>(X[0], z));
+        f32x4 Y = mma_lo(X[1], lds_frag_fo_lo(sAn, L::LDC, 0, 0), reg_frag<__bf16>(Dd[0], z));
+        Dd[1] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 16, 0), reg_frag<__bf16>(Y, z));
+        const Frag<__bf16> Df0 = reg_frag<__bf16>(Dd[0], Dd[1]);
+        Y = mma(X[2], lds_frag_fo(sAn, L::LDC, 16, 0), Df0);
+        f32x4 Y3 = mma(X[3], lds_frag_fo(sAn, L::LDC, 32, 0), Df0);
+        Dd[2] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 32, 0), reg_frag<__bf16>(Y, z));
+        Y3 = mma_lo(Y3, lds_frag_fo_lo(sAn, L::LDC, 32, 32), reg_frag<__bf16>(Dd[2], z));
+        Dd[3] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 48, 0), reg_frag<__bf16>(Y3, z));
+        const Frag<__bf16> Df1 = reg_frag<__bf16>(Dd[2], Dd[3]);
 
         // O = Q+ S + P D
         f32x4 O[4];
@@ -465,14 +586,15 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    sV[(16 * rt + 4 * gq + e) * L::LDC + vcol] = (__bf16)O[rt][e];
+                    *reinterpret_cast<__bf16 *>(sV + v_st[e] + 2048 * rt) = (__bf16)O[rt][e];
             asm volatile("" ::: "memory");
             const int t = c * WS_T + lane;
             if (t < T) {
-                const f32x4 *src = reinterpret_cast<const f32x4 *>(sV + lane * L::LDC + 16 * wave);
+                const f32x4 o0 = *reinterpret_cast<const f32x4 *>(sV + v_rd0);
+                const f32x4 o1 = *reinterpret_cast<const f32x4 *>(sV + v_rd1);
                 f32x4 *dst = reinterpret_cast<f32x4 *>(args.o + (row_base + (long)t * H) * V + v0 + 16 * wave);
-                dst[0] = src[0];
-                dst[1] = src[1];
+                dst[0] = o0;
+                dst[1] = o1;
             }
         }
 
@@ -480,13 +602,21 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
         f32x4 Dt[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
-            Dt[rt] = D[rt] * *reinterpret_cast<const f32x4 *>(sEgn + 16 * rt + 4 * gq);
-        const Frag<__bf16> Ef0 = reg_frag<__bf16>(Dt[0], Dt[1]), Ef1 = reg_frag<__bf16>(Dt[2], Dt[3]);
+            Dt[rt] = Dd[rt] * *reinterpret_cast<const f32x4 *>(sEgn + 16 * rt + 4 * gq);
+        const Frag<__bf16> Ef[2] = {reg_frag<__bf16>(Dt[0], Dt[1]), reg_frag<__bf16>(Dt[2], Dt[3])};
+        unsigned ktr_addr[NKB];
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) ktr_addr[kk] = opaque(lds_u32(sK) + k_tr[kk]);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             S_acc[ct] *= egN;
-            S_acc[ct] = mma(S_acc[ct], lds_frag_fos(sKT, L::LDT, 16 * ct, 0, kt_swz(16 * ct + r16)), Ef0);
-            S_acc[ct] = mma(S_acc[ct], lds_frag_fos(sKT, L::LDT, 16 * ct, 32, kt_swz(16 * ct + r16)), Ef1);
+            const unsigned pk = ktr_addr[ct >> 1] + 8 * (ct & 1);
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                const bf16x4 lo = lds_read_tr(pk + L::RB * 32 * kb2);
+                const bf16x4 hi = lds_read_tr(pk + L::RB * (32 * kb2 + 16));
+                S_acc[ct] = mma(S_acc[ct], Frag<__bf16>{cat8(lo, hi)}, Ef[kb2]);
+            }
         }
         lds_barrier();
     }
@@ -496,7 +626,7 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ST[(16 * ct + 4 * gq + e) * V + v0 + vcol] = S_acc[ct][e];
+            for (int e = 0; e < 4; ++e) ST[key_of(ct, e) * V + v0 + vcol] = S_acc[ct][e];
     }
 }
 
