@@ -35,6 +35,9 @@
 
 namespace gdn {
 
+// Scheduling fence: the compiler moves no instruction across it.
+#define GDN_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 constexpr int WS_T = 64;       // tokens per chunk
 constexpr int WS_VB = 64;      // value columns per workgroup
 constexpr int WS_NTHR = 512;   // 4 chain waves + 4 prep waves
@@ -49,9 +52,11 @@ template <int K> struct WsSmem {
     static constexpr int PAD = 8;                 // bf16 elements = 16 bytes
     static constexpr int LDC = WS_T + PAD;        // rows of -A and P (fragment order)
     static constexpr int LDD = 16;                // rows of T_ii
-    // q/k: a ring of three stages (k at +0, q at +TILE); v: a ring of two
+    // q/k: a ring of three stages (k at +0, q at +TILE, then g and beta of the
+    // chunk, 64 floats each); v: a ring of two
+    static constexpr int STAGE = 2 * TILE + 2 * WS_T * 4;
     static constexpr int oKQ = 0;
-    static constexpr int oV = oKQ + 3 * 2 * TILE;
+    static constexpr int oV = oKQ + 3 * STAGE;
     static constexpr int oD = oV + 2 * VTILE;
     // derived buffer (two of them): what the prep waves compute for one chunk
     static constexpr int dAn = 0;                           // [48][LDC] rows 16..63 of -A
@@ -63,14 +68,11 @@ template <int K> struct WsSmem {
     static constexpr int dEgn = dEg + WS_T * 4;             // e^{gamma_n - gamma_t}
     static constexpr int dEgN = dEgn + WS_T * 4;            // e^{gamma_n}
     static constexpr int DBUF = al(dEgN + 16);
-    // prep-private tables of the chunk being prepared (see ws_gram_tile)
-    static constexpr int kGam = oD + 2 * DBUF;                 // gamma_t [64]
-    static constexpr int kRowf = kGam + WS_T * 4;              // [3][64] e^{gamma_t - gamma_{16j+15}}
-    static constexpr int kBrowf = kRowf + 3 * WS_T * 4;        // [3][64] beta_t * rowf
-    static constexpr int kColf = kBrowf + 3 * WS_T * 4;        // [64] e^{gamma_{16b+15} - gamma_s}
-    static constexpr int kAd = kColf + WS_T * 4;               // [4][16][16] fp32 -A of diagonal blocks
-    static constexpr int kGB = kAd + 4 * 16 * 16 * 4;          // [2][2][64] g and beta of a chunk
-    static constexpr int kCtr = kGB + 2 * 2 * WS_T * 4;        // prep arrival counter
+    // per prep wave: gamma_t and beta_t of the chunk it prepares, and -A of its
+    // diagonal block (fp32)
+    static constexpr int kPriv = oD + 2 * DBUF;                // [4][2][64] floats
+    static constexpr int kAd = kPriv + 4 * 2 * WS_T * 4;       // [4][16][16] floats
+    static constexpr int kCtr = kAd + 4 * 16 * 16 * 4;         // prep arrival counter
     static constexpr int bytes = al(kCtr + 16);
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
@@ -186,88 +188,113 @@ __device__ __forceinline__ f32x4 unit_lower_inverse16_rows(const float *negA) {
     return y;
 }
 
-// One Gram tile pair of the chunk: rows s of block J against columns t of block
-// I (J <= I), computed transposed (k_s . k_t and k_s . q_t) so that each lane
-// ends with four consecutive columns s of one row t of A and P and writes them
-// as one 8-byte piece in fragment order.  bK/bQ hold the B fragments of the k
-// and q rows of block I.
-//   off-diagonal (J < I): the decay e^{gamma_t - gamma_s} is the product of
-//     the two table factors e^{gamma_t - gamma_r} (row) and e^{gamma_r - gamma_s}
-//     (column), r the last token of block J; both are <= 1, so no overflow.
-//   diagonal (J == I): masked, with one exponential per element; returns A's
-//     tile (lane (gq, r16) holds A[t][s0 .. s0+3]).
-template <int I, int J, int NKB, int CPR, int LDC>
-__device__ __forceinline__ f32x4 ws_gram_tile(const Frag<__bf16> (&bK)[NKB], const Frag<__bf16> (&bQ)[NKB],
-                                              const char *sK, __bf16 *sAn, __bf16 *sP,
-                                              const float *gam, const float *rowf, const float *browf,
-                                              const float *colf, const float *beta)
+// Gram blocks of the chunk, 16 x 16 each: block (I, J), J <= I, holds rows t
+// of block I and columns s of block J of A (A_ts = beta_t k_t.k_s e^{gamma_t -
+// gamma_s}, s < t) and P (P_ts = q_t.k_s e^{gamma_t - gamma_s}, s <= t).  A
+// block is computed transposed (k_s . k_t and k_s . q_t: the A operand is k of
+// block J, the B operands k and q of block I), so that each lane ends with four
+// consecutive columns s of one row t and writes them as one 8-byte piece in
+// fragment order.
+template <int NKB>
+__device__ __forceinline__ void gram_mma(const Frag<__bf16> (&aJ)[NKB], const Frag<__bf16> (&kI)[NKB],
+                                         const Frag<__bf16> (&qI)[NKB], f32x4 &aA, f32x4 &aP)
 {
-    const int gq = lane_gq(), r16 = lane_r16();
-    f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
+    aA = f32x4{0.f, 0.f, 0.f, 0.f};
+    aP = aA;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-        const Frag<__bf16> fa = qk_frag<CPR>(sK, 16 * J, kb);
-        aA = mma(aA, fa, bK[kb]);
-        aP = mma(aP, fa, bQ[kb]);
-    }
-    const int t = 16 * I + r16;            // row of A and P held by this lane
-    const int s0 = 16 * J + 4 * gq;        // its four columns s0 .. s0+3
-    if constexpr (J < I) {
-        const f32x4 cf = *reinterpret_cast<const f32x4 *>(colf + s0);
-        const f32x4 a = aA * cf * browf[J * WS_T + t];
-        const f32x4 p = aP * cf * rowf[J * WS_T + t];
-        *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * LDC + frag_col(s0)) = cvt4(-a);
-        *reinterpret_cast<bf16x4 *>(sP + t * LDC + frag_col(s0)) = cvt4(p);
-        return f32x4{0.f, 0.f, 0.f, 0.f};
-    } else {
-        const float gt = gam[t], bt = beta[t];
-        const f32x4 gs = *reinterpret_cast<const f32x4 *>(gam + s0);
-        f32x4 a, p;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int s = s0 + e;
-            const float dec = (s <= t) ? __expf(gt - gs[e]) : 0.f;
-            a[e] = (s < t) ? bt * aA[e] * dec : 0.f;
-            p[e] = aP[e] * dec;
-        }
-        *reinterpret_cast<bf16x4 *>(sP + t * LDC + frag_col(s0)) = cvt4(p);
-        return a;
+        aA = mma(aA, aJ[kb], kI[kb]);
+        aP = mma(aP, aJ[kb], qI[kb]);
     }
 }
 
-// Gram work of prep wave PW (rows grouped so B fragments are loaded once per
-// row, one diagonal tile each):
-//   PW0: (3,0) (3,1) (0,0)   PW1: (3,2) (3,3)   PW2: (2,0) (2,1) (2,2)   PW3: (1,0) (1,1)
-// Returns A of its diagonal tile d (see ws_gram_tile).
-template <int PW, int NKB, int CPR, int LDC>
-__device__ __forceinline__ f32x4 ws_gram_wave(const char *sK, const char *sQ, __bf16 *sAn,
-                                              __bf16 *sP, const float *gam, const float *rowf,
-                                              const float *browf, const float *colf,
-                                              const float *beta, int &diag)
+// Off-diagonal block (J < I): the decay e^{gamma_t - gamma_s} is taken as
+// e^{gamma_t - gamma_r} e^{gamma_r - gamma_s} with r the last token of block J,
+// both factors <= 1.  gam/bet: this wave's gamma_t and beta_t; x: its scan
+// register (lane = token).  Writes -A and P.
+template <int I, int J, int LDC>
+__device__ __forceinline__ void gram_off(f32x4 aA, f32x4 aP, const float *gam, const float *bet,
+                                         float x, __bf16 *sAn, __bf16 *sP)
 {
-    Frag<__bf16> bK[NKB], bQ[NKB];
-    auto row = [&](int i) {
+    const int t = 16 * I + lane_r16(), s0 = 16 * J + 4 * lane_gq();
+    const float gr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * J + 15));
+    const float rf = __expf(gam[t] - gr);
+    const float brf = bet[t] * rf;
+    const f32x4 gs = *reinterpret_cast<const f32x4 *>(gam + s0);
+    f32x4 cf;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            bK[kb] = qk_frag<CPR>(sK, 16 * i, kb);
-            bQ[kb] = qk_frag<CPR>(sQ, 16 * i, kb);
-        }
-    };
-#define GDN_TILE(I, J) ws_gram_tile<I, J, NKB, CPR, LDC>(bK, bQ, sK, sAn, sP, gam, rowf, browf, colf, beta)
-    if constexpr (PW == 0) {
-        row(3); GDN_TILE(3, 0); GDN_TILE(3, 1);
-        row(0); diag = 0; return GDN_TILE(0, 0);
-    } else if constexpr (PW == 1) {
-        row(3); GDN_TILE(3, 2);
-        diag = 3; return GDN_TILE(3, 3);
-    } else if constexpr (PW == 2) {
-        row(2); GDN_TILE(2, 0); GDN_TILE(2, 1);
-        diag = 2; return GDN_TILE(2, 2);
-    } else {
-        row(1); GDN_TILE(1, 0);
-        diag = 1; return GDN_TILE(1, 1);
+    for (int e = 0; e < 4; ++e) cf[e] = __expf(gr - gs[e]);
+    *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * LDC + frag_col(s0)) = cvt4(aA * cf * -brf);
+    *reinterpret_cast<bf16x4 *>(sP + t * LDC + frag_col(s0)) = cvt4(aP * cf * rf);
+}
+
+// Diagonal block D: masked, one exponential per element.  Writes P and returns
+// A's block (lane (gq, r16) holds A[t][s0 .. s0+3]).
+template <int D, int LDC>
+__device__ __forceinline__ f32x4 gram_diag(f32x4 aA, f32x4 aP, const float *gam, const float *bet,
+                                           __bf16 *sP)
+{
+    const int t = 16 * D + lane_r16(), s0 = 16 * D + 4 * lane_gq();
+    const float gt = gam[t], bt = bet[t];
+    const f32x4 gs = *reinterpret_cast<const f32x4 *>(gam + s0);
+    f32x4 a, p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int s = s0 + e;
+        const float dec = (s <= t) ? __expf(gt - gs[e]) : 0.f;
+        a[e] = (s < t) ? bt * aA[e] * dec : 0.f;
+        p[e] = aP[e] * dec;
     }
-#undef GDN_TILE
+    *reinterpret_cast<bf16x4 *>(sP + t * LDC + frag_col(s0)) = cvt4(p);
+    return a;
+}
+
+// Gram work and diagonal inverse of prep wave PW.  Each wave owns one diagonal
+// block D and the off-diagonal blocks of one block row I:
+//   PW0: D=0, (3,0) (3,1)   PW1: D=3, (3,2)   PW2: D=2, (2,0) (2,1)   PW3: D=1, (1,0)
+// All fragments are read first; the diagonal block comes first because its
+// inverse is the longest dependent chain, and the off-diagonal products can
+// overlap it.  T_DD goes to sTd rows 16 D .. 16 D + 15.
+template <int PW, int NKB, int CPR, int LDC, int LDD>
+__device__ __forceinline__ void ws_gram_wave(const char *sK, const char *sQ, __bf16 *sAn, __bf16 *sP,
+                                             __bf16 *sTd, const float *gam, const float *bet,
+                                             float x, float *sAd)
+{
+    constexpr int D = PW == 0 ? 0 : PW == 1 ? 3 : PW == 2 ? 2 : 1;
+    constexpr int I = PW == 0 ? 3 : D;
+    constexpr int J0 = PW == 1 ? 2 : 0;
+    constexpr int NOFF = (PW == 1 || PW == 3) ? 1 : 2;
+    Frag<__bf16> kD[NKB], qD[NKB], kI[NKB], qI[NKB], kJ[2][NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        kD[kb] = qk_frag<CPR>(sK, 16 * D, kb);
+        qD[kb] = qk_frag<CPR>(sQ, 16 * D, kb);
+        if constexpr (I != D) {
+            kI[kb] = qk_frag<CPR>(sK, 16 * I, kb);
+            qI[kb] = qk_frag<CPR>(sQ, 16 * I, kb);
+        } else {
+            kI[kb] = kD[kb];
+            qI[kb] = qD[kb];
+        }
+#pragma unroll
+        for (int j = 0; j < NOFF; ++j)
+            kJ[j][kb] = (J0 + j == D) ? kD[kb] : qk_frag<CPR>(sK, 16 * (J0 + j), kb);
+    }
+    GDN_SCHED_FENCE();
+    f32x4 aA, aP;
+    gram_mma<NKB>(kD, kD, qD, aA, aP);
+    const f32x4 a = gram_diag<D, LDC>(aA, aP, gam, bet, sP);
+    // -A_DD row-major; the same wave reads it back, in order, for the inverse
+    *reinterpret_cast<f32x4 *>(sAd + lane_r16() * 16 + 4 * lane_gq()) = -a;
+    gram_mma<NKB>(kJ[0], kI, qI, aA, aP);
+    gram_off<I, J0, LDC>(aA, aP, gam, bet, x, sAn, sP);
+    if constexpr (NOFF == 2) {
+        gram_mma<NKB>(kJ[1], kI, qI, aA, aP);
+        gram_off<I, J0 + 1, LDC>(aA, aP, gam, bet, x, sAn, sP);
+    }
+    const f32x4 tr = unit_lower_inverse16_rows(sAd);
+    const int lane = threadIdx.x & 63;
+    *reinterpret_cast<bf16x4 *>(sTd + (16 * D + (lane >> 2)) * LDD + 4 * (lane & 3)) = cvt4(tr);
 }
 
 struct WsArgs {
@@ -315,7 +342,7 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
     const long row_base = (long)b * T * H + h;   // row of token 0 in [B*T*H]
     const int nchunks = (T + WS_T - 1) / WS_T;
 
-    auto kq_stage = [&](int c) { return smem + L::oKQ + (c % 3) * 2 * L::TILE; };
+    auto kq_stage = [&](int c) { return smem + L::oKQ + (c % 3) * L::STAGE; };
     auto v_stage = [&](int c) { return smem + L::oV + (c & 1) * L::VTILE; };
     auto dbuf = [&](int c) { return smem + L::oD + (c & 1) * L::DBUF; };
     unsigned *ctr = reinterpret_cast<unsigned *>(smem + L::kCtr);
@@ -325,10 +352,8 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
     if (wave >= 4) {
         // ============================ prep waves ============================
         const int pw = __builtin_amdgcn_readfirstlane(wave - 4);   // wave-uniform
-        float *gam = reinterpret_cast<float *>(smem + L::kGam);
-        float *rowf = reinterpret_cast<float *>(smem + L::kRowf);
-        float *browf = reinterpret_cast<float *>(smem + L::kBrowf);
-        float *colf = reinterpret_cast<float *>(smem + L::kColf);
+        float *gam = reinterpret_cast<float *>(smem + L::kPriv) + pw * 2 * WS_T;   // this wave's gamma_t
+        float *bet = gam + WS_T;                                                   // and beta_t
         float *sAd = reinterpret_cast<float *>(smem + L::kAd) + pw * 256;
 
         // This wave copies rows [16 pw, 16 pw + 16) of q, k and v of a chunk.
@@ -351,6 +376,13 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
         auto copy_qk = [&](int n) {
             char *st = kq_stage(n);
             const int t0 = n * WS_T;
+            if (pw == 0) {
+                // g and beta of the chunk (lane = token), from a clamped row; the
+                // scan zeroes tokens past T
+                const long r = row_base + (long)min(t0 + lane, T - 1) * H;
+                g2lds4(args.g + r, st + 2 * L::TILE);
+                g2lds4(args.beta + r, st + 2 * L::TILE + WS_T * 4);
+            }
             if (t0 + WS_T <= T) {
                 const long tok = row_base + (long)t0 * H;
                 const __bf16 *kb = args.k + tok * K, *qb = args.q + tok * K;
@@ -392,15 +424,6 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 }
             }
         };
-        // g and beta of chunk n into LDS (prep wave 0, lane = token), from a
-        // clamped row; the scan zeroes tokens past T.
-        auto copy_gb = [&](int n) {
-            char *st = smem + L::kGB + (n & 1) * 2 * WS_T * 4;
-            const long r = row_base + (long)min(n * WS_T + lane, T - 1) * H;
-            g2lds4(args.g + r, st);
-            g2lds4(args.beta + r, st + WS_T * 4);
-        };
-
         unsigned arrivals = 0;
         // Chunk n: copy v(n) and q/k(n+1), scan g(n), then (once q/k(n) have
         // landed in every prep wave) the Gram blocks and diagonal inverses.
@@ -409,64 +432,45 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
             __bf16 *sAn = reinterpret_cast<__bf16 *>(D + L::dAn);
             __bf16 *sP = reinterpret_cast<__bf16 *>(D + L::dP);
             __bf16 *sTd = reinterpret_cast<__bf16 *>(D + L::dTd);
-            float *sBeta = reinterpret_cast<float *>(D + L::dBeta);
             copy_v(n);
             copy_qk(n + 1);
-            if (pw == 0) {
-                wait_vm<NVL + 2 * NQK>();           // q/k(n), g/beta(n) landed (v(n), q/k(n+1) may fly)
-                // running sum of g over the chunk (lane = token), its decays, and
-                // the factor tables of the Gram tiles (block ends r_j = gamma_{16j+15})
-                const float *gb = reinterpret_cast<const float *>(smem + L::kGB + (n & 1) * 2 * WS_T * 4);
-                const bool live = n * WS_T + lane < T;
-                const float pg = live ? gb[lane] : 0.f, pb = live ? gb[WS_T + lane] : 0.f;
-                const float x = wave_inclusive_sum(pg);
-                const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-                const float e0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
-                const float e1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
-                const float e2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
-                const float eg = __expf(x);
-                gam[lane] = x;
-                reinterpret_cast<float *>(D + L::dEg)[lane] = eg;
-                reinterpret_cast<float *>(D + L::dBeg)[lane] = pb * eg;
-                reinterpret_cast<float *>(D + L::dEgn)[lane] = __expf(gn - x);
-                if (lane == 0) reinterpret_cast<float *>(D + L::dEgN)[0] = __expf(gn);
-                sBeta[lane] = pb;
-                const float ends[3] = {e0, e1, e2};
-#pragma unroll
-                for (int jb = 0; jb < 3; ++jb) {
-                    const float f = lane > 16 * jb + 15 ? __expf(x - ends[jb]) : 0.f;
-                    rowf[jb * WS_T + lane] = f;
-                    browf[jb * WS_T + lane] = pb * f;
-                }
-                const int blk = lane >> 4;
-                const float end = blk == 0 ? e0 : blk == 1 ? e1 : blk == 2 ? e2 : gn;
-                colf[lane] = __expf(end - x);
-                // the g/beta slot read above is rewritten two chunks later, after
-                // this wave's reads of it have completed (prep_barrier waits for them)
-                copy_gb(n + 1);
-            } else {
-                wait_vm<NVL + 2 * NQK>();           // q/k(n) landed (v(n), q/k(n+1) may fly)
-            }
+            // q/k(n) (and g/beta(n)) landed; v(n), q/k(n+1) (g/beta(n+1)) may fly
+            if (pw == 0) wait_vm<NVL + 2 * NQK + 2>();
+            else wait_vm<NVL + 2 * NQK>();
             arrivals += 4;
             prep_barrier(ctr, arrivals);
 
-            // Gram tiles and the diagonal inverse (static per-wave schedule)
-            const char *sK = kq_stage(n), *sQ = kq_stage(n) + L::TILE;
-            int diag = 0;
-            f32x4 a;
+            // every prep wave scans g itself (lane = token): its own gamma_t and
+            // beta_t for its Gram blocks; waves 1 and 3 also write the chain's
+            // per-token factors
+            const char *st = kq_stage(n);
+            const float *gb = reinterpret_cast<const float *>(st + 2 * L::TILE);
+            const bool live = n * WS_T + lane < T;
+            const float pg = live ? gb[lane] : 0.f, pb = live ? gb[WS_T + lane] : 0.f;
+            const float x = wave_inclusive_sum(pg);
+            gam[lane] = x;
+            bet[lane] = pb;
+            if (pw == 1) {
+                const float eg = __expf(x);
+                reinterpret_cast<float *>(D + L::dEg)[lane] = eg;
+                reinterpret_cast<float *>(D + L::dBeg)[lane] = pb * eg;
+                reinterpret_cast<float *>(D + L::dBeta)[lane] = pb;
+            } else if (pw == 3) {
+                const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+                reinterpret_cast<float *>(D + L::dEgn)[lane] = __expf(gn - x);
+                if (lane == 0) reinterpret_cast<float *>(D + L::dEgN)[0] = __expf(gn);
+            }
+
+            // Gram blocks and the diagonal inverse (static per-wave schedule)
+            const char *sK = st, *sQ = st + L::TILE;
             if (pw == 0)
-                a = ws_gram_wave<0, NKB, CPR, L::LDC>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
+                ws_gram_wave<0, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd);
             else if (pw == 1)
-                a = ws_gram_wave<1, NKB, CPR, L::LDC>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
+                ws_gram_wave<1, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd);
             else if (pw == 2)
-                a = ws_gram_wave<2, NKB, CPR, L::LDC>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
+                ws_gram_wave<2, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd);
             else
-                a = ws_gram_wave<3, NKB, CPR, L::LDC>(sK, sQ, sAn, sP, gam, rowf, browf, colf, sBeta, diag);
-            // -A_dd row-major (lane (gq, r16) holds row r16, columns 4gq..4gq+3);
-            // the same wave reads it back, in order, for the row-wise inverse.
-            *reinterpret_cast<f32x4 *>(sAd + r16 * 16 + 4 * gq) = -a;
-            const f32x4 tr = unit_lower_inverse16_rows(sAd);
-            *reinterpret_cast<bf16x4 *>(sTd + (16 * diag + (lane >> 2)) * L::LDD + 4 * (lane & 3)) = cvt4(tr);
+                ws_gram_wave<3, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd);
             // v(n) landed before the hand-over barrier
             if (pw == 0) wait_vm<2 * NQK + 2>();
             else wait_vm<2 * NQK>();
@@ -474,7 +478,6 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
 
         if (nchunks > 0) {
             copy_qk(0);
-            if (pw == 0) copy_gb(0);
             prepare(0);
             lds_barrier();
         }
@@ -529,59 +532,123 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
         const float *sEgn = reinterpret_cast<const float *>(D + L::dEgn);
         const float egN = reinterpret_cast<const float *>(D + L::dEgN)[0];
 
-        // K S and Q S (the e^{gamma} row factors are applied below)
-        f32x4 KS[4], QS[4];
-        {
-            Frag<__bf16> Sb[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) Sb[kb] = reg_frag<__bf16>(S_acc[2 * kb], S_acc[2 * kb + 1]);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    ak = mma(ak, qk_frag<CPR>(sK, 16 * rt, kb), Sb[kb]);
-                    aq = mma(aq, qk_frag<CPR>(sQ, 16 * rt, kb), Sb[kb]);
-                }
-                KS[rt] = ak;
-                QS[rt] = aq * *reinterpret_cast<const f32x4 *>(sEg + 16 * rt + 4 * gq);
-            }
-        }
-        // X = diag(beta) V - diag(beta e^{gamma}) K S, v read in accumulator layout
         const unsigned vtr_addr = opaque(lds_u32(sV) + v_tr);
+        unsigned ktr_addr[NKB];
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) ktr_addr[kk] = opaque(lds_u32(sK) + k_tr[kk]);
+
+        // The chunk runs in phases separated by scheduling fences; each phase
+        // issues the LDS reads of the next one, so that their latency hides
+        // behind matrix-core work instead of stalling this (single) wave.
+
+        // Phase A: K S and Q S, the q/k fragments read one row tile ahead.
+        Frag<__bf16> Sb[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) Sb[kb] = reg_frag<__bf16>(S_acc[2 * kb], S_acc[2 * kb + 1]);
+        Frag<__bf16> fk[4][NKB], fq[4][NKB];
+        auto load_rt = [&](int rt) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                fk[rt][kb] = qk_frag<CPR>(sK, 16 * rt, kb);
+                fq[rt][kb] = qk_frag<CPR>(sQ, 16 * rt, kb);
+            }
+        };
+        bf16x4 vv[4];
+        f32x4 bt[4], be[4], eg[4], egn[4];
+        Frag<__bf16> fT[4], fA10, fA2, fA3, fA32, fP0, fP1, fP2, fP2b, fP3, fP3b;
+        f32x4 KS[4], QS[4];
+        load_rt(0);
+        GDN_SCHED_FENCE();
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            if (rt + 1 < 4) load_rt(rt + 1);
+            if (rt == 1) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    vv[r] = lds_read_tr(vtr_addr + 2048 * r);
+                    bt[r] = *reinterpret_cast<const f32x4 *>(sBeta + 16 * r + 4 * gq);
+                    be[r] = *reinterpret_cast<const f32x4 *>(sBeg + 16 * r + 4 * gq);
+                }
+            } else if (rt == 2) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    eg[r] = *reinterpret_cast<const f32x4 *>(sEg + 16 * r + 4 * gq);
+                    fT[r] = lds_frag_lo(sTd, L::LDD, 16 * r, 0);
+                }
+                fA10 = lds_frag_fo_lo(sAn, L::LDC, 0, 0);
+                fA2 = lds_frag_fo(sAn, L::LDC, 16, 0);
+                fA3 = lds_frag_fo(sAn, L::LDC, 32, 0);
+                fA32 = lds_frag_fo_lo(sAn, L::LDC, 32, 32);
+            } else if (rt == 3) {
+                fP0 = lds_frag_fo_lo(sP, L::LDC, 0, 0);
+                fP1 = lds_frag_fo(sP, L::LDC, 16, 0);
+                fP2 = lds_frag_fo(sP, L::LDC, 32, 0);
+                fP2b = lds_frag_fo_lo(sP, L::LDC, 32, 32);
+                fP3 = lds_frag_fo(sP, L::LDC, 48, 0);
+                fP3b = lds_frag_fo(sP, L::LDC, 48, 32);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) egn[r] = *reinterpret_cast<const f32x4 *>(sEgn + 16 * r + 4 * gq);
+            }
+            f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                ak = mma(ak, fk[rt][kb], Sb[kb]);
+                aq = mma(aq, fq[rt][kb], Sb[kb]);
+            }
+            KS[rt] = ak;
+            QS[rt] = aq;
+            GDN_SCHED_FENCE();
+        }
+
+        // Phase B: X = diag(beta) V - diag(beta e^{gamma}) K S (v in accumulator
+        // layout), then (I + A) D = X by block forward substitution (-A stored).
         f32x4 X[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            const bf16x4 vv = lds_read_tr(vtr_addr + 2048 * rt);
-            const f32x4 bt = *reinterpret_cast<const f32x4 *>(sBeta + 16 * rt + 4 * gq);
-            const f32x4 be = *reinterpret_cast<const f32x4 *>(sBeg + 16 * rt + 4 * gq);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) X[rt][e] = __builtin_fmaf(-be[e], KS[rt][e], bt[e] * (float)vv[e]);
+            for (int e = 0; e < 4; ++e) X[rt][e] = __builtin_fmaf(-be[rt][e], KS[rt][e], bt[rt][e] * (float)vv[rt][e]);
+            QS[rt] *= eg[rt];
         }
-        // (I + A) D = X by block forward substitution (sAn holds -A, rows from 16)
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 Dd[4];
-        Dd[0] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 0, 0), reg_frag<__bf16>(X[0], z));
-        f32x4 Y = mma_lo(X[1], lds_frag_fo_lo(sAn, L::LDC, 0, 0), reg_frag<__bf16>(Dd[0], z));
-        Dd[1] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 16, 0), reg_frag<__bf16>(Y, z));
+        Dd[0] = mma_lo(z, fT[0], reg_frag<__bf16>(X[0], z));
+        f32x4 Y = mma_lo(X[1], fA10, reg_frag<__bf16>(Dd[0], z));
+        Dd[1] = mma_lo(z, fT[1], reg_frag<__bf16>(Y, z));
         const Frag<__bf16> Df0 = reg_frag<__bf16>(Dd[0], Dd[1]);
-        Y = mma(X[2], lds_frag_fo(sAn, L::LDC, 16, 0), Df0);
-        f32x4 Y3 = mma(X[3], lds_frag_fo(sAn, L::LDC, 32, 0), Df0);
-        Dd[2] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 32, 0), reg_frag<__bf16>(Y, z));
-        Y3 = mma_lo(Y3, lds_frag_fo_lo(sAn, L::LDC, 32, 32), reg_frag<__bf16>(Dd[2], z));
-        Dd[3] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 48, 0), reg_frag<__bf16>(Y3, z));
+        Y = mma(X[2], fA2, Df0);
+        f32x4 Y3 = mma(X[3], fA3, Df0);
+        Dd[2] = mma_lo(z, fT[2], reg_frag<__bf16>(Y, z));
+        Y3 = mma_lo(Y3, fA32, reg_frag<__bf16>(Dd[2], z));
+        Dd[3] = mma_lo(z, fT[3], reg_frag<__bf16>(Y3, z));
         const Frag<__bf16> Df1 = reg_frag<__bf16>(Dd[2], Dd[3]);
+        GDN_SCHED_FENCE();
 
-        // O = Q+ S + P D
+        // Phase C: O = Q+ S + P D, stored through this wave's own (consumed) v
+        // columns for row-wise 16-byte stores; the k^T reads of the state update
+        // start behind it.
+        bf16x4 kt[NT][4];
+        auto load_ct = [&](int ct) {
+            const unsigned pk = ktr_addr[ct >> 1] + 8 * (ct & 1);
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                kt[ct][2 * kb2] = lds_read_tr(pk + L::RB * 32 * kb2);
+                kt[ct][2 * kb2 + 1] = lds_read_tr(pk + L::RB * (32 * kb2 + 16));
+            }
+        };
+        load_ct(0);
+        load_ct(1);
         f32x4 O[4];
-        O[0] = mma_lo(QS[0], lds_frag_fo_lo(sP, L::LDC, 0, 0), Df0);
-        O[1] = mma(QS[1], lds_frag_fo(sP, L::LDC, 16, 0), Df0);
-        O[2] = mma(QS[2], lds_frag_fo(sP, L::LDC, 32, 0), Df0);
-        O[2] = mma_lo(O[2], lds_frag_fo_lo(sP, L::LDC, 32, 32), Df1);
-        O[3] = mma(QS[3], lds_frag_fo(sP, L::LDC, 48, 0), Df0);
-        O[3] = mma(O[3], lds_frag_fo(sP, L::LDC, 48, 32), Df1);
+        O[0] = mma_lo(QS[0], fP0, Df0);
+        O[1] = mma(QS[1], fP1, Df0);
+        O[2] = mma(QS[2], fP2, Df0);
+        O[2] = mma_lo(O[2], fP2b, Df1);
+        O[3] = mma(QS[3], fP3, Df0);
+        O[3] = mma(O[3], fP3b, Df1);
+        f32x4 Dt[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) Dt[rt] = Dd[rt] * egn[rt];
+        const Frag<__bf16> Ef[2] = {reg_frag<__bf16>(Dt[0], Dt[1]), reg_frag<__bf16>(Dt[2], Dt[3])};
         if (args.o) {
-            // through this wave's own v columns (already consumed) for row stores
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -597,26 +664,18 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 dst[1] = o1;
             }
         }
+        GDN_SCHED_FENCE();
 
-        // S' = e^{gamma_n} S + K^T (e^{gamma_n - gamma} D)
-        f32x4 Dt[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-            Dt[rt] = Dd[rt] * *reinterpret_cast<const f32x4 *>(sEgn + 16 * rt + 4 * gq);
-        const Frag<__bf16> Ef[2] = {reg_frag<__bf16>(Dt[0], Dt[1]), reg_frag<__bf16>(Dt[2], Dt[3])};
-        unsigned ktr_addr[NKB];
-#pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) ktr_addr[kk] = opaque(lds_u32(sK) + k_tr[kk]);
+        // Phase D: S' = e^{gamma_n} S + K^T (e^{gamma_n - gamma} D), the k^T
+        // fragments read two tiles ahead.
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
+            if (ct + 2 < NT) load_ct(ct + 2);
             S_acc[ct] *= egN;
-            const unsigned pk = ktr_addr[ct >> 1] + 8 * (ct & 1);
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-                const bf16x4 lo = lds_read_tr(pk + L::RB * 32 * kb2);
-                const bf16x4 hi = lds_read_tr(pk + L::RB * (32 * kb2 + 16));
-                S_acc[ct] = mma(S_acc[ct], Frag<__bf16>{cat8(lo, hi)}, Ef[kb2]);
-            }
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+                S_acc[ct] = mma(S_acc[ct], Frag<__bf16>{cat8(kt[ct][2 * kb2], kt[ct][2 * kb2 + 1])}, Ef[kb2]);
+            GDN_SCHED_FENCE();
         }
         lds_barrier();
     }
