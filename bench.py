@@ -8,7 +8,8 @@ fused recurrent decode step (256 sequences x 48 heads of 128x128 fp32 state, 64
 chained in-place steps) and reports its HBM bandwidth, and times the fp64 CPU
 oracle on a bounded sample of the prefill workload.
 
-Prints one JSON line.  Options: --gpus (1 only), --steps, --warmup,
+Prints one JSON line.  Options: --gpus (1 only), --steps (100), --warmup (50:
+the clocks settle over the first tens of launches),
 --no-cpu (skip the CPU baseline), --only {all,chunk,decode}.
 """
 import argparse
@@ -169,8 +170,8 @@ def cpu_baseline(chunk_inputs_dev, cfg, target_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["all", "chunk", "decode"], default="all")
     args = ap.parse_args()

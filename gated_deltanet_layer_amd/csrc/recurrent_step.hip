@@ -12,24 +12,32 @@
 // few hundred bytes of vectors; it uses plain fp32 VALU work and wave-level
 // reductions, no matrix cores.
 //
-// Work split: one 256-thread workgroup per (n, h) slice.  Thread t owns the
-// float4 column group t % (V/4) of rows t / (V/4) + i * (256 / (V/4)), so one
-// wave-wide load covers whole 512-byte state rows.  The slice stays in
-// registers between the two reductions and the write-back, so S is read once
-// and written once, in place.  A slice belongs to exactly one workgroup, so the
-// in-place update has no races.
+// Work split: columns of S never mix, so each (n, h) slice is split into blocks
+// of at most 64 value columns, one 256-thread workgroup per block (twice the
+// workgroups of one per slice, which keeps more of the state in flight).
+// Thread t owns the float4 column group t % (VW/4) of rows t / (VW/4) +
+// i * (256 / (VW/4)), so one wave-wide load covers whole 256-byte row pieces.
+// The block stays in registers between the two reductions and the write-back,
+// so S is read once and written once, in place.  A block belongs to exactly one
+// workgroup, so the in-place update has no races.
 #include "gdn_common.h"
 
 namespace gdn {
 
+constexpr int RS_NTHR = 256;
+constexpr int RS_NWAVE = RS_NTHR / 64;
+constexpr int RS_VW = 64;             // value columns per workgroup (at most)
+
 template <typename DT, int K, int V, bool CHANNEL>
-__global__ __launch_bounds__(256) void recurrent_step_kernel(
+__global__ __launch_bounds__(RS_NTHR) void recurrent_step_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     float *__restrict__ S, DT *__restrict__ o)
 {
-    constexpr int TPR = V / 4;        // threads per state row (float4 each)
-    constexpr int RPP = 256 / TPR;    // rows covered by one pass of the block
+    constexpr int VW = V < RS_VW ? V : RS_VW;   // columns of this workgroup
+    constexpr int NVW = V / VW;                 // workgroups per slice
+    constexpr int TPR = VW / 4;       // threads per state row (float4 each)
+    constexpr int RPP = RS_NTHR / TPR; // rows covered by one pass of the block
     constexpr int NP = K / RPP;       // passes
     static_assert(K % RPP == 0 && TPR <= 64 && 64 % TPR == 0, "unsupported K/V");
 
@@ -37,11 +45,12 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     __shared__ float s_aq[K];         // alpha * q
     __shared__ float s_al[K];         // alpha
     __shared__ float s_k[K];          // k
-    __shared__ float s_qk[4];
-    __shared__ f32x4 s_red[4][TPR][2];
+    __shared__ float s_qk[RS_NWAVE];
+    __shared__ f32x4 s_red[RS_NWAVE][TPR][2];
     __shared__ f32x4 s_delta[TPR];
 
-    const long slice = blockIdx.x;
+    const long slice = blockIdx.x / NVW;
+    const int c0 = (blockIdx.x % NVW) * VW;     // first column of this workgroup
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -49,11 +58,13 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const int row0 = tid / TPR;
 
     // Issue the state loads first so they are in flight during the small loads.
-    float *Sp = S + slice * (long)(K * V);
+    // The state streams through once per step, far larger than the caches, so
+    // its loads and stores are marked non-temporal.
+    float *Sp = S + slice * (long)(K * V) + c0;
     f32x4 st[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i)
-        st[i] = *reinterpret_cast<const f32x4 *>(Sp + (row0 + i * RPP) * V + 4 * col4);
+        st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sp + (row0 + i * RPP) * V + 4 * col4));
 
     float qk_part = 0.f;
     if (tid < K) {
@@ -95,21 +106,26 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     __syncthreads();
 
     if (tid < TPR) {
-        f32x4 uu = s_red[0][tid][0] + s_red[1][tid][0] + s_red[2][tid][0] + s_red[3][tid][0];
-        f32x4 yy = s_red[0][tid][1] + s_red[1][tid][1] + s_red[2][tid][1] + s_red[3][tid][1];
-        const float qk = s_qk[0] + s_qk[1] + s_qk[2] + s_qk[3];
+        f32x4 uu = s_red[0][tid][0], yy = s_red[0][tid][1];
+        float qk = s_qk[0];
+#pragma unroll
+        for (int w = 1; w < RS_NWAVE; ++w) {
+            uu += s_red[w][tid][0];
+            yy += s_red[w][tid][1];
+            qk += s_qk[w];
+        }
         const float b = beta[slice];
         f32x4 d, oo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float ve = to_f32(v[slice * V + 4 * tid + e]);
+            const float ve = to_f32(v[slice * V + c0 + 4 * tid + e]);
             d[e] = b * (ve - uu[e]);
             oo[e] = yy[e] + qk * d[e];
         }
         s_delta[tid] = d;
         if (o) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[slice * V + 4 * tid + e] = from_f32<DT>(oo[e]);
+            for (int e = 0; e < 4; ++e) o[slice * V + c0 + 4 * tid + e] = from_f32<DT>(oo[e]);
         }
     }
     __syncthreads();
@@ -119,7 +135,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     for (int i = 0; i < NP; ++i) {
         const int r = row0 + i * RPP;
         const f32x4 nv = st[i] * s_al[r] + d * s_k[r];
-        *reinterpret_cast<f32x4 *>(Sp + r * V + 4 * col4) = nv;
+        __builtin_nontemporal_store(nv, reinterpret_cast<f32x4 *>(Sp + r * V + 4 * col4));
     }
 }
 
@@ -128,7 +144,8 @@ static hipError_t launch_step(const void *q, const void *k, const void *v, const
                               const float *beta, float *S, void *o, long nslices,
                               hipStream_t stream)
 {
-    hipLaunchKernelGGL((recurrent_step_kernel<DT, K, V, CH>), dim3((unsigned)nslices), dim3(256),
+    constexpr int NVW = V / (V < RS_VW ? V : RS_VW);
+    hipLaunchKernelGGL((recurrent_step_kernel<DT, K, V, CH>), dim3((unsigned)(nslices * NVW)), dim3(RS_NTHR),
                        0, stream, (const DT *)q, (const DT *)k, (const DT *)v, g, beta, S,
                        (DT *)o);
     return hipGetLastError();
