@@ -36,9 +36,9 @@ CSRC = os.path.join(ROOT, "gated_deltanet_layer_amd", "csrc")
 # kernel changed since its counters were taken reports null.
 MEASURED_TRAFFIC = {
     "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "gdn_common.h", "mfma_frag.h"),
-                                 "2858895f78bc23a6", 865451268),
+                                 "b34a338a73c7eac5", 862649471),
     "recurrent_step_kernel<bf16,128,128,channel>": (("recurrent_step.hip", "gdn_common.h"),
-                                                    "2da4a3cf64ce937c", 1630324235),
+                                                    "1864f0aa1a777d85", 1642879592),
 }
 
 
