@@ -35,8 +35,9 @@ CSRC = os.path.join(ROOT, "gated_deltanet_layer_amd", "csrc")
 # tensor.  Each entry is keyed by a digest of the kernel's sources, so that a
 # kernel changed since its counters were taken reports null.
 MEASURED_TRAFFIC = {
-    "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "gdn_common.h", "mfma_frag.h"),
-                                 "b34a338a73c7eac5", 862649471),
+    "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
+                                  "mfma_frag.h"),
+                                 "0c3103afe43f5070", 862649471),
     "recurrent_step_kernel<bf16,128,128,channel>": (("recurrent_step.hip", "gdn_common.h"),
                                                     "1864f0aa1a777d85", 1642879592),
 }
