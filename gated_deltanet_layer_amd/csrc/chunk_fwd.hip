@@ -523,15 +523,21 @@ static hipError_t launch_chunk(const ChunkArgs &a, hipStream_t stream)
 hipError_t chunk_fwd_ws_launch(int K, const void *q, const void *k, const void *v, const float *g,
                                const float *beta, const float *S0, void *o, float *S_T, int B,
                                int T, int H, int V, hipStream_t st);
+hipError_t chunk_fwd_wsc_launch(int K, const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const float *S0, void *o, float *S_T, int B,
+                                int T, int H, int V, hipStream_t st);
 
-// Host entry used by the C ABI after validation.  bf16 operands with the
-// scalar gate take the warp-specialised kernel (chunk_fwd_ws.hip).
+// Host entry used by the C ABI after validation.  bf16 operands take the
+// warp-specialised kernels (chunk_fwd_ws.hip for the scalar gate,
+// chunk_fwd_wsc.hip for the per-channel gate).
 hipError_t chunk_fwd_launch(bool bf16, bool channel, int K, const void *q, const void *k,
                             const void *v, const float *g, const float *beta, const float *S0,
                             void *o, float *S_T, int B, int T, int H, int V, hipStream_t st)
 {
     if (bf16 && !channel)
         return chunk_fwd_ws_launch(K, q, k, v, g, beta, S0, o, S_T, B, T, H, V, st);
+    if (bf16 && channel)
+        return chunk_fwd_wsc_launch(K, q, k, v, g, beta, S0, o, S_T, B, T, H, V, st);
     ChunkArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = S0; a.o = o; a.S_T = S_T;
     a.B = B; a.T = T; a.H = H; a.V = V;

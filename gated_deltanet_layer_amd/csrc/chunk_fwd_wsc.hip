@@ -1,0 +1,530 @@
+// chunk_fwd_wsc.hip -- warp-specialised chunkwise forward for bf16 operands and
+// the per-key-channel gate (GDN-2 / KDA: one log-decay per key channel).
+//
+// Mathematics (Atomic-GDN2 model card, section 2.1; the chunkwise mode of the
+// MindPattern "Gated DeltaNet" page).  For a chunk of 64 tokens in four blocks
+// of 16, with g in [-5, 0] per token and key channel c:
+//   lambda_tc  running sum of g_c from the start of t's block (|lambda| <= 80)
+//   E_bc       e^{sum of g_c over block b}                   (<= 1)
+//   R_ic       sum of g_c over the blocks before i,  gn_c the chunk total
+//   KL = k e^{lambda},  QL = q e^{lambda},  KI = k e^{-lambda}  (<= e^80: fits bf16)
+//   K+ S (rows of block i) = KL_i (Diag(e^{R_i}) S),  likewise Q+ S with QL_i
+//   A_ij = diag(beta_i) KL_i (KI_j * F_ij)^T,  P_ij = QL_i (KI_j * F_ij)^T,
+//          F_ij = e^{R_i - R_j} = E_j ... E_{i-1} per channel (1 for i = j)
+//   (I + A) D = diag(beta)(V - K+ S),  O = Q+ S + P D,
+//   S' = Diag(e^{gn}) S + K-^T D,  K- = KI e^{gn - R_i}  (<= 1).
+// Every exponential stays in range because the decay is split at 16-token
+// blocks (the card notes that its kernel bounds the decay for the same reason).
+//
+// Work split (as in chunk_fwd_ws.hip): 4 chain waves own 16 value columns each
+// of the fp32 state and run chunk c; 4 prep waves get chunk c+1 ready.  Prep
+// wave w owns token block w of the chunk: it loads that block's q, k, g (the
+// MFMA fragment layout, straight from global memory), scans g across its 16
+// rows with DPP, forms KL, QL, KI and K-, writes them to LDS, and computes the
+// Gram blocks of its rows and columns and its diagonal inverse.  The chain
+// waves take v straight from global memory one chunk ahead.
+#include "ws_common.h"
+
+namespace gdn {
+
+constexpr int WC_T = 64;       // tokens per chunk
+constexpr int WC_VB = 64;      // value columns per workgroup
+constexpr int WC_NTHR = 512;   // 4 chain waves + 4 prep waves
+
+template <int K> struct WcSmem {
+    static constexpr int al(int x) { return (x + 255) & ~255; }
+    static constexpr int RB = K * 2;              // bytes per tile row
+    static constexpr int CPR = RB / 16;           // 16-byte chunks per row
+    static constexpr int TILE = WC_T * RB;
+    static constexpr int PAD = 8;
+    static constexpr int LDC = WC_T + PAD;        // rows of -A and P (fragment order)
+    static constexpr int LDD = 16;                // rows of T_ii
+    // chain buffers (two): KL, QL, K- of a chunk, row-major, chunks swizzled
+    static constexpr int cKL = 0, cQL = TILE, cKM = 2 * TILE;
+    static constexpr int CBUF = 3 * TILE;
+    static constexpr int oC = 0;
+    // KI of token blocks 0 and 2 of the chunk being prepared (the only blocks
+    // another wave reads), at local rows 0..15 and 16..31
+    static constexpr int oKI = oC + 2 * CBUF;
+    // O staging, private to each chain wave: 64 rows of 32 bytes
+    static constexpr int oO = oKI + 32 * RB;
+    static constexpr int oD = oO + 4 * WC_T * 32;
+    // derived buffers (two)
+    static constexpr int dAn = 0;                           // [48][LDC] rows 16..63 of -A
+    static constexpr int dP = dAn + (WC_T - 16) * LDC * 2;  // [64][LDC] P
+    static constexpr int dTd = dP + WC_T * LDC * 2;         // [64][16] T_ii
+    static constexpr int dBeta = dTd + WC_T * LDD * 2;      // beta_t
+    static constexpr int dCF = dBeta + WC_T * 4;            // [4][K]: e^{R_1}, e^{R_2}, e^{R_3}, e^{gn}
+    static constexpr int DBUF = al(dCF + 4 * K * 4);
+    static constexpr int kE = oD + 2 * DBUF;                // [4][K] E_b of the chunk being prepared
+    static constexpr int kAd = kE + 4 * K * 4;              // [4][16][16] fp32 -A of diagonal blocks
+    static constexpr int kCtr = kAd + 4 * 16 * 16 * 4;
+    static constexpr int bytes = al(kCtr + 16);
+    static_assert(bytes <= 160 * 1024, "LDS budget");
+};
+
+// 8 bf16 scaled by 8 factors (fp32 arithmetic), back to bf16.
+__device__ __forceinline__ bf16x8 scale8(bf16x8 x, f32x4 f0, f32x4 f1) {
+    f32x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        a[e] = (float)x[e] * f0[e];
+        b[e] = (float)x[4 + e] * f1[e];
+    }
+    return cat8(cvt4(a), cvt4(b));
+}
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (lane r16 = token).
+__device__ __forceinline__ float row_inclusive_sum(float x) {
+    x += dpp_shr<0x111>(x);   // row_shr:1
+    x += dpp_shr<0x112>(x);   // row_shr:2
+    x += dpp_shr<0x114>(x);   // row_shr:4
+    x += dpp_shr<0x118>(x);   // row_shr:8
+    return x;
+}
+
+struct WcArgs {
+    const __bf16 *q, *k, *v;
+    const float *g, *beta, *S0;
+    __bf16 *o;
+    float *S_T;
+    int T, H, V, nvb;
+    int xcd_map;
+};
+
+template <int K>
+__global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
+{
+    using L = WcSmem<K>;
+    constexpr int NT = K / 16;          // 16-row tiles of S
+    constexpr int NKB = K / 32;         // 32-key blocks
+    constexpr int CPR = L::CPR;
+
+    extern __shared__ __attribute__((aligned(256))) char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r16 = lane & 15;
+    const int gq = lane >> 4;
+
+    const int T = args.T, H = args.H, V = args.V, nvb = args.nvb;
+    int bh, vb;
+    {
+        const int w = blockIdx.x;
+        if (args.xcd_map) {
+            const int xcd = w & 7, slot = w >> 3;
+            vb = slot % nvb;
+            bh = (slot / nvb) * 8 + xcd;
+        } else {
+            bh = w / nvb;
+            vb = w % nvb;
+        }
+    }
+    const int b = bh / args.H, h = bh % args.H;
+    const int v0 = vb * WC_VB;
+    const long row_base = (long)b * T * H + h;   // row of token 0 in [B*T*H]
+    const int nchunks = (T + WC_T - 1) / WC_T;
+
+    auto cbuf = [&](int c) { return smem + L::oC + (c & 1) * L::CBUF; };
+    auto dbuf = [&](int c) { return smem + L::oD + (c & 1) * L::DBUF; };
+    char *sKI = smem + L::oKI;
+    float *sE = reinterpret_cast<float *>(smem + L::kE);
+    unsigned *ctr = reinterpret_cast<unsigned *>(smem + L::kCtr);
+    if (tid == 0) *ctr = 0u;
+    lds_barrier();
+
+    if (wave >= 4) {
+        // ============================ prep waves ============================
+        const int pw = __builtin_amdgcn_readfirstlane(wave - 4);   // token block of this wave
+        float *sAd = reinterpret_cast<float *>(smem + L::kAd) + pw * 256;
+        const int row = 16 * pw + r16;                             // token row of this lane
+        // raw q, k, g of this lane's row, fragment layout: keys 32 kb + 8 gq .. +7
+        bf16x8 rk[NKB], rq[NKB];
+        f32x4 rg[NKB][2];
+        float rb = 0.f;
+        auto fetch = [&](int n) __attribute__((always_inline)) {
+            const int t = n * WC_T + row;
+            const long r = row_base + (long)min(t, T - 1) * H;   // rows past T repeat row T-1
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const long off = r * K + 32 * kb + 8 * gq;
+                rk[kb] = *reinterpret_cast<const bf16x8 *>(args.k + off);
+                rq[kb] = *reinterpret_cast<const bf16x8 *>(args.q + off);
+                rg[kb][0] = *reinterpret_cast<const f32x4 *>(args.g + off);
+                rg[kb][1] = *reinterpret_cast<const f32x4 *>(args.g + off + 4);
+            }
+            rb = args.beta[r];
+        };
+
+        unsigned arrivals = 0;
+        auto prepare = [&](int n) __attribute__((always_inline)) {
+            char *C = cbuf(n);
+            char *D = dbuf(n);
+            __bf16 *sAn = reinterpret_cast<__bf16 *>(D + L::dAn);
+            __bf16 *sP = reinterpret_cast<__bf16 *>(D + L::dP);
+            __bf16 *sTd = reinterpret_cast<__bf16 *>(D + L::dTd);
+            float *sCF = reinterpret_cast<float *>(D + L::dCF);
+            const bool live = n * WC_T + row < T;      // tokens past T: g = beta = 0
+
+            // --- this block's rows: lambda, E_pw, KL, QL, KI (kept), beta
+            Frag<__bf16> fKL[NKB], fQL[NKB], fKI[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                f32x4 lam[2], el[2], ei[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        lam[hh][e] = row_inclusive_sum(live ? rg[kb][hh][e] : 0.f);
+                        el[hh][e] = __expf(lam[hh][e]);
+                        ei[hh][e] = __expf(-lam[hh][e]);
+                    }
+                fKL[kb].v = scale8(rk[kb], el[0], el[1]);
+                fQL[kb].v = scale8(rq[kb], el[0], el[1]);
+                fKI[kb].v = scale8(rk[kb], ei[0], ei[1]);
+                const int off = qk_off<CPR>(row, 4 * kb + gq);
+                *reinterpret_cast<bf16x8 *>(C + L::cKL + off) = fKL[kb].v;
+                *reinterpret_cast<bf16x8 *>(C + L::cQL + off) = fQL[kb].v;
+                if ((pw & 1) == 0)   // row - 16 pw / 2 keeps the swizzle of row
+                    *reinterpret_cast<bf16x8 *>(sKI + off - 8 * pw * L::RB) = fKI[kb].v;
+                if (r16 == 15) {   // block totals: E_pw = e^{lambda of the last row}
+                    float *eb = sE + pw * K + 32 * kb + 8 * gq;
+                    *reinterpret_cast<f32x4 *>(eb) = el[0];
+                    *reinterpret_cast<f32x4 *>(eb + 4) = el[1];
+                }
+            }
+            const float bt = live ? rb : 0.f;
+            if (gq == 0) reinterpret_cast<float *>(D + L::dBeta)[row] = bt;
+            if (n + 1 < nchunks) fetch(n + 1);   // next chunk's rows, in flight from here
+            arrivals += 4;
+            prep_barrier(ctr, arrivals);         // KL, QL, KI and E of all blocks written
+
+            // --- chain factors: wave w writes row w of e^{R_1}, e^{R_2}, e^{R_3}, e^{gn}
+            //     (products of E_0..E_w), two channels per lane
+            if (2 * lane < K) {
+                const int c = 2 * lane;
+                f32x2 f = {1.f, 1.f};
+                for (int bb = 0; bb <= pw; ++bb) f *= *reinterpret_cast<const f32x2 *>(sE + bb * K + c);
+                *reinterpret_cast<f32x2 *>(sCF + pw * K + c) = f;
+            }
+            // --- K- of this block: KI * e^{gn - R_pw} = KI * E_pw ... E_3
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                f32x4 f0 = {1.f, 1.f, 1.f, 1.f}, f1 = f0;
+                for (int bb = pw; bb < 4; ++bb) {
+                    const float *eb = sE + bb * K + 32 * kb + 8 * gq;
+                    f0 *= *reinterpret_cast<const f32x4 *>(eb);
+                    f1 *= *reinterpret_cast<const f32x4 *>(eb + 4);
+                }
+                *reinterpret_cast<bf16x8 *>(C + L::cKM + qk_off<CPR>(row, 4 * kb + gq)) =
+                    scale8(fKI[kb].v, f0, f1);
+            }
+
+            // --- Gram blocks.  Off-diagonal (I, J): the A operand is KI_J * F_IJ,
+            //     the B operands KL_I and QL_I.
+            //       w0: (1,0) (3,0)   w1: (2,1) (3,1)   w2: (2,0)   w3: (3,2)
+            //     (own rows in registers, the other block's from LDS).
+            const int tq = lane_gq();
+            auto off_block = [&](int I, int J, const Frag<__bf16> (&aJ)[NKB], const Frag<__bf16> (&bK)[NKB],
+                                 const Frag<__bf16> (&bQ)[NKB]) __attribute__((always_inline)) {
+                f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    f32x4 f0 = {1.f, 1.f, 1.f, 1.f}, f1 = f0;
+                    for (int bb = J; bb < I; ++bb) {
+                        const float *eb = sE + bb * K + 32 * kb + 8 * tq;
+                        f0 *= *reinterpret_cast<const f32x4 *>(eb);
+                        f1 *= *reinterpret_cast<const f32x4 *>(eb + 4);
+                    }
+                    const Frag<__bf16> a = {scale8(aJ[kb].v, f0, f1)};
+                    aA = mma(aA, a, bK[kb]);
+                    aP = mma(aP, a, bQ[kb]);
+                }
+                const int t = 16 * I + lane_r16(), s0 = 16 * J + 4 * tq;
+                const float btt = reinterpret_cast<const float *>(D + L::dBeta)[t];
+                *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * L::LDC + frag_col(s0)) = cvt4(aA * -btt);
+                *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(aP);
+            };
+            auto lds_rows = [&](const char *M, int blk, Frag<__bf16> (&f)[NKB]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) f[kb] = qk_frag<CPR>(M, 16 * blk, kb);
+            };
+            {
+                Frag<__bf16> x0[NKB], x1[NKB];
+                if (pw == 0) {
+                    lds_rows(C + L::cKL, 1, x0);
+                    lds_rows(C + L::cQL, 1, x1);
+                    off_block(1, 0, fKI, x0, x1);
+                    lds_rows(C + L::cKL, 3, x0);
+                    lds_rows(C + L::cQL, 3, x1);
+                    off_block(3, 0, fKI, x0, x1);
+                } else if (pw == 1) {
+                    lds_rows(C + L::cKL, 2, x0);
+                    lds_rows(C + L::cQL, 2, x1);
+                    off_block(2, 1, fKI, x0, x1);
+                    lds_rows(C + L::cKL, 3, x0);
+                    lds_rows(C + L::cQL, 3, x1);
+                    off_block(3, 1, fKI, x0, x1);
+                } else if (pw == 2) {
+                    lds_rows(sKI, 0, x0);   // KI of block 0
+                    off_block(2, 0, x0, fKL, fQL);
+                } else {
+                    lds_rows(sKI, 1, x0);   // KI of block 2
+                    off_block(3, 2, x0, fKL, fQL);
+                }
+            }
+            // diagonal block pw: F = 1, masked
+            {
+                f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    aA = mma(aA, fKI[kb], fKL[kb]);
+                    aP = mma(aP, fKI[kb], fQL[kb]);
+                }
+                const int t = 16 * pw + r16, s0 = 16 * pw + 4 * gq;
+                const float btt = reinterpret_cast<const float *>(D + L::dBeta)[t];
+                f32x4 a, p;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = s0 + e;
+                    a[e] = (s < t) ? btt * aA[e] : 0.f;
+                    p[e] = (s <= t) ? aP[e] : 0.f;
+                }
+                *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(p);
+                // -A_dd row-major; this wave reads it back, in order, for the inverse
+                *reinterpret_cast<f32x4 *>(sAd + r16 * 16 + 4 * gq) = -a;
+            }
+            const f32x4 tr = unit_lower_inverse16_rows(sAd);
+            *reinterpret_cast<bf16x4 *>(sTd + (16 * pw + (lane >> 2)) * L::LDD + 4 * (lane & 3)) = cvt4(tr);
+        };
+
+        if (nchunks > 0) {
+            fetch(0);
+            prepare(0);
+            lds_barrier();
+        }
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) prepare(c + 1);
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ============================= chain waves =============================
+    // Accumulator tile ct = 2kb + hh, lane (gq, r16), element e holds S[key][col]
+    // with key = 32kb + 8gq + 4hh + e and col = v0 + 16 wave + r16.
+    const int vcol = 16 * wave + r16;
+    auto key_of = [&](int ct, int e) { return 32 * (ct >> 1) + 8 * gq + 4 * (ct & 1) + e; };
+    f32x4 S_acc[NT];
+    {
+        const float *S0 = args.S0 ? args.S0 + (long)bh * K * V : nullptr;
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S_acc[ct][e] = S0 ? S0[key_of(ct, e) * V + v0 + vcol] : 0.f;
+    }
+    // v of a chunk in the accumulator layout (rows 16 rt + 4 gq + e of this
+    // lane's column), loaded one chunk ahead; rows past T repeat row T-1
+    unsigned short vr[4][4];
+    auto fetch_v = [&](int n) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = min(n * WC_T + 16 * rt + 4 * gq + e, T - 1);
+                vr[rt][e] = reinterpret_cast<const unsigned short *>(args.v)[(row_base + (long)t * H) * V + v0 + vcol];
+            }
+    };
+    if (nchunks > 0) {
+        fetch_v(0);
+        lds_barrier();     // chunk 0 is ready
+    }
+
+    const int trow = 4 * gq + (r16 >> 2), tq = r16 & 3;
+    int k_tr[NKB];                         // + 8 hh + RB (32 kb2 + 16 s)
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) k_tr[kk] = qk_off<CPR>(trow, 4 * kk + tq);
+    // O staging: row r of this wave's 16 columns is 32 bytes, its two 16-byte
+    // halves swapped on rows with bit 3 set (conflict-free writes and reads)
+    char *sO = smem + L::oO + wave * (WC_T * 32);
+    int o_st[4];                           // + 512 rt
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = 4 * gq + e;
+        o_st[e] = r * 32 + (((r16 >> 3) ^ ((r >> 3) & 1)) << 4) + 2 * (r16 & 7);
+    }
+    const int o_rd0 = lane * 32 + (((lane >> 3) & 1) << 4), o_rd1 = o_rd0 ^ 16;
+
+    for (int c = 0; c < nchunks; ++c) {
+        const char *C = cbuf(c);
+        const char *sKL = C + L::cKL, *sQL = C + L::cQL, *sKM = C + L::cKM;
+        const char *D = dbuf(c);
+        const __bf16 *sAn = reinterpret_cast<const __bf16 *>(D + L::dAn);
+        const __bf16 *sP = reinterpret_cast<const __bf16 *>(D + L::dP);
+        const __bf16 *sTd = reinterpret_cast<const __bf16 *>(D + L::dTd);
+        const float *sBeta = reinterpret_cast<const float *>(D + L::dBeta);
+        const float *sCF = reinterpret_cast<const float *>(D + L::dCF);
+        unsigned ktr_addr[NKB];
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) ktr_addr[kk] = opaque(lds_u32(sKM) + k_tr[kk]);
+
+        // Phase A: K+ S and Q+ S.  Row tile rt (token block rt) takes the state
+        // with its key rows scaled by e^{R_rt}.
+        f32x4 KS[4], QS[4];
+        {
+            Frag<__bf16> fk[NKB], fq[NKB];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                Frag<__bf16> Sb[NKB];
+                if (rt == 0) {
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) Sb[kb] = reg_frag<__bf16>(S_acc[2 * kb], S_acc[2 * kb + 1]);
+                } else {
+                    const float *cf = sCF + (rt - 1) * K;
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) {
+                        const f32x4 f0 = *reinterpret_cast<const f32x4 *>(cf + 32 * kb + 8 * gq);
+                        const f32x4 f1 = *reinterpret_cast<const f32x4 *>(cf + 32 * kb + 8 * gq + 4);
+                        Sb[kb] = reg_frag<__bf16>(S_acc[2 * kb] * f0, S_acc[2 * kb + 1] * f1);
+                    }
+                }
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    fk[kb] = qk_frag<CPR>(sKL, 16 * rt, kb);
+                    fq[kb] = qk_frag<CPR>(sQL, 16 * rt, kb);
+                }
+                f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    ak = mma(ak, fk[kb], Sb[kb]);
+                    aq = mma(aq, fq[kb], Sb[kb]);
+                }
+                KS[rt] = ak;
+                QS[rt] = aq;
+                GDN_SCHED_FENCE();
+            }
+        }
+
+        // Phase B: X = diag(beta)(V - K+ S), then (I + A) D = X by block forward
+        // substitution (-A stored); the next chunk's v goes in flight.
+        f32x4 X[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const f32x4 bt = *reinterpret_cast<const f32x4 *>(sBeta + 16 * rt + 4 * gq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                X[rt][e] = bt[e] * (__builtin_bit_cast(float, (unsigned)vr[rt][e] << 16) - KS[rt][e]);
+        }
+        if (c + 1 < nchunks) fetch_v(c + 1);
+        const Frag<__bf16> fT0 = lds_frag_lo(sTd, L::LDD, 0, 0), fT1 = lds_frag_lo(sTd, L::LDD, 16, 0);
+        const Frag<__bf16> fT2 = lds_frag_lo(sTd, L::LDD, 32, 0), fT3 = lds_frag_lo(sTd, L::LDD, 48, 0);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 Dd[4];
+        Dd[0] = mma_lo(z, fT0, reg_frag<__bf16>(X[0], z));
+        f32x4 Y = mma_lo(X[1], lds_frag_fo_lo(sAn, L::LDC, 0, 0), reg_frag<__bf16>(Dd[0], z));
+        Dd[1] = mma_lo(z, fT1, reg_frag<__bf16>(Y, z));
+        const Frag<__bf16> Df0 = reg_frag<__bf16>(Dd[0], Dd[1]);
+        Y = mma(X[2], lds_frag_fo(sAn, L::LDC, 16, 0), Df0);
+        f32x4 Y3 = mma(X[3], lds_frag_fo(sAn, L::LDC, 32, 0), Df0);
+        Dd[2] = mma_lo(z, fT2, reg_frag<__bf16>(Y, z));
+        Y3 = mma_lo(Y3, lds_frag_fo_lo(sAn, L::LDC, 32, 32), reg_frag<__bf16>(Dd[2], z));
+        Dd[3] = mma_lo(z, fT3, reg_frag<__bf16>(Y3, z));
+        const Frag<__bf16> Df1 = reg_frag<__bf16>(Dd[2], Dd[3]);
+        GDN_SCHED_FENCE();
+
+        // Phase C: O = Q+ S + P D, staged through this wave's private rows for
+        // row-wise 16-byte stores.
+        bf16x4 kt[NT][4];
+        auto load_ct = [&](int ct) __attribute__((always_inline)) {
+            const unsigned pk = ktr_addr[ct >> 1] + 8 * (ct & 1);
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                kt[ct][2 * kb2] = lds_read_tr(pk + L::RB * 32 * kb2);
+                kt[ct][2 * kb2 + 1] = lds_read_tr(pk + L::RB * (32 * kb2 + 16));
+            }
+        };
+        load_ct(0);
+        load_ct(1);
+        f32x4 O[4];
+        O[0] = mma_lo(QS[0], lds_frag_fo_lo(sP, L::LDC, 0, 0), Df0);
+        O[1] = mma(QS[1], lds_frag_fo(sP, L::LDC, 16, 0), Df0);
+        O[2] = mma(QS[2], lds_frag_fo(sP, L::LDC, 32, 0), Df0);
+        O[2] = mma_lo(O[2], lds_frag_fo_lo(sP, L::LDC, 32, 32), Df1);
+        O[3] = mma(QS[3], lds_frag_fo(sP, L::LDC, 48, 0), Df0);
+        O[3] = mma(O[3], lds_frag_fo(sP, L::LDC, 48, 32), Df1);
+        if (args.o) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    *reinterpret_cast<__bf16 *>(sO + o_st[e] + 512 * rt) = (__bf16)O[rt][e];
+            asm volatile("" ::: "memory");
+            const int t = c * WC_T + lane;
+            if (t < T) {
+                const f32x4 o0 = *reinterpret_cast<const f32x4 *>(sO + o_rd0);
+                const f32x4 o1 = *reinterpret_cast<const f32x4 *>(sO + o_rd1);
+                f32x4 *dst = reinterpret_cast<f32x4 *>(args.o + (row_base + (long)t * H) * V + v0 + 16 * wave);
+                dst[0] = o0;
+                dst[1] = o1;
+            }
+        }
+        const Frag<__bf16> Ef[2] = {Df0, Df1};
+        GDN_SCHED_FENCE();
+
+        // Phase D: S' = Diag(e^{gn}) S + K-^T D, the k^T fragments read two
+        // tiles ahead.
+        const float *egn = sCF + 3 * K;
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            if (ct + 2 < NT) load_ct(ct + 2);
+            S_acc[ct] *= *reinterpret_cast<const f32x4 *>(egn + key_of(ct, 0));
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+                S_acc[ct] = mma(S_acc[ct], Frag<__bf16>{cat8(kt[ct][2 * kb2], kt[ct][2 * kb2 + 1])}, Ef[kb2]);
+            GDN_SCHED_FENCE();
+        }
+        lds_barrier();
+    }
+
+    if (args.S_T) {
+        float *ST = args.S_T + (long)bh * K * V;
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ST[key_of(ct, e) * V + v0 + vcol] = S_acc[ct][e];
+    }
+}
+
+template <int K>
+static hipError_t launch_wsc(const WcArgs &a, long nwg, hipStream_t stream)
+{
+    using L = WcSmem<K>;
+    static bool attr_set = false;  // benign race: every thread sets the same value
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_wsc_kernel<K>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(chunk_fwd_wsc_kernel<K>, dim3((unsigned)nwg), dim3(WC_NTHR), L::bytes, stream, a);
+    return hipGetLastError();
+}
+
+// Host entry for bf16 operands with the per-key-channel gate (K = 64 or 128).
+hipError_t chunk_fwd_wsc_launch(int K, const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const float *S0, void *o, float *S_T, int B,
+                                int T, int H, int V, hipStream_t st)
+{
+    WcArgs a;
+    a.q = (const __bf16 *)q; a.k = (const __bf16 *)k; a.v = (const __bf16 *)v;
+    a.g = g; a.beta = beta; a.S0 = S0; a.o = (__bf16 *)o; a.S_T = S_T;
+    a.T = T; a.H = H; a.V = V;
+    a.nvb = V / WC_VB;
+    const long bhn = (long)B * H;
+    a.xcd_map = (a.nvb > 1 && bhn % 8 == 0) ? 1 : 0;
+    const long nwg = bhn * a.nvb;
+    return K == 64 ? launch_wsc<64>(a, nwg, st) : launch_wsc<128>(a, nwg, st);
+}
+
+} // namespace gdn
