@@ -20,10 +20,15 @@
 // of the fp32 state and run chunk c; 4 prep waves get chunk c+1 ready.  Prep
 // wave w owns token block w of the chunk: it loads that block's q, k, g (the
 // MFMA fragment layout, straight from global memory), scans g across its 16
-// rows with DPP, forms KL, QL, KI and K-, writes them to LDS, and computes the
-// Gram blocks of its rows and columns and its diagonal inverse.  The chain
-// waves take v straight from global memory one chunk ahead.
+// rows with DPP, forms KL, QL, KI, writes them to LDS, computes its diagonal
+// Gram block and inverse; after the prep waves have met (all block totals E
+// written), they write the chain factors (one channel per lane) and each scales
+// its KI into K-.  The six off-diagonal Gram blocks are left to the chain
+// waves, which are idle once their state update for chunk c is done; they
+// start as soon as the prep waves have met.  The chain waves take v straight from global memory one
+// chunk ahead and write O straight from their accumulators.
 #include "ws_common.h"
+#include <type_traits>
 
 namespace gdn {
 
@@ -43,12 +48,10 @@ template <int K> struct WcSmem {
     static constexpr int cKL = 0, cQL = TILE, cKM = 2 * TILE;
     static constexpr int CBUF = 3 * TILE;
     static constexpr int oC = 0;
-    // KI of token blocks 0 and 2 of the chunk being prepared (the only blocks
-    // another wave reads), at local rows 0..15 and 16..31
+    // KI of token blocks 0, 1, 2 of the chunk being prepared (the A operands of
+    // the off-diagonal Gram blocks), rows 0..47
     static constexpr int oKI = oC + 2 * CBUF;
-    // O staging, private to each chain wave: 64 rows of 32 bytes
-    static constexpr int oO = oKI + 32 * RB;
-    static constexpr int oD = oO + 4 * WC_T * 32;
+    static constexpr int oD = oKI + 48 * RB;
     // derived buffers (two)
     static constexpr int dAn = 0;                           // [48][LDC] rows 16..63 of -A
     static constexpr int dP = dAn + (WC_T - 16) * LDC * 2;  // [64][LDC] P
@@ -74,13 +77,15 @@ __device__ __forceinline__ bf16x8 scale8(bf16x8 x, f32x4 f0, f32x4 f1) {
     return cat8(cvt4(a), cvt4(b));
 }
 
-// Inclusive prefix sum over the 16 lanes of each DPP row (lane r16 = token).
-__device__ __forceinline__ float row_inclusive_sum(float x) {
-    x += dpp_shr<0x111>(x);   // row_shr:1
-    x += dpp_shr<0x112>(x);   // row_shr:2
-    x += dpp_shr<0x114>(x);   // row_shr:4
-    x += dpp_shr<0x118>(x);   // row_shr:8
-    return x;
+// Wait (bounded, like prep_barrier) until the prep waves' arrival counter
+// reaches `target`, without arriving.
+__device__ __forceinline__ void wait_arrivals(unsigned *ctr, unsigned target) {
+    for (int it = 0; it < (1 << 22); ++it) {
+        const unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if ((unsigned)__builtin_amdgcn_readfirstlane((int)v) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
 }
 
 struct WcArgs {
@@ -142,138 +147,84 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         bf16x8 rk[NKB], rq[NKB];
         f32x4 rg[NKB][2];
         float rb = 0.f;
-        auto fetch = [&](int n) __attribute__((always_inline)) {
+        // Loads of one key block (k, q, g) or of beta for chunk n; rows past T
+        // read as zero (g = beta = 0: they change nothing).
+        auto fetch_kb = [&](int n, int kb) __attribute__((always_inline)) {
             const int t = n * WC_T + row;
-            const long r = row_base + (long)min(t, T - 1) * H;   // rows past T repeat row T-1
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const long off = r * K + 32 * kb + 8 * gq;
+            if (t < T) {
+                const long off = (row_base + (long)t * H) * K + 32 * kb + 8 * gq;
                 rk[kb] = *reinterpret_cast<const bf16x8 *>(args.k + off);
                 rq[kb] = *reinterpret_cast<const bf16x8 *>(args.q + off);
                 rg[kb][0] = *reinterpret_cast<const f32x4 *>(args.g + off);
                 rg[kb][1] = *reinterpret_cast<const f32x4 *>(args.g + off + 4);
+            } else {
+                rk[kb] = bf16x8{};
+                rq[kb] = bf16x8{};
+                rg[kb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                rg[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            rb = args.beta[r];
+        };
+        auto fetch_beta = [&](int n) __attribute__((always_inline)) {
+            const int t = n * WC_T + row;
+            rb = t < T ? args.beta[row_base + (long)t * H] : 0.f;
         };
 
         unsigned arrivals = 0;
         auto prepare = [&](int n) __attribute__((always_inline)) {
             char *C = cbuf(n);
             char *D = dbuf(n);
-            __bf16 *sAn = reinterpret_cast<__bf16 *>(D + L::dAn);
             __bf16 *sP = reinterpret_cast<__bf16 *>(D + L::dP);
             __bf16 *sTd = reinterpret_cast<__bf16 *>(D + L::dTd);
             float *sCF = reinterpret_cast<float *>(D + L::dCF);
-            const bool live = n * WC_T + row < T;      // tokens past T: g = beta = 0
 
             // --- this block's rows: lambda, E_pw, KL, QL, KI (kept), beta
+            // lambda: each scan step over all 32 values of the lane at once, so the
+            // dependent DPP adds of one value interleave with the others
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = rg[kb][hh][e];
+                            rg[kb][hh][e] = x + (st == 0 ? dpp_shr<0x111>(x) : st == 1 ? dpp_shr<0x112>(x)
+                                                 : st == 2 ? dpp_shr<0x114>(x) : dpp_shr<0x118>(x));
+                        }
             Frag<__bf16> fKL[NKB], fQL[NKB], fKI[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                f32x4 lam[2], el[2], ei[2];
+                f32x4 el[2], ei[2];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        lam[hh][e] = row_inclusive_sum(live ? rg[kb][hh][e] : 0.f);
-                        el[hh][e] = __expf(lam[hh][e]);
-                        ei[hh][e] = __expf(-lam[hh][e]);
+                        // lambda log2(e), then e^{lambda} and e^{-lambda} by exp2
+                        const float x = rg[kb][hh][e] * 1.44269504088896341f;
+                        el[hh][e] = __builtin_amdgcn_exp2f(x);
+                        ei[hh][e] = __builtin_amdgcn_exp2f(-x);
                     }
                 fKL[kb].v = scale8(rk[kb], el[0], el[1]);
                 fQL[kb].v = scale8(rq[kb], el[0], el[1]);
                 fKI[kb].v = scale8(rk[kb], ei[0], ei[1]);
+                // this key block of the next chunk goes in flight (spread over the
+                // loop rather than issued as one burst)
+                if (n + 1 < nchunks) fetch_kb(n + 1, kb);
                 const int off = qk_off<CPR>(row, 4 * kb + gq);
                 *reinterpret_cast<bf16x8 *>(C + L::cKL + off) = fKL[kb].v;
                 *reinterpret_cast<bf16x8 *>(C + L::cQL + off) = fQL[kb].v;
-                if ((pw & 1) == 0)   // row - 16 pw / 2 keeps the swizzle of row
-                    *reinterpret_cast<bf16x8 *>(sKI + off - 8 * pw * L::RB) = fKI[kb].v;
+                if (pw < 3) *reinterpret_cast<bf16x8 *>(sKI + off) = fKI[kb].v;
                 if (r16 == 15) {   // block totals: E_pw = e^{lambda of the last row}
                     float *eb = sE + pw * K + 32 * kb + 8 * gq;
                     *reinterpret_cast<f32x4 *>(eb) = el[0];
                     *reinterpret_cast<f32x4 *>(eb + 4) = el[1];
                 }
             }
-            const float bt = live ? rb : 0.f;
+            const float bt = rb;
+            if (n + 1 < nchunks) fetch_beta(n + 1);
             if (gq == 0) reinterpret_cast<float *>(D + L::dBeta)[row] = bt;
-            if (n + 1 < nchunks) fetch(n + 1);   // next chunk's rows, in flight from here
-            arrivals += 4;
-            prep_barrier(ctr, arrivals);         // KL, QL, KI and E of all blocks written
-
-            // --- chain factors: wave w writes row w of e^{R_1}, e^{R_2}, e^{R_3}, e^{gn}
-            //     (products of E_0..E_w), two channels per lane
-            if (2 * lane < K) {
-                const int c = 2 * lane;
-                f32x2 f = {1.f, 1.f};
-                for (int bb = 0; bb <= pw; ++bb) f *= *reinterpret_cast<const f32x2 *>(sE + bb * K + c);
-                *reinterpret_cast<f32x2 *>(sCF + pw * K + c) = f;
-            }
-            // --- K- of this block: KI * e^{gn - R_pw} = KI * E_pw ... E_3
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                f32x4 f0 = {1.f, 1.f, 1.f, 1.f}, f1 = f0;
-                for (int bb = pw; bb < 4; ++bb) {
-                    const float *eb = sE + bb * K + 32 * kb + 8 * gq;
-                    f0 *= *reinterpret_cast<const f32x4 *>(eb);
-                    f1 *= *reinterpret_cast<const f32x4 *>(eb + 4);
-                }
-                *reinterpret_cast<bf16x8 *>(C + L::cKM + qk_off<CPR>(row, 4 * kb + gq)) =
-                    scale8(fKI[kb].v, f0, f1);
-            }
-
-            // --- Gram blocks.  Off-diagonal (I, J): the A operand is KI_J * F_IJ,
-            //     the B operands KL_I and QL_I.
-            //       w0: (1,0) (3,0)   w1: (2,1) (3,1)   w2: (2,0)   w3: (3,2)
-            //     (own rows in registers, the other block's from LDS).
-            const int tq = lane_gq();
-            auto off_block = [&](int I, int J, const Frag<__bf16> (&aJ)[NKB], const Frag<__bf16> (&bK)[NKB],
-                                 const Frag<__bf16> (&bQ)[NKB]) __attribute__((always_inline)) {
-                f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    f32x4 f0 = {1.f, 1.f, 1.f, 1.f}, f1 = f0;
-                    for (int bb = J; bb < I; ++bb) {
-                        const float *eb = sE + bb * K + 32 * kb + 8 * tq;
-                        f0 *= *reinterpret_cast<const f32x4 *>(eb);
-                        f1 *= *reinterpret_cast<const f32x4 *>(eb + 4);
-                    }
-                    const Frag<__bf16> a = {scale8(aJ[kb].v, f0, f1)};
-                    aA = mma(aA, a, bK[kb]);
-                    aP = mma(aP, a, bQ[kb]);
-                }
-                const int t = 16 * I + lane_r16(), s0 = 16 * J + 4 * tq;
-                const float btt = reinterpret_cast<const float *>(D + L::dBeta)[t];
-                *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * L::LDC + frag_col(s0)) = cvt4(aA * -btt);
-                *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(aP);
-            };
-            auto lds_rows = [&](const char *M, int blk, Frag<__bf16> (&f)[NKB]) __attribute__((always_inline)) {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) f[kb] = qk_frag<CPR>(M, 16 * blk, kb);
-            };
-            {
-                Frag<__bf16> x0[NKB], x1[NKB];
-                if (pw == 0) {
-                    lds_rows(C + L::cKL, 1, x0);
-                    lds_rows(C + L::cQL, 1, x1);
-                    off_block(1, 0, fKI, x0, x1);
-                    lds_rows(C + L::cKL, 3, x0);
-                    lds_rows(C + L::cQL, 3, x1);
-                    off_block(3, 0, fKI, x0, x1);
-                } else if (pw == 1) {
-                    lds_rows(C + L::cKL, 2, x0);
-                    lds_rows(C + L::cQL, 2, x1);
-                    off_block(2, 1, fKI, x0, x1);
-                    lds_rows(C + L::cKL, 3, x0);
-                    lds_rows(C + L::cQL, 3, x1);
-                    off_block(3, 1, fKI, x0, x1);
-                } else if (pw == 2) {
-                    lds_rows(sKI, 0, x0);   // KI of block 0
-                    off_block(2, 0, x0, fKL, fQL);
-                } else {
-                    lds_rows(sKI, 1, x0);   // KI of block 2
-                    off_block(3, 2, x0, fKL, fQL);
-                }
-            }
-            // diagonal block pw: F = 1, masked
+            // --- diagonal block pw (F = 1, masked) and its inverse: own rows only
             {
                 f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
 #pragma unroll
@@ -282,12 +233,11 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                     aP = mma(aP, fKI[kb], fQL[kb]);
                 }
                 const int t = 16 * pw + r16, s0 = 16 * pw + 4 * gq;
-                const float btt = reinterpret_cast<const float *>(D + L::dBeta)[t];
                 f32x4 a, p;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s = s0 + e;
-                    a[e] = (s < t) ? btt * aA[e] : 0.f;
+                    a[e] = (s < t) ? bt * aA[e] : 0.f;
                     p[e] = (s <= t) ? aP[e] : 0.f;
                 }
                 *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(p);
@@ -296,10 +246,62 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
             }
             const f32x4 tr = unit_lower_inverse16_rows(sAd);
             *reinterpret_cast<bf16x4 *>(sTd + (16 * pw + (lane >> 2)) * L::LDD + 4 * (lane & 3)) = cvt4(tr);
+            arrivals += 4;
+            prep_barrier(ctr, arrivals);         // KL, QL, KI and E of all blocks written
+
+            // --- chain factors e^{R_1} = E_0, e^{R_2}, e^{R_3}, e^{gn}: one channel
+            //     per lane (wave w takes channels w K/4 .. (w+1) K/4 - 1)
+            if (lane < K / 4) {
+                const int c = (K / 4) * pw + lane;
+                const float e0 = sE[c], e1 = sE[K + c], e2 = sE[2 * K + c], e3 = sE[3 * K + c];
+                const float e01 = e0 * e1, e012 = e01 * e2;
+                sCF[c] = e0;
+                sCF[K + c] = e01;
+                sCF[2 * K + c] = e012;
+                sCF[3 * K + c] = e012 * e3;
+            }
+            // --- K- of this block: KI * e^{gn - R_pw} = KI * E_pw ... E_3 (all
+            //     factors read before any tile write)
+            auto kminus = [&](auto pwc) __attribute__((always_inline)) {
+                constexpr int PW = decltype(pwc)::value;
+                bf16x8 km[NKB];
+#pragma unroll
+                for (int hb = 0; hb < NKB; hb += NKB / 2) {
+                    f32x4 E[NKB / 2][4 - PW][2];
+#pragma unroll
+                    for (int i = 0; i < NKB / 2; ++i)
+#pragma unroll
+                        for (int bb = PW; bb < 4; ++bb) {
+                            const float *F = sE + bb * K + 32 * (hb + i) + 8 * gq;
+                            E[i][bb - PW][0] = *reinterpret_cast<const f32x4 *>(F);
+                            E[i][bb - PW][1] = *reinterpret_cast<const f32x4 *>(F + 4);
+                        }
+                    GDN_SCHED_FENCE();
+#pragma unroll
+                    for (int i = 0; i < NKB / 2; ++i) {
+                        f32x4 f0 = E[i][0][0], f1 = E[i][0][1];
+#pragma unroll
+                        for (int bb = PW + 1; bb < 4; ++bb) {
+                            f0 *= E[i][bb - PW][0];
+                            f1 *= E[i][bb - PW][1];
+                        }
+                        km[hb + i] = scale8(fKI[hb + i].v, f0, f1);
+                    }
+                }
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+                    *reinterpret_cast<bf16x8 *>(C + L::cKM + qk_off<CPR>(row, 4 * kb + gq)) = km[kb];
+            };
+            if (pw == 0) kminus(std::integral_constant<int, 0>());
+            else if (pw == 1) kminus(std::integral_constant<int, 1>());
+            else if (pw == 2) kminus(std::integral_constant<int, 2>());
+            else kminus(std::integral_constant<int, 3>());
         };
 
         if (nchunks > 0) {
-            fetch(0);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) fetch_kb(0, kb);
+            fetch_beta(0);
             prepare(0);
             lds_barrier();
         }
@@ -326,18 +328,118 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
     }
     // v of a chunk in the accumulator layout (rows 16 rt + 4 gq + e of this
     // lane's column), loaded one chunk ahead; rows past T repeat row T-1
+    const unsigned v_lane = (unsigned)(4 * gq * H * V + v0 + vcol);   // row 4 gq of a chunk
     unsigned short vr[4][4];
+    const unsigned short *vsrc = reinterpret_cast<const unsigned short *>(args.v);
     auto fetch_v = [&](int n) __attribute__((always_inline)) {
+        if ((n + 1) * WC_T <= T) {
+            // whole chunk inside the sequence: a wave-uniform base per row (scalar
+            // address arithmetic) and one 32-bit lane offset
+            const unsigned short *pn = vsrc + (row_base + (long)n * WC_T * H) * V;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+            for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = min(n * WC_T + 16 * rt + 4 * gq + e, T - 1);
-                vr[rt][e] = reinterpret_cast<const unsigned short *>(args.v)[(row_base + (long)t * H) * V + v0 + vcol];
+                for (int e = 0; e < 4; ++e) vr[rt][e] = (pn + (long)(16 * rt + e) * H * V)[v_lane];
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = min(n * WC_T + 16 * rt + 4 * gq + e, T - 1);
+                    vr[rt][e] = vsrc[(row_base + (long)t * H) * V + v0 + vcol];
+                }
+        }
+    };
+    // Off-diagonal Gram blocks (I, J) of chunk n: A = KI_J * F_IJ (per channel),
+    // B = KL_I and QL_I, computed transposed (the product's rows are s of block
+    // J, its columns t of block I), so that each lane holds four consecutive
+    // columns s of one row t:
+    //   w0: (1,0) (3,0)   w1: (2,1) (3,1)   w2: (3,2)   w3: (2,0)
+    // F_IJ = E_J ... E_{I-1} per channel.  Waits until the prep waves have
+    // written KL, QL, KI and E of the chunk.
+    auto gram_pairs = [&](int n) __attribute__((always_inline)) {
+        wait_arrivals(ctr, 4u * (unsigned)(n + 1));
+        const char *C = cbuf(n);
+        char *D = dbuf(n);
+        __bf16 *sAn = reinterpret_cast<__bf16 *>(D + L::dAn);
+        __bf16 *sP = reinterpret_cast<__bf16 *>(D + L::dP);
+        const float *sBn = reinterpret_cast<const float *>(D + L::dBeta);
+        // Blocks (I1, J) and, if I2 > 0, (I2, J) (they share the A source KI_J),
+        // half of the key blocks at a time: every LDS read of the half is issued
+        // before any product.
+        auto pairs = [&](auto i1c, auto i2c, auto jc) __attribute__((always_inline)) {
+            constexpr int I1 = decltype(i1c)::value, I2 = decltype(i2c)::value, J = decltype(jc)::value;
+            constexpr int IM = I2 > 0 ? I2 : I1;       // E rows J .. IM-1 are needed
+            constexpr int NH = NKB / 2;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            f32x4 aA1 = z, aP1 = z, aA2 = z, aP2 = z;
+#pragma unroll
+            for (int hb = 0; hb < NKB; hb += NH) {
+                Frag<__bf16> fa[NH], fk1[NH], fq1[NH], fk2[NH], fq2[NH];
+                f32x4 E[NH][IM - J][2];
+#pragma unroll
+                for (int i = 0; i < NH; ++i) {
+                    const int kb = hb + i;
+                    fa[i] = qk_frag<CPR>(sKI, 16 * J, kb);
+                    fk1[i] = qk_frag<CPR>(C + L::cKL, 16 * I1, kb);
+                    fq1[i] = qk_frag<CPR>(C + L::cQL, 16 * I1, kb);
+                    if constexpr (I2 > 0) {
+                        fk2[i] = qk_frag<CPR>(C + L::cKL, 16 * I2, kb);
+                        fq2[i] = qk_frag<CPR>(C + L::cQL, 16 * I2, kb);
+                    }
+#pragma unroll
+                    for (int bb = J; bb < IM; ++bb) {
+                        const float *F = sE + bb * K + 32 * kb + 8 * gq;
+                        E[i][bb - J][0] = *reinterpret_cast<const f32x4 *>(F);
+                        E[i][bb - J][1] = *reinterpret_cast<const f32x4 *>(F + 4);
+                    }
+                }
+                GDN_SCHED_FENCE();
+#pragma unroll
+                for (int i = 0; i < NH; ++i) {
+                    f32x4 f0 = E[i][0][0], f1 = E[i][0][1];
+#pragma unroll
+                    for (int bb = J + 1; bb < I1; ++bb) {
+                        f0 *= E[i][bb - J][0];
+                        f1 *= E[i][bb - J][1];
+                    }
+                    const Frag<__bf16> a1 = {scale8(fa[i].v, f0, f1)};
+                    aA1 = mma(aA1, a1, fk1[i]);
+                    aP1 = mma(aP1, a1, fq1[i]);
+                    if constexpr (I2 > 0) {
+#pragma unroll
+                        for (int bb = I1; bb < I2; ++bb) {
+                            f0 *= E[i][bb - J][0];
+                            f1 *= E[i][bb - J][1];
+                        }
+                        const Frag<__bf16> a2 = {scale8(fa[i].v, f0, f1)};
+                        aA2 = mma(aA2, a2, fk2[i]);
+                        aP2 = mma(aP2, a2, fq2[i]);
+                    }
+                }
             }
+            const int s0 = 16 * J + 4 * gq;
+            {
+                const int t = 16 * I1 + r16;
+                *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * L::LDC + frag_col(s0)) = cvt4(aA1 * -sBn[t]);
+                *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(aP1);
+            }
+            if constexpr (I2 > 0) {
+                const int t = 16 * I2 + r16;
+                *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * L::LDC + frag_col(s0)) = cvt4(aA2 * -sBn[t]);
+                *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(aP2);
+            }
+        };
+        using std::integral_constant;
+        const int cw = __builtin_amdgcn_readfirstlane(wave);
+        if (cw == 0) pairs(integral_constant<int, 1>(), integral_constant<int, 3>(), integral_constant<int, 0>());
+        else if (cw == 1) pairs(integral_constant<int, 2>(), integral_constant<int, 3>(), integral_constant<int, 1>());
+        else if (cw == 2) pairs(integral_constant<int, 3>(), integral_constant<int, 0>(), integral_constant<int, 2>());
+        else pairs(integral_constant<int, 2>(), integral_constant<int, 0>(), integral_constant<int, 0>());
     };
     if (nchunks > 0) {
         fetch_v(0);
+        gram_pairs(0);
         lds_barrier();     // chunk 0 is ready
     }
 
@@ -345,16 +447,6 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
     int k_tr[NKB];                         // + 8 hh + RB (32 kb2 + 16 s)
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) k_tr[kk] = qk_off<CPR>(trow, 4 * kk + tq);
-    // O staging: row r of this wave's 16 columns is 32 bytes, its two 16-byte
-    // halves swapped on rows with bit 3 set (conflict-free writes and reads)
-    char *sO = smem + L::oO + wave * (WC_T * 32);
-    int o_st[4];                           // + 512 rt
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int r = 4 * gq + e;
-        o_st[e] = r * 32 + (((r16 >> 3) ^ ((r >> 3) & 1)) << 4) + 2 * (r16 & 7);
-    }
-    const int o_rd0 = lane * 32 + (((lane >> 3) & 1) << 4), o_rd1 = o_rd0 ^ 16;
 
     for (int c = 0; c < nchunks; ++c) {
         const char *C = cbuf(c);
@@ -374,20 +466,27 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         f32x4 KS[4], QS[4];
         {
             Frag<__bf16> fk[NKB], fq[NKB];
+            f32x4 cfv[2][NKB][2];                  // e^{R_rt} of this lane's keys, one tile ahead
+            auto load_cf = [&](int rt) __attribute__((always_inline)) {
+                const float *cf = sCF + (rt - 1) * K + 8 * gq;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    cfv[rt & 1][kb][0] = *reinterpret_cast<const f32x4 *>(cf + 32 * kb);
+                    cfv[rt & 1][kb][1] = *reinterpret_cast<const f32x4 *>(cf + 32 * kb + 4);
+                }
+            };
+            load_cf(1);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
+                if (rt >= 1 && rt + 1 < 4) load_cf(rt + 1);
                 Frag<__bf16> Sb[NKB];
                 if (rt == 0) {
 #pragma unroll
                     for (int kb = 0; kb < NKB; ++kb) Sb[kb] = reg_frag<__bf16>(S_acc[2 * kb], S_acc[2 * kb + 1]);
                 } else {
-                    const float *cf = sCF + (rt - 1) * K;
 #pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) {
-                        const f32x4 f0 = *reinterpret_cast<const f32x4 *>(cf + 32 * kb + 8 * gq);
-                        const f32x4 f1 = *reinterpret_cast<const f32x4 *>(cf + 32 * kb + 8 * gq + 4);
-                        Sb[kb] = reg_frag<__bf16>(S_acc[2 * kb] * f0, S_acc[2 * kb + 1] * f1);
-                    }
+                    for (int kb = 0; kb < NKB; ++kb)
+                        Sb[kb] = reg_frag<__bf16>(S_acc[2 * kb] * cfv[rt & 1][kb][0], S_acc[2 * kb + 1] * cfv[rt & 1][kb][1]);
                 }
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
@@ -433,8 +532,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         const Frag<__bf16> Df1 = reg_frag<__bf16>(Dd[2], Dd[3]);
         GDN_SCHED_FENCE();
 
-        // Phase C: O = Q+ S + P D, staged through this wave's private rows for
-        // row-wise 16-byte stores.
+        // Phase C: O = Q+ S + P D.
         bf16x4 kt[NT][4];
         auto load_ct = [&](int ct) __attribute__((always_inline)) {
             const unsigned pk = ktr_addr[ct >> 1] + 8 * (ct & 1);
@@ -446,6 +544,9 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         };
         load_ct(0);
         load_ct(1);
+        f32x4 egn[NT];                     // e^{gn} of this lane's key rows
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) egn[ct] = *reinterpret_cast<const f32x4 *>(sCF + 3 * K + key_of(ct, 0));
         f32x4 O[4];
         O[0] = mma_lo(QS[0], lds_frag_fo_lo(sP, L::LDC, 0, 0), Df0);
         O[1] = mma(QS[1], lds_frag_fo(sP, L::LDC, 16, 0), Df0);
@@ -454,19 +555,21 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         O[3] = mma(QS[3], lds_frag_fo(sP, L::LDC, 48, 0), Df0);
         O[3] = mma(O[3], lds_frag_fo(sP, L::LDC, 48, 32), Df1);
         if (args.o) {
+            // straight from the accumulators: 16 lanes write 32 contiguous bytes of a row
+            if ((c + 1) * WC_T <= T) {
+                __bf16 *pn = args.o + (row_base + (long)c * WC_T * H) * V;
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+                for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    *reinterpret_cast<__bf16 *>(sO + o_st[e] + 512 * rt) = (__bf16)O[rt][e];
-            asm volatile("" ::: "memory");
-            const int t = c * WC_T + lane;
-            if (t < T) {
-                const f32x4 o0 = *reinterpret_cast<const f32x4 *>(sO + o_rd0);
-                const f32x4 o1 = *reinterpret_cast<const f32x4 *>(sO + o_rd1);
-                f32x4 *dst = reinterpret_cast<f32x4 *>(args.o + (row_base + (long)t * H) * V + v0 + 16 * wave);
-                dst[0] = o0;
-                dst[1] = o1;
+                    for (int e = 0; e < 4; ++e) (pn + (long)(16 * rt + e) * H * V)[v_lane] = (__bf16)O[rt][e];
+            } else {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = c * WC_T + 16 * rt + 4 * gq + e;
+                        if (t < T) args.o[(row_base + (long)t * H) * V + v0 + vcol] = (__bf16)O[rt][e];
+                    }
             }
         }
         const Frag<__bf16> Ef[2] = {Df0, Df1};
@@ -474,16 +577,16 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
 
         // Phase D: S' = Diag(e^{gn}) S + K-^T D, the k^T fragments read two
         // tiles ahead.
-        const float *egn = sCF + 3 * K;
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             if (ct + 2 < NT) load_ct(ct + 2);
-            S_acc[ct] *= *reinterpret_cast<const f32x4 *>(egn + key_of(ct, 0));
+            S_acc[ct] *= egn[ct];
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
                 S_acc[ct] = mma(S_acc[ct], Frag<__bf16>{cat8(kt[ct][2 * kb2], kt[ct][2 * kb2 + 1])}, Ef[kb2]);
             GDN_SCHED_FENCE();
         }
+        if (c + 1 < nchunks) gram_pairs(c + 1);
         lds_barrier();
     }
 
