@@ -20,12 +20,12 @@
 // of the fp32 state and run chunk c; 4 prep waves get chunk c+1 ready.  Prep
 // wave w owns token block w of the chunk: it loads that block's q, k, g (the
 // MFMA fragment layout, straight from global memory), scans g across its 16
-// rows with DPP, forms KL, QL, KI, writes them to LDS, computes its diagonal
-// Gram block and inverse; after the prep waves have met (all block totals E
-// written), they write the chain factors (one channel per lane) and each scales
-// its KI into K-.  The six off-diagonal Gram blocks are left to the chain
-// waves, which are idle once their state update for chunk c is done; they
-// start as soon as the prep waves have met.  The chain waves take v straight from global memory one
+// rows with DPP, forms KL, QL, KI and writes them to LDS; after the prep waves
+// have met (all block totals E written), they write the chain factors (one
+// channel per lane) and each scales its KI into K-.  The Gram blocks (diagonal
+// blocks with their inverses, and the six off-diagonal blocks) are left to the
+// chain waves, which are idle once their state update for chunk c is done;
+// they start as soon as the prep waves have met.  The chain waves take v straight from global memory one
 // chunk ahead and write O straight from their accumulators.
 #include "ws_common.h"
 #include <type_traits>
@@ -48,10 +48,9 @@ template <int K> struct WcSmem {
     static constexpr int cKL = 0, cQL = TILE, cKM = 2 * TILE;
     static constexpr int CBUF = 3 * TILE;
     static constexpr int oC = 0;
-    // KI of token blocks 0, 1, 2 of the chunk being prepared (the A operands of
-    // the off-diagonal Gram blocks), rows 0..47
+    // KI of the chunk being prepared (the A operands of the Gram blocks)
     static constexpr int oKI = oC + 2 * CBUF;
-    static constexpr int oD = oKI + 48 * RB;
+    static constexpr int oD = oKI + TILE;
     // derived buffers (two)
     static constexpr int dAn = 0;                           // [48][LDC] rows 16..63 of -A
     static constexpr int dP = dAn + (WC_T - 16) * LDC * 2;  // [64][LDC] P
@@ -141,7 +140,6 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
     if (wave >= 4) {
         // ============================ prep waves ============================
         const int pw = __builtin_amdgcn_readfirstlane(wave - 4);   // token block of this wave
-        float *sAd = reinterpret_cast<float *>(smem + L::kAd) + pw * 256;
         const int row = 16 * pw + r16;                             // token row of this lane
         // raw q, k, g of this lane's row, fragment layout: keys 32 kb + 8 gq .. +7
         bf16x8 rk[NKB], rq[NKB];
@@ -173,8 +171,6 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         auto prepare = [&](int n) __attribute__((always_inline)) {
             char *C = cbuf(n);
             char *D = dbuf(n);
-            __bf16 *sP = reinterpret_cast<__bf16 *>(D + L::dP);
-            __bf16 *sTd = reinterpret_cast<__bf16 *>(D + L::dTd);
             float *sCF = reinterpret_cast<float *>(D + L::dCF);
 
             // --- this block's rows: lambda, E_pw, KL, QL, KI (kept), beta
@@ -192,7 +188,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                             rg[kb][hh][e] = x + (st == 0 ? dpp_shr<0x111>(x) : st == 1 ? dpp_shr<0x112>(x)
                                                  : st == 2 ? dpp_shr<0x114>(x) : dpp_shr<0x118>(x));
                         }
-            Frag<__bf16> fKL[NKB], fQL[NKB], fKI[NKB];
+            Frag<__bf16> fKL[NKB], fQL[NKB], fKI[NKB];   // KI kept for K-
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 f32x4 el[2], ei[2];
@@ -214,38 +210,15 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                 const int off = qk_off<CPR>(row, 4 * kb + gq);
                 *reinterpret_cast<bf16x8 *>(C + L::cKL + off) = fKL[kb].v;
                 *reinterpret_cast<bf16x8 *>(C + L::cQL + off) = fQL[kb].v;
-                if (pw < 3) *reinterpret_cast<bf16x8 *>(sKI + off) = fKI[kb].v;
+                *reinterpret_cast<bf16x8 *>(sKI + off) = fKI[kb].v;
                 if (r16 == 15) {   // block totals: E_pw = e^{lambda of the last row}
                     float *eb = sE + pw * K + 32 * kb + 8 * gq;
                     *reinterpret_cast<f32x4 *>(eb) = el[0];
                     *reinterpret_cast<f32x4 *>(eb + 4) = el[1];
                 }
             }
-            const float bt = rb;
+            if (gq == 0) reinterpret_cast<float *>(D + L::dBeta)[row] = rb;
             if (n + 1 < nchunks) fetch_beta(n + 1);
-            if (gq == 0) reinterpret_cast<float *>(D + L::dBeta)[row] = bt;
-            // --- diagonal block pw (F = 1, masked) and its inverse: own rows only
-            {
-                f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    aA = mma(aA, fKI[kb], fKL[kb]);
-                    aP = mma(aP, fKI[kb], fQL[kb]);
-                }
-                const int t = 16 * pw + r16, s0 = 16 * pw + 4 * gq;
-                f32x4 a, p;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s = s0 + e;
-                    a[e] = (s < t) ? bt * aA[e] : 0.f;
-                    p[e] = (s <= t) ? aP[e] : 0.f;
-                }
-                *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(p);
-                // -A_dd row-major; this wave reads it back, in order, for the inverse
-                *reinterpret_cast<f32x4 *>(sAd + r16 * 16 + 4 * gq) = -a;
-            }
-            const f32x4 tr = unit_lower_inverse16_rows(sAd);
-            *reinterpret_cast<bf16x4 *>(sTd + (16 * pw + (lane >> 2)) * L::LDD + 4 * (lane & 3)) = cvt4(tr);
             arrivals += 4;
             prep_barrier(ctr, arrivals);         // KL, QL, KI and E of all blocks written
 
@@ -350,13 +323,15 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                 }
         }
     };
-    // Off-diagonal Gram blocks (I, J) of chunk n: A = KI_J * F_IJ (per channel),
+    float *sAd = reinterpret_cast<float *>(smem + L::kAd) + wave * 256;   // -A of a diagonal block
+    // Gram blocks of chunk n, once the prep waves have written KL, QL, KI, E
+    // and beta: the diagonal block of this wave's index and its inverse T_ii,
+    // then off-diagonal blocks (I, J): A = KI_J * F_IJ (per channel),
     // B = KL_I and QL_I, computed transposed (the product's rows are s of block
     // J, its columns t of block I), so that each lane holds four consecutive
     // columns s of one row t:
     //   w0: (1,0) (3,0)   w1: (2,1) (3,1)   w2: (3,2)   w3: (2,0)
-    // F_IJ = E_J ... E_{I-1} per channel.  Waits until the prep waves have
-    // written KL, QL, KI and E of the chunk.
+    // F_IJ = E_J ... E_{I-1} per channel.
     auto gram_pairs = [&](int n) __attribute__((always_inline)) {
         wait_arrivals(ctr, 4u * (unsigned)(n + 1));
         const char *C = cbuf(n);
@@ -432,6 +407,37 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         };
         using std::integral_constant;
         const int cw = __builtin_amdgcn_readfirstlane(wave);
+        // diagonal block cw (F = 1, masked) and its inverse
+        {
+            f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
+            Frag<__bf16> fi[NKB], fl[NKB], fq[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                fi[kb] = qk_frag<CPR>(sKI, 16 * cw, kb);
+                fl[kb] = qk_frag<CPR>(C + L::cKL, 16 * cw, kb);
+                fq[kb] = qk_frag<CPR>(C + L::cQL, 16 * cw, kb);
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                aA = mma(aA, fi[kb], fl[kb]);
+                aP = mma(aP, fi[kb], fq[kb]);
+            }
+            const int t = 16 * cw + r16, s0 = 16 * cw + 4 * gq;
+            const float bt = sBn[t];
+            f32x4 a, p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = s0 + e;
+                a[e] = (s < t) ? bt * aA[e] : 0.f;
+                p[e] = (s <= t) ? aP[e] : 0.f;
+            }
+            *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(p);
+            // -A of the block row-major; this wave reads it back, in order, for the inverse
+            *reinterpret_cast<f32x4 *>(sAd + r16 * 16 + 4 * gq) = -a;
+            const f32x4 tr = unit_lower_inverse16_rows(sAd);
+            *reinterpret_cast<bf16x4 *>(reinterpret_cast<__bf16 *>(D + L::dTd) + (16 * cw + (lane >> 2)) * L::LDD +
+                                        4 * (lane & 3)) = cvt4(tr);
+        }
         if (cw == 0) pairs(integral_constant<int, 1>(), integral_constant<int, 3>(), integral_constant<int, 0>());
         else if (cw == 1) pairs(integral_constant<int, 2>(), integral_constant<int, 3>(), integral_constant<int, 1>());
         else if (cw == 2) pairs(integral_constant<int, 3>(), integral_constant<int, 0>(), integral_constant<int, 2>());
