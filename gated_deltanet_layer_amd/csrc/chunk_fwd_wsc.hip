@@ -65,6 +65,22 @@ template <int K> struct WcSmem {
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
+// Byte offset of the 16-byte chunk `ch` of row `row` of a q/k-shaped tile
+// (rows of CPR chunks).  For 128 keys the chunk index is XORed with the row's
+// low four bits in swapped halves, so that both the 16-row fragment reads (one
+// chunk of 16 consecutive rows) and the transposed reads (four chunks of four
+// consecutive rows) fall on distinct banks; 64 keys use the plain row XOR.
+template <int CPR> __device__ __forceinline__ int wc_off(int row, int ch) {
+    if constexpr (CPR == 16)
+        return row * 256 + ((ch ^ (((row & 3) << 2) | ((row >> 2) & 3))) << 4);
+    else
+        return qk_off<CPR>(row, ch);
+}
+// Fragment: rows row0 + r16, keys 32 kb + 8 gq .. +7 (one 16-byte read).
+template <int CPR> __device__ __forceinline__ Frag<__bf16> wc_frag(const char *M, int row0, int kb) {
+    return {*reinterpret_cast<const bf16x8 *>(M + wc_off<CPR>(row0 + lane_r16(), 4 * kb + lane_gq()))};
+}
+
 // 8 bf16 scaled by 8 factors (fp32 arithmetic), back to bf16.
 __device__ __forceinline__ bf16x8 scale8(bf16x8 x, f32x4 f0, f32x4 f1) {
     f32x4 a, b;
@@ -207,7 +223,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                 // this key block of the next chunk goes in flight (spread over the
                 // loop rather than issued as one burst)
                 if (n + 1 < nchunks) fetch_kb(n + 1, kb);
-                const int off = qk_off<CPR>(row, 4 * kb + gq);
+                const int off = wc_off<CPR>(row, 4 * kb + gq);
                 *reinterpret_cast<bf16x8 *>(C + L::cKL + off) = fKL[kb].v;
                 *reinterpret_cast<bf16x8 *>(C + L::cQL + off) = fQL[kb].v;
                 *reinterpret_cast<bf16x8 *>(sKI + off) = fKI[kb].v;
@@ -263,7 +279,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                 }
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
-                    *reinterpret_cast<bf16x8 *>(C + L::cKM + qk_off<CPR>(row, 4 * kb + gq)) = km[kb];
+                    *reinterpret_cast<bf16x8 *>(C + L::cKM + wc_off<CPR>(row, 4 * kb + gq)) = km[kb];
             };
             if (pw == 0) kminus(std::integral_constant<int, 0>());
             else if (pw == 1) kminus(std::integral_constant<int, 1>());
@@ -355,12 +371,12 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
 #pragma unroll
                 for (int i = 0; i < NH; ++i) {
                     const int kb = hb + i;
-                    fa[i] = qk_frag<CPR>(sKI, 16 * J, kb);
-                    fk1[i] = qk_frag<CPR>(C + L::cKL, 16 * I1, kb);
-                    fq1[i] = qk_frag<CPR>(C + L::cQL, 16 * I1, kb);
+                    fa[i] = wc_frag<CPR>(sKI, 16 * J, kb);
+                    fk1[i] = wc_frag<CPR>(C + L::cKL, 16 * I1, kb);
+                    fq1[i] = wc_frag<CPR>(C + L::cQL, 16 * I1, kb);
                     if constexpr (I2 > 0) {
-                        fk2[i] = qk_frag<CPR>(C + L::cKL, 16 * I2, kb);
-                        fq2[i] = qk_frag<CPR>(C + L::cQL, 16 * I2, kb);
+                        fk2[i] = wc_frag<CPR>(C + L::cKL, 16 * I2, kb);
+                        fq2[i] = wc_frag<CPR>(C + L::cQL, 16 * I2, kb);
                     }
 #pragma unroll
                     for (int bb = J; bb < IM; ++bb) {
@@ -413,9 +429,9 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
             Frag<__bf16> fi[NKB], fl[NKB], fq[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                fi[kb] = qk_frag<CPR>(sKI, 16 * cw, kb);
-                fl[kb] = qk_frag<CPR>(C + L::cKL, 16 * cw, kb);
-                fq[kb] = qk_frag<CPR>(C + L::cQL, 16 * cw, kb);
+                fi[kb] = wc_frag<CPR>(sKI, 16 * cw, kb);
+                fl[kb] = wc_frag<CPR>(C + L::cKL, 16 * cw, kb);
+                fq[kb] = wc_frag<CPR>(C + L::cQL, 16 * cw, kb);
             }
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -452,7 +468,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
     const int trow = 4 * gq + (r16 >> 2), tq = r16 & 3;
     int k_tr[NKB];                         // + 8 hh + RB (32 kb2 + 16 s)
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) k_tr[kk] = qk_off<CPR>(trow, 4 * kk + tq);
+    for (int kk = 0; kk < NKB; ++kk) k_tr[kk] = wc_off<CPR>(trow, 4 * kk + tq);
 
     for (int c = 0; c < nchunks; ++c) {
         const char *C = cbuf(c);
@@ -469,6 +485,9 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
 
         // Phase A: K+ S and Q+ S.  Row tile rt (token block rt) takes the state
         // with its key rows scaled by e^{R_rt}.
+        // QS and O are computed transposed (rows: value columns, columns:
+        // tokens), by swapping the MFMA operands: the same fragments serve, and
+        // each lane ends with four consecutive value columns of one token.
         f32x4 KS[4], QS[4];
         {
             Frag<__bf16> fk[NKB], fq[NKB];
@@ -496,14 +515,14 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                 }
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    fk[kb] = qk_frag<CPR>(sKL, 16 * rt, kb);
-                    fq[kb] = qk_frag<CPR>(sQL, 16 * rt, kb);
+                    fk[kb] = wc_frag<CPR>(sKL, 16 * rt, kb);
+                    fq[kb] = wc_frag<CPR>(sQL, 16 * rt, kb);
                 }
                 f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
                     ak = mma(ak, fk[kb], Sb[kb]);
-                    aq = mma(aq, fq[kb], Sb[kb]);
+                    aq = mma(aq, Sb[kb], fq[kb]);   // transposed: (Q+ S)^T
                 }
                 KS[rt] = ak;
                 QS[rt] = aq;
@@ -554,28 +573,21 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) egn[ct] = *reinterpret_cast<const f32x4 *>(sCF + 3 * K + key_of(ct, 0));
         f32x4 O[4];
-        O[0] = mma_lo(QS[0], lds_frag_fo_lo(sP, L::LDC, 0, 0), Df0);
-        O[1] = mma(QS[1], lds_frag_fo(sP, L::LDC, 16, 0), Df0);
-        O[2] = mma(QS[2], lds_frag_fo(sP, L::LDC, 32, 0), Df0);
-        O[2] = mma_lo(O[2], lds_frag_fo_lo(sP, L::LDC, 32, 32), Df1);
-        O[3] = mma(QS[3], lds_frag_fo(sP, L::LDC, 48, 0), Df0);
-        O[3] = mma(O[3], lds_frag_fo(sP, L::LDC, 48, 32), Df1);
+        O[0] = mma_lo(QS[0], Df0, lds_frag_fo_lo(sP, L::LDC, 0, 0));
+        O[1] = mma(QS[1], Df0, lds_frag_fo(sP, L::LDC, 16, 0));
+        O[2] = mma(QS[2], Df0, lds_frag_fo(sP, L::LDC, 32, 0));
+        O[2] = mma_lo(O[2], Df1, lds_frag_fo_lo(sP, L::LDC, 32, 32));
+        O[3] = mma(QS[3], Df0, lds_frag_fo(sP, L::LDC, 48, 0));
+        O[3] = mma(O[3], Df1, lds_frag_fo(sP, L::LDC, 48, 32));
         if (args.o) {
-            // straight from the accumulators: 16 lanes write 32 contiguous bytes of a row
-            if ((c + 1) * WC_T <= T) {
-                __bf16 *pn = args.o + (row_base + (long)c * WC_T * H) * V;
+            // lane (gq, r16) holds value columns 16 wave + 4 gq .. +3 of token
+            // 16 rt + r16: one 8-byte store per row tile
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) (pn + (long)(16 * rt + e) * H * V)[v_lane] = (__bf16)O[rt][e];
-            } else {
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = c * WC_T + 16 * rt + 4 * gq + e;
-                        if (t < T) args.o[(row_base + (long)t * H) * V + v0 + vcol] = (__bf16)O[rt][e];
-                    }
+            for (int rt = 0; rt < 4; ++rt) {
+                const int t = c * WC_T + 16 * rt + r16;
+                if (t < T)
+                    *reinterpret_cast<bf16x4 *>(args.o + (row_base + (long)t * H) * V + v0 + 16 * wave + 4 * gq) =
+                        cvt4(O[rt]);
             }
         }
         const Frag<__bf16> Ef[2] = {Df0, Df1};
