@@ -26,10 +26,11 @@
 // rows of the state are kept in a fixed order of the key index: accumulator row
 // 32b + 16h + 4g + e holds key 32b + 8g + 4h + e.
 //
-// A single workgroup barrier per chunk hands the buffers over.  The prep waves
-// also need one barrier among themselves per chunk (all of q and k landed
-// before the Gram blocks); it is an LDS arrival counter that only those four
-// waves use.
+// A single workgroup barrier per chunk hands the buffers over.  Each prep wave
+// waits for its own copies before that barrier, so the q and k a prep wave reads
+// in the next period (copied by all four) are in LDS without further waits;
+// only the first chunk needs a barrier among the prep waves (an LDS arrival
+// counter that only those four waves use).
 #include "ws_common.h"
 
 namespace gdn {
@@ -289,21 +290,18 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 }
             }
         };
-        unsigned arrivals = 0;
-        // Chunk n: copy v(n) and q/k(n+1), scan g(n), then (once q/k(n) have
-        // landed in every prep wave) the Gram blocks and diagonal inverses.
+        // Chunk n: copy v(n) and q/k(n+1), scan g(n), the Gram blocks and
+        // diagonal inverses, then wait for the copies (the next period's q/k
+        // then needs no wait: the hand-over barrier orders it).
         auto prepare = [&](int n) {
             char *D = dbuf(n);
             __bf16 *sAn = reinterpret_cast<__bf16 *>(D + L::dAn);
             __bf16 *sP = reinterpret_cast<__bf16 *>(D + L::dP);
             __bf16 *sTd = reinterpret_cast<__bf16 *>(D + L::dTd);
+            // v(n) and q/k(n+1) go in flight; q/k(n) (and g/beta(n)) of every
+            // prep wave landed before the barrier that started this period
             copy_v(n);
             copy_qk(n + 1);
-            // q/k(n) (and g/beta(n)) landed; v(n), q/k(n+1) (g/beta(n+1)) may fly
-            if (pw == 0) wait_vm<NVL + 2 * NQK + 2>();
-            else wait_vm<NVL + 2 * NQK>();
-            arrivals += 4;
-            prep_barrier(ctr, arrivals);
 
             // every prep wave scans g itself (lane = token): its own gamma_t and
             // beta_t for its Gram blocks; waves 1 and 3 also write the chain's
@@ -336,13 +334,14 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 ws_gram_wave<2, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd);
             else
                 ws_gram_wave<3, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd);
-            // v(n) landed before the hand-over barrier
-            if (pw == 0) wait_vm<2 * NQK + 2>();
-            else wait_vm<2 * NQK>();
+            // v(n) and q/k(n+1) landed before the hand-over barrier
+            wait_vm<0>();
         };
 
         if (nchunks > 0) {
             copy_qk(0);
+            wait_vm<0>();
+            prep_barrier(ctr, 4);   // q/k(0) of every prep wave landed
             prepare(0);
             lds_barrier();
         }

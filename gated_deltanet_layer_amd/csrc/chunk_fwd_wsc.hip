@@ -92,17 +92,6 @@ __device__ __forceinline__ bf16x8 scale8(bf16x8 x, f32x4 f0, f32x4 f1) {
     return cat8(cvt4(a), cvt4(b));
 }
 
-// Wait (bounded, like prep_barrier) until the prep waves' arrival counter
-// reaches `target`, without arriving.
-__device__ __forceinline__ void wait_arrivals(unsigned *ctr, unsigned target) {
-    for (int it = 0; it < (1 << 22); ++it) {
-        const unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if ((unsigned)__builtin_amdgcn_readfirstlane((int)v) >= target) break;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    asm volatile("" ::: "memory");
-}
-
 struct WcArgs {
     const __bf16 *q, *k, *v;
     const float *g, *beta, *S0;

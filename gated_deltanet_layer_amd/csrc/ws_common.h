@@ -86,6 +86,17 @@ __device__ __forceinline__ void prep_barrier(unsigned *ctr, unsigned target) {
     asm volatile("" ::: "memory");
 }
 
+// Wait (bounded, like prep_barrier) until the arrival counter reaches
+// `target`, without arriving.
+__device__ __forceinline__ void wait_arrivals(unsigned *ctr, unsigned target) {
+    for (int it = 0; it < (1 << 22); ++it) {
+        const unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if ((unsigned)__builtin_amdgcn_readfirstlane((int)v) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
 // Broadcast lane Q of each group of four lanes to the group (DPP quad_perm).
 template <int Q> __device__ __forceinline__ float quad_bcast(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), Q * 0x55, 0xf, 0xf, false));
