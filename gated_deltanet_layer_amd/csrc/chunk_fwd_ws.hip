@@ -225,11 +225,12 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
         // This wave copies rows [16 pw, 16 pw + 16) of q, k and v of a chunk.
         // Lane l of copy instruction i fills LDS row rq = 16 pw + i RPI + l / CPR,
         // slot l % CPR, with logical chunk slot ^ (rq & (CPR-1)) of that row.
-        int qk_src[NQK], v_src[NVL];
+        unsigned qk_src[NQK];   // byte offsets from the chunk's first row
+        int v_src[NVL];
 #pragma unroll
         for (int i = 0; i < NQK; ++i) {
             const int rq = 16 * pw + i * RPI + lane / CPR, slot = lane % CPR;
-            qk_src[i] = rq * H * K + 8 * (slot ^ (rq & (CPR - 1)));
+            qk_src[i] = 2u * (unsigned)(rq * H * K + 8 * (slot ^ (rq & (CPR - 1))));
         }
 #pragma unroll
         for (int i = 0; i < NVL; ++i) {
@@ -251,11 +252,11 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
             }
             if (t0 + WS_T <= T) {
                 const long tok = row_base + (long)t0 * H;
-                const __bf16 *kb = args.k + tok * K, *qb = args.q + tok * K;
+                const __bf16 *kb = args.k + tok * K, *qb = args.q + tok * K;   // wave-uniform
 #pragma unroll
-                for (int i = 0; i < NQK; ++i) g2lds16(kb + qk_src[i], st + (16 * pw + i * RPI) * L::RB);
+                for (int i = 0; i < NQK; ++i) g2lds16s(kb, qk_src[i], st + (16 * pw + i * RPI) * L::RB);
 #pragma unroll
-                for (int i = 0; i < NQK; ++i) g2lds16(qb + qk_src[i], st + L::TILE + (16 * pw + i * RPI) * L::RB);
+                for (int i = 0; i < NQK; ++i) g2lds16s(qb, qk_src[i], st + L::TILE + (16 * pw + i * RPI) * L::RB);
             } else {
 #pragma unroll
                 for (int i = 0; i < NQK; ++i) {

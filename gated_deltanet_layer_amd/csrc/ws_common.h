@@ -59,6 +59,12 @@ __device__ __forceinline__ void g2lds16(const void *src, char *lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                  ::"v"(src), "s"(lds_addr(lds)) : "memory", "m0");
 }
+// Same, from a wave-uniform base (held in SGPRs) plus a 32-bit per-lane byte
+// offset: no 64-bit address per lane.
+__device__ __forceinline__ void g2lds16s(const void *base, unsigned off, char *lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 ::"v"(off), "s"(base), "s"(lds_addr(lds)) : "memory", "m0");
+}
 __device__ __forceinline__ void g2lds4(const void *src, char *lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                  ::"v"(src), "s"(lds_addr(lds)) : "memory", "m0");
