@@ -37,7 +37,11 @@ CSRC = os.path.join(ROOT, "gated_deltanet_layer_amd", "csrc")
 MEASURED_TRAFFIC = {
     "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
                                   "mfma_frag.h"),
-                                 "0c3103afe43f5070", 862649471),
+                                 "d0587a5fc5e60ae6", 868861033),
+    # the B=16 H=8 T=2048 channel-gate case (o and S_T written)
+    "chunk_fwd_wsc_kernel<128>": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
+                                   "mfma_frag.h"),
+                                  "721cac350622c52a", 420161311),
     "recurrent_step_kernel<bf16,128,128,channel>": (("recurrent_step.hip", "gdn_common.h"),
                                                     "1864f0aa1a777d85", 1642879592),
 }
@@ -111,6 +115,42 @@ def bench_chunk(torch, gdn, steps, warmup):
                 dense_tflops=dense / s / 1e12, inputs=d)
 
 
+def bench_channel(torch, gdn, name, steps, warmup):
+    """Per-key-channel-gate chunkwise forward on one of the channel configs, timed
+    like the headline case: o and S_T for the batched case, only S_T (from a
+    random S0) for the long prefill."""
+    from gdn_inputs import CHUNK_CONFIGS, chunk_inputs
+    cfg = CHUNK_CONFIGS[name]
+    d = chunk_inputs(cfg, device="cuda")
+    B, T, H, K, V = cfg.B, cfg.T, cfg.H, cfg.K, cfg.V
+    want_o = d["S0"] is None
+    o = torch.empty(B, T, H, V, dtype=torch.bfloat16, device="cuda") if want_o else None
+    S_T = torch.empty(B, H, K, V, dtype=torch.float32, device="cuda")
+    run = lambda: gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o, S_T)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    es = 2
+    per_ht = 2 * K * es + V * es + (V * es if want_o else 0) + K * 4 + 4
+    nbytes = B * T * H * per_ht + B * H * K * V * 4 * ((1 if d["S0"] is not None else 0) + 1)
+    del d
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": f"per-key-channel-gate GDN chunkwise forward, B={B} H={H} T={T} "
+                        f"d_k=d_v={K} chunk={cfg.chunk}, bf16 q/k/v" + ("/o" if want_o else "") +
+                        ", fp32 g/beta/state" + (", returns S_T only from a random S0" if not want_o else ", S0=0"),
+            "ms": ms, "mtok_s": B * T / (ms / 1e3) / 1e6, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+            "bytes_per_launch": nbytes, "kernel": "chunk_fwd_wsc_kernel<128>",
+            "traffic": measured_traffic("chunk_fwd_wsc_kernel<128>") if want_o else None,
+            "steps": steps, "warmup": warmup}
+
+
 def bench_decode(torch, gdn, reps):
     from gdn_inputs import DECODE_CONFIG, decode_inputs
     cfg = DECODE_CONFIG
@@ -174,7 +214,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["all", "chunk", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "channel"], default="all")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -235,6 +275,15 @@ def main():
                                "unit": "GB/s", "frac": dc["gbs"] / HBM_PEAK_GBS,
                                "traffic": dec["traffic"],
                                "kernel": "recurrent_step_kernel<bf16,128,128,channel>"}
+    if args.only in ("all", "channel"):
+        out["channel"] = [bench_channel(torch, gdn, "channel_bf16", args.steps, min(args.warmup, 20)),
+                          bench_channel(torch, gdn, "channel_long", max(2, min(args.steps, 5)),
+                                        max(1, min(args.warmup, 3)))]
+        if ch is None and args.only == "channel":
+            first = out["channel"][0]
+            out["value"] = first["mtok_s"]
+            out["ms_per_step"] = first["ms"]
+            out["config"] = {"workload": first["workload"]}
     if ch is not None and not args.no_cpu:
         torch.cuda.synchronize()
         cb = cpu_baseline(ch["inputs"], ch["cfg"])

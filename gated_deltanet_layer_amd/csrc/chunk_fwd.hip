@@ -546,10 +546,7 @@ hipError_t chunk_fwd_launch(bool bf16, bool channel, int K, const void *q, const
     // The hardware hands consecutive workgroups to the 8 XCDs in turn; keep the
     // column blocks of one head on one XCD so its q/k/g are fetched into one L2.
     a.xcd_map = (a.nvb > 1 && bhn % 8 == 0) ? 1 : 0;
-    if (bf16) {
-        if (K == 64) return channel ? launch_chunk<__bf16, 64, true>(a, st) : launch_chunk<__bf16, 64, false>(a, st);
-        return channel ? launch_chunk<__bf16, 128, true>(a, st) : launch_chunk<__bf16, 128, false>(a, st);
-    }
+    // fp32 operands (K = 64)
     return channel ? launch_chunk<float, 64, true>(a, st) : launch_chunk<float, 64, false>(a, st);
 }
 
