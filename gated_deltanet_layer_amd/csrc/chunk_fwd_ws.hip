@@ -240,37 +240,29 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
         // q and k of chunk n into its stage.  Rows past T repeat row T-1 (their
         // beta and g are zero, so they never contribute); n = nchunks copies
         // only such rows into a free stage, which keeps the wait counts fixed.
-        auto copy_qk = [&](int n) {
+        auto copy_qk = [&](int n, int which) {   // which 0: k (and g, beta), 1: q
             char *st = kq_stage(n);
             const int t0 = n * WS_T;
-            if (pw == 0) {
+            if (which == 0 && pw == 0) {
                 // g and beta of the chunk (lane = token), from a clamped row; the
                 // scan zeroes tokens past T
                 const long r = row_base + (long)min(t0 + lane, T - 1) * H;
                 g2lds4(args.g + r, st + 2 * L::TILE);
                 g2lds4(args.beta + r, st + 2 * L::TILE + WS_T * 4);
             }
+            const __bf16 *src = which == 0 ? args.k : args.q;
+            char *tile = st + (which == 0 ? 0 : L::TILE);
             if (t0 + WS_T <= T) {
-                const long tok = row_base + (long)t0 * H;
-                const __bf16 *kb = args.k + tok * K, *qb = args.q + tok * K;   // wave-uniform
+                const __bf16 *base = src + (row_base + (long)t0 * H) * K;   // wave-uniform
 #pragma unroll
-                for (int i = 0; i < NQK; ++i) g2lds16s(kb, qk_src[i], st + (16 * pw + i * RPI) * L::RB);
-#pragma unroll
-                for (int i = 0; i < NQK; ++i) g2lds16s(qb, qk_src[i], st + L::TILE + (16 * pw + i * RPI) * L::RB);
+                for (int i = 0; i < NQK; ++i) g2lds16s(base, qk_src[i], tile + (16 * pw + i * RPI) * L::RB);
             } else {
 #pragma unroll
                 for (int i = 0; i < NQK; ++i) {
                     const int rq = 16 * pw + i * RPI + lane / CPR, slot = lane % CPR;
                     const int t = min(t0 + rq, T - 1);
                     const long off = (row_base + (long)t * H) * K + 8 * (slot ^ (rq & (CPR - 1)));
-                    g2lds16(args.k + off, st + (16 * pw + i * RPI) * L::RB);
-                }
-#pragma unroll
-                for (int i = 0; i < NQK; ++i) {
-                    const int rq = 16 * pw + i * RPI + lane / CPR, slot = lane % CPR;
-                    const int t = min(t0 + rq, T - 1);
-                    const long off = (row_base + (long)t * H) * K + 8 * (slot ^ (rq & (CPR - 1)));
-                    g2lds16(args.q + off, st + L::TILE + (16 * pw + i * RPI) * L::RB);
+                    g2lds16(src + off, tile + (16 * pw + i * RPI) * L::RB);
                 }
             }
         };
@@ -302,7 +294,7 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
             // v(n) and q/k(n+1) go in flight; q/k(n) (and g/beta(n)) of every
             // prep wave landed before the barrier that started this period
             copy_v(n);
-            copy_qk(n + 1);
+            copy_qk(n + 1, 0);
 
             // every prep wave scans g itself (lane = token): its own gamma_t and
             // beta_t for its Gram blocks; waves 1 and 3 also write the chain's
@@ -325,6 +317,9 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 if (lane == 0) reinterpret_cast<float *>(D + L::dEgN)[0] = __expf(gn);
             }
 
+            // q(n+1) goes in flight only now: issued together with v(n) and k(n+1)
+            // the copies would stall this wave until the memory pipeline drains
+            copy_qk(n + 1, 1);
             // Gram blocks and the diagonal inverse (static per-wave schedule)
             const char *sK = st, *sQ = st + L::TILE;
             if (pw == 0)
@@ -340,7 +335,8 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
         };
 
         if (nchunks > 0) {
-            copy_qk(0);
+            copy_qk(0, 0);
+            copy_qk(0, 1);
             wait_vm<0>();
             prep_barrier(ctr, 4);   // q/k(0) of every prep wave landed
             prepare(0);

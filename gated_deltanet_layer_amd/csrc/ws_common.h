@@ -61,9 +61,14 @@ __device__ __forceinline__ void g2lds16(const void *src, char *lds) {
 }
 // Same, from a wave-uniform base (held in SGPRs) plus a 32-bit per-lane byte
 // offset: no 64-bit address per lane.
+// `base` must be the same in every lane (it is read from the first active one).
 __device__ __forceinline__ void g2lds16s(const void *base, unsigned off, char *lds) {
+    const unsigned long long b = (unsigned long long)(uintptr_t)base;
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+    const void *sb = (const void *)(uintptr_t)(((unsigned long long)hi << 32) | lo);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 ::"v"(off), "s"(base), "s"(lds_addr(lds)) : "memory", "m0");
+                 ::"v"(off), "s"(sb), "s"(lds_addr(lds)) : "memory", "m0");
 }
 __device__ __forceinline__ void g2lds4(const void *src, char *lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
