@@ -179,6 +179,44 @@ def bench_decode(torch, gdn, reps):
     return dict(cfg=cfg, ms_per_step=ms, bytes=nbytes, gbs=nbytes / (ms / 1e3) / 1e9)
 
 
+def bench_verify(torch, gdn, M, keep_hist, reps, warmup):
+    """M draft tokens per sequence from one state (gdn_recurrent_steps) on the
+    decode workload's shape: o of every token plus either the final state or the
+    state after every token (rollback).  S0 is left untouched (S_T is a separate
+    buffer), so the same call repeats."""
+    from gdn_inputs import DECODE_CONFIG, decode_inputs
+    cfg = DECODE_CONFIG.with_(steps=M)
+    d = decode_inputs(cfg, device="cuda")
+    N, H, K, V = cfg.N, cfg.H, cfg.K, cfg.V
+    nm = lambda t: t.transpose(0, 1).contiguous()
+    q, k, v, g, beta = (nm(d[n]) for n in ("q", "k", "v", "g", "beta"))
+    S0 = d["S0"]
+    o = torch.empty(N, M, H, V, dtype=torch.bfloat16, device="cuda")
+    S_T = None if keep_hist else torch.empty_like(S0)
+    S_hist = torch.empty(N, M, H, K, V, dtype=torch.float32, device="cuda") if keep_hist else None
+    run = lambda: gdn.gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    state = K * V * 4
+    per_tok = 2 * K * 2 + V * 2 + V * 2 + K * 4 + 4
+    nbytes = N * H * (state + (M * state if keep_hist else state) + M * per_tok)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": f"{M} draft tokens per sequence from one state, N={N} H={H} "
+                        f"d_k=d_v={K}, per-channel gate, bf16 q/k/v/o, fp32 state; "
+                        + ("state after every token kept" if keep_hist else "final state written"),
+            "M": M, "ms": ms, "tokens_per_s": N * M / (ms / 1e3), "gbs": gbs,
+            "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_call": nbytes,
+            "kernel": "recurrent_multi_kernel<bf16,128,128,channel>"}
+
+
 def cpu_baseline(chunk_inputs_dev, cfg, target_s=15.0):
     """fp64 oracle on a bounded sample of the prefill workload: whole sequences of
     some (b, h) slices, one OpenMP thread per slice."""
@@ -214,7 +252,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "channel"], default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "channel", "verify"], default="all")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -275,6 +313,13 @@ def main():
                                "unit": "GB/s", "frac": dc["gbs"] / HBM_PEAK_GBS,
                                "traffic": dec["traffic"],
                                "kernel": "recurrent_step_kernel<bf16,128,128,channel>"}
+    if args.only in ("all", "verify"):
+        reps = max(3, min(args.steps, 50))
+        ver = [bench_verify(torch, gdn, 4, False, reps, 5), bench_verify(torch, gdn, 4, True, reps, 5)]
+        if "decode" in out:
+            for x in ver:   # the same tokens as M one-token decode steps
+                x["vs_single_steps"] = x["M"] * out["decode"]["ms_per_step"] / x["ms"]
+        out["verify"] = ver
     if args.only in ("all", "channel"):
         out["channel"] = [bench_channel(torch, gdn, "channel_bf16", args.steps, min(args.warmup, 20)),
                           bench_channel(torch, gdn, "channel_long", max(2, min(args.steps, 5)),

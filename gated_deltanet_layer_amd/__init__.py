@@ -8,6 +8,7 @@ fallback: if ``libgdn.so`` has not been built, every call raises.
 Entry points (same names as the C ABI):
     gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk=64)
     gdn_recurrent_step(q, k, v, g, beta, S, o)
+    gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist)
 Conveniences that allocate the outputs:
     chunk_fwd(q, k, v, g, beta, S0=None, want_o=True) -> (o, S_T)
     recurrent_step_(q, k, v, g, beta, S) -> o      (S updated in place)
@@ -24,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_OK, GDN_EINVAL, GDN_ENOTSUP, GDN_EHIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_HEAD, GDN_GATE_CHANNEL = 0, 1
-SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_status_str", "gdn_abi_version")
+SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_steps", "gdn_status_str",
+           "gdn_abi_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -54,6 +56,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp,
                                          i, i, i, i, i, i, vp]
         L.gdn_recurrent_step.restype = i
+        L.gdn_recurrent_steps.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp,
+                                          i, i, i, i, i, i, i, vp]
+        L.gdn_recurrent_steps.restype = i
         L.gdn_status_str.argtypes = [i]
         L.gdn_status_str.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -169,6 +174,44 @@ def gdn_recurrent_step(q, k, v, g, beta, S, o, stream=None) -> None:
                                   _ptr(o), N, H, K, V, _dtype_code(q), gate, _stream(stream))
     if rc != GDN_OK:
         raise GDNError(rc, "gdn_recurrent_step")
+
+
+def gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist=None, stream=None) -> None:
+    """M tokens per sequence from one state (speculative-decoding verification).
+
+    q, k [N,M,H,K], v [N,M,H,V] (fp32 or bf16); g [N,M,H] or [N,M,H,K] fp32; beta
+    [N,M,H] fp32; S0 [N,H,K,V] fp32 or None (zeros).  Writes o [N,M,H,V], S_T
+    [N,H,K,V] (may be S0) and S_hist [N,M,H,K,V] (state after each token); any of
+    them may be None, not all.  Enqueued on the current torch stream.
+    """
+    import torch
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [N, M, H, D]")
+    N, M, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    dt = q.dtype
+    _check(q, "q", dtype=dt)
+    _check(k, "k", (N, M, H, K), dt, dev)
+    _check(v, "v", (N, M, H, V), dt, dev)
+    if g.dim() == 4:
+        gate = GDN_GATE_CHANNEL
+        _check(g, "g", (N, M, H, K), torch.float32, dev)
+    else:
+        gate = GDN_GATE_HEAD
+        _check(g, "g", (N, M, H), torch.float32, dev)
+    _check(beta, "beta", (N, M, H), torch.float32, dev)
+    _check(S0, "S0", (N, H, K, V), torch.float32, dev)
+    _check(o, "o", (N, M, H, V), dt, dev)
+    _check(S_T, "S_T", (N, H, K, V), torch.float32, dev)
+    _check(S_hist, "S_hist", (N, M, H, K, V), torch.float32, dev)
+    rc = lib().gdn_recurrent_steps(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                                   _ptr(o), _ptr(S_T), _ptr(S_hist), N, M, H, K, V,
+                                   _dtype_code(q), gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_recurrent_steps")
 
 
 def chunk_fwd(q, k, v, g, beta, S0=None, want_o: bool = True, chunk: int = 64, stream=None):

@@ -16,6 +16,10 @@ hipError_t recurrent_step_launch(bool bf16, bool channel, int K, int V, const vo
                                  const void *k, const void *v, const float *g,
                                  const float *beta, float *S, void *o, long nslices,
                                  hipStream_t st);
+hipError_t recurrent_multi_launch(bool bf16, bool channel, int K, int V, const void *q,
+                                  const void *k, const void *v, const float *g,
+                                  const float *beta, const float *S0, void *o, float *S_T,
+                                  float *S_hist, long nslices, int M, int H, hipStream_t st);
 } // namespace gdn
 
 namespace {
@@ -145,6 +149,54 @@ gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v, const
     const hipError_t e = gdn::recurrent_step_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL,
                                                     K, V, q, k, v, g, beta, S, o, ns,
                                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_recurrent_steps(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *S0, void *o, float *S_T,
+                               float *S_hist, int N, int M, int H, int K, int V,
+                               gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EINVAL;
+    if (gate != GDN_GATE_HEAD && gate != GDN_GATE_CHANNEL) return GDN_EINVAL;
+    if (N < 0 || M < 0 || H < 0 || K <= 0 || V <= 0) return GDN_EINVAL;
+    if (!o && !S_T && !S_hist) return GDN_EINVAL;
+    const long long es = dtype == GDN_BF16 ? 2 : 4;
+    const long long ns = prod(N, H), ntok = prod(N, M, H);
+    const long long nqk = prod(N, M, H, K), nv = prod(N, M, H, V), nst = prod(N, H, K, V);
+    const long long nhist = nqk < 0 ? -1 : prod(nqk, V);
+    if (ns < 0 || ntok < 0 || nqk < 0 || nv < 0 || nst < 0 || nhist < 0) return GDN_EINVAL;
+    const long long ng = gate == GDN_GATE_CHANNEL ? nqk : ntok;
+    if (ntok > 0 && (!q || !k || !v || !g || !beta)) return GDN_EINVAL;
+    // The vectors are read and o written element by element; every state tensor
+    // is streamed as 16-byte vectors.
+    for (const void *p : {q, k, v, (const void *)o})
+        if (p && !aligned(p, (unsigned)es)) return GDN_EINVAL;
+    for (const void *p : {(const void *)g, (const void *)beta})
+        if (p && !aligned(p, 4)) return GDN_EINVAL;
+    for (const void *p : {(const void *)S0, (const void *)S_T, (const void *)S_hist})
+        if (p && !aligned16(p)) return GDN_EINVAL;
+    // No output may touch an input or another output; S_T may be S0 exactly.
+    const Range rq = range(q, nqk * es), rk = range(k, nqk * es), rv = range(v, nv * es);
+    const Range rg = range(g, ng * 4), rb = range(beta, ntok * 4);
+    const Range rs0 = range(S0, S0 ? nst * 4 : 0), rst = range(S_T, S_T ? nst * 4 : 0);
+    const Range ro = range(o, o ? nv * es : 0), rh = range(S_hist, S_hist ? nhist * 4 : 0);
+    for (Range r : {rq, rk, rv, rg, rb, rs0, rst, rh})
+        if (overlap(ro, r)) return GDN_EINVAL;
+    for (Range r : {rq, rk, rv, rg, rb, rs0, rst})
+        if (overlap(rh, r)) return GDN_EINVAL;
+    for (Range r : {rq, rk, rv, rg, rb})
+        if (overlap(rst, r)) return GDN_EINVAL;
+    if (S0 && S_T && (const void *)S0 != (const void *)S_T && overlap(rs0, rst)) return GDN_EINVAL;
+
+    if (!kv_supported(K) || !kv_supported(V)) return GDN_ENOTSUP;
+    if (prod(ns, V / 64 > 0 ? V / 64 : 1) > 0x7fffffffLL) return GDN_ENOTSUP;
+    if (ns == 0) return GDN_OK;
+    if (M == 0 && !S_T) return GDN_OK;   // nothing to write
+
+    const hipError_t e = gdn::recurrent_multi_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL,
+                                                     K, V, q, k, v, g, beta, S0, o, S_T, S_hist,
+                                                     ns, M, H, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

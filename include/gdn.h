@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -104,6 +104,38 @@ GDN_API gdn_status gdn_recurrent_step(const void *q, const void *k, const void *
                               float *S, void *o,
                               int N, int H, int K, int V,
                               gdn_dtype dtype, gdn_gate gate, void *stream);
+
+/*
+ * M tokens of each of N sequences, applied in order from one state: the
+ * verification step of speculative decoding (M draft tokens scored from the
+ * state of the accepted prefix: the chained multi-token-prediction speculative
+ * decoding behind the single-card decode figure on the MindPattern "Gated
+ * DeltaNet" page, finding of 2026-08-18).  Each token is
+ * one step of the recurrence above, computed as gdn_recurrent_step computes it,
+ * so M = 1 gives gdn_recurrent_step's results.
+ *
+ *   q, k    [N, M, H, K]   dtype        v  [N, M, H, V]   dtype
+ *   g       [N, M, H] or [N, M, H, K] fp32          beta [N, M, H] fp32
+ *   S0      [N, H, K, V]   fp32 state before the first token, or NULL for zeros
+ *   o       [N, M, H, V]   dtype output of every token, or NULL
+ *   S_T     [N, H, K, V]   fp32 state after the last token, or NULL.  May equal
+ *                          S0 (updated in place).
+ *   S_hist  [N, M, H, K, V] fp32 state after every token (S_hist[n, j] is the
+ *                          state after token j: rolling back to an accepted
+ *                          prefix of j + 1 tokens is taking it), or NULL.
+ *
+ * At least one of o, S_T, S_hist must be non-NULL.  No output may overlap an
+ * input or another output (except S_T == S0).  q, k, v, o need their element
+ * alignment, g and beta 4 bytes, S0, S_T and S_hist 16 bytes.  K and V: 64 or
+ * 128.  N, M or H equal to 0 is a valid call (with M = 0, S_T receives S0).
+ * The state is read once and S_T written once whatever M is; S_hist adds M
+ * state writes.
+ */
+GDN_API gdn_status gdn_recurrent_steps(const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *S0,
+                               void *o, float *S_T, float *S_hist,
+                               int N, int M, int H, int K, int V,
+                               gdn_dtype dtype, gdn_gate gate, void *stream);
 
 /* Static English text for a status code (never NULL). */
 GDN_API const char *gdn_status_str(gdn_status s);

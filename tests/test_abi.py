@@ -41,7 +41,7 @@ def test_only_declared_symbols_are_exported():
 
 
 def test_version_and_status_strings(L):
-    assert gdn.abi_version() == 1
+    assert gdn.abi_version() == 2
     assert gdn.status_str(0) == "ok"
     assert "invalid" in gdn.status_str(1)
     assert "unsupported" in gdn.status_str(2)
@@ -128,6 +128,48 @@ def test_step_unsupported(L, kw):
 
 def test_step_empty_is_a_noop(L):
     assert _step(L, N=0) == gdn.GDN_OK
+
+
+def _steps(L, **kw):
+    q, k, v, g, beta, S0, o, S_T, S_hist = _ptrs(9)
+    a = dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, o=o, S_T=S_T, S_hist=S_hist,
+             N=4, M=3, H=3, K=128, V=128, dtype=1, gate=1)
+    a.update(kw)
+    return L.gdn_recurrent_steps(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["o"],
+                                 a["S_T"], a["S_hist"], a["N"], a["M"], a["H"], a["K"], a["V"],
+                                 a["dtype"], a["gate"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=2), dict(gate=3), dict(N=-1), dict(M=-1), dict(H=-1), dict(K=0), dict(V=-1),
+    dict(o=None, S_T=None, S_hist=None), dict(q=None), dict(v=None), dict(g=None),
+    dict(beta=None), dict(q=BASE + 1), dict(o=BASE + 6 * SEP + 1), dict(g=BASE + 3 * SEP + 2),
+    dict(S0=BASE + 5 * SEP + 8), dict(S_T=BASE + 7 * SEP + 4), dict(S_hist=BASE + 8 * SEP + 8),
+    dict(o=BASE + 5 * SEP),             # o aliases S0
+    dict(S_hist=BASE + 7 * SEP),        # S_hist aliases S_T
+    dict(S_hist=BASE + 2 * SEP + 64),   # S_hist overlaps v
+    dict(S_T=BASE),                     # S_T aliases q
+    dict(S_T=BASE + 5 * SEP + 16),      # S_T partially overlaps S0
+    dict(N=1 << 30, M=1 << 30, H=1 << 30),  # size overflow
+])
+def test_steps_rejects_invalid(L, kw):
+    assert _steps(L, **kw) == gdn.GDN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(K=32), dict(V=256), dict(K=96, dtype=0)])
+def test_steps_unsupported(L, kw):
+    assert _steps(L, **kw) == gdn.GDN_ENOTSUP
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(H=0), dict(M=0, S_T=None),
+                                dict(N=0, q=None, k=None, v=None, g=None, beta=None, S0=None)])
+def test_steps_empty_is_a_noop(L, kw):
+    assert _steps(L, **kw) == gdn.GDN_OK
+
+
+def test_steps_in_place_state_passes_validation(L):
+    # S_T == S0 is allowed; an unsupported K stops the call right after the checks
+    assert _steps(L, S_T=BASE + 5 * SEP, K=32) == gdn.GDN_ENOTSUP
 
 
 def test_element_aligned_vectors_are_accepted_by_validation(L):
