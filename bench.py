@@ -37,13 +37,22 @@ CSRC = os.path.join(ROOT, "gated_deltanet_layer_amd", "csrc")
 MEASURED_TRAFFIC = {
     "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
                                   "mfma_frag.h"),
-                                 "d0587a5fc5e60ae6", 868861033),
+                                 "4bfeabc03baca055", 862346361),
     # the B=16 H=8 T=2048 channel-gate case (o and S_T written)
     "chunk_fwd_wsc_kernel<128>": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                    "mfma_frag.h"),
-                                  "721cac350622c52a", 420161311),
+                                  "aea3bbff97305fd5", 420122323),
+    # the B=1 H=48 T=262144 channel-gate case (S_T only, from a random S0)
+    "chunk_fwd_wsc_kernel<128>/long": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
+                                        "mfma_frag.h"),
+                                       "aea3bbff97305fd5", 16671410339),
     "recurrent_step_kernel<bf16,128,128,channel>": (("recurrent_step.hip", "gdn_common.h"),
-                                                    "1864f0aa1a777d85", 1642879592),
+                                                    "1864f0aa1a777d85", 1642881106),
+    # M = 4 draft tokens on the decode shape: final state only / every token's state
+    "recurrent_multi_kernel<bf16,128,128,channel>/final": (("recurrent_multi.hip", "gdn_common.h"),
+                                                           "e96c18f898c72e85", 1739636872),
+    "recurrent_multi_kernel<bf16,128,128,channel>/hist": (("recurrent_multi.hip", "gdn_common.h"),
+                                                          "e96c18f898c72e85", 4158922376),
 }
 
 
@@ -147,7 +156,7 @@ def bench_channel(torch, gdn, name, steps, warmup):
                         ", fp32 g/beta/state" + (", returns S_T only from a random S0" if not want_o else ", S0=0"),
             "ms": ms, "mtok_s": B * T / (ms / 1e3) / 1e6, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
             "bytes_per_launch": nbytes, "kernel": "chunk_fwd_wsc_kernel<128>",
-            "traffic": measured_traffic("chunk_fwd_wsc_kernel<128>") if want_o else None,
+            "traffic": measured_traffic("chunk_fwd_wsc_kernel<128>" + ("" if want_o else "/long")),
             "steps": steps, "warmup": warmup}
 
 
@@ -214,6 +223,8 @@ def bench_verify(torch, gdn, M, keep_hist, reps, warmup):
                         + ("state after every token kept" if keep_hist else "final state written"),
             "M": M, "ms": ms, "tokens_per_s": N * M / (ms / 1e3), "gbs": gbs,
             "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_call": nbytes,
+            "traffic": measured_traffic("recurrent_multi_kernel<bf16,128,128,channel>/"
+                                        + ("hist" if keep_hist else "final")),
             "kernel": "recurrent_multi_kernel<bf16,128,128,channel>"}
 
 
