@@ -1,4 +1,4 @@
-"""Gated DeltaNet mixer forward on MI355X (gfx950): Python binding of libgdn.so.
+"""Gated DeltaNet mixer on MI355X (gfx950): Python binding of libgdn.so.
 
 The work runs in the HIP kernels behind the C ABI declared in ``include/gdn.h``;
 this module only checks tensors, marshals pointers and sizes, and passes the
@@ -9,9 +9,12 @@ Entry points (same names as the C ABI):
     gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk=64)
     gdn_recurrent_step(q, k, v, g, beta, S, o)
     gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist)
+    gdn_chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace)
+    gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk=64) -> bytes
 Conveniences that allocate the outputs:
     chunk_fwd(q, k, v, g, beta, S0=None, want_o=True) -> (o, S_T)
     recurrent_step_(q, k, v, g, beta, S) -> o      (S updated in place)
+    chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T) -> dict of dq, dk, dv, dg, dbeta, dS0
 """
 from __future__ import annotations
 
@@ -25,7 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_OK, GDN_EINVAL, GDN_ENOTSUP, GDN_EHIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_HEAD, GDN_GATE_CHANNEL = 0, 1
-SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_steps", "gdn_status_str",
+SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_steps",
+           "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_status_str",
            "gdn_abi_version")
 
 _lock = threading.Lock()
@@ -59,6 +63,12 @@ def lib() -> ctypes.CDLL:
         L.gdn_recurrent_steps.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp,
                                           i, i, i, i, i, i, i, vp]
         L.gdn_recurrent_steps.restype = i
+        sz = ctypes.c_size_t
+        L.gdn_chunk_bwd_workspace_size.argtypes = [i, i, i, i, i, i, ctypes.POINTER(sz)]
+        L.gdn_chunk_bwd_workspace_size.restype = i
+        L.gdn_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp,
+                                    vp, sz, i, i, i, i, i, i, i, i, vp]
+        L.gdn_chunk_bwd.restype = i
         L.gdn_status_str.argtypes = [i]
         L.gdn_status_str.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -212,6 +222,75 @@ def gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist=None, stream=None) 
                                    _dtype_code(q), gate, _stream(stream))
     if rc != GDN_OK:
         raise GDNError(rc, "gdn_recurrent_steps")
+
+
+def gdn_chunk_bwd_workspace_size(B: int, T: int, H: int, K: int, V: int, chunk: int = 64) -> int:
+    """Bytes of device workspace gdn_chunk_bwd needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    rc = lib().gdn_chunk_bwd_workspace_size(B, T, H, K, V, int(chunk), ctypes.byref(n))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_bwd_workspace_size")
+    return int(n.value)
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace,
+                  chunk: int = 64, stream=None) -> None:
+    """Chunkwise backward: gradients of a loss through gdn_chunk_fwd's operation.
+
+    Inputs as for gdn_chunk_fwd plus d_o [B,T,H,V] (q's dtype) and dS_T [B,H,K,V] fp32
+    (or None).  Writes dq, dk [B,T,H,K] and dv [B,T,H,V] (q's dtype), dg (g's shape)
+    and dbeta [B,T,H] fp32, and dS0 [B,H,K,V] fp32 (or None).  ``workspace`` is a
+    device tensor of at least gdn_chunk_bwd_workspace_size(...) bytes.
+    """
+    import torch
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, D]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    dt = q.dtype
+    _check(q, "q", dtype=dt)
+    for t, name in ((k, "k"), (dq, "dq"), (dk, "dk")):
+        _check(t, name, (B, T, H, K), dt, dev)
+    for t, name in ((v, "v"), (d_o, "d_o"), (dv, "dv")):
+        _check(t, name, (B, T, H, V), dt, dev)
+    gshape = (B, T, H, K) if g.dim() == 4 else (B, T, H)
+    gate = GDN_GATE_CHANNEL if g.dim() == 4 else GDN_GATE_HEAD
+    _check(g, "g", gshape, torch.float32, dev)
+    _check(dg, "dg", gshape, torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    _check(dbeta, "dbeta", (B, T, H), torch.float32, dev)
+    for t, name in ((S0, "S0"), (dS_T, "dS_T"), (dS0, "dS0")):
+        _check(t, name, (B, H, K, V), torch.float32, dev)
+    _check(workspace, "workspace", device=dev)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                             _ptr(d_o), _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                             _ptr(dbeta), _ptr(dS0), _ptr(workspace), nbytes,
+                             B, T, H, K, V, int(chunk), _dtype_code(q), gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_bwd")
+
+
+def chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T, want_dS0: bool = True, workspace=None,
+              chunk: int = 64, stream=None):
+    """Allocate the gradients (and the workspace unless one is given), run
+    gdn_chunk_bwd, return a dict with dq, dk, dv, dg, dbeta, dS0."""
+    import torch
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
+               dS0=torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if want_dS0 else None)
+    if workspace is None:
+        n = gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    gdn_chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T, out["dq"], out["dk"], out["dv"], out["dg"],
+                  out["dbeta"], out["dS0"], workspace, chunk=chunk, stream=stream)
+    return out
 
 
 def chunk_fwd(q, k, v, g, beta, S0=None, want_o: bool = True, chunk: int = 64, stream=None):

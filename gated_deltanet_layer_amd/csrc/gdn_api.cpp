@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/gdn.h"
+#include "chunk_bwd.h"
 
 namespace gdn {
 hipError_t chunk_fwd_launch(bool bf16, bool channel, int K, const void *q, const void *k,
@@ -52,6 +53,22 @@ long long prod(long long a, long long b, long long c = 1, long long d = 1) {
         n *= f;
     }
     return n;
+}
+
+// Size checks shared by gdn_chunk_bwd and its workspace query: EINVAL for
+// negative or overflowing sizes, ENOTSUP for shapes without a kernel or grids
+// past the launch limits; *nch = number of 64-token chunks over all slices.
+gdn_status bwd_sizes(int B, int T, int H, int K, int V, int chunk, long long *nch) {
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0 || chunk <= 0) return GDN_EINVAL;
+    const long long nqk = prod(B, T, H, K), nv = prod(B, T, H, V), nst = prod(B, H, K, V);
+    if (nqk < 0 || nv < 0 || nst < 0) return GDN_EINVAL;
+    if (!kv_supported(K) || !kv_supported(V) || chunk != 64) return GDN_ENOTSUP;
+    const long long n = prod(B, H, (T + 63) / 64);
+    const long long nvb = prod(B, H, V / gdn::bw_vb(K));
+    // one 256-thread workgroup per chunk / per value block: grid x * 256 < 2^32
+    if (n < 0 || nvb < 0 || n >= (1LL << 24) || nvb >= (1LL << 24)) return GDN_ENOTSUP;
+    *nch = n;
+    return GDN_OK;
 }
 
 } // namespace
@@ -197,6 +214,79 @@ gdn_status gdn_recurrent_steps(const void *q, const void *k, const void *v, cons
     const hipError_t e = gdn::recurrent_multi_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL,
                                                      K, V, q, k, v, g, beta, S0, o, S_T, S_hist,
                                                      ns, M, H, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_chunk_bwd_workspace_size(int B, int T, int H, int K, int V, int chunk,
+                                        size_t *bytes)
+{
+    if (!bytes) return GDN_EINVAL;
+    long long nch = 0;
+    const gdn_status st = bwd_sizes(B, T, H, K, V, chunk, &nch);
+    if (st != GDN_OK) return st;
+    *bytes = (size_t)gdn::bw_workspace((unsigned long long)nch, K, V, nullptr, nullptr);
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *S0, const void *d_o, const float *dS_T,
+                         void *dq, void *dk, void *dv, float *dg, float *dbeta, float *dS0,
+                         void *workspace, size_t workspace_bytes, int B, int T, int H, int K,
+                         int V, int chunk, gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EINVAL;
+    if (gate != GDN_GATE_HEAD && gate != GDN_GATE_CHANNEL) return GDN_EINVAL;
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0 || chunk <= 0) return GDN_EINVAL;
+    const long long es = dtype == GDN_BF16 ? 2 : 4;
+    const long long ntok = prod(B, T, H);
+    const long long nqk = prod(B, T, H, K), nv = prod(B, T, H, V), nst = prod(B, H, K, V);
+    if (ntok < 0 || nqk < 0 || nv < 0 || nst < 0) return GDN_EINVAL;
+    const long long ng = gate == GDN_GATE_CHANNEL ? nqk : ntok;
+    if (ntok > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+        return GDN_EINVAL;
+    for (const void *p : {q, k, v, d_o, (const void *)dq, (const void *)dk, (const void *)dv})
+        if (p && !aligned(p, (unsigned)es)) return GDN_EINVAL;
+    for (const void *p : {(const void *)g, (const void *)beta, (const void *)S0,
+                          (const void *)dS_T, (const void *)dg, (const void *)dbeta,
+                          (const void *)dS0})
+        if (p && !aligned(p, 4)) return GDN_EINVAL;
+    if (workspace && !aligned(workspace, 256)) return GDN_EINVAL;
+
+    long long nch = 0;
+    const gdn_status st = bwd_sizes(B, T, H, K, V, chunk, &nch);
+    if (st == GDN_EINVAL) return st;
+    // the workspace check needs the size, which needs a supported shape
+    const unsigned long long need =
+        st == GDN_OK ? gdn::bw_workspace((unsigned long long)nch, K, V, nullptr, nullptr) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_EINVAL;
+
+    // No output may touch an input, another output or the workspace.
+    const Range in[] = {range(q, nqk * es), range(k, nqk * es), range(v, nv * es),
+                        range(g, ng * 4), range(beta, ntok * 4), range(S0, S0 ? nst * 4 : 0),
+                        range(d_o, nv * es), range(dS_T, dS_T ? nst * 4 : 0)};
+    const Range out[] = {range(dq, nqk * es), range(dk, nqk * es), range(dv, nv * es),
+                         range(dg, ng * 4), range(dbeta, ntok * 4),
+                         range(dS0, dS0 ? nst * 4 : 0), range(workspace, need)};
+    const int nout = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (Range r : in)
+            if (overlap(out[i], r)) return GDN_EINVAL;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(out[i], out[j])) return GDN_EINVAL;
+    }
+    if (st != GDN_OK) return st;   // ENOTSUP
+    if (B == 0 || H == 0) return GDN_OK;
+    if (T == 0 && !dS0) return GDN_OK;   // nothing to write
+
+    gdn::BwArgs a;
+    a.q = q; a.k = k; a.v = v; a.d_o = d_o;
+    a.g = g; a.beta = beta; a.S0 = S0; a.dS_T = dS_T;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
+    gdn::bw_workspace((unsigned long long)nch, K, V, workspace, &a.ws);
+    a.T = T; a.H = H; a.NC = (T + 63) / 64;
+    const hipError_t e = gdn::chunk_bwd_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL, K, V,
+                                               a, (long)B * H, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

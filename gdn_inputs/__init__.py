@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the Gated DeltaNet mixer forward.
+"""Seeded synthetic inputs for the Gated DeltaNet mixer (forward and backward).
 
 This module is shared by the tests, the bench and the smoke check.  It holds none
 of the method's arithmetic: it only draws random tensors and shapes them into the
@@ -12,6 +12,9 @@ card, section 2.1: g = -min(softplus(g_raw), 5), so alpha = exp(g) lies in
 Every tensor is drawn from one ``torch.Generator`` seeded once, in the fixed order
 q, k, v, beta_raw, g_raw, S0.  CPU and GPU generators give different streams;
 each test draws once and hands the same stored tensors to both sides.
+
+``grad_inputs`` draws the cotangents of a backward call (dL/do, dL/dS_T) from a
+generator of their own, so that adding them changes none of the forward inputs.
 """
 from __future__ import annotations
 
@@ -20,8 +23,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["ChunkConfig", "DecodeConfig", "CHUNK_CONFIGS", "DECODE_CONFIG",
-           "chunk_inputs", "decode_inputs", "head_tokens"]
+__all__ = ["ChunkConfig", "DecodeConfig", "CHUNK_CONFIGS", "DECODE_CONFIG", "BWD_CONFIG",
+           "chunk_inputs", "decode_inputs", "grad_inputs", "head_tokens"]
 
 
 @dataclass(frozen=True)
@@ -81,6 +84,12 @@ CHUNK_CONFIGS = {
 }
 
 DECODE_CONFIG = DecodeConfig("decode_256x48", N=256, H=48, K=128, V=128, steps=64)
+
+# forward + backward at the shape of the Atomic-GDN2 card's kernel benchmark
+# (section 5.1: batch 4, head dimension 128, up to 6 heads, 4096 tokens; the
+# log-decay domain [-5, 0] of section 5)
+BWD_CONFIG = ChunkConfig("bwd_channel_bf16", B=4, H=6, T=4096, K=128, V=128, dtype="bf16",
+                         gate="channel", g_sigma=2.0, g_cap=5.0, s0_sigma=0.02)
 
 _DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
@@ -145,3 +154,14 @@ def decode_inputs(cfg: DecodeConfig, device="cpu", seed: Optional[int] = None):
     S0 = cfg.s_sigma * torch.randn(N, H, K, V, **f32)
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), g=g,
                 beta=beta.contiguous(), S0=S0.contiguous())
+
+
+def grad_inputs(cfg: ChunkConfig, device="cpu", seed: Optional[int] = None):
+    """Cotangents of one backward call: d_o [B,T,H,V] (storage dtype) ~ N(0, 1) and
+    dS_T [B,H,K,V] fp32 ~ N(0, 1), from a generator seeded with seed + 7919."""
+    device = torch.device(device)
+    gen = _gen(device, (cfg.seed if seed is None else seed) + 7919)
+    f32 = dict(device=device, dtype=torch.float32, generator=gen)
+    d_o = torch.randn(cfg.B, cfg.T, cfg.H, cfg.V, **f32).to(_DT[cfg.dtype])
+    dS_T = torch.randn(cfg.B, cfg.H, cfg.K, cfg.V, **f32)
+    return dict(d_o=d_o.contiguous(), dS_T=dS_T.contiguous())

@@ -1,5 +1,5 @@
 /*
- * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet mixer forward.
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet mixer: forward and backward.
  *
  * The operation (Atomic-GDN2 model card, section 2.1 "Gated DeltaNet-2"), for
  * every batch row b and head h independently, token by token:
@@ -27,7 +27,8 @@
  *    row-major in the layouts given, aligned to their element size.  The
  *    streamed operands need 16 bytes: q, k, v, o and a per-channel g of
  *    gdn_chunk_fwd, and S of gdn_recurrent_step.  The library allocates nothing
- *    and keeps no state between calls.
+ *    and keeps no state between calls (gdn_chunk_bwd takes a caller-provided
+ *    workspace).
  *  - q, k, v and o share one storage type (gdn_dtype).  g, beta and every state
  *    tensor are fp32.  Arithmetic is fp32 with fp32 accumulation; for
  *    GDN_BF16 the matrix products take bf16 operands on the MFMA units.
@@ -43,11 +44,13 @@
 #ifndef GDN_H
 #define GDN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -136,6 +139,46 @@ GDN_API gdn_status gdn_recurrent_steps(const void *q, const void *k, const void 
                                void *o, float *S_T, float *S_hist,
                                int N, int M, int H, int K, int V,
                                gdn_dtype dtype, gdn_gate gate, void *stream);
+
+/*
+ * Bytes of device workspace that gdn_chunk_bwd needs for these sizes (written
+ * to *bytes).  Same argument rules as gdn_chunk_bwd; 0 for an empty problem.
+ */
+GDN_API gdn_status gdn_chunk_bwd_workspace_size(int B, int T, int H, int K, int V, int chunk,
+                                                size_t *bytes);
+
+/*
+ * Chunkwise backward: the gradients of a loss L through gdn_chunk_fwd's
+ * operation, given dL/do and dL/dS_T (the card's kernel benchmark, section 5.1
+ * of the Atomic-GDN2 model card, times forward and backward together; training
+ * runs the chunk mode).  Same inputs as the forward; the forward's outputs are
+ * not needed (the states are recomputed).
+ *
+ *   q, k, v, g, beta, S0   as for gdn_chunk_fwd (S0 may be NULL = zeros)
+ *   d_o   [B, T, H, V]   dtype    dL/do
+ *   dS_T  [B, H, K, V]   fp32     dL/dS_T, or NULL for zeros
+ *   dq, dk [B, T, H, K]  dtype    outputs
+ *   dv    [B, T, H, V]   dtype    output
+ *   dg    shaped as g,   fp32     dL/dg (the log-decay)
+ *   dbeta [B, T, H]      fp32
+ *   dS0   [B, H, K, V]   fp32     dL/dS0, or NULL if not wanted
+ *   workspace            device memory of at least workspace_bytes >=
+ *                        gdn_chunk_bwd_workspace_size(...) bytes, 256-byte
+ *                        aligned, owned by the caller; its contents on entry
+ *                        do not matter and on return are unspecified.
+ *
+ * K and V: 64 or 128; chunk: 64; dtype GDN_F32 or GDN_BF16 (the arithmetic is
+ * fp32 for both).  Every pointer needs its element alignment.  No output may
+ * overlap an input, another output or the workspace.  B, T or H equal to 0 is a
+ * valid call (T = 0: dS0 receives dS_T, or zeros).  Calls that share one
+ * workspace must not run concurrently.
+ */
+GDN_API gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *S0, const void *d_o,
+                                 const float *dS_T, void *dq, void *dk, void *dv, float *dg,
+                                 float *dbeta, float *dS0, void *workspace,
+                                 size_t workspace_bytes, int B, int T, int H, int K, int V,
+                                 int chunk, gdn_dtype dtype, gdn_gate gate, void *stream);
 
 /* Static English text for a status code (never NULL). */
 GDN_API const char *gdn_status_str(gdn_status s);

@@ -41,7 +41,7 @@ def test_only_declared_symbols_are_exported():
 
 
 def test_version_and_status_strings(L):
-    assert gdn.abi_version() == 2
+    assert gdn.abi_version() == 3
     assert gdn.status_str(0) == "ok"
     assert "invalid" in gdn.status_str(1)
     assert "unsupported" in gdn.status_str(2)
@@ -170,6 +170,80 @@ def test_steps_empty_is_a_noop(L, kw):
 def test_steps_in_place_state_passes_validation(L):
     # S_T == S0 is allowed; an unsupported K stops the call right after the checks
     assert _steps(L, S_T=BASE + 5 * SEP, K=32) == gdn.GDN_ENOTSUP
+
+
+def _bwd(L, ws_bytes=None, **kw):
+    p = _ptrs(16)
+    a = dict(q=p[0], k=p[1], v=p[2], g=p[3], beta=p[4], S0=p[5], d_o=p[6], dS_T=p[7],
+             dq=p[8], dk=p[9], dv=p[10], dg=p[11], dbeta=p[12], dS0=p[13], ws=p[14],
+             B=2, T=100, H=3, K=128, V=128, chunk=64, dtype=1, gate=1)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = SEP   # large enough for these sizes
+    return L.gdn_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["d_o"],
+                           a["dS_T"], a["dq"], a["dk"], a["dv"], a["dg"], a["dbeta"], a["dS0"],
+                           a["ws"], ws_bytes, a["B"], a["T"], a["H"], a["K"], a["V"],
+                           a["chunk"], a["dtype"], a["gate"], None)
+
+
+def _ws_size(L, B, T, H, K, V, chunk=64):
+    import ctypes
+    n = ctypes.c_size_t(12345)
+    rc = L.gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk, ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=2), dict(gate=2), dict(B=-1), dict(T=-1), dict(H=-1), dict(K=0), dict(V=-1),
+    dict(chunk=0), dict(q=None), dict(d_o=None), dict(dq=None), dict(dg=None), dict(dbeta=None),
+    dict(ws=None), dict(q=BASE + 1), dict(dv=BASE + 10 * SEP + 1), dict(g=BASE + 3 * SEP + 2),
+    dict(dS0=BASE + 13 * SEP + 2), dict(ws=BASE + 14 * SEP + 64),
+    dict(dq=BASE),                      # dq aliases q
+    dict(dv=BASE + 6 * SEP + 64),       # dv overlaps d_o
+    dict(dg=BASE + 12 * SEP),           # dg aliases dbeta
+    dict(dS0=BASE + 5 * SEP),           # dS0 aliases S0
+    dict(ws=BASE + 13 * SEP),           # workspace over dS0
+    dict(dbeta=BASE + 14 * SEP + 256),  # an output inside the workspace
+    dict(B=1 << 30, T=1 << 30, H=1 << 30),
+])
+def test_bwd_rejects_invalid(L, kw):
+    assert _bwd(L, **kw) == gdn.GDN_EINVAL
+
+
+def test_bwd_rejects_small_workspace(L):
+    rc, need = _ws_size(L, 2, 100, 3, 128, 128)
+    assert rc == gdn.GDN_OK and need > 0
+    assert _bwd(L, ws_bytes=need - 1) == gdn.GDN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(K=96), dict(V=32), dict(chunk=32), dict(K=256, dtype=0)])
+def test_bwd_unsupported(L, kw):
+    assert _bwd(L, **kw) == gdn.GDN_ENOTSUP
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=0, dS0=None),
+                                dict(B=0, q=None, k=None, v=None, g=None, beta=None, d_o=None,
+                                     dq=None, dk=None, dv=None, dg=None, dbeta=None, ws=None)])
+def test_bwd_empty_is_a_noop(L, kw):
+    assert _bwd(L, **kw) == gdn.GDN_OK
+
+
+def test_bwd_workspace_size(L):
+    import ctypes
+    assert L.gdn_chunk_bwd_workspace_size(1, 64, 1, 128, 128, 64, None) == gdn.GDN_EINVAL
+    assert _ws_size(L, 1, 64, 1, 96, 128)[0] == gdn.GDN_ENOTSUP
+    assert _ws_size(L, 1, 64, 1, 128, 128, chunk=32)[0] == gdn.GDN_ENOTSUP
+    assert _ws_size(L, -1, 64, 1, 128, 128)[0] == gdn.GDN_EINVAL
+    assert _ws_size(L, 3, 0, 2, 128, 128) == (gdn.GDN_OK, 0)
+    # fifteen fp32 arrays over the chunks, each rounded up to 256 bytes
+    for B, T, H, K, V in [(1, 1, 1, 64, 64), (2, 100, 3, 128, 64), (4, 4096, 6, 128, 128)]:
+        nch = B * H * ((T + 63) // 64)
+        per = [64 * K, 64 * 64, 64 * 64, 64 * 64, K * V, K * V, 64 * V, 64 * V,
+               64 * K, 64 * K, 64 * K, 64 * 64, 64 * 64, K, 64]
+        want = sum((nch * x * 4 + 255) // 256 * 256 for x in per)
+        assert _ws_size(L, B, T, H, K, V) == (gdn.GDN_OK, want)
+        assert gdn.gdn_chunk_bwd_workspace_size(B, T, H, K, V) == want
+    assert ctypes.sizeof(ctypes.c_size_t) == 8
 
 
 def test_element_aligned_vectors_are_accepted_by_validation(L):
