@@ -228,6 +228,62 @@ def bench_verify(torch, gdn, M, keep_hist, reps, warmup):
             "kernel": "recurrent_multi_kernel<bf16,128,128,channel>"}
 
 
+def bwd_bytes(B, T, H, K, V, es, channel):
+    """Algorithmic HBM bytes of one chunkwise backward: q, k, v, g, beta, S0, d_o and
+    dS_T read once, dq, dk, dv, dg, dbeta and dS0 written once."""
+    gb = (K if channel else 1) * 4
+    per_ht = (2 * K + 2 * V) * es + gb + 4          # q, k, v, d_o, g, beta
+    per_ht += (2 * K + V) * es + gb + 4             # dq, dk, dv, dg, dbeta
+    return B * T * H * per_ht + 3 * B * H * K * V * 4
+
+
+def bench_bwd(torch, gdn, steps, warmup):
+    """gdn_chunk_bwd at the card's kernel-benchmark shape (B=4 H=6 T=4096,
+    d_k = d_v = 128, per-channel gate in [-5, 0], bf16), alone and after the
+    forward (the card times forward and backward together)."""
+    from gdn_inputs import BWD_CONFIG, chunk_inputs, grad_inputs
+    cfg = BWD_CONFIG
+    d = chunk_inputs(cfg, device="cuda")
+    gr = grad_inputs(cfg, device="cuda")
+    B, T, H, K, V = cfg.B, cfg.T, cfg.H, cfg.K, cfg.V
+    nws = gdn.gdn_chunk_bwd_workspace_size(B, T, H, K, V)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    g = dict(dq=torch.empty_like(d["q"]), dk=torch.empty_like(d["k"]), dv=torch.empty_like(d["v"]),
+             dg=torch.empty_like(d["g"]), dbeta=torch.empty_like(d["beta"]),
+             dS0=torch.empty_like(d["S0"]))
+    o = torch.empty_like(d["v"])
+    S_T = torch.empty_like(d["S0"])
+    bwd = lambda: gdn.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], gr["d_o"],
+                                    gr["dS_T"], g["dq"], g["dk"], g["dv"], g["dg"], g["dbeta"],
+                                    g["dS0"], ws)
+    fwd = lambda: gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o, S_T)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_bwd = timed(bwd)
+    ms_fb = timed(lambda: (fwd(), bwd()))
+    nbytes = bwd_bytes(B, T, H, K, V, 2, True)
+    gbs = nbytes / (ms_bwd / 1e3) / 1e9
+    return {"workload": f"chunkwise backward, B={B} H={H} T={T} d_k=d_v={K} chunk=64, per-channel "
+                        f"gate, bf16 q/k/v/do and dq/dk/dv, fp32 g/beta/states and their gradients, "
+                        f"dL/do and dL/dS_T ~ N(0, 1)",
+            "ms": ms_bwd, "ms_fwd_bwd": ms_fb, "mtok_s_fwd_bwd": B * T / (ms_fb / 1e3) / 1e6,
+            "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_call": nbytes,
+            "workspace_bytes": nws, "steps": steps, "warmup": warmup,
+            "kernels": ["bwd_prep_kernel", "bwd_states_kernel", "bwd_dstates_kernel",
+                        "bwd_vgrad_kernel", "bwd_kgrad_kernel"]}
+
+
 def cpu_baseline(chunk_inputs_dev, cfg, target_s=15.0):
     """fp64 oracle on a bounded sample of the prefill workload: whole sequences of
     some (b, h) slices, one OpenMP thread per slice."""
@@ -263,7 +319,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "channel", "verify"], default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "channel", "verify", "bwd"],
+                    default="all")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -340,6 +397,12 @@ def main():
             out["value"] = first["mtok_s"]
             out["ms_per_step"] = first["ms"]
             out["config"] = {"workload": first["workload"]}
+    if args.only in ("all", "bwd"):
+        out["backward"] = bench_bwd(torch, gdn, max(2, min(args.steps, 20)), max(1, min(args.warmup, 5)))
+        if ch is None and args.only == "bwd":
+            out["value"] = out["backward"]["mtok_s_fwd_bwd"]
+            out["ms_per_step"] = out["backward"]["ms_fwd_bwd"]
+            out["config"] = {"workload": out["backward"]["workload"]}
     if ch is not None and not args.no_cpu:
         torch.cuda.synchronize()
         cb = cpu_baseline(ch["inputs"], ch["cfg"])

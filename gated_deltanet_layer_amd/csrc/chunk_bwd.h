@@ -7,16 +7,17 @@
 
 namespace gdn {
 
-// value columns per workgroup in the two state sweeps (K x VB = 2048 floats)
-constexpr int bw_vb(int K) { return 2048 / K; }
+// value columns per workgroup in the two state sweeps
+constexpr int BW_VB = 16;
 
 // fp32 intermediates, each an array over the B*H*ceil(T/64) chunks
 // (chunk ci = (b H + h) NC + c), rows of a chunk contiguous:
 struct BwWs {
     float *gam;   // [64][K]  in-chunk cumulative log-decay
     float *Tm;    // [64][64] (I + diag(beta) G)^{-1}
+    float *TT;    // [64][64] its transpose
     float *Gm;    // [64][64] G, strictly lower
-    float *Pm;    // [64][64] P, lower with the diagonal
+    float *PT;    // [64][64] P^T (P lower with the diagonal)
     float *hS;    // [K][V]   state entering the chunk
     float *dhS;   // [K][V]   dL/d(state leaving the chunk)
     float *Dl;    // [64][V]  Delta
@@ -28,6 +29,12 @@ struct BwWs {
     float *dT;    // [64][64] dDelta (beta V)^T
     float *dgn;   // [K]      e^{gn} rowsum(S * dS')
     float *dbv;   // [64]     rowsum(V * T^T dDelta)
+    float *Kp;    // [64][K]  k e^{gamma}
+    float *Km;    // [64][K]  k e^{gn - gamma}
+    float *KpT;   // [K][64]  Kp^T
+    float *KmT;   // [K][64]  Km^T
+    float *QpT;   // [K][64]  (q e^{gamma})^T
+    float *egn;   // [K]      e^{gn}
 };
 
 struct BwArgs {
@@ -45,17 +52,20 @@ inline unsigned long long bw_workspace(unsigned long long nchunks, int K, int V,
                                        BwWs *ws)
 {
     const unsigned long long C = 64, Ku = (unsigned)K, Vu = (unsigned)V;
-    const unsigned long long per[15] = {C * Ku, C * C, C * C, C * C, Ku * Vu, Ku * Vu, C * Vu,
-                                        C * Vu, C * Ku, C * Ku, C * Ku, C * C, C * C, Ku, C};
-    float **dst[15] = {nullptr};
+    constexpr int NA = 22;
+    const unsigned long long per[NA] = {C * Ku, C * C, C * C, C * C, C * C, Ku * Vu, Ku * Vu,
+                                        C * Vu, C * Vu, C * Ku, C * Ku, C * Ku, C * C, C * C,
+                                        Ku, C, C * Ku, C * Ku, C * Ku, C * Ku, C * Ku, Ku};
+    float **dst[NA] = {nullptr};
     if (ws) {
-        float **p[15] = {&ws->gam, &ws->Tm, &ws->Gm, &ws->Pm, &ws->hS, &ws->dhS, &ws->Dl,
-                         &ws->dDl, &ws->dQp, &ws->dKm, &ws->dWn, &ws->dP, &ws->dT, &ws->dgn,
-                         &ws->dbv};
-        for (int i = 0; i < 15; ++i) dst[i] = p[i];
+        float **p[NA] = {&ws->gam, &ws->Tm, &ws->TT, &ws->Gm, &ws->PT, &ws->hS, &ws->dhS,
+                         &ws->Dl, &ws->dDl, &ws->dQp, &ws->dKm, &ws->dWn, &ws->dP, &ws->dT,
+                         &ws->dgn, &ws->dbv, &ws->Kp, &ws->Km, &ws->KpT, &ws->KmT, &ws->QpT,
+                         &ws->egn};
+        for (int i = 0; i < NA; ++i) dst[i] = p[i];
     }
     unsigned long long off = 0;
-    for (int i = 0; i < 15; ++i) {
+    for (int i = 0; i < NA; ++i) {
         if (ws && base) *dst[i] = reinterpret_cast<float *>(static_cast<char *>(base) + off);
         off += (nchunks * per[i] * 4 + 255) / 256 * 256;
     }

@@ -37,9 +37,12 @@
 // only on column j), which is what lets 2 and 3 run one workgroup per block of
 // value columns.  Intermediates live in a caller-provided fp32 workspace.
 //
-// Products are LDS-tiled fp32 FMAs: each thread owns a small output tile whose
-// rows and columns are interleaved across the workgroup, so that the operand
-// reads of a wave hit consecutive or odd-strided LDS addresses.
+// The two sweeps run their products on the fp32 matrix cores (16 x 16 x 4),
+// with the per-chunk operands streamed from the workspace into registers one
+// chunk ahead.  The per-chunk kernels use LDS-tiled fp32 FMAs: each thread owns
+// a small output tile whose rows and columns are interleaved across the
+// workgroup, so that the operand reads of a wave hit consecutive or odd-strided
+// LDS addresses.  Every load of a tile is issued before the first is used.
 #include "gdn_common.h"
 #include "chunk_bwd.h"
 
@@ -87,6 +90,55 @@ __device__ __forceinline__ long tok_row(const BwArgs &a, int sl, int t)
     return (b * a.T + t) * a.H + h;
 }
 
+// Registers holding an R x W tile of a row-major global array (row stride gs
+// elements), fetched with 16-byte loads that are all issued before any is used,
+// and stored to LDS as fp32 (row stride ls).  Rows at or past nrows read as zero.
+template <typename T, int R, int W> struct TileRegs {
+    static constexpr int VE = 16 / (int)sizeof(T);
+    static constexpr int VPR = W / VE, NV = R * VPR, PER = (NV + BW_NTHR - 1) / BW_NTHR;
+    static_assert(W % VE == 0, "row width");
+    typedef T vec __attribute__((ext_vector_type(VE)));
+    vec r[PER];
+    __device__ __forceinline__ void load(const T *src, long gs, int nrows) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * BW_NTHR;
+            const int row = v / VPR, col = (v % VPR) * VE;
+            if ((NV % BW_NTHR == 0 || v < NV) && row < nrows)
+                r[i] = *reinterpret_cast<const vec *>(src + row * gs + col);
+            else
+                r[i] = vec{};
+        }
+    }
+    // LOWER: keep the entries with column <= row, zero the rest
+    template <bool LOWER = false> __device__ __forceinline__ void store(float *dst, int ls) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * BW_NTHR;
+            if (NV % BW_NTHR == 0 || v < NV) {
+                const int row = v / VPR, col = (v % VPR) * VE;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    const float x = to_f32(r[i][e]);
+                    dst[row * ls + col + e] = (!LOWER || col + e <= row) ? x : 0.f;
+                }
+            }
+        }
+    }
+};
+
+// Store an R x W fp32 LDS tile (row stride ls) to global rows gs floats apart,
+// four columns per 16-byte store.
+template <int R, int W>
+__device__ __forceinline__ void store_tile(float *dst, long gs, const float *src, int ls)
+{
+    for (int v = threadIdx.x; v < R * W / 4; v += BW_NTHR) {
+        const int row = v / (W / 4), col = (v % (W / 4)) * 4;
+        const float *s = src + row * ls + col;
+        *reinterpret_cast<f32x4 *>(dst + row * gs + col) = f32x4{s[0], s[1], s[2], s[3]};
+    }
+}
+
 // ---------------------------------------------------------------- 1 prep
 template <typename DT, int K, bool CH>
 __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
@@ -94,47 +146,84 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
     constexpr int C = BW_C, KP = K + 1, CP = C + 1;
     extern __shared__ __attribute__((aligned(256))) float sm[];
     float *sk = sm, *sq = sk + C * KP, *sg = sq + C * KP, *sA = sg + C * KP, *sT = sA + C * CP;
-    float *sb = sT + C * CP;
+    float *sb = sT + C * CP, *sgs = sb + C;
     const int tid = threadIdx.x;
     const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
     const int t0 = c * C, n = min(C, a.T - t0);
     const long ci = (long)sl * a.NC + c;
-    const DT *q = (const DT *)a.q, *k = (const DT *)a.k;
-
-    for (int idx = tid; idx < C * K; idx += BW_NTHR) {
-        const int t = idx / K, x = idx % K;
-        float kv = 0.f, qv = 0.f, gv = 0.f;
-        if (t < n) {
-            const long r = tok_row(a, sl, t0 + t);
-            kv = to_f32(k[r * K + x]);
-            qv = to_f32(q[r * K + x]);
-            gv = CH ? a.g[r * K + x] : a.g[r];
+    const long H = a.H, r0 = tok_row(a, sl, t0);   // token t of the chunk: row r0 + t H
+    {
+        TileRegs<DT, C, K> tk, tq;
+        tk.load((const DT *)a.k + r0 * K, H * K, n);
+        tq.load((const DT *)a.q + r0 * K, H * K, n);
+        if (CH) {
+            TileRegs<float, C, K> tg;
+            tg.load(a.g + r0 * K, H * K, n);
+            tg.store(sg, KP);
+        } else if (tid < C) {
+            sgs[tid] = tid < n ? a.g[r0 + tid * H] : 0.f;
         }
-        sk[t * KP + x] = kv;
-        sq[t * KP + x] = qv;
-        sg[t * KP + x] = gv;
+        if (tid < C) sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
+        tk.store(sk, KP);
+        tq.store(sq, KP);
     }
-    if (tid < C) sb[tid] = tid < n ? a.beta[tok_row(a, sl, t0 + tid)] : 0.f;
-    __syncthreads();
+    lds_barrier();
     if (tid < K) {   // gamma: running sum over the chunk, one channel per thread
         float acc = 0.f;
         for (int t = 0; t < C; ++t) {
-            acc += sg[t * KP + tid];
+            acc += CH ? sg[t * KP + tid] : sgs[t];
             sg[t * KP + tid] = acc;
         }
     }
-    __syncthreads();
-    float *gam = a.ws.gam + ci * (C * K);
-    for (int idx = tid; idx < C * K; idx += BW_NTHR) gam[idx] = sg[(idx / K) * KP + idx % K];
+    lds_barrier();
+    {   // gamma and the row-scaled operands, by rows (gamma, Kp, Km) and
+        // transposed (Kp^T, Km^T, Qp^T); e^{gn}
+        float *gam = a.ws.gam + ci * (C * K), *Kp = a.ws.Kp + ci * (C * K);
+        float *Km = a.ws.Km + ci * (C * K);
+        for (int v = tid; v < C * K / 4; v += BW_NTHR) {
+            const int t = v / (K / 4), x = (v % (K / 4)) * 4;
+            f32x4 g4, kp, km;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float gm = sg[t * KP + x + e], gn = sg[(C - 1) * KP + x + e];
+                g4[e] = gm;
+                kp[e] = sk[t * KP + x + e] * __expf(gm);
+                km[e] = sk[t * KP + x + e] * __expf(gn - gm);
+            }
+            *reinterpret_cast<f32x4 *>(gam + t * K + x) = g4;
+            *reinterpret_cast<f32x4 *>(Kp + t * K + x) = kp;
+            *reinterpret_cast<f32x4 *>(Km + t * K + x) = km;
+        }
+        float *KpT = a.ws.KpT + ci * (K * C), *KmT = a.ws.KmT + ci * (K * C);
+        float *QpT = a.ws.QpT + ci * (K * C);
+        for (int v = tid; v < C * K / 4; v += BW_NTHR) {
+            const int x = v / (C / 4), t = (v % (C / 4)) * 4;
+            const float gn = sg[(C - 1) * KP + x];
+            f32x4 kp, km, qp;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float gm = sg[(t + e) * KP + x], eg = __expf(gm);
+                kp[e] = sk[(t + e) * KP + x] * eg;
+                qp[e] = sq[(t + e) * KP + x] * eg;
+                km[e] = sk[(t + e) * KP + x] * __expf(gn - gm);
+            }
+            *reinterpret_cast<f32x4 *>(KpT + x * C + t) = kp;
+            *reinterpret_cast<f32x4 *>(KmT + x * C + t) = km;
+            *reinterpret_cast<f32x4 *>(QpT + x * C + t) = qp;
+        }
+        if (tid < K) a.ws.egn[ci * K + tid] = __expf(sg[(C - 1) * KP + tid]);
+    }
 
-    // G and P over the pairs s <= t (2080 of them), one pair per thread at a time
-    float *Gm = a.ws.Gm + ci * (C * C), *Pm = a.ws.Pm + ci * (C * C);
+    // G and P over the pairs s <= t (2080 of them), one pair per thread at a time;
+    // P is stored transposed
+    float *Gm = a.ws.Gm + ci * (C * C), *PT = a.ws.PT + ci * (C * C);
     for (int p = tid; p < C * (C + 1) / 2; p += BW_NTHR) {
         int t = (int)((sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
         while (t * (t + 1) / 2 > p) --t;
         while ((t + 1) * (t + 2) / 2 <= p) ++t;
         const int s = p - t * (t + 1) / 2;
         float gk = 0.f, pq = 0.f;
+#pragma unroll 8
         for (int x = 0; x < K; ++x) {
             const float ks = sk[s * KP + x] * __expf(sg[t * KP + x] - sg[s * KP + x]);
             gk = fmaf(sk[t * KP + x], ks, gk);
@@ -142,224 +231,299 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
         }
         const float gts = s < t ? gk : 0.f;
         Gm[t * C + s] = gts;
-        Pm[t * C + s] = pq;
+        PT[s * C + t] = pq;
         sA[t * CP + s] = sb[t] * gts;
     }
     for (int idx = tid; idx < C * C; idx += BW_NTHR) {
         const int t = idx / C, s = idx % C;
         if (s > t) {
             Gm[idx] = 0.f;
-            Pm[idx] = 0.f;
+            PT[s * C + t] = 0.f;
             sA[t * CP + s] = 0.f;
         }
     }
-    __syncthreads();
-    // T = (I + A)^{-1} by forward substitution, one column per thread
+    lds_barrier();
+    // T = (I + A)^{-1} by forward substitution, one column per thread, the
+    // column held in registers (the row of A is the same for every lane)
     if (tid < C) {
         const int j = tid;
+        float col[C];
+#pragma unroll
         for (int i = 0; i < C; ++i) {
-            float acc = i == j ? 1.f : 0.f;
-            for (int s = 0; s < i; ++s) acc = fmaf(-sA[i * CP + s], sT[s * CP + j], acc);
-            sT[i * CP + j] = acc;
+            float acc0 = i == j ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int s = 0; s + 1 < i; s += 2) {
+                acc0 = fmaf(-sA[i * CP + s], col[s], acc0);
+                acc1 = fmaf(-sA[i * CP + s + 1], col[s + 1], acc1);
+            }
+            if (i & 1) acc0 = fmaf(-sA[i * CP + i - 1], col[i - 1], acc0);
+            col[i] = acc0 + acc1;
         }
+#pragma unroll
+        for (int i = 0; i < C; ++i) sT[i * CP + j] = col[i];
+        float *TT = a.ws.TT + ci * (C * C) + j * C;   // T^T row j = column j of T
+#pragma unroll
+        for (int i = 0; i < C; i += 4)
+            *reinterpret_cast<f32x4 *>(TT + i) = f32x4{col[i], col[i + 1], col[i + 2], col[i + 3]};
     }
-    __syncthreads();
-    float *Tm = a.ws.Tm + ci * (C * C);
-    for (int idx = tid; idx < C * C; idx += BW_NTHR) Tm[idx] = sT[(idx / C) * CP + idx % C];
+    lds_barrier();
+    store_tile<C, C>(a.ws.Tm + ci * (C * C), C, sT, CP);
 }
 
 // ---------------------------------------------------------------- 2 states
-template <typename DT, int K, int V, bool CH>
+// MFMA helpers of the two sweeps (fp32, 16 x 16 x 4).  Lane l = 16 gq + r.  An
+// A fragment is a lane's share of 16 rows: row r, the contraction indices
+// 16 a + 4 gq + e (a < NA, e < 4), loaded as float4 from a row of a row-major
+// array.  B comes from an LDS tile stored transposed (Bt[col][k]), so a lane's
+// four k values for column r are one float4.  Accumulators hold rows 4 gq + e
+// of column r, which is again four consecutive k values of a transposed tile.
+template <int NA> __device__ __forceinline__ void ld_afrag(f32x4 *f, const float *row)
+{
+    const int gq = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int a = 0; a < NA; ++a) f[a] = *reinterpret_cast<const f32x4 *>(row + 16 * a + 4 * gq);
+}
+
+template <int NA>
+__device__ __forceinline__ f32x4 mma_rows(f32x4 acc, const f32x4 *f, const float *Bt, int ldb)
+{
+    const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(Bt + r * ldb + 16 * a + 4 * gq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(f[a][e], b[e], acc);
+    }
+    return acc;
+}
+
+// Store a K x 16 block held transposed in LDS (St[y][x], row stride ls) to
+// global rows V floats apart (dst points at column v0 of row 0).
+template <int K, int V>
+__device__ __forceinline__ void store_state_block(float *dst, const float *St, int ls)
+{
+    for (int v = threadIdx.x; v < K * 4; v += BW_NTHR) {
+        const int x = v >> 2, y = (v & 3) * 4;
+        *reinterpret_cast<f32x4 *>(dst + (long)x * V + y) =
+            f32x4{St[y * ls + x], St[(y + 1) * ls + x], St[(y + 2) * ls + x], St[(y + 3) * ls + x]};
+    }
+}
+
+// One workgroup per (slice, block of 16 value columns), chunks in order; wave
+// w owns rows 16 w .. 16 w + 15 of the C x 16 products and K/4 rows of the
+// state block, which stays in its accumulators.  Each A fragment is refilled
+// for the next chunk right after its last use, so those loads run under the
+// rest of the chunk; the barriers in the loop wait for LDS traffic only.
+template <typename DT, int K, int V>
 __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
 {
-    constexpr int C = BW_C, VB = bw_vb(K), KP = K + 1, CP = C + 1, VP = VB + 1, NVB = V / VB;
+    constexpr int C = BW_C, VB = 16, NVB = V / VB, KT = K / 64, LK = K + 4, LC = C + 4, VP = VB + 1;
     extern __shared__ __attribute__((aligned(256))) float sm[];
-    float *sKp = sm, *sKm = sKp + C * KP, *sT = sKm + C * KP, *sS = sT + C * CP;
-    float *sR = sS + K * VP, *sD = sR + C * VP, *sb = sD + C * VP, *sgn = sb + C;
-    const int tid = threadIdx.x;
+    float *sSt = sm;                 // [16][LK]  S, transposed
+    float *sRt = sSt + VB * LK;      // [16][LC]  R = beta (V - Kp S), transposed
+    float *sDt = sRt + VB * LC;      // [16][LC]  Delta, transposed
+    float *sV = sDt + VB * LC;       // [C][VP]   v tile
+    float *sb = sV + C * VP;         // [C]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r = lane & 15;
     const int vb = blockIdx.x % NVB, sl = blockIdx.x / NVB, v0 = vb * VB;
-    const DT *k = (const DT *)a.k, *v = (const DT *)a.v;
+    const long H = a.H;
 
-    for (int idx = tid; idx < K * VB; idx += BW_NTHR) {
-        const int x = idx / VB, y = idx % VB;
-        sS[x * VP + y] = a.S0 ? a.S0[((long)sl * K + x) * V + v0 + y] : 0.f;
+    f32x4 fKp[K / 16];       // Kp row 16 w + r
+    f32x4 fT[C / 16];        // T row 16 w + r
+    f32x4 fKm[KT][C / 16];   // Km^T rows 16 (KT w + h) + r
+    f32x4 fg[KT];            // e^{gn} of this lane's accumulator rows
+    TileRegs<DT, C, VB> pV;
+    float pb = 0.f;
+    auto fetch_kp = [&](long ci) { ld_afrag<K / 16>(fKp, a.ws.Kp + ci * (C * K) + (16 * w + r) * K); };
+    auto fetch_t = [&](long ci) { ld_afrag<C / 16>(fT, a.ws.Tm + ci * (C * C) + (16 * w + r) * C); };
+    auto fetch_km = [&](long ci) {
+#pragma unroll
+        for (int h = 0; h < KT; ++h) {
+            ld_afrag<C / 16>(fKm[h], a.ws.KmT + ci * (K * C) + (16 * (KT * w + h) + r) * C);
+            fg[h] = *reinterpret_cast<const f32x4 *>(a.ws.egn + ci * K + 16 * (KT * w + h) + 4 * gq);
+        }
+    };
+    auto fetch_v = [&](int c) {
+        const long r0 = tok_row(a, sl, c * C);
+        const int n = min(C, a.T - c * C);
+        pV.load((const DT *)a.v + r0 * V + v0, H * V, n);
+        pb = tid < n ? a.beta[r0 + tid * H] : 0.f;
+    };
+
+    f32x4 S[KT];
+#pragma unroll
+    for (int h = 0; h < KT; ++h) {
+        const int x0 = 16 * (KT * w + h) + 4 * gq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[h][e] = a.S0 ? a.S0[((long)sl * K + x0 + e) * V + v0 + r] : 0.f;
+        *reinterpret_cast<f32x4 *>(sSt + r * LK + x0) = S[h];
+    }
+    if (a.NC > 0) {
+        const long ci0 = (long)sl * a.NC;
+        fetch_kp(ci0);
+        fetch_t(ci0);
+        fetch_km(ci0);
+        fetch_v(0);
     }
     for (int c = 0; c < a.NC; ++c) {
-        const int t0 = c * C, n = min(C, a.T - t0);
         const long ci = (long)sl * a.NC + c;
-        const float *gam = a.ws.gam + ci * (C * K);
-        __syncthreads();   // the previous chunk's readers are done
-        for (int idx = tid; idx < C * K; idx += BW_NTHR) {
-            const int t = idx / K, x = idx % K;
-            const float kv = t < n ? to_f32(k[tok_row(a, sl, t0 + t) * K + x]) : 0.f;
-            const float gm = gam[idx], gn = gam[(C - 1) * K + x];
-            sKp[t * KP + x] = kv * __expf(gm);
-            sKm[t * KP + x] = kv * __expf(gn - gm);
-        }
-        if (tid < K) sgn[tid] = __expf(gam[(C - 1) * K + tid]);
-        const float *Tm = a.ws.Tm + ci * (C * C);
-        for (int idx = tid; idx < C * C; idx += BW_NTHR) sT[(idx / C) * CP + idx % C] = Tm[idx];
-        for (int idx = tid; idx < C * VB; idx += BW_NTHR) {
-            const int t = idx / VB, y = idx % VB;
-            sR[t * VP + y] = t < n ? to_f32(v[tok_row(a, sl, t0 + t) * V + v0 + y]) : 0.f;
-        }
-        if (tid < C) sb[tid] = tid < n ? a.beta[tok_row(a, sl, t0 + tid)] : 0.f;
-        float *hS = a.ws.hS + ci * (K * V);
-        for (int idx = tid; idx < K * VB; idx += BW_NTHR) {
-            const int x = idx / VB, y = idx % VB;
-            hS[x * V + v0 + y] = sS[x * VP + y];
-        }
-        __syncthreads();
-        {   // R = beta (V - Kp S), in place over the v tile
-            using TL = Tile<C, VB, 4, VB / 16>;
-            const TL tl;
-            float acc[4][VB / 16] = {};
-            mm_acc<C, VB, 4, VB / 16, K, KP, 1, VP, 1>(acc, sKp, sS, tl.mt, tl.nt);
+        const bool more = c + 1 < a.NC;
+        lds_barrier();   // S^T complete; the previous chunk's readers are done
+        pV.store(sV, VP);
+        if (tid < C) sb[tid] = pb;
+        store_state_block<K, V>(a.ws.hS + ci * (K * V) + v0, sSt, LK);   // state entering c
+        lds_barrier();
+        if (more) fetch_v(c + 1);
+        {   // R = beta (V - Kp S)
+            const f32x4 X = mma_rows<K / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, fKp, sSt, LK);
+            if (more) fetch_kp(ci + 1);
+            f32x4 R;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < VB / 16; ++j) {
-                    const int t = tl.row(i), y = tl.col(j);
-                    sR[t * VP + y] = sb[t] * (sR[t * VP + y] - acc[i][j]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * w + 4 * gq + e;
+                R[e] = sb[t] * (sV[t * VP + r] - X[e]);
+            }
+            *reinterpret_cast<f32x4 *>(sRt + r * LC + 16 * w + 4 * gq) = R;
         }
-        __syncthreads();
+        lds_barrier();
         {   // Delta = T R
-            using TL = Tile<C, VB, 4, VB / 16>;
-            const TL tl;
-            float acc[4][VB / 16] = {};
-            mm_acc<C, VB, 4, VB / 16, C, CP, 1, VP, 1>(acc, sT, sR, tl.mt, tl.nt);
-            float *Dl = a.ws.Dl + ci * (C * V);
+            const f32x4 D = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, fT, sRt, LC);
+            if (more) fetch_t(ci + 1);
+            *reinterpret_cast<f32x4 *>(sDt + r * LC + 16 * w + 4 * gq) = D;
+            float *Dl = a.ws.Dl + ci * (C * V) + v0 + r;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < VB / 16; ++j) {
-                    const int t = tl.row(i), y = tl.col(j);
-                    sD[t * VP + y] = acc[i][j];
-                    Dl[t * V + v0 + y] = acc[i][j];
-                }
+            for (int e = 0; e < 4; ++e) Dl[(16 * w + 4 * gq + e) * V] = D[e];
         }
-        __syncthreads();
-        {   // S = Diag(e^{gn}) S + Km^T Delta
-            using TL = Tile<K, VB, K / 16, VB / 16>;
-            const TL tl;
-            float acc[K / 16][VB / 16] = {};
-            mm_acc<K, VB, K / 16, VB / 16, C, 1, KP, VP, 1>(acc, sKm, sD, tl.mt, tl.nt);
+        lds_barrier();
+        // S = Diag(e^{gn}) S + Km^T Delta
 #pragma unroll
-            for (int i = 0; i < K / 16; ++i)
-#pragma unroll
-                for (int j = 0; j < VB / 16; ++j) {
-                    const int x = tl.row(i), y = tl.col(j);
-                    sS[x * VP + y] = sgn[x] * sS[x * VP + y] + acc[i][j];
-                }
+        for (int h = 0; h < KT; ++h) {
+            S[h] *= fg[h];
+            S[h] = mma_rows<C / 16>(S[h], fKm[h], sDt, LC);
         }
+        if (more) fetch_km(ci + 1);
+#pragma unroll
+        for (int h = 0; h < KT; ++h)
+            *reinterpret_cast<f32x4 *>(sSt + r * LK + 16 * (KT * w + h) + 4 * gq) = S[h];
     }
 }
 
 // ---------------------------------------------------------------- 3 dstates
-template <typename DT, int K, int V, bool CH>
+// Same layout as the forward sweep, chunks in reverse order.
+template <typename DT, int K, int V>
 __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
 {
-    constexpr int C = BW_C, VB = bw_vb(K), KP = K + 1, CP = C + 1, VP = VB + 1, NVB = V / VB;
+    constexpr int C = BW_C, VB = 16, NVB = V / VB, KT = K / 64;
+    constexpr int LK = K + 4, LC = C + 4, L2 = 2 * C + 4;
     extern __shared__ __attribute__((aligned(256))) float sm[];
-    float *sQK = sm;                 // rows 0..C-1: Qp, rows C..2C-1: Kp
-    float *sKm = sQK + 2 * C * KP, *sP = sKm + C * KP, *sT = sP + C * CP, *sdS = sT + C * CP;
-    float *sOY = sdS + K * VP;       // rows 0..C-1: dO, rows C..2C-1: -beta Y
-    float *sdD = sOY + 2 * C * VP, *sb = sdD + C * VP, *sgn = sb + C;
-    const int tid = threadIdx.x;
+    float *sdSt = sm;                // [16][LK]  dS', transposed
+    float *sOYt = sdSt + VB * LK;    // [16][L2]  columns 0..C-1: dO^T, C..2C-1: (-beta Y)^T
+    float *sdDt = sOYt + VB * L2;    // [16][LC]  dDelta, transposed
+    float *sb = sdDt + VB * LC;      // [C]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r = lane & 15;
     const int vb = blockIdx.x % NVB, sl = blockIdx.x / NVB, v0 = vb * VB;
-    const DT *q = (const DT *)a.q, *k = (const DT *)a.k, *dO = (const DT *)a.d_o;
+    const long H = a.H;
 
-    for (int idx = tid; idx < K * VB; idx += BW_NTHR) {
-        const int x = idx / VB, y = idx % VB;
-        sdS[x * VP + y] = a.dS_T ? a.dS_T[((long)sl * K + x) * V + v0 + y] : 0.f;
+    f32x4 fKm[K / 16];             // Km row 16 w + r
+    f32x4 fPT[C / 16];             // P^T row 16 w + r
+    f32x4 fTT[C / 16];             // T^T row 16 w + r
+    f32x4 fQK[KT][2 * C / 16];     // [Qp^T | Kp^T] rows 16 (KT w + h) + r
+    f32x4 fg[KT];
+    TileRegs<DT, C, VB> pO;
+    float pb = 0.f;
+    auto fetch_kp = [&](long ci) {
+        ld_afrag<K / 16>(fKm, a.ws.Km + ci * (C * K) + (16 * w + r) * K);
+        ld_afrag<C / 16>(fPT, a.ws.PT + ci * (C * C) + (16 * w + r) * C);
+    };
+    auto fetch_t = [&](long ci) { ld_afrag<C / 16>(fTT, a.ws.TT + ci * (C * C) + (16 * w + r) * C); };
+    auto fetch_qk = [&](long ci) {
+#pragma unroll
+        for (int h = 0; h < KT; ++h) {
+            const int x = 16 * (KT * w + h) + r;
+            ld_afrag<C / 16>(&fQK[h][0], a.ws.QpT + ci * (K * C) + x * C);
+            ld_afrag<C / 16>(&fQK[h][C / 16], a.ws.KpT + ci * (K * C) + x * C);
+            fg[h] = *reinterpret_cast<const f32x4 *>(a.ws.egn + ci * K + 16 * (KT * w + h) + 4 * gq);
+        }
+    };
+    auto fetch_o = [&](int c) {
+        const long r0 = tok_row(a, sl, c * C);
+        const int n = min(C, a.T - c * C);
+        pO.load((const DT *)a.d_o + r0 * V + v0, H * V, n);
+        pb = tid < n ? a.beta[r0 + tid * H] : 0.f;
+    };
+
+    f32x4 dS[KT];
+#pragma unroll
+    for (int h = 0; h < KT; ++h) {
+        const int x0 = 16 * (KT * w + h) + 4 * gq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dS[h][e] = a.dS_T ? a.dS_T[((long)sl * K + x0 + e) * V + v0 + r] : 0.f;
+        *reinterpret_cast<f32x4 *>(sdSt + r * LK + x0) = dS[h];
+    }
+    if (a.NC > 0) {
+        const long cl = (long)sl * a.NC + a.NC - 1;
+        fetch_kp(cl);
+        fetch_t(cl);
+        fetch_qk(cl);
+        fetch_o(a.NC - 1);
     }
     for (int c = a.NC - 1; c >= 0; --c) {
-        const int t0 = c * C, n = min(C, a.T - t0);
         const long ci = (long)sl * a.NC + c;
-        const float *gam = a.ws.gam + ci * (C * K);
-        __syncthreads();
-        for (int idx = tid; idx < C * K; idx += BW_NTHR) {
-            const int t = idx / K, x = idx % K;
-            float kv = 0.f, qv = 0.f;
-            if (t < n) {
-                const long r = tok_row(a, sl, t0 + t);
-                kv = to_f32(k[r * K + x]);
-                qv = to_f32(q[r * K + x]);
+        const bool more = c > 0;
+        lds_barrier();
+        {   // dO tile, transposed
+            constexpr int VE = TileRegs<DT, C, VB>::VE, VPR = VB / VE, NV = C * VPR;
+#pragma unroll
+            for (int i = 0; i < TileRegs<DT, C, VB>::PER; ++i) {
+                const int v = tid + i * BW_NTHR;
+                if (NV % BW_NTHR == 0 || v < NV) {
+                    const int t = v / VPR, y = (v % VPR) * VE;
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) sOYt[(y + e) * L2 + t] = to_f32(pO.r[i][e]);
+                }
             }
-            const float gm = gam[idx], gn = gam[(C - 1) * K + x], e = __expf(gm);
-            sQK[t * KP + x] = qv * e;
-            sQK[(C + t) * KP + x] = kv * e;
-            sKm[t * KP + x] = kv * __expf(gn - gm);
         }
-        if (tid < K) sgn[tid] = __expf(gam[(C - 1) * K + tid]);
-        const float *Pm = a.ws.Pm + ci * (C * C), *Tm = a.ws.Tm + ci * (C * C);
-        for (int idx = tid; idx < C * C; idx += BW_NTHR) {
-            const int t = idx / C, s = idx % C;
-            sP[t * CP + s] = Pm[idx];
-            sT[t * CP + s] = Tm[idx];
-        }
-        for (int idx = tid; idx < C * VB; idx += BW_NTHR) {
-            const int t = idx / VB, y = idx % VB;
-            sOY[t * VP + y] = t < n ? to_f32(dO[tok_row(a, sl, t0 + t) * V + v0 + y]) : 0.f;
-        }
-        if (tid < C) sb[tid] = tid < n ? a.beta[tok_row(a, sl, t0 + tid)] : 0.f;
-        float *dhS = a.ws.dhS + ci * (K * V);
-        for (int idx = tid; idx < K * VB; idx += BW_NTHR) {
-            const int x = idx / VB, y = idx % VB;
-            dhS[x * V + v0 + y] = sdS[x * VP + y];
-        }
-        __syncthreads();
+        if (tid < C) sb[tid] = pb;
+        store_state_block<K, V>(a.ws.dhS + ci * (K * V) + v0, sdSt, LK);   // dL/d(state leaving c)
+        lds_barrier();
+        if (more) fetch_o(c - 1);
         {   // dDelta = Km dS' + P^T dO
-            using TL = Tile<C, VB, 4, VB / 16>;
-            const TL tl;
-            float acc[4][VB / 16] = {};
-            mm_acc<C, VB, 4, VB / 16, K, KP, 1, VP, 1>(acc, sKm, sdS, tl.mt, tl.nt);
-            mm_acc<C, VB, 4, VB / 16, C, 1, CP, VP, 1>(acc, sP, sOY, tl.mt, tl.nt);
-            float *dDl = a.ws.dDl + ci * (C * V);
+            f32x4 dD = mma_rows<K / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, fKm, sdSt, LK);
+            dD = mma_rows<C / 16>(dD, fPT, sOYt, L2);
+            if (more) fetch_kp(ci - 1);
+            *reinterpret_cast<f32x4 *>(sdDt + r * LC + 16 * w + 4 * gq) = dD;
+            float *dDl = a.ws.dDl + ci * (C * V) + v0 + r;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < VB / 16; ++j) {
-                    const int t = tl.row(i), y = tl.col(j);
-                    sdD[t * VP + y] = acc[i][j];
-                    dDl[t * V + v0 + y] = acc[i][j];
-                }
+            for (int e = 0; e < 4; ++e) dDl[(16 * w + 4 * gq + e) * V] = dD[e];
         }
-        __syncthreads();
-        {   // Y = T^T dDelta, stored as -beta Y under dO
-            using TL = Tile<C, VB, 4, VB / 16>;
-            const TL tl;
-            float acc[4][VB / 16] = {};
-            mm_acc<C, VB, 4, VB / 16, C, 1, CP, VP, 1>(acc, sT, sdD, tl.mt, tl.nt);
+        lds_barrier();
+        {   // Y = T^T dDelta, kept as -beta Y
+            f32x4 Y = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, fTT, sdDt, LC);
+            if (more) fetch_t(ci - 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < VB / 16; ++j) {
-                    const int t = tl.row(i), y = tl.col(j);
-                    sOY[(C + t) * VP + y] = -sb[t] * acc[i][j];
-                }
+            for (int e = 0; e < 4; ++e) Y[e] *= -sb[16 * w + 4 * gq + e];
+            *reinterpret_cast<f32x4 *>(sOYt + r * L2 + C + 16 * w + 4 * gq) = Y;
         }
-        __syncthreads();
-        {   // dS = Diag(e^{gn}) dS' + [Qp; Kp]^T [dO; -beta Y]
-            using TL = Tile<K, VB, K / 16, VB / 16>;
-            const TL tl;
-            float acc[K / 16][VB / 16] = {};
-            mm_acc<K, VB, K / 16, VB / 16, 2 * C, 1, KP, VP, 1>(acc, sQK, sOY, tl.mt, tl.nt);
+        lds_barrier();
+        // dS = Diag(e^{gn}) dS' + [Qp^T | Kp^T] [dO; -beta Y]
 #pragma unroll
-            for (int i = 0; i < K / 16; ++i)
-#pragma unroll
-                for (int j = 0; j < VB / 16; ++j) {
-                    const int x = tl.row(i), y = tl.col(j);
-                    sdS[x * VP + y] = sgn[x] * sdS[x * VP + y] + acc[i][j];
-                }
+        for (int h = 0; h < KT; ++h) {
+            dS[h] *= fg[h];
+            dS[h] = mma_rows<2 * C / 16>(dS[h], fQK[h], sOYt, L2);
         }
+        if (more) fetch_qk(ci - 1);
+#pragma unroll
+        for (int h = 0; h < KT; ++h)
+            *reinterpret_cast<f32x4 *>(sdSt + r * LK + 16 * (KT * w + h) + 4 * gq) = dS[h];
     }
-    __syncthreads();
     if (a.dS0) {
-        for (int idx = tid; idx < K * VB; idx += BW_NTHR) {
-            const int x = idx / VB, y = idx % VB;
-            a.dS0[((long)sl * K + x) * V + v0 + y] = sdS[x * VP + y];
+#pragma unroll
+        for (int h = 0; h < KT; ++h) {
+            const int x0 = 16 * (KT * w + h) + 4 * gq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.dS0[((long)sl * K + x0 + e) * V + v0 + r] = dS[h][e];
         }
     }
 }
@@ -376,14 +540,17 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_vgrad_kernel(BwArgs a)
     const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
     const int t0 = c * C, n = min(C, a.T - t0);
     const long ci = (long)sl * a.NC + c;
-    const DT *v = (const DT *)a.v, *dO = (const DT *)a.d_o;
-    DT *dv = (DT *)a.dv;
+    const long H = a.H, r0 = tok_row(a, sl, t0);
+    const DT *v = (const DT *)a.v + r0 * V, *dO = (const DT *)a.d_o + r0 * V;
+    DT *dv = (DT *)a.dv + r0 * V;
     const float *hS = a.ws.hS + ci * (K * V), *dhS = a.ws.dhS + ci * (K * V);
     const float *Dl = a.ws.Dl + ci * (C * V), *dDl = a.ws.dDl + ci * (C * V);
-
-    const float *Tm = a.ws.Tm + ci * (C * C);
-    for (int idx = tid; idx < C * C; idx += BW_NTHR) sT[(idx / C) * CP + idx % C] = Tm[idx];
-    if (tid < C) sb[tid] = tid < n ? a.beta[tok_row(a, sl, t0 + tid)] : 0.f;
+    {
+        TileRegs<float, C, C> tT;
+        tT.load(a.ws.Tm + ci * (C * C), C, C);
+        tT.store(sT, CP);
+        if (tid < C) sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
+    }
 
     using TCK = Tile<C, K, 4, K / 16>;
     using TCC = Tile<C, C, 4, 4>;
@@ -397,26 +564,25 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_vgrad_kernel(BwArgs a)
     float dgn = 0.f;
 
     for (int v0 = 0; v0 < V; v0 += VB) {
-        __syncthreads();
-        for (int idx = tid; idx < K * VB; idx += BW_NTHR) {
-            const int x = idx / VB, y = idx % VB;
-            sS[x * VP + y] = hS[x * V + v0 + y];
-            sdS[x * VP + y] = dhS[x * V + v0 + y];
+        lds_barrier();
+        {
+            TileRegs<float, K, VB> ts, tds;
+            TileRegs<DT, C, VB> to, tvv;
+            TileRegs<float, C, VB> tD, tdD;
+            ts.load(hS + v0, V, K);
+            tds.load(dhS + v0, V, K);
+            to.load(dO + v0, H * V, n);
+            tvv.load(v + v0, H * V, n);
+            tD.load(Dl + v0, V, C);
+            tdD.load(dDl + v0, V, C);
+            ts.store(sS, VP);
+            tds.store(sdS, VP);
+            to.store(sdO, VP);
+            tvv.store(sV, VP);
+            tD.store(sDl, VP);
+            tdD.store(sdD, VP);
         }
-        for (int idx = tid; idx < C * VB; idx += BW_NTHR) {
-            const int t = idx / VB, y = idx % VB;
-            float o = 0.f, vv = 0.f;
-            if (t < n) {
-                const long r = tok_row(a, sl, t0 + t);
-                o = to_f32(dO[r * V + v0 + y]);
-                vv = to_f32(v[r * V + v0 + y]);
-            }
-            sdO[t * VP + y] = o;
-            sV[t * VP + y] = vv;
-            sDl[t * VP + y] = Dl[t * V + v0 + y];
-            sdD[t * VP + y] = dDl[t * V + v0 + y];
-        }
-        __syncthreads();
+        lds_barrier();
         // dQp += dO S^T, dKm += Delta dS'^T, dWn += dDelta S^T   (C x K, sum over the block)
         mm_acc<C, K, 4, K / 16, VB, VP, 1, 1, VP>(aQ, sdO, sS, tk.mt, tk.nt);
         mm_acc<C, K, 4, K / 16, VB, VP, 1, 1, VP>(aKm, sDl, sdS, tk.mt, tk.nt);
@@ -431,7 +597,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_vgrad_kernel(BwArgs a)
             for (int i = 0; i < 4; ++i) {
                 const int t = tv.row(i), yy = tv.col(0);
                 dbv[i] = fmaf(sV[t * VP + yy], y[i][0], dbv[i]);
-                if (t < n) dv[tok_row(a, sl, t0 + t) * V + v0 + yy] = from_f32<DT>(sb[t] * y[i][0]);
+                if (t < n) dv[t * H * V + v0 + yy] = from_f32<DT>(sb[t] * y[i][0]);
             }
         }
         if (tid < K)
@@ -467,10 +633,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_vgrad_kernel(BwArgs a)
         s += __shfl_xor(s, 8, 16);
         if (tv.nt == 0) a.ws.dbv[ci * C + tv.row(i)] = s;
     }
-    if (tid < K) {
-        const float gn = a.ws.gam[ci * (C * K) + (C - 1) * K + tid];
-        a.ws.dgn[ci * K + tid] = __expf(gn) * dgn;
-    }
+    if (tid < K) a.ws.dgn[ci * K + tid] = a.ws.egn[ci * K + tid] * dgn;
 }
 
 // ---------------------------------------------------------------- 5 kgrad
@@ -492,29 +655,25 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad_kernel(BwArgs a)
     const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
     const int t0 = c * C, n = min(C, a.T - t0);
     const long ci = (long)sl * a.NC + c;
-    const DT *q = (const DT *)a.q, *k = (const DT *)a.k;
-    const float *gam = a.ws.gam + ci * (C * K);
+    const long H = a.H, r0 = tok_row(a, sl, t0);
     float *Zg = a.ws.dWn + ci * (C * K);   // dWn is replaced by Z once it is in LDS
-
-    for (int idx = tid; idx < C * K; idx += BW_NTHR) {
-        const int t = idx / K, x = idx % K;
-        const float kv = t < n ? to_f32(k[tok_row(a, sl, t0 + t) * K + x]) : 0.f;
-        sKp[t * KP + x] = kv * __expf(gam[idx]);
-        sWn[t * KP + x] = Zg[idx];
-    }
     {
-        const float *Tm = a.ws.Tm + ci * (C * C), *dT = a.ws.dT + ci * (C * C);
-        for (int idx = tid; idx < C * C; idx += BW_NTHR) {
-            const int t = idx / C, s = idx % C;
-            sT[t * CP + s] = Tm[idx];
-            sdG[t * CP + s] = dT[idx];
+        TileRegs<float, C, K> tW, tK;
+        TileRegs<float, C, C> tT, tdT;
+        tW.load(Zg, K, C);
+        tK.load(a.ws.Kp + ci * (C * K), K, C);
+        tT.load(a.ws.Tm + ci * (C * C), C, C);
+        tdT.load(a.ws.dT + ci * (C * C), C, C);
+        if (tid < C) {
+            sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
+            sdb[tid] = a.ws.dbv[ci * C + tid];
         }
+        tW.store(sWn, KP);
+        tK.store(sKp, KP);
+        tT.store(sT, CP);
+        tdT.store(sdG, CP);
     }
-    if (tid < C) {
-        sb[tid] = tid < n ? a.beta[tok_row(a, sl, t0 + tid)] : 0.f;
-        sdb[tid] = a.ws.dbv[ci * C + tid];
-    }
-    __syncthreads();
+    lds_barrier();
     {   // Z = -T^T dWn (to global, in place of dWn); dbeta += rowsum(Kp * Z)
         using TL = Tile<C, K, 4, K / 16>;
         const TL tl;
@@ -550,7 +709,26 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad_kernel(BwArgs a)
                 sdG[t * CP + s] -= sb[s] * acc[i][j];
             }
     }
+    // Z goes to global memory and is read back below by other threads of the
+    // workgroup: a full barrier (global and LDS).
     __syncthreads();
+    // phase-3 operands, fetched now and stored once phase 2 is done with the LDS
+    const int x = tid % K, sp = tid / K, rb = sp * RP;
+    TileRegs<DT, C, K> tk, tq;
+    TileRegs<float, C, K> tg;
+    tk.load((const DT *)a.k + r0 * K, H * K, n);
+    tq.load((const DT *)a.q + r0 * K, H * K, n);
+    tg.load(a.ws.gam + ci * (C * K), K, C);
+    float pq[RP], pk[RP], pz[RP];
+    {
+        const float *dQp = a.ws.dQp + ci * (C * K), *dKm = a.ws.dKm + ci * (C * K);
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+            pq[i] = dQp[(rb + i) * K + x];
+            pk[i] = dKm[(rb + i) * K + x];
+            pz[i] = Zg[(rb + i) * K + x];
+        }
+    }
     {   // M1 = T^T dT (over dWn, which is no longer read); dP masked to s <= t
         using TL = Tile<C, C, 4, 4>;
         const TL tl;
@@ -560,13 +738,11 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad_kernel(BwArgs a)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) sM[tl.row(i) * CP + tl.col(j)] = acc[i][j];
-        const float *dP = a.ws.dP + ci * (C * C);
-        for (int idx = tid; idx < C * C; idx += BW_NTHR) {
-            const int t = idx / C, s = idx % C;
-            sdP[t * CP + s] = s <= t ? dP[idx] : 0.f;
-        }
+        TileRegs<float, C, C> tP;
+        tP.load(a.ws.dP + ci * (C * C), C, C);
+        tP.store<true>(sdP, CP);
     }
-    __syncthreads();
+    lds_barrier();
     {   // dA = -M1 T^T (strictly lower); dG = diag(beta) dA; dbeta += rowsum(dA * G)
         using TL = Tile<C, C, 4, 4>;
         const TL tl;
@@ -591,87 +767,80 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad_kernel(BwArgs a)
             if (tl.nt == 0) sdb[t] += part;
         }
     }
-    __syncthreads();
-    // phase 3: k, gamma, q by rows, one key channel per thread
-    for (int idx = tid; idx < C * K; idx += BW_NTHR) {
-        const int t = idx / K;
-        float kv = 0.f, qv = 0.f;
-        if (t < n) {
-            const long r = tok_row(a, sl, t0 + t);
-            kv = to_f32(k[r * K + idx % K]);
-            qv = to_f32(q[r * K + idx % K]);
-        }
-        sk[idx] = kv;
-        sq[idx] = qv;
-        sg[idx] = gam[idx];
-    }
-    __syncthreads();
-    const int x = tid % K, sp = tid / K;
-    const int r0 = sp * RP;
+    lds_barrier();
+    tk.store(sk, K);
+    tq.store(sq, K);
+    tg.store(sg, K);
+    lds_barrier();
+    // phase 3: one key channel per thread, rows rb .. rb + RP - 1
     const float gn = sg[(C - 1) * K + x];
-    const float *dQp = a.ws.dQp + ci * (C * K), *dKm = a.ws.dKm + ci * (C * K);
-    float *dgam = a.ws.dQp + ci * (C * K);   // dQp is replaced by d gamma element by element
-    DT *dq = (DT *)a.dq, *dk = (DT *)a.dk;
+    DT *dq = (DT *)a.dq + r0 * K, *dk = (DT *)a.dk + r0 * K;
+    float dgm[RP];
     float tot = 0.f, dgn_loc = 0.f;
-    for (int r = r0; r < r0 + RP; ++r) {
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+        const int r = rb + i;
         const float kr = sk[r * K + x], qr = sq[r * K + x], gr = sg[r * K + x];
         float accq = 0.f, acck = 0.f, accs = 0.f;
+#pragma unroll 4
         for (int s = 0; s <= r; ++s) {          // r as the later token
             const float w = sk[s * K + x] * __expf(gr - sg[s * K + x]);
             accq = fmaf(sdP[r * CP + s], w, accq);
             acck = fmaf(sdG[r * CP + s], w, acck);
         }
+#pragma unroll 4
         for (int t = r; t < C; ++t) {           // r as the earlier token
             const float e = __expf(sg[t * K + x] - gr);
             accs = fmaf(fmaf(sdG[t * CP + r], sk[t * K + x], sdP[t * CP + r] * sq[t * K + x]), e, accs);
         }
         const float eg = __expf(gr), em = __expf(gn - gr);
-        const float dqp = dQp[r * K + x], dkm = dKm[r * K + x], z = Zg[r * K + x] * sb[r];
+        const float dqp = pq[i], dkm = pk[i], z = pz[i] * sb[r];
         const float dqv = fmaf(dqp, eg, accq);
         const float dkv = acck + accs + z * eg + dkm * em;
-        const float dgm = qr * accq + kr * (acck - accs) + (dqp * qr + z * kr) * eg - dkm * kr * em;
+        dgm[i] = qr * accq + kr * (acck - accs) + (dqp * qr + z * kr) * eg - dkm * kr * em;
         dgn_loc = fmaf(dkm * kr, em, dgn_loc);
         if (r < n) {
-            const long row = tok_row(a, sl, t0 + r);
-            dq[row * K + x] = from_f32<DT>(dqv);
-            dk[row * K + x] = from_f32<DT>(dkv);
+            dq[r * H * K + x] = from_f32<DT>(dqv);
+            dk[r * H * K + x] = from_f32<DT>(dkv);
         }
-        dgam[r * K + x] = dgm;
-        tot += dgm;
+        tot += dgm[i];
     }
     stot[sp * K + x] = tot;
     sdgn[sp * K + x] = dgn_loc;
-    __syncthreads();
+    lds_barrier();
     {   // dg = reverse running sum of d gamma, plus the gn terms on the last row
         float run = a.ws.dgn[ci * K + x];
 #pragma unroll
         for (int p = 0; p < NSPL; ++p) run += sdgn[p * K + x] + (p > sp ? stot[p * K + x] : 0.f);
-        for (int r = r0 + RP - 1; r >= r0; --r) {
-            run += dgam[r * K + x];
+#pragma unroll
+        for (int i = RP - 1; i >= 0; --i) {
+            const int r = rb + i;
+            run += dgm[i];
             if (CH) {
-                if (r < n) a.dg[tok_row(a, sl, t0 + r) * K + x] = run;
+                if (r < n) a.dg[(r0 + r * H) * K + x] = run;
             } else {
                 sk[r * K + x] = run;            // k is no longer read
             }
         }
     }
     if (!CH) {
-        __syncthreads();
+        lds_barrier();
         if (tid < n) {
             float s = 0.f;
             for (int y = 0; y < K; ++y) s += sk[tid * K + y];
-            a.dg[tok_row(a, sl, t0 + tid)] = s;
+            a.dg[r0 + tid * H] = s;
         }
     }
-    if (tid < n) a.dbeta[tok_row(a, sl, t0 + tid)] = sdb[tid];
+    if (tid < n) a.dbeta[r0 + tid * H] = sdb[tid];
 }
 
 // ---------------------------------------------------------------- host side
 template <int K, int V> struct BwLds {
-    static constexpr int C = BW_C, KP = K + 1, CP = C + 1, VB = bw_vb(K), VP = VB + 1;
-    static constexpr int prep = 4 * (3 * C * KP + 2 * C * CP + C);
-    static constexpr int states = 4 * (2 * C * KP + C * CP + K * VP + 2 * C * VP + C + K);
-    static constexpr int dstates = 4 * (3 * C * KP + 2 * C * CP + K * VP + 3 * C * VP + C + K);
+    static constexpr int C = BW_C, KP = K + 1, CP = C + 1, VB = BW_VB, VP = VB + 1;
+    static constexpr int LK = K + 4, LC = C + 4, L2 = 2 * C + 4;
+    static constexpr int prep = 4 * (3 * C * KP + 2 * C * CP + 2 * C);
+    static constexpr int states = 4 * (VB * LK + 2 * VB * LC + C * VP + C);
+    static constexpr int dstates = 4 * (VB * LK + VB * L2 + VB * LC + C);
     static constexpr int vgrad = 4 * (2 * K * 17 + 4 * C * 17 + C * CP + C);
     static constexpr int kscr12 = 2 * C * KP + C * CP, kscr3 = 3 * C * K;
     static constexpr int kgrad = 4 * (2 * C + 2 * (BW_NTHR / K) * K + 2 * C * CP +
@@ -696,16 +865,16 @@ static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
     static bool s1 = false, s2 = false, s3 = false, s4 = false, s5 = false;
     hipError_t e;
     if ((e = set_lds(bwd_prep_kernel<DT, K, CH>, L::prep, s1)) != hipSuccess) return e;
-    if ((e = set_lds(bwd_states_kernel<DT, K, V, CH>, L::states, s2)) != hipSuccess) return e;
-    if ((e = set_lds(bwd_dstates_kernel<DT, K, V, CH>, L::dstates, s3)) != hipSuccess) return e;
+    if ((e = set_lds(bwd_states_kernel<DT, K, V>, L::states, s2)) != hipSuccess) return e;
+    if ((e = set_lds(bwd_dstates_kernel<DT, K, V>, L::dstates, s3)) != hipSuccess) return e;
     if ((e = set_lds(bwd_vgrad_kernel<DT, K, V>, L::vgrad, s4)) != hipSuccess) return e;
     if ((e = set_lds(bwd_kgrad_kernel<DT, K, CH>, L::kgrad, s5)) != hipSuccess) return e;
     const unsigned nch = (unsigned)(nslices * a.NC), nvb = (unsigned)(nslices * (V / L::VB));
     if (nch > 0) {
         hipLaunchKernelGGL((bwd_prep_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::prep, st, a);
-        hipLaunchKernelGGL((bwd_states_kernel<DT, K, V, CH>), dim3(nvb), dim3(BW_NTHR), L::states, st, a);
+        hipLaunchKernelGGL((bwd_states_kernel<DT, K, V>), dim3(nvb), dim3(BW_NTHR), L::states, st, a);
     }
-    hipLaunchKernelGGL((bwd_dstates_kernel<DT, K, V, CH>), dim3(nvb), dim3(BW_NTHR), L::dstates, st, a);
+    hipLaunchKernelGGL((bwd_dstates_kernel<DT, K, V>), dim3(nvb), dim3(BW_NTHR), L::dstates, st, a);
     if (nch > 0) {
         hipLaunchKernelGGL((bwd_vgrad_kernel<DT, K, V>), dim3(nch), dim3(BW_NTHR), L::vgrad, st, a);
         hipLaunchKernelGGL((bwd_kgrad_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::kgrad, st, a);

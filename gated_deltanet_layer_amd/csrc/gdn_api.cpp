@@ -64,7 +64,7 @@ gdn_status bwd_sizes(int B, int T, int H, int K, int V, int chunk, long long *nc
     if (nqk < 0 || nv < 0 || nst < 0) return GDN_EINVAL;
     if (!kv_supported(K) || !kv_supported(V) || chunk != 64) return GDN_ENOTSUP;
     const long long n = prod(B, H, (T + 63) / 64);
-    const long long nvb = prod(B, H, V / gdn::bw_vb(K));
+    const long long nvb = prod(B, H, V / gdn::BW_VB);
     // one 256-thread workgroup per chunk / per value block: grid x * 256 < 2^32
     if (n < 0 || nvb < 0 || n >= (1LL << 24) || nvb >= (1LL << 24)) return GDN_ENOTSUP;
     *nch = n;
@@ -244,10 +244,14 @@ gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const floa
     const long long ng = gate == GDN_GATE_CHANNEL ? nqk : ntok;
     if (ntok > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
         return GDN_EINVAL;
-    for (const void *p : {q, k, v, d_o, (const void *)dq, (const void *)dk, (const void *)dv})
+    // q, k, v, d_o, a per-channel g, S0 and dS_T are read as 16-byte vectors
+    // from row starts; the outputs are written element by element.
+    for (const void *p : {q, k, v, d_o, (const void *)S0, (const void *)dS_T})
+        if (p && !aligned16(p)) return GDN_EINVAL;
+    if (g && !aligned(g, gate == GDN_GATE_CHANNEL ? 16 : 4)) return GDN_EINVAL;
+    for (const void *p : {(const void *)dq, (const void *)dk, (const void *)dv})
         if (p && !aligned(p, (unsigned)es)) return GDN_EINVAL;
-    for (const void *p : {(const void *)g, (const void *)beta, (const void *)S0,
-                          (const void *)dS_T, (const void *)dg, (const void *)dbeta,
+    for (const void *p : {(const void *)beta, (const void *)dg, (const void *)dbeta,
                           (const void *)dS0})
         if (p && !aligned(p, 4)) return GDN_EINVAL;
     if (workspace && !aligned(workspace, 256)) return GDN_EINVAL;

@@ -168,7 +168,8 @@ GDN_API gdn_status gdn_chunk_bwd_workspace_size(int B, int T, int H, int K, int 
  *                        do not matter and on return are unspecified.
  *
  * K and V: 64 or 128; chunk: 64; dtype GDN_F32 or GDN_BF16 (the arithmetic is
- * fp32 for both).  Every pointer needs its element alignment.  No output may
+ * fp32 for both).  q, k, v, d_o, a per-channel g, S0 and dS_T need 16-byte
+ * alignment, every other pointer its element alignment.  No output may
  * overlap an input, another output or the workspace.  B, T or H equal to 0 is a
  * valid call (T = 0: dS0 receives dS_T, or zeros).  Calls that share one
  * workspace must not run concurrently.

@@ -196,7 +196,9 @@ def _ws_size(L, B, T, H, K, V, chunk=64):
 @pytest.mark.parametrize("kw", [
     dict(dtype=2), dict(gate=2), dict(B=-1), dict(T=-1), dict(H=-1), dict(K=0), dict(V=-1),
     dict(chunk=0), dict(q=None), dict(d_o=None), dict(dq=None), dict(dg=None), dict(dbeta=None),
-    dict(ws=None), dict(q=BASE + 1), dict(dv=BASE + 10 * SEP + 1), dict(g=BASE + 3 * SEP + 2),
+    dict(ws=None), dict(q=BASE + 1), dict(k=BASE + SEP + 8), dict(d_o=BASE + 6 * SEP + 2),
+    dict(S0=BASE + 5 * SEP + 4), dict(dS_T=BASE + 7 * SEP + 8), dict(g=BASE + 3 * SEP + 4),
+    dict(dv=BASE + 10 * SEP + 1), dict(g=BASE + 3 * SEP + 2),
     dict(dS0=BASE + 13 * SEP + 2), dict(ws=BASE + 14 * SEP + 64),
     dict(dq=BASE),                      # dq aliases q
     dict(dv=BASE + 6 * SEP + 64),       # dv overlaps d_o
@@ -235,11 +237,11 @@ def test_bwd_workspace_size(L):
     assert _ws_size(L, 1, 64, 1, 128, 128, chunk=32)[0] == gdn.GDN_ENOTSUP
     assert _ws_size(L, -1, 64, 1, 128, 128)[0] == gdn.GDN_EINVAL
     assert _ws_size(L, 3, 0, 2, 128, 128) == (gdn.GDN_OK, 0)
-    # fifteen fp32 arrays over the chunks, each rounded up to 256 bytes
+    # twenty-two fp32 arrays over the chunks, each rounded up to 256 bytes
     for B, T, H, K, V in [(1, 1, 1, 64, 64), (2, 100, 3, 128, 64), (4, 4096, 6, 128, 128)]:
         nch = B * H * ((T + 63) // 64)
-        per = [64 * K, 64 * 64, 64 * 64, 64 * 64, K * V, K * V, 64 * V, 64 * V,
-               64 * K, 64 * K, 64 * K, 64 * 64, 64 * 64, K, 64]
+        per = [64 * K] + [64 * 64] * 4 + [K * V] * 2 + [64 * V] * 2 + [64 * K] * 3 + \
+              [64 * 64] * 2 + [K, 64] + [64 * K] * 5 + [K]
         want = sum((nch * x * 4 + 255) // 256 * 256 for x in per)
         assert _ws_size(L, B, T, H, K, V) == (gdn.GDN_OK, want)
         assert gdn.gdn_chunk_bwd_workspace_size(B, T, H, K, V) == want
