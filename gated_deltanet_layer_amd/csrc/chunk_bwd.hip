@@ -32,7 +32,9 @@
 //                                         chunk, dDelta, and dS0
 //   4 vgrad    one per chunk:             every product that sums over the
 //                                         value dimension; dv
-//   5 kgrad    one per chunk:             the rest; dq, dk, dg, dbeta
+//   5 kgrad1   one per chunk:             the C x C part of the chain; dbeta
+//   6 kgrad2   one per chunk:             the sums over token pairs (matrix
+//                                         cores); dq, dk, dg
 // The state recursions split by value column (column j of S and of dS depends
 // only on column j), which is what lets 2 and 3 run one workgroup per block of
 // value columns.  Intermediates live in a caller-provided fp32 workspace.
@@ -636,34 +638,31 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_vgrad_kernel(BwArgs a)
     if (tid < K) a.ws.dgn[ci * K + tid] = a.ws.egn[ci * K + tid] * dgn;
 }
 
-// ---------------------------------------------------------------- 5 kgrad
-template <typename DT, int K, bool CH>
-__global__ __launch_bounds__(BW_NTHR) void bwd_kgrad_kernel(BwArgs a)
+// ---------------------------------------------------------------- 5 kgrad1
+// The C x C part of the chain: Z = -T^T dWn (replaces dWn in the workspace),
+// dT -= dWn (beta Kp)^T, dA = -T^T dT T^T, dG = diag(beta) dA (replaces dT),
+// and the final dbeta = rowsum(V * Y) + rowsum(Kp * Z) + rowsum(dA * G).
+template <typename DT, int K>
+__global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
 {
     constexpr int C = BW_C, KP = K + 1, CP = C + 1;
-    constexpr int NSPL = BW_NTHR / K;   // threads per key channel in the pair phase
-    constexpr int RP = C / NSPL;        // rows per thread there
     extern __shared__ __attribute__((aligned(256))) float sm[];
-    // fixed: small arrays, dG (first dT), dP
-    float *sb = sm, *sdb = sb + C, *stot = sdb + C, *sdgn = stot + NSPL * K;
-    float *sdG = sdgn + NSPL * K, *sdP = sdG + C * CP;
-    float *scr = sdP + C * CP;
-    // phases 1-2: dWn (then M1), Kp, T;  phase 3: k, gamma, q (unpadded rows)
-    float *sWn = scr, *sM = scr, *sKp = scr + C * KP, *sT = sKp + C * KP;
-    float *sk = scr, *sg = scr + C * K, *sq = sg + C * K;
+    float *sb = sm, *sdb = sb + C, *sWn = sdb + C, *sKp = sWn + C * KP, *sT = sKp + C * KP;
+    float *sdT = sT + C * CP, *sM = sdT + C * CP;
     const int tid = threadIdx.x;
     const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
     const int t0 = c * C, n = min(C, a.T - t0);
     const long ci = (long)sl * a.NC + c;
     const long H = a.H, r0 = tok_row(a, sl, t0);
-    float *Zg = a.ws.dWn + ci * (C * K);   // dWn is replaced by Z once it is in LDS
+    float *Zg = a.ws.dWn + ci * (C * K);    // dWn is replaced by Z once it is in LDS
+    float *dGg = a.ws.dT + ci * (C * C);    // dT is replaced by dG likewise
     {
         TileRegs<float, C, K> tW, tK;
         TileRegs<float, C, C> tT, tdT;
         tW.load(Zg, K, C);
         tK.load(a.ws.Kp + ci * (C * K), K, C);
         tT.load(a.ws.Tm + ci * (C * C), C, C);
-        tdT.load(a.ws.dT + ci * (C * C), C, C);
+        tdT.load(dGg, C, C);
         if (tid < C) {
             sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
             sdb[tid] = a.ws.dbv[ci * C + tid];
@@ -671,10 +670,10 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad_kernel(BwArgs a)
         tW.store(sWn, KP);
         tK.store(sKp, KP);
         tT.store(sT, CP);
-        tdT.store(sdG, CP);
+        tdT.store(sdT, CP);
     }
     lds_barrier();
-    {   // Z = -T^T dWn (to global, in place of dWn); dbeta += rowsum(Kp * Z)
+    {   // Z = -T^T dWn; dbeta += rowsum(Kp * Z)
         using TL = Tile<C, K, 4, K / 16>;
         const TL tl;
         float acc[4][K / 16] = {};
@@ -706,41 +705,19 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad_kernel(BwArgs a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = tl.row(i), s = tl.col(j);
-                sdG[t * CP + s] -= sb[s] * acc[i][j];
+                sdT[t * CP + s] -= sb[s] * acc[i][j];
             }
     }
-    // Z goes to global memory and is read back below by other threads of the
-    // workgroup: a full barrier (global and LDS).
-    __syncthreads();
-    // phase-3 operands, fetched now and stored once phase 2 is done with the LDS
-    const int x = tid % K, sp = tid / K, rb = sp * RP;
-    TileRegs<DT, C, K> tk, tq;
-    TileRegs<float, C, K> tg;
-    tk.load((const DT *)a.k + r0 * K, H * K, n);
-    tq.load((const DT *)a.q + r0 * K, H * K, n);
-    tg.load(a.ws.gam + ci * (C * K), K, C);
-    float pq[RP], pk[RP], pz[RP];
-    {
-        const float *dQp = a.ws.dQp + ci * (C * K), *dKm = a.ws.dKm + ci * (C * K);
-#pragma unroll
-        for (int i = 0; i < RP; ++i) {
-            pq[i] = dQp[(rb + i) * K + x];
-            pk[i] = dKm[(rb + i) * K + x];
-            pz[i] = Zg[(rb + i) * K + x];
-        }
-    }
-    {   // M1 = T^T dT (over dWn, which is no longer read); dP masked to s <= t
+    lds_barrier();
+    {   // M1 = T^T dT
         using TL = Tile<C, C, 4, 4>;
         const TL tl;
         float acc[4][4] = {};
-        mm_acc<C, C, 4, 4, C, 1, CP, CP, 1>(acc, sT, sdG, tl.mt, tl.nt);
+        mm_acc<C, C, 4, 4, C, 1, CP, CP, 1>(acc, sT, sdT, tl.mt, tl.nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) sM[tl.row(i) * CP + tl.col(j)] = acc[i][j];
-        TileRegs<float, C, C> tP;
-        tP.load(a.ws.dP + ci * (C * C), C, C);
-        tP.store<true>(sdP, CP);
     }
     lds_barrier();
     {   // dA = -M1 T^T (strictly lower); dG = diag(beta) dA; dbeta += rowsum(dA * G)
@@ -758,7 +735,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad_kernel(BwArgs a)
                 const int s = tl.col(j);
                 const float da = s < t ? -acc[i][j] : 0.f;
                 part = fmaf(da, Gm[t * C + s], part);
-                sdG[t * CP + s] = sb[t] * da;
+                dGg[t * C + s] = sb[t] * da;
             }
             part += __shfl_xor(part, 1, 16);
             part += __shfl_xor(part, 2, 16);
@@ -768,70 +745,223 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad_kernel(BwArgs a)
         }
     }
     lds_barrier();
-    tk.store(sk, K);
-    tq.store(sq, K);
-    tg.store(sg, K);
-    lds_barrier();
-    // phase 3: one key channel per thread, rows rb .. rb + RP - 1
-    const float gn = sg[(C - 1) * K + x];
-    DT *dq = (DT *)a.dq + r0 * K, *dk = (DT *)a.dk + r0 * K;
-    float dgm[RP];
-    float tot = 0.f, dgn_loc = 0.f;
-#pragma unroll
-    for (int i = 0; i < RP; ++i) {
-        const int r = rb + i;
-        const float kr = sk[r * K + x], qr = sq[r * K + x], gr = sg[r * K + x];
-        float accq = 0.f, acck = 0.f, accs = 0.f;
-#pragma unroll 4
-        for (int s = 0; s <= r; ++s) {          // r as the later token
-            const float w = sk[s * K + x] * __expf(gr - sg[s * K + x]);
-            accq = fmaf(sdP[r * CP + s], w, accq);
-            acck = fmaf(sdG[r * CP + s], w, acck);
-        }
-#pragma unroll 4
-        for (int t = r; t < C; ++t) {           // r as the earlier token
-            const float e = __expf(sg[t * K + x] - gr);
-            accs = fmaf(fmaf(sdG[t * CP + r], sk[t * K + x], sdP[t * CP + r] * sq[t * K + x]), e, accs);
-        }
-        const float eg = __expf(gr), em = __expf(gn - gr);
-        const float dqp = pq[i], dkm = pk[i], z = pz[i] * sb[r];
-        const float dqv = fmaf(dqp, eg, accq);
-        const float dkv = acck + accs + z * eg + dkm * em;
-        dgm[i] = qr * accq + kr * (acck - accs) + (dqp * qr + z * kr) * eg - dkm * kr * em;
-        dgn_loc = fmaf(dkm * kr, em, dgn_loc);
-        if (r < n) {
-            dq[r * H * K + x] = from_f32<DT>(dqv);
-            dk[r * H * K + x] = from_f32<DT>(dkv);
-        }
-        tot += dgm[i];
+    if (tid < n) a.dbeta[r0 + tid * H] = sdb[tid];
+}
+
+// ---------------------------------------------------------------- 6 kgrad2
+// The sums over token pairs, on the fp32 matrix cores, then dq, dk and dg:
+//   accq[r] = sum_{s<=r} dP_rs k_s e^{gamma_r - gamma_s}
+//   acck[r] = sum_{s<r}  dG_rs k_s e^{gamma_r - gamma_s}
+//   accs[u] = sum_{t>=u} (dG_tu k_t + dP_tu q_t) e^{gamma_t - gamma_u}
+// (per key channel).  Per-channel gate: the 64 tokens are cut into blocks of
+// 16 with a reference row rho in the middle of each, and e^{gamma_r - gamma_s}
+// is split through the reference of the block of s (of t for accs), so each
+// block pair is a 16 x 16 x 16 product of dP or dG with a row-scaled k or q,
+// scaled afterwards per element.  No factor exceeds e^{8 * 5}: the log-decay
+// is at least -5 per token (the configured domain of the Atomic-GDN2 card,
+// section 2.1).  Scalar gate: the decay depends on the token pair only, so dP
+// and dG are scaled by e^{gamma_r - gamma_s} before the products, exactly.
+template <typename DT, int K, bool CH>
+__global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
+{
+    constexpr int C = BW_C, L = C + 4, XB = K / 64;       // x blocks of 16 per wave
+    constexpr int NSPL = BW_NTHR / K, RP = C / NSPL;
+    extern __shared__ __attribute__((aligned(256))) float sm[];
+    float *sKt = sm;                 // [K][L]  (k e^{gamma_rho - gamma})^T   later: d gamma [C][K]
+    float *sKh = sKt + K * L;        // [K][L]  (k e^{gamma - gamma_rho})^T
+    float *sQh = sKh + K * L;        // [K][L]  (q e^{gamma - gamma_rho})^T
+    float *sdP = sQh + K * L;        // [C][L]  dP, lower with the diagonal
+    float *sdG = sdP + C * L;        // [C][L]  dG, strictly lower
+    float *sb = sdG + C * L, *sgs = sb + C, *stot = sgs + C, *sdgn = stot + NSPL * K;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
+    const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
+    const int t0 = c * C, n = min(C, a.T - t0);
+    const long ci = (long)sl * a.NC + c;
+    const long H = a.H, r0 = tok_row(a, sl, t0);
+    const DT *q = (const DT *)a.q + r0 * K, *k = (const DT *)a.k + r0 * K;
+    const float *gam = a.ws.gam + ci * (C * K);
+    {
+        TileRegs<float, C, C> tP, tG;
+        tP.load(a.ws.dP + ci * (C * C), C, C);
+        tG.load(a.ws.dT + ci * (C * C), C, C);
+        tP.store<true>(sdP, L);
+        tG.store(sdG, L);
     }
-    stot[sp * K + x] = tot;
-    sdgn[sp * K + x] = dgn_loc;
-    lds_barrier();
-    {   // dg = reverse running sum of d gamma, plus the gn terms on the last row
-        float run = a.ws.dgn[ci * K + x];
+    if (tid < C) {
+        sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
+        sgs[tid] = gam[tid * K];
+    }
+    // row-scaled k and q, transposed, four channels of one token per thread
+    // (consecutive threads take consecutive tokens: conflict-free LDS writes)
+    for (int v = tid; v < C * K / 4; v += BW_NTHR) {
+        const int t = v % C, x = (v / C) * 4;
+        f32x4 kv = {0.f, 0.f, 0.f, 0.f}, qv = {0.f, 0.f, 0.f, 0.f};
+        if (t < n) {
 #pragma unroll
-        for (int p = 0; p < NSPL; ++p) run += sdgn[p * K + x] + (p > sp ? stot[p * K + x] : 0.f);
-#pragma unroll
-        for (int i = RP - 1; i >= 0; --i) {
-            const int r = rb + i;
-            run += dgm[i];
-            if (CH) {
-                if (r < n) a.dg[(r0 + r * H) * K + x] = run;
-            } else {
-                sk[r * K + x] = run;            // k is no longer read
+            for (int e = 0; e < 4; ++e) {
+                kv[e] = to_f32(k[t * H * K + x + e]);
+                qv[e] = to_f32(q[t * H * K + x + e]);
             }
+        }
+        f32x4 up = {1.f, 1.f, 1.f, 1.f}, dn = {1.f, 1.f, 1.f, 1.f};
+        if (CH) {
+            const f32x4 g = *reinterpret_cast<const f32x4 *>(gam + t * K + x);
+            const f32x4 gr = *reinterpret_cast<const f32x4 *>(gam + (16 * (t / 16) + 8) * K + x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                up[e] = __expf(gr[e] - g[e]);
+                dn[e] = __expf(g[e] - gr[e]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sKt[(x + e) * L + t] = kv[e] * up[e];
+            sKh[(x + e) * L + t] = kv[e] * dn[e];
+            sQh[(x + e) * L + t] = qv[e] * dn[e];
+        }
+    }
+    lds_barrier();
+    if (!CH) {   // scalar gate: fold e^{gamma_r - gamma_s} into dP and dG
+        for (int idx = tid; idx < C * C; idx += BW_NTHR) {
+            const int t = idx / C, s = idx % C;
+            if (s <= t) {
+                const float e = __expf(sgs[t] - sgs[s]);
+                sdP[t * L + s] *= e;
+                sdG[t * L + s] *= e;
+            }
+        }
+        lds_barrier();
+    }
+
+    // One x block of 16 key channels at a time: the three sums for its 64 rows,
+    // then dq, dk and d gamma of those elements.  d gamma goes to the workspace
+    // in place of dQp (each element read, then written, by the same lane).
+    const float *dKm = a.ws.dKm + ci * (C * K), *Zg = a.ws.dWn + ci * (C * K);
+    float *dQp = a.ws.dQp + ci * (C * K);
+    DT *dq = (DT *)a.dq + r0 * K, *dk = (DT *)a.dk + r0 * K;
+#pragma unroll 1
+    for (int xi = 0; xi < XB; ++xi) {
+        const int x = 16 * (XB * w + xi) + r16;   // key channel of this lane
+        float gv[4][4], grho[4];                  // gamma at rows 16 R + 4 gq + e, and at rho_R
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gv[R][e] = gam[(16 * R + 4 * gq + e) * K + x];
+            grho[R] = gam[(16 * R + 8) * K + x];
+        }
+        f32x4 accq[4], acck[4], accs[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            accq[R] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acck[R] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int J = 0; J <= R; ++J) {
+                const f32x4 ap = *reinterpret_cast<const f32x4 *>(sdP + (16 * R + r16) * L + 16 * J + 4 * gq);
+                const f32x4 ag = *reinterpret_cast<const f32x4 *>(sdG + (16 * R + r16) * L + 16 * J + 4 * gq);
+                const f32x4 bk = *reinterpret_cast<const f32x4 *>(sKt + x * L + 16 * J + 4 * gq);
+                f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pq = mfma_f32(ap[e], bk[e], pq);
+                    pk = mfma_f32(ag[e], bk[e], pk);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float f = CH ? __expf(gv[R][e] - grho[J]) : 1.f;
+                    accq[R][e] = fmaf(f, pq[e], accq[R][e]);
+                    acck[R][e] = fmaf(f, pk[e], acck[R][e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int U = 0; U < 4; ++U) {
+            accs[U] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int I = U; I < 4; ++I) {
+                // A = dG^T and dP^T: rows 16 U + r16, k = 16 I + 4 gq + e
+                f32x4 ag, ap;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ag[e] = sdG[(16 * I + 4 * gq + e) * L + 16 * U + r16];
+                    ap[e] = sdP[(16 * I + 4 * gq + e) * L + 16 * U + r16];
+                }
+                const f32x4 bk = *reinterpret_cast<const f32x4 *>(sKh + x * L + 16 * I + 4 * gq);
+                const f32x4 bq = *reinterpret_cast<const f32x4 *>(sQh + x * L + 16 * I + 4 * gq);
+                f32x4 ps = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ps = mfma_f32(ag[e], bk[e], ps);
+                    ps = mfma_f32(ap[e], bq[e], ps);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float f = CH ? __expf(grho[I] - gv[U][e]) : 1.f;
+                    accs[U][e] = fmaf(f, ps[e], accs[U][e]);
+                }
+            }
+        }
+        // per element: dq, dk, d gamma; the gn terms summed over this channel
+        const float gn = gam[(C - 1) * K + x];
+        float dgn = 0.f;
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 16 * R + 4 * gq + e;
+                const float gr = gam[rr * K + x];
+                const float kr = rr < n ? to_f32(k[rr * H * K + x]) : 0.f;
+                const float qr = rr < n ? to_f32(q[rr * H * K + x]) : 0.f;
+                const float eg = __expf(gr), em = __expf(gn - gr);
+                const float dqp = dQp[rr * K + x], dkm = dKm[rr * K + x], z = Zg[rr * K + x] * sb[rr];
+                const float aq = accq[R][e], ak = acck[R][e], as = accs[R][e];
+                dQp[rr * K + x] = qr * aq + kr * (ak - as) + (dqp * qr + z * kr) * eg - dkm * kr * em;
+                dgn = fmaf(dkm * kr, em, dgn);
+                if (rr < n) {
+                    dq[rr * H * K + x] = from_f32<DT>(fmaf(dqp, eg, aq));
+                    dk[rr * H * K + x] = from_f32<DT>(ak + as + z * eg + dkm * em);
+                }
+            }
+        dgn += __shfl_xor(dgn, 16);
+        dgn += __shfl_xor(dgn, 32);
+        if (gq == 0) sdgn[x] = dgn;
+    }
+    // d gamma (global) and sdgn are read below by other threads: a full barrier
+    __syncthreads();
+    // dg = reverse running sum of d gamma plus the gn terms, one channel per thread
+    const int x = tid % K, sp = tid / K, rb = sp * RP;
+    float dgm[RP];
+    {
+        float tot = 0.f;
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+            dgm[i] = dQp[(rb + i) * K + x];
+            tot += dgm[i];
+        }
+        stot[sp * K + x] = tot;
+    }
+    lds_barrier();
+    float run = a.ws.dgn[ci * K + x] + sdgn[x];
+#pragma unroll
+    for (int p = 0; p < NSPL; ++p) run += p > sp ? stot[p * K + x] : 0.f;
+    float *sdg = sKt;   // [C][K] row sums for the scalar gate (the k tile is no longer read)
+#pragma unroll
+    for (int i = RP - 1; i >= 0; --i) {
+        const int r = rb + i;
+        run += dgm[i];
+        if (CH) {
+            if (r < n) a.dg[(r0 + r * H) * K + x] = run;
+        } else {
+            sdg[r * K + x] = run;
         }
     }
     if (!CH) {
         lds_barrier();
         if (tid < n) {
-            float s = 0.f;
-            for (int y = 0; y < K; ++y) s += sk[tid * K + y];
-            a.dg[r0 + tid * H] = s;
+            float sum = 0.f;
+            for (int y = 0; y < K; ++y) sum += sdg[tid * K + y];
+            a.dg[r0 + tid * H] = sum;
         }
     }
-    if (tid < n) a.dbeta[r0 + tid * H] = sdb[tid];
 }
 
 // ---------------------------------------------------------------- host side
@@ -842,11 +972,11 @@ template <int K, int V> struct BwLds {
     static constexpr int states = 4 * (VB * LK + 2 * VB * LC + C * VP + C);
     static constexpr int dstates = 4 * (VB * LK + VB * L2 + VB * LC + C);
     static constexpr int vgrad = 4 * (2 * K * 17 + 4 * C * 17 + C * CP + C);
-    static constexpr int kscr12 = 2 * C * KP + C * CP, kscr3 = 3 * C * K;
-    static constexpr int kgrad = 4 * (2 * C + 2 * (BW_NTHR / K) * K + 2 * C * CP +
-                                      (kscr12 > kscr3 ? kscr12 : kscr3));
+    static constexpr int kgrad1 = 4 * (2 * C + 2 * C * KP + 3 * C * CP);
+    static constexpr int kgrad2 = 4 * (3 * K * LC + 2 * C * LC + 2 * C + (BW_NTHR / K) * K + K);
     static_assert(prep <= 160 * 1024 && states <= 160 * 1024 && dstates <= 160 * 1024 &&
-                  vgrad <= 160 * 1024 && kgrad <= 160 * 1024, "LDS budget");
+                  vgrad <= 160 * 1024 && kgrad1 <= 160 * 1024 && kgrad2 <= 160 * 1024,
+                  "LDS budget");
 };
 
 template <typename F> static hipError_t set_lds(F *kern, int bytes, bool &done)
@@ -862,13 +992,14 @@ template <typename DT, int K, int V, bool CH>
 static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
 {
     using L = BwLds<K, V>;
-    static bool s1 = false, s2 = false, s3 = false, s4 = false, s5 = false;
+    static bool s1 = false, s2 = false, s3 = false, s4 = false, s5 = false, s6 = false;
     hipError_t e;
     if ((e = set_lds(bwd_prep_kernel<DT, K, CH>, L::prep, s1)) != hipSuccess) return e;
     if ((e = set_lds(bwd_states_kernel<DT, K, V>, L::states, s2)) != hipSuccess) return e;
     if ((e = set_lds(bwd_dstates_kernel<DT, K, V>, L::dstates, s3)) != hipSuccess) return e;
     if ((e = set_lds(bwd_vgrad_kernel<DT, K, V>, L::vgrad, s4)) != hipSuccess) return e;
-    if ((e = set_lds(bwd_kgrad_kernel<DT, K, CH>, L::kgrad, s5)) != hipSuccess) return e;
+    if ((e = set_lds(bwd_kgrad1_kernel<DT, K>, L::kgrad1, s5)) != hipSuccess) return e;
+    if ((e = set_lds(bwd_kgrad2_kernel<DT, K, CH>, L::kgrad2, s6)) != hipSuccess) return e;
     const unsigned nch = (unsigned)(nslices * a.NC), nvb = (unsigned)(nslices * (V / L::VB));
     if (nch > 0) {
         hipLaunchKernelGGL((bwd_prep_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::prep, st, a);
@@ -877,7 +1008,8 @@ static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
     hipLaunchKernelGGL((bwd_dstates_kernel<DT, K, V>), dim3(nvb), dim3(BW_NTHR), L::dstates, st, a);
     if (nch > 0) {
         hipLaunchKernelGGL((bwd_vgrad_kernel<DT, K, V>), dim3(nch), dim3(BW_NTHR), L::vgrad, st, a);
-        hipLaunchKernelGGL((bwd_kgrad_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::kgrad, st, a);
+        hipLaunchKernelGGL((bwd_kgrad1_kernel<DT, K>), dim3(nch), dim3(BW_NTHR), L::kgrad1, st, a);
+        hipLaunchKernelGGL((bwd_kgrad2_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::kgrad2, st, a);
     }
     return hipGetLastError();
 }
