@@ -44,6 +44,7 @@ struct BwArgs {
     float *dg, *dbeta, *dS0;                 // dS0 may be null (not wanted)
     BwWs ws;
     int T, H, NC;
+    int NS;                                  // slices, B * H
 };
 
 // Byte size of the workspace for nchunks chunks; with base != null also fills

@@ -85,6 +85,23 @@ template <int M, int N, int TM, int TN> struct Tile {
     __device__ __forceinline__ int col(int j) const { return nt + j * NS; }
 };
 
+// (slice, block of 16 value columns) of a sweep workgroup.  Workgroups are
+// dealt to the 8 XCDs in turn (workgroup i to XCD i mod 8); when the slice count
+// allows, the value blocks of one slice stay on one XCD, so the per-chunk
+// operands that all of them read come from one L2 rather than eight.
+__device__ __forceinline__ void sweep_block(int nslices, int nvb, int &sl, int &vb)
+{
+    const int b = blockIdx.x;
+    if (nslices % 8 == 0) {
+        const int j = b >> 3;
+        sl = (b & 7) + 8 * (j / nvb);
+        vb = j % nvb;
+    } else {
+        sl = b / nvb;
+        vb = b % nvb;
+    }
+}
+
 // Row of token t of slice sl in the [B, T, H] token layout.
 __device__ __forceinline__ long tok_row(const BwArgs &a, int sl, int t)
 {
@@ -327,7 +344,9 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
     float *sV = sDt + VB * LC;       // [C][VP]   v tile
     float *sb = sV + C * VP;         // [C]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r = lane & 15;
-    const int vb = blockIdx.x % NVB, sl = blockIdx.x / NVB, v0 = vb * VB;
+    int sl, vb;
+    sweep_block(a.NS, NVB, sl, vb);
+    const int v0 = vb * VB;
     const long H = a.H;
 
     f32x4 fKp[K / 16];       // Kp row 16 w + r
@@ -424,7 +443,9 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
     float *sdDt = sOYt + VB * L2;    // [16][LC]  dDelta, transposed
     float *sb = sdDt + VB * LC;      // [C]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r = lane & 15;
-    const int vb = blockIdx.x % NVB, sl = blockIdx.x / NVB, v0 = vb * VB;
+    int sl, vb;
+    sweep_block(a.NS, NVB, sl, vb);
+    const int v0 = vb * VB;
     const long H = a.H;
 
     f32x4 fKm[K / 16];             // Km row 16 w + r

@@ -288,7 +288,7 @@ gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const floa
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
     gdn::bw_workspace((unsigned long long)nch, K, V, workspace, &a.ws);
-    a.T = T; a.H = H; a.NC = (T + 63) / 64;
+    a.T = T; a.H = H; a.NC = (T + 63) / 64; a.NS = B * H;
     const hipError_t e = gdn::chunk_bwd_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL, K, V,
                                                a, (long)B * H, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;

@@ -119,3 +119,36 @@ def test_bwd_benchmark_shape_sampled():
         err = _errors(got, ref)
         _say(f"[bwd] slice ({b},{h}): " + " ".join(f"{n}={e:.2e}" for n, e in err.items()))
         assert max(err.values()) <= TOL_BF16, err
+
+
+@pytest.mark.parametrize("gval", [-5.0, 0.0])
+@pytest.mark.parametrize("gate", ["channel", "head"])
+def test_bwd_decay_at_the_domain_edges(gate, gval):
+    """Every log-decay at the edge of the per-channel domain [-5, 0] (the
+    Atomic-GDN2 card, section 2.1): the largest in-chunk decay range the pair
+    products have to carry, and no decay at all."""
+    cfg = _cfg(2, 200, 2, 128, 128, "fp32", gate, seed=11)
+    d, gr = chunk_inputs(cfg), grad_inputs(cfg)
+    d["g"] = torch.full_like(d["g"], gval)
+    _say(f"[bwd] g = {gval} everywhere, {gate} gate")
+    out = _run(d, gr)
+    for n, t in out.items():
+        assert torch.isfinite(t).all(), n
+    ref = oracle_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], gr["d_o"], gr["dS_T"])
+    err = _errors(out, ref)
+    _say(f"[bwd] " + " ".join(f"{n}={e:.2e}" for n, e in err.items()))
+    assert max(err.values()) <= TOL_FP32, err
+
+
+@pytest.mark.parametrize("K,V", [(128, 64), (64, 128)])
+def test_bwd_slice_count_multiple_of_eight(K, V):
+    """8 slices: the sweeps keep the value blocks of a slice on one XCD (the
+    other tests use slice counts that take the plain mapping)."""
+    cfg = _cfg(2, 130, 4, K, V, "fp32", "channel", seed=21)
+    d, gr = chunk_inputs(cfg), grad_inputs(cfg)
+    _say(f"[bwd] 8 slices {K}x{V}")
+    out = _run(d, gr)
+    ref = oracle_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], gr["d_o"], gr["dS_T"])
+    err = _errors(out, ref)
+    _say(f"[bwd] " + " ".join(f"{n}={e:.2e}" for n, e in err.items()))
+    assert max(err.values()) <= TOL_FP32, err
