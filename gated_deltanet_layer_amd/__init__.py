@@ -11,10 +11,15 @@ Entry points (same names as the C ABI):
     gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist)
     gdn_chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace)
     gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk=64) -> bytes
+    gdn_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, cs_q, cs_k, cs_v,
+                 q, k, v, g, beta, cs_q_out, cs_k_out, cs_v_out, g_cap=5.0, act="silu")
+    gdn_recurrent_step_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v,
+                 cs_q, cs_k, cs_v, cs_q_out, cs_k_out, cs_v_out, S, o, g_cap=5.0, act="silu")
 Conveniences that allocate the outputs:
     chunk_fwd(q, k, v, g, beta, S0=None, want_o=True) -> (o, S_T)
     recurrent_step_(q, k, v, g, beta, S) -> o      (S updated in place)
     chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T) -> dict of dq, dk, dv, dg, dbeta, dS0
+    prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, state=None) -> dict
 """
 from __future__ import annotations
 
@@ -28,9 +33,11 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_OK, GDN_EINVAL, GDN_ENOTSUP, GDN_EHIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_HEAD, GDN_GATE_CHANNEL = 0, 1
+GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
+_ACTS = {"none": GDN_ACT_NONE, "silu": GDN_ACT_SILU}
 SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_steps",
-           "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_status_str",
-           "gdn_abi_version")
+           "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_prologue",
+           "gdn_recurrent_step_prologue", "gdn_status_str", "gdn_abi_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -69,6 +76,13 @@ def lib() -> ctypes.CDLL:
         L.gdn_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp,
                                     vp, sz, i, i, i, i, i, i, i, i, vp]
         L.gdn_chunk_bwd.restype = i
+        f = ctypes.c_float
+        L.gdn_prologue.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, vp, vp, vp, vp, fp, fp,
+                                   vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+        L.gdn_prologue.restype = i
+        L.gdn_recurrent_step_prologue.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, vp,
+                                                  vp, vp, vp, fp, vp, i, i, i, i, f, i, i, i, vp]
+        L.gdn_recurrent_step_prologue.restype = i
         L.gdn_status_str.argtypes = [i]
         L.gdn_status_str.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -311,3 +325,109 @@ def recurrent_step_(q, k, v, g, beta, S, o=None, stream=None):
         o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     gdn_recurrent_step(q, k, v, g, beta, S, o, stream=stream)
     return o
+
+
+def gdn_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, cs_q, cs_k, cs_v, q, k, v, g,
+                 beta, cs_q_out, cs_k_out, cs_v_out, g_cap: float = 5.0, act: str = "silu",
+                 stream=None) -> None:
+    """The prologue of a chunk-mode call (convolution, activation, q/k norm, gates).
+
+    Raw q_raw, k_raw [B,T,H,K] and v_raw [B,T,H,V] (fp32 or bf16), g_raw [B,T,H(,K)] and
+    b_raw [B,T,H] fp32, taps w_q, w_k [H*K,4] and w_v [H*V,4] fp32, carried states
+    cs_* [B,3,H*D] (raw dtype) or None.  Writes q, k, v, g, beta and, if given, the
+    states after the sequence (each may be its own input).
+    """
+    import torch
+    if q_raw.dim() != 4 or v_raw.dim() != 4:
+        raise ValueError("q_raw, k_raw, v_raw must be [B, T, H, D]")
+    B, T, H, K = q_raw.shape
+    V = v_raw.shape[-1]
+    dev = q_raw.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    dt = q_raw.dtype
+    for t, name in ((q_raw, "q_raw"), (k_raw, "k_raw"), (q, "q"), (k, "k")):
+        _check(t, name, (B, T, H, K), dt, dev)
+    for t, name in ((v_raw, "v_raw"), (v, "v")):
+        _check(t, name, (B, T, H, V), dt, dev)
+    gshape = (B, T, H, K) if g_raw.dim() == 4 else (B, T, H)
+    gate = GDN_GATE_CHANNEL if g_raw.dim() == 4 else GDN_GATE_HEAD
+    for t, name in ((g_raw, "g_raw"), (g, "g")):
+        _check(t, name, gshape, torch.float32, dev)
+    for t, name in ((b_raw, "b_raw"), (beta, "beta")):
+        _check(t, name, (B, T, H), torch.float32, dev)
+    for t, name, D in ((w_q, "w_q", H * K), (w_k, "w_k", H * K), (w_v, "w_v", H * V)):
+        _check(t, name, (D, 4), torch.float32, dev)
+    for t, name, D in ((cs_q, "cs_q", H * K), (cs_k, "cs_k", H * K), (cs_v, "cs_v", H * V),
+                       (cs_q_out, "cs_q_out", H * K), (cs_k_out, "cs_k_out", H * K),
+                       (cs_v_out, "cs_v_out", H * V)):
+        _check(t, name, (B, 3, D), dt, dev)
+    rc = lib().gdn_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(g_raw), _ptr(b_raw),
+                            _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(cs_q), _ptr(cs_k), _ptr(cs_v),
+                            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cs_q_out),
+                            _ptr(cs_k_out), _ptr(cs_v_out), B, T, H, K, V, float(g_cap),
+                            _ACTS[act], _dtype_code(q_raw), gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_prologue")
+
+
+def prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, state=None, g_cap: float = 5.0,
+             act: str = "silu", want_state: bool = True, stream=None):
+    """Allocate the outputs (and the states after the sequence if wanted), run
+    gdn_prologue; ``state`` is a (cs_q, cs_k, cs_v) tuple or None.  Returns a dict
+    with q, k, v, g, beta and state (a tuple, or None)."""
+    import torch
+    B, T, H, K = q_raw.shape
+    V = v_raw.shape[-1]
+    dev, dt = q_raw.device, q_raw.dtype
+    cs = state if state is not None else (None, None, None)
+    outs = None
+    if want_state:
+        outs = (torch.empty(B, 3, H * K, dtype=dt, device=dev), torch.empty(B, 3, H * K, dtype=dt, device=dev),
+                torch.empty(B, 3, H * V, dtype=dt, device=dev))
+    r = dict(q=torch.empty_like(q_raw), k=torch.empty_like(k_raw), v=torch.empty_like(v_raw),
+             g=torch.empty_like(g_raw), beta=torch.empty_like(b_raw))
+    o3 = outs if outs is not None else (None, None, None)
+    gdn_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, cs[0], cs[1], cs[2], r["q"],
+                 r["k"], r["v"], r["g"], r["beta"], o3[0], o3[1], o3[2], g_cap=g_cap, act=act,
+                 stream=stream)
+    r["state"] = outs
+    return r
+
+
+def gdn_recurrent_step_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, cs_q, cs_k,
+                                cs_v, cs_q_out, cs_k_out, cs_v_out, S, o, g_cap: float = 5.0,
+                                act: str = "silu", stream=None) -> None:
+    """One decode token from the raw projections: prologue and recurrence in one
+    kernel.  q_raw, k_raw [N,H,K], v_raw [N,H,V]; g_raw [N,H(,K)], b_raw [N,H] fp32;
+    cs_* [N,3,H*D] or None; cs_*_out the states after the token (never the inputs)
+    or None; S [N,H,K,V] fp32 updated in place; o [N,H,V] or None."""
+    import torch
+    if q_raw.dim() != 3 or v_raw.dim() != 3:
+        raise ValueError("q_raw, k_raw, v_raw must be [N, H, D]")
+    N, H, K = q_raw.shape
+    V = v_raw.shape[-1]
+    dev = q_raw.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    dt = q_raw.dtype
+    _check(k_raw, "k_raw", (N, H, K), dt, dev)
+    _check(v_raw, "v_raw", (N, H, V), dt, dev)
+    gate = GDN_GATE_CHANNEL if g_raw.dim() == 3 else GDN_GATE_HEAD
+    _check(g_raw, "g_raw", (N, H, K) if gate == GDN_GATE_CHANNEL else (N, H), torch.float32, dev)
+    _check(b_raw, "b_raw", (N, H), torch.float32, dev)
+    for t, name, D in ((w_q, "w_q", H * K), (w_k, "w_k", H * K), (w_v, "w_v", H * V)):
+        _check(t, name, (D, 4), torch.float32, dev)
+    for t, name, D in ((cs_q, "cs_q", H * K), (cs_k, "cs_k", H * K), (cs_v, "cs_v", H * V),
+                       (cs_q_out, "cs_q_out", H * K), (cs_k_out, "cs_k_out", H * K),
+                       (cs_v_out, "cs_v_out", H * V)):
+        _check(t, name, (N, 3, D), dt, dev)
+    _check(S, "S", (N, H, K, V), torch.float32, dev)
+    _check(o, "o", (N, H, V), dt, dev)
+    rc = lib().gdn_recurrent_step_prologue(
+        _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(g_raw), _ptr(b_raw), _ptr(w_q), _ptr(w_k),
+        _ptr(w_v), _ptr(cs_q), _ptr(cs_k), _ptr(cs_v), _ptr(cs_q_out), _ptr(cs_k_out),
+        _ptr(cs_v_out), _ptr(S), _ptr(o), N, H, K, V, float(g_cap), _ACTS[act],
+        _dtype_code(q_raw), gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_recurrent_step_prologue")

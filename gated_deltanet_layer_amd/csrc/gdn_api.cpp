@@ -8,6 +8,7 @@
 
 #include "../../include/gdn.h"
 #include "chunk_bwd.h"
+#include "prologue.h"
 
 namespace gdn {
 hipError_t chunk_fwd_launch(bool bf16, bool channel, int K, const void *q, const void *k,
@@ -291,6 +292,135 @@ gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const floa
     a.T = T; a.H = H; a.NC = (T + 63) / 64; a.NS = B * H;
     const hipError_t e = gdn::chunk_bwd_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL, K, V,
                                                a, (long)B * H, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_prologue(const void *q_raw, const void *k_raw, const void *v_raw, const float *g_raw,
+                        const float *b_raw, const float *w_q, const float *w_k, const float *w_v,
+                        const void *cs_q, const void *cs_k, const void *cs_v, void *q, void *k,
+                        void *v, float *g, float *beta, void *cs_q_out, void *cs_k_out,
+                        void *cs_v_out, int B, int T, int H, int K, int V, float g_cap,
+                        gdn_act act, gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EINVAL;
+    if (gate != GDN_GATE_HEAD && gate != GDN_GATE_CHANNEL) return GDN_EINVAL;
+    if (act != GDN_ACT_NONE && act != GDN_ACT_SILU) return GDN_EINVAL;
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0 || !(g_cap > 0.f)) return GDN_EINVAL;
+    const long long es = dtype == GDN_BF16 ? 2 : 4;
+    const long long ntok = prod(B, T, H), nqk = prod(B, T, H, K), nv = prod(B, T, H, V);
+    const long long nsk = prod(B, 3, H, K), nsv = prod(B, 3, H, V);
+    const long long nwk = prod(H, K, 4), nwv = prod(H, V, 4);
+    if (ntok < 0 || nqk < 0 || nv < 0 || nsk < 0 || nsv < 0 || nwk < 0 || nwv < 0) return GDN_EINVAL;
+    const bool ch = gate == GDN_GATE_CHANNEL;
+    const long long ng = ch ? nqk : ntok;
+    if (ntok > 0 && (!q_raw || !k_raw || !v_raw || !g_raw || !b_raw || !w_q || !w_k || !w_v ||
+                     !q || !k || !v || !g || !beta))
+        return GDN_EINVAL;
+    for (const void *p : {q_raw, k_raw, v_raw, (const void *)q, (const void *)k, (const void *)v,
+                          (const void *)w_q, (const void *)w_k, (const void *)w_v, cs_q, cs_k,
+                          cs_v, (const void *)cs_q_out, (const void *)cs_k_out,
+                          (const void *)cs_v_out})
+        if (p && !aligned16(p)) return GDN_EINVAL;
+    for (const void *p : {(const void *)g_raw, (const void *)g})
+        if (p && !aligned(p, ch ? 16 : 4)) return GDN_EINVAL;
+    for (const void *p : {(const void *)b_raw, (const void *)beta})
+        if (p && !aligned(p, 4)) return GDN_EINVAL;
+    const Range in[] = {range(q_raw, nqk * es), range(k_raw, nqk * es), range(v_raw, nv * es),
+                        range(g_raw, ng * 4), range(b_raw, ntok * 4), range(w_q, nwk * 4),
+                        range(w_k, nwk * 4), range(w_v, nwv * 4)};
+    const Range sin[] = {range(cs_q, cs_q ? nsk * es : 0), range(cs_k, cs_k ? nsk * es : 0),
+                         range(cs_v, cs_v ? nsv * es : 0)};
+    const Range sout[] = {range(cs_q_out, cs_q_out ? nsk * es : 0),
+                          range(cs_k_out, cs_k_out ? nsk * es : 0),
+                          range(cs_v_out, cs_v_out ? nsv * es : 0)};
+    const Range out[] = {range(q, nqk * es), range(k, nqk * es), range(v, nv * es),
+                         range(g, ng * 4), range(beta, ntok * 4), sout[0], sout[1], sout[2]};
+    const int nout = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (Range r : in)
+            if (overlap(out[i], r)) return GDN_EINVAL;
+        for (int j = 0; j < 3; ++j) {
+            // a state output may be exactly its own input
+            const bool own = i >= 5 && i - 5 == j && sin[j].lo == out[i].lo && sin[j].hi == out[i].hi;
+            if (!own && overlap(out[i], sin[j])) return GDN_EINVAL;
+        }
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(out[i], out[j])) return GDN_EINVAL;
+    }
+    if (!kv_supported(K) || !kv_supported(V)) return GDN_ENOTSUP;
+    // one thread per token and 8 channels (at most 16 per token): the grid's
+    // work-items must stay below 2^32
+    if (prod(ntok, 16) >= (1LL << 32) || prod(B, H, 16) >= (1LL << 32)) return GDN_ENOTSUP;
+    if (B == 0 || H == 0) return GDN_OK;
+    if (T == 0 && !cs_q_out && !cs_k_out && !cs_v_out) return GDN_OK;
+
+    gdn::PrArgs a;
+    a.q_raw = q_raw; a.k_raw = k_raw; a.v_raw = v_raw; a.g_raw = g_raw; a.b_raw = b_raw;
+    a.w_q = w_q; a.w_k = w_k; a.w_v = w_v; a.cs_q = cs_q; a.cs_k = cs_k; a.cs_v = cs_v;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.cs_q_out = cs_q_out; a.cs_k_out = cs_k_out; a.cs_v_out = cs_v_out;
+    a.cap = g_cap; a.B = B; a.T = T; a.H = H;
+    const hipError_t e = gdn::prologue_launch(dtype == GDN_BF16, ch, act == GDN_ACT_SILU, K, V, a,
+                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_recurrent_step_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
+                                       const float *g_raw, const float *b_raw, const float *w_q,
+                                       const float *w_k, const float *w_v, const void *cs_q,
+                                       const void *cs_k, const void *cs_v, void *cs_q_out,
+                                       void *cs_k_out, void *cs_v_out, float *S, void *o, int N,
+                                       int H, int K, int V, float g_cap, gdn_act act,
+                                       gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EINVAL;
+    if (gate != GDN_GATE_HEAD && gate != GDN_GATE_CHANNEL) return GDN_EINVAL;
+    if (act != GDN_ACT_NONE && act != GDN_ACT_SILU) return GDN_EINVAL;
+    if (N < 0 || H < 0 || K <= 0 || V <= 0 || !(g_cap > 0.f)) return GDN_EINVAL;
+    const long long es = dtype == GDN_BF16 ? 2 : 4;
+    const long long ns = prod(N, H), nk = prod(N, H, K), nv = prod(N, H, V);
+    const long long nsk = prod(N, 3, H, K), nsv = prod(N, 3, H, V), nst = prod(N, H, K, V);
+    const long long nwk = prod(H, K, 4), nwv = prod(H, V, 4);
+    if (ns < 0 || nk < 0 || nv < 0 || nsk < 0 || nsv < 0 || nst < 0 || nwk < 0 || nwv < 0)
+        return GDN_EINVAL;
+    const bool ch = gate == GDN_GATE_CHANNEL;
+    const long long ng = ch ? nk : ns;
+    if (ns > 0 && (!q_raw || !k_raw || !v_raw || !g_raw || !b_raw || !w_q || !w_k || !w_v || !S))
+        return GDN_EINVAL;
+    for (const void *p : {q_raw, k_raw, v_raw, cs_q, cs_k, cs_v, (const void *)cs_q_out,
+                          (const void *)cs_k_out, (const void *)cs_v_out, (const void *)o})
+        if (p && !aligned(p, (unsigned)es)) return GDN_EINVAL;
+    for (const void *p : {(const void *)w_q, (const void *)w_k, (const void *)w_v, (const void *)S})
+        if (p && !aligned16(p)) return GDN_EINVAL;
+    for (const void *p : {(const void *)g_raw, (const void *)b_raw})
+        if (p && !aligned(p, 4)) return GDN_EINVAL;
+    const Range in[] = {range(q_raw, nk * es), range(k_raw, nk * es), range(v_raw, nv * es),
+                        range(g_raw, ng * 4), range(b_raw, ns * 4), range(w_q, nwk * 4),
+                        range(w_k, nwk * 4), range(w_v, nwv * 4),
+                        range(cs_q, cs_q ? nsk * es : 0), range(cs_k, cs_k ? nsk * es : 0),
+                        range(cs_v, cs_v ? nsv * es : 0)};
+    const Range out[] = {range(S, nst * 4), range(o, o ? nv * es : 0),
+                         range(cs_q_out, cs_q_out ? nsk * es : 0),
+                         range(cs_k_out, cs_k_out ? nsk * es : 0),
+                         range(cs_v_out, cs_v_out ? nsv * es : 0)};
+    const int nout = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (Range r : in)
+            if (overlap(out[i], r)) return GDN_EINVAL;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(out[i], out[j])) return GDN_EINVAL;
+    }
+    if (!kv_supported(K) || !kv_supported(V)) return GDN_ENOTSUP;
+    if (prod(ns, V / 64 > 0 ? V / 64 : 1) > 0x7fffffffLL) return GDN_ENOTSUP;
+    if (ns == 0) return GDN_OK;
+
+    gdn::RpArgs a;
+    a.q_raw = q_raw; a.k_raw = k_raw; a.v_raw = v_raw; a.g_raw = g_raw; a.b_raw = b_raw;
+    a.w_q = w_q; a.w_k = w_k; a.w_v = w_v; a.cs_q = cs_q; a.cs_k = cs_k; a.cs_v = cs_v;
+    a.cs_q_out = cs_q_out; a.cs_k_out = cs_k_out; a.cs_v_out = cs_v_out;
+    a.S = S; a.o = o; a.cap = g_cap; a.H = H;
+    const hipError_t e = gdn::step_prologue_launch(dtype == GDN_BF16, ch, act == GDN_ACT_SILU, K, V,
+                                                   a, ns, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

@@ -24,7 +24,7 @@ from typing import Optional
 import torch
 
 __all__ = ["ChunkConfig", "DecodeConfig", "CHUNK_CONFIGS", "DECODE_CONFIG", "BWD_CONFIG",
-           "chunk_inputs", "decode_inputs", "grad_inputs", "head_tokens"]
+           "chunk_inputs", "decode_inputs", "grad_inputs", "prologue_inputs", "head_tokens"]
 
 
 @dataclass(frozen=True)
@@ -165,3 +165,30 @@ def grad_inputs(cfg: ChunkConfig, device="cpu", seed: Optional[int] = None):
     d_o = torch.randn(cfg.B, cfg.T, cfg.H, cfg.V, **f32).to(_DT[cfg.dtype])
     dS_T = torch.randn(cfg.B, cfg.H, cfg.K, cfg.V, **f32)
     return dict(d_o=d_o.contiguous(), dS_T=dS_T.contiguous())
+
+
+def prologue_inputs(B: int, T: int, H: int, K: int, V: int, dtype: str = "bf16",
+                    gate: str = "channel", state: bool = True, device="cpu", seed: int = 0):
+    """Raw inputs of the prologue: the projections' outputs q_raw, k_raw [B,T,H,K],
+    v_raw [B,T,H,V] ~ N(0,1) (storage dtype), g_raw [B,T,H(,K)] ~ N(0, 2^2),
+    b_raw [B,T,H] ~ N(0,1); depthwise taps w_q, w_k [H*K,4], w_v [H*V,4] ~ N(0, 0.5^2)
+    fp32; carried states cs_q, cs_k [B,3,H*K], cs_v [B,3,H*V] ~ N(0,1) (storage
+    dtype) or None.  Drawn in that order from one generator."""
+    device = torch.device(device)
+    gen = _gen(device, seed)
+    dt = _DT[dtype]
+    f32 = dict(device=device, dtype=torch.float32, generator=gen)
+    d = dict(q_raw=torch.randn(B, T, H, K, **f32).to(dt), k_raw=torch.randn(B, T, H, K, **f32).to(dt),
+             v_raw=torch.randn(B, T, H, V, **f32).to(dt))
+    d["g_raw"] = 2.0 * torch.randn(*((B, T, H, K) if gate == "channel" else (B, T, H)), **f32)
+    d["b_raw"] = torch.randn(B, T, H, **f32)
+    d["w_q"] = 0.5 * torch.randn(H * K, 4, **f32)
+    d["w_k"] = 0.5 * torch.randn(H * K, 4, **f32)
+    d["w_v"] = 0.5 * torch.randn(H * V, 4, **f32)
+    if state:
+        d["cs_q"] = torch.randn(B, 3, H * K, **f32).to(dt)
+        d["cs_k"] = torch.randn(B, 3, H * K, **f32).to(dt)
+        d["cs_v"] = torch.randn(B, 3, H * V, **f32).to(dt)
+    else:
+        d["cs_q"] = d["cs_k"] = d["cs_v"] = None
+    return {n: (x.contiguous() if x is not None else None) for n, x in d.items()}

@@ -1,5 +1,6 @@
 /*
- * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet mixer: forward and backward.
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet mixer: prologue, forward,
+ * decode, verify and backward.
  *
  * The operation (Atomic-GDN2 model card, section 2.1 "Gated DeltaNet-2"), for
  * every batch row b and head h independently, token by token:
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -67,6 +68,7 @@ typedef enum {
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 typedef enum { GDN_GATE_HEAD = 0, GDN_GATE_CHANNEL = 1 } gdn_gate;
+typedef enum { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_act;
 
 /*
  * Chunkwise forward over a whole sequence batch.
@@ -180,6 +182,67 @@ GDN_API gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, co
                                  float *dbeta, float *dS0, void *workspace,
                                  size_t workspace_bytes, int B, int T, int H, int K, int V,
                                  int chunk, gdn_dtype dtype, gdn_gate gate, void *stream);
+
+/*
+ * The prologue: the steps between the layer's projections and the recurrence,
+ * for a whole chunk-mode call, in one launch.  Per token:
+ *   q, k, v  <- causal depthwise 4-tap convolution over time, per channel (the
+ *               kernel-4 convolution of the DeltaNet layers: "Hybrid layouts:
+ *               three DeltaNet, one attention", 01 Concept): channel c of token
+ *               t is sum_j w[c][j] * raw[t - 3 + j][c], the tokens before the
+ *               sequence taken from the carried state
+ *            <- SiLU if act == GDN_ACT_SILU
+ *   q, k     <- divided by max(L2 norm over the K channels of the head, 1e-12)
+ *   g        <- -min(softplus(g_raw), g_cap)  (g_cap = 5 on the Atomic-GDN2
+ *   beta     <- sigmoid(b_raw)                 card, section 2.1)
+ * so that the outputs feed gdn_chunk_fwd / gdn_chunk_bwd directly.
+ *
+ *   q_raw, k_raw [B, T, H, K]  dtype      v_raw [B, T, H, V]  dtype
+ *   g_raw   shaped as g of gdn_chunk_fwd, fp32      b_raw [B, T, H] fp32
+ *   w_q, w_k [H*K, 4] fp32, w_v [H*V, 4] fp32: the taps of channel c = h*K + x
+ *   cs_q, cs_k [B, 3, H*K], cs_v [B, 3, H*V]  dtype: the raw inputs of the three
+ *           tokens before the sequence (row j = token j - 3), or NULL for zeros
+ *   q, k, v, g, beta   outputs in the layouts of gdn_chunk_fwd's inputs
+ *   cs_*_out  the raw inputs of the last three tokens (older rows from cs_* when
+ *           T < 3), or NULL.  Each may be its own input exactly (updated in place).
+ *
+ * K and V: 64 or 128.  g_cap > 0 (+inf: no cap).  q_raw, k_raw, v_raw, q, k, v,
+ * the taps, the carried states and a per-channel g_raw / g need 16-byte
+ * alignment; b_raw, beta and a scalar g 4 bytes.  No output may overlap an input
+ * or another output, except a state output that is its own input.  B, T or H
+ * equal to 0 is a valid call (with T = 0 the states pass through).
+ */
+GDN_API gdn_status gdn_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
+                                const float *g_raw, const float *b_raw, const float *w_q,
+                                const float *w_k, const float *w_v, const void *cs_q,
+                                const void *cs_k, const void *cs_v, void *q, void *k, void *v,
+                                float *g, float *beta, void *cs_q_out, void *cs_k_out,
+                                void *cs_v_out, int B, int T, int H, int K, int V, float g_cap,
+                                gdn_act act, gdn_dtype dtype, gdn_gate gate, void *stream);
+
+/*
+ * One decode token of N sequences from the raw projections: the prologue above
+ * and gdn_recurrent_step in one kernel (S updated in place, o written).
+ *
+ *   q_raw, k_raw [N, H, K], v_raw [N, H, V] dtype; g_raw [N, H] or [N, H, K] and
+ *   b_raw [N, H] fp32; w_* as for gdn_prologue; cs_* [N, 3, H*K] / [N, 3, H*V]
+ *   dtype or NULL (zeros); cs_*_out the states after this token, or NULL.  A
+ *   state output must not overlap any state input (the value blocks of a head
+ *   all read the incoming q/k state): keep two state buffers and alternate.
+ *   S [N, H, K, V] fp32 in place; o [N, H, V] dtype or NULL.
+ *
+ * K and V: 64 or 128.  The taps and S need 16-byte alignment, every other
+ * pointer its element alignment.
+ */
+GDN_API gdn_status gdn_recurrent_step_prologue(const void *q_raw, const void *k_raw,
+                                               const void *v_raw, const float *g_raw,
+                                               const float *b_raw, const float *w_q,
+                                               const float *w_k, const float *w_v,
+                                               const void *cs_q, const void *cs_k,
+                                               const void *cs_v, void *cs_q_out, void *cs_k_out,
+                                               void *cs_v_out, float *S, void *o, int N, int H,
+                                               int K, int V, float g_cap, gdn_act act,
+                                               gdn_dtype dtype, gdn_gate gate, void *stream);
 
 /* Static English text for a status code (never NULL). */
 GDN_API const char *gdn_status_str(gdn_status s);

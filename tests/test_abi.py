@@ -41,7 +41,7 @@ def test_only_declared_symbols_are_exported():
 
 
 def test_version_and_status_strings(L):
-    assert gdn.abi_version() == 3
+    assert gdn.abi_version() == 4
     assert gdn.status_str(0) == "ok"
     assert "invalid" in gdn.status_str(1)
     assert "unsupported" in gdn.status_str(2)
@@ -246,6 +246,81 @@ def test_bwd_workspace_size(L):
         assert _ws_size(L, B, T, H, K, V) == (gdn.GDN_OK, want)
         assert gdn.gdn_chunk_bwd_workspace_size(B, T, H, K, V) == want
     assert ctypes.sizeof(ctypes.c_size_t) == 8
+
+
+def _pro(L, **kw):
+    p = _ptrs(20)
+    a = dict(q_raw=p[0], k_raw=p[1], v_raw=p[2], g_raw=p[3], b_raw=p[4], w_q=p[5], w_k=p[6],
+             w_v=p[7], cs_q=p[8], cs_k=p[9], cs_v=p[10], q=p[11], k=p[12], v=p[13], g=p[14],
+             beta=p[15], cs_q_out=p[16], cs_k_out=p[17], cs_v_out=p[18],
+             B=2, T=50, H=3, K=128, V=128, cap=5.0, act=1, dtype=1, gate=1)
+    a.update(kw)
+    return L.gdn_prologue(*[a[n] for n in ("q_raw", "k_raw", "v_raw", "g_raw", "b_raw", "w_q",
+                                           "w_k", "w_v", "cs_q", "cs_k", "cs_v", "q", "k", "v",
+                                           "g", "beta", "cs_q_out", "cs_k_out", "cs_v_out", "B",
+                                           "T", "H", "K", "V", "cap", "act", "dtype", "gate")],
+                          None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=2), dict(gate=2), dict(act=2), dict(B=-1), dict(T=-1), dict(K=0), dict(V=-1),
+    dict(cap=0.0), dict(cap=-1.0), dict(cap=float("nan")), dict(q_raw=None), dict(w_v=None),
+    dict(beta=None), dict(q=BASE + 11 * SEP + 8), dict(w_k=BASE + 6 * SEP + 4),
+    dict(cs_v=BASE + 10 * SEP + 2), dict(g_raw=BASE + 3 * SEP + 4), dict(b_raw=BASE + 4 * SEP + 2),
+    dict(q=BASE),                       # q over q_raw
+    dict(v=BASE + 7 * SEP),             # v over the v taps
+    dict(g=BASE + 15 * SEP),            # g over beta
+    dict(cs_q_out=BASE + 8 * SEP + 16), # partial overlap with its own input
+    dict(cs_k_out=BASE + 8 * SEP),      # over another state input
+    dict(cs_v_out=BASE + 16 * SEP),     # two outputs on one buffer
+])
+def test_prologue_rejects_invalid(L, kw):
+    assert _pro(L, **kw) == gdn.GDN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(K=96), dict(V=32)])
+def test_prologue_unsupported(L, kw):
+    assert _pro(L, **kw) == gdn.GDN_ENOTSUP
+
+
+def test_prologue_state_in_place_and_no_cap_pass_validation(L):
+    assert _pro(L, cs_q_out=BASE + 8 * SEP, cs_k_out=BASE + 9 * SEP, cs_v_out=BASE + 10 * SEP,
+                cap=float("inf"), K=96) == gdn.GDN_ENOTSUP
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=0, cs_q_out=None, cs_k_out=None,
+                                                           cs_v_out=None)])
+def test_prologue_empty_is_a_noop(L, kw):
+    assert _pro(L, **kw) == gdn.GDN_OK
+
+
+def _stp(L, **kw):
+    p = _ptrs(20)
+    a = dict(q_raw=p[0], k_raw=p[1], v_raw=p[2], g_raw=p[3], b_raw=p[4], w_q=p[5], w_k=p[6],
+             w_v=p[7], cs_q=p[8], cs_k=p[9], cs_v=p[10], cs_q_out=p[11], cs_k_out=p[12],
+             cs_v_out=p[13], S=p[14], o=p[15], N=4, H=3, K=128, V=128, cap=5.0, act=1, dtype=1,
+             gate=1)
+    a.update(kw)
+    return L.gdn_recurrent_step_prologue(*[a[n] for n in (
+        "q_raw", "k_raw", "v_raw", "g_raw", "b_raw", "w_q", "w_k", "w_v", "cs_q", "cs_k", "cs_v",
+        "cs_q_out", "cs_k_out", "cs_v_out", "S", "o", "N", "H", "K", "V", "cap", "act", "dtype",
+        "gate")], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=2), dict(act=-1), dict(N=-1), dict(cap=0.0), dict(S=None), dict(w_q=None),
+    dict(S=BASE + 14 * SEP + 8), dict(w_v=BASE + 7 * SEP + 4), dict(q_raw=BASE + 1),
+    dict(cs_q_out=BASE + 8 * SEP),      # a state output on its input: not allowed here
+    dict(o=BASE + 14 * SEP),            # o on S
+    dict(cs_v_out=BASE + 2 * SEP),      # over v_raw
+])
+def test_step_prologue_rejects_invalid(L, kw):
+    assert _stp(L, **kw) == gdn.GDN_EINVAL
+
+
+def test_step_prologue_unsupported_and_empty(L):
+    assert _stp(L, K=32) == gdn.GDN_ENOTSUP
+    assert _stp(L, N=0) == gdn.GDN_OK
 
 
 def test_element_aligned_vectors_are_accepted_by_validation(L):
