@@ -284,6 +284,97 @@ def bench_bwd(torch, gdn, steps, warmup):
                         "bwd_vgrad_kernel", "bwd_kgrad_kernel"]}
 
 
+def prologue_bytes(B, T, H, K, V, es, channel):
+    """Algorithmic HBM bytes of gdn_prologue: raw q, k, v, g, b read once, q, k, v,
+    g, beta written once, the taps and the carried states once."""
+    gb = (K if channel else 1) * 4
+    per_ht = 2 * ((2 * K + V) * es + gb + 4)
+    return B * T * H * per_ht + H * (2 * K + V) * 16 + 2 * B * 3 * H * (2 * K + V) * es
+
+
+def bench_prologue(torch, gdn, steps, warmup):
+    """gdn_prologue on the headline forward's shape (B=8 H=12 T=8192, d_k=d_v=128,
+    scalar gate, bf16, SiLU) and, on the decode shape (N=256 H=48, per-channel
+    gate), the fused decode token against the prologue and the step as two launches."""
+    from gdn_inputs import prologue_inputs
+    out = {}
+    B, T, H, K, V = 8, 8192, 12, 128, 128
+    d = prologue_inputs(B, T, H, K, V, "bf16", "head", device="cuda")
+    r = {n: torch.empty_like(d[n]) for n in ("q_raw", "k_raw", "v_raw", "g_raw", "b_raw")}
+    cso = [torch.empty_like(d["cs_q"]), torch.empty_like(d["cs_k"]), torch.empty_like(d["cs_v"])]
+    run = lambda: gdn.gdn_prologue(d["q_raw"], d["k_raw"], d["v_raw"], d["g_raw"], d["b_raw"],
+                                   d["w_q"], d["w_k"], d["w_v"], d["cs_q"], d["cs_k"], d["cs_v"],
+                                   r["q_raw"], r["k_raw"], r["v_raw"], r["g_raw"], r["b_raw"],
+                                   cso[0], cso[1], cso[2])
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = prologue_bytes(B, T, H, K, V, 2, False)
+    out["chunk"] = {"workload": f"gdn_prologue, B={B} T={T} H={H} d_k=d_v={K}, scalar gate, bf16, "
+                                f"SiLU, carried states in and out",
+                    "ms": ms, "gbs": nbytes / (ms / 1e3) / 1e9,
+                    "frac_hbm": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_call": nbytes,
+                    "kernel": "prologue_kernel<bf16,128,128,scalar,silu>"}
+    del d, r, cso
+    # the decode token: fused against two launches
+    N, H = 256, 48
+    d = prologue_inputs(N, 1, H, K, V, "bf16", "channel", device="cuda", seed=1)
+    d = {n: (x[:, 0].contiguous() if n in ("q_raw", "k_raw", "v_raw", "g_raw", "b_raw") else x)
+         for n, x in d.items()}
+    S = 0.02 * torch.randn(N, H, K, V, device="cuda")
+    o = torch.empty(N, H, V, dtype=torch.bfloat16, device="cuda")
+    cs = [[d["cs_q"], d["cs_k"], d["cs_v"]],
+          [torch.empty_like(d["cs_q"]), torch.empty_like(d["cs_k"]), torch.empty_like(d["cs_v"])]]
+    pro = {n: torch.empty(N, 1, *d[n].shape[1:], dtype=d[n].dtype, device="cuda")
+           for n in ("q_raw", "k_raw", "v_raw", "g_raw", "b_raw")}
+    raw1 = {n: d[n].unsqueeze(1) for n in ("q_raw", "k_raw", "v_raw", "g_raw", "b_raw")}
+
+    def fused(j):
+        a, b = cs[j % 2], cs[(j + 1) % 2]
+        gdn.gdn_recurrent_step_prologue(d["q_raw"], d["k_raw"], d["v_raw"], d["g_raw"], d["b_raw"],
+                                        d["w_q"], d["w_k"], d["w_v"], a[0], a[1], a[2], b[0], b[1],
+                                        b[2], S, o)
+
+    def two(j):
+        a, b = cs[j % 2], cs[(j + 1) % 2]
+        gdn.gdn_prologue(raw1["q_raw"], raw1["k_raw"], raw1["v_raw"], raw1["g_raw"], raw1["b_raw"],
+                         d["w_q"], d["w_k"], d["w_v"], a[0], a[1], a[2], pro["q_raw"], pro["k_raw"],
+                         pro["v_raw"], pro["g_raw"], pro["b_raw"], b[0], b[1], b[2])
+        gdn.gdn_recurrent_step(pro["q_raw"][:, 0], pro["k_raw"][:, 0], pro["v_raw"][:, 0],
+                               pro["g_raw"][:, 0], pro["b_raw"][:, 0], S, o)
+
+    res = {}
+    for name, fn in (("fused", fused), ("two_launches", two)):
+        for j in range(warmup):
+            fn(j)
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch)
+        e0.record()
+        for j in range(steps):
+            fn(j)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    state = N * H * K * V * 4
+    nb = 2 * state + N * H * ((2 * K + V) * 2 + K * 4 + 4 + V * 2) + H * (2 * K + V) * 16 \
+        + 2 * N * 3 * H * (2 * K + V) * 2
+    out["decode"] = {"workload": f"decode token from the raw projections, N={N} H={H} "
+                                 f"d_k=d_v={K}, per-channel gate, bf16, SiLU, state in place",
+                     "ms_fused": res["fused"], "ms_two_launches": res["two_launches"],
+                     "gbs_fused": nb / (res["fused"] / 1e3) / 1e9,
+                     "frac_hbm_fused": nb / (res["fused"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "bytes_per_step": nb,
+                     "kernel": "recurrent_step_prologue_kernel<bf16,128,128,channel,silu>"}
+    return out
+
+
 def cpu_baseline(chunk_inputs_dev, cfg, target_s=15.0):
     """fp64 oracle on a bounded sample of the prefill workload: whole sequences of
     some (b, h) slices, one OpenMP thread per slice."""
@@ -319,8 +410,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "channel", "verify", "bwd"],
-                    default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "channel", "verify", "bwd",
+                                       "prologue"], default="all")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -403,6 +494,13 @@ def main():
             out["value"] = out["backward"]["mtok_s_fwd_bwd"]
             out["ms_per_step"] = out["backward"]["ms_fwd_bwd"]
             out["config"] = {"workload": out["backward"]["workload"]}
+    if args.only in ("all", "prologue"):
+        out["prologue"] = bench_prologue(torch, gdn, max(3, min(args.steps, 50)), max(1, min(args.warmup, 5)))
+        if ch is None and args.only == "prologue":
+            out["value"] = out["prologue"]["chunk"]["gbs"]
+            out["unit"] = "GB/s"
+            out["ms_per_step"] = out["prologue"]["chunk"]["ms"]
+            out["config"] = {"workload": out["prologue"]["chunk"]["workload"]}
     if ch is not None and not args.no_cpu:
         torch.cuda.synchronize()
         cb = cpu_baseline(ch["inputs"], ch["cfg"])

@@ -62,16 +62,25 @@ template <> __device__ __forceinline__ void st8<__bf16>(__bf16 *p, const float (
     *reinterpret_cast<bf16x8 *>(p) = a;
 }
 
-// The convolution of 8 channels c .. c+7 of token t of batch row b: x is the raw
-// [B, T, D] tensor, cs the carried state [B, 3, D] (null: zeros), w the [D, 4] taps.
-template <typename DT, bool SILU>
-__device__ __forceinline__ void conv8(const DT *x, const DT *cs, const float *w, long b, int t,
-                                      int T, int D, int c, float (&y)[8])
+// Segments (blockIdx.y): 0 q, 1 k, 2 v, 3 gates.  A thread owns 8 channels of
+// one head and walks PR_TT consecutive tokens with the taps in registers and a
+// sliding window of the last four raw rows, so each token costs one 16-byte
+// load.  The K/8 threads of one head are consecutive lanes on the same tokens
+// and reduce the squared norm with shuffles; consecutive heads follow, so a
+// wave reads whole token rows.
+constexpr int PR_TT = 16;
+
+template <typename DT, int W, bool NORM, bool SILU>
+__device__ __forceinline__ void conv_run(const DT *x, const DT *cs, const float *w, DT *y, long b,
+                                         int t0, int T, int D, int c)
 {
+    f32x4 wt[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wt[e] = *reinterpret_cast<const f32x4 *>(w + (long)(c + e) * 4);
     float win[4][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tt = t - 3 + j;
+    for (int j = 0; j < 3; ++j) {
+        const int tt = t0 - 3 + j;
         if (tt >= 0) {
             ld8(x + (b * T + tt) * (long)D + c, win[j]);
         } else if (cs) {
@@ -81,76 +90,86 @@ __device__ __forceinline__ void conv8(const DT *x, const DT *cs, const float *w,
             for (int e = 0; e < 8; ++e) win[j][e] = 0.f;
         }
     }
+    const int tend = min(t0 + PR_TT, T);   // the same for every lane of a head
+#pragma unroll 4
+    for (int t = t0; t < tend; ++t) {
+        ld8(x + (b * T + t) * (long)D + c, win[3]);
+        float o[8];
+        float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const f32x4 wt = *reinterpret_cast<const f32x4 *>(w + (long)(c + e) * 4);
-        float s = wt[0] * win[0][e];
-        s = fmaf(wt[1], win[1][e], s);
-        s = fmaf(wt[2], win[2][e], s);
-        s = fmaf(wt[3], win[3][e], s);
-        y[e] = SILU ? pr_silu(s) : s;
+        for (int e = 0; e < 8; ++e) {
+            float v = wt[e][0] * win[0][e];
+            v = fmaf(wt[e][1], win[1][e], v);
+            v = fmaf(wt[e][2], win[2][e], v);
+            v = fmaf(wt[e][3], win[3][e], v);
+            o[e] = SILU ? pr_silu(v) : v;
+            ss = fmaf(o[e], o[e], ss);
+        }
+        if (NORM) {
+#pragma unroll
+            for (int off = 1; off < W; off <<= 1) ss += __shfl_xor(ss, off, W);
+            const float rn = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= rn;
+        }
+        st8(y + (b * T + t) * (long)D + c, o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            win[0][e] = win[1][e];
+            win[1][e] = win[2][e];
+            win[2][e] = win[3][e];
+        }
     }
 }
 
-// Segments (blockIdx.y): 0 q, 1 k, 2 v, 3 gates.  One thread per token and 8
-// channels; the K/8 threads of one (token, head) are consecutive lanes, which
-// reduce the squared norm with shuffles.
 template <typename DT, int K, int V, bool CH, bool SILU>
 __global__ __launch_bounds__(PR_NTHR) void prologue_kernel(PrArgs a)
 {
     const long idx = (long)blockIdx.x * PR_NTHR + threadIdx.x;
     const int seg = blockIdx.y;
-    const long BT = (long)a.B * a.T, BTH = BT * a.H;
-    if (seg <= 1) {
-        constexpr int G = K / 8;                  // lanes per (token, head)
-        if (idx >= BTH * G) return;               // whole groups of G lanes
-        const long row = idx / G;                 // (b, t, h)
-        const int h = (int)(row % a.H);
-        const long bt = row / a.H;
-        const int t = (int)(bt % a.T);
-        const long b = bt / a.T;
-        const int D = a.H * K, c = h * K + (int)(idx % G) * 8;
-        const DT *x = (const DT *)(seg == 0 ? a.q_raw : a.k_raw);
-        const DT *cs = (const DT *)(seg == 0 ? a.cs_q : a.cs_k);
-        float y[8];
-        conv8<DT, SILU>(x, cs, seg == 0 ? a.w_q : a.w_k, b, t, a.T, D, c, y);
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
-#pragma unroll
-        for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off, G);
-        const float rn = 1.f / fmaxf(sqrtf(ss), 1e-12f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] *= rn;
-        st8((DT *)(seg == 0 ? a.q : a.k) + bt * D + c, y);
-    } else if (seg == 2) {
-        constexpr int G = V / 8;
-        if (idx >= BTH * G) return;
-        const long row = idx / G;
-        const int h = (int)(row % a.H);
-        const long bt = row / a.H;
-        const int t = (int)(bt % a.T);
-        const long b = bt / a.T;
-        const int D = a.H * V, c = h * V + (int)(idx % G) * 8;
-        float y[8];
-        conv8<DT, SILU>((const DT *)a.v_raw, (const DT *)a.cs_v, a.w_v, b, t, a.T, D, c, y);
-        st8((DT *)a.v + bt * D + c, y);
+    const int NTB = (a.T + PR_TT - 1) / PR_TT;
+    const long rows = (long)a.B * NTB * a.H;      // (b, token block, h)
+    if (seg <= 2) {
+        const int E = seg == 2 ? V : K, G = E / 8;   // lanes per (token block, head)
+        if (idx >= rows * G) return;                 // whole groups of G lanes
+        const long r = idx / G;
+        const int h = (int)(r % a.H);
+        const long btb = r / a.H;
+        const int tb = (int)(btb % NTB);
+        const long b = btb / NTB;
+        const int D = a.H * E, c = h * E + (int)(idx % G) * 8;
+        if (seg == 0)
+            conv_run<DT, K / 8, true, SILU>((const DT *)a.q_raw, (const DT *)a.cs_q, a.w_q,
+                                            (DT *)a.q, b, tb * PR_TT, a.T, D, c);
+        else if (seg == 1)
+            conv_run<DT, K / 8, true, SILU>((const DT *)a.k_raw, (const DT *)a.cs_k, a.w_k,
+                                            (DT *)a.k, b, tb * PR_TT, a.T, D, c);
+        else
+            conv_run<DT, V / 8, false, SILU>((const DT *)a.v_raw, (const DT *)a.cs_v, a.w_v,
+                                             (DT *)a.v, b, tb * PR_TT, a.T, D, c);
     } else {
-        if (CH) {
-            constexpr int G = K / 4;
-            if (idx >= BTH * G) return;
-            const long row = idx / G;
-            const int x0 = (int)(idx % G) * 4;
-            const f32x4 gr = *reinterpret_cast<const f32x4 *>(a.g_raw + row * K + x0);
-            f32x4 gv;
+        constexpr int G = CH ? K / 4 : 1;
+        if (idx >= rows * G) return;
+        const long r = idx / G;
+        const int h = (int)(r % a.H);
+        const long btb = r / a.H;
+        const int tb = (int)(btb % NTB);
+        const long b = btb / NTB;
+        const int x0 = (int)(idx % G) * 4;
+        const int t0 = tb * PR_TT, tend = min(t0 + PR_TT, a.T);
+        for (int t = t0; t < tend; ++t) {
+            const long row = (b * a.T + t) * a.H + h;
+            if (CH) {
+                const f32x4 gr = *reinterpret_cast<const f32x4 *>(a.g_raw + row * K + x0);
+                f32x4 gv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gv[e] = pr_gate(gr[e], a.cap);
-            *reinterpret_cast<f32x4 *>(a.g + row * K + x0) = gv;
-            if (x0 == 0) a.beta[row] = pr_sigmoid(a.b_raw[row]);
-        } else {
-            if (idx >= BTH) return;
-            a.g[idx] = pr_gate(a.g_raw[idx], a.cap);
-            a.beta[idx] = pr_sigmoid(a.b_raw[idx]);
+                for (int e = 0; e < 4; ++e) gv[e] = pr_gate(gr[e], a.cap);
+                *reinterpret_cast<f32x4 *>(a.g + row * K + x0) = gv;
+                if (x0 == 0) a.beta[row] = pr_sigmoid(a.b_raw[row]);
+            } else {
+                a.g[row] = pr_gate(a.g_raw[row], a.cap);
+                a.beta[row] = pr_sigmoid(a.b_raw[row]);
+            }
         }
     }
 }
@@ -197,11 +216,11 @@ __global__ __launch_bounds__(PR_NTHR) void prologue_state_kernel(PrArgs a)
 template <typename DT, int K, int V, bool CH, bool SILU>
 static hipError_t launch_prologue(const PrArgs &a, hipStream_t st)
 {
-    const long bth = (long)a.B * a.T * a.H;
-    long nthr = bth * (K / 8);
-    nthr = nthr > bth * (V / 8) ? nthr : bth * (V / 8);
-    nthr = nthr > bth * (CH ? K / 4 : 1) ? nthr : bth * (CH ? K / 4 : 1);
-    if (bth > 0)
+    const long rows = (long)a.B * ((a.T + PR_TT - 1) / PR_TT) * a.H;
+    long nthr = rows * (K / 8);
+    nthr = nthr > rows * (V / 8) ? nthr : rows * (V / 8);
+    nthr = nthr > rows * (CH ? K / 4 : 1) ? nthr : rows * (CH ? K / 4 : 1);
+    if (rows > 0)
         hipLaunchKernelGGL((prologue_kernel<DT, K, V, CH, SILU>),
                            dim3((unsigned)((nthr + PR_NTHR - 1) / PR_NTHR), 4), dim3(PR_NTHR), 0, st, a);
     if (a.cs_q_out || a.cs_k_out || a.cs_v_out) {
