@@ -330,9 +330,20 @@ __device__ __forceinline__ void store_state_block(float *dst, const float *St, i
 
 // One workgroup per (slice, block of 16 value columns), chunks in order; wave
 // w owns rows 16 w .. 16 w + 15 of the C x 16 products and K/4 rows of the
-// state block, which stays in its accumulators.  Each A fragment is refilled
-// for the next chunk right after its last use, so those loads run under the
-// rest of the chunk; the barriers in the loop wait for LDS traffic only.
+// state block, which stays in its accumulators.  The A fragments of a chunk
+// sit in one of two register sets: all of the next chunk's loads go into the
+// other set right after this chunk's operands are in LDS, a whole chunk of
+// work before they are used (the loop is unrolled by two so that the sets keep
+// fixed registers).  The barriers in the loop wait for LDS traffic only.
+template <typename DT, int K, int C, int KT, int VB> struct StSet {
+    f32x4 kp[K / 16];        // Kp row 16 w + r
+    f32x4 t[C / 16];         // T row 16 w + r
+    f32x4 km[KT][C / 16];    // Km^T rows 16 (KT w + h) + r
+    f32x4 g[KT];             // e^{gn} of this lane's accumulator rows
+    TileRegs<DT, C, VB> v;   // v tile
+    float b;                 // beta of token tid
+};
+
 template <typename DT, int K, int V>
 __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
 {
@@ -348,27 +359,22 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
     sweep_block(a.NS, NVB, sl, vb);
     const int v0 = vb * VB;
     const long H = a.H;
+    using Set = StSet<DT, K, C, KT, VB>;
 
-    f32x4 fKp[K / 16];       // Kp row 16 w + r
-    f32x4 fT[C / 16];        // T row 16 w + r
-    f32x4 fKm[KT][C / 16];   // Km^T rows 16 (KT w + h) + r
-    f32x4 fg[KT];            // e^{gn} of this lane's accumulator rows
-    TileRegs<DT, C, VB> pV;
-    float pb = 0.f;
-    auto fetch_kp = [&](long ci) { ld_afrag<K / 16>(fKp, a.ws.Kp + ci * (C * K) + (16 * w + r) * K); };
-    auto fetch_t = [&](long ci) { ld_afrag<C / 16>(fT, a.ws.Tm + ci * (C * C) + (16 * w + r) * C); };
-    auto fetch_km = [&](long ci) {
+    // The loads are issued in the order of first use, so that each wait covers
+    // only what it needs (the memory counter retires loads in order).
+    auto fetch = [&](Set &f, int c) {
+        const long ci = (long)sl * a.NC + c, r0 = tok_row(a, sl, c * C);
+        const int n = min(C, a.T - c * C);
+        f.v.load((const DT *)a.v + r0 * V + v0, H * V, n);
+        f.b = tid < n ? a.beta[r0 + tid * H] : 0.f;
+        ld_afrag<K / 16>(f.kp, a.ws.Kp + ci * (C * K) + (16 * w + r) * K);
+        ld_afrag<C / 16>(f.t, a.ws.Tm + ci * (C * C) + (16 * w + r) * C);
 #pragma unroll
         for (int h = 0; h < KT; ++h) {
-            ld_afrag<C / 16>(fKm[h], a.ws.KmT + ci * (K * C) + (16 * (KT * w + h) + r) * C);
-            fg[h] = *reinterpret_cast<const f32x4 *>(a.ws.egn + ci * K + 16 * (KT * w + h) + 4 * gq);
+            ld_afrag<C / 16>(f.km[h], a.ws.KmT + ci * (K * C) + (16 * (KT * w + h) + r) * C);
+            f.g[h] = *reinterpret_cast<const f32x4 *>(a.ws.egn + ci * K + 16 * (KT * w + h) + 4 * gq);
         }
-    };
-    auto fetch_v = [&](int c) {
-        const long r0 = tok_row(a, sl, c * C);
-        const int n = min(C, a.T - c * C);
-        pV.load((const DT *)a.v + r0 * V + v0, H * V, n);
-        pb = tid < n ? a.beta[r0 + tid * H] : 0.f;
     };
 
     f32x4 S[KT];
@@ -380,25 +386,19 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
             S[h][e] = a.S0 ? a.S0[((long)sl * K + x0 + e) * V + v0 + r] : 0.f;
         *reinterpret_cast<f32x4 *>(sSt + r * LK + x0) = S[h];
     }
-    if (a.NC > 0) {
-        const long ci0 = (long)sl * a.NC;
-        fetch_kp(ci0);
-        fetch_t(ci0);
-        fetch_km(ci0);
-        fetch_v(0);
-    }
-    for (int c = 0; c < a.NC; ++c) {
+
+    auto chunk = [&](Set &f, Set &nf, int c) {
         const long ci = (long)sl * a.NC + c;
-        const bool more = c + 1 < a.NC;
         lds_barrier();   // S^T complete; the previous chunk's readers are done
-        pV.store(sV, VP);
-        if (tid < C) sb[tid] = pb;
+        f.v.store(sV, VP);
+        if (tid < C) sb[tid] = f.b;
         store_state_block<K, V>(a.ws.hS + ci * (K * V) + v0, sSt, LK);   // state entering c
         lds_barrier();
-        if (more) fetch_v(c + 1);
+        // unconditional (the last chunk fetches itself again), so that the
+        // compiler's waits see one straight path
+        fetch(nf, min(c + 1, a.NC - 1));
         {   // R = beta (V - Kp S)
-            const f32x4 X = mma_rows<K / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, fKp, sSt, LK);
-            if (more) fetch_kp(ci + 1);
+            const f32x4 X = mma_rows<K / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.kp, sSt, LK);
             f32x4 R;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -409,8 +409,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
         }
         lds_barrier();
         {   // Delta = T R
-            const f32x4 D = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, fT, sRt, LC);
-            if (more) fetch_t(ci + 1);
+            const f32x4 D = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.t, sRt, LC);
             *reinterpret_cast<f32x4 *>(sDt + r * LC + 16 * w + 4 * gq) = D;
             float *Dl = a.ws.Dl + ci * (C * V) + v0 + r;
 #pragma unroll
@@ -420,18 +419,36 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
         // S = Diag(e^{gn}) S + Km^T Delta
 #pragma unroll
         for (int h = 0; h < KT; ++h) {
-            S[h] *= fg[h];
-            S[h] = mma_rows<C / 16>(S[h], fKm[h], sDt, LC);
-        }
-        if (more) fetch_km(ci + 1);
-#pragma unroll
-        for (int h = 0; h < KT; ++h)
+            S[h] *= f.g[h];
+            S[h] = mma_rows<C / 16>(S[h], f.km[h], sDt, LC);
             *reinterpret_cast<f32x4 *>(sSt + r * LK + 16 * (KT * w + h) + 4 * gq) = S[h];
+        }
+    };
+
+    Set A, B;
+    if (a.NC == 0) return;
+    fetch(A, 0);
+    int c = 0;
+    for (; c + 1 < a.NC; c += 2) {
+        chunk(A, B, c);
+        chunk(B, A, c + 1);
     }
+    if (c < a.NC) chunk(A, B, c);
 }
 
 // ---------------------------------------------------------------- 3 dstates
-// Same layout as the forward sweep, chunks in reverse order.
+// Same layout as the forward sweep, chunks in reverse order, with the same two
+// register sets of A fragments.
+template <typename DT, int K, int C, int KT, int VB> struct DsSet {
+    TileRegs<DT, C, VB> o;       // dO tile
+    float b;                     // beta of token tid
+    f32x4 km[K / 16];            // Km row 16 w + r
+    f32x4 pt[C / 16];            // P^T row 16 w + r
+    f32x4 tt[C / 16];            // T^T row 16 w + r
+    f32x4 qk[KT][2 * C / 16];    // [Qp^T | Kp^T] rows 16 (KT w + h) + r
+    f32x4 g[KT];
+};
+
 template <typename DT, int K, int V>
 __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
 {
@@ -447,33 +464,24 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
     sweep_block(a.NS, NVB, sl, vb);
     const int v0 = vb * VB;
     const long H = a.H;
+    using Set = DsSet<DT, K, C, KT, VB>;
 
-    f32x4 fKm[K / 16];             // Km row 16 w + r
-    f32x4 fPT[C / 16];             // P^T row 16 w + r
-    f32x4 fTT[C / 16];             // T^T row 16 w + r
-    f32x4 fQK[KT][2 * C / 16];     // [Qp^T | Kp^T] rows 16 (KT w + h) + r
-    f32x4 fg[KT];
-    TileRegs<DT, C, VB> pO;
-    float pb = 0.f;
-    auto fetch_kp = [&](long ci) {
-        ld_afrag<K / 16>(fKm, a.ws.Km + ci * (C * K) + (16 * w + r) * K);
-        ld_afrag<C / 16>(fPT, a.ws.PT + ci * (C * C) + (16 * w + r) * C);
-    };
-    auto fetch_t = [&](long ci) { ld_afrag<C / 16>(fTT, a.ws.TT + ci * (C * C) + (16 * w + r) * C); };
-    auto fetch_qk = [&](long ci) {
+    // in the order of first use
+    auto fetch = [&](Set &f, int c) {
+        const long ci = (long)sl * a.NC + c, r0 = tok_row(a, sl, c * C);
+        const int n = min(C, a.T - c * C);
+        f.o.load((const DT *)a.d_o + r0 * V + v0, H * V, n);
+        f.b = tid < n ? a.beta[r0 + tid * H] : 0.f;
+        ld_afrag<K / 16>(f.km, a.ws.Km + ci * (C * K) + (16 * w + r) * K);
+        ld_afrag<C / 16>(f.pt, a.ws.PT + ci * (C * C) + (16 * w + r) * C);
+        ld_afrag<C / 16>(f.tt, a.ws.TT + ci * (C * C) + (16 * w + r) * C);
 #pragma unroll
         for (int h = 0; h < KT; ++h) {
             const int x = 16 * (KT * w + h) + r;
-            ld_afrag<C / 16>(&fQK[h][0], a.ws.QpT + ci * (K * C) + x * C);
-            ld_afrag<C / 16>(&fQK[h][C / 16], a.ws.KpT + ci * (K * C) + x * C);
-            fg[h] = *reinterpret_cast<const f32x4 *>(a.ws.egn + ci * K + 16 * (KT * w + h) + 4 * gq);
+            ld_afrag<C / 16>(&f.qk[h][0], a.ws.QpT + ci * (K * C) + x * C);
+            ld_afrag<C / 16>(&f.qk[h][C / 16], a.ws.KpT + ci * (K * C) + x * C);
+            f.g[h] = *reinterpret_cast<const f32x4 *>(a.ws.egn + ci * K + 16 * (KT * w + h) + 4 * gq);
         }
-    };
-    auto fetch_o = [&](int c) {
-        const long r0 = tok_row(a, sl, c * C);
-        const int n = min(C, a.T - c * C);
-        pO.load((const DT *)a.d_o + r0 * V + v0, H * V, n);
-        pb = tid < n ? a.beta[r0 + tid * H] : 0.f;
     };
 
     f32x4 dS[KT];
@@ -485,16 +493,9 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
             dS[h][e] = a.dS_T ? a.dS_T[((long)sl * K + x0 + e) * V + v0 + r] : 0.f;
         *reinterpret_cast<f32x4 *>(sdSt + r * LK + x0) = dS[h];
     }
-    if (a.NC > 0) {
-        const long cl = (long)sl * a.NC + a.NC - 1;
-        fetch_kp(cl);
-        fetch_t(cl);
-        fetch_qk(cl);
-        fetch_o(a.NC - 1);
-    }
-    for (int c = a.NC - 1; c >= 0; --c) {
+
+    auto chunk = [&](Set &f, Set &nf, int c) {
         const long ci = (long)sl * a.NC + c;
-        const bool more = c > 0;
         lds_barrier();
         {   // dO tile, transposed
             constexpr int VE = TileRegs<DT, C, VB>::VE, VPR = VB / VE, NV = C * VPR;
@@ -504,18 +505,17 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
                 if (NV % BW_NTHR == 0 || v < NV) {
                     const int t = v / VPR, y = (v % VPR) * VE;
 #pragma unroll
-                    for (int e = 0; e < VE; ++e) sOYt[(y + e) * L2 + t] = to_f32(pO.r[i][e]);
+                    for (int e = 0; e < VE; ++e) sOYt[(y + e) * L2 + t] = to_f32(f.o.r[i][e]);
                 }
             }
         }
-        if (tid < C) sb[tid] = pb;
+        if (tid < C) sb[tid] = f.b;
         store_state_block<K, V>(a.ws.dhS + ci * (K * V) + v0, sdSt, LK);   // dL/d(state leaving c)
         lds_barrier();
-        if (more) fetch_o(c - 1);
+        fetch(nf, max(c - 1, 0));   // unconditional: one straight path for the compiler's waits
         {   // dDelta = Km dS' + P^T dO
-            f32x4 dD = mma_rows<K / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, fKm, sdSt, LK);
-            dD = mma_rows<C / 16>(dD, fPT, sOYt, L2);
-            if (more) fetch_kp(ci - 1);
+            f32x4 dD = mma_rows<K / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.km, sdSt, LK);
+            dD = mma_rows<C / 16>(dD, f.pt, sOYt, L2);
             *reinterpret_cast<f32x4 *>(sdDt + r * LC + 16 * w + 4 * gq) = dD;
             float *dDl = a.ws.dDl + ci * (C * V) + v0 + r;
 #pragma unroll
@@ -523,8 +523,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
         }
         lds_barrier();
         {   // Y = T^T dDelta, kept as -beta Y
-            f32x4 Y = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, fTT, sdDt, LC);
-            if (more) fetch_t(ci - 1);
+            f32x4 Y = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.tt, sdDt, LC);
 #pragma unroll
             for (int e = 0; e < 4; ++e) Y[e] *= -sb[16 * w + 4 * gq + e];
             *reinterpret_cast<f32x4 *>(sOYt + r * L2 + C + 16 * w + 4 * gq) = Y;
@@ -533,13 +532,21 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
         // dS = Diag(e^{gn}) dS' + [Qp^T | Kp^T] [dO; -beta Y]
 #pragma unroll
         for (int h = 0; h < KT; ++h) {
-            dS[h] *= fg[h];
-            dS[h] = mma_rows<2 * C / 16>(dS[h], fQK[h], sOYt, L2);
-        }
-        if (more) fetch_qk(ci - 1);
-#pragma unroll
-        for (int h = 0; h < KT; ++h)
+            dS[h] *= f.g[h];
+            dS[h] = mma_rows<2 * C / 16>(dS[h], f.qk[h], sOYt, L2);
             *reinterpret_cast<f32x4 *>(sdSt + r * LK + 16 * (KT * w + h) + 4 * gq) = dS[h];
+        }
+    };
+
+    if (a.NC > 0) {
+        Set A, B;
+        fetch(A, a.NC - 1);
+        int c = a.NC - 1;
+        for (; c >= 1; c -= 2) {
+            chunk(A, B, c);
+            chunk(B, A, c - 1);
+        }
+        if (c == 0) chunk(A, B, 0);
     }
     if (a.dS0) {
 #pragma unroll
