@@ -37,22 +37,27 @@ CSRC = os.path.join(ROOT, "gated_deltanet_layer_amd", "csrc")
 MEASURED_TRAFFIC = {
     "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
                                   "mfma_frag.h"),
-                                 "4bfeabc03baca055", 862346361),
+                                 "4bfeabc03baca055", 862345934),
     # the B=16 H=8 T=2048 channel-gate case (o and S_T written)
     "chunk_fwd_wsc_kernel<128>": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                    "mfma_frag.h"),
-                                  "aea3bbff97305fd5", 420122323),
+                                  "aea3bbff97305fd5", 420119881),
     # the B=1 H=48 T=262144 channel-gate case (S_T only, from a random S0)
     "chunk_fwd_wsc_kernel<128>/long": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                         "mfma_frag.h"),
-                                       "aea3bbff97305fd5", 16671410339),
+                                       "aea3bbff97305fd5", 16641126925),
     "recurrent_step_kernel<bf16,128,128,channel>": (("recurrent_step.hip", "gdn_common.h"),
-                                                    "1864f0aa1a777d85", 1642881106),
+                                                    "1864f0aa1a777d85", 1642880935),
     # M = 4 draft tokens on the decode shape: final state only / every token's state
     "recurrent_multi_kernel<bf16,128,128,channel>/final": (("recurrent_multi.hip", "gdn_common.h"),
-                                                           "e96c18f898c72e85", 1739636872),
+                                                           "e96c18f898c72e85", 1739629851),
     "recurrent_multi_kernel<bf16,128,128,channel>/hist": (("recurrent_multi.hip", "gdn_common.h"),
-                                                          "e96c18f898c72e85", 4158922376),
+                                                          "e96c18f898c72e85", 4159188123),
+    # the chunk-mode prologue at B8 H12 T8192 (scalar gate) and the fused decode token
+    "prologue_kernel<bf16,128,128,scalar,silu>": (("prologue.hip", "prologue.h", "gdn_common.h"),
+                                                  "0ed5faf9f34cfc2f", 1335877252),
+    "recurrent_step_prologue_kernel<bf16,128,128,channel,silu>": (("prologue.hip", "prologue.h",
+                                                                  "gdn_common.h"), "0ed5faf9f34cfc2f", 1719380966),
 }
 
 
@@ -321,6 +326,7 @@ def bench_prologue(torch, gdn, steps, warmup):
                                 f"SiLU, carried states in and out",
                     "ms": ms, "gbs": nbytes / (ms / 1e3) / 1e9,
                     "frac_hbm": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_call": nbytes,
+                    "traffic": measured_traffic("prologue_kernel<bf16,128,128,scalar,silu>"),
                     "kernel": "prologue_kernel<bf16,128,128,scalar,silu>"}
     del d, r, cso
     # the decode token: fused against two launches
@@ -371,6 +377,7 @@ def bench_prologue(torch, gdn, steps, warmup):
                      "gbs_fused": nb / (res["fused"] / 1e3) / 1e9,
                      "frac_hbm_fused": nb / (res["fused"] / 1e3) / 1e9 / HBM_PEAK_GBS,
                      "bytes_per_step": nb,
+                     "traffic": measured_traffic("recurrent_step_prologue_kernel<bf16,128,128,channel,silu>"),
                      "kernel": "recurrent_step_prologue_kernel<bf16,128,128,channel,silu>"}
     return out
 
