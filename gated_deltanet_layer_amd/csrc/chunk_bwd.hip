@@ -25,7 +25,7 @@
 // its last row); a scalar gate sums dg over the key channels.
 //
 // Kernels, in stream order (each launch covers every slice):
-//   1 prep     one workgroup per chunk:   gamma, G, P, T
+//   1 prep     one workgroup per chunk:   gamma, G, P (matrix cores), T
 //   2 states   one per value block:       walks the chunks forward; the state
 //                                         entering each chunk and Delta
 //   3 dstates  one per value block:       walks them backward; dL/dS' of each
@@ -162,7 +162,7 @@ __device__ __forceinline__ void store_tile(float *dst, long gs, const float *src
 template <typename DT, int K, bool CH>
 __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
 {
-    constexpr int C = BW_C, KP = K + 1, CP = C + 1;
+    constexpr int C = BW_C, KP = K + 4, CP = C + 1;   // rows of k, q, gamma 16-byte aligned
     extern __shared__ __attribute__((aligned(256))) float sm[];
     float *sk = sm, *sq = sk + C * KP, *sg = sq + C * KP, *sA = sg + C * KP, *sT = sA + C * CP;
     float *sb = sT + C * CP, *sgs = sb + C;
@@ -233,29 +233,67 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
         if (tid < K) a.ws.egn[ci * K + tid] = __expf(sg[(C - 1) * KP + tid]);
     }
 
-    // G and P over the pairs s <= t (2080 of them), one pair per thread at a time;
-    // P is stored transposed
+    // G and P (P stored transposed) by 16 x 16 blocks I >= J on the matrix
+    // cores, one block pair per wave at a time.  Per-channel gate: e^{gamma_t -
+    // gamma_s} is split through the reference row rho in the middle of the block
+    // of t: A rows k_t e^{gamma_t - gamma_rho} (q_t for P), B rows
+    // k_s e^{gamma_rho - gamma_s}.  With g >= -5 per token no factor exceeds
+    // e^{8 * 5}; for s in an earlier block the B factor is at most 1.  Scalar
+    // gate: the plain products, scaled by e^{gamma_t - gamma_s} afterwards.
     float *Gm = a.ws.Gm + ci * (C * C), *PT = a.ws.PT + ci * (C * C);
-    for (int p = tid; p < C * (C + 1) / 2; p += BW_NTHR) {
-        int t = (int)((sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
-        while (t * (t + 1) / 2 > p) --t;
-        while ((t + 1) * (t + 2) / 2 <= p) ++t;
-        const int s = p - t * (t + 1) / 2;
-        float gk = 0.f, pq = 0.f;
-#pragma unroll 8
-        for (int x = 0; x < K; ++x) {
-            const float ks = sk[s * KP + x] * __expf(sg[t * KP + x] - sg[s * KP + x]);
-            gk = fmaf(sk[t * KP + x], ks, gk);
-            pq = fmaf(sq[t * KP + x], ks, pq);
+    {
+        const int lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
+        for (int p = w; p < 10; p += 4) {
+            const int I = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0, J = p - I * (I + 1) / 2;
+            const float *ka = sk + (16 * I + r16) * KP, *qa = sq + (16 * I + r16) * KP;
+            const float *ga = sg + (16 * I + r16) * KP, *gr = sg + (16 * I + 8) * KP;
+            const float *kb = sk + (16 * J + r16) * KP, *gb = sg + (16 * J + r16) * KP;
+            f32x4 gacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+            for (int a0 = 0; a0 < K; a0 += 16) {
+                const int c = a0 + 4 * gq;
+                f32x4 kA = *reinterpret_cast<const f32x4 *>(ka + c);
+                f32x4 qA = *reinterpret_cast<const f32x4 *>(qa + c);
+                f32x4 kB = *reinterpret_cast<const f32x4 *>(kb + c);
+                if (CH) {
+                    const f32x4 gA = *reinterpret_cast<const f32x4 *>(ga + c);
+                    const f32x4 gR = *reinterpret_cast<const f32x4 *>(gr + c);
+                    const f32x4 gB = *reinterpret_cast<const f32x4 *>(gb + c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float fa = __expf(gA[e] - gR[e]);
+                        kA[e] *= fa;
+                        qA[e] *= fa;
+                        kB[e] *= __expf(gR[e] - gB[e]);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    gacc = mfma_f32(kA[e], kB[e], gacc);
+                    pacc = mfma_f32(qA[e], kB[e], pacc);
+                }
+            }
+            // this lane holds rows t = 16 I + 4 gq + e of column s = 16 J + r16
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * I + 4 * gq + e, s = 16 * J + r16;
+                float gv = gacc[e], pv = pacc[e];
+                if (!CH) {
+                    const float f = s <= t ? __expf(sg[t * KP] - sg[s * KP]) : 0.f;
+                    gv *= f;
+                    pv *= f;
+                }
+                gv = s < t ? gv : 0.f;
+                pv = s <= t ? pv : 0.f;
+                Gm[t * C + s] = gv;
+                PT[s * C + t] = pv;
+                sA[t * CP + s] = sb[t] * gv;
+            }
         }
-        const float gts = s < t ? gk : 0.f;
-        Gm[t * C + s] = gts;
-        PT[s * C + t] = pq;
-        sA[t * CP + s] = sb[t] * gts;
     }
-    for (int idx = tid; idx < C * C; idx += BW_NTHR) {
+    for (int idx = tid; idx < C * C; idx += BW_NTHR) {   // the blocks above the diagonal
         const int t = idx / C, s = idx % C;
-        if (s > t) {
+        if (s / 16 > t / 16) {
             Gm[idx] = 0.f;
             PT[s * C + t] = 0.f;
             sA[t * CP + s] = 0.f;
@@ -996,7 +1034,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
 template <int K, int V> struct BwLds {
     static constexpr int C = BW_C, KP = K + 1, CP = C + 1, VB = BW_VB, VP = VB + 1;
     static constexpr int LK = K + 4, LC = C + 4, L2 = 2 * C + 4;
-    static constexpr int prep = 4 * (3 * C * KP + 2 * C * CP + 2 * C);
+    static constexpr int prep = 4 * (3 * C * (K + 4) + 2 * C * CP + 2 * C);
     static constexpr int states = 4 * (VB * LK + 2 * VB * LC + C * VP + C);
     static constexpr int dstates = 4 * (VB * LK + VB * L2 + VB * LC + C);
     static constexpr int vgrad = 4 * (2 * K * 17 + 4 * C * 17 + C * CP + C);
