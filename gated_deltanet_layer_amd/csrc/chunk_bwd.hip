@@ -790,8 +790,14 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
         using TL = Tile<C, C, 4, 4>;
         const TL tl;
         float acc[4][4] = {};
-        mm_acc<C, C, 4, 4, C, CP, 1, 1, CP>(acc, sM, sT, tl.mt, tl.nt);
+        // G is read before dG is stored (as far as the compiler knows they may alias)
         const float *Gm = a.ws.Gm + ci * (C * C);
+        float gv[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) gv[i][j] = Gm[tl.row(i) * C + tl.col(j)];
+        mm_acc<C, C, 4, 4, C, CP, 1, 1, CP>(acc, sM, sT, tl.mt, tl.nt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = tl.row(i);
@@ -800,7 +806,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
             for (int j = 0; j < 4; ++j) {
                 const int s = tl.col(j);
                 const float da = s < t ? -acc[i][j] : 0.f;
-                part = fmaf(da, Gm[t * C + s], part);
+                part = fmaf(da, gv[i][j], part);
                 dGg[t * C + s] = sb[t] * da;
             }
             part += __shfl_xor(part, 1, 16);
@@ -966,27 +972,44 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
                 }
             }
         }
-        // per element: dq, dk, d gamma; the gn terms summed over this channel
+        // per element: dq, dk, d gamma; the gn terms summed over this channel.
+        // Two row blocks at a time, every load issued before any store (the
+        // stores may alias the loads as far as the compiler knows, which would
+        // otherwise serialise them element by element).
         const float gn = gam[(C - 1) * K + x];
         float dgn = 0.f;
 #pragma unroll
-        for (int R = 0; R < 4; ++R)
+        for (int R0 = 0; R0 < 4; R0 += 2) {
+            float lg[2][4], lk[2][4], lq[2][4], lqp[2][4], lkm[2][4], lz[2][4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * R + 4 * gq + e;
-                const float gr = gam[rr * K + x];
-                const float kr = rr < n ? to_f32(k[rr * H * K + x]) : 0.f;
-                const float qr = rr < n ? to_f32(q[rr * H * K + x]) : 0.f;
-                const float eg = __expf(gr), em = __expf(gn - gr);
-                const float dqp = dQp[rr * K + x], dkm = dKm[rr * K + x], z = Zg[rr * K + x] * sb[rr];
-                const float aq = accq[R][e], ak = acck[R][e], as = accs[R][e];
-                dQp[rr * K + x] = qr * aq + kr * (ak - as) + (dqp * qr + z * kr) * eg - dkm * kr * em;
-                dgn = fmaf(dkm * kr, em, dgn);
-                if (rr < n) {
-                    dq[rr * H * K + x] = from_f32<DT>(fmaf(dqp, eg, aq));
-                    dk[rr * H * K + x] = from_f32<DT>(ak + as + z * eg + dkm * em);
+            for (int R = 0; R < 2; ++R)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = 16 * (R0 + R) + 4 * gq + e;
+                    lg[R][e] = gam[rr * K + x];
+                    lk[R][e] = rr < n ? to_f32(k[rr * H * K + x]) : 0.f;
+                    lq[R][e] = rr < n ? to_f32(q[rr * H * K + x]) : 0.f;
+                    lqp[R][e] = dQp[rr * K + x];
+                    lkm[R][e] = dKm[rr * K + x];
+                    lz[R][e] = Zg[rr * K + x];
                 }
-            }
+#pragma unroll
+            for (int R = 0; R < 2; ++R)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = 16 * (R0 + R) + 4 * gq + e;
+                    const float kr = lk[R][e], qr = lq[R][e];
+                    const float eg = __expf(lg[R][e]), em = __expf(gn - lg[R][e]);
+                    const float dqp = lqp[R][e], dkm = lkm[R][e], z = lz[R][e] * sb[rr];
+                    const float aq = accq[R0 + R][e], ak = acck[R0 + R][e], as = accs[R0 + R][e];
+                    dQp[rr * K + x] = qr * aq + kr * (ak - as) + (dqp * qr + z * kr) * eg - dkm * kr * em;
+                    dgn = fmaf(dkm * kr, em, dgn);
+                    if (rr < n) {
+                        dq[rr * H * K + x] = from_f32<DT>(fmaf(dqp, eg, aq));
+                        dk[rr * H * K + x] = from_f32<DT>(ak + as + z * eg + dkm * em);
+                    }
+                }
+        }
         dgn += __shfl_xor(dgn, 16);
         dgn += __shfl_xor(dgn, 32);
         if (gq == 0) sdgn[x] = dgn;
