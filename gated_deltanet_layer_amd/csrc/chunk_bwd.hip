@@ -597,14 +597,25 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
 }
 
 // ---------------------------------------------------------------- 4 vgrad
+// Every product that sums over the value dimension, on the fp32 matrix cores,
+// 16 value columns at a time: dQp += dO S^T, dKm += Delta dS'^T, dWn += dDelta
+// S^T (C x K), dP += dO Delta^T, dT += dDelta V^T (C x C), and Y = T^T dDelta
+// for dv = beta Y and dbeta += rowsum(V * Y).  Each wave owns fixed output
+// tiles (16 x 16) whose accumulators persist across the value blocks; both
+// operands of every step are float4 LDS reads along the 16 value columns.
+// Held to two waves per SIMD so that one group's loads overlap the other's
+// products (the K = 128 accumulators alone take 128 registers).
 template <typename DT, int K, int V>
-__global__ __launch_bounds__(BW_NTHR) void bwd_vgrad_kernel(BwArgs a)
+__global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) void bwd_vgrad_kernel(BwArgs a)
 {
-    constexpr int C = BW_C, VB = 16, CP = C + 1, VP = VB + 1;
+    constexpr int C = BW_C, VB = 16, LV = VB + 4, LC = C + 4, XB = K / 64;
     extern __shared__ __attribute__((aligned(256))) float sm[];
-    float *sS = sm, *sdS = sS + K * VP, *sdO = sdS + K * VP, *sDl = sdO + C * VP;
-    float *sdD = sDl + C * VP, *sV = sdD + C * VP, *sT = sV + C * VP, *sb = sT + C * CP;
-    const int tid = threadIdx.x;
+    float *sS = sm, *sdS = sS + K * LV;                   // [K][LV]
+    float *sdO = sdS + K * LV, *sDl = sdO + C * LV;       // [C][LV]
+    float *sdD = sDl + C * LV, *sV = sdD + C * LV;        // [C][LV]
+    float *sTT = sV + C * LV;                             // [C][LC]  T^T
+    float *sb = sTT + C * LC;                             // [C]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
     const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
     const int t0 = c * C, n = min(C, a.T - t0);
     const long ci = (long)sl * a.NC + c;
@@ -615,20 +626,19 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_vgrad_kernel(BwArgs a)
     const float *Dl = a.ws.Dl + ci * (C * V), *dDl = a.ws.dDl + ci * (C * V);
     {
         TileRegs<float, C, C> tT;
-        tT.load(a.ws.Tm + ci * (C * C), C, C);
-        tT.store(sT, CP);
+        tT.load(a.ws.TT + ci * (C * C), C, C);
+        tT.store(sTT, LC);
         if (tid < C) sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
     }
-
-    using TCK = Tile<C, K, 4, K / 16>;
-    using TCC = Tile<C, C, 4, 4>;
-    using TCV = Tile<C, VB, 4, 1>;
-    const TCK tk;
-    const TCC tc;
-    const TCV tv;
-    float aQ[4][K / 16] = {}, aKm[4][K / 16] = {}, aWn[4][K / 16] = {};
-    float aP[4][4] = {}, aT[4][4] = {};
-    float dbv[4] = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 aQ[XB][4], aKm[XB][4], aWn[XB][4], aP[4], aT[4];   // [x block][row block]
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+#pragma unroll
+        for (int xi = 0; xi < XB; ++xi) aQ[xi][R] = aKm[xi][R] = aWn[xi][R] = z4;
+        aP[R] = aT[R] = z4;
+    }
+    float dbv[4] = {0.f, 0.f, 0.f, 0.f};   // rows 16 w + 4 gq + e
     float dgn = 0.f;
 
     for (int v0 = 0; v0 < V; v0 += VB) {
@@ -643,63 +653,89 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_vgrad_kernel(BwArgs a)
             tvv.load(v + v0, H * V, n);
             tD.load(Dl + v0, V, C);
             tdD.load(dDl + v0, V, C);
-            ts.store(sS, VP);
-            tds.store(sdS, VP);
-            to.store(sdO, VP);
-            tvv.store(sV, VP);
-            tD.store(sDl, VP);
-            tdD.store(sdD, VP);
+            ts.store(sS, LV);
+            tds.store(sdS, LV);
+            to.store(sdO, LV);
+            tvv.store(sV, LV);
+            tD.store(sDl, LV);
+            tdD.store(sdD, LV);
         }
         lds_barrier();
-        // dQp += dO S^T, dKm += Delta dS'^T, dWn += dDelta S^T   (C x K, sum over the block)
-        mm_acc<C, K, 4, K / 16, VB, VP, 1, 1, VP>(aQ, sdO, sS, tk.mt, tk.nt);
-        mm_acc<C, K, 4, K / 16, VB, VP, 1, 1, VP>(aKm, sDl, sdS, tk.mt, tk.nt);
-        mm_acc<C, K, 4, K / 16, VB, VP, 1, 1, VP>(aWn, sdD, sS, tk.mt, tk.nt);
-        // dP += dO Delta^T, dT += dDelta V^T (beta applied at the end)
-        mm_acc<C, C, 4, 4, VB, VP, 1, 1, VP>(aP, sdO, sDl, tc.mt, tc.nt);
-        mm_acc<C, C, 4, 4, VB, VP, 1, 1, VP>(aT, sdD, sV, tc.mt, tc.nt);
-        {   // Y = T^T dDelta: dv = beta Y, dbeta += rowsum(V * Y)
-            float y[4][1] = {};
-            mm_acc<C, VB, 4, 1, C, 1, CP, VP, 1>(y, sT, sdD, tv.mt, tv.nt);
+        const int vo = 4 * gq;   // this lane's four value columns of the block
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = tv.row(i), yy = tv.col(0);
-                dbv[i] = fmaf(sV[t * VP + yy], y[i][0], dbv[i]);
-                if (t < n) dv[t * H * V + v0 + yy] = from_f32<DT>(sb[t] * y[i][0]);
+        for (int R = 0; R < 4; ++R) {
+            const int tr = 16 * R + r16;   // A row of this lane
+            const f32x4 fO = *reinterpret_cast<const f32x4 *>(sdO + tr * LV + vo);
+            const f32x4 fD = *reinterpret_cast<const f32x4 *>(sDl + tr * LV + vo);
+            const f32x4 fdD = *reinterpret_cast<const f32x4 *>(sdD + tr * LV + vo);
+#pragma unroll
+            for (int xi = 0; xi < XB; ++xi) {
+                const int xr = 16 * (XB * w + xi) + r16;   // B column (key channel)
+                const f32x4 bS = *reinterpret_cast<const f32x4 *>(sS + xr * LV + vo);
+                const f32x4 bdS = *reinterpret_cast<const f32x4 *>(sdS + xr * LV + vo);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    aQ[xi][R] = mfma_f32(fO[e], bS[e], aQ[xi][R]);
+                    aKm[xi][R] = mfma_f32(fD[e], bdS[e], aKm[xi][R]);
+                    aWn[xi][R] = mfma_f32(fdD[e], bS[e], aWn[xi][R]);
+                }
+            }
+            const int sr = 16 * w + r16;   // B column (token s) of this lane
+            const f32x4 bD = *reinterpret_cast<const f32x4 *>(sDl + sr * LV + vo);
+            const f32x4 bV = *reinterpret_cast<const f32x4 *>(sV + sr * LV + vo);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                aP[R] = mfma_f32(fO[e], bD[e], aP[R]);
+                aT[R] = mfma_f32(fdD[e], bV[e], aT[R]);
+            }
+        }
+        {   // Y = T^T dDelta for rows 16 w .., all 16 columns: dv and dbeta
+            f32x4 y = z4;
+#pragma unroll
+            for (int a0 = 0; a0 < C; a0 += 16) {
+                const f32x4 fT = *reinterpret_cast<const f32x4 *>(sTT + (16 * w + r16) * LC + a0 + 4 * gq);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y = mfma_f32(fT[e], sdD[(a0 + 4 * gq + e) * LV + r16], y);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * w + 4 * gq + e;
+                dbv[e] = fmaf(sV[t * LV + r16], y[e], dbv[e]);
+                if (t < n) dv[t * H * V + v0 + r16] = from_f32<DT>(sb[t] * y[e]);
             }
         }
         if (tid < K)
-            for (int y = 0; y < VB; ++y) dgn = fmaf(sS[tid * VP + y], sdS[tid * VP + y], dgn);
+            for (int yy = 0; yy < VB; ++yy) dgn = fmaf(sS[tid * LV + yy], sdS[tid * LV + yy], dgn);
     }
 
     float *dQp = a.ws.dQp + ci * (C * K), *dKm = a.ws.dKm + ci * (C * K), *dWn = a.ws.dWn + ci * (C * K);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < K / 16; ++j) {
-            const int t = tk.row(i), x = tk.col(j);
-            dQp[t * K + x] = aQ[i][j];
-            dKm[t * K + x] = aKm[i][j];
-            dWn[t * K + x] = aWn[i][j];
-        }
     float *dP = a.ws.dP + ci * (C * C), *dT = a.ws.dT + ci * (C * C);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int R = 0; R < 4; ++R)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = tc.row(i), s = tc.col(j);
-            dP[t * C + s] = aP[i][j];
-            dT[t * C + s] = aT[i][j] * sb[s];
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * R + 4 * gq + e;
+#pragma unroll
+            for (int xi = 0; xi < XB; ++xi) {
+                const int x = 16 * (XB * w + xi) + r16;
+                dQp[t * K + x] = aQ[xi][R][e];
+                dKm[t * K + x] = aKm[xi][R][e];
+                dWn[t * K + x] = aWn[xi][R][e];
+            }
+            const int s = 16 * w + r16;
+            dP[t * C + s] = aP[R][e];
+            dT[t * C + s] = aT[R][e] * sb[s];
         }
-    // rows tv.row(i) are shared by the 16 consecutive lanes with the same tv.mt
+    // rows 16 w + 4 gq + e: the 16 lanes with the same gq hold the 16 columns
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float s = dbv[i];
-        s += __shfl_xor(s, 1, 16);
-        s += __shfl_xor(s, 2, 16);
-        s += __shfl_xor(s, 4, 16);
-        s += __shfl_xor(s, 8, 16);
-        if (tv.nt == 0) a.ws.dbv[ci * C + tv.row(i)] = s;
+    for (int e = 0; e < 4; ++e) {
+        float sum = dbv[e];
+        sum += __shfl_xor(sum, 1, 16);
+        sum += __shfl_xor(sum, 2, 16);
+        sum += __shfl_xor(sum, 4, 16);
+        sum += __shfl_xor(sum, 8, 16);
+        if (r16 == 0) a.ws.dbv[ci * C + 16 * w + 4 * gq + e] = sum;
     }
     if (tid < K) a.ws.dgn[ci * K + tid] = a.ws.egn[ci * K + tid] * dgn;
 }
@@ -1060,7 +1096,7 @@ template <int K, int V> struct BwLds {
     static constexpr int prep = 4 * (3 * C * (K + 4) + 2 * C * CP + 2 * C);
     static constexpr int states = 4 * (VB * LK + 2 * VB * LC + C * VP + C);
     static constexpr int dstates = 4 * (VB * LK + VB * L2 + VB * LC + C);
-    static constexpr int vgrad = 4 * (2 * K * 17 + 4 * C * 17 + C * CP + C);
+    static constexpr int vgrad = 4 * (2 * K * 20 + 4 * C * 20 + C * LC + C);
     static constexpr int kgrad1 = 4 * (2 * C + 2 * C * KP + 3 * C * CP);
     static constexpr int kgrad2 = 4 * (3 * K * LC + 2 * C * LC + 2 * C + (BW_NTHR / K) * K + K);
     static_assert(prep <= 160 * 1024 && states <= 160 * 1024 && dstates <= 160 * 1024 &&
