@@ -146,6 +146,54 @@ template <typename T, int R, int W> struct TileRegs {
     }
 };
 
+// Fragment order of an R x L fp32 array (R and L multiples of 16): the layout
+// in which the matrix-core A operands are read.  1 KB segments, one per
+// (16-row block, 16-column block), row block major; lane 16 g + r of a segment
+// holds row r, columns 4 g .. 4 g + 3 of its block as one float4.  A wave's
+// load of one A fragment is then one contiguous 1 KB read (eight whole cache
+// lines) instead of 64 bytes from each of 16 rows.
+template <int L> __device__ __forceinline__ int frag_idx(int row, int col)
+{
+    return ((((row >> 4) * (L / 16) + (col >> 4)) * 64 + ((col & 15) >> 2) * 16 + (row & 15)) << 2) +
+           (col & 3);
+}
+
+// Registers holding an R x L array in fragment order, fetched with contiguous
+// 16-byte loads that are all issued before any is used, stored to LDS row-major
+// (row stride ls).
+template <int R, int L> struct FragRegs {
+    static constexpr int NV = R * L / 4, PER = NV / BW_NTHR;
+    static_assert(NV % BW_NTHR == 0, "fragment tile");
+    f32x4 r[PER];
+    __device__ __forceinline__ void load(const float *src) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            r[i] = *reinterpret_cast<const f32x4 *>(src + 4 * (threadIdx.x + i * BW_NTHR));
+    }
+    __device__ __forceinline__ void store(float *dst, int ls) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * BW_NTHR, seg = v >> 6, l = v & 63;
+            const int row = 16 * (seg / (L / 16)) + (l & 15), col = 16 * (seg % (L / 16)) + 4 * (l >> 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[row * ls + col + e] = r[i][e];
+        }
+    }
+};
+
+// Store an R x L fp32 LDS tile (row stride ls) in fragment order, one
+// contiguous 16-byte store per thread and step.
+template <int R, int L>
+__device__ __forceinline__ void store_frag(float *dst, const float *src, int ls)
+{
+    for (int v = threadIdx.x; v < R * L / 4; v += BW_NTHR) {
+        const int seg = v >> 6, l = v & 63;
+        const int row = 16 * (seg / (L / 16)) + (l & 15), col = 16 * (seg % (L / 16)) + 4 * (l >> 4);
+        const float *s = src + row * ls + col;
+        *reinterpret_cast<f32x4 *>(dst + 4 * v) = f32x4{s[0], s[1], s[2], s[3]};
+    }
+}
+
 // Store an R x W fp32 LDS tile (row stride ls) to global rows gs floats apart,
 // four columns per 16-byte store.
 template <int R, int W>
@@ -195,28 +243,34 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
         }
     }
     lds_barrier();
-    {   // gamma and the row-scaled operands, by rows (gamma, Kp, Km) and
-        // transposed (Kp^T, Km^T, Qp^T); e^{gn}
-        float *gam = a.ws.gam + ci * (C * K), *Kp = a.ws.Kp + ci * (C * K);
-        float *Km = a.ws.Km + ci * (C * K);
+    {   // gamma by rows; the row-scaled operands in fragment order, as rows
+        // (Kp, Km) and transposed (Kp^T, Km^T, Qp^T); e^{gn}
+        float *gam = a.ws.gam + ci * (C * K);
         for (int v = tid; v < C * K / 4; v += BW_NTHR) {
             const int t = v / (K / 4), x = (v % (K / 4)) * 4;
-            f32x4 g4, kp, km;
+            *reinterpret_cast<f32x4 *>(gam + t * K + x) = *reinterpret_cast<const f32x4 *>(sg + t * KP + x);
+        }
+        float *Kp = a.ws.Kp + ci * (C * K), *Km = a.ws.Km + ci * (C * K);
+        for (int v = tid; v < C * K / 4; v += BW_NTHR) {
+            const int seg = v >> 6, l = v & 63;
+            const int t = 16 * (seg / (K / 16)) + (l & 15), x = 16 * (seg % (K / 16)) + 4 * (l >> 4);
+            const f32x4 k4 = *reinterpret_cast<const f32x4 *>(sk + t * KP + x);
+            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sg + t * KP + x);
+            const f32x4 n4 = *reinterpret_cast<const f32x4 *>(sg + (C - 1) * KP + x);
+            f32x4 kp, km;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float gm = sg[t * KP + x + e], gn = sg[(C - 1) * KP + x + e];
-                g4[e] = gm;
-                kp[e] = sk[t * KP + x + e] * __expf(gm);
-                km[e] = sk[t * KP + x + e] * __expf(gn - gm);
+                kp[e] = k4[e] * __expf(g4[e]);
+                km[e] = k4[e] * __expf(n4[e] - g4[e]);
             }
-            *reinterpret_cast<f32x4 *>(gam + t * K + x) = g4;
-            *reinterpret_cast<f32x4 *>(Kp + t * K + x) = kp;
-            *reinterpret_cast<f32x4 *>(Km + t * K + x) = km;
+            *reinterpret_cast<f32x4 *>(Kp + 4 * v) = kp;
+            *reinterpret_cast<f32x4 *>(Km + 4 * v) = km;
         }
         float *KpT = a.ws.KpT + ci * (K * C), *KmT = a.ws.KmT + ci * (K * C);
         float *QpT = a.ws.QpT + ci * (K * C);
         for (int v = tid; v < C * K / 4; v += BW_NTHR) {
-            const int x = v / (C / 4), t = (v % (C / 4)) * 4;
+            const int seg = v >> 6, l = v & 63;
+            const int x = 16 * (seg / (C / 16)) + (l & 15), t = 16 * (seg % (C / 16)) + 4 * (l >> 4);
             const float gn = sg[(C - 1) * KP + x];
             f32x4 kp, km, qp;
 #pragma unroll
@@ -226,9 +280,9 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
                 qp[e] = sq[(t + e) * KP + x] * eg;
                 km[e] = sk[(t + e) * KP + x] * __expf(gn - gm);
             }
-            *reinterpret_cast<f32x4 *>(KpT + x * C + t) = kp;
-            *reinterpret_cast<f32x4 *>(KmT + x * C + t) = km;
-            *reinterpret_cast<f32x4 *>(QpT + x * C + t) = qp;
+            *reinterpret_cast<f32x4 *>(KpT + 4 * v) = kp;
+            *reinterpret_cast<f32x4 *>(KmT + 4 * v) = km;
+            *reinterpret_cast<f32x4 *>(QpT + 4 * v) = qp;
         }
         if (tid < K) a.ws.egn[ci * K + tid] = __expf(sg[(C - 1) * KP + tid]);
     }
@@ -273,7 +327,10 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
                     pacc = mfma_f32(qA[e], kB[e], pacc);
                 }
             }
-            // this lane holds rows t = 16 I + 4 gq + e of column s = 16 J + r16
+            // this lane holds rows t = 16 I + 4 gq + e of column s = 16 J + r16,
+            // which in P^T is row s, columns t: lane 16 gq + r16 of the
+            // fragment-order segment (J, I)
+            f32x4 p4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * I + 4 * gq + e, s = 16 * J + r16;
@@ -284,18 +341,18 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
                     pv *= f;
                 }
                 gv = s < t ? gv : 0.f;
-                pv = s <= t ? pv : 0.f;
+                p4[e] = s <= t ? pv : 0.f;
                 Gm[t * C + s] = gv;
-                PT[s * C + t] = pv;
                 sA[t * CP + s] = sb[t] * gv;
             }
+            *reinterpret_cast<f32x4 *>(PT + 4 * ((J * (C / 16) + I) * 64 + lane)) = p4;
         }
     }
     for (int idx = tid; idx < C * C; idx += BW_NTHR) {   // the blocks above the diagonal
         const int t = idx / C, s = idx % C;
         if (s / 16 > t / 16) {
             Gm[idx] = 0.f;
-            PT[s * C + t] = 0.f;
+            PT[frag_idx<C>(s, t)] = 0.f;
             sA[t * CP + s] = 0.f;
         }
     }
@@ -318,27 +375,28 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
         }
 #pragma unroll
         for (int i = 0; i < C; ++i) sT[i * CP + j] = col[i];
-        float *TT = a.ws.TT + ci * (C * C) + j * C;   // T^T row j = column j of T
+        float *TT = a.ws.TT + ci * (C * C);   // T^T row j = column j of T
 #pragma unroll
         for (int i = 0; i < C; i += 4)
-            *reinterpret_cast<f32x4 *>(TT + i) = f32x4{col[i], col[i + 1], col[i + 2], col[i + 3]};
+            *reinterpret_cast<f32x4 *>(TT + frag_idx<C>(j, i)) = f32x4{col[i], col[i + 1], col[i + 2], col[i + 3]};
     }
     lds_barrier();
-    store_tile<C, C>(a.ws.Tm + ci * (C * C), C, sT, CP);
+    store_frag<C, C>(a.ws.Tm + ci * (C * C), sT, CP);
 }
 
 // ---------------------------------------------------------------- 2 states
 // MFMA helpers of the two sweeps (fp32, 16 x 16 x 4).  Lane l = 16 gq + r.  An
 // A fragment is a lane's share of 16 rows: row r, the contraction indices
-// 16 a + 4 gq + e (a < NA, e < 4), loaded as float4 from a row of a row-major
-// array.  B comes from an LDS tile stored transposed (Bt[col][k]), so a lane's
-// four k values for column r are one float4.  Accumulators hold rows 4 gq + e
-// of column r, which is again four consecutive k values of a transposed tile.
-template <int NA> __device__ __forceinline__ void ld_afrag(f32x4 *f, const float *row)
+// 16 a + 4 gq + e (a < NA, e < 4), loaded as float4 from the row block's NA
+// consecutive segments of a fragment-order array.  B comes from an LDS tile
+// stored transposed (Bt[col][k]), so a lane's four k values for column r are
+// one float4.  Accumulators hold rows 4 gq + e of column r, which is again four
+// consecutive k values of a transposed tile.
+template <int NA> __device__ __forceinline__ void ld_afrag(f32x4 *f, const float *blk)
 {
-    const int gq = (threadIdx.x & 63) >> 4;
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int a = 0; a < NA; ++a) f[a] = *reinterpret_cast<const f32x4 *>(row + 16 * a + 4 * gq);
+    for (int a = 0; a < NA; ++a) f[a] = *reinterpret_cast<const f32x4 *>(blk + 4 * (64 * a + lane));
 }
 
 template <int NA>
@@ -352,6 +410,19 @@ __device__ __forceinline__ f32x4 mma_rows(f32x4 acc, const f32x4 *f, const float
         for (int e = 0; e < 4; ++e) acc = mfma_f32(f[a][e], b[e], acc);
     }
     return acc;
+}
+
+// Ask the scheduler to alternate N vector-memory loads with matrix-core
+// instructions in the current region.  Issuing a chunk's operand loads stalls
+// the wave while the memory pipeline drains; spread between the products, the
+// stalls overlap the matrix cores' work instead of delaying it.
+template <int N> __device__ __forceinline__ void interleave_loads()
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    }
 }
 
 // Store a K x 16 block held transposed in LDS (St[y][x], row stride ls) to
@@ -406,13 +477,16 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
         const int n = min(C, a.T - c * C);
         f.v.load((const DT *)a.v + r0 * V + v0, H * V, n);
         f.b = tid < n ? a.beta[r0 + tid * H] : 0.f;
-        ld_afrag<K / 16>(f.kp, a.ws.Kp + ci * (C * K) + (16 * w + r) * K);
-        ld_afrag<C / 16>(f.t, a.ws.Tm + ci * (C * C) + (16 * w + r) * C);
+        // the decay factors first: the compiler moves the state's rescaling
+        // to the start of the chunk, where it must not wait for the rest
 #pragma unroll
-        for (int h = 0; h < KT; ++h) {
-            ld_afrag<C / 16>(f.km[h], a.ws.KmT + ci * (K * C) + (16 * (KT * w + h) + r) * C);
+        for (int h = 0; h < KT; ++h)
             f.g[h] = *reinterpret_cast<const f32x4 *>(a.ws.egn + ci * K + 16 * (KT * w + h) + 4 * gq);
-        }
+        ld_afrag<K / 16>(f.kp, a.ws.Kp + ci * (C * K) + w * (16 * K));
+        ld_afrag<C / 16>(f.t, a.ws.Tm + ci * (C * C) + w * (16 * C));
+#pragma unroll
+        for (int h = 0; h < KT; ++h)
+            ld_afrag<C / 16>(f.km[h], a.ws.KmT + ci * (K * C) + (KT * w + h) * (16 * C));
     };
 
     f32x4 S[KT];
@@ -445,6 +519,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
             }
             *reinterpret_cast<f32x4 *>(sRt + r * LC + 16 * w + 4 * gq) = R;
         }
+        interleave_loads<KT + K / 16 + C / 16 + KT * C / 16>();
         lds_barrier();
         {   // Delta = T R
             const f32x4 D = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.t, sRt, LC);
@@ -510,15 +585,17 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
         const int n = min(C, a.T - c * C);
         f.o.load((const DT *)a.d_o + r0 * V + v0, H * V, n);
         f.b = tid < n ? a.beta[r0 + tid * H] : 0.f;
-        ld_afrag<K / 16>(f.km, a.ws.Km + ci * (C * K) + (16 * w + r) * K);
-        ld_afrag<C / 16>(f.pt, a.ws.PT + ci * (C * C) + (16 * w + r) * C);
-        ld_afrag<C / 16>(f.tt, a.ws.TT + ci * (C * C) + (16 * w + r) * C);
+#pragma unroll
+        for (int h = 0; h < KT; ++h)   // first, as in the forward sweep
+            f.g[h] = *reinterpret_cast<const f32x4 *>(a.ws.egn + ci * K + 16 * (KT * w + h) + 4 * gq);
+        ld_afrag<K / 16>(f.km, a.ws.Km + ci * (C * K) + w * (16 * K));
+        ld_afrag<C / 16>(f.pt, a.ws.PT + ci * (C * C) + w * (16 * C));
+        ld_afrag<C / 16>(f.tt, a.ws.TT + ci * (C * C) + w * (16 * C));
 #pragma unroll
         for (int h = 0; h < KT; ++h) {
-            const int x = 16 * (KT * w + h) + r;
-            ld_afrag<C / 16>(&f.qk[h][0], a.ws.QpT + ci * (K * C) + x * C);
-            ld_afrag<C / 16>(&f.qk[h][C / 16], a.ws.KpT + ci * (K * C) + x * C);
-            f.g[h] = *reinterpret_cast<const f32x4 *>(a.ws.egn + ci * K + 16 * (KT * w + h) + 4 * gq);
+            const long xb = (KT * w + h) * (16 * C);   // row block of Qp^T and Kp^T
+            ld_afrag<C / 16>(&f.qk[h][0], a.ws.QpT + ci * (K * C) + xb);
+            ld_afrag<C / 16>(&f.qk[h][C / 16], a.ws.KpT + ci * (K * C) + xb);
         }
     };
 
@@ -559,6 +636,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) dDl[(16 * w + 4 * gq + e) * V] = dD[e];
         }
+        interleave_loads<KT + K / 16 + 2 * C / 16 + KT * 2 * C / 16>();
         lds_barrier();
         {   // Y = T^T dDelta, kept as -beta Y
             f32x4 Y = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.tt, sdDt, LC);
@@ -625,8 +703,8 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
     const float *hS = a.ws.hS + ci * (K * V), *dhS = a.ws.dhS + ci * (K * V);
     const float *Dl = a.ws.Dl + ci * (C * V), *dDl = a.ws.dDl + ci * (C * V);
     {
-        TileRegs<float, C, C> tT;
-        tT.load(a.ws.TT + ci * (C * C), C, C);
+        FragRegs<C, C> tT;
+        tT.load(a.ws.TT + ci * (C * C));
         tT.store(sTT, LC);
         if (tid < C) sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
     }
@@ -759,11 +837,13 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
     float *Zg = a.ws.dWn + ci * (C * K);    // dWn is replaced by Z once it is in LDS
     float *dGg = a.ws.dT + ci * (C * C);    // dT is replaced by dG likewise
     {
-        TileRegs<float, C, K> tW, tK;
-        TileRegs<float, C, C> tT, tdT;
+        TileRegs<float, C, K> tW;
+        FragRegs<C, K> tK;
+        FragRegs<C, C> tT;
+        TileRegs<float, C, C> tdT;
         tW.load(Zg, K, C);
-        tK.load(a.ws.Kp + ci * (C * K), K, C);
-        tT.load(a.ws.Tm + ci * (C * C), C, C);
+        tK.load(a.ws.Kp + ci * (C * K));
+        tT.load(a.ws.Tm + ci * (C * C));
         tdT.load(dGg, C, C);
         if (tid < C) {
             sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
