@@ -10,14 +10,17 @@ namespace gdn {
 // value columns per workgroup in the two state sweeps
 constexpr int BW_VB = 16;
 
-// fp32 intermediates, each an array over the B*H*ceil(T/64) chunks
-// (chunk ci = (b H + h) NC + c), rows of a chunk contiguous:
+// Intermediates, each an array over the B*H*ceil(T/64) chunks (chunk
+// ci = (b H + h) NC + c).  fp32, rows of a chunk contiguous, except where
+// marked F: fragment order (the matrix-core operand layout of the sweeps), and
+// S: the sweeps' operands, fragment order in the input dtype (bf16 inputs use
+// half of the fp32-sized slot; the last three arrays are used by bf16 only):
 struct BwWs {
     float *gam;   // [64][K]  in-chunk cumulative log-decay
-    float *Tm;    // [64][64] (I + diag(beta) G)^{-1}
-    float *TT;    // [64][64] its transpose
+    float *Tm;    // [64][64] (I + diag(beta) G)^{-1}                          F
+    float *TT;    // [64][64] its transpose                                     F
     float *Gm;    // [64][64] G, strictly lower
-    float *PT;    // [64][64] P^T (P lower with the diagonal)
+    float *PT;    // [64][64] P^T (P lower with the diagonal)                     S
     float *hS;    // [K][V]   state entering the chunk
     float *dhS;   // [K][V]   dL/d(state leaving the chunk)
     float *Dl;    // [64][V]  Delta
@@ -29,12 +32,15 @@ struct BwWs {
     float *dT;    // [64][64] dDelta (beta V)^T
     float *dgn;   // [K]      e^{gn} rowsum(S * dS')
     float *dbv;   // [64]     rowsum(V * T^T dDelta)
-    float *Kp;    // [64][K]  k e^{gamma}
-    float *Km;    // [64][K]  k e^{gn - gamma}
-    float *KpT;   // [K][64]  Kp^T
-    float *KmT;   // [K][64]  Km^T
-    float *QpT;   // [K][64]  (q e^{gamma})^T
+    float *Kp;    // [64][K]  k e^{gamma}                                       F
+    float *Km;    // [64][K]  k e^{gn - gamma}                                  S
+    float *KpT;   // [K][64]  Kp^T                                              S
+    float *KmT;   // [K][64]  Km^T                                              S
+    float *QpT;   // [K][64]  (q e^{gamma})^T                                   S
     float *egn;   // [K]      e^{gn}
+    float *Kps;   // [64][K]  Kp                                                S, bf16
+    float *Tms;   // [64][64] T                                                 S, bf16
+    float *TTs;   // [64][64] T^T                                               S, bf16
 };
 
 struct BwArgs {
@@ -53,16 +59,17 @@ inline unsigned long long bw_workspace(unsigned long long nchunks, int K, int V,
                                        BwWs *ws)
 {
     const unsigned long long C = 64, Ku = (unsigned)K, Vu = (unsigned)V;
-    constexpr int NA = 22;
+    constexpr int NA = 25;
     const unsigned long long per[NA] = {C * Ku, C * C, C * C, C * C, C * C, Ku * Vu, Ku * Vu,
                                         C * Vu, C * Vu, C * Ku, C * Ku, C * Ku, C * C, C * C,
-                                        Ku, C, C * Ku, C * Ku, C * Ku, C * Ku, C * Ku, Ku};
+                                        Ku, C, C * Ku, C * Ku, C * Ku, C * Ku, C * Ku, Ku,
+                                        C * Ku / 2, C * C / 2, C * C / 2};
     float **dst[NA] = {nullptr};
     if (ws) {
         float **p[NA] = {&ws->gam, &ws->Tm, &ws->TT, &ws->Gm, &ws->PT, &ws->hS, &ws->dhS,
                          &ws->Dl, &ws->dDl, &ws->dQp, &ws->dKm, &ws->dWn, &ws->dP, &ws->dT,
                          &ws->dgn, &ws->dbv, &ws->Kp, &ws->Km, &ws->KpT, &ws->KmT, &ws->QpT,
-                         &ws->egn};
+                         &ws->egn, &ws->Kps, &ws->Tms, &ws->TTs};
         for (int i = 0; i < NA; ++i) dst[i] = p[i];
     }
     unsigned long long off = 0;

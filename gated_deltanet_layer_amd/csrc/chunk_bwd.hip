@@ -45,6 +45,8 @@
 // a small output tile whose rows and columns are interleaved across the
 // workgroup, so that the operand reads of a wave hit consecutive or odd-strided
 // LDS addresses.  Every load of a tile is issued before the first is used.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "chunk_bwd.h"
 
@@ -146,16 +148,45 @@ template <typename T, int R, int W> struct TileRegs {
     }
 };
 
-// Fragment order of an R x L fp32 array (R and L multiples of 16): the layout
-// in which the matrix-core A operands are read.  1 KB segments, one per
-// (16-row block, 16-column block), row block major; lane 16 g + r of a segment
-// holds row r, columns 4 g .. 4 g + 3 of its block as one float4.  A wave's
-// load of one A fragment is then one contiguous 1 KB read (eight whole cache
-// lines) instead of 64 bytes from each of 16 rows.
-template <int L> __device__ __forceinline__ int frag_idx(int row, int col)
+// Fragment order of an R x L array of OT (R and L multiples of 16): the layout
+// in which the matrix-core A operands are read.  1 KB segments, row-block
+// major; lane 16 g + r of a segment holds 16 bytes of row r: in fp32, columns
+// 4 g .. 4 g + 3 of one 16-column block; in bf16, those of two neighbouring
+// blocks (2p, then 2p + 1).  A wave's load of one fragment is then one
+// contiguous 1 KB read (eight whole cache lines) instead of 64 or 32 bytes from
+// each of 16 rows.  A 16-row block starts 16 L elements into the array.
+template <typename OT> struct FragOf {
+    static constexpr int VE = 16 / (int)sizeof(OT);   // elements per lane
+    static constexpr int SP = VE / 4;                 // 16-column blocks per segment
+};
+template <typename OT, int L> __device__ __forceinline__ int frag_idx(int row, int col)
 {
-    return ((((row >> 4) * (L / 16) + (col >> 4)) * 64 + ((col & 15) >> 2) * 16 + (row & 15)) << 2) +
-           (col & 3);
+    constexpr int VE = FragOf<OT>::VE, SP = FragOf<OT>::SP;
+    const int a = col >> 4;
+    return (((row >> 4) * (L / 16 / SP) + a / SP) * 64 + ((col & 15) >> 2) * 16 + (row & 15)) * VE +
+           (a % SP) * 4 + (col & 3);
+}
+
+// Four consecutive elements of a fragment-order array (one 8- or 16-byte store).
+__device__ __forceinline__ void st4(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+__device__ __forceinline__ void st4(__bf16 *p, f32x4 x) { *reinterpret_cast<bf16x4 *>(p) = cvt4(x); }
+
+// Write an R x L array of OT in fragment order, one 16-byte store per thread
+// and step; val(row, col) gives the four values at columns col .. col + 3.
+template <typename OT, int R, int L, typename F>
+__device__ __forceinline__ void write_frag(OT *dst, F val)
+{
+    constexpr int VE = FragOf<OT>::VE, SP = FragOf<OT>::SP, NSR = L / 16 / SP;
+    for (int v = threadIdx.x; v < R * L / VE; v += BW_NTHR) {
+        const int seg = v >> 6, l = v & 63;
+        const int row = 16 * (seg / NSR) + (l & 15), col = 16 * SP * (seg % NSR) + 4 * (l >> 4);
+        if constexpr (SP == 1) {
+            st4(dst + VE * v, val(row, col));
+        } else {
+            const f32x4 x0 = val(row, col), x1 = val(row, col + 16);
+            *reinterpret_cast<bf16x8 *>(dst + VE * v) = cat8(cvt4(x0), cvt4(x1));
+        }
+    }
 }
 
 // Registers holding an R x L array in fragment order, fetched with contiguous
@@ -181,17 +212,14 @@ template <int R, int L> struct FragRegs {
     }
 };
 
-// Store an R x L fp32 LDS tile (row stride ls) in fragment order, one
-// contiguous 16-byte store per thread and step.
-template <int R, int L>
-__device__ __forceinline__ void store_frag(float *dst, const float *src, int ls)
+// Store an R x L fp32 LDS tile (row stride ls) in fragment order.
+template <typename OT, int R, int L>
+__device__ __forceinline__ void store_frag(OT *dst, const float *src, int ls)
 {
-    for (int v = threadIdx.x; v < R * L / 4; v += BW_NTHR) {
-        const int seg = v >> 6, l = v & 63;
-        const int row = 16 * (seg / (L / 16)) + (l & 15), col = 16 * (seg % (L / 16)) + 4 * (l >> 4);
+    write_frag<OT, R, L>(dst, [&](int row, int col) {
         const float *s = src + row * ls + col;
-        *reinterpret_cast<f32x4 *>(dst + 4 * v) = f32x4{s[0], s[1], s[2], s[3]};
-    }
+        return f32x4{s[0], s[1], s[2], s[3]};
+    });
 }
 
 // Store an R x W fp32 LDS tile (row stride ls) to global rows gs floats apart,
@@ -210,6 +238,7 @@ __device__ __forceinline__ void store_tile(float *dst, long gs, const float *src
 template <typename DT, int K, bool CH>
 __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
 {
+    using OT = DT;   // storage of the sweeps' operands
     constexpr int C = BW_C, KP = K + 4, CP = C + 1;   // rows of k, q, gamma 16-byte aligned
     extern __shared__ __attribute__((aligned(256))) float sm[];
     float *sk = sm, *sq = sk + C * KP, *sg = sq + C * KP, *sA = sg + C * KP, *sT = sA + C * CP;
@@ -250,40 +279,51 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
             const int t = v / (K / 4), x = (v % (K / 4)) * 4;
             *reinterpret_cast<f32x4 *>(gam + t * K + x) = *reinterpret_cast<const f32x4 *>(sg + t * KP + x);
         }
-        float *Kp = a.ws.Kp + ci * (C * K), *Km = a.ws.Km + ci * (C * K);
-        for (int v = tid; v < C * K / 4; v += BW_NTHR) {
-            const int seg = v >> 6, l = v & 63;
-            const int t = 16 * (seg / (K / 16)) + (l & 15), x = 16 * (seg % (K / 16)) + 4 * (l >> 4);
+        // by rows: element (t, x), four channels x .. x + 3
+        auto kp_row = [&](int t, int x) {
+            const f32x4 k4 = *reinterpret_cast<const f32x4 *>(sk + t * KP + x);
+            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sg + t * KP + x);
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = k4[e] * __expf(g4[e]);
+            return o;
+        };
+        auto km_row = [&](int t, int x) {
             const f32x4 k4 = *reinterpret_cast<const f32x4 *>(sk + t * KP + x);
             const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sg + t * KP + x);
             const f32x4 n4 = *reinterpret_cast<const f32x4 *>(sg + (C - 1) * KP + x);
-            f32x4 kp, km;
+            f32x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kp[e] = k4[e] * __expf(g4[e]);
-                km[e] = k4[e] * __expf(n4[e] - g4[e]);
-            }
-            *reinterpret_cast<f32x4 *>(Kp + 4 * v) = kp;
-            *reinterpret_cast<f32x4 *>(Km + 4 * v) = km;
-        }
-        float *KpT = a.ws.KpT + ci * (K * C), *KmT = a.ws.KmT + ci * (K * C);
-        float *QpT = a.ws.QpT + ci * (K * C);
-        for (int v = tid; v < C * K / 4; v += BW_NTHR) {
-            const int seg = v >> 6, l = v & 63;
-            const int x = 16 * (seg / (C / 16)) + (l & 15), t = 16 * (seg % (C / 16)) + 4 * (l >> 4);
+            for (int e = 0; e < 4; ++e) o[e] = k4[e] * __expf(n4[e] - g4[e]);
+            return o;
+        };
+        // transposed: element (x, t), four tokens t .. t + 3
+        auto kp_col = [&](int x, int t) {
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = sk[(t + e) * KP + x] * __expf(sg[(t + e) * KP + x]);
+            return o;
+        };
+        auto qp_col = [&](int x, int t) {
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = sq[(t + e) * KP + x] * __expf(sg[(t + e) * KP + x]);
+            return o;
+        };
+        auto km_col = [&](int x, int t) {
             const float gn = sg[(C - 1) * KP + x];
-            f32x4 kp, km, qp;
+            f32x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float gm = sg[(t + e) * KP + x], eg = __expf(gm);
-                kp[e] = sk[(t + e) * KP + x] * eg;
-                qp[e] = sq[(t + e) * KP + x] * eg;
-                km[e] = sk[(t + e) * KP + x] * __expf(gn - gm);
-            }
-            *reinterpret_cast<f32x4 *>(KpT + 4 * v) = kp;
-            *reinterpret_cast<f32x4 *>(KmT + 4 * v) = km;
-            *reinterpret_cast<f32x4 *>(QpT + 4 * v) = qp;
-        }
+            for (int e = 0; e < 4; ++e) o[e] = sk[(t + e) * KP + x] * __expf(gn - sg[(t + e) * KP + x]);
+            return o;
+        };
+        write_frag<float, C, K>(a.ws.Kp + ci * (C * K), kp_row);   // fp32 for the gradient kernels
+        if constexpr (!std::is_same<OT, float>::value)
+            write_frag<OT, C, K>(reinterpret_cast<OT *>(a.ws.Kps) + ci * (C * K), kp_row);
+        write_frag<OT, C, K>(reinterpret_cast<OT *>(a.ws.Km) + ci * (C * K), km_row);
+        write_frag<OT, K, C>(reinterpret_cast<OT *>(a.ws.KpT) + ci * (K * C), kp_col);
+        write_frag<OT, K, C>(reinterpret_cast<OT *>(a.ws.KmT) + ci * (K * C), km_col);
+        write_frag<OT, K, C>(reinterpret_cast<OT *>(a.ws.QpT) + ci * (K * C), qp_col);
         if (tid < K) a.ws.egn[ci * K + tid] = __expf(sg[(C - 1) * KP + tid]);
     }
 
@@ -294,7 +334,8 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
     // k_s e^{gamma_rho - gamma_s}.  With g >= -5 per token no factor exceeds
     // e^{8 * 5}; for s in an earlier block the B factor is at most 1.  Scalar
     // gate: the plain products, scaled by e^{gamma_t - gamma_s} afterwards.
-    float *Gm = a.ws.Gm + ci * (C * C), *PT = a.ws.PT + ci * (C * C);
+    float *Gm = a.ws.Gm + ci * (C * C);
+    OT *PT = reinterpret_cast<OT *>(a.ws.PT) + ci * (C * C);
     {
         const int lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
         for (int p = w; p < 10; p += 4) {
@@ -328,8 +369,8 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
                 }
             }
             // this lane holds rows t = 16 I + 4 gq + e of column s = 16 J + r16,
-            // which in P^T is row s, columns t: lane 16 gq + r16 of the
-            // fragment-order segment (J, I)
+            // which in P^T is row s, columns t: four consecutive elements in
+            // fragment order
             f32x4 p4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -345,14 +386,14 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
                 Gm[t * C + s] = gv;
                 sA[t * CP + s] = sb[t] * gv;
             }
-            *reinterpret_cast<f32x4 *>(PT + 4 * ((J * (C / 16) + I) * 64 + lane)) = p4;
+            st4(PT + frag_idx<OT, C>(16 * J + r16, 16 * I + 4 * gq), p4);
         }
     }
     for (int idx = tid; idx < C * C; idx += BW_NTHR) {   // the blocks above the diagonal
         const int t = idx / C, s = idx % C;
         if (s / 16 > t / 16) {
             Gm[idx] = 0.f;
-            PT[frag_idx<C>(s, t)] = 0.f;
+            PT[frag_idx<OT, C>(s, t)] = OT(0.f);
             sA[t * CP + s] = 0.f;
         }
     }
@@ -376,38 +417,66 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
 #pragma unroll
         for (int i = 0; i < C; ++i) sT[i * CP + j] = col[i];
         float *TT = a.ws.TT + ci * (C * C);   // T^T row j = column j of T
+        OT *TTs = reinterpret_cast<OT *>(a.ws.TTs) + ci * (C * C);
 #pragma unroll
-        for (int i = 0; i < C; i += 4)
-            *reinterpret_cast<f32x4 *>(TT + frag_idx<C>(j, i)) = f32x4{col[i], col[i + 1], col[i + 2], col[i + 3]};
+        for (int i = 0; i < C; i += 4) {
+            const f32x4 x = {col[i], col[i + 1], col[i + 2], col[i + 3]};
+            st4(TT + frag_idx<float, C>(j, i), x);
+            if constexpr (!std::is_same<OT, float>::value) st4(TTs + frag_idx<OT, C>(j, i), x);
+        }
     }
     lds_barrier();
-    store_frag<C, C>(a.ws.Tm + ci * (C * C), sT, CP);
+    store_frag<float, C, C>(a.ws.Tm + ci * (C * C), sT, CP);
+    if constexpr (!std::is_same<OT, float>::value)
+        store_frag<OT, C, C>(reinterpret_cast<OT *>(a.ws.Tms) + ci * (C * C), sT, CP);
 }
 
 // ---------------------------------------------------------------- 2 states
 // MFMA helpers of the two sweeps (fp32, 16 x 16 x 4).  Lane l = 16 gq + r.  An
 // A fragment is a lane's share of 16 rows: row r, the contraction indices
-// 16 a + 4 gq + e (a < NA, e < 4), loaded as float4 from the row block's NA
-// consecutive segments of a fragment-order array.  B comes from an LDS tile
-// stored transposed (Bt[col][k]), so a lane's four k values for column r are
-// one float4.  Accumulators hold rows 4 gq + e of column r, which is again four
+// 16 a + 4 gq + e (a < NA, e < 4), loaded with 16-byte loads from the row
+// block's consecutive segments of a fragment-order array (bf16 operands are
+// widened to fp32 as they are used).  B comes from an LDS tile stored
+// transposed (Bt[col][k]), so a lane's four k values for column r are one
+// float4.  Accumulators hold rows 4 gq + e of column r, which is again four
 // consecutive k values of a transposed tile.
-template <int NA> __device__ __forceinline__ void ld_afrag(f32x4 *f, const float *blk)
-{
-    const int lane = threadIdx.x & 63;
+template <typename OT, int NA> struct AFrag;
+template <int NA> struct AFrag<float, NA> {
+    f32x4 f[NA];
+    // steps A0 .. A0 + N - 1 from a row block of N steps
+    template <int A0, int N> __device__ __forceinline__ void load(const float *blk) {
+        const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int a = 0; a < NA; ++a) f[a] = *reinterpret_cast<const f32x4 *>(blk + 4 * (64 * a + lane));
-}
+        for (int a = 0; a < N; ++a) f[A0 + a] = *reinterpret_cast<const f32x4 *>(blk + 4 * (64 * a + lane));
+    }
+    __device__ __forceinline__ f32x4 get(int a) const { return f[a]; }
+};
+template <int NA> struct AFrag<__bf16, NA> {
+    static_assert(NA % 2 == 0, "bf16 fragments come in pairs of steps");
+    uint4 u[NA / 2];
+    template <int A0, int N> __device__ __forceinline__ void load(const __bf16 *blk) {
+        static_assert(A0 % 2 == 0 && N % 2 == 0, "pairs of steps");
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int p = 0; p < N / 2; ++p) u[A0 / 2 + p] = *reinterpret_cast<const uint4 *>(blk + 8 * (64 * p + lane));
+    }
+    __device__ __forceinline__ f32x4 get(int a) const {
+        const unsigned lo = (a & 1) ? u[a >> 1].z : u[a >> 1].x, hi = (a & 1) ? u[a >> 1].w : u[a >> 1].y;
+        return f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                     __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+    }
+};
 
-template <int NA>
-__device__ __forceinline__ f32x4 mma_rows(f32x4 acc, const f32x4 *f, const float *Bt, int ldb)
+template <int NA, typename OT>
+__device__ __forceinline__ f32x4 mma_rows(f32x4 acc, const AFrag<OT, NA> &f, const float *Bt, int ldb)
 {
     const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
         const f32x4 b = *reinterpret_cast<const f32x4 *>(Bt + r * ldb + 16 * a + 4 * gq);
+        const f32x4 x = f.get(a);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = mfma_f32(f[a][e], b[e], acc);
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(x[e], b[e], acc);
     }
     return acc;
 }
@@ -445,10 +514,10 @@ __device__ __forceinline__ void store_state_block(float *dst, const float *St, i
 // work before they are used (the loop is unrolled by two so that the sets keep
 // fixed registers).  The barriers in the loop wait for LDS traffic only.
 template <typename DT, int K, int C, int KT, int VB> struct StSet {
-    f32x4 kp[K / 16];        // Kp row 16 w + r
-    f32x4 t[C / 16];         // T row 16 w + r
-    f32x4 km[KT][C / 16];    // Km^T rows 16 (KT w + h) + r
-    f32x4 g[KT];             // e^{gn} of this lane's accumulator rows
+    AFrag<DT, K / 16> kp;        // Kp row 16 w + r
+    AFrag<DT, C / 16> t;         // T row 16 w + r
+    AFrag<DT, C / 16> km[KT];    // Km^T rows 16 (KT w + h) + r
+    f32x4 g[KT];                 // e^{gn} of this lane's accumulator rows
     TileRegs<DT, C, VB> v;   // v tile
     float b;                 // beta of token tid
 };
@@ -469,6 +538,11 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
     const int v0 = vb * VB;
     const long H = a.H;
     using Set = StSet<DT, K, C, KT, VB>;
+    constexpr int SP = FragOf<DT>::SP;
+    constexpr bool F32 = std::is_same<DT, float>::value;
+    // fp32 operands are the gradient kernels' own arrays; bf16 ones are copies
+    const DT *kp_src = reinterpret_cast<const DT *>(F32 ? a.ws.Kp : a.ws.Kps);
+    const DT *t_src = reinterpret_cast<const DT *>(F32 ? a.ws.Tm : a.ws.Tms);
 
     // The loads are issued in the order of first use, so that each wait covers
     // only what it needs (the memory counter retires loads in order).
@@ -482,11 +556,11 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
 #pragma unroll
         for (int h = 0; h < KT; ++h)
             f.g[h] = *reinterpret_cast<const f32x4 *>(a.ws.egn + ci * K + 16 * (KT * w + h) + 4 * gq);
-        ld_afrag<K / 16>(f.kp, a.ws.Kp + ci * (C * K) + w * (16 * K));
-        ld_afrag<C / 16>(f.t, a.ws.Tm + ci * (C * C) + w * (16 * C));
+        f.kp.template load<0, K / 16>(kp_src + ci * (C * K) + w * (16 * K));
+        f.t.template load<0, C / 16>(t_src + ci * (C * C) + w * (16 * C));
 #pragma unroll
         for (int h = 0; h < KT; ++h)
-            ld_afrag<C / 16>(f.km[h], a.ws.KmT + ci * (K * C) + (KT * w + h) * (16 * C));
+            f.km[h].template load<0, C / 16>(reinterpret_cast<const DT *>(a.ws.KmT) + ci * (K * C) + (KT * w + h) * (16 * C));
     };
 
     f32x4 S[KT];
@@ -519,7 +593,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
             }
             *reinterpret_cast<f32x4 *>(sRt + r * LC + 16 * w + 4 * gq) = R;
         }
-        interleave_loads<KT + K / 16 + C / 16 + KT * C / 16>();
+        interleave_loads<KT + (K / 16 + C / 16 + KT * C / 16) / SP>();
         lds_barrier();
         {   // Delta = T R
             const f32x4 D = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.t, sRt, LC);
@@ -555,10 +629,10 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
 template <typename DT, int K, int C, int KT, int VB> struct DsSet {
     TileRegs<DT, C, VB> o;       // dO tile
     float b;                     // beta of token tid
-    f32x4 km[K / 16];            // Km row 16 w + r
-    f32x4 pt[C / 16];            // P^T row 16 w + r
-    f32x4 tt[C / 16];            // T^T row 16 w + r
-    f32x4 qk[KT][2 * C / 16];    // [Qp^T | Kp^T] rows 16 (KT w + h) + r
+    AFrag<DT, K / 16> km;            // Km row 16 w + r
+    AFrag<DT, C / 16> pt;            // P^T row 16 w + r
+    AFrag<DT, C / 16> tt;            // T^T row 16 w + r
+    AFrag<DT, 2 * C / 16> qk[KT];    // [Qp^T | Kp^T] rows 16 (KT w + h) + r
     f32x4 g[KT];
 };
 
@@ -578,6 +652,8 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
     const int v0 = vb * VB;
     const long H = a.H;
     using Set = DsSet<DT, K, C, KT, VB>;
+    constexpr int SP = FragOf<DT>::SP;
+    const DT *tt_src = reinterpret_cast<const DT *>(std::is_same<DT, float>::value ? a.ws.TT : a.ws.TTs);
 
     // in the order of first use
     auto fetch = [&](Set &f, int c) {
@@ -588,14 +664,14 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
 #pragma unroll
         for (int h = 0; h < KT; ++h)   // first, as in the forward sweep
             f.g[h] = *reinterpret_cast<const f32x4 *>(a.ws.egn + ci * K + 16 * (KT * w + h) + 4 * gq);
-        ld_afrag<K / 16>(f.km, a.ws.Km + ci * (C * K) + w * (16 * K));
-        ld_afrag<C / 16>(f.pt, a.ws.PT + ci * (C * C) + w * (16 * C));
-        ld_afrag<C / 16>(f.tt, a.ws.TT + ci * (C * C) + w * (16 * C));
+        f.km.template load<0, K / 16>(reinterpret_cast<const DT *>(a.ws.Km) + ci * (C * K) + w * (16 * K));
+        f.pt.template load<0, C / 16>(reinterpret_cast<const DT *>(a.ws.PT) + ci * (C * C) + w * (16 * C));
+        f.tt.template load<0, C / 16>(tt_src + ci * (C * C) + w * (16 * C));
 #pragma unroll
         for (int h = 0; h < KT; ++h) {
             const long xb = (KT * w + h) * (16 * C);   // row block of Qp^T and Kp^T
-            ld_afrag<C / 16>(&f.qk[h][0], a.ws.QpT + ci * (K * C) + xb);
-            ld_afrag<C / 16>(&f.qk[h][C / 16], a.ws.KpT + ci * (K * C) + xb);
+            f.qk[h].template load<0, C / 16>(reinterpret_cast<const DT *>(a.ws.QpT) + ci * (K * C) + xb);
+            f.qk[h].template load<C / 16, C / 16>(reinterpret_cast<const DT *>(a.ws.KpT) + ci * (K * C) + xb);
         }
     };
 
@@ -636,7 +712,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) dDl[(16 * w + 4 * gq + e) * V] = dD[e];
         }
-        interleave_loads<KT + K / 16 + 2 * C / 16 + KT * 2 * C / 16>();
+        interleave_loads<KT + (K / 16 + 2 * C / 16 + KT * 2 * C / 16) / SP>();
         lds_barrier();
         {   // Y = T^T dDelta, kept as -beta Y
             f32x4 Y = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.tt, sdDt, LC);
