@@ -432,14 +432,17 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
 }
 
 // ---------------------------------------------------------------- 2 states
-// MFMA helpers of the two sweeps (fp32, 16 x 16 x 4).  Lane l = 16 gq + r.  An
-// A fragment is a lane's share of 16 rows: row r, the contraction indices
-// 16 a + 4 gq + e (a < NA, e < 4), loaded with 16-byte loads from the row
-// block's consecutive segments of a fragment-order array (bf16 operands are
-// widened to fp32 as they are used).  B comes from an LDS tile stored
+// MFMA helpers of the two sweeps.  Lane l = 16 gq + r.  An A fragment is a
+// lane's share of 16 rows: row r, the contraction indices 16 a + 4 gq + e
+// (a < NA, e < 4), loaded with 16-byte loads from the row block's consecutive
+// segments of a fragment-order array.  B comes from an fp32 LDS tile stored
 // transposed (Bt[col][k]), so a lane's four k values for column r are one
-// float4.  Accumulators hold rows 4 gq + e of column r, which is again four
-// consecutive k values of a transposed tile.
+// float4.  fp32 operands use the 16 x 16 x 4 fp32 instruction, one step a at a
+// time; bf16 operands the 16 x 16 x 32 bf16 one, two steps at a time (the
+// pair of column blocks of a bf16 segment is exactly that instruction's
+// k-slot run per lane group), with B rounded to bf16 as it is read.
+// Accumulators hold rows 4 gq + e of column r, which is again four consecutive
+// k values of a transposed tile.
 template <typename OT, int NA> struct AFrag;
 template <int NA> struct AFrag<float, NA> {
     f32x4 f[NA];
@@ -460,23 +463,31 @@ template <int NA> struct AFrag<__bf16, NA> {
 #pragma unroll
         for (int p = 0; p < N / 2; ++p) u[A0 / 2 + p] = *reinterpret_cast<const uint4 *>(blk + 8 * (64 * p + lane));
     }
-    __device__ __forceinline__ f32x4 get(int a) const {
-        const unsigned lo = (a & 1) ? u[a >> 1].z : u[a >> 1].x, hi = (a & 1) ? u[a >> 1].w : u[a >> 1].y;
-        return f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
-                     __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
-    }
 };
 
-template <int NA, typename OT>
-__device__ __forceinline__ f32x4 mma_rows(f32x4 acc, const AFrag<OT, NA> &f, const float *Bt, int ldb)
+template <int NA>
+__device__ __forceinline__ f32x4 mma_rows(f32x4 acc, const AFrag<float, NA> &f, const float *Bt, int ldb)
 {
     const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
         const f32x4 b = *reinterpret_cast<const f32x4 *>(Bt + r * ldb + 16 * a + 4 * gq);
-        const f32x4 x = f.get(a);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = mfma_f32(x[e], b[e], acc);
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(f.f[a][e], b[e], acc);
+    }
+    return acc;
+}
+
+template <int NA>
+__device__ __forceinline__ f32x4 mma_rows(f32x4 acc, const AFrag<__bf16, NA> &f, const float *Bt, int ldb)
+{
+    const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int p = 0; p < NA / 2; ++p) {
+        const float *b = Bt + r * ldb + 32 * p + 4 * gq;
+        const bf16x8 bb = cat8(cvt4(*reinterpret_cast<const f32x4 *>(b)),
+                               cvt4(*reinterpret_cast<const f32x4 *>(b + 16)));
+        acc = mfma_bf16(__builtin_bit_cast(bf16x8, f.u[p]), bb, acc);
     }
     return acc;
 }
