@@ -398,34 +398,62 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
         }
     }
     lds_barrier();
-    // T = (I + A)^{-1} by forward substitution, one column per thread, the
-    // column held in registers (the row of A is the same for every lane)
-    if (tid < C) {
-        const int j = tid;
-        float col[C];
+    // T = (I + A)^{-1} by blocks of 16 (A strictly lower, so T is unit lower):
+    // the four diagonal inverses T_II by forward substitution (lane j of wave
+    // I solves column j), then block rows I = 1, 2, 3 in turn, each block on
+    // its own wave: T_IJ = -T_II sum_{J <= M < I} A_IM T_MJ, on the fp32 matrix
+    // cores.  A k-step j takes k = 4 gq + j in each lane group, so the
+    // accumulator of the sum is already the B operand of the product with T_II.
+    {
+        const int lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
+        if (lane < 16) {
+            const int j = lane, I0 = 16 * w;
+            float x[16];
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            float acc0 = i == j ? 1.f : 0.f, acc1 = 0.f;
+            for (int i = 0; i < 16; ++i) {
+                float acc = i == j ? 1.f : 0.f;
 #pragma unroll
-            for (int s = 0; s + 1 < i; s += 2) {
-                acc0 = fmaf(-sA[i * CP + s], col[s], acc0);
-                acc1 = fmaf(-sA[i * CP + s + 1], col[s + 1], acc1);
+                for (int s2 = 0; s2 < i; ++s2) acc = fmaf(-sA[(I0 + i) * CP + I0 + s2], x[s2], acc);
+                x[i] = acc;
             }
-            if (i & 1) acc0 = fmaf(-sA[i * CP + i - 1], col[i - 1], acc0);
-            col[i] = acc0 + acc1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sT[(I0 + i) * CP + I0 + j] = x[i];
         }
+        // blocks above the diagonal
+        for (int idx = tid; idx < C * C; idx += BW_NTHR) {
+            const int t = idx / C, s2 = idx % C;
+            if (s2 / 16 > t / 16) sT[t * CP + s2] = 0.f;
+        }
+        lds_barrier();
 #pragma unroll
-        for (int i = 0; i < C; ++i) sT[i * CP + j] = col[i];
-        float *TT = a.ws.TT + ci * (C * C);   // T^T row j = column j of T
-        OT *TTs = reinterpret_cast<OT *>(a.ws.TTs) + ci * (C * C);
+        for (int I = 1; I < 4; ++I) {
+            if (w < I) {
+                const int J = w;
+                f32x4 X = {0.f, 0.f, 0.f, 0.f};
+                for (int M = J; M < I; ++M) {
 #pragma unroll
-        for (int i = 0; i < C; i += 4) {
-            const f32x4 x = {col[i], col[i + 1], col[i + 2], col[i + 3]};
-            st4(TT + frag_idx<float, C>(j, i), x);
-            if constexpr (!std::is_same<OT, float>::value) st4(TTs + frag_idx<OT, C>(j, i), x);
+                    for (int j = 0; j < 4; ++j)
+                        X = mfma_f32(sA[(16 * I + r16) * CP + 16 * M + 4 * gq + j],
+                                     sT[(16 * M + 4 * gq + j) * CP + 16 * J + r16], X);
+                }
+                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    Y = mfma_f32(sT[(16 * I + r16) * CP + 16 * I + 4 * gq + j], X[j], Y);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sT[(16 * I + 4 * gq + e) * CP + 16 * J + r16] = -Y[e];
+            }
+            lds_barrier();
         }
     }
-    lds_barrier();
+    // T^T in fragment order (row j of T^T is column j of T), and T
+    auto tt_val = [&](int row, int col) {
+        return f32x4{sT[col * CP + row], sT[(col + 1) * CP + row], sT[(col + 2) * CP + row],
+                     sT[(col + 3) * CP + row]};
+    };
+    write_frag<float, C, C>(a.ws.TT + ci * (C * C), tt_val);
+    if constexpr (!std::is_same<OT, float>::value)
+        write_frag<OT, C, C>(reinterpret_cast<OT *>(a.ws.TTs) + ci * (C * C), tt_val);
     store_frag<float, C, C>(a.ws.Tm + ci * (C * C), sT, CP);
     if constexpr (!std::is_same<OT, float>::value)
         store_frag<OT, C, C>(reinterpret_cast<OT *>(a.ws.Tms) + ci * (C * C), sT, CP);
