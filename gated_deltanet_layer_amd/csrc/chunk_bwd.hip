@@ -934,23 +934,68 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ---------------------------------------------------------------- 5 kgrad1
+// One 16 x 16 output tile on the fp32 matrix cores from LDS operands:
+// acc(row0 + 4 gq + e, col0 + r) += sum_{k < KD} A(row, k) B(k, col), with
+// A(row, k) = A[row AR + k AK] and B(k, col) = B[k BK + col BC].  The k-step j
+// of each 16-wide k block takes k = 4 gq + j in lane group gq; where the k
+// stride is 1 the lane's four k values are one 16-byte read.
+template <int KD, int AR, int AK, int BK, int BC>
+__device__ __forceinline__ f32x4 mma_lds(f32x4 acc, const float *A, const float *B, int row0, int col0)
+{
+    const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
+    const float *a = A + (row0 + r) * AR + 4 * gq * AK, *b = B + 4 * gq * BK + (col0 + r) * BC;
+#pragma unroll
+    for (int k0 = 0; k0 < KD; k0 += 16) {
+        f32x4 av, bv;
+        if constexpr (AK == 1) {
+            av = *reinterpret_cast<const f32x4 *>(a + k0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) av[j] = a[(k0 + j) * AK];
+        }
+        if constexpr (BK == 1) {
+            bv = *reinterpret_cast<const f32x4 *>(b + k0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = b[(k0 + j) * BK];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma_f32(av[j], bv[j], acc);
+    }
+    return acc;
+}
+
+// Sum a per-lane value over the 16 lanes of a lane group (one row of a tile).
+__device__ __forceinline__ float sum16(float x)
+{
+    x += __shfl_xor(x, 1, 16);
+    x += __shfl_xor(x, 2, 16);
+    x += __shfl_xor(x, 4, 16);
+    x += __shfl_xor(x, 8, 16);
+    return x;
+}
+
 // The C x C part of the chain: Z = -T^T dWn (replaces dWn in the workspace),
 // dT -= dWn (beta Kp)^T, dA = -T^T dT T^T, dG = diag(beta) dA (replaces dT),
-// and the final dbeta = rowsum(V * Y) + rowsum(Kp * Z) + rowsum(dA * G).
+// and the final dbeta = rowsum(V * Y) + rowsum(Kp * Z) + rowsum(dA * G).  All
+// four products on the fp32 matrix cores; LDS rows padded to K + 4 and C + 4
+// floats, which keeps every operand read of a wave on distinct banks.
 template <typename DT, int K>
 __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
 {
-    constexpr int C = BW_C, KP = K + 1, CP = C + 1;
+    constexpr int C = BW_C, LK = K + 4, LC = C + 4, NXB = K / 16;
     extern __shared__ __attribute__((aligned(256))) float sm[];
-    float *sb = sm, *sdb = sb + C, *sWn = sdb + C, *sKp = sWn + C * KP, *sT = sKp + C * KP;
-    float *sdT = sT + C * CP, *sM = sdT + C * CP;
-    const int tid = threadIdx.x;
+    float *sb = sm, *sdb = sb + C, *sWn = sdb + C, *sKp = sWn + C * LK, *sT = sKp + C * LK;
+    float *sdT = sT + C * LC, *sM = sdT + C * LC, *spart = sM + C * LC;   // spart [4][C]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
     const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
     const int t0 = c * C, n = min(C, a.T - t0);
     const long ci = (long)sl * a.NC + c;
     const long H = a.H, r0 = tok_row(a, sl, t0);
     float *Zg = a.ws.dWn + ci * (C * K);    // dWn is replaced by Z once it is in LDS
     float *dGg = a.ws.dT + ci * (C * C);    // dT is replaced by dG likewise
+    const float *Gm = a.ws.Gm + ci * (C * C);
+    float gv[4][4];   // G at rows 16 w + 4 gq + e, columns 16 J + r16 (read before dG is stored)
     {
         TileRegs<float, C, K> tW;
         FragRegs<C, K> tK;
@@ -960,91 +1005,85 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
         tK.load(a.ws.Kp + ci * (C * K));
         tT.load(a.ws.Tm + ci * (C * C));
         tdT.load(dGg, C, C);
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gv[J][e] = Gm[(16 * w + 4 * gq + e) * C + 16 * J + r16];
         if (tid < C) {
             sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
             sdb[tid] = a.ws.dbv[ci * C + tid];
         }
-        tW.store(sWn, KP);
-        tK.store(sKp, KP);
-        tT.store(sT, CP);
-        tdT.store(sdT, CP);
+        tW.store(sWn, LK);
+        tK.store(sKp, LK);
+        tT.store(sT, LC);
+        tdT.store(sdT, LC);
     }
     lds_barrier();
-    {   // Z = -T^T dWn; dbeta += rowsum(Kp * Z)
-        using TL = Tile<C, K, 4, K / 16>;
-        const TL tl;
-        float acc[4][K / 16] = {};
-        mm_acc<C, K, 4, K / 16, C, 1, CP, KP, 1>(acc, sT, sWn, tl.mt, tl.nt);
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    {   // Z = -T^T dWn (all rows, this wave's column blocks); rowsum(Kp * Z) per
+        // wave, added to dbeta in a fixed order below (results do not depend on
+        // the waves' timing)
+        constexpr int XW = NXB / 4;   // column blocks per wave
+        float part[4][4] = {};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = tl.row(i);
-            float part = 0.f;
+        for (int R = 0; R < 4; ++R)
 #pragma unroll
-            for (int j = 0; j < K / 16; ++j) {
-                const int x = tl.col(j);
-                Zg[t * K + x] = -acc[i][j];
-                part = fmaf(sKp[t * KP + x], -acc[i][j], part);
+            for (int xb = 0; xb < XW; ++xb) {
+                const int x0 = 16 * (XW * w + xb);
+                const f32x4 acc = mma_lds<C, 1, LC, LK, 1>(z4, sT, sWn, 16 * R, x0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * R + 4 * gq + e, x = x0 + r16;
+                    Zg[t * K + x] = -acc[e];
+                    part[R][e] = fmaf(sKp[t * LK + x], -acc[e], part[R][e]);
+                }
             }
-            part += __shfl_xor(part, 1, 16);
-            part += __shfl_xor(part, 2, 16);
-            part += __shfl_xor(part, 4, 16);
-            part += __shfl_xor(part, 8, 16);
-            if (tl.nt == 0) sdb[t] += part;
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p2 = sum16(part[R][e]);
+                if (r16 == 0) spart[w * C + 16 * R + 4 * gq + e] = p2;
+            }
+    }
+    {   // dT -= dWn (beta Kp)^T: this wave's row block
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            const f32x4 acc = mma_lds<K, LK, 1, 1, LK>(z4, sWn, sKp, 16 * w, 16 * J);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * w + 4 * gq + e, s2 = 16 * J + r16;
+                sdT[t * LC + s2] -= sb[s2] * acc[e];
+            }
         }
     }
-    {   // dT -= dWn (beta Kp)^T
-        using TL = Tile<C, C, 4, 4>;
-        const TL tl;
-        float acc[4][4] = {};
-        mm_acc<C, C, 4, 4, K, KP, 1, 1, KP>(acc, sWn, sKp, tl.mt, tl.nt);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = tl.row(i), s = tl.col(j);
-                sdT[t * CP + s] -= sb[s] * acc[i][j];
-            }
-    }
     lds_barrier();
-    {   // M1 = T^T dT
-        using TL = Tile<C, C, 4, 4>;
-        const TL tl;
-        float acc[4][4] = {};
-        mm_acc<C, C, 4, 4, C, 1, CP, CP, 1>(acc, sT, sdT, tl.mt, tl.nt);
+    if (tid < C) sdb[tid] += (spart[tid] + spart[C + tid]) + (spart[2 * C + tid] + spart[3 * C + tid]);
+    // M1 = T^T dT
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int J = 0; J < 4; ++J) {
+        const f32x4 acc = mma_lds<C, 1, LC, LC, 1>(z4, sT, sdT, 16 * w, 16 * J);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sM[tl.row(i) * CP + tl.col(j)] = acc[i][j];
+        for (int e = 0; e < 4; ++e) sM[(16 * w + 4 * gq + e) * LC + 16 * J + r16] = acc[e];
     }
     lds_barrier();
     {   // dA = -M1 T^T (strictly lower); dG = diag(beta) dA; dbeta += rowsum(dA * G)
-        using TL = Tile<C, C, 4, 4>;
-        const TL tl;
-        float acc[4][4] = {};
-        // G is read before dG is stored (as far as the compiler knows they may alias)
-        const float *Gm = a.ws.Gm + ci * (C * C);
-        float gv[4][4];
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int J = 0; J < 4; ++J) {
+            const f32x4 acc = mma_lds<C, LC, 1, 1, LC>(z4, sM, sT, 16 * w, 16 * J);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) gv[i][j] = Gm[tl.row(i) * C + tl.col(j)];
-        mm_acc<C, C, 4, 4, C, CP, 1, 1, CP>(acc, sM, sT, tl.mt, tl.nt);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = tl.row(i);
-            float part = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int s = tl.col(j);
-                const float da = s < t ? -acc[i][j] : 0.f;
-                part = fmaf(da, gv[i][j], part);
-                dGg[t * C + s] = sb[t] * da;
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * w + 4 * gq + e, s2 = 16 * J + r16;
+                const float da = s2 < t ? -acc[e] : 0.f;
+                part[e] = fmaf(da, gv[J][e], part[e]);
+                dGg[t * C + s2] = sb[t] * da;
             }
-            part += __shfl_xor(part, 1, 16);
-            part += __shfl_xor(part, 2, 16);
-            part += __shfl_xor(part, 4, 16);
-            part += __shfl_xor(part, 8, 16);
-            if (tl.nt == 0) sdb[t] += part;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {   // this wave's rows: one writer each
+            const float p2 = sum16(part[e]);
+            if (r16 == 0) sdb[16 * w + 4 * gq + e] += p2;
         }
     }
     lds_barrier();
@@ -1292,7 +1331,7 @@ template <int K, int V> struct BwLds {
     static constexpr int states = 4 * (VB * LK + 2 * VB * LC + C * VP + C);
     static constexpr int dstates = 4 * (VB * LK + VB * L2 + VB * LC + C);
     static constexpr int vgrad = 4 * (2 * K * 20 + 4 * C * 20 + C * LC + C);
-    static constexpr int kgrad1 = 4 * (2 * C + 2 * C * KP + 3 * C * CP);
+    static constexpr int kgrad1 = 4 * (2 * C + 2 * C * LK + 3 * C * LC + 4 * C);
     static constexpr int kgrad2 = 4 * (3 * K * LC + 2 * C * LC + 2 * C + (BW_NTHR / K) * K + K);
     static_assert(prep <= 160 * 1024 && states <= 160 * 1024 && dstates <= 160 * 1024 &&
                   vgrad <= 160 * 1024 && kgrad1 <= 160 * 1024 && kgrad2 <= 160 * 1024,

@@ -48,6 +48,30 @@ template <> __device__ __forceinline__ void ld8<__bf16>(const __bf16 *p, float (
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
 }
+// 8 consecutive elements of a row kept in their storage type until used.
+template <typename DT> struct Raw8;
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = *reinterpret_cast<const f32x4 *>(p);
+        b = *reinterpret_cast<const f32x4 *>(p + 4);
+    }
+    __device__ __forceinline__ void get(float (&x)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = a[e];
+            x[4 + e] = b[e];
+        }
+    }
+};
+template <> struct Raw8<__bf16> {
+    bf16x8 a;
+    __device__ __forceinline__ void load(const __bf16 *p) { a = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p)); }
+    __device__ __forceinline__ void get(float (&x)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+    }
+};
 template <typename DT> __device__ __forceinline__ void st8(DT *p, const float (&x)[8]);
 template <> __device__ __forceinline__ void st8<float>(float *p, const float (&x)[8])
 {
@@ -59,10 +83,10 @@ template <> __device__ __forceinline__ void st8<__bf16>(__bf16 *p, const float (
     bf16x8 a;
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = (__bf16)x[e];
-    *reinterpret_cast<bf16x8 *>(p) = a;
+    __builtin_nontemporal_store(a, reinterpret_cast<bf16x8 *>(p));
 }
 
-// Segments (blockIdx.y): 0 q, 1 k, 2 v, 3 gates.  A thread owns 8 channels of
+// Segments: q, k, v and the gates (blockIdx.y 1, 2, 3 and 0).  A thread owns 8 channels of
 // one head and walks PR_TT consecutive tokens with the taps in registers and a
 // sliding window of the last four raw rows, so each token costs one 16-byte
 // load.  The K/8 threads of one head are consecutive lanes on the same tokens
@@ -77,7 +101,7 @@ __device__ __forceinline__ void conv_run(const DT *x, const DT *cs, const float 
     f32x4 wt[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) wt[e] = *reinterpret_cast<const f32x4 *>(w + (long)(c + e) * 4);
-    float win[4][8];
+    float win[3][8];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         const int tt = t0 - 3 + j;
@@ -90,10 +114,7 @@ __device__ __forceinline__ void conv_run(const DT *x, const DT *cs, const float 
             for (int e = 0; e < 8; ++e) win[j][e] = 0.f;
         }
     }
-    const int tend = min(t0 + PR_TT, T);   // the same for every lane of a head
-#pragma unroll 4
-    for (int t = t0; t < tend; ++t) {
-        ld8(x + (b * T + t) * (long)D + c, win[3]);
+    auto token = [&](int t, const float (&xt)[8]) {
         float o[8];
         float ss = 0.f;
 #pragma unroll
@@ -101,7 +122,7 @@ __device__ __forceinline__ void conv_run(const DT *x, const DT *cs, const float 
             float v = wt[e][0] * win[0][e];
             v = fmaf(wt[e][1], win[1][e], v);
             v = fmaf(wt[e][2], win[2][e], v);
-            v = fmaf(wt[e][3], win[3][e], v);
+            v = fmaf(wt[e][3], xt[e], v);
             o[e] = SILU ? pr_silu(v) : v;
             ss = fmaf(o[e], o[e], ss);
         }
@@ -117,7 +138,26 @@ __device__ __forceinline__ void conv_run(const DT *x, const DT *cs, const float 
         for (int e = 0; e < 8; ++e) {
             win[0][e] = win[1][e];
             win[1][e] = win[2][e];
-            win[2][e] = win[3][e];
+            win[2][e] = xt[e];
+        }
+    };
+    if (t0 + PR_TT <= T) {
+        // a whole block of tokens (the same for every lane of a head): all of
+        // its loads in flight before the first token is computed
+        Raw8<DT> xs[PR_TT];
+#pragma unroll
+        for (int i = 0; i < PR_TT; ++i) xs[i].load(x + (b * T + t0 + i) * (long)D + c);
+#pragma unroll
+        for (int i = 0; i < PR_TT; ++i) {
+            float xt[8];
+            xs[i].get(xt);
+            token(t0 + i, xt);
+        }
+    } else {
+        for (int t = t0; t < T; ++t) {
+            float xt[8];
+            ld8(x + (b * T + t) * (long)D + c, xt);
+            token(t, xt);
         }
     }
 }
@@ -126,7 +166,9 @@ template <typename DT, int K, int V, bool CH, bool SILU>
 __global__ __launch_bounds__(PR_NTHR) void prologue_kernel(PrArgs a)
 {
     const long idx = (long)blockIdx.x * PR_NTHR + threadIdx.x;
-    const int seg = blockIdx.y;
+    // the small gates segment first in dispatch order, so that it runs beside
+    // the convolutions instead of after them
+    const int seg = blockIdx.y == 0 ? 3 : blockIdx.y - 1;
     const int NTB = (a.T + PR_TT - 1) / PR_TT;
     const long rows = (long)a.B * NTB * a.H;      // (b, token block, h)
     if (seg <= 2) {
@@ -156,19 +198,33 @@ __global__ __launch_bounds__(PR_NTHR) void prologue_kernel(PrArgs a)
         const int tb = (int)(btb % NTB);
         const long b = btb / NTB;
         const int x0 = (int)(idx % G) * 4;
-        const int t0 = tb * PR_TT, tend = min(t0 + PR_TT, a.T);
-        for (int t = t0; t < tend; ++t) {
-            const long row = (b * a.T + t) * a.H + h;
-            if (CH) {
-                const f32x4 gr = *reinterpret_cast<const f32x4 *>(a.g_raw + row * K + x0);
-                f32x4 gv;
+        const int t0 = tb * PR_TT, nt = min(PR_TT, a.T - t0);
+        const long row0 = (b * a.T + t0) * a.H + h;   // token t0 + i: row0 + i H
+        // every load of the block in flight before the first is used (rows past
+        // the end re-read the last one and are not stored)
+        f32x4 gr[PR_TT];
+        float br[PR_TT];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) gv[e] = pr_gate(gr[e], a.cap);
-                *reinterpret_cast<f32x4 *>(a.g + row * K + x0) = gv;
-                if (x0 == 0) a.beta[row] = pr_sigmoid(a.b_raw[row]);
-            } else {
-                a.g[row] = pr_gate(a.g_raw[row], a.cap);
-                a.beta[row] = pr_sigmoid(a.b_raw[row]);
+        for (int i = 0; i < PR_TT; ++i) {
+            const long row = row0 + (long)min(i, nt - 1) * a.H;
+            if (CH) gr[i] = *reinterpret_cast<const f32x4 *>(a.g_raw + row * K + x0);
+            else gr[i][0] = a.g_raw[row];
+            br[i] = (!CH || x0 == 0) ? a.b_raw[row] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < PR_TT; ++i) {
+            if (i < nt) {
+                const long row = row0 + (long)i * a.H;
+                if (CH) {
+                    f32x4 gv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gv[e] = pr_gate(gr[i][e], a.cap);
+                    *reinterpret_cast<f32x4 *>(a.g + row * K + x0) = gv;
+                    if (x0 == 0) a.beta[row] = pr_sigmoid(br[i]);
+                } else {
+                    a.g[row] = pr_gate(gr[i][0], a.cap);
+                    a.beta[row] = pr_sigmoid(br[i]);
+                }
             }
         }
     }
