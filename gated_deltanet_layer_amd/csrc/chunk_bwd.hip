@@ -222,6 +222,31 @@ __device__ __forceinline__ void store_frag(OT *dst, const float *src, int ls)
     });
 }
 
+// 8 consecutive elements of a row kept in their storage type until used.
+template <typename DT> struct Raw8;
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = *reinterpret_cast<const f32x4 *>(p);
+        b = *reinterpret_cast<const f32x4 *>(p + 4);
+    }
+    __device__ __forceinline__ void get(float (&x)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = a[e];
+            x[4 + e] = b[e];
+        }
+    }
+};
+template <> struct Raw8<__bf16> {
+    bf16x8 a;
+    __device__ __forceinline__ void load(const __bf16 *p) { a = *reinterpret_cast<const bf16x8 *>(p); }
+    __device__ __forceinline__ void get(float (&x)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+    }
+};
+
 // Store an R x W fp32 LDS tile (row stride ls) to global rows gs floats apart,
 // four columns per 16-byte store.
 template <int R, int W>
@@ -1133,33 +1158,47 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
         sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
         sgs[tid] = gam[tid * K];
     }
-    // row-scaled k and q, transposed, four channels of one token per thread
-    // (consecutive threads take consecutive tokens: conflict-free LDS writes)
-    for (int v = tid; v < C * K / 4; v += BW_NTHR) {
-        const int t = v % C, x = (v / C) * 4;
-        f32x4 kv = {0.f, 0.f, 0.f, 0.f}, qv = {0.f, 0.f, 0.f, 0.f};
-        if (t < n) {
+    // row-scaled k and q, transposed: eight channels of one token per thread,
+    // consecutive threads on consecutive channels (whole rows per load
+    // instruction), every load of the tile issued before the first is used
+    {
+        constexpr int NV = C * K / 8, PER = NV / BW_NTHR;
+        static_assert(NV % BW_NTHR == 0, "tile map");
+        Raw8<DT> kr[PER], qr[PER];
+        f32x4 g0[PER], g1[PER], gr0[PER], gr1[PER];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kv[e] = to_f32(k[t * H * K + x + e]);
-                qv[e] = to_f32(q[t * H * K + x + e]);
+        for (int i = 0; i < PER; ++i) {
+            const int v = tid + i * BW_NTHR, t = v / (K / 8), x = (v % (K / 8)) * 8;
+            const int tr = min(t, n - 1);   // rows past the end: loaded, then zeroed
+            kr[i].load(k + tr * H * K + x);
+            qr[i].load(q + tr * H * K + x);
+            if (CH) {
+                g0[i] = *reinterpret_cast<const f32x4 *>(gam + t * K + x);
+                g1[i] = *reinterpret_cast<const f32x4 *>(gam + t * K + x + 4);
+                gr0[i] = *reinterpret_cast<const f32x4 *>(gam + (16 * (t / 16) + 8) * K + x);
+                gr1[i] = *reinterpret_cast<const f32x4 *>(gam + (16 * (t / 16) + 8) * K + x + 4);
             }
         }
-        f32x4 up = {1.f, 1.f, 1.f, 1.f}, dn = {1.f, 1.f, 1.f, 1.f};
-        if (CH) {
-            const f32x4 g = *reinterpret_cast<const f32x4 *>(gam + t * K + x);
-            const f32x4 gr = *reinterpret_cast<const f32x4 *>(gam + (16 * (t / 16) + 8) * K + x);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                up[e] = __expf(gr[e] - g[e]);
-                dn[e] = __expf(g[e] - gr[e]);
+        for (int i = 0; i < PER; ++i) {
+            const int v = tid + i * BW_NTHR, t = v / (K / 8), x = (v % (K / 8)) * 8;
+            float kv[8], qv[8];
+            kr[i].get(kv);
+            qr[i].get(qv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kk = t < n ? kv[e] : 0.f, qq = t < n ? qv[e] : 0.f;
+                float up = 1.f, dn = 1.f;
+                if (CH) {
+                    const float g = e < 4 ? g0[i][e] : g1[i][e - 4];
+                    const float gr = e < 4 ? gr0[i][e] : gr1[i][e - 4];
+                    up = __expf(gr - g);
+                    dn = __expf(g - gr);
+                }
+                sKt[(x + e) * L + t] = kk * up;
+                sKh[(x + e) * L + t] = kk * dn;
+                sQh[(x + e) * L + t] = qq * dn;
             }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sKt[(x + e) * L + t] = kv[e] * up[e];
-            sKh[(x + e) * L + t] = kv[e] * dn[e];
-            sQh[(x + e) * L + t] = qv[e] * dn[e];
         }
     }
     lds_barrier();
