@@ -37,27 +37,27 @@ CSRC = os.path.join(ROOT, "gated_deltanet_layer_amd", "csrc")
 MEASURED_TRAFFIC = {
     "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
                                   "mfma_frag.h"),
-                                 "4bfeabc03baca055", 862345934),
+                                 "4bfeabc03baca055", 862345451),
     # the B=16 H=8 T=2048 channel-gate case (o and S_T written)
     "chunk_fwd_wsc_kernel<128>": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                    "mfma_frag.h"),
-                                  "aea3bbff97305fd5", 420119881),
+                                  "aea3bbff97305fd5", 420197770),
     # the B=1 H=48 T=262144 channel-gate case (S_T only, from a random S0)
     "chunk_fwd_wsc_kernel<128>/long": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                         "mfma_frag.h"),
-                                       "aea3bbff97305fd5", 16641126925),
+                                       "aea3bbff97305fd5", 16646596775),
     "recurrent_step_kernel<bf16,128,128,channel>": (("recurrent_step.hip", "gdn_common.h"),
-                                                    "1864f0aa1a777d85", 1642880935),
+                                                    "1864f0aa1a777d85", 1642879983),
     # M = 4 draft tokens on the decode shape: final state only / every token's state
     "recurrent_multi_kernel<bf16,128,128,channel>/final": (("recurrent_multi.hip", "gdn_common.h"),
-                                                           "e96c18f898c72e85", 1739629851),
+                                                           "e96c18f898c72e85", 1739625626),
     "recurrent_multi_kernel<bf16,128,128,channel>/hist": (("recurrent_multi.hip", "gdn_common.h"),
-                                                          "e96c18f898c72e85", 4159188123),
+                                                          "e96c18f898c72e85", 4158918874),
     # the chunk-mode prologue at B8 H12 T8192 (scalar gate) and the fused decode token
     "prologue_kernel<bf16,128,128,scalar,silu>": (("prologue.hip", "prologue.h", "gdn_common.h"),
-                                                  "0ed5faf9f34cfc2f", 1335877252),
+                                                  "b156e582ccb66343", 1307921585),
     "recurrent_step_prologue_kernel<bf16,128,128,channel,silu>": (("prologue.hip", "prologue.h",
-                                                                  "gdn_common.h"), "0ed5faf9f34cfc2f", 1719380966),
+                                                                  "gdn_common.h"), "b156e582ccb66343", 1719319814),
 }
 
 
@@ -502,7 +502,9 @@ def main():
             out["ms_per_step"] = out["backward"]["ms_fwd_bwd"]
             out["config"] = {"workload": out["backward"]["workload"]}
     if args.only in ("all", "prologue"):
-        out["prologue"] = bench_prologue(torch, gdn, max(3, min(args.steps, 50)), max(1, min(args.warmup, 5)))
+        # the chunk-mode launch settles only after a few dozen launches on fresh
+        # buffers: warm up as long as the headline forward does
+        out["prologue"] = bench_prologue(torch, gdn, max(3, min(args.steps, 50)), max(1, min(args.warmup, 50)))
         if ch is None and args.only == "prologue":
             out["value"] = out["prologue"]["chunk"]["gbs"]
             out["unit"] = "GB/s"
