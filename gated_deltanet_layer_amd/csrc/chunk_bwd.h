@@ -12,9 +12,10 @@ constexpr int BW_VB = 16;
 
 // Intermediates, each an array over the B*H*ceil(T/64) chunks (chunk
 // ci = (b H + h) NC + c).  fp32, rows of a chunk contiguous, except where
-// marked F: fragment order (the matrix-core operand layout of the sweeps), and
-// S: the sweeps' operands, fragment order in the input dtype (bf16 inputs use
-// half of the fp32-sized slot; the last three arrays are used by bf16 only):
+// marked F: fragment order (the matrix-core operand layout of the sweeps); A:
+// accumulator-tile order (the layout of a matrix-core result); and S: the
+// sweeps' operands, fragment order in the input dtype (bf16 inputs use half of
+// the fp32-sized slot; the last three arrays are used by bf16 only):
 struct BwWs {
     float *gam;   // [64][K]  in-chunk cumulative log-decay
     float *Tm;    // [64][64] (I + diag(beta) G)^{-1}                          F
@@ -25,11 +26,11 @@ struct BwWs {
     float *dhS;   // [K][V]   dL/d(state leaving the chunk)
     float *Dl;    // [64][V]  Delta
     float *dDl;   // [64][V]  dL/dDelta
-    float *dQp;   // [64][K]  dL/dQp (then d gamma)
-    float *dKm;   // [64][K]  dL/dKm
-    float *dWn;   // [64][K]  dDelta S^T (then Z = -T^T of it)
-    float *dP;    // [64][64] dO Delta^T
-    float *dT;    // [64][64] dDelta (beta V)^T
+    float *dQp;   // [64][K]  dL/dQp (then d gamma)                           A
+    float *dKm;   // [64][K]  dL/dKm                                            A
+    float *dWn;   // [64][K]  dDelta S^T (then Z = -T^T of it)                A
+    float *dP;    // [64][64] dO Delta^T                                        A
+    float *dT;    // [64][64] dDelta (beta V)^T (then dG)                       A
     float *dgn;   // [K]      e^{gn} rowsum(S * dS')
     float *dbv;   // [64]     rowsum(V * T^T dDelta)
     float *Kp;    // [64][K]  k e^{gamma}                                       F

@@ -222,6 +222,46 @@ __device__ __forceinline__ void store_frag(OT *dst, const float *src, int ls)
     });
 }
 
+// Accumulator-tile order of an R x L fp32 array (R and L multiples of 16): 1 KB
+// tiles of 16 x 16, row-block major; lane 16 g + r of a tile holds rows
+// 4 g .. 4 g + 3 of column r, the matrix-core accumulator's own layout.  A wave
+// stores an accumulator, or loads the same tile back, as one contiguous 1 KB
+// access (instead of 64-byte pieces of 16 rows).
+template <int L> __device__ __forceinline__ int acc_idx(int row, int col)
+{
+    return (((row >> 4) * (L / 16) + (col >> 4)) * 64 + ((row & 15) >> 2) * 16 + (col & 15)) * 4 +
+           (row & 3);
+}
+// Offset of lane `lane`'s float4 in tile (row block rb, column block cb).
+template <int L> __device__ __forceinline__ int acc_tile(int rb, int cb, int lane)
+{
+    return ((rb * (L / 16) + cb) * 64 + lane) * 4;
+}
+
+// Registers holding an R x L array in accumulator-tile order (contiguous
+// 16-byte loads, all issued before any is used), stored to LDS row-major (row
+// stride ls); LOWER keeps the entries with column <= row and zeroes the rest.
+template <int R, int L> struct AccRegs {
+    static constexpr int NV = R * L / 4, PER = NV / BW_NTHR;
+    static_assert(NV % BW_NTHR == 0, "accumulator tile");
+    f32x4 r[PER];
+    __device__ __forceinline__ void load(const float *src) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            r[i] = *reinterpret_cast<const f32x4 *>(src + 4 * (threadIdx.x + i * BW_NTHR));
+    }
+    template <bool LOWER = false> __device__ __forceinline__ void store(float *dst, int ls) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * BW_NTHR, tile = v >> 6, l = v & 63;
+            const int row0 = 16 * (tile / (L / 16)) + 4 * (l >> 4), col = 16 * (tile % (L / 16)) + (l & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dst[(row0 + e) * ls + col] = (!LOWER || col <= row0 + e) ? r[i][e] : 0.f;
+        }
+    }
+};
+
 // 8 consecutive elements of a row kept in their storage type until used.
 template <typename DT> struct Raw8;
 template <> struct Raw8<float> {
@@ -929,22 +969,20 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
 
     float *dQp = a.ws.dQp + ci * (C * K), *dKm = a.ws.dKm + ci * (C * K), *dWn = a.ws.dWn + ci * (C * K);
     float *dP = a.ws.dP + ci * (C * C), *dT = a.ws.dT + ci * (C * C);
+    // accumulator-tile order: each accumulator leaves as one 16-byte store per lane
 #pragma unroll
-    for (int R = 0; R < 4; ++R)
+    for (int R = 0; R < 4; ++R) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * R + 4 * gq + e;
-#pragma unroll
-            for (int xi = 0; xi < XB; ++xi) {
-                const int x = 16 * (XB * w + xi) + r16;
-                dQp[t * K + x] = aQ[xi][R][e];
-                dKm[t * K + x] = aKm[xi][R][e];
-                dWn[t * K + x] = aWn[xi][R][e];
-            }
-            const int s = 16 * w + r16;
-            dP[t * C + s] = aP[R][e];
-            dT[t * C + s] = aT[R][e] * sb[s];
+        for (int xi = 0; xi < XB; ++xi) {
+            const int o = acc_tile<K>(R, XB * w + xi, lane);
+            *reinterpret_cast<f32x4 *>(dQp + o) = aQ[xi][R];
+            *reinterpret_cast<f32x4 *>(dKm + o) = aKm[xi][R];
+            *reinterpret_cast<f32x4 *>(dWn + o) = aWn[xi][R];
         }
+        const int o = acc_tile<C>(R, w, lane);
+        *reinterpret_cast<f32x4 *>(dP + o) = aP[R];
+        *reinterpret_cast<f32x4 *>(dT + o) = aT[R] * sb[16 * w + r16];
+    }
     // rows 16 w + 4 gq + e: the 16 lanes with the same gq hold the 16 columns
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1022,14 +1060,14 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
     const float *Gm = a.ws.Gm + ci * (C * C);
     float gv[4][4];   // G at rows 16 w + 4 gq + e, columns 16 J + r16 (read before dG is stored)
     {
-        TileRegs<float, C, K> tW;
+        AccRegs<C, K> tW;
         FragRegs<C, K> tK;
         FragRegs<C, C> tT;
-        TileRegs<float, C, C> tdT;
-        tW.load(Zg, K, C);
+        AccRegs<C, C> tdT;
+        tW.load(Zg);
         tK.load(a.ws.Kp + ci * (C * K));
         tT.load(a.ws.Tm + ci * (C * C));
-        tdT.load(dGg, C, C);
+        tdT.load(dGg);
 #pragma unroll
         for (int J = 0; J < 4; ++J)
 #pragma unroll
@@ -1056,10 +1094,10 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
             for (int xb = 0; xb < XW; ++xb) {
                 const int x0 = 16 * (XW * w + xb);
                 const f32x4 acc = mma_lds<C, 1, LC, LK, 1>(z4, sT, sWn, 16 * R, x0);
+                *reinterpret_cast<f32x4 *>(Zg + acc_tile<K>(R, XW * w + xb, lane)) = -acc;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * R + 4 * gq + e, x = x0 + r16;
-                    Zg[t * K + x] = -acc[e];
                     part[R][e] = fmaf(sKp[t * LK + x], -acc[e], part[R][e]);
                 }
             }
@@ -1097,13 +1135,15 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             const f32x4 acc = mma_lds<C, LC, 1, 1, LC>(z4, sM, sT, 16 * w, 16 * J);
+            f32x4 dg4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * w + 4 * gq + e, s2 = 16 * J + r16;
                 const float da = s2 < t ? -acc[e] : 0.f;
                 part[e] = fmaf(da, gv[J][e], part[e]);
-                dGg[t * C + s2] = sb[t] * da;
+                dg4[e] = sb[t] * da;
             }
+            *reinterpret_cast<f32x4 *>(dGg + acc_tile<C>(w, J, lane)) = dg4;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {   // this wave's rows: one writer each
@@ -1148,9 +1188,9 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
     const DT *q = (const DT *)a.q + r0 * K, *k = (const DT *)a.k + r0 * K;
     const float *gam = a.ws.gam + ci * (C * K);
     {
-        TileRegs<float, C, C> tP, tG;
-        tP.load(a.ws.dP + ci * (C * C), C, C);
-        tG.load(a.ws.dT + ci * (C * C), C, C);
+        AccRegs<C, C> tP, tG;
+        tP.load(a.ws.dP + ci * (C * C));
+        tG.load(a.ws.dT + ci * (C * C));
         tP.store<true>(sdP, L);
         tG.store(sdG, L);
     }
@@ -1289,21 +1329,25 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
         float dgn = 0.f;
 #pragma unroll
         for (int R0 = 0; R0 < 4; R0 += 2) {
-            float lg[2][4], lk[2][4], lq[2][4], lqp[2][4], lkm[2][4], lz[2][4];
+            float lg[2][4], lk[2][4], lq[2][4];
+            f32x4 lqp[2], lkm[2], lz[2];   // accumulator-tile order: one 16-byte load each
 #pragma unroll
-            for (int R = 0; R < 2; ++R)
+            for (int R = 0; R < 2; ++R) {
+                const int o = acc_tile<K>(R0 + R, XB * w + xi, lane);
+                lqp[R] = *reinterpret_cast<const f32x4 *>(dQp + o);
+                lkm[R] = *reinterpret_cast<const f32x4 *>(dKm + o);
+                lz[R] = *reinterpret_cast<const f32x4 *>(Zg + o);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int rr = 16 * (R0 + R) + 4 * gq + e;
                     lg[R][e] = gam[rr * K + x];
                     lk[R][e] = rr < n ? to_f32(k[rr * H * K + x]) : 0.f;
                     lq[R][e] = rr < n ? to_f32(q[rr * H * K + x]) : 0.f;
-                    lqp[R][e] = dQp[rr * K + x];
-                    lkm[R][e] = dKm[rr * K + x];
-                    lz[R][e] = Zg[rr * K + x];
                 }
+            }
 #pragma unroll
-            for (int R = 0; R < 2; ++R)
+            for (int R = 0; R < 2; ++R) {
+                f32x4 dgam;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int rr = 16 * (R0 + R) + 4 * gq + e;
@@ -1311,13 +1355,15 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
                     const float eg = __expf(lg[R][e]), em = __expf(gn - lg[R][e]);
                     const float dqp = lqp[R][e], dkm = lkm[R][e], z = lz[R][e] * sb[rr];
                     const float aq = accq[R0 + R][e], ak = acck[R0 + R][e], as = accs[R0 + R][e];
-                    dQp[rr * K + x] = qr * aq + kr * (ak - as) + (dqp * qr + z * kr) * eg - dkm * kr * em;
+                    dgam[e] = qr * aq + kr * (ak - as) + (dqp * qr + z * kr) * eg - dkm * kr * em;
                     dgn = fmaf(dkm * kr, em, dgn);
                     if (rr < n) {
                         dq[rr * H * K + x] = from_f32<DT>(fmaf(dqp, eg, aq));
                         dk[rr * H * K + x] = from_f32<DT>(ak + as + z * eg + dkm * em);
                     }
                 }
+                *reinterpret_cast<f32x4 *>(dQp + acc_tile<K>(R0 + R, XB * w + xi, lane)) = dgam;
+            }
         }
         dgn += __shfl_xor(dgn, 16);
         dgn += __shfl_xor(dgn, 32);
@@ -1332,7 +1378,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
         float tot = 0.f;
 #pragma unroll
         for (int i = 0; i < RP; ++i) {
-            dgm[i] = dQp[(rb + i) * K + x];
+            dgm[i] = dQp[acc_idx<K>(rb + i, x)];
             tot += dgm[i];
         }
         stot[sp * K + x] = tot;
