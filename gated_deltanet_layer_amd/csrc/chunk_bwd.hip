@@ -1038,18 +1038,56 @@ __device__ __forceinline__ float sum16(float x)
     return x;
 }
 
+// Column blocks [cb0, cb0 + LW/16) of an R x L array in accumulator-tile order
+// (A) or fragment order (F): contiguous 16-byte loads, all issued before any is
+// used, stored to LDS row-major with the block's first column at column 0.
+template <int R, int LW, int L, bool FRAG> struct ColRegs {
+    static constexpr int NV = R * LW / 4, PER = NV / BW_NTHR, NB = LW / 16;
+    static_assert(NV % BW_NTHR == 0, "column block");
+    f32x4 r[PER];
+    __device__ __forceinline__ void load(const float *src, int cb0) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * BW_NTHR, tile = v >> 6;
+            const int gt = (tile / NB) * (L / 16) + cb0 + tile % NB;   // the tile in the whole array
+            r[i] = *reinterpret_cast<const f32x4 *>(src + 4 * (gt * 64 + (v & 63)));
+        }
+    }
+    __device__ __forceinline__ void store(float *dst, int ls) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * BW_NTHR, tile = v >> 6, l = v & 63;
+            const int rb = tile / NB, cb = tile % NB;
+            if (FRAG) {   // lane 16 g + r: row r, columns 4 g .. 4 g + 3
+                const int row = 16 * rb + (l & 15), col = 16 * cb + 4 * (l >> 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[row * ls + col + e] = r[i][e];
+            } else {      // lane 16 g + r: rows 4 g .. 4 g + 3, column r
+                const int row = 16 * rb + 4 * (l >> 4), col = 16 * cb + (l & 15);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(row + e) * ls + col] = r[i][e];
+            }
+        }
+    }
+};
+
 // The C x C part of the chain: Z = -T^T dWn (replaces dWn in the workspace),
 // dT -= dWn (beta Kp)^T, dA = -T^T dT T^T, dG = diag(beta) dA (replaces dT),
 // and the final dbeta = rowsum(V * Y) + rowsum(Kp * Z) + rowsum(dA * G).  All
-// four products on the fp32 matrix cores; LDS rows padded to K + 4 and C + 4
-// floats, which keeps every operand read of a wave on distinct banks.
+// four products on the fp32 matrix cores; LDS rows padded to 64 + 4 floats,
+// which keeps every operand read of a wave on distinct banks.  dWn and Kp pass
+// through LDS 64 key channels at a time (the sum over channels of the dT update
+// stays in registers), and M1 reuses their space afterwards: 71 KB of LDS, two
+// workgroups per CU, so one's loads overlap the other's products.
 template <typename DT, int K>
-__global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
+__global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kgrad1_kernel(BwArgs a)
 {
-    constexpr int C = BW_C, LK = K + 4, LC = C + 4, NXB = K / 16;
+    constexpr int C = BW_C, KH = 64, NH = K / KH, LH = KH + 4, LC = C + 4;
     extern __shared__ __attribute__((aligned(256))) float sm[];
-    float *sb = sm, *sdb = sb + C, *sWn = sdb + C, *sKp = sWn + C * LK, *sT = sKp + C * LK;
-    float *sdT = sT + C * LC, *sM = sdT + C * LC, *spart = sM + C * LC;   // spart [4][C]
+    float *sb = sm, *sdb = sb + C, *spart = sdb + C;            // spart [4][C]
+    float *sWn = spart + 4 * C, *sKp = sWn + C * LH;             // this half's channels
+    float *sM = sWn;                                             // after the halves
+    float *sT = sKp + C * LH, *sdT = sT + C * LC;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
     const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
     const int t0 = c * C, n = min(C, a.T - t0);
@@ -1059,13 +1097,16 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
     float *dGg = a.ws.dT + ci * (C * C);    // dT is replaced by dG likewise
     const float *Gm = a.ws.Gm + ci * (C * C);
     float gv[4][4];   // G at rows 16 w + 4 gq + e, columns 16 J + r16 (read before dG is stored)
+    ColRegs<C, KH, K, false> tW[NH];
+    ColRegs<C, KH, K, true> tK[NH];
     {
-        AccRegs<C, K> tW;
-        FragRegs<C, K> tK;
         FragRegs<C, C> tT;
         AccRegs<C, C> tdT;
-        tW.load(Zg);
-        tK.load(a.ws.Kp + ci * (C * K));
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+            tW[hh].load(Zg, hh * (KH / 16));
+            tK[hh].load(a.ws.Kp + ci * (C * K), hh * (KH / 16));
+        }
         tT.load(a.ws.Tm + ci * (C * C));
         tdT.load(dGg);
 #pragma unroll
@@ -1076,53 +1117,50 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
             sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
             sdb[tid] = a.ws.dbv[ci * C + tid];
         }
-        tW.store(sWn, LK);
-        tK.store(sKp, LK);
         tT.store(sT, LC);
         tdT.store(sdT, LC);
     }
-    lds_barrier();
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    {   // Z = -T^T dWn (all rows, this wave's column blocks); rowsum(Kp * Z) per
-        // wave, added to dbeta in a fixed order below (results do not depend on
-        // the waves' timing)
-        constexpr int XW = NXB / 4;   // column blocks per wave
-        float part[4][4] = {};
+    f32x4 adT[4] = {z4, z4, z4, z4};   // dWn (Kp)^T, rows 16 w .., column block J, over all channels
+    float part[4][4] = {};             // rowsum(Kp * Z) of this wave's columns
 #pragma unroll
-        for (int R = 0; R < 4; ++R)
+    for (int hh = 0; hh < NH; ++hh) {
+        if (hh > 0) lds_barrier();     // the previous half's readers are done
+        tW[hh].store(sWn, LH);
+        tK[hh].store(sKp, LH);
+        lds_barrier();
+        // Z = -T^T dWn: all rows, column block w of this half
 #pragma unroll
-            for (int xb = 0; xb < XW; ++xb) {
-                const int x0 = 16 * (XW * w + xb);
-                const f32x4 acc = mma_lds<C, 1, LC, LK, 1>(z4, sT, sWn, 16 * R, x0);
-                *reinterpret_cast<f32x4 *>(Zg + acc_tile<K>(R, XW * w + xb, lane)) = -acc;
+        for (int R = 0; R < 4; ++R) {
+            const f32x4 acc = mma_lds<C, 1, LC, LH, 1>(z4, sT, sWn, 16 * R, 16 * w);
+            *reinterpret_cast<f32x4 *>(Zg + acc_tile<K>(R, hh * (KH / 16) + w, lane)) = -acc;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * R + 4 * gq + e, x = x0 + r16;
-                    part[R][e] = fmaf(sKp[t * LK + x], -acc[e], part[R][e]);
-                }
-            }
-#pragma unroll
-        for (int R = 0; R < 4; ++R)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p2 = sum16(part[R][e]);
-                if (r16 == 0) spart[w * C + 16 * R + 4 * gq + e] = p2;
-            }
-    }
-    {   // dT -= dWn (beta Kp)^T: this wave's row block
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            const f32x4 acc = mma_lds<K, LK, 1, 1, LK>(z4, sWn, sKp, 16 * w, 16 * J);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * w + 4 * gq + e, s2 = 16 * J + r16;
-                sdT[t * LC + s2] -= sb[s2] * acc[e];
-            }
+            for (int e = 0; e < 4; ++e)
+                part[R][e] = fmaf(sKp[(16 * R + 4 * gq + e) * LH + 16 * w + r16], -acc[e], part[R][e]);
         }
+        // dWn (Kp)^T over this half's channels: this wave's row block
+#pragma unroll
+        for (int J = 0; J < 4; ++J) adT[J] = mma_lds<KH, LH, 1, 1, LH>(adT[J], sWn, sKp, 16 * w, 16 * J);
     }
+    // dT -= dWn (beta Kp)^T (one writer per element); the per-wave row sums
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * w + 4 * gq + e, s2 = 16 * J + r16;
+            sdT[t * LC + s2] -= sb[s2] * adT[J][e];
+        }
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p2 = sum16(part[R][e]);
+            if (r16 == 0) spart[w * C + 16 * R + 4 * gq + e] = p2;
+        }
     lds_barrier();
+    // dbeta in a fixed order (results do not depend on the waves' timing)
     if (tid < C) sdb[tid] += (spart[tid] + spart[C + tid]) + (spart[2 * C + tid] + spart[3 * C + tid]);
-    // M1 = T^T dT
+    // M1 = T^T dT (into the space of the halves)
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
         const f32x4 acc = mma_lds<C, 1, LC, LC, 1>(z4, sT, sdT, 16 * w, 16 * J);
@@ -1131,7 +1169,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
     }
     lds_barrier();
     {   // dA = -M1 T^T (strictly lower); dG = diag(beta) dA; dbeta += rowsum(dA * G)
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        float pa[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             const f32x4 acc = mma_lds<C, LC, 1, 1, LC>(z4, sM, sT, 16 * w, 16 * J);
@@ -1140,14 +1178,14 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad1_kernel(BwArgs a)
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * w + 4 * gq + e, s2 = 16 * J + r16;
                 const float da = s2 < t ? -acc[e] : 0.f;
-                part[e] = fmaf(da, gv[J][e], part[e]);
+                pa[e] = fmaf(da, gv[J][e], pa[e]);
                 dg4[e] = sb[t] * da;
             }
             *reinterpret_cast<f32x4 *>(dGg + acc_tile<C>(w, J, lane)) = dg4;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {   // this wave's rows: one writer each
-            const float p2 = sum16(part[e]);
+            const float p2 = sum16(pa[e]);
             if (r16 == 0) sdb[16 * w + 4 * gq + e] += p2;
         }
     }
@@ -1416,7 +1454,7 @@ template <int K, int V> struct BwLds {
     static constexpr int states = 4 * (VB * LK + 2 * VB * LC + C * VP + C);
     static constexpr int dstates = 4 * (VB * LK + VB * L2 + VB * LC + C);
     static constexpr int vgrad = 4 * (2 * K * 20 + 4 * C * 20 + C * LC + C);
-    static constexpr int kgrad1 = 4 * (2 * C + 2 * C * LK + 3 * C * LC + 4 * C);
+    static constexpr int kgrad1 = 4 * (6 * C + 2 * C * (64 + 4) + 2 * C * LC);
     static constexpr int kgrad2 = 4 * (3 * K * LC + 2 * C * LC + 2 * C + (BW_NTHR / K) * K + K);
     static_assert(prep <= 160 * 1024 && states <= 160 * 1024 && dstates <= 160 * 1024 &&
                   vgrad <= 160 * 1024 && kgrad1 <= 160 * 1024 && kgrad2 <= 160 * 1024,
