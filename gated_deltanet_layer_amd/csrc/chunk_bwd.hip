@@ -91,9 +91,8 @@ template <int M, int N, int TM, int TN> struct Tile {
 // dealt to the 8 XCDs in turn (workgroup i to XCD i mod 8); when the slice count
 // allows, the value blocks of one slice stay on one XCD, so the per-chunk
 // operands that all of them read come from one L2 rather than eight.
-__device__ __forceinline__ void sweep_block(int nslices, int nvb, int &sl, int &vb)
+__device__ __forceinline__ void sweep_block(int b, int nslices, int nvb, int &sl, int &vb)
 {
-    const int b = blockIdx.x;
     if (nslices % 8 == 0) {
         const int j = b >> 3;
         sl = (b & 7) + 8 * (j / nvb);
@@ -627,7 +626,7 @@ template <typename DT, int K, int C, int KT, int VB> struct StSet {
 };
 
 template <typename DT, int K, int V>
-__global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
+__device__ __forceinline__ void states_sweep(const BwArgs &a, int blk)
 {
     constexpr int C = BW_C, VB = 16, NVB = V / VB, KT = K / 64, LK = K + 4, LC = C + 4, VP = VB + 1;
     extern __shared__ __attribute__((aligned(256))) float sm[];
@@ -638,7 +637,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_states_kernel(BwArgs a)
     float *sb = sV + C * VP;         // [C]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r = lane & 15;
     int sl, vb;
-    sweep_block(a.NS, NVB, sl, vb);
+    sweep_block(blk, a.NS, NVB, sl, vb);
     const int v0 = vb * VB;
     const long H = a.H;
     using Set = StSet<DT, K, C, KT, VB>;
@@ -741,7 +740,7 @@ template <typename DT, int K, int C, int KT, int VB> struct DsSet {
 };
 
 template <typename DT, int K, int V>
-__global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
+__device__ __forceinline__ void dstates_sweep(const BwArgs &a, int blk)
 {
     constexpr int C = BW_C, VB = 16, NVB = V / VB, KT = K / 64;
     constexpr int LK = K + 4, LC = C + 4, L2 = 2 * C + 4;
@@ -752,7 +751,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
     float *sb = sdDt + VB * LC;      // [C]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r = lane & 15;
     int sl, vb;
-    sweep_block(a.NS, NVB, sl, vb);
+    sweep_block(blk, a.NS, NVB, sl, vb);
     const int v0 = vb * VB;
     const long H = a.H;
     using Set = DsSet<DT, K, C, KT, VB>;
@@ -852,6 +851,33 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_dstates_kernel(BwArgs a)
             for (int e = 0; e < 4; ++e) a.dS0[((long)sl * K + x0 + e) * V + v0 + r] = dS[h][e];
         }
     }
+}
+
+// The two sweeps in one launch: the backward one reads only prep's operands,
+// dO and dL/dS_T, not the forward one's results, so they run side by side
+// (workgroups [0, nvb) walk forward, [nvb, 2 nvb) backward).  With both at two
+// waves per SIMD, each CU can hold one of each, and the chip's 256 CUs are no
+// longer a quarter idle as with either sweep alone.  nvb is a multiple of 8
+// whenever the XCD mapping applies, so the backward half keeps it.  fp32
+// operands need more registers than two waves per SIMD allow: that variant
+// keeps one.
+template <typename DT, int K, int V> __device__ __forceinline__ void sweeps(const BwArgs &a)
+{
+    const int nvb = a.NS * (V / BW_VB);
+    if ((int)blockIdx.x < nvb)
+        states_sweep<DT, K, V>(a, blockIdx.x);
+    else
+        dstates_sweep<DT, K, V>(a, blockIdx.x - nvb);
+}
+template <typename DT, int K, int V>
+__global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) void bwd_sweeps_kernel(BwArgs a)
+{
+    sweeps<DT, K, V>(a);
+}
+template <typename DT, int K, int V>
+__global__ __launch_bounds__(BW_NTHR) void bwd_sweeps_f32_kernel(BwArgs a)
+{
+    sweeps<DT, K, V>(a);
 }
 
 // ---------------------------------------------------------------- 4 vgrad
@@ -1474,20 +1500,26 @@ template <typename DT, int K, int V, bool CH>
 static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
 {
     using L = BwLds<K, V>;
-    static bool s1 = false, s2 = false, s3 = false, s4 = false, s5 = false, s6 = false;
+    static bool s1 = false, s2 = false, s4 = false, s5 = false, s6 = false;
+    constexpr int lds_sweeps = L::states > L::dstates ? L::states : L::dstates;
     hipError_t e;
     if ((e = set_lds(bwd_prep_kernel<DT, K, CH>, L::prep, s1)) != hipSuccess) return e;
-    if ((e = set_lds(bwd_states_kernel<DT, K, V>, L::states, s2)) != hipSuccess) return e;
-    if ((e = set_lds(bwd_dstates_kernel<DT, K, V>, L::dstates, s3)) != hipSuccess) return e;
+    constexpr bool F32 = std::is_same<DT, float>::value;
+    void (*sweeps_kern)(BwArgs);
+    if constexpr (F32)
+        sweeps_kern = bwd_sweeps_f32_kernel<DT, K, V>;
+    else
+        sweeps_kern = bwd_sweeps_kernel<DT, K, V>;
+    if ((e = set_lds(sweeps_kern, lds_sweeps, s2)) != hipSuccess) return e;
     if ((e = set_lds(bwd_vgrad_kernel<DT, K, V>, L::vgrad, s4)) != hipSuccess) return e;
     if ((e = set_lds(bwd_kgrad1_kernel<DT, K>, L::kgrad1, s5)) != hipSuccess) return e;
     if ((e = set_lds(bwd_kgrad2_kernel<DT, K, CH>, L::kgrad2, s6)) != hipSuccess) return e;
     const unsigned nch = (unsigned)(nslices * a.NC), nvb = (unsigned)(nslices * (V / L::VB));
-    if (nch > 0) {
+    if (nch > 0)
         hipLaunchKernelGGL((bwd_prep_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::prep, st, a);
-        hipLaunchKernelGGL((bwd_states_kernel<DT, K, V>), dim3(nvb), dim3(BW_NTHR), L::states, st, a);
-    }
-    hipLaunchKernelGGL((bwd_dstates_kernel<DT, K, V>), dim3(nvb), dim3(BW_NTHR), L::dstates, st, a);
+    // with no chunks the forward sweep returns at once and the backward one
+    // passes dL/dS_T to dS0
+    hipLaunchKernelGGL(sweeps_kern, dim3(2 * nvb), dim3(BW_NTHR), lds_sweeps, st, a);
     if (nch > 0) {
         hipLaunchKernelGGL((bwd_vgrad_kernel<DT, K, V>), dim3(nch), dim3(BW_NTHR), L::vgrad, st, a);
         hipLaunchKernelGGL((bwd_kgrad1_kernel<DT, K>), dim3(nch), dim3(BW_NTHR), L::kgrad1, st, a);
