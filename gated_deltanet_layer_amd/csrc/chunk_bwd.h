@@ -32,7 +32,6 @@ struct BwWs {
     float *dP;    // [64][64] dO Delta^T                                        A
     float *dT;    // [64][64] dDelta (beta V)^T (then dG)                       A
     float *dgn;   // [K]      e^{gn} rowsum(S * dS')
-    float *dbv;   // [64]     rowsum(V * T^T dDelta)
     float *Kp;    // [64][K]  k e^{gamma}                                       F
     float *Km;    // [64][K]  k e^{gn - gamma}                                  S
     float *KpT;   // [K][64]  Kp^T                                              S
@@ -60,16 +59,16 @@ inline unsigned long long bw_workspace(unsigned long long nchunks, int K, int V,
                                        BwWs *ws)
 {
     const unsigned long long C = 64, Ku = (unsigned)K, Vu = (unsigned)V;
-    constexpr int NA = 25;
+    constexpr int NA = 24;
     const unsigned long long per[NA] = {C * Ku, C * C, C * C, C * C, C * C, Ku * Vu, Ku * Vu,
                                         C * Vu, C * Vu, C * Ku, C * Ku, C * Ku, C * C, C * C,
-                                        Ku, C, C * Ku, C * Ku, C * Ku, C * Ku, C * Ku, Ku,
+                                        Ku, C * Ku, C * Ku, C * Ku, C * Ku, C * Ku, Ku,
                                         C * Ku / 2, C * C / 2, C * C / 2};
     float **dst[NA] = {nullptr};
     if (ws) {
         float **p[NA] = {&ws->gam, &ws->Tm, &ws->TT, &ws->Gm, &ws->PT, &ws->hS, &ws->dhS,
                          &ws->Dl, &ws->dDl, &ws->dQp, &ws->dKm, &ws->dWn, &ws->dP, &ws->dT,
-                         &ws->dgn, &ws->dbv, &ws->Kp, &ws->Km, &ws->KpT, &ws->KmT, &ws->QpT,
+                         &ws->dgn, &ws->Kp, &ws->Km, &ws->KpT, &ws->KmT, &ws->QpT,
                          &ws->egn, &ws->Kps, &ws->Tms, &ws->TTs};
         for (int i = 0; i < NA; ++i) dst[i] = p[i];
     }

@@ -25,26 +25,24 @@
 // its last row); a scalar gate sums dg over the key channels.
 //
 // Kernels, in stream order (each launch covers every slice):
-//   1 prep     one workgroup per chunk:   gamma, G, P (matrix cores), T
-//   2 states   one per value block:       walks the chunks forward; the state
-//                                         entering each chunk and Delta
-//   3 dstates  one per value block:       walks them backward; dL/dS' of each
-//                                         chunk, dDelta, and dS0
-//   4 vgrad    one per chunk:             every product that sums over the
-//                                         value dimension; dv
-//   5 kgrad1   one per chunk:             the C x C part of the chain; dbeta
-//   6 kgrad2   one per chunk:             the sums over token pairs (matrix
-//                                         cores); dq, dk, dg
+//   1 prep     one workgroup per chunk:   gamma, G, P and T (matrix cores), the
+//                                         sweeps' operands in fragment order
+//   2 sweeps   one per value block and    forward: the state entering each
+//              direction, in one launch:  chunk and Delta; backward: dL/dS' of
+//                                         each chunk, dDelta, and dS0
+//   3 vgrad    one per chunk:             every product that sums over the
+//                                         value dimension (dv), then the C x C
+//                                         part of the chain (dbeta)
+//   4 kgrad2   one per chunk:             the sums over token pairs; dq, dk, dg
 // The state recursions split by value column (column j of S and of dS depends
-// only on column j), which is what lets 2 and 3 run one workgroup per block of
-// value columns.  Intermediates live in a caller-provided fp32 workspace.
+// only on column j), which is what lets the sweeps run one workgroup per block
+// of value columns, and the backward sweep needs none of the forward sweep's
+// results.  Intermediates live in a caller-provided workspace.
 //
-// The two sweeps run their products on the fp32 matrix cores (16 x 16 x 4),
-// with the per-chunk operands streamed from the workspace into registers one
-// chunk ahead.  The per-chunk kernels use LDS-tiled fp32 FMAs: each thread owns
-// a small output tile whose rows and columns are interleaved across the
-// workgroup, so that the operand reads of a wave hit consecutive or odd-strided
-// LDS addresses.  Every load of a tile is issued before the first is used.
+// Every product runs on the matrix cores: fp32 16 x 16 x 4, and in the sweeps
+// bf16 16 x 16 x 32 when the inputs are bf16.  The sweeps stream their
+// per-chunk operands from the workspace into registers one chunk ahead.  Every
+// load of a tile is issued before the first is used.
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -54,38 +52,6 @@ namespace gdn {
 
 constexpr int BW_C = 64;
 constexpr int BW_NTHR = 256;
-
-// acc[i][j] += sum_{x < KD} A[(mt + i*MS) AM + x AK] * B[x BK + (nt + j*NS) BN]
-// with MS = M / TM and NS = N / TN: the thread's tile is rows mt + i*MS and
-// columns nt + j*NS of an M x N output.
-template <int M, int N, int TM, int TN, int KD, int AM, int AK, int BK, int BN>
-__device__ __forceinline__ void mm_acc(float (&acc)[TM][TN], const float *A, const float *B,
-                                       int mt, int nt)
-{
-    constexpr int MS = M / TM, NS = N / TN;
-#pragma unroll 4
-    for (int x = 0; x < KD; ++x) {
-        float a[TM], b[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = A[(mt + i * MS) * AM + x * AK];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = B[x * BK + (nt + j * NS) * BN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-}
-
-// One tile per thread: (M/TM) x (N/TN) == 256.
-template <int M, int N, int TM, int TN> struct Tile {
-    static_assert(M % TM == 0 && N % TN == 0 && (M / TM) * (N / TN) == BW_NTHR, "tile map");
-    static constexpr int MS = M / TM, NS = N / TN;
-    int mt, nt;
-    __device__ __forceinline__ Tile() : mt(threadIdx.x / NS), nt(threadIdx.x % NS) {}
-    __device__ __forceinline__ int row(int i) const { return mt + i * MS; }
-    __device__ __forceinline__ int col(int j) const { return nt + j * NS; }
-};
 
 // (slice, block of 16 value columns) of a sweep workgroup.  Workgroups are
 // dealt to the 8 XCDs in turn (workgroup i to XCD i mod 8); when the slice count
@@ -285,18 +251,6 @@ template <> struct Raw8<__bf16> {
         for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
     }
 };
-
-// Store an R x W fp32 LDS tile (row stride ls) to global rows gs floats apart,
-// four columns per 16-byte store.
-template <int R, int W>
-__device__ __forceinline__ void store_tile(float *dst, long gs, const float *src, int ls)
-{
-    for (int v = threadIdx.x; v < R * W / 4; v += BW_NTHR) {
-        const int row = v / (W / 4), col = (v % (W / 4)) * 4;
-        const float *s = src + row * ls + col;
-        *reinterpret_cast<f32x4 *>(dst + row * gs + col) = f32x4{s[0], s[1], s[2], s[3]};
-    }
-}
 
 // ---------------------------------------------------------------- 1 prep
 template <typename DT, int K, bool CH>
@@ -880,18 +834,104 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_sweeps_f32_kernel(BwArgs a)
     sweeps<DT, K, V>(a);
 }
 
-// ---------------------------------------------------------------- 4 vgrad
-// Every product that sums over the value dimension, on the fp32 matrix cores,
-// 16 value columns at a time: dQp += dO S^T, dKm += Delta dS'^T, dWn += dDelta
-// S^T (C x K), dP += dO Delta^T, dT += dDelta V^T (C x C), and Y = T^T dDelta
-// for dv = beta Y and dbeta += rowsum(V * Y).  Each wave owns fixed output
-// tiles (16 x 16) whose accumulators persist across the value blocks; both
-// operands of every step are float4 LDS reads along the 16 value columns.
-// Held to two waves per SIMD so that one group's loads overlap the other's
-// products (the K = 128 accumulators alone take 128 registers).
+// ---------------------------------------------------------------- helpers of the C x C chain
+// One 16 x 16 output tile on the fp32 matrix cores from LDS operands:
+// acc(row0 + 4 gq + e, col0 + r) += sum_{k < KD} A(row, k) B(k, col), with
+// A(row, k) = A[row AR + k AK] and B(k, col) = B[k BK + col BC].  The k-step j
+// of each 16-wide k block takes k = 4 gq + j in lane group gq; where the k
+// stride is 1 the lane's four k values are one 16-byte read.
+template <int KD, int AR, int AK, int BK, int BC>
+__device__ __forceinline__ f32x4 mma_lds(f32x4 acc, const float *A, const float *B, int row0, int col0)
+{
+    const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
+    const float *a = A + (row0 + r) * AR + 4 * gq * AK, *b = B + 4 * gq * BK + (col0 + r) * BC;
+#pragma unroll
+    for (int k0 = 0; k0 < KD; k0 += 16) {
+        f32x4 av, bv;
+        if constexpr (AK == 1) {
+            av = *reinterpret_cast<const f32x4 *>(a + k0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) av[j] = a[(k0 + j) * AK];
+        }
+        if constexpr (BK == 1) {
+            bv = *reinterpret_cast<const f32x4 *>(b + k0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = b[(k0 + j) * BK];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma_f32(av[j], bv[j], acc);
+    }
+    return acc;
+}
+
+// Sum a per-lane value over the 16 lanes of a lane group (one row of a tile).
+__device__ __forceinline__ float sum16(float x)
+{
+    x += __shfl_xor(x, 1, 16);
+    x += __shfl_xor(x, 2, 16);
+    x += __shfl_xor(x, 4, 16);
+    x += __shfl_xor(x, 8, 16);
+    return x;
+}
+
+// Column blocks [cb0, cb0 + LW/16) of an R x L array in accumulator-tile order
+// (A) or fragment order (F): contiguous 16-byte loads, all issued before any is
+// used, stored to LDS row-major with the block's first column at column 0.
+template <int R, int LW, int L, bool FRAG> struct ColRegs {
+    static constexpr int NV = R * LW / 4, PER = NV / BW_NTHR, NB = LW / 16;
+    static_assert(NV % BW_NTHR == 0, "column block");
+    f32x4 r[PER];
+    __device__ __forceinline__ void load(const float *src, int cb0) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * BW_NTHR, tile = v >> 6;
+            const int gt = (tile / NB) * (L / 16) + cb0 + tile % NB;   // the tile in the whole array
+            r[i] = *reinterpret_cast<const f32x4 *>(src + 4 * (gt * 64 + (v & 63)));
+        }
+    }
+    __device__ __forceinline__ void store(float *dst, int ls) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * BW_NTHR, tile = v >> 6, l = v & 63;
+            const int rb = tile / NB, cb = tile % NB;
+            if (FRAG) {   // lane 16 g + r: row r, columns 4 g .. 4 g + 3
+                const int row = 16 * rb + (l & 15), col = 16 * cb + 4 * (l >> 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[row * ls + col + e] = r[i][e];
+            } else {      // lane 16 g + r: rows 4 g .. 4 g + 3, column r
+                const int row = 16 * rb + 4 * (l >> 4), col = 16 * cb + (l & 15);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(row + e) * ls + col] = r[i][e];
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------- 4 vgrad (+ kgrad1)
+// Part 1: every product that sums over the value dimension, on the fp32 matrix
+// cores, 16 value columns at a time: dQp += dO S^T, dKm += Delta dS'^T,
+// dWn += dDelta S^T (C x K), dP += dO Delta^T, dT += dDelta V^T (C x C), and
+// Y = T^T dDelta for dv = beta Y and dbeta += rowsum(V * Y).  Each wave owns
+// fixed output tiles (16 x 16) whose accumulators persist across the value
+// blocks; both operands of every step are float4 LDS reads along the 16 value
+// columns.
+// Part 2, the C x C part of the chain, on the same chunk in the same workgroup
+// (dWn, dT and the first part of dbeta go from the accumulators straight into
+// its LDS layout): Z = -T^T dWn (into the dWn slot of the workspace),
+// dT -= dWn (beta Kp)^T, dA = -T^T dT T^T, dG = diag(beta) dA (into the dT
+// slot), and dbeta = rowsum(V * Y) + rowsum(Kp * Z) + rowsum(dA * G).  Its four
+// products are on the fp32 matrix cores too, with LDS rows padded to 64 + 4
+// floats (every operand read of a wave on distinct banks); dWn and Kp pass
+// through LDS 64 key channels at a time (the channel sum of the dT update stays
+// in registers) and M1 reuses their space: 71 KB of LDS, held to two waves per
+// SIMD, so two workgroups share a CU and one's loads overlap the other's
+// products.
 template <typename DT, int K, int V>
 __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) void bwd_vgrad_kernel(BwArgs a)
 {
+    // ----- part 1: the products over the value dimension
     constexpr int C = BW_C, VB = 16, LV = VB + 4, LC = C + 4, XB = K / 64;
     extern __shared__ __attribute__((aligned(256))) float sm[];
     float *sS = sm, *sdS = sS + K * LV;                   // [K][LV]
@@ -993,8 +1033,8 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
             for (int yy = 0; yy < VB; ++yy) dgn = fmaf(sS[tid * LV + yy], sdS[tid * LV + yy], dgn);
     }
 
-    float *dQp = a.ws.dQp + ci * (C * K), *dKm = a.ws.dKm + ci * (C * K), *dWn = a.ws.dWn + ci * (C * K);
-    float *dP = a.ws.dP + ci * (C * C), *dT = a.ws.dT + ci * (C * C);
+    float *dQp = a.ws.dQp + ci * (C * K), *dKm = a.ws.dKm + ci * (C * K);
+    float *dP = a.ws.dP + ci * (C * C);
     // accumulator-tile order: each accumulator leaves as one 16-byte store per lane
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
@@ -1003,156 +1043,64 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
             const int o = acc_tile<K>(R, XB * w + xi, lane);
             *reinterpret_cast<f32x4 *>(dQp + o) = aQ[xi][R];
             *reinterpret_cast<f32x4 *>(dKm + o) = aKm[xi][R];
-            *reinterpret_cast<f32x4 *>(dWn + o) = aWn[xi][R];
         }
-        const int o = acc_tile<C>(R, w, lane);
-        *reinterpret_cast<f32x4 *>(dP + o) = aP[R];
-        *reinterpret_cast<f32x4 *>(dT + o) = aT[R] * sb[16 * w + r16];
+        *reinterpret_cast<f32x4 *>(dP + acc_tile<C>(R, w, lane)) = aP[R];
     }
     // rows 16 w + 4 gq + e: the 16 lanes with the same gq hold the 16 columns
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        float sum = dbv[e];
-        sum += __shfl_xor(sum, 1, 16);
-        sum += __shfl_xor(sum, 2, 16);
-        sum += __shfl_xor(sum, 4, 16);
-        sum += __shfl_xor(sum, 8, 16);
-        if (r16 == 0) a.ws.dbv[ci * C + 16 * w + 4 * gq + e] = sum;
-    }
+    for (int e = 0; e < 4; ++e) dbv[e] = sum16(dbv[e]);
     if (tid < K) a.ws.dgn[ci * K + tid] = a.ws.egn[ci * K + tid] * dgn;
-}
+    const float beta_s = sb[16 * w + r16];   // beta of this lane's dT column
+    lds_barrier();                          // part 1's LDS is free from here
 
-// ---------------------------------------------------------------- 5 kgrad1
-// One 16 x 16 output tile on the fp32 matrix cores from LDS operands:
-// acc(row0 + 4 gq + e, col0 + r) += sum_{k < KD} A(row, k) B(k, col), with
-// A(row, k) = A[row AR + k AK] and B(k, col) = B[k BK + col BC].  The k-step j
-// of each 16-wide k block takes k = 4 gq + j in lane group gq; where the k
-// stride is 1 the lane's four k values are one 16-byte read.
-template <int KD, int AR, int AK, int BK, int BC>
-__device__ __forceinline__ f32x4 mma_lds(f32x4 acc, const float *A, const float *B, int row0, int col0)
-{
-    const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
-    const float *a = A + (row0 + r) * AR + 4 * gq * AK, *b = B + 4 * gq * BK + (col0 + r) * BC;
-#pragma unroll
-    for (int k0 = 0; k0 < KD; k0 += 16) {
-        f32x4 av, bv;
-        if constexpr (AK == 1) {
-            av = *reinterpret_cast<const f32x4 *>(a + k0);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) av[j] = a[(k0 + j) * AK];
-        }
-        if constexpr (BK == 1) {
-            bv = *reinterpret_cast<const f32x4 *>(b + k0);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bv[j] = b[(k0 + j) * BK];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma_f32(av[j], bv[j], acc);
-    }
-    return acc;
-}
-
-// Sum a per-lane value over the 16 lanes of a lane group (one row of a tile).
-__device__ __forceinline__ float sum16(float x)
-{
-    x += __shfl_xor(x, 1, 16);
-    x += __shfl_xor(x, 2, 16);
-    x += __shfl_xor(x, 4, 16);
-    x += __shfl_xor(x, 8, 16);
-    return x;
-}
-
-// Column blocks [cb0, cb0 + LW/16) of an R x L array in accumulator-tile order
-// (A) or fragment order (F): contiguous 16-byte loads, all issued before any is
-// used, stored to LDS row-major with the block's first column at column 0.
-template <int R, int LW, int L, bool FRAG> struct ColRegs {
-    static constexpr int NV = R * LW / 4, PER = NV / BW_NTHR, NB = LW / 16;
-    static_assert(NV % BW_NTHR == 0, "column block");
-    f32x4 r[PER];
-    __device__ __forceinline__ void load(const float *src, int cb0) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int v = threadIdx.x + i * BW_NTHR, tile = v >> 6;
-            const int gt = (tile / NB) * (L / 16) + cb0 + tile % NB;   // the tile in the whole array
-            r[i] = *reinterpret_cast<const f32x4 *>(src + 4 * (gt * 64 + (v & 63)));
-        }
-    }
-    __device__ __forceinline__ void store(float *dst, int ls) const {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int v = threadIdx.x + i * BW_NTHR, tile = v >> 6, l = v & 63;
-            const int rb = tile / NB, cb = tile % NB;
-            if (FRAG) {   // lane 16 g + r: row r, columns 4 g .. 4 g + 3
-                const int row = 16 * rb + (l & 15), col = 16 * cb + 4 * (l >> 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dst[row * ls + col + e] = r[i][e];
-            } else {      // lane 16 g + r: rows 4 g .. 4 g + 3, column r
-                const int row = 16 * rb + 4 * (l >> 4), col = 16 * cb + (l & 15);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dst[(row + e) * ls + col] = r[i][e];
-            }
-        }
-    }
-};
-
-// The C x C part of the chain: Z = -T^T dWn (replaces dWn in the workspace),
-// dT -= dWn (beta Kp)^T, dA = -T^T dT T^T, dG = diag(beta) dA (replaces dT),
-// and the final dbeta = rowsum(V * Y) + rowsum(Kp * Z) + rowsum(dA * G).  All
-// four products on the fp32 matrix cores; LDS rows padded to 64 + 4 floats,
-// which keeps every operand read of a wave on distinct banks.  dWn and Kp pass
-// through LDS 64 key channels at a time (the sum over channels of the dT update
-// stays in registers), and M1 reuses their space afterwards: 71 KB of LDS, two
-// workgroups per CU, so one's loads overlap the other's products.
-template <typename DT, int K>
-__global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kgrad1_kernel(BwArgs a)
-{
-    constexpr int C = BW_C, KH = 64, NH = K / KH, LH = KH + 4, LC = C + 4;
-    extern __shared__ __attribute__((aligned(256))) float sm[];
-    float *sb = sm, *sdb = sb + C, *spart = sdb + C;            // spart [4][C]
+    // ----- part 2: the C x C chain
+    constexpr int KH = 64, NH = K / KH, LH = KH + 4;
+    float *sb2 = sm, *sdb = sb2 + C, *spart = sdb + C;          // spart [4][C]
     float *sWn = spart + 4 * C, *sKp = sWn + C * LH;             // this half's channels
     float *sM = sWn;                                             // after the halves
     float *sT = sKp + C * LH, *sdT = sT + C * LC;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
-    const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
-    const int t0 = c * C, n = min(C, a.T - t0);
-    const long ci = (long)sl * a.NC + c;
-    const long H = a.H, r0 = tok_row(a, sl, t0);
-    float *Zg = a.ws.dWn + ci * (C * K);    // dWn is replaced by Z once it is in LDS
-    float *dGg = a.ws.dT + ci * (C * C);    // dT is replaced by dG likewise
+    float *Zg = a.ws.dWn + ci * (C * K);    // Z goes where dWn would be
+    float *dGg = a.ws.dT + ci * (C * C);    // dG where dT would be
     const float *Gm = a.ws.Gm + ci * (C * C);
-    float gv[4][4];   // G at rows 16 w + 4 gq + e, columns 16 J + r16 (read before dG is stored)
-    ColRegs<C, KH, K, false> tW[NH];
+    float gv[4][4];   // G at rows 16 w + 4 gq + e, columns 16 J + r16
     ColRegs<C, KH, K, true> tK[NH];
     {
         FragRegs<C, C> tT;
-        AccRegs<C, C> tdT;
 #pragma unroll
-        for (int hh = 0; hh < NH; ++hh) {
-            tW[hh].load(Zg, hh * (KH / 16));
-            tK[hh].load(a.ws.Kp + ci * (C * K), hh * (KH / 16));
-        }
+        for (int hh = 0; hh < NH; ++hh) tK[hh].load(a.ws.Kp + ci * (C * K), hh * (KH / 16));
         tT.load(a.ws.Tm + ci * (C * C));
-        tdT.load(dGg);
 #pragma unroll
         for (int J = 0; J < 4; ++J)
 #pragma unroll
             for (int e = 0; e < 4; ++e) gv[J][e] = Gm[(16 * w + 4 * gq + e) * C + 16 * J + r16];
-        if (tid < C) {
-            sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
-            sdb[tid] = a.ws.dbv[ci * C + tid];
+        if (tid < C) sb2[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
+        if (r16 == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sdb[16 * w + 4 * gq + e] = dbv[e];
         }
         tT.store(sT, LC);
-        tdT.store(sdT, LC);
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sdT[(16 * R + 4 * gq + e) * LC + 16 * w + r16] = aT[R][e] * beta_s;
     }
-    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     f32x4 adT[4] = {z4, z4, z4, z4};   // dWn (Kp)^T, rows 16 w .., column block J, over all channels
     float part[4][4] = {};             // rowsum(Kp * Z) of this wave's columns
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
         if (hh > 0) lds_barrier();     // the previous half's readers are done
-        tW[hh].store(sWn, LH);
+        // this half's dWn from the waves whose column blocks lie in it
+#pragma unroll
+        for (int xi = 0; xi < XB; ++xi) {
+            const int xb = XB * w + xi;
+            if (xb / (KH / 16) == hh) {
+#pragma unroll
+                for (int R = 0; R < 4; ++R)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sWn[(16 * R + 4 * gq + e) * LH + 16 * (xb % (KH / 16)) + r16] = aWn[xi][R][e];
+            }
+        }
         tK[hh].store(sKp, LH);
         lds_barrier();
         // Z = -T^T dWn: all rows, column block w of this half
@@ -1174,7 +1122,7 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = 16 * w + 4 * gq + e, s2 = 16 * J + r16;
-            sdT[t * LC + s2] -= sb[s2] * adT[J][e];
+            sdT[t * LC + s2] -= sb2[s2] * adT[J][e];
         }
 #pragma unroll
     for (int R = 0; R < 4; ++R)
@@ -1205,7 +1153,7 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
                 const int t = 16 * w + 4 * gq + e, s2 = 16 * J + r16;
                 const float da = s2 < t ? -acc[e] : 0.f;
                 pa[e] = fmaf(da, gv[J][e], pa[e]);
-                dg4[e] = sb[t] * da;
+                dg4[e] = sb2[t] * da;
             }
             *reinterpret_cast<f32x4 *>(dGg + acc_tile<C>(w, J, lane)) = dg4;
         }
@@ -1479,11 +1427,12 @@ template <int K, int V> struct BwLds {
     static constexpr int prep = 4 * (3 * C * (K + 4) + 2 * C * CP + 2 * C);
     static constexpr int states = 4 * (VB * LK + 2 * VB * LC + C * VP + C);
     static constexpr int dstates = 4 * (VB * LK + VB * L2 + VB * LC + C);
-    static constexpr int vgrad = 4 * (2 * K * 20 + 4 * C * 20 + C * LC + C);
-    static constexpr int kgrad1 = 4 * (6 * C + 2 * C * (64 + 4) + 2 * C * LC);
+    static constexpr int vgrad1 = 4 * (2 * K * 20 + 4 * C * 20 + C * LC + C);   // part 1
+    static constexpr int vgrad2 = 4 * (6 * C + 2 * C * (64 + 4) + 2 * C * LC);  // part 2
+    static constexpr int vgrad = vgrad1 > vgrad2 ? vgrad1 : vgrad2;
     static constexpr int kgrad2 = 4 * (3 * K * LC + 2 * C * LC + 2 * C + (BW_NTHR / K) * K + K);
     static_assert(prep <= 160 * 1024 && states <= 160 * 1024 && dstates <= 160 * 1024 &&
-                  vgrad <= 160 * 1024 && kgrad1 <= 160 * 1024 && kgrad2 <= 160 * 1024,
+                  vgrad <= 160 * 1024 && kgrad2 <= 160 * 1024,
                   "LDS budget");
 };
 
@@ -1500,7 +1449,7 @@ template <typename DT, int K, int V, bool CH>
 static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
 {
     using L = BwLds<K, V>;
-    static bool s1 = false, s2 = false, s4 = false, s5 = false, s6 = false;
+    static bool s1 = false, s2 = false, s4 = false, s6 = false;
     constexpr int lds_sweeps = L::states > L::dstates ? L::states : L::dstates;
     hipError_t e;
     if ((e = set_lds(bwd_prep_kernel<DT, K, CH>, L::prep, s1)) != hipSuccess) return e;
@@ -1512,7 +1461,6 @@ static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
         sweeps_kern = bwd_sweeps_kernel<DT, K, V>;
     if ((e = set_lds(sweeps_kern, lds_sweeps, s2)) != hipSuccess) return e;
     if ((e = set_lds(bwd_vgrad_kernel<DT, K, V>, L::vgrad, s4)) != hipSuccess) return e;
-    if ((e = set_lds(bwd_kgrad1_kernel<DT, K>, L::kgrad1, s5)) != hipSuccess) return e;
     if ((e = set_lds(bwd_kgrad2_kernel<DT, K, CH>, L::kgrad2, s6)) != hipSuccess) return e;
     const unsigned nch = (unsigned)(nslices * a.NC), nvb = (unsigned)(nslices * (V / L::VB));
     if (nch > 0)
@@ -1522,7 +1470,6 @@ static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
     hipLaunchKernelGGL(sweeps_kern, dim3(2 * nvb), dim3(BW_NTHR), lds_sweeps, st, a);
     if (nch > 0) {
         hipLaunchKernelGGL((bwd_vgrad_kernel<DT, K, V>), dim3(nch), dim3(BW_NTHR), L::vgrad, st, a);
-        hipLaunchKernelGGL((bwd_kgrad1_kernel<DT, K>), dim3(nch), dim3(BW_NTHR), L::kgrad1, st, a);
         hipLaunchKernelGGL((bwd_kgrad2_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::kgrad2, st, a);
     }
     return hipGetLastError();

@@ -237,12 +237,12 @@ def test_bwd_workspace_size(L):
     assert _ws_size(L, 1, 64, 1, 128, 128, chunk=32)[0] == gdn.GDN_ENOTSUP
     assert _ws_size(L, -1, 64, 1, 128, 128)[0] == gdn.GDN_EINVAL
     assert _ws_size(L, 3, 0, 2, 128, 128) == (gdn.GDN_OK, 0)
-    # twenty-five arrays over the chunks (the last three half-size), each
+    # twenty-four arrays over the chunks (the last three half-size), each
     # rounded up to 256 bytes
     for B, T, H, K, V in [(1, 1, 1, 64, 64), (2, 100, 3, 128, 64), (4, 4096, 6, 128, 128)]:
         nch = B * H * ((T + 63) // 64)
         per = [64 * K] + [64 * 64] * 4 + [K * V] * 2 + [64 * V] * 2 + [64 * K] * 3 + \
-              [64 * 64] * 2 + [K, 64] + [64 * K] * 5 + [K] + [32 * K, 32 * 64, 32 * 64]
+              [64 * 64] * 2 + [K] + [64 * K] * 5 + [K] + [32 * K, 32 * 64, 32 * 64]
         want = sum((nch * x * 4 + 255) // 256 * 256 for x in per)
         assert _ws_size(L, B, T, H, K, V) == (gdn.GDN_OK, want)
         assert gdn.gdn_chunk_bwd_workspace_size(B, T, H, K, V) == want
