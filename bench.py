@@ -285,8 +285,8 @@ def bench_bwd(torch, gdn, steps, warmup):
             "ms": ms_bwd, "ms_fwd_bwd": ms_fb, "mtok_s_fwd_bwd": B * T / (ms_fb / 1e3) / 1e6,
             "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_call": nbytes,
             "workspace_bytes": nws, "steps": steps, "warmup": warmup,
-            "kernels": ["bwd_prep_kernel", "bwd_states_kernel", "bwd_dstates_kernel",
-                        "bwd_vgrad_kernel", "bwd_kgrad_kernel"]}
+            "kernels": ["bwd_prep_kernel", "bwd_sweeps_kernel", "bwd_vgrad_kernel",
+                        "bwd_kgrad2_kernel"]}
 
 
 def prologue_bytes(B, T, H, K, V, es, channel):
