@@ -121,10 +121,10 @@ __device__ __forceinline__ f32x4 gram_diag(f32x4 aA, f32x4 aP, const float *gam,
 // All fragments are read first; the diagonal block comes first because its
 // inverse is the longest dependent chain, and the off-diagonal products can
 // overlap it.  T_DD goes to sTd rows 16 D .. 16 D + 15.
-template <int PW, int NKB, int CPR, int LDC, int LDD>
+template <int PW, int NKB, int CPR, int LDC, int LDD, typename Mid>
 __device__ __forceinline__ void ws_gram_wave(const char *sK, const char *sQ, __bf16 *sAn, __bf16 *sP,
                                              __bf16 *sTd, const float *gam, const float *bet,
-                                             float x, float *sAd)
+                                             float x, float *sAd, Mid mid)
 {
     constexpr int D = PW == 0 ? 0 : PW == 1 ? 3 : PW == 2 ? 2 : 1;
     constexpr int I = PW == 0 ? 3 : D;
@@ -149,6 +149,8 @@ __device__ __forceinline__ void ws_gram_wave(const char *sK, const char *sQ, __b
     GDN_SCHED_FENCE();
     f32x4 aA, aP;
     gram_mma<NKB>(kD, kD, qD, aA, aP);
+    // work handed in by the caller (copies) goes out while the products run
+    mid();
     const f32x4 a = gram_diag<D, LDC>(aA, aP, gam, bet, sP);
     // -A_DD row-major; the same wave reads it back, in order, for the inverse
     *reinterpret_cast<f32x4 *>(sAd + lane_r16() * 16 + 4 * lane_gq()) = -a;
@@ -317,19 +319,21 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 if (lane == 0) reinterpret_cast<float *>(D + L::dEgN)[0] = __expf(gn);
             }
 
-            // q(n+1) goes in flight only now: issued together with v(n) and k(n+1)
-            // the copies would stall this wave until the memory pipeline drains
-            copy_qk(n + 1, 1);
+            // q(n+1) goes in flight only after the wave's first Gram products are
+            // issued: issued together with v(n) and k(n+1) the copies would stall
+            // this wave until the memory pipeline drains, and behind the products
+            // the stall overlaps the matrix cores' work
+            auto copy_q = [&] { copy_qk(n + 1, 1); };
             // Gram blocks and the diagonal inverse (static per-wave schedule)
             const char *sK = st, *sQ = st + L::TILE;
             if (pw == 0)
-                ws_gram_wave<0, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd);
+                ws_gram_wave<0, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd, copy_q);
             else if (pw == 1)
-                ws_gram_wave<1, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd);
+                ws_gram_wave<1, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd, copy_q);
             else if (pw == 2)
-                ws_gram_wave<2, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd);
+                ws_gram_wave<2, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd, copy_q);
             else
-                ws_gram_wave<3, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd);
+                ws_gram_wave<3, NKB, CPR, L::LDC, L::LDD>(sK, sQ, sAn, sP, sTd, gam, bet, x, sAd, copy_q);
             // v(n) and q/k(n+1) landed before the hand-over barrier
             wait_vm<0>();
         };
