@@ -37,7 +37,7 @@ CSRC = os.path.join(ROOT, "gated_deltanet_layer_amd", "csrc")
 MEASURED_TRAFFIC = {
     "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
                                   "mfma_frag.h"),
-                                 "4bfeabc03baca055", 862345451),
+                                 "f90ca00e7c53ad4c", 862394877),
     # the B=16 H=8 T=2048 channel-gate case (o and S_T written)
     "chunk_fwd_wsc_kernel<128>": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                    "mfma_frag.h"),
