@@ -520,14 +520,6 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 for (int e = 0; e < 4; ++e)
                     *reinterpret_cast<__bf16 *>(sV + v_st[e] + 2048 * rt) = (__bf16)O[rt][e];
             asm volatile("" ::: "memory");
-            const int t = c * WS_T + lane;
-            if (t < T) {
-                const f32x4 o0 = *reinterpret_cast<const f32x4 *>(sV + v_rd0);
-                const f32x4 o1 = *reinterpret_cast<const f32x4 *>(sV + v_rd1);
-                f32x4 *dst = reinterpret_cast<f32x4 *>(args.o + (row_base + (long)t * H) * V + v0 + 16 * wave);
-                dst[0] = o0;
-                dst[1] = o1;
-            }
         }
         GDN_SCHED_FENCE();
 
@@ -540,6 +532,18 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
                 S_acc[ct] = mma(S_acc[ct], Frag<__bf16>{cat8(kt[ct][2 * kb2], kt[ct][2 * kb2 + 1])}, Ef[kb2]);
+            if (ct == 0 && args.o) {
+                // o leaves behind the first products of the update (its stores'
+                // issue overlaps the matrix cores)
+                const int t = c * WS_T + lane;
+                if (t < T) {
+                    const f32x4 o0 = *reinterpret_cast<const f32x4 *>(sV + v_rd0);
+                    const f32x4 o1 = *reinterpret_cast<const f32x4 *>(sV + v_rd1);
+                    f32x4 *dst = reinterpret_cast<f32x4 *>(args.o + (row_base + (long)t * H) * V + v0 + 16 * wave);
+                    dst[0] = o0;
+                    dst[1] = o1;
+                }
+            }
             GDN_SCHED_FENCE();
         }
         lds_barrier();
