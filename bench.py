@@ -37,7 +37,7 @@ CSRC = os.path.join(ROOT, "gated_deltanet_layer_amd", "csrc")
 MEASURED_TRAFFIC = {
     "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
                                   "mfma_frag.h"),
-                                 "f90ca00e7c53ad4c", 862394877),
+                                 "34acdf37d6007014", 862390784),
     # the B=16 H=8 T=2048 channel-gate case (o and S_T written)
     "chunk_fwd_wsc_kernel<128>": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                    "mfma_frag.h"),
@@ -55,9 +55,9 @@ MEASURED_TRAFFIC = {
                                                           "e96c18f898c72e85", 4158918874),
     # the chunk-mode prologue at B8 H12 T8192 (scalar gate) and the fused decode token
     "prologue_kernel<bf16,128,128,scalar,silu>": (("prologue.hip", "prologue.h", "gdn_common.h"),
-                                                  "b156e582ccb66343", 1307921585),
+                                                  "85e864cbbee4c042", 1307213043),
     "recurrent_step_prologue_kernel<bf16,128,128,channel,silu>": (("prologue.hip", "prologue.h",
-                                                                  "gdn_common.h"), "b156e582ccb66343", 1719319814),
+                                                                  "gdn_common.h"), "85e864cbbee4c042", 1719316569),
 }
 
 
