@@ -362,12 +362,12 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
             const float *ga = sg + (16 * I + r16) * KP, *gr = sg + (16 * I + 8) * KP;
             const float *kb = sk + (16 * J + r16) * KP, *gb = sg + (16 * J + r16) * KP;
             f32x4 gacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-            for (int a0 = 0; a0 < K; a0 += 16) {
-                const int c = a0 + 4 * gq;
-                f32x4 kA = *reinterpret_cast<const f32x4 *>(ka + c);
-                f32x4 qA = *reinterpret_cast<const f32x4 *>(qa + c);
-                f32x4 kB = *reinterpret_cast<const f32x4 *>(kb + c);
+            // four channels c .. c + 3 of the A rows (k and q) and the B row (k),
+            // decay-scaled for the per-channel gate
+            auto operands = [&](int c, f32x4 &kA, f32x4 &qA, f32x4 &kB) {
+                kA = *reinterpret_cast<const f32x4 *>(ka + c);
+                qA = *reinterpret_cast<const f32x4 *>(qa + c);
+                kB = *reinterpret_cast<const f32x4 *>(kb + c);
                 if (CH) {
                     const f32x4 gA = *reinterpret_cast<const f32x4 *>(ga + c);
                     const f32x4 gR = *reinterpret_cast<const f32x4 *>(gr + c);
@@ -380,10 +380,30 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
                         kB[e] *= __expf(gR[e] - gB[e]);
                     }
                 }
+            };
+            if constexpr (std::is_same<DT, float>::value) {
+#pragma unroll 2
+                for (int a0 = 0; a0 < K; a0 += 16) {
+                    f32x4 kA, qA, kB;
+                    operands(a0 + 4 * gq, kA, qA, kB);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    gacc = mfma_f32(kA[e], kB[e], gacc);
-                    pacc = mfma_f32(qA[e], kB[e], pacc);
+                    for (int e = 0; e < 4; ++e) {
+                        gacc = mfma_f32(kA[e], kB[e], gacc);
+                        pacc = mfma_f32(qA[e], kB[e], pacc);
+                    }
+                }
+            } else {
+                // bf16 inputs: the scaled rows rounded to bf16, 32 channels per
+                // 16 x 16 x 32 product (k-slots 4 gq .. +3 and 16 + 4 gq .. +3 of
+                // each 32-channel block, the same for A and B)
+#pragma unroll
+                for (int a0 = 0; a0 < K; a0 += 32) {
+                    f32x4 kA0, qA0, kB0, kA1, qA1, kB1;
+                    operands(a0 + 4 * gq, kA0, qA0, kB0);
+                    operands(a0 + 16 + 4 * gq, kA1, qA1, kB1);
+                    const bf16x8 bk = cat8(cvt4(kB0), cvt4(kB1));
+                    gacc = mfma_bf16(cat8(cvt4(kA0), cvt4(kA1)), bk, gacc);
+                    pacc = mfma_bf16(cat8(cvt4(qA0), cvt4(qA1)), bk, pacc);
                 }
             }
             // this lane holds rows t = 16 I + 4 gq + e of column s = 16 J + r16,
