@@ -101,6 +101,8 @@ template <> __device__ __forceinline__ void st8<__bf16>(__bf16 *p, const float (
 // wave reads whole token rows.
 constexpr int PR_TT = 16;
 
+constexpr unsigned ilog2c(unsigned x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
 template <typename DT, int W, bool NORM, bool SILU>
 __device__ __forceinline__ void conv_run(const DT *x, const DT *cs, const float *w, DT *y, long b,
                                          int t0, int T, int D, int c)
@@ -172,21 +174,25 @@ __device__ __forceinline__ void conv_run(const DT *x, const DT *cs, const float 
 template <typename DT, int K, int V, bool CH, bool SILU>
 __global__ __launch_bounds__(PR_NTHR) void prologue_kernel(PrArgs a)
 {
-    const long idx = (long)blockIdx.x * PR_NTHR + threadIdx.x;
+    // The entry point keeps 16 work items per token below 2^32, so the index
+    // arithmetic is 32-bit (a 64-bit division by a run-time value costs a long
+    // instruction sequence per thread).
+    const unsigned idx = blockIdx.x * PR_NTHR + threadIdx.x;
     // the small gates segment first in dispatch order, so that it runs beside
     // the convolutions instead of after them
     const int seg = blockIdx.y == 0 ? 3 : blockIdx.y - 1;
-    const int NTB = (a.T + PR_TT - 1) / PR_TT;
-    const long rows = (long)a.B * NTB * a.H;      // (b, token block, h)
+    const unsigned NTB = (a.T + PR_TT - 1) / PR_TT, Hu = a.H;
+    const unsigned long long rows = (unsigned long long)a.B * NTB * Hu;   // (b, token block, h)
     if (seg <= 2) {
-        const int E = seg == 2 ? V : K, G = E / 8;   // lanes per (token block, head)
-        if (idx >= rows * G) return;                 // whole groups of G lanes
-        const long r = idx / G;
-        const int h = (int)(r % a.H);
-        const long btb = r / a.H;
+        const int E = seg == 2 ? V : K;
+        const unsigned lg = seg == 2 ? ilog2c(V / 8) : ilog2c(K / 8);   // lanes per (token block, head): 2^lg
+        if (idx >= (rows << lg)) return;                                // whole groups of lanes
+        const unsigned r = idx >> lg;
+        const int h = (int)(r % Hu);
+        const unsigned btb = r / Hu;
         const int tb = (int)(btb % NTB);
         const long b = btb / NTB;
-        const int D = a.H * E, c = h * E + (int)(idx % G) * 8;
+        const int D = a.H * E, c = h * E + (int)(idx & ((1u << lg) - 1)) * 8;
         if (seg == 0)
             conv_run<DT, K / 8, true, SILU>((const DT *)a.q_raw, (const DT *)a.cs_q, a.w_q,
                                             (DT *)a.q, b, tb * PR_TT, a.T, D, c);
@@ -197,11 +203,11 @@ __global__ __launch_bounds__(PR_NTHR) void prologue_kernel(PrArgs a)
             conv_run<DT, V / 8, false, SILU>((const DT *)a.v_raw, (const DT *)a.cs_v, a.w_v,
                                              (DT *)a.v, b, tb * PR_TT, a.T, D, c);
     } else {
-        constexpr int G = CH ? K / 4 : 1;
+        constexpr unsigned G = CH ? K / 4 : 1;
         if (idx >= rows * G) return;
-        const long r = idx / G;
-        const int h = (int)(r % a.H);
-        const long btb = r / a.H;
+        const unsigned r = idx / G;
+        const int h = (int)(r % Hu);
+        const unsigned btb = r / Hu;
         const int tb = (int)(btb % NTB);
         const long b = btb / NTB;
         const int x0 = (int)(idx % G) * 4;
