@@ -22,8 +22,8 @@ struct BwWs {
     float *TT;    // [64][64] its transpose                                     F
     float *Gm;    // [64][64] G, strictly lower
     float *PT;    // [64][64] P^T (P lower with the diagonal)                     S
-    float *hS;    // [K][V]   state entering the chunk
-    float *dhS;   // [K][V]   dL/d(state leaving the chunk)
+    float *hS;    // [K][V]   state entering the chunk                      (input dtype)
+    float *dhS;   // [K][V]   dL/d(state leaving the chunk)                 (input dtype)
     float *Dl;    // [64][V]  Delta
     float *dDl;   // [64][V]  dL/dDelta
     float *dQp;   // [64][K]  dL/dQp (then d gamma)                           A

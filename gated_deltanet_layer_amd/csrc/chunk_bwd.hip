@@ -572,14 +572,17 @@ template <int N> __device__ __forceinline__ void interleave_loads()
 }
 
 // Store a K x 16 block held transposed in LDS (St[y][x], row stride ls) to
-// global rows V floats apart (dst points at column v0 of row 0).
-template <int K, int V>
-__device__ __forceinline__ void store_state_block(float *dst, const float *St, int ls)
+// global rows V elements apart (dst points at column v0 of row 0), in the
+// input dtype: bf16 inputs keep the per-chunk states and their gradients as
+// bf16 (the gradient kernels read them as operands of their products, as the
+// forward kernel rounds its state for its own).
+template <int K, int V, typename ST>
+__device__ __forceinline__ void store_state_block(ST *dst, const float *St, int ls)
 {
     for (int v = threadIdx.x; v < K * 4; v += BW_NTHR) {
         const int x = v >> 2, y = (v & 3) * 4;
-        *reinterpret_cast<f32x4 *>(dst + (long)x * V + y) =
-            f32x4{St[y * ls + x], St[(y + 1) * ls + x], St[(y + 2) * ls + x], St[(y + 3) * ls + x]};
+        st4(dst + (long)x * V + y,
+            f32x4{St[y * ls + x], St[(y + 1) * ls + x], St[(y + 2) * ls + x], St[(y + 3) * ls + x]});
     }
 }
 
@@ -655,7 +658,7 @@ __device__ __forceinline__ void states_sweep(const BwArgs &a, int blk)
         lds_barrier();   // S^T complete; the previous chunk's readers are done
         f.v.store(sV, VP);
         if (tid < C) sb[tid] = f.b;
-        store_state_block<K, V>(a.ws.hS + ci * (K * V) + v0, sSt, LK);   // state entering c
+        store_state_block<K, V>(reinterpret_cast<DT *>(a.ws.hS) + ci * (K * V) + v0, sSt, LK);   // state entering c
         lds_barrier();
         // unconditional (the last chunk fetches itself again), so that the
         // compiler's waits see one straight path
@@ -778,7 +781,7 @@ __device__ __forceinline__ void dstates_sweep(const BwArgs &a, int blk)
             }
         }
         if (tid < C) sb[tid] = f.b;
-        store_state_block<K, V>(a.ws.dhS + ci * (K * V) + v0, sdSt, LK);   // dL/d(state leaving c)
+        store_state_block<K, V>(reinterpret_cast<DT *>(a.ws.dhS) + ci * (K * V) + v0, sdSt, LK);   // dL/d(state leaving c)
         lds_barrier();
         fetch(nf, max(c - 1, 0));   // unconditional: one straight path for the compiler's waits
         {   // dDelta = Km dS' + P^T dO
@@ -966,7 +969,8 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
     const long H = a.H, r0 = tok_row(a, sl, t0);
     const DT *v = (const DT *)a.v + r0 * V, *dO = (const DT *)a.d_o + r0 * V;
     DT *dv = (DT *)a.dv + r0 * V;
-    const float *hS = a.ws.hS + ci * (K * V), *dhS = a.ws.dhS + ci * (K * V);
+    const DT *hS = reinterpret_cast<const DT *>(a.ws.hS) + ci * (K * V);
+    const DT *dhS = reinterpret_cast<const DT *>(a.ws.dhS) + ci * (K * V);
     const float *Dl = a.ws.Dl + ci * (C * V), *dDl = a.ws.dDl + ci * (C * V);
     {
         FragRegs<C, C> tT;
@@ -988,7 +992,7 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int v0 = 0; v0 < V; v0 += VB) {
         lds_barrier();
         {
-            TileRegs<float, K, VB> ts, tds;
+            TileRegs<DT, K, VB> ts, tds;
             TileRegs<DT, C, VB> to, tvv;
             TileRegs<float, C, VB> tD, tdD;
             ts.load(hS + v0, V, K);
