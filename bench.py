@@ -55,9 +55,9 @@ MEASURED_TRAFFIC = {
                                                           "e96c18f898c72e85", 4158918874),
     # the chunk-mode prologue at B8 H12 T8192 (scalar gate) and the fused decode token
     "prologue_kernel<bf16,128,128,scalar,silu>": (("prologue.hip", "prologue.h", "gdn_common.h"),
-                                                  "85e864cbbee4c042", 1307213043),
+                                                  "1fb5d0b92490e05a", 1307185835),
     "recurrent_step_prologue_kernel<bf16,128,128,channel,silu>": (("prologue.hip", "prologue.h",
-                                                                  "gdn_common.h"), "85e864cbbee4c042", 1719316569),
+                                                                  "gdn_common.h"), "1fb5d0b92490e05a", 1719304713),
 }
 
 
