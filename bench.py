@@ -132,7 +132,7 @@ def bench_chunk(torch, gdn, steps, warmup):
 def bench_channel(torch, gdn, name, steps, warmup):
     """Per-key-channel-gate chunkwise forward on one of the channel configs, timed
     like the headline case: o and S_T for the batched case, only S_T (from a
-    random S0) for the long prefill."""
+    random S0) for the long prefill, which then reads no q."""
     from gdn_inputs import CHUNK_CONFIGS, chunk_inputs
     cfg = CHUNK_CONFIGS[name]
     d = chunk_inputs(cfg, device="cuda")
@@ -152,12 +152,13 @@ def bench_channel(torch, gdn, name, steps, warmup):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     es = 2
-    per_ht = 2 * K * es + V * es + (V * es if want_o else 0) + K * 4 + 4
+    # q is read only when o is wanted: the final state does not depend on it
+    per_ht = (2 if want_o else 1) * K * es + V * es + (V * es if want_o else 0) + K * 4 + 4
     nbytes = B * T * H * per_ht + B * H * K * V * 4 * ((1 if d["S0"] is not None else 0) + 1)
     del d
     gbs = nbytes / (ms / 1e3) / 1e9
     return {"workload": f"per-key-channel-gate GDN chunkwise forward, B={B} H={H} T={T} "
-                        f"d_k=d_v={K} chunk={cfg.chunk}, bf16 q/k/v" + ("/o" if want_o else "") +
+                        f"d_k=d_v={K} chunk={cfg.chunk}, bf16 " + ("q/k/v/o" if want_o else "k/v (q not read)") +
                         ", fp32 g/beta/state" + (", returns S_T only from a random S0" if not want_o else ", S0=0"),
             "ms": ms, "mtok_s": B * T / (ms / 1e3) / 1e6, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
             "bytes_per_launch": nbytes, "kernel": "chunk_fwd_wsc_kernel<128>",

@@ -101,7 +101,9 @@ struct WcArgs {
     int xcd_map;
 };
 
-template <int K>
+// WO = false: the final state only (no o).  q is then not read, and QL, P, Q+ S
+// and O are not formed: the state update needs none of them.
+template <int K, bool WO>
 __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
 {
     using L = WcSmem<K>;
@@ -157,12 +159,12 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
             if (t < T) {
                 const long off = (row_base + (long)t * H) * K + 32 * kb + 8 * gq;
                 rk[kb] = *reinterpret_cast<const bf16x8 *>(args.k + off);
-                rq[kb] = *reinterpret_cast<const bf16x8 *>(args.q + off);
+                if constexpr (WO) rq[kb] = *reinterpret_cast<const bf16x8 *>(args.q + off);
                 rg[kb][0] = *reinterpret_cast<const f32x4 *>(args.g + off);
                 rg[kb][1] = *reinterpret_cast<const f32x4 *>(args.g + off + 4);
             } else {
                 rk[kb] = bf16x8{};
-                rq[kb] = bf16x8{};
+                if constexpr (WO) rq[kb] = bf16x8{};
                 rg[kb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
                 rg[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
@@ -207,14 +209,14 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                         ei[hh][e] = __builtin_amdgcn_exp2f(-x);
                     }
                 fKL[kb].v = scale8(rk[kb], el[0], el[1]);
-                fQL[kb].v = scale8(rq[kb], el[0], el[1]);
+                if constexpr (WO) fQL[kb].v = scale8(rq[kb], el[0], el[1]);
                 fKI[kb].v = scale8(rk[kb], ei[0], ei[1]);
                 // this key block of the next chunk goes in flight (spread over the
                 // loop rather than issued as one burst)
                 if (n + 1 < nchunks) fetch_kb(n + 1, kb);
                 const int off = wc_off<CPR>(row, 4 * kb + gq);
                 *reinterpret_cast<bf16x8 *>(C + L::cKL + off) = fKL[kb].v;
-                *reinterpret_cast<bf16x8 *>(C + L::cQL + off) = fQL[kb].v;
+                if constexpr (WO) *reinterpret_cast<bf16x8 *>(C + L::cQL + off) = fQL[kb].v;
                 *reinterpret_cast<bf16x8 *>(sKI + off) = fKI[kb].v;
                 if (r16 == 15) {   // block totals: E_pw = e^{lambda of the last row}
                     float *eb = sE + pw * K + 32 * kb + 8 * gq;
@@ -362,10 +364,10 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                     const int kb = hb + i;
                     fa[i] = wc_frag<CPR>(sKI, 16 * J, kb);
                     fk1[i] = wc_frag<CPR>(C + L::cKL, 16 * I1, kb);
-                    fq1[i] = wc_frag<CPR>(C + L::cQL, 16 * I1, kb);
+                    if constexpr (WO) fq1[i] = wc_frag<CPR>(C + L::cQL, 16 * I1, kb);
                     if constexpr (I2 > 0) {
                         fk2[i] = wc_frag<CPR>(C + L::cKL, 16 * I2, kb);
-                        fq2[i] = wc_frag<CPR>(C + L::cQL, 16 * I2, kb);
+                        if constexpr (WO) fq2[i] = wc_frag<CPR>(C + L::cQL, 16 * I2, kb);
                     }
 #pragma unroll
                     for (int bb = J; bb < IM; ++bb) {
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                     }
                     const Frag<__bf16> a1 = {scale8(fa[i].v, f0, f1)};
                     aA1 = mma(aA1, a1, fk1[i]);
-                    aP1 = mma(aP1, a1, fq1[i]);
+                    if constexpr (WO) aP1 = mma(aP1, a1, fq1[i]);
                     if constexpr (I2 > 0) {
 #pragma unroll
                         for (int bb = I1; bb < I2; ++bb) {
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                         }
                         const Frag<__bf16> a2 = {scale8(fa[i].v, f0, f1)};
                         aA2 = mma(aA2, a2, fk2[i]);
-                        aP2 = mma(aP2, a2, fq2[i]);
+                        if constexpr (WO) aP2 = mma(aP2, a2, fq2[i]);
                     }
                 }
             }
@@ -402,12 +404,12 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
             {
                 const int t = 16 * I1 + r16;
                 *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * L::LDC + frag_col(s0)) = cvt4(aA1 * -sBn[t]);
-                *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(aP1);
+                if constexpr (WO) *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(aP1);
             }
             if constexpr (I2 > 0) {
                 const int t = 16 * I2 + r16;
                 *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * L::LDC + frag_col(s0)) = cvt4(aA2 * -sBn[t]);
-                *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(aP2);
+                if constexpr (WO) *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(aP2);
             }
         };
         using std::integral_constant;
@@ -420,12 +422,12 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
             for (int kb = 0; kb < NKB; ++kb) {
                 fi[kb] = wc_frag<CPR>(sKI, 16 * cw, kb);
                 fl[kb] = wc_frag<CPR>(C + L::cKL, 16 * cw, kb);
-                fq[kb] = wc_frag<CPR>(C + L::cQL, 16 * cw, kb);
+                if constexpr (WO) fq[kb] = wc_frag<CPR>(C + L::cQL, 16 * cw, kb);
             }
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 aA = mma(aA, fi[kb], fl[kb]);
-                aP = mma(aP, fi[kb], fq[kb]);
+                if constexpr (WO) aP = mma(aP, fi[kb], fq[kb]);
             }
             const int t = 16 * cw + r16, s0 = 16 * cw + 4 * gq;
             const float bt = sBn[t];
@@ -436,7 +438,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                 a[e] = (s < t) ? bt * aA[e] : 0.f;
                 p[e] = (s <= t) ? aP[e] : 0.f;
             }
-            *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(p);
+            if constexpr (WO) *reinterpret_cast<bf16x4 *>(sP + t * L::LDC + frag_col(s0)) = cvt4(p);
             // -A of the block row-major; this wave reads it back, in order, for the inverse
             *reinterpret_cast<f32x4 *>(sAd + r16 * 16 + 4 * gq) = -a;
             const f32x4 tr = unit_lower_inverse16_rows(sAd);
@@ -505,13 +507,13 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
                     fk[kb] = wc_frag<CPR>(sKL, 16 * rt, kb);
-                    fq[kb] = wc_frag<CPR>(sQL, 16 * rt, kb);
+                    if constexpr (WO) fq[kb] = wc_frag<CPR>(sQL, 16 * rt, kb);
                 }
                 f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = ak;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
                     ak = mma(ak, fk[kb], Sb[kb]);
-                    aq = mma(aq, Sb[kb], fq[kb]);   // transposed: (Q+ S)^T
+                    if constexpr (WO) aq = mma(aq, Sb[kb], fq[kb]);   // transposed: (Q+ S)^T
                 }
                 KS[rt] = ak;
                 QS[rt] = aq;
@@ -561,14 +563,14 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         f32x4 egn[NT];                     // e^{gn} of this lane's key rows
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) egn[ct] = *reinterpret_cast<const f32x4 *>(sCF + 3 * K + key_of(ct, 0));
-        f32x4 O[4];
-        O[0] = mma_lo(QS[0], Df0, lds_frag_fo_lo(sP, L::LDC, 0, 0));
-        O[1] = mma(QS[1], Df0, lds_frag_fo(sP, L::LDC, 16, 0));
-        O[2] = mma(QS[2], Df0, lds_frag_fo(sP, L::LDC, 32, 0));
-        O[2] = mma_lo(O[2], Df1, lds_frag_fo_lo(sP, L::LDC, 32, 32));
-        O[3] = mma(QS[3], Df0, lds_frag_fo(sP, L::LDC, 48, 0));
-        O[3] = mma(O[3], Df1, lds_frag_fo(sP, L::LDC, 48, 32));
-        if (args.o) {
+        if constexpr (WO) {
+            f32x4 O[4];
+            O[0] = mma_lo(QS[0], Df0, lds_frag_fo_lo(sP, L::LDC, 0, 0));
+            O[1] = mma(QS[1], Df0, lds_frag_fo(sP, L::LDC, 16, 0));
+            O[2] = mma(QS[2], Df0, lds_frag_fo(sP, L::LDC, 32, 0));
+            O[2] = mma_lo(O[2], Df1, lds_frag_fo_lo(sP, L::LDC, 32, 32));
+            O[3] = mma(QS[3], Df0, lds_frag_fo(sP, L::LDC, 48, 0));
+            O[3] = mma(O[3], Df1, lds_frag_fo(sP, L::LDC, 48, 32));
             // lane (gq, r16) holds value columns 16 wave + 4 gq .. +3 of token
             // 16 rt + r16: one 8-byte store per row tile
 #pragma unroll
@@ -606,18 +608,18 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
     }
 }
 
-template <int K>
+template <int K, bool WO>
 static hipError_t launch_wsc(const WcArgs &a, long nwg, hipStream_t stream)
 {
     using L = WcSmem<K>;
     static bool attr_set = false;  // benign race: every thread sets the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_wsc_kernel<K>,
+        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_wsc_kernel<K, WO>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(chunk_fwd_wsc_kernel<K>, dim3((unsigned)nwg), dim3(WC_NTHR), L::bytes, stream, a);
+    hipLaunchKernelGGL((chunk_fwd_wsc_kernel<K, WO>), dim3((unsigned)nwg), dim3(WC_NTHR), L::bytes, stream, a);
     return hipGetLastError();
 }
 
@@ -634,7 +636,9 @@ hipError_t chunk_fwd_wsc_launch(int K, const void *q, const void *k, const void 
     const long bhn = (long)B * H;
     a.xcd_map = (a.nvb > 1 && bhn % 8 == 0) ? 1 : 0;
     const long nwg = bhn * a.nvb;
-    return K == 64 ? launch_wsc<64>(a, nwg, st) : launch_wsc<128>(a, nwg, st);
+    if (o)
+        return K == 64 ? launch_wsc<64, true>(a, nwg, st) : launch_wsc<128, true>(a, nwg, st);
+    return K == 64 ? launch_wsc<64, false>(a, nwg, st) : launch_wsc<128, false>(a, nwg, st);
 }
 
 } // namespace gdn

@@ -273,11 +273,15 @@ def test_ragged_bf16(T, K, gate):
 @pytest.mark.timeout(600)
 def test_long_prefill_48_heads_sampled():
     """T = 262144 with 48 heads of 128 x 128 fp32 state and a given S0: the GPU
-    runs the whole batch; the oracle follows three heads over the whole sequence."""
+    runs the whole batch; the oracle follows three heads over the whole sequence.
+    The call without o (the final state only, which skips q) gives the same state
+    bit for bit."""
     cfg = CHUNK_CONFIGS["channel_long"]
     _say(f"[modes] long prefill B{cfg.B} H{cfg.H} T{cfg.T}")
     d = chunk_inputs(cfg, device=DEV)
     o, S = _chunk(d)
+    _, S_only = _chunk(d, want_o=False)
+    assert torch.equal(S_only, S)
     heads = [0, 23, cfg.H - 1]
     sel = lambda x: x[:, :, heads].cpu().contiguous()
     _say("[modes] long prefill: GPU done, oracle on 3 heads")
