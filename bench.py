@@ -41,11 +41,11 @@ MEASURED_TRAFFIC = {
     # the B=16 H=8 T=2048 channel-gate case (o and S_T written)
     "chunk_fwd_wsc_kernel<128>": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                    "mfma_frag.h"),
-                                  "aea3bbff97305fd5", 420197770),
-    # the B=1 H=48 T=262144 channel-gate case (S_T only, from a random S0)
+                                  "4db84347cb4fcae9", 420155567),
+    # the B=1 H=48 T=262144 channel-gate case (S_T only, from a random S0; no q read)
     "chunk_fwd_wsc_kernel<128>/long": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                         "mfma_frag.h"),
-                                       "aea3bbff97305fd5", 16646596775),
+                                       "4db84347cb4fcae9", 14202992153),
     "recurrent_step_kernel<bf16,128,128,channel>": (("recurrent_step.hip", "gdn_common.h"),
                                                     "1864f0aa1a777d85", 1642879983),
     # M = 4 draft tokens on the decode shape: final state only / every token's state
