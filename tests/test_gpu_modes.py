@@ -200,7 +200,7 @@ def test_deterministic(gate):
 
 
 @pytest.mark.parametrize("K,dtype,gate", [(64, "fp32", "head"), (128, "bf16", "head"),
-                                          (128, "bf16", "channel")])
+                                          (64, "bf16", "channel"), (128, "bf16", "channel")])
 def test_in_place_state_and_state_only(K, dtype, gate):
     """S_T may alias S0, and o may be omitted; neither changes the state."""
     cfg = ChunkConfig("alias", B=2, H=3, T=130, K=K, V=K, dtype=dtype, gate=gate, s0_sigma=0.1,
