@@ -61,6 +61,34 @@ MEASURED_TRAFFIC = {
 }
 
 
+# bf16 matrix-core work per launch of the headline kernel from rocprofv3
+# (SQ_INSTS_VALU_MFMA_MOPS_BF16, in units of 512 flops), keyed like
+# MEASURED_TRAFFIC on the kernel's sources.
+MEASURED_MFMA_MOPS = {
+    "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
+                                  "mfma_frag.h"),
+                                 "34acdf37d6007014", 257949696),
+}
+
+
+def _sources_match(files, digest):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16] == digest
+
+
+def measured_mfma_flops(kernel):
+    """Counter-measured bf16 MFMA flops per launch of ``kernel``, or None when
+    its sources changed since the counters were taken."""
+    if kernel not in MEASURED_MFMA_MOPS:
+        return None
+    files, digest, mops = MEASURED_MFMA_MOPS[kernel]
+    return mops * 512 if _sources_match(files, digest) else None
+
+
 def measured_traffic(kernel):
     """Counter-measured HBM bytes per launch of ``kernel``, or None when the
     kernel's sources no longer match the ones the counters were taken on."""
@@ -461,6 +489,10 @@ def main():
             "useful_tflops": ch["useful_tflops"], "dense_tile_tflops": ch["dense_tflops"],
             "peak_tflops": BF16_PEAK_TFLOPS,
             "frac_useful": ch["useful_tflops"] / BF16_PEAK_TFLOPS}
+        cfl = measured_mfma_flops(kname)
+        out["mfma"]["counter_flops_per_launch"] = cfl
+        out["mfma"]["counter_frac_issued"] = (None if cfl is None else
+                                              cfl / (ch["ms"] / 1e3) / (BF16_PEAK_TFLOPS * 1e12))
         out["head_tokens_per_s"] = ch["head_tokens"] / (ch["ms"] / 1e3)
     if args.only in ("all", "decode"):
         dc = bench_decode(torch, gdn, reps=max(3, min(args.steps, 10)))
