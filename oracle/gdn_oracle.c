@@ -22,7 +22,8 @@
  *                                        k v^T puts keys on the rows)
  *   u <- S^T k                          (what the memory currently returns
  *                                        for key k)
- *   S <- S + beta k (v - u)^T           ("write the error, not the value")
+ *   S <- S + beta k (v - u)^T           (delta rule: store the correction
+ *                                        v - u, not v itself)
  *   o <- S^T q                          (read after the write)
  * Expanding: (I - beta k k^T) Diag(alpha) S + beta k v^T
  *          = Diag(alpha) S - beta k (k^T Diag(alpha) S) + beta k v^T.

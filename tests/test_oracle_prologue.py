@@ -12,8 +12,12 @@ and the mathematics fix, independently of its own code:
   below), beta = sigmoid(b_raw) with sigmoid(0) = 1/2 and symmetry;
 * q and k leave with unit L2 norm per head, and a positive rescaling of the
   raw input does not change them; SiLU at known points;
+* the g and beta outputs of prologue() itself, element by element, for caps
+  5, 2.5, 0.75 and none, from raw inputs built as closed-form preimages
+  (g_raw = log(e^c - 1), b_raw = logit(p));
 * planted mistakes (an anti-causal filter, reversed taps, normalising over the
-  wrong axis, no cap) fail these pins.
+  wrong axis, no cap, g_raw and b_raw swapped, the cap argument ignored, a
+  flipped gate sign, beta = sigmoid(-b_raw)) fail these pins.
 """
 import math
 
@@ -150,3 +154,78 @@ def test_planted_mistakes_are_caught():
     assert np.allclose(out["q"], cq / np.linalg.norm(cq, axis=-1, keepdims=True), rtol=1e-13)
     # no cap: large g_raw would fall below -5
     assert np.any(-P.softplus(d["g_raw"]) < -5.0) and np.all(out["g"] >= -5.0)
+
+
+# ---------------------------------------------------------------------------
+# The gate outputs of prologue() itself, element by element.
+#
+# The raw gate inputs are built from targets with closed-form preimages, so that
+# the expected outputs are known without evaluating softplus or the sigmoid:
+#   softplus(log(e^c - 1)) = c, so g_raw = log(expm1(c)) must give g = -min(c, cap)
+#   (Atomic-GDN2 card, section 2.1: g = -min(softplus(g_raw), cap));
+#   sigmoid(log(p / (1 - p))) = p, so b_raw = logit(p) must give beta = p.
+# The softplus targets c span [0.05, 9] (many above every finite cap used) and
+# the sigmoid targets p span [0.02, 0.98], drawn independently, so that swapping
+# g_raw and b_raw, ignoring the cap or flipping a sign changes the outputs.
+def _gate_case(gate, cap, B=2, T=7, H=3, K=4, V=4, seed=11):
+    r = np.random.default_rng(seed)
+    gshape = (B, T, H, K) if gate == "channel" else (B, T, H)
+    c = r.uniform(0.05, 9.0, gshape)               # softplus targets, some above any cap used
+    p = r.uniform(0.02, 0.98, (B, T, H))           # sigmoid targets
+    d = _raw(B, T, H, K, V, gate)
+    d["g_raw"] = np.log(np.expm1(c))
+    d["b_raw"] = np.log(p) - np.log1p(-p)
+    want_g = -np.minimum(c, cap)
+    return d, want_g, p
+
+
+def _gate_pins_hold(fn, gate, cap):
+    d, want_g, want_b = _gate_case(gate, cap)
+    out = fn(**d, silu_act=True, cap=cap)
+    return (np.allclose(out["g"], want_g, rtol=1e-12, atol=1e-12)
+            and np.allclose(out["beta"], want_b, rtol=1e-12, atol=1e-12))
+
+
+@pytest.mark.parametrize("cap", [5.0, 2.5, 0.75, math.inf])
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prologue_gate_outputs_elementwise(gate, cap):
+    d, want_g, want_b = _gate_case(gate, cap)
+    out = P.prologue(**d, silu_act=True, cap=cap)
+    assert out["g"].shape == want_g.shape and out["beta"].shape == want_b.shape
+    assert np.allclose(out["g"], want_g, rtol=1e-12, atol=1e-12)
+    assert np.allclose(out["beta"], want_b, rtol=1e-12, atol=1e-12)
+    # the cap is reached exactly where the target exceeds it
+    if math.isfinite(cap):
+        hit = want_g == -cap
+        assert hit.any() and np.all(out["g"][hit] == -cap)
+
+
+def test_prologue_gate_pins_catch_planted_mistakes():
+    real = P.prologue
+    assert _gate_pins_hold(real, "head", 2.5) and _gate_pins_hold(real, "channel", 2.5)
+
+    def swapped(**kw):            # g_raw and b_raw exchanged (same shape under the scalar gate)
+        kw["g_raw"], kw["b_raw"] = kw["b_raw"], kw["g_raw"]
+        return real(**kw)
+
+    def cap_ignored(**kw):        # the cap argument dropped in favour of the card's 5
+        kw["cap"] = 5.0
+        return real(**kw)
+
+    def no_cap(**kw):             # no clamp at all
+        kw["cap"] = math.inf
+        return real(**kw)
+
+    def sign_flipped(**kw):       # g = +min(softplus, cap)
+        out = real(**kw)
+        out["g"] = -out["g"]
+        return out
+
+    def beta_complement(**kw):    # beta = sigmoid(-b_raw)
+        kw["b_raw"] = -np.asarray(kw["b_raw"])
+        return real(**kw)
+
+    assert not _gate_pins_hold(swapped, "head", 2.5)
+    for gate in ("head", "channel"):
+        for mutant in (cap_ignored, no_cap, sign_flipped, beta_complement):
+            assert not _gate_pins_hold(mutant, gate, 2.5), (mutant.__name__, gate)
