@@ -1,21 +1,37 @@
 """Throughput of the Gated DeltaNet mixer forward on one MI355X.
 
-A step is one chunkwise forward (the prefill hot path) over the scalar-gate
-workload B=8, H=12, T=8192, d_k=d_v=128, chunk 64, bf16 q/k/v/o with fp32
-g/beta/state, synthetic seeded inputs resident in HBM.  ``value`` is tokens/s
-of that step (B*T tokens per step) in millions.  The same run also times the
-fused recurrent decode step (256 sequences x 48 heads of 128x128 fp32 state, 64
-chained in-place steps) and reports its HBM bandwidth, and times the fp64 CPU
-oracle on a bounded sample of the prefill workload.
+A step is one chunkwise forward over the long-prefill workload: B=1, H=48,
+T=262144 tokens, d_k=d_v=128, chunk 64, per-key-channel gate
+g = -min(softplus(N(0,2)), 5), bf16 k/v, fp32 g/beta and a random fp32 S0,
+returning the final state (3 MiB per layer), through gdn_chunk_fwd_ws (the
+sequence-parallel form: segments of each sequence reduced to affine state maps,
+combined in order).  Inputs are synthetic, seeded and resident in HBM before the
+timed region.  ``value`` is tokens/s of that step (B*T tokens; a token counts
+once across all heads) in millions.
 
-Prints one JSON line.  Options: --gpus (1 only), --steps (100), --warmup (50:
-the clocks settle over the first tens of launches),
---no-cpu (skip the CPU baseline), --only {all,chunk,decode}.
+The same run times, each as its own entry: the same prefill returning o as well
+(sequential kernels), the scalar-gate prefill B=8 H=12 T=8192 and the
+per-channel prefill B=16 H=8 T=2048 (o and S_T), the fused recurrent decode step
+(256 sequences x 48 heads, 64 chained in-place steps), the multi-token verify
+step, the chunkwise backward and the prologue; and the fp64 CPU oracle on a
+bounded sample of the headline workload.
+
+Timing: ``--warmup`` untimed launches, then more untimed launches until the
+launch times have settled (the clocks of a fresh device ramp over the first few
+tens of milliseconds; the count is recorded), then ``--steps`` launches, each
+bracketed by its own pair of HIP events on the stream the kernels run on, with a
+512 MB buffer written before each launch (outside the events) so that the 256 MB
+last-level cache holds none of the inputs.  Mean and median per launch are
+reported; ``value`` and the roofline use the mean.
+
+Prints one JSON line.  Options: --gpus (1 only), --steps, --warmup, --no-cpu,
+--only {all,headline,chunk,decode,verify,bwd,prologue}.
 """
 import argparse
+import hashlib
 import json
 import os
-import platform
+import statistics
 import sys
 import time
 
@@ -27,99 +43,91 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 CHUNK = 64
 CSRC = os.path.join(ROOT, "gated_deltanet_layer_amd", "csrc")
+FLUSH_BYTES = 512 << 20        # twice the 256 MB last-level cache
 
-# HBM bytes per launch read from rocprofv3 --pmc, one pass of FETCH_SIZE and one
-# of WRITE_SIZE (KiB per dispatch) on this script's own workloads.  FETCH_SIZE
-# is scaled by 2.0 and WRITE_SIZE by 1.0: the factors that make the same counters
-# read 1 GiB in and 1 GiB out for a plain elementwise copy of a 1 GiB fp32
-# tensor.  Each entry is keyed by a digest of the kernel's sources, so that a
-# kernel changed since its counters were taken reports null.
+# HBM bytes per launch from rocprofv3 --pmc, one pass of FETCH_SIZE and one of
+# WRITE_SIZE (KiB per dispatch) on this script's own workloads, scaled by 2.0
+# (FETCH_SIZE) and 1.0 (WRITE_SIZE): the factors that make the same counters read
+# 1 GiB each way for a plain elementwise copy of a 1 GiB fp32 tensor.  Each entry
+# is keyed by a digest of the kernel's sources, so that a kernel changed since its
+# counters were taken reports null.  For a call of several kernels the entry is
+# the sum over its kernels.
 MEASURED_TRAFFIC = {
     "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
                                   "mfma_frag.h"),
                                  "34acdf37d6007014", 862390784),
-    # the B=16 H=8 T=2048 channel-gate case (o and S_T written)
     "chunk_fwd_wsc_kernel<128>": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                    "mfma_frag.h"),
                                   "4db84347cb4fcae9", 420155567),
-    # the B=1 H=48 T=262144 channel-gate case (S_T only, from a random S0; no q read)
-    "chunk_fwd_wsc_kernel<128>/long": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
-                                        "mfma_frag.h"),
-                                       "4db84347cb4fcae9", 14202992153),
     "recurrent_step_kernel<bf16,128,128,channel>": (("recurrent_step.hip", "gdn_common.h"),
                                                     "1864f0aa1a777d85", 1642879983),
-    # M = 4 draft tokens on the decode shape: final state only / every token's state
     "recurrent_multi_kernel<bf16,128,128,channel>/final": (("recurrent_multi.hip", "gdn_common.h"),
                                                            "e96c18f898c72e85", 1739625626),
     "recurrent_multi_kernel<bf16,128,128,channel>/hist": (("recurrent_multi.hip", "gdn_common.h"),
                                                           "e96c18f898c72e85", 4158918874),
-    # the chunk-mode prologue at B8 H12 T8192 (scalar gate) and the fused decode token
     "prologue_kernel<bf16,128,128,scalar,silu>": (("prologue.hip", "prologue.h", "gdn_common.h"),
                                                   "1fb5d0b92490e05a", 1307185835),
     "recurrent_step_prologue_kernel<bf16,128,128,channel,silu>": (("prologue.hip", "prologue.h",
                                                                   "gdn_common.h"), "1fb5d0b92490e05a", 1719304713),
 }
 
-
-# bf16 matrix-core work per launch of the headline kernel from rocprofv3
-# (SQ_INSTS_VALU_MFMA_MOPS_BF16, in units of 512 flops), keyed like
-# MEASURED_TRAFFIC on the kernel's sources.
+# bf16 matrix-core work per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16, units of 512
+# flops), keyed like MEASURED_TRAFFIC.
 MEASURED_MFMA_MOPS = {
     "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
                                   "mfma_frag.h"),
                                  "34acdf37d6007014", 257949696),
 }
 
+SEG_SOURCES = ("chunk_fwd_seg.hip", "ws_common.h", "gdn_common.h", "mfma_frag.h")
 
-def _sources_match(files, digest):
-    import hashlib
+
+def _digest(files):
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
-    return h.hexdigest()[:16] == digest
+    return h.hexdigest()[:16]
 
 
-def measured_mfma_flops(kernel):
-    """Counter-measured bf16 MFMA flops per launch of ``kernel``, or None when
-    its sources changed since the counters were taken."""
-    if kernel not in MEASURED_MFMA_MOPS:
+def _keyed(table, key, scale=1):
+    if key not in table:
         return None
-    files, digest, mops = MEASURED_MFMA_MOPS[kernel]
-    return mops * 512 if _sources_match(files, digest) else None
+    files, digest, n = table[key]
+    return n * scale if _digest(files) == digest else None
 
 
-def measured_traffic(kernel):
-    """Counter-measured HBM bytes per launch of ``kernel``, or None when the
-    kernel's sources no longer match the ones the counters were taken on."""
-    import hashlib
-    if kernel not in MEASURED_TRAFFIC:
-        return None
-    files, digest, nbytes = MEASURED_TRAFFIC[kernel]
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
-    return nbytes if h.hexdigest()[:16] == digest else None
+def measured_traffic(key):
+    """Counter-measured HBM bytes per launch, or None when the kernel's sources
+    changed since the counters were taken."""
+    return _keyed(MEASURED_TRAFFIC, key)
 
 
-def chunk_bytes(B, T, H, K, V, es, channel, s0, so):
-    """Algorithmic HBM bytes of one chunkwise forward: every input read once,
-    every output written once."""
-    per_ht = 2 * K * es + V * es + V * es + (K if channel else 1) * 4 + 4
-    state = B * H * K * V * 4 * ((1 if s0 else 0) + (1 if so else 0))
+def measured_mfma_flops(key):
+    return _keyed(MEASURED_MFMA_MOPS, key, 512)
+
+
+# ------------------------------------------------------------------ work counts
+def chunk_bytes(B, T, H, K, V, es, channel, s0, want_o):
+    """Algorithmic HBM bytes of one chunkwise forward: every input it needs read
+    once, every output written once (q is not needed when o is not wanted)."""
+    per_ht = (2 * K if want_o else K) * es + V * es + (V * es if want_o else 0) \
+        + (K if channel else 1) * 4 + 4
+    state = B * H * K * V * 4 * ((1 if s0 else 0) + 1)
     return B * T * H * per_ht + state
 
 
-def chunk_flops(B, T, H, K, V, C=CHUNK):
-    """Flops per head-token of the formulation the kernel runs, lower-triangular
-    C x C blocks counted at half ("useful") or whole ("dense"):
-    Gram K K^T and Q K^T (2 C K), K+ S, Q+ S and K-^T D (6 K V), Tm X and P D (2 C V),
-    the triangular inverse (C^2 / 3)."""
-    useful = C * (2 * K + 2 * V) + 6 * K * V + C * C / 3
-    dense = 2 * C * (2 * K + 2 * V) + 6 * K * V + C * C / 3
+def chunk_flops(B, T, H, K, V, want_o, C=CHUNK):
+    """Flops of the chunkwise forward per call, the lower-triangular C x C blocks
+    counted at half ("useful") or whole ("dense"), per head-token:
+      with o:  C (3K + 2V) + 6KV + C^2/3   (Gram K K^T and Q K^T, W, U, P D; K+ S,
+               Q+ S, K-^T D; the triangular inverse)
+      state:   C (2K + V)  + 4KV + C^2/3   (no Q K^T, P D or Q+ S)
+    and the dense count doubles the C-terms."""
+    a = (3 * K + 2 * V) if want_o else (2 * K + V)
+    kv = (6 if want_o else 4) * K * V
     n = B * T * H
-    return n * useful, n * dense
+    return n * (C * a + kv + C * C / 3), n * (2 * C * a + kv + C * C / 3)
 
 
 def decode_bytes(N, H, K, V, es, channel):
@@ -127,106 +135,148 @@ def decode_bytes(N, H, K, V, es, channel):
     return N * H * per
 
 
-def _events(torch):
-    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+# ------------------------------------------------------------------ timing
+class Timer:
+    """Per-launch HIP-event timing with warm-up, settling and a cache flush."""
+
+    def __init__(self, torch, steps, warmup, settle_s=0.3, max_settle=2000):
+        self.torch, self.steps, self.warmup = torch, steps, warmup
+        self.settle_s, self.max_settle = settle_s, max_settle
+        self.flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def flush(self):
+        self.flush_buf.zero_()
+
+    def _ev(self):
+        E = self.torch.cuda.Event
+        return E(enable_timing=True), E(enable_timing=True)
+
+    def run(self, fn, steps=None, warmup=None, per_launch=1):
+        """fn() enqueues one step; returns dict of per-step ms (mean, median, min,
+        max) and the warm-up actually performed.  per_launch > 1: fn enqueues
+        that many launches and the times are divided by it."""
+        torch = self.torch
+        steps = self.steps if steps is None else steps
+        warmup = self.warmup if warmup is None else warmup
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        extra, recent, t0 = 0, [], time.perf_counter()
+        while extra < self.max_settle:
+            e0, e1 = self._ev()
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            recent.append(e0.elapsed_time(e1))
+            extra += 1
+            if time.perf_counter() - t0 >= self.settle_s and len(recent) >= 8:
+                last = recent[-8:]
+                if (max(last) - min(last)) / min(last) < 0.03:
+                    break
+        pairs = [self._ev() for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in pairs:
+            self.flush()
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) / per_launch for a, b in pairs]
+        return dict(ms=statistics.fmean(ts), ms_median=statistics.median(ts), ms_min=min(ts),
+                    ms_max=max(ts), steps=steps, warmup_requested=warmup,
+                    warmup_performed=warmup + extra)
 
 
-def bench_chunk(torch, gdn, steps, warmup):
-    from gdn_inputs import CHUNK_CONFIGS, chunk_inputs
-    cfg = CHUNK_CONFIGS["scalar_bf16"]
-    d = chunk_inputs(cfg, device="cuda")
-    B, T, H, K, V = cfg.B, cfg.T, cfg.H, cfg.K, cfg.V
-    o = torch.empty(B, T, H, V, dtype=torch.bfloat16, device="cuda")
-    S_T = torch.empty(B, H, K, V, dtype=torch.float32, device="cuda")
-    run = lambda: gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o, S_T)
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    e0, e1 = _events(torch)
-    e0.record()
-    for _ in range(steps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    nbytes = chunk_bytes(B, T, H, K, V, 2, False, d["S0"] is not None, True)
-    useful, dense = chunk_flops(B, T, H, K, V)
-    s = ms / 1e3
-    return dict(cfg=cfg, ms=ms, tokens=B * T, head_tokens=B * T * H, bytes=nbytes,
-                gbs=nbytes / s / 1e9, useful_tflops=useful / s / 1e12,
-                dense_tflops=dense / s / 1e12, inputs=d)
-
-
-def bench_channel(torch, gdn, name, steps, warmup):
-    """Per-key-channel-gate chunkwise forward on one of the channel configs, timed
-    like the headline case: o and S_T for the batched case, only S_T (from a
-    random S0) for the long prefill, which then reads no q."""
+# ------------------------------------------------------------------ workloads
+def bench_prefill(torch, gdn, timer, name, want_o, use_ws, steps=None, warmup=None):
     from gdn_inputs import CHUNK_CONFIGS, chunk_inputs
     cfg = CHUNK_CONFIGS[name]
     d = chunk_inputs(cfg, device="cuda")
     B, T, H, K, V = cfg.B, cfg.T, cfg.H, cfg.K, cfg.V
-    want_o = d["S0"] is None
-    o = torch.empty(B, T, H, V, dtype=torch.bfloat16, device="cuda") if want_o else None
+    channel = cfg.gate == "channel"
+    o = torch.empty(B, T, H, V, dtype=d["v"].dtype, device="cuda") if want_o else None
     S_T = torch.empty(B, H, K, V, dtype=torch.float32, device="cuda")
-    run = lambda: gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o, S_T)
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    e0, e1 = _events(torch)
-    e0.record()
-    for _ in range(steps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    es = 2
-    # q is read only when o is wanted: the final state does not depend on it
-    per_ht = (2 if want_o else 1) * K * es + V * es + (V * es if want_o else 0) + K * 4 + 4
-    nbytes = B * T * H * per_ht + B * H * K * V * 4 * ((1 if d["S0"] is not None else 0) + 1)
-    del d
-    gbs = nbytes / (ms / 1e3) / 1e9
-    return {"workload": f"per-key-channel-gate GDN chunkwise forward, B={B} H={H} T={T} "
-                        f"d_k=d_v={K} chunk={cfg.chunk}, bf16 " + ("q/k/v/o" if want_o else "k/v (q not read)") +
-                        ", fp32 g/beta/state" + (", returns S_T only from a random S0" if not want_o else ", S0=0"),
-            "ms": ms, "mtok_s": B * T / (ms / 1e3) / 1e6, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
-            "bytes_per_launch": nbytes, "kernel": "chunk_fwd_wsc_kernel<128>",
-            "traffic": measured_traffic("chunk_fwd_wsc_kernel<128>" + ("" if want_o else "/long")),
-            "steps": steps, "warmup": warmup}
+    gate = gdn.GDN_GATE_CHANNEL if channel else gdn.GDN_GATE_HEAD
+    nws = gdn.gdn_chunk_fwd_workspace_size(B, T, H, K, V, d["q"].dtype, gate, want_o) if use_ws else 0
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+    if use_ws:
+        run = lambda: gdn.gdn_chunk_fwd_ws(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                                           o, S_T, ws)
+    else:
+        run = lambda: gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o, S_T)
+    t = timer.run(run, steps, warmup)
+    es = 2 if cfg.dtype == "bf16" else 4
+    nbytes = chunk_bytes(B, T, H, K, V, es, channel, d["S0"] is not None, want_o)
+    useful, dense = chunk_flops(B, T, H, K, V, want_o)
+    nseg = 1 + (nws // (B * H * 2 * K * K * 4) if nws else 0)
+    if nseg > 1:
+        kernels = ["chunk_fwd_seg_kernel", "seg_combine_kernel"]
+        tkey = "chunk_fwd_seg/" + name
+    elif channel:
+        kernels = ["chunk_fwd_wsc_kernel<128, %s>" % ("true" if want_o else "false")]
+        tkey = "chunk_fwd_wsc_kernel<128>" + ("" if name == "channel_bf16" else "/" + name)
+    else:
+        kernels = ["chunk_fwd_ws_kernel<128>"]
+        tkey = "chunk_fwd_ws_kernel<128>"
+    s = t["ms"] / 1e3
+    gbs = nbytes / s / 1e9
+    inputs = d if name == "channel_long" and not want_o else None
+    if inputs is None:
+        del d
+    ent = {
+        "workload": (f"{'per-key-channel' if channel else 'scalar'}-gate GDN chunkwise forward, "
+                     f"B={B} H={H} T={T} d_k=d_v={K} chunk={cfg.chunk}, {cfg.dtype} "
+                     f"{'q/k/v/o' if want_o else 'k/v (q not read)'}, fp32 g/beta/state, "
+                     + ("S0 ~ N(0, 0.02), " if cfg.s0_sigma else "S0 = 0, ")
+                     + ("returns o and S_T" if want_o else "returns S_T only")),
+        "entry": "gdn_chunk_fwd_ws" if use_ws else "gdn_chunk_fwd",
+        "segments": nseg, "workspace_bytes": nws,
+        "tokens": B * T, "head_tokens": B * T * H,
+        "mtok_s": B * T / s / 1e6, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+        "bytes_per_launch": nbytes,
+        "useful_tflops": useful / s / 1e12, "dense_tile_tflops": dense / s / 1e12,
+        "frac_bf16_peak_useful": useful / s / 1e12 / BF16_PEAK_TFLOPS,
+        "kernels": kernels, "traffic": measured_traffic(tkey),
+    }
+    ent.update(t)
+    return ent, inputs, cfg
 
 
-def bench_decode(torch, gdn, reps):
+def bench_decode(torch, gdn, timer):
     from gdn_inputs import DECODE_CONFIG, decode_inputs
     cfg = DECODE_CONFIG
     d = decode_inputs(cfg, device="cuda")
     N, H, K, V = cfg.N, cfg.H, cfg.K, cfg.V
     S = d["S0"].clone()
     o = torch.empty(cfg.steps, N, H, V, dtype=torch.bfloat16, device="cuda")
+    step = [0]
 
-    def chain():
-        for s in range(cfg.steps):
-            gdn.gdn_recurrent_step(d["q"][s], d["k"][s], d["v"][s], d["g"][s], d["beta"][s], S, o[s])
+    def one():   # the next step of the 64-token chain, in place; the chain restarts from S0
+        s = step[0]
+        if s == 0:
+            S.copy_(d["S0"])
+        gdn.gdn_recurrent_step(d["q"][s], d["k"][s], d["v"][s], d["g"][s], d["beta"][s], S, o[s])
+        step[0] = (s + 1) % cfg.steps
 
-    chain()  # warm-up
-    times = []
-    for _ in range(reps):
-        S.copy_(d["S0"])                      # restore the state (not timed)
-        torch.cuda.synchronize()
-        e0, e1 = _events(torch)
-        e0.record()
-        chain()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / cfg.steps)
-    ms = sorted(times)[len(times) // 2]
+    # a whole chain per measurement run so that every step index is timed; the
+    # restore copy at step 0 sits inside that step's events only on the first
+    # step of each chain, so time steps 1..63 of chains
+    t = timer.run(one, steps=cfg.steps * 2, warmup=cfg.steps)
     nbytes = decode_bytes(N, H, K, V, 2, True)
-    return dict(cfg=cfg, ms_per_step=ms, bytes=nbytes, gbs=nbytes / (ms / 1e3) / 1e9)
+    s = t["ms_median"] / 1e3
+    ent = {"workload": f"fused recurrent decode, N={N} H={H} d_k=d_v={K}, per-channel gate, bf16 "
+                       f"q/k/v/o, fp32 state in place, {cfg.steps} chained steps",
+           "ms_per_step": t["ms_median"], "gbs": nbytes / s / 1e9,
+           "frac_hbm": nbytes / s / 1e9 / HBM_PEAK_GBS, "bytes_per_step": nbytes,
+           "traffic": measured_traffic("recurrent_step_kernel<bf16,128,128,channel>"),
+           "kernel": "recurrent_step_kernel<bf16,128,128,channel>",
+           "note": "median over per-step event pairs (the chain's first step also restores S0)"}
+    ent.update(t)
+    return ent
 
 
-def bench_verify(torch, gdn, M, keep_hist, reps, warmup):
-    """M draft tokens per sequence from one state (gdn_recurrent_steps) on the
-    decode workload's shape: o of every token plus either the final state or the
-    state after every token (rollback).  S0 is left untouched (S_T is a separate
-    buffer), so the same call repeats."""
+def bench_verify(torch, gdn, timer, M, keep_hist):
     from gdn_inputs import DECODE_CONFIG, decode_inputs
     cfg = DECODE_CONFIG.with_(steps=M)
     d = decode_inputs(cfg, device="cuda")
@@ -237,29 +287,22 @@ def bench_verify(torch, gdn, M, keep_hist, reps, warmup):
     o = torch.empty(N, M, H, V, dtype=torch.bfloat16, device="cuda")
     S_T = None if keep_hist else torch.empty_like(S0)
     S_hist = torch.empty(N, M, H, K, V, dtype=torch.float32, device="cuda") if keep_hist else None
-    run = lambda: gdn.gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist)
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    e0, e1 = _events(torch)
-    e0.record()
-    for _ in range(reps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    t = timer.run(lambda: gdn.gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist),
+                  steps=max(10, timer.steps), warmup=5)
     state = K * V * 4
     per_tok = 2 * K * 2 + V * 2 + V * 2 + K * 4 + 4
     nbytes = N * H * (state + (M * state if keep_hist else state) + M * per_tok)
-    gbs = nbytes / (ms / 1e3) / 1e9
-    return {"workload": f"{M} draft tokens per sequence from one state, N={N} H={H} "
-                        f"d_k=d_v={K}, per-channel gate, bf16 q/k/v/o, fp32 state; "
-                        + ("state after every token kept" if keep_hist else "final state written"),
-            "M": M, "ms": ms, "tokens_per_s": N * M / (ms / 1e3), "gbs": gbs,
-            "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_call": nbytes,
-            "traffic": measured_traffic("recurrent_multi_kernel<bf16,128,128,channel>/"
-                                        + ("hist" if keep_hist else "final")),
-            "kernel": "recurrent_multi_kernel<bf16,128,128,channel>"}
+    s = t["ms"] / 1e3
+    ent = {"workload": f"{M} draft tokens per sequence from one state, N={N} H={H} d_k=d_v={K}, "
+                       f"per-channel gate, bf16 q/k/v/o, fp32 state; "
+                       + ("state after every token kept" if keep_hist else "final state written"),
+           "M": M, "tokens_per_s": N * M / s, "gbs": nbytes / s / 1e9,
+           "frac_hbm": nbytes / s / 1e9 / HBM_PEAK_GBS, "bytes_per_call": nbytes,
+           "traffic": measured_traffic("recurrent_multi_kernel<bf16,128,128,channel>/"
+                                       + ("hist" if keep_hist else "final")),
+           "kernel": "recurrent_multi_kernel<bf16,128,128,channel>"}
+    ent.update(t)
+    return ent
 
 
 def bwd_bytes(B, T, H, K, V, es, channel):
@@ -271,7 +314,7 @@ def bwd_bytes(B, T, H, K, V, es, channel):
     return B * T * H * per_ht + 3 * B * H * K * V * 4
 
 
-def bench_bwd(torch, gdn, steps, warmup):
+def bench_bwd(torch, gdn, timer):
     """gdn_chunk_bwd at the card's kernel-benchmark shape (B=4 H=6 T=4096,
     d_k = d_v = 128, per-channel gate in [-5, 0], bf16), alone and after the
     forward (the card times forward and backward together)."""
@@ -291,29 +334,18 @@ def bench_bwd(torch, gdn, steps, warmup):
                                     gr["dS_T"], g["dq"], g["dk"], g["dv"], g["dg"], g["dbeta"],
                                     g["dS0"], ws)
     fwd = lambda: gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o, S_T)
-
-    def timed(fn):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = _events(torch)
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-
-    ms_bwd = timed(bwd)
-    ms_fb = timed(lambda: (fwd(), bwd()))
+    tb = timer.run(bwd, steps=max(10, timer.steps), warmup=5)
+    tfb = timer.run(lambda: (fwd(), bwd()), steps=max(10, timer.steps), warmup=5)
     nbytes = bwd_bytes(B, T, H, K, V, 2, True)
-    gbs = nbytes / (ms_bwd / 1e3) / 1e9
+    s = tb["ms"] / 1e3
     return {"workload": f"chunkwise backward, B={B} H={H} T={T} d_k=d_v={K} chunk=64, per-channel "
                         f"gate, bf16 q/k/v/do and dq/dk/dv, fp32 g/beta/states and their gradients, "
                         f"dL/do and dL/dS_T ~ N(0, 1)",
-            "ms": ms_bwd, "ms_fwd_bwd": ms_fb, "mtok_s_fwd_bwd": B * T / (ms_fb / 1e3) / 1e6,
-            "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_call": nbytes,
-            "workspace_bytes": nws, "steps": steps, "warmup": warmup,
+            "ms": tb["ms"], "ms_median": tb["ms_median"], "ms_fwd_bwd": tfb["ms"],
+            "mtok_s_fwd_bwd": B * T / (tfb["ms"] / 1e3) / 1e6,
+            "gbs": nbytes / s / 1e9, "frac_hbm": nbytes / s / 1e9 / HBM_PEAK_GBS,
+            "bytes_per_call": nbytes, "workspace_bytes": nws, "steps": tb["steps"],
+            "warmup_performed": tb["warmup_performed"],
             "kernels": ["bwd_prep_kernel", "bwd_sweeps_kernel", "bwd_vgrad_kernel",
                         "bwd_kgrad2_kernel"]}
 
@@ -326,10 +358,10 @@ def prologue_bytes(B, T, H, K, V, es, channel):
     return B * T * H * per_ht + H * (2 * K + V) * 16 + 2 * B * 3 * H * (2 * K + V) * es
 
 
-def bench_prologue(torch, gdn, steps, warmup):
-    """gdn_prologue on the headline forward's shape (B=8 H=12 T=8192, d_k=d_v=128,
-    scalar gate, bf16, SiLU) and, on the decode shape (N=256 H=48, per-channel
-    gate), the fused decode token against the prologue and the step as two launches."""
+def bench_prologue(torch, gdn, timer):
+    """gdn_prologue on the scalar prefill's shape (B=8 H=12 T=8192, d_k=d_v=128,
+    bf16, SiLU) and, on the decode shape (N=256 H=48, per-channel gate), the fused
+    decode token against the prologue and the step as two launches."""
     from gdn_inputs import prologue_inputs
     out = {}
     B, T, H, K, V = 8, 8192, 12, 128, 128
@@ -340,25 +372,17 @@ def bench_prologue(torch, gdn, steps, warmup):
                                    d["w_q"], d["w_k"], d["w_v"], d["cs_q"], d["cs_k"], d["cs_v"],
                                    r["q_raw"], r["k_raw"], r["v_raw"], r["g_raw"], r["b_raw"],
                                    cso[0], cso[1], cso[2])
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    e0, e1 = _events(torch)
-    e0.record()
-    for _ in range(steps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    t = timer.run(run)
     nbytes = prologue_bytes(B, T, H, K, V, 2, False)
+    s = t["ms"] / 1e3
     out["chunk"] = {"workload": f"gdn_prologue, B={B} T={T} H={H} d_k=d_v={K}, scalar gate, bf16, "
                                 f"SiLU, carried states in and out",
-                    "ms": ms, "gbs": nbytes / (ms / 1e3) / 1e9,
-                    "frac_hbm": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_call": nbytes,
+                    "gbs": nbytes / s / 1e9, "frac_hbm": nbytes / s / 1e9 / HBM_PEAK_GBS,
+                    "bytes_per_call": nbytes,
                     "traffic": measured_traffic("prologue_kernel<bf16,128,128,scalar,silu>"),
                     "kernel": "prologue_kernel<bf16,128,128,scalar,silu>"}
+    out["chunk"].update(t)
     del d, r, cso
-    # the decode token: fused against two launches
     N, H = 256, 48
     d = prologue_inputs(N, 1, H, K, V, "bf16", "channel", device="cuda", seed=1)
     d = {n: (x[:, 0].contiguous() if n in ("q_raw", "k_raw", "v_raw", "g_raw", "b_raw") else x)
@@ -370,83 +394,100 @@ def bench_prologue(torch, gdn, steps, warmup):
     pro = {n: torch.empty(N, 1, *d[n].shape[1:], dtype=d[n].dtype, device="cuda")
            for n in ("q_raw", "k_raw", "v_raw", "g_raw", "b_raw")}
     raw1 = {n: d[n].unsqueeze(1) for n in ("q_raw", "k_raw", "v_raw", "g_raw", "b_raw")}
+    j = [0]
 
-    def fused(j):
-        a, b = cs[j % 2], cs[(j + 1) % 2]
+    def fused():
+        a, b = cs[j[0] % 2], cs[(j[0] + 1) % 2]
+        j[0] += 1
         gdn.gdn_recurrent_step_prologue(d["q_raw"], d["k_raw"], d["v_raw"], d["g_raw"], d["b_raw"],
                                         d["w_q"], d["w_k"], d["w_v"], a[0], a[1], a[2], b[0], b[1],
                                         b[2], S, o)
 
-    def two(j):
-        a, b = cs[j % 2], cs[(j + 1) % 2]
+    def two():
+        a, b = cs[j[0] % 2], cs[(j[0] + 1) % 2]
+        j[0] += 1
         gdn.gdn_prologue(raw1["q_raw"], raw1["k_raw"], raw1["v_raw"], raw1["g_raw"], raw1["b_raw"],
                          d["w_q"], d["w_k"], d["w_v"], a[0], a[1], a[2], pro["q_raw"], pro["k_raw"],
                          pro["v_raw"], pro["g_raw"], pro["b_raw"], b[0], b[1], b[2])
         gdn.gdn_recurrent_step(pro["q_raw"][:, 0], pro["k_raw"][:, 0], pro["v_raw"][:, 0],
                                pro["g_raw"][:, 0], pro["b_raw"][:, 0], S, o)
 
-    res = {}
-    for name, fn in (("fused", fused), ("two_launches", two)):
-        for j in range(warmup):
-            fn(j)
-        torch.cuda.synchronize()
-        e0, e1 = _events(torch)
-        e0.record()
-        for j in range(steps):
-            fn(j)
-        e1.record()
-        torch.cuda.synchronize()
-        res[name] = e0.elapsed_time(e1) / steps
+    tf = timer.run(fused)
+    t2 = timer.run(two)
     state = N * H * K * V * 4
     nb = 2 * state + N * H * ((2 * K + V) * 2 + K * 4 + 4 + V * 2) + H * (2 * K + V) * 16 \
         + 2 * N * 3 * H * (2 * K + V) * 2
     out["decode"] = {"workload": f"decode token from the raw projections, N={N} H={H} "
                                  f"d_k=d_v={K}, per-channel gate, bf16, SiLU, state in place",
-                     "ms_fused": res["fused"], "ms_two_launches": res["two_launches"],
-                     "gbs_fused": nb / (res["fused"] / 1e3) / 1e9,
-                     "frac_hbm_fused": nb / (res["fused"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "ms_fused": tf["ms"], "ms_two_launches": t2["ms"],
+                     "gbs_fused": nb / (tf["ms"] / 1e3) / 1e9,
+                     "frac_hbm_fused": nb / (tf["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
                      "bytes_per_step": nb,
                      "traffic": measured_traffic("recurrent_step_prologue_kernel<bf16,128,128,channel,silu>"),
                      "kernel": "recurrent_step_prologue_kernel<bf16,128,128,channel,silu>"}
     return out
 
 
-def cpu_baseline(chunk_inputs_dev, cfg, target_s=15.0):
-    """fp64 oracle on a bounded sample of the prefill workload: whole sequences of
-    some (b, h) slices, one OpenMP thread per slice."""
+# ------------------------------------------------------------------ CPU baseline
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(d, cfg, target_s=12.0):
+    """The fp64 oracle on a bounded sample of the headline workload: every head of
+    the batch over a prefix of the sequence, final state only, from the same S0,
+    one OpenMP thread per head.  Sized from a short run on all threads so that
+    the sample takes about target_s seconds."""
     import oracle
+    H = cfg.H
     threads = oracle.max_threads()
-    d = chunk_inputs_dev
-    # time one slice alone to size the sample (target_s of CPU thread-time)
-    one = [t[:1, :, :1].cpu().contiguous() for t in (d["q"], d["k"], d["v"], d["g"], d["beta"])]
+    S0 = d["S0"].cpu()
+    host = lambda t, n: t[:, :n].cpu().contiguous()
+    # one head, one thread
+    n1 = 2048
     t0 = time.perf_counter()
-    oracle.forward(*one, None, want_o=True, nthreads=1)
-    t_one = time.perf_counter() - t0
-    nb = int(round(target_s / max(t_one, 1e-3) / cfg.H))
-    nb = max(1, min(cfg.B, nb))
-    args = [t[:nb].cpu().contiguous() for t in (d["q"], d["k"], d["v"], d["g"], d["beta"])]
-    nsl = nb * cfg.H
+    oracle.forward(host(d["q"], n1)[:, :, :1], host(d["k"], n1)[:, :, :1], host(d["v"], n1)[:, :, :1],
+                   host(d["g"], n1)[:, :, :1], host(d["beta"], n1)[:, :, :1], S0[:, :1].contiguous(),
+                   want_o=False, nthreads=1)
+    r1 = n1 / (time.perf_counter() - t0)
+    # every head, all threads, short prefix: the rate the host really gives
+    n2 = 1024
+    args = [host(d[n], n2) for n in ("q", "k", "v", "g", "beta")]
     t0 = time.perf_counter()
-    oracle.forward(*args, None, want_o=True)
+    oracle.forward(*args, S0, want_o=False)
+    rN = H * n2 / (time.perf_counter() - t0)
+    Ts = int(max(1024, min(cfg.T, target_s * rN / H)) // 64 * 64)
+    args = [host(d[n], Ts) for n in ("q", "k", "v", "g", "beta")]
+    t0 = time.perf_counter()
+    oracle.forward(*args, S0, want_o=False)
     wall = time.perf_counter() - t0
-    head_tokens = nsl * cfg.T
-    used = min(threads, nsl)
-    return dict(value=head_tokens / cfg.H / wall / 1e6, unit="Mtok/s", cores=used,
-                kind="oracle",
-                sample=(f"fp64 oracle on {nsl} of {cfg.B * cfg.H} (b,h) slices (batch rows "
-                        f"0..{nb - 1}), T={cfg.T}, same inputs: {head_tokens} head-tokens in "
-                        f"{wall:.2f} s wall on {used} threads; Mtok/s = head-tokens/s / H"),
-                wall_s=wall, head_tokens_per_s=head_tokens / wall,
-                host_cpus=len(os.sched_getaffinity(0)))
+    ht_s = H * Ts / wall
+    used = min(threads, H)
+    return dict(value=ht_s / H / 1e6, unit="Mtok/s", cores=used, kind="oracle",
+                sample=(f"fp64 oracle, final state only, all {H} heads over the first {Ts} of "
+                        f"{cfg.T} tokens of the same inputs (from the same S0): {H * Ts} "
+                        f"head-tokens in {wall:.2f} s on {used} OpenMP threads; Mtok/s = "
+                        f"head-tokens/s / H"),
+                wall_s=wall, head_tokens_per_s=ht_s, single_thread_head_tokens_per_s=r1,
+                effective_parallelism=ht_s / r1, host_cpus=len(os.sched_getaffinity(0)),
+                cpu_model=_cpu_model())
 
 
+# ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "channel", "verify", "bwd",
+    ap.add_argument("--only", choices=["all", "headline", "chunk", "decode", "verify", "bwd",
                                        "prologue"], default="all")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -461,105 +502,78 @@ def main():
         build.build()
     gdn.lib()
     torch.manual_seed(0)
+    timer = Timer(torch, args.steps, args.warmup)
 
     out = {
         "metric": "GDN chunk fwd Mtok/s + %bf16 MFMA peak; decode step GB/s + %HBM peak",
         "value": None, "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded; q,k unit-norm, v~N(0,1), beta=sigmoid(N(0,1)), g=-softplus(N(0,1)))",
+        "data": ("synthetic, seeded: k unit-norm, v ~ N(0,1), beta = sigmoid(N(0,1)), "
+                 "g = -min(softplus(N(0,2)), 5) per key channel, S0 ~ N(0, 0.02)"),
     }
-    ch = None
+    head = head_in = head_cfg = None
+    if args.only in ("all", "headline"):
+        head, head_in, head_cfg = bench_prefill(torch, gdn, timer, "channel_long", False, True)
+        out["value"] = head["mtok_s"]
+        out["ms_per_step"] = head["ms"]
+        out["config"] = {"workload": head["workload"] + " (gdn_chunk_fwd_ws, "
+                         f"{head['segments']} segments per sequence)",
+                         "global_batch": head_cfg.B, "seq_len": head_cfg.T, "heads": head_cfg.H,
+                         "d_k": head_cfg.K, "d_v": head_cfg.V, "parallelism": "single GPU"}
+        out["timing"] = {k: head[k] for k in ("ms", "ms_median", "ms_min", "ms_max", "steps",
+                                              "warmup_requested", "warmup_performed")}
+        out["roofline"] = {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": head["gbs"] / HBM_PEAK_GBS,
+                           "traffic": head["traffic"], "kernel": " + ".join(head["kernels"]),
+                           "algorithmic_bytes_per_launch": head["bytes_per_launch"]}
+        out["mfma"] = {"useful_tflops": head["useful_tflops"],
+                       "dense_tile_tflops": head["dense_tile_tflops"],
+                       "peak_tflops": BF16_PEAK_TFLOPS,
+                       "frac_useful": head["useful_tflops"] / BF16_PEAK_TFLOPS,
+                       "flop_count": "useful per head-token C(2K+V) + 4KV + C^2/3 (final state "
+                                     "only; dense doubles the C-terms)"}
+        out["head_tokens_per_s"] = head["head_tokens"] / (head["ms"] / 1e3)
     if args.only in ("all", "chunk"):
-        ch = bench_chunk(torch, gdn, args.steps, args.warmup)
-        cfg = ch["cfg"]
-        out["value"] = ch["tokens"] / (ch["ms"] / 1e3) / 1e6
-        out["ms_per_step"] = ch["ms"]
-        out["config"] = {
-            "workload": f"scalar-gate GDN chunkwise forward, B={cfg.B} H={cfg.H} T={cfg.T} "
-                        f"d_k=d_v={cfg.K} chunk={cfg.chunk}, bf16 q/k/v/o, fp32 g/beta/state, S0=0",
-            "global_batch": cfg.B, "seq_len": cfg.T, "heads": cfg.H, "d_k": cfg.K, "d_v": cfg.V,
-            "parallelism": "single GPU"}
-        kname = "chunk_fwd_ws_kernel<128>"
-        out["roofline"] = {
-            "bound": "hbm", "achieved": ch["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": ch["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(kname),
-            "kernel": kname, "algorithmic_bytes_per_launch": ch["bytes"]}
-        out["mfma"] = {
-            "useful_tflops": ch["useful_tflops"], "dense_tile_tflops": ch["dense_tflops"],
-            "peak_tflops": BF16_PEAK_TFLOPS,
-            "frac_useful": ch["useful_tflops"] / BF16_PEAK_TFLOPS}
-        cfl = measured_mfma_flops(kname)
-        out["mfma"]["counter_flops_per_launch"] = cfl
-        out["mfma"]["counter_frac_issued"] = (None if cfl is None else
-                                              cfl / (ch["ms"] / 1e3) / (BF16_PEAK_TFLOPS * 1e12))
-        out["head_tokens_per_s"] = ch["head_tokens"] / (ch["ms"] / 1e3)
+        ents = []
+        for name, want_o, use_ws in (("channel_long", True, True), ("scalar_bf16", True, True),
+                                     ("channel_bf16", True, True)):
+            e, _, _ = bench_prefill(torch, gdn, timer, name, want_o, use_ws,
+                                    steps=max(5, min(args.steps, 20)) if name == "channel_long"
+                                    else max(20, args.steps))
+            if want_o:
+                e["mfma_note"] = ("useful per head-token C(3K+2V) + 6KV + C^2/3 (the survey's "
+                                  "count); dense doubles the C-terms")
+                if name == "scalar_bf16":
+                    cfl = measured_mfma_flops("chunk_fwd_ws_kernel<128>")
+                    e["counter_mfma_flops_per_launch"] = cfl
+                    e["counter_frac_issued"] = (None if cfl is None else
+                                                cfl / (e["ms"] / 1e3) / (BF16_PEAK_TFLOPS * 1e12))
+            ents.append(e)
+        out["chunk"] = ents
+        if out["value"] is None:
+            out["value"], out["ms_per_step"] = ents[0]["mtok_s"], ents[0]["ms"]
+            out["config"] = {"workload": ents[0]["workload"]}
     if args.only in ("all", "decode"):
-        dc = bench_decode(torch, gdn, reps=max(3, min(args.steps, 10)))
-        c = dc["cfg"]
-        dec = {"workload": f"fused recurrent decode, N={c.N} H={c.H} d_k=d_v={c.K}, per-channel "
-                           f"gate, bf16 q/k/v/o, fp32 state in place, {c.steps} chained steps",
-               "ms_per_step": dc["ms_per_step"], "gbs": dc["gbs"],
-               "frac_hbm": dc["gbs"] / HBM_PEAK_GBS, "bytes_per_step": dc["bytes"],
-               "traffic": measured_traffic("recurrent_step_kernel<bf16,128,128,channel>")}
-        out["decode"] = dec
-        if ch is None:
-            out["value"] = dc["gbs"]
-            out["unit"] = "GB/s"
-            out["ms_per_step"] = dc["ms_per_step"]
-            out["config"] = {"workload": dec["workload"]}
-            out["roofline"] = {"bound": "hbm", "achieved": dc["gbs"], "peak": HBM_PEAK_GBS,
-                               "unit": "GB/s", "frac": dc["gbs"] / HBM_PEAK_GBS,
-                               "traffic": dec["traffic"],
-                               "kernel": "recurrent_step_kernel<bf16,128,128,channel>"}
+        out["decode"] = bench_decode(torch, gdn, timer)
+        if out["value"] is None:
+            out["value"], out["unit"] = out["decode"]["gbs"], "GB/s"
+            out["ms_per_step"] = out["decode"]["ms_per_step"]
+            out["config"] = {"workload": out["decode"]["workload"]}
     if args.only in ("all", "verify"):
-        reps = max(3, min(args.steps, 50))
-        ver = [bench_verify(torch, gdn, 4, False, reps, 5), bench_verify(torch, gdn, 4, True, reps, 5)]
+        ver = [bench_verify(torch, gdn, timer, 4, False), bench_verify(torch, gdn, timer, 4, True)]
         if "decode" in out:
             for x in ver:   # the same tokens as M one-token decode steps
                 x["vs_single_steps"] = x["M"] * out["decode"]["ms_per_step"] / x["ms"]
         out["verify"] = ver
-    if args.only in ("all", "channel"):
-        out["channel"] = [bench_channel(torch, gdn, "channel_bf16", args.steps, min(args.warmup, 20)),
-                          bench_channel(torch, gdn, "channel_long", max(2, min(args.steps, 5)),
-                                        max(1, min(args.warmup, 3)))]
-        if ch is None and args.only == "channel":
-            first = out["channel"][0]
-            out["value"] = first["mtok_s"]
-            out["ms_per_step"] = first["ms"]
-            out["config"] = {"workload": first["workload"]}
     if args.only in ("all", "bwd"):
-        out["backward"] = bench_bwd(torch, gdn, max(2, min(args.steps, 20)), max(1, min(args.warmup, 5)))
-        if ch is None and args.only == "bwd":
-            out["value"] = out["backward"]["mtok_s_fwd_bwd"]
-            out["ms_per_step"] = out["backward"]["ms_fwd_bwd"]
-            out["config"] = {"workload": out["backward"]["workload"]}
+        out["backward"] = bench_bwd(torch, gdn, timer)
     if args.only in ("all", "prologue"):
-        # the chunk-mode launch settles only after a few dozen launches on fresh
-        # buffers: warm up as long as the headline forward does
-        out["prologue"] = bench_prologue(torch, gdn, max(3, min(args.steps, 50)), max(1, min(args.warmup, 50)))
-        if ch is None and args.only == "prologue":
-            out["value"] = out["prologue"]["chunk"]["gbs"]
-            out["unit"] = "GB/s"
-            out["ms_per_step"] = out["prologue"]["chunk"]["ms"]
-            out["config"] = {"workload": out["prologue"]["chunk"]["workload"]}
-    if ch is not None and not args.no_cpu:
+        out["prologue"] = bench_prologue(torch, gdn, timer)
+    if head_in is not None and not args.no_cpu:
         torch.cuda.synchronize()
-        cb = cpu_baseline(ch["inputs"], ch["cfg"])
-        cb["cpu_model"] = platform.processor() or _cpu_model()
-        out["cpu_baseline"] = cb
+        out["cpu_baseline"] = cpu_baseline(head_in, head_cfg)
     print(json.dumps(out), flush=True)
-
-
-def _cpu_model():
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return "unknown"
 
 
 if __name__ == "__main__":

@@ -7,6 +7,8 @@ fallback: if ``libgdn.so`` has not been built, every call raises.
 
 Entry points (same names as the C ABI):
     gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk=64)
+    gdn_chunk_fwd_ws(q, k, v, g, beta, S0, o, S_T, workspace, chunk=64)
+    gdn_chunk_fwd_workspace_size(B, T, H, K, V, dtype, gate, want_o) -> bytes
     gdn_recurrent_step(q, k, v, g, beta, S, o)
     gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist)
     gdn_chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace)
@@ -35,7 +37,7 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_HEAD, GDN_GATE_CHANNEL = 0, 1
 GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 _ACTS = {"none": GDN_ACT_NONE, "silu": GDN_ACT_SILU}
-SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_steps",
+SYMBOLS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd_ws", "gdn_recurrent_step", "gdn_recurrent_steps",
            "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_prologue",
            "gdn_recurrent_step_prologue", "gdn_status_str", "gdn_abi_version")
 
@@ -71,6 +73,11 @@ def lib() -> ctypes.CDLL:
                                           i, i, i, i, i, i, i, vp]
         L.gdn_recurrent_steps.restype = i
         sz = ctypes.c_size_t
+        L.gdn_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+        L.gdn_chunk_fwd_workspace_size.restype = i
+        L.gdn_chunk_fwd_ws.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, sz,
+                                       i, i, i, i, i, i, i, i, vp]
+        L.gdn_chunk_fwd_ws.restype = i
         L.gdn_chunk_bwd_workspace_size.argtypes = [i, i, i, i, i, i, ctypes.POINTER(sz)]
         L.gdn_chunk_bwd_workspace_size.restype = i
         L.gdn_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp,
@@ -132,13 +139,8 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk: int = 64, stream=None) -> None:
-    """Chunkwise forward; writes o [B,T,H,V] and/or S_T [B,H,K,V] (either may be None).
-
-    q, k [B,T,H,K] and v [B,T,H,V] share a dtype (fp32 or bf16); g is [B,T,H] (scalar
-    gate) or [B,T,H,K] (per key channel), fp32; beta [B,T,H] fp32; S0 [B,H,K,V] fp32
-    or None.  S_T may be S0 (in place).  Enqueued on the current torch stream.
-    """
+def _chunk_fwd_args(q, k, v, g, beta, S0, o, S_T):
+    """Check the tensors of a chunkwise forward; returns (B, T, H, K, V, gate)."""
     import torch
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, T, H, D]")
@@ -161,11 +163,54 @@ def gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk: int = 64, stream=None) ->
     _check(S0, "S0", (B, H, K, V), torch.float32, dev)
     _check(o, "o", (B, T, H, V), dt, dev)
     _check(S_T, "S_T", (B, H, K, V), torch.float32, dev)
+    return B, T, H, K, V, gate
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk: int = 64, stream=None) -> None:
+    """Chunkwise forward; writes o [B,T,H,V] and/or S_T [B,H,K,V] (either may be None).
+
+    q, k [B,T,H,K] and v [B,T,H,V] share a dtype (fp32 or bf16); g is [B,T,H] (scalar
+    gate) or [B,T,H,K] (per key channel), fp32; beta [B,T,H] fp32; S0 [B,H,K,V] fp32
+    or None.  S_T may be S0 (in place).  Enqueued on the current torch stream.
+    """
+    B, T, H, K, V, gate = _chunk_fwd_args(q, k, v, g, beta, S0, o, S_T)
     rc = lib().gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
                              _ptr(o), _ptr(S_T), B, T, H, K, V, int(chunk),
                              _dtype_code(q), gate, _stream(stream))
     if rc != GDN_OK:
         raise GDNError(rc, "gdn_chunk_fwd")
+
+
+def gdn_chunk_fwd_workspace_size(B: int, T: int, H: int, K: int, V: int, dtype, gate: int,
+                                 want_o: bool, chunk: int = 64) -> int:
+    """Bytes of workspace gdn_chunk_fwd_ws needs (0: none).  dtype is a torch dtype
+    or GDN_F32 / GDN_BF16; gate GDN_GATE_HEAD or GDN_GATE_CHANNEL."""
+    if not isinstance(dtype, int):
+        import torch
+        dtype = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    n = ctypes.c_size_t(0)
+    rc = lib().gdn_chunk_fwd_workspace_size(int(B), int(T), int(H), int(K), int(V), int(chunk),
+                                            int(dtype), int(gate), int(bool(want_o)),
+                                            ctypes.byref(n))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd_workspace_size")
+    return int(n.value)
+
+
+def gdn_chunk_fwd_ws(q, k, v, g, beta, S0, o, S_T, workspace, chunk: int = 64,
+                     stream=None) -> None:
+    """gdn_chunk_fwd with a workspace (a uint8 device tensor, or None when
+    gdn_chunk_fwd_workspace_size is 0): a final-state-only call may then run
+    the sequence-parallel form."""
+    B, T, H, K, V, gate = _chunk_fwd_args(q, k, v, g, beta, S0, o, S_T)
+    if workspace is not None:
+        _check(workspace, "workspace", device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().gdn_chunk_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                                _ptr(o), _ptr(S_T), _ptr(workspace), nbytes, B, T, H, K, V,
+                                int(chunk), _dtype_code(q), gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd_ws")
 
 
 def gdn_recurrent_step(q, k, v, g, beta, S, o, stream=None) -> None:
@@ -307,14 +352,24 @@ def chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T, want_dS0: bool = True, workspace=
     return out
 
 
-def chunk_fwd(q, k, v, g, beta, S0=None, want_o: bool = True, chunk: int = 64, stream=None):
-    """Allocate o (if wanted) and S_T, run gdn_chunk_fwd, return (o, S_T)."""
+def chunk_fwd(q, k, v, g, beta, S0=None, want_o: bool = True, chunk: int = 64, stream=None,
+              workspace=None):
+    """Allocate o (if wanted), S_T and, when the call can use one, a workspace;
+    run gdn_chunk_fwd_ws; return (o, S_T).  workspace=False forces gdn_chunk_fwd
+    (no workspace, the sequential kernels)."""
     import torch
     B, T, H, K = q.shape
     V = v.shape[-1]
     o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device) if want_o else None
     S_T = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
-    gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk=chunk, stream=stream)
+    if workspace is False:
+        gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk=chunk, stream=stream)
+        return o, S_T
+    if workspace is None:
+        gate = GDN_GATE_CHANNEL if g.dim() == 4 else GDN_GATE_HEAD
+        n = gdn_chunk_fwd_workspace_size(B, T, H, K, V, q.dtype, gate, want_o, chunk)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
+    gdn_chunk_fwd_ws(q, k, v, g, beta, S0, o, S_T, workspace, chunk=chunk, stream=stream)
     return o, S_T
 
 

@@ -1,0 +1,675 @@
+// chunk_fwd_seg.hip -- sequence-parallel chunkwise forward for the final state
+// only: bf16 operands, the per-key-channel gate, K = V = 128.
+//
+// Mathematics (Atomic-GDN2 model card, section 2.1, the recurrence; the
+// chunkwise mode of the MindPattern "Gated DeltaNet" page).  A chunk maps the
+// state affinely, S' = M S + N, and so does any run of chunks; maps compose
+// associatively (the card's kernel benchmark, section 5.1, compares against an
+// associative scan of the same recurrence).  A long sequence is cut into
+// segments of whole chunks that run at the same time:
+//
+//   segment 0 runs the recurrence from the true S0 and leaves its final state
+//   in S_T;  every later segment s runs the same chunk recurrence on the
+//   augmented state [N | M] (K x (V + K)), started from [0 | I]: the value
+//   columns see the segment's v, the K extra columns see v = 0, so at the end
+//   N_s is the state the segment reaches from zero and M_s the matrix that
+//   carries any incoming state through it.
+//
+// A second kernel then walks the segments of each head in order,
+// S <- M_s S + N_s, in fp32, and writes S_T.
+//
+// Per chunk (n <= 64 tokens, per key channel c; block b = 16 tokens):
+//   lambda_tc  running sum of g_c from the start of t's block (>= -80 for g >= -5)
+//   E_bc       e^{block total}, R_b = sum of the blocks before b, gn = chunk total
+//   KL = k e^{lambda}, KI = k e^{-lambda}          (Gram operands, in range)
+//   K+ = KL e^{R_b} = k e^{gamma},  K- = KI e^{gn - R_b} = k e^{gn - gamma}  (<= 1)
+//   A_ij = diag(beta_i) KL_i (KI_j F_ij)^T,  F_ij = E_j ... E_{i-1}  (j < i)
+//   (I + A) D = diag(beta)(V - K+ S),   S' = Diag(e^{gn}) S + K-^T D
+// with V = 0 in the columns of M.
+//
+// Work split: one workgroup of 8 waves per (head, segment).  Prep waves 4..7
+// get chunk n + 1 ready while chain waves 0..3 run chunk n.  Prep wave p owns
+// key block p (keys 32p .. 32p+31) of all 64 tokens, so the running sums, the
+// block factors and the four scaled tiles of its keys are computed without any
+// other wave; after the four prep waves have met (an LDS arrival counter), each
+// computes its share of the Gram blocks and one diagonal inverse.  Chain wave w
+// owns 64 columns of the augmented state (w = 0, 1: value columns; w = 2, 3:
+// columns of M, idle in segment 0) in MFMA accumulators for the whole segment;
+// per chunk it forms D one 16-column tile at a time and updates the state two
+// tiles (32 columns) at a time, so that the k^T fragments are read twice per
+// chunk and the registers stay within the two-waves-per-SIMD budget.  One workgroup barrier per
+// chunk hands the chunk's data over; the chain's data is double-buffered.
+#include "ws_common.h"
+#include <type_traits>
+
+namespace gdn {
+
+constexpr int SG_T = 64;        // tokens per chunk
+constexpr int SG_K = 128;       // keys = value columns
+constexpr int SG_NTHR = 512;    // 4 chain waves + 4 prep waves
+
+constexpr int sg_al(int x) { return (x + 255) & ~255; }
+
+struct SgSmem {
+    static constexpr int RB = SG_K * 2;          // bytes per tile row
+    static constexpr int TILE = SG_T * RB;       // one 64 x 128 bf16 tile
+    static constexpr int LDC = SG_T + 8;         // row length of -A (bf16, fragment order)
+    static constexpr int LDD = 16;               // row length of T_ii
+    // prep buffer (one): KL, KI, block factors E [4][K], per-wave 16 x 16 fp32 scratch
+    static constexpr int pKL = 0, pKI = TILE, pE = 2 * TILE, pAd = pE + 4 * SG_K * 4;
+    static constexpr int PREP = sg_al(pAd + 4 * 256 * 4);
+    // hand-over buffers (two): what the chain reads for one chunk
+    static constexpr int hKP = 0, hKM = TILE, hV = 2 * TILE, hAn = 3 * TILE;
+    static constexpr int hTd = hAn + 48 * LDC * 2;
+    static constexpr int hBeta = hTd + SG_T * LDD * 2;
+    static constexpr int hEgn = hBeta + SG_T * 4;
+    static constexpr int HBUF = sg_al(hEgn + SG_K * 4);
+    static constexpr int oH = PREP;
+    static constexpr int kCtr = oH + 2 * HBUF;
+    static constexpr int bytes = sg_al(kCtr + 16);
+    static_assert(bytes <= 160 * 1024, "LDS budget");
+};
+
+// Byte offset of the 16-byte chunk `ch` of row `row` of a 64 x 128 bf16 tile:
+// the chunk index is XORed with the row's low four bits in swapped halves, so
+// that the 16-row fragment reads and the transposed reads hit distinct banks.
+__device__ __forceinline__ int sg_off(int row, int ch) {
+    return row * 256 + ((ch ^ (((row & 3) << 2) | ((row >> 2) & 3))) << 4);
+}
+__device__ __forceinline__ Frag<__bf16> sg_frag(const char *M, int row0, int kb) {
+    return {*reinterpret_cast<const bf16x8 *>(M + sg_off(row0 + lane_r16(), 4 * kb + lane_gq()))};
+}
+
+// 8 bf16 times 8 fp32 factors (fp32 arithmetic), as 8 fp32.
+__device__ __forceinline__ void unpack8(bf16x8 x, f32x4 &lo, f32x4 &hi) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lo[e] = (float)x[e];
+        hi[e] = (float)x[4 + e];
+    }
+}
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) { return cat8(cvt4(lo), cvt4(hi)); }
+
+struct SgArgs {
+    const __bf16 *k, *v;
+    const float *g, *beta, *S0;
+    float *S_T;       // segment 0 leaves its final state here
+    float *mapN;      // [B*H][nseg-1][K][V]
+    float *mapM;      // [B*H][nseg-1][K][K]
+    int T, H, nseg, seg_len;
+};
+
+__global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
+{
+    using L = SgSmem;
+    constexpr int K = SG_K;
+    constexpr int NKB = K / 32;
+
+    extern __shared__ __attribute__((aligned(256))) char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r16 = lane & 15;
+    const int gq = lane >> 4;
+
+    const int T = a.T, H = a.H;
+    const int bh = blockIdx.x / a.nseg, seg = blockIdx.x % a.nseg;
+    const int b = bh / H, h = bh % H;
+    const long row_base = (long)b * T * H + h;   // row of token 0 in [B*T*H]
+    const int nchunks = (T + SG_T - 1) / SG_T;
+    const int c0 = seg * a.seg_len, c1 = min(nchunks, c0 + a.seg_len);
+
+    auto hbuf = [&](int c) { return smem + L::oH + (c & 1) * L::HBUF; };
+    char *sKL = smem + L::pKL;
+    char *sKI = smem + L::pKI;
+    float *sE = reinterpret_cast<float *>(smem + L::pE);
+    unsigned *ctr = reinterpret_cast<unsigned *>(smem + L::kCtr);
+    if (tid == 0) *ctr = 0u;
+    lds_barrier();
+
+    if (wave >= 4) {
+        // ============================ prep waves ============================
+        const int pw = __builtin_amdgcn_readfirstlane(wave - 4);   // key block of this wave
+        // This lane: rows 16 rt + r16 of the chunk, keys 32 pw + 8 gq .. +7.
+        unsigned loff[4], boff[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            boff[rt] = (unsigned)((16 * rt + r16) * H);
+            loff[rt] = boff[rt] * (unsigned)K + (unsigned)(32 * pw + 8 * gq);
+        }
+        // v copies: instruction i fills rows 16 pw + 4 i .. +3 (lane l: row
+        // + l / 16, physical slot l % 16, holding logical chunk slot ^ swizzle)
+        unsigned voff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * pw + 4 * i + (lane >> 4), slot = lane & 15;
+            const int ch = slot ^ (((row & 3) << 2) | ((row >> 2) & 3));
+            voff[i] = 2u * (unsigned)(row * H * K + 8 * ch);
+        }
+
+        struct Raw {
+            bf16x8 k[4];
+            f32x4 g[4][2];
+            float b[4];
+        };
+        // Loads of chunk n: always the same number of memory instructions
+        // (rows past T read row T-1 and are zeroed: g = beta = k = 0 there,
+        // an identity step).
+        auto fetch = [&](int n, Raw &r) __attribute__((always_inline)) {
+            const int t0 = n * SG_T;
+            const int nlive = T - t0;                        // rows of this chunk inside T
+            const long rbase = row_base + (long)t0 * H;      // wave-uniform
+            const __bf16 *kb = a.k + rbase * K;
+            const float *gb = a.g + rbase * K;
+            const float *bb = a.beta + rbase;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int row = 16 * rt + r16;
+                const bool live = row < nlive;
+                const unsigned lo = live ? loff[rt] : (unsigned)((nlive - 1) * H * K + 32 * pw + 8 * gq);
+                const unsigned bo = live ? boff[rt] : (unsigned)((nlive - 1) * H);
+                r.k[rt] = *reinterpret_cast<const bf16x8 *>(kb + lo);
+                r.g[rt][0] = *reinterpret_cast<const f32x4 *>(gb + lo);
+                r.g[rt][1] = *reinterpret_cast<const f32x4 *>(gb + lo + 4);
+                r.b[rt] = bb[bo];
+            }
+        };
+        auto zero_dead = [&](int n, Raw &r) __attribute__((always_inline)) {
+            const int nlive = T - n * SG_T;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if (16 * rt + r16 >= nlive) {
+                    r.k[rt] = bf16x8{};
+                    r.g[rt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    r.g[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    r.b[rt] = 0.f;
+                }
+            }
+        };
+        auto copy_v = [&](int n) __attribute__((always_inline)) {
+            char *dst = hbuf(n) + L::hV + 16 * pw * L::RB;
+            const int t0 = n * SG_T;
+            if (t0 + SG_T <= T) {
+                const __bf16 *vb = a.v + (row_base + (long)t0 * H) * K;   // wave-uniform
+#pragma unroll
+                for (int i = 0; i < 4; ++i) g2lds16s(vb, voff[i], dst + 4 * i * L::RB);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * pw + 4 * i + (lane >> 4), slot = lane & 15;
+                    const int ch = slot ^ (((row & 3) << 2) | ((row >> 2) & 3));
+                    const int t = min(t0 + row, T - 1);
+                    g2lds16(a.v + (row_base + (long)t * H) * K + 8 * ch, dst + 4 * i * L::RB);
+                }
+            }
+        };
+
+        unsigned arrivals = 0;
+        // Chunk n from its raw loads r; issues the v copies of chunk n and the
+        // loads of chunk n + 1 (into nx) first.
+        Raw r, nx;
+        auto prepare = [&](int n) __attribute__((always_inline)) {
+            char *Hb = hbuf(n);
+            // The loads of chunk n (issued a period ago) are complete before the
+            // v copies go out.  A compiler-visible wait: the compiler's own wait
+            // for them would otherwise count the untracked copies too.
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            r = nx;
+            zero_dead(n, r);
+            copy_v(n);
+
+            // Forward over the four token blocks: lambda (4 DPP scan steps over
+            // the block's 16 rows), e^{+-lambda}, the block factor E_rt (row 15),
+            // and the tiles KL, KI and K+ = KL e^{R_rt} (R_rt: the blocks before).
+            f32x4 E[4][2], ki[4][2];
+            f32x4 ER0 = {1.f, 1.f, 1.f, 1.f}, ER1 = ER0;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 lam[2] = {r.g[rt][0], r.g[rt][1]};
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = lam[hh][e];
+                            lam[hh][e] = x + (st == 0 ? dpp_shr<0x111>(x) : st == 1 ? dpp_shr<0x112>(x)
+                                              : st == 2 ? dpp_shr<0x114>(x) : dpp_shr<0x118>(x));
+                        }
+                f32x4 el[2], ei[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = lam[hh][e] * 1.44269504088896341f;
+                        el[hh][e] = __builtin_amdgcn_exp2f(x);
+                        ei[hh][e] = __builtin_amdgcn_exp2f(-x);
+                        E[rt][hh][e] = lane_in_row<15>(el[hh][e]);
+                    }
+                f32x4 k0, k1;
+                unpack8(r.k[rt], k0, k1);
+                const f32x4 kl0 = k0 * el[0], kl1 = k1 * el[1];
+                ki[rt][0] = k0 * ei[0];
+                ki[rt][1] = k1 * ei[1];
+                const int off = sg_off(16 * rt + r16, 4 * pw + gq);
+                *reinterpret_cast<bf16x8 *>(sKL + off) = pack8(kl0, kl1);
+                *reinterpret_cast<bf16x8 *>(sKI + off) = pack8(ki[rt][0], ki[rt][1]);
+                *reinterpret_cast<bf16x8 *>(Hb + L::hKP + off) = pack8(kl0 * ER0, kl1 * ER1);
+                ER0 *= E[rt][0];
+                ER1 *= E[rt][1];
+            }
+            // Backward: K- = KI e^{gn - R_rt} = KI E_rt ... E_3; e^{gn} at the end.
+            {
+                f32x4 ES0 = {1.f, 1.f, 1.f, 1.f}, ES1 = ES0;
+#pragma unroll
+                for (int rt = 3; rt >= 0; --rt) {
+                    ES0 *= E[rt][0];
+                    ES1 *= E[rt][1];
+                    *reinterpret_cast<bf16x8 *>(Hb + L::hKM + sg_off(16 * rt + r16, 4 * pw + gq)) =
+                        pack8(ki[rt][0] * ES0, ki[rt][1] * ES1);
+                }
+                if (r16 == 0) {
+                    float *go = reinterpret_cast<float *>(Hb + L::hEgn) + 32 * pw + 8 * gq;
+                    *reinterpret_cast<f32x4 *>(go) = ES0;
+                    *reinterpret_cast<f32x4 *>(go + 4) = ES1;
+                }
+            }
+            if (r16 == 0) {
+                float *eo = sE + 32 * pw + 8 * gq;
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    *reinterpret_cast<f32x4 *>(eo + rt * K) = E[rt][0];
+                    *reinterpret_cast<f32x4 *>(eo + rt * K + 4) = E[rt][1];
+                }
+            }
+            if (pw == 0 && gq == 0) {
+                float *bo = reinterpret_cast<float *>(Hb + L::hBeta);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) bo[16 * rt + r16] = r.b[rt];
+            }
+            // the next chunk's loads go in flight behind the v copies
+            if (n + 1 < c1) fetch(n + 1, nx);
+            arrivals += 4;
+            prep_barrier(ctr, arrivals);   // KL, KI, E and beta of every key block written
+
+            // ---- Gram blocks of chunk n: the diagonal block pw with its inverse,
+            // then off-diagonal blocks (I, J), computed transposed (rows s of
+            // block J, columns t of block I):
+            //   p0: (1,0) (3,0)   p1: (2,1) (3,1)   p2: (3,2)   p3: (2,0)
+            __bf16 *sAn = reinterpret_cast<__bf16 *>(Hb + L::hAn);
+            const float *sB = reinterpret_cast<const float *>(Hb + L::hBeta);
+            float *sAd = reinterpret_cast<float *>(smem + L::pAd) + pw * 256;
+            {
+                Frag<__bf16> fi[NKB], fl[NKB];
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    fi[kb] = sg_frag(sKI, 16 * pw, kb);
+                    fl[kb] = sg_frag(sKL, 16 * pw, kb);
+                }
+                f32x4 aA = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) aA = mma(aA, fi[kb], fl[kb]);
+                const int t = 16 * pw + r16, s0 = 16 * pw + 4 * gq;
+                const float bt = sB[t];
+                f32x4 na;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) na[e] = (s0 + e < t) ? -bt * aA[e] : 0.f;
+                *reinterpret_cast<f32x4 *>(sAd + r16 * 16 + 4 * gq) = na;
+                const f32x4 tr = unit_lower_inverse16_rows(sAd);
+                *reinterpret_cast<bf16x4 *>(reinterpret_cast<__bf16 *>(Hb + L::hTd) +
+                                            (16 * pw + (lane >> 2)) * L::LDD + 4 * (lane & 3)) = cvt4(tr);
+            }
+            auto pairs = [&](auto i1c, auto i2c, auto jc) __attribute__((always_inline)) {
+                constexpr int I1 = decltype(i1c)::value, I2 = decltype(i2c)::value, J = decltype(jc)::value;
+                constexpr int IM = I2 > 0 ? I2 : I1;       // E rows J .. IM-1 are needed
+                constexpr int NH = NKB / 2;
+                f32x4 aA1 = {0.f, 0.f, 0.f, 0.f}, aA2 = aA1;
+#pragma unroll
+                for (int hb = 0; hb < NKB; hb += NH) {
+                    Frag<__bf16> fa[NH], fk1[NH], fk2[NH];
+                    f32x4 Ef[NH][IM - J][2];
+#pragma unroll
+                    for (int i = 0; i < NH; ++i) {
+                        const int kb = hb + i;
+                        fa[i] = sg_frag(sKI, 16 * J, kb);
+                        fk1[i] = sg_frag(sKL, 16 * I1, kb);
+                        if constexpr (I2 > 0) fk2[i] = sg_frag(sKL, 16 * I2, kb);
+#pragma unroll
+                        for (int bb = J; bb < IM; ++bb) {
+                            const float *F = sE + bb * K + 32 * kb + 8 * gq;
+                            Ef[i][bb - J][0] = *reinterpret_cast<const f32x4 *>(F);
+                            Ef[i][bb - J][1] = *reinterpret_cast<const f32x4 *>(F + 4);
+                        }
+                    }
+                    GDN_SCHED_FENCE();
+#pragma unroll
+                    for (int i = 0; i < NH; ++i) {
+                        f32x4 f0 = Ef[i][0][0], f1 = Ef[i][0][1];
+#pragma unroll
+                        for (int bb = J + 1; bb < I1; ++bb) {
+                            f0 *= Ef[i][bb - J][0];
+                            f1 *= Ef[i][bb - J][1];
+                        }
+                        f32x4 x0, x1;
+                        unpack8(fa[i].v, x0, x1);
+                        aA1 = mma(aA1, Frag<__bf16>{pack8(x0 * f0, x1 * f1)}, fk1[i]);
+                        if constexpr (I2 > 0) {
+#pragma unroll
+                            for (int bb = I1; bb < I2; ++bb) {
+                                f0 *= Ef[i][bb - J][0];
+                                f1 *= Ef[i][bb - J][1];
+                            }
+                            aA2 = mma(aA2, Frag<__bf16>{pack8(x0 * f0, x1 * f1)}, fk2[i]);
+                        }
+                    }
+                }
+                const int s0 = 16 * J + 4 * gq;
+                {
+                    const int t = 16 * I1 + r16;
+                    *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * L::LDC + frag_col(s0)) = cvt4(aA1 * -sB[t]);
+                }
+                if constexpr (I2 > 0) {
+                    const int t = 16 * I2 + r16;
+                    *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * L::LDC + frag_col(s0)) = cvt4(aA2 * -sB[t]);
+                }
+            };
+            using std::integral_constant;
+            if (pw == 0) pairs(integral_constant<int, 1>(), integral_constant<int, 3>(), integral_constant<int, 0>());
+            else if (pw == 1) pairs(integral_constant<int, 2>(), integral_constant<int, 3>(), integral_constant<int, 1>());
+            else if (pw == 2) pairs(integral_constant<int, 3>(), integral_constant<int, 0>(), integral_constant<int, 2>());
+            else pairs(integral_constant<int, 2>(), integral_constant<int, 0>(), integral_constant<int, 0>());
+            // the v copies of chunk n landed before the hand-over barrier; the
+            // 16 loads of chunk n + 1 issued after them may stay in flight
+            if (n + 1 < c1) wait_vm<16>();
+            else wait_vm<0>();
+        };
+
+        if (c0 < c1) {
+            fetch(c0, nx);
+            prepare(c0);
+            lds_barrier();                      // chunk c0 is ready
+        }
+        for (int c = c0; c < c1; ++c) {
+            if (c + 1 < c1) prepare(c + 1);
+            lds_barrier();
+        }
+        wait_vm<0>();   // nothing in flight at exit
+        return;
+    }
+
+    // ============================= chain waves =============================
+    // Column group cg (16 columns) of this wave: augmented column 64 wave +
+    // 16 cg + r16 (below 128: value columns; from 128: columns of M).
+    // Accumulator S[cg][ct], ct = 2 kb + hh, element e holds the row of key
+    // 32 kb + 8 gq + 4 hh + e.
+    const int cw = wave;
+    const bool mcols = cw >= 2;
+    const bool active = seg > 0 || !mcols;
+    auto key_of = [&](int ct, int e) { return 32 * (ct >> 1) + 8 * gq + 4 * (ct & 1) + e; };
+    f32x4 S[4][8];
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+        const int col = 64 * cw + 16 * cg + r16;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x = 0.f;
+                if (seg == 0) {
+                    if (!mcols && a.S0) x = a.S0[((long)bh * K + key_of(ct, e)) * K + col];
+                } else if (mcols) {
+                    x = key_of(ct, e) == col - K ? 1.f : 0.f;
+                }
+                S[cg][ct][e] = x;
+            }
+    }
+
+    // per-lane LDS offsets that do not change between chunks
+    const int trow = 4 * gq + (r16 >> 2), tq = r16 & 3;
+    int k_tr[NKB];
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) k_tr[kk] = sg_off(trow, 4 * kk + tq);
+    int v_tr[4];
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) v_tr[cg] = sg_off(trow, 2 * (4 * cw + cg) + (tq >> 1)) + 8 * (tq & 1);
+
+    if (c0 < c1) lds_barrier();             // chunk c0 is ready
+
+    for (int c = c0; c < c1; ++c) {
+        if (active) {
+            const char *Hb = hbuf(c);
+            const char *sKP = Hb + L::hKP;
+            const unsigned vbase = lds_u32(Hb + L::hV);
+            const __bf16 *sAn = reinterpret_cast<const __bf16 *>(Hb + L::hAn);
+            const __bf16 *sTd = reinterpret_cast<const __bf16 *>(Hb + L::hTd);
+            const float *sBeta = reinterpret_cast<const float *>(Hb + L::hBeta);
+            const float *sEgn = reinterpret_cast<const float *>(Hb + L::hEgn);
+            unsigned ktr_addr[NKB];
+#pragma unroll
+            for (int kk = 0; kk < NKB; ++kk) ktr_addr[kk] = opaque(lds_u32(Hb + L::hKM) + k_tr[kk]);
+
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                // Phases A and B, one 16-column tile at a time: K+ S, then
+                // X = diag(beta)(V - K+ S) (V = 0 in the columns of M) and
+                // (I + A) D = X by block forward substitution (-A stored).
+                Frag<__bf16> Df[2][2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int cg = 2 * half + j;
+                    Frag<__bf16> Sf[NKB];
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) Sf[kb] = reg_frag<__bf16>(S[cg][2 * kb], S[cg][2 * kb + 1]);
+                    f32x4 X[4];
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        Frag<__bf16> fk[NKB];
+#pragma unroll
+                        for (int kb = 0; kb < NKB; ++kb) fk[kb] = sg_frag(sKP, 16 * rt, kb);
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kb = 0; kb < NKB; ++kb) acc = mma(acc, fk[kb], Sf[kb]);
+                        X[rt] = acc;
+                    }
+                    GDN_SCHED_FENCE();
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        const f32x4 bt = *reinterpret_cast<const f32x4 *>(sBeta + 16 * rt + 4 * gq);
+                        if (!mcols) {
+                            const bf16x4 vv = lds_read_tr(vbase + v_tr[cg] + 16 * rt * L::RB);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) X[rt][e] = bt[e] * ((float)vv[e] - X[rt][e]);
+                        } else {
+                            X[rt] = -(bt * X[rt]);
+                        }
+                    }
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    f32x4 Dd[4];
+                    Dd[0] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 0, 0), reg_frag<__bf16>(X[0], z));
+                    f32x4 Y = mma_lo(X[1], lds_frag_fo_lo(sAn, L::LDC, 0, 0), reg_frag<__bf16>(Dd[0], z));
+                    Dd[1] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 16, 0), reg_frag<__bf16>(Y, z));
+                    Df[j][0] = reg_frag<__bf16>(Dd[0], Dd[1]);
+                    Y = mma(X[2], lds_frag_fo(sAn, L::LDC, 16, 0), Df[j][0]);
+                    f32x4 Y3 = mma(X[3], lds_frag_fo(sAn, L::LDC, 32, 0), Df[j][0]);
+                    Dd[2] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 32, 0), reg_frag<__bf16>(Y, z));
+                    Y3 = mma_lo(Y3, lds_frag_fo_lo(sAn, L::LDC, 32, 32), reg_frag<__bf16>(Dd[2], z));
+                    Dd[3] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 48, 0), reg_frag<__bf16>(Y3, z));
+                    Df[j][1] = reg_frag<__bf16>(Dd[2], Dd[3]);
+                    GDN_SCHED_FENCE();
+                }
+
+                // Phase D: S' = Diag(e^{gn}) S + K-^T D for the columns of this half
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) {
+                    const unsigned pk = ktr_addr[ct >> 1] + 8 * (ct & 1);
+                    bf16x4 kt[4];
+#pragma unroll
+                    for (int kb2 = 0; kb2 < 2; ++kb2) {
+                        kt[2 * kb2] = lds_read_tr(pk + L::RB * 32 * kb2);
+                        kt[2 * kb2 + 1] = lds_read_tr(pk + L::RB * (32 * kb2 + 16));
+                    }
+                    const f32x4 eg = *reinterpret_cast<const f32x4 *>(sEgn + key_of(ct, 0));
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        f32x4 s = S[2 * half + j][ct] * eg;
+#pragma unroll
+                        for (int kb2 = 0; kb2 < 2; ++kb2)
+                            s = mma(s, Frag<__bf16>{cat8(kt[2 * kb2], kt[2 * kb2 + 1])}, Df[j][kb2]);
+                        S[2 * half + j][ct] = s;
+                    }
+                }
+                GDN_SCHED_FENCE();
+            }
+        }
+        lds_barrier();
+    }
+
+    if (!active) return;
+    float *dst;
+    int ld;
+    if (seg == 0) {
+        dst = a.S_T + (long)bh * K * K;
+        ld = K;
+    } else {
+        const long slot = (long)bh * (a.nseg - 1) + (seg - 1);
+        dst = (mcols ? a.mapM : a.mapN) + slot * K * K;
+        ld = K;
+    }
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+        const int col = (64 * cw + 16 * cg + r16) & (K - 1);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[key_of(ct, e) * ld + col] = S[cg][ct][e];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: for each head, S <- M_s S + N_s over segments s = 1 .. nseg-1 in
+// order, starting from segment 0's final state in S_T; fp32 matrix cores
+// (16 x 16 x 4).  One workgroup of 4 waves per (head, 16 value columns): wave
+// w computes rows 32 w .. 32 w + 31; the state block lives in LDS between steps.
+struct SgCombArgs {
+    const float *mapN, *mapM;
+    float *S_T;
+    int nseg, xcd_map;
+    long nbh;
+};
+
+__global__ __launch_bounds__(256) void seg_combine_kernel(SgCombArgs a)
+{
+    constexpr int K = SG_K, V = SG_K, NCB = V / 16, LDS_LD = 16 + 4;
+    __shared__ float sS[K * LDS_LD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, gq = lane >> 4;
+    long bh;
+    int cb;
+    {
+        const long w = blockIdx.x;
+        if (a.xcd_map) {   // the column blocks of one head on one XCD (shared M_s in its L2)
+            const long xcd = w & 7, slot = w >> 3;
+            cb = (int)(slot % NCB);
+            bh = (slot / NCB) * 8 + xcd;
+        } else {
+            bh = w / NCB;
+            cb = (int)(w % NCB);
+        }
+    }
+    float *ST = a.S_T + bh * K * V;
+    for (int i = tid; i < K * 16; i += 256) sS[(i >> 4) * LDS_LD + (i & 15)] = ST[(i >> 4) * V + 16 * cb + (i & 15)];
+    __syncthreads();
+    const int col = 16 * cb + r16;
+    for (int s = 1; s < a.nseg; ++s) {
+        const long slot = bh * (a.nseg - 1) + (s - 1);
+        const float *Mp = a.mapM + slot * K * K;
+        const float *Np = a.mapN + slot * K * V;
+        f32x4 acc[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rt][e] = Np[(32 * wave + 16 * rt + 4 * gq + e) * V + col];
+        f32x4 am[8][2];
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+                am[m][rt] = *reinterpret_cast<const f32x4 *>(Mp + (32 * wave + 16 * rt + r16) * K + 16 * m + 4 * gq);
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float bv = sS[(16 * m + 4 * gq + e) * LDS_LD + r16];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) acc[rt] = mfma_f32(am[m][rt][e], bv, acc[rt]);
+            }
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sS[(32 * wave + 16 * rt + 4 * gq + e) * LDS_LD + r16] = acc[rt][e];
+        __syncthreads();
+    }
+    for (int i = tid; i < K * 16; i += 256) ST[(i >> 4) * V + 16 * cb + (i & 15)] = sS[(i >> 4) * LDS_LD + (i & 15)];
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+// Segments per (b, h) for the sequence-parallel form, or 1 when the call should
+// run the sequential kernel: long sequences with too few heads to fill the
+// chip.  Enough segments for about three workgroups per CU of a 256-CU part,
+// at least 16 chunks per segment, at most 64 segments (the combine walks them
+// in order).
+int chunk_fwd_seg_count(long B, long T, long H)
+{
+    const long nch = (T + SG_T - 1) / SG_T;
+    const long bh = B * H;
+    if (bh <= 0 || nch <= 0 || bh * 2 >= 256) return 1;
+    long nseg = (768 + bh - 1) / bh;
+    nseg = nseg < nch / 16 ? nseg : nch / 16;
+    nseg = nseg < 64 ? nseg : 64;
+    if (nseg < 2) return 1;
+    // equal whole-chunk segments, none empty
+    const long len = (nch + nseg - 1) / nseg;
+    return (int)((nch + len - 1) / len);
+}
+
+unsigned long long chunk_fwd_seg_workspace(long B, long H, int nseg)
+{
+    if (nseg <= 1) return 0;
+    return (unsigned long long)B * H * (nseg - 1) * (2ull * SG_K * SG_K) * 4ull;
+}
+
+hipError_t chunk_fwd_seg_launch(const void *k, const void *v, const float *g, const float *beta,
+                                const float *S0, float *S_T, void *ws, int B, int T, int H, int nseg,
+                                hipStream_t st)
+{
+    using L = SgSmem;
+    static bool attr_set = false;  // benign race: every thread sets the same value
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_seg_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const long nch = (T + SG_T - 1) / SG_T;
+    const long bh = (long)B * H;
+    SgArgs a;
+    a.k = (const __bf16 *)k; a.v = (const __bf16 *)v; a.g = g; a.beta = beta; a.S0 = S0;
+    a.S_T = S_T;
+    a.seg_len = (int)((nch + nseg - 1) / nseg);
+    a.nseg = nseg;
+    a.mapN = (float *)ws;
+    a.mapM = a.mapN + bh * (nseg - 1) * SG_K * SG_K;
+    a.T = T; a.H = H;
+    hipLaunchKernelGGL(chunk_fwd_seg_kernel, dim3((unsigned)(bh * nseg)), dim3(SG_NTHR), L::bytes, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nseg == 1) return e;
+    SgCombArgs c;
+    c.mapN = a.mapN; c.mapM = a.mapM; c.S_T = S_T; c.nseg = nseg; c.nbh = bh;
+    c.xcd_map = bh % 8 == 0 ? 1 : 0;
+    hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(bh * (SG_K / 16))), dim3(256), 0, st, c);
+    return hipGetLastError();
+}
+
+} // namespace gdn

@@ -18,6 +18,11 @@ hipError_t recurrent_step_launch(bool bf16, bool channel, int K, int V, const vo
                                  const void *k, const void *v, const float *g,
                                  const float *beta, float *S, void *o, long nslices,
                                  hipStream_t st);
+int chunk_fwd_seg_count(long B, long T, long H);
+unsigned long long chunk_fwd_seg_workspace(long B, long H, int nseg);
+hipError_t chunk_fwd_seg_launch(const void *k, const void *v, const float *g, const float *beta,
+                                const float *S0, float *S_T, void *ws, int B, int T, int H, int nseg,
+                                hipStream_t st);
 hipError_t recurrent_multi_launch(bool bf16, bool channel, int K, int V, const void *q,
                                   const void *k, const void *v, const float *g,
                                   const float *beta, const float *S0, void *o, float *S_T,
@@ -56,42 +61,21 @@ long long prod(long long a, long long b, long long c = 1, long long d = 1) {
     return n;
 }
 
-// Size checks shared by gdn_chunk_bwd and its workspace query: EINVAL for
-// negative or overflowing sizes, ENOTSUP for shapes without a kernel or grids
-// past the launch limits; *nch = number of 64-token chunks over all slices.
-gdn_status bwd_sizes(int B, int T, int H, int K, int V, int chunk, long long *nch) {
-    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0 || chunk <= 0) return GDN_EINVAL;
-    const long long nqk = prod(B, T, H, K), nv = prod(B, T, H, V), nst = prod(B, H, K, V);
-    if (nqk < 0 || nv < 0 || nst < 0) return GDN_EINVAL;
-    if (!kv_supported(K) || !kv_supported(V) || chunk != 64) return GDN_ENOTSUP;
-    const long long n = prod(B, H, (T + 63) / 64);
-    const long long nvb = prod(B, H, V / gdn::BW_VB);
-    // one 256-thread workgroup per chunk / per value block: grid x * 256 < 2^32
-    if (n < 0 || nvb < 0 || n >= (1LL << 24) || nvb >= (1LL << 24)) return GDN_ENOTSUP;
-    *nch = n;
-    return GDN_OK;
+// The chunk kernels address a chunk's rows with 32-bit per-lane offsets from a
+// wave-uniform base: 64 rows of H * max(K, V) elements of at most 4 bytes must
+// stay below 2^31 bytes.
+bool chunk_offsets_fit(long long H, int K, int V) {
+    const long long w = K > V ? K : V;
+    const long long n = prod(64 * 4, H, w);
+    return n >= 0 && n < (1LL << 31);
 }
 
-} // namespace
-
-extern "C" {
-
-const char *gdn_status_str(gdn_status s) {
-    switch (s) {
-    case GDN_OK: return "ok";
-    case GDN_EINVAL: return "invalid argument";
-    case GDN_ENOTSUP: return "unsupported shape or type";
-    case GDN_EHIP: return "HIP launch failed";
-    }
-    return "unknown status";
-}
-
-int gdn_abi_version(void) { return GDN_ABI_VERSION; }
-
-gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
-                         const float *beta, const float *S0, void *o, float *S_T,
-                         int B, int T, int H, int K, int V, int chunk,
-                         gdn_dtype dtype, gdn_gate gate, void *stream)
+// Argument checks of the chunkwise forward (shared by gdn_chunk_fwd and
+// gdn_chunk_fwd_ws).  GDN_OK means a kernel exists for the call.
+gdn_status chunk_fwd_check(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *S0, const void *o, const float *S_T,
+                           int B, int T, int H, int K, int V, int chunk, gdn_dtype dtype,
+                           gdn_gate gate)
 {
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EINVAL;
     if (gate != GDN_GATE_HEAD && gate != GDN_GATE_CHANNEL) return GDN_EINVAL;
@@ -125,12 +109,125 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const floa
     if (!kv_supported(K) || !kv_supported(V) || chunk != 64) return GDN_ENOTSUP;
     if (dtype == GDN_F32 && K != 64) return GDN_ENOTSUP;
     if (prod(B, H, V / 64) > 0x7fffffffLL) return GDN_ENOTSUP;
+    if (!chunk_offsets_fit(H, K, V)) return GDN_ENOTSUP;
+    return GDN_OK;
+}
+
+// Segments of the sequence-parallel form for a chunkwise forward (1: the
+// sequential kernels) and the workspace it needs.  Only final-state calls with
+// bf16 operands, the per-key-channel gate and K = V = 128 take that form.
+int chunk_fwd_plan(int B, int T, int H, int K, int V, gdn_dtype dtype, gdn_gate gate, bool want_o,
+                   unsigned long long *bytes)
+{
+    *bytes = 0;
+    if (want_o || dtype != GDN_BF16 || gate != GDN_GATE_CHANNEL || K != 128 || V != 128) return 1;
+    const int nseg = gdn::chunk_fwd_seg_count(B, T, H);
+    *bytes = gdn::chunk_fwd_seg_workspace(B, H, nseg);
+    return nseg;
+}
+
+// Size checks shared by gdn_chunk_bwd and its workspace query: EINVAL for
+// negative or overflowing sizes, ENOTSUP for shapes without a kernel or grids
+// past the launch limits; *nch = number of 64-token chunks over all slices.
+gdn_status bwd_sizes(int B, int T, int H, int K, int V, int chunk, long long *nch) {
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0 || chunk <= 0) return GDN_EINVAL;
+    const long long nqk = prod(B, T, H, K), nv = prod(B, T, H, V), nst = prod(B, H, K, V);
+    if (nqk < 0 || nv < 0 || nst < 0) return GDN_EINVAL;
+    if (!kv_supported(K) || !kv_supported(V) || chunk != 64) return GDN_ENOTSUP;
+    if (!chunk_offsets_fit(H, K, V)) return GDN_ENOTSUP;
+    const long long n = prod(B, H, (T + 63) / 64);
+    const long long nvb = prod(B, H, V / gdn::BW_VB);
+    // one 256-thread workgroup per chunk / per value block: grid x * 256 < 2^32
+    if (n < 0 || nvb < 0 || n >= (1LL << 24) || nvb >= (1LL << 24)) return GDN_ENOTSUP;
+    *nch = n;
+    return GDN_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *gdn_status_str(gdn_status s) {
+    switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_EINVAL: return "invalid argument";
+    case GDN_ENOTSUP: return "unsupported shape or type";
+    case GDN_EHIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *S0, void *o, float *S_T,
+                         int B, int T, int H, int K, int V, int chunk,
+                         gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    const gdn_status st = chunk_fwd_check(q, k, v, g, beta, S0, o, S_T, B, T, H, K, V, chunk,
+                                          dtype, gate);
+    if (st != GDN_OK) return st;
     if (B == 0 || H == 0) return GDN_OK;
     if (!S_T && T == 0) return GDN_OK;  // nothing to write
 
     const hipError_t e = gdn::chunk_fwd_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL, K,
                                                q, k, v, g, beta, S0, o, S_T, B, T, H, V,
                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, int chunk,
+                                        gdn_dtype dtype, gdn_gate gate, int want_o,
+                                        size_t *bytes)
+{
+    if (!bytes) return GDN_EINVAL;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EINVAL;
+    if (gate != GDN_GATE_HEAD && gate != GDN_GATE_CHANNEL) return GDN_EINVAL;
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0 || chunk <= 0) return GDN_EINVAL;
+    if (prod(B, T, H, K > V ? K : V) < 0) return GDN_EINVAL;
+    if (!kv_supported(K) || !kv_supported(V) || chunk != 64) return GDN_ENOTSUP;
+    if (dtype == GDN_F32 && K != 64) return GDN_ENOTSUP;
+    if (prod(B, H, V / 64) > 0x7fffffffLL || !chunk_offsets_fit(H, K, V)) return GDN_ENOTSUP;
+    unsigned long long need = 0;
+    chunk_fwd_plan(B, T, H, K, V, dtype, gate, want_o != 0, &need);
+    *bytes = (size_t)need;
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd_ws(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *S0, void *o, float *S_T,
+                            void *workspace, size_t workspace_bytes,
+                            int B, int T, int H, int K, int V, int chunk,
+                            gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    const gdn_status st = chunk_fwd_check(q, k, v, g, beta, S0, o, S_T, B, T, H, K, V, chunk,
+                                          dtype, gate);
+    if (st != GDN_OK) return st;
+    unsigned long long need = 0;
+    const int nseg = chunk_fwd_plan(B, T, H, K, V, dtype, gate, o != nullptr, &need);
+    if (need > 0) {
+        if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return GDN_EINVAL;
+        // the workspace must not touch any input or output
+        const long long es = dtype == GDN_BF16 ? 2 : 4;
+        const long long nqk = prod(B, T, H, K), nv = prod(B, T, H, V), nst = prod(B, H, K, V);
+        const long long ng = gate == GDN_GATE_CHANNEL ? nqk : prod(B, T, H);
+        const Range rw = range(workspace, need);
+        const Range all[] = {range(q, nqk * es), range(k, nqk * es), range(v, nv * es),
+                             range(g, ng * 4), range(beta, prod(B, T, H) * 4),
+                             range(S0, S0 ? nst * 4 : 0), range(S_T, S_T ? nst * 4 : 0),
+                             range(o, o ? nv * es : 0)};
+        for (Range r : all)
+            if (overlap(rw, r)) return GDN_EINVAL;
+    }
+    if (B == 0 || H == 0) return GDN_OK;
+    if (!S_T && T == 0) return GDN_OK;
+    hipError_t e;
+    if (nseg > 1)
+        e = gdn::chunk_fwd_seg_launch(k, v, g, beta, S0, S_T, workspace, B, T, H, nseg,
+                                      static_cast<hipStream_t>(stream));
+    else
+        e = gdn::chunk_fwd_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL, K, q, k, v, g, beta,
+                                  S0, o, S_T, B, T, H, V, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
@@ -348,6 +445,10 @@ gdn_status gdn_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
             if (overlap(out[i], out[j])) return GDN_EINVAL;
     }
     if (!kv_supported(K) || !kv_supported(V)) return GDN_ENOTSUP;
+    // the per-channel chunk kernels split the decay at 16-token blocks, which
+    // keeps every factor in range for g >= -5 only: a larger cap would produce
+    // inputs they cannot take
+    if (ch && !(g_cap <= 5.f)) return GDN_ENOTSUP;
     // one thread per token and 8 channels (at most 16 per token): the grid's
     // work-items must stay below 2^32
     if (prod(ntok, 16) >= (1LL << 32) || prod(B, H, 16) >= (1LL << 32)) return GDN_ENOTSUP;

@@ -24,7 +24,8 @@ from typing import Optional
 import torch
 
 __all__ = ["ChunkConfig", "DecodeConfig", "CHUNK_CONFIGS", "DECODE_CONFIG", "BWD_CONFIG",
-           "chunk_inputs", "decode_inputs", "grad_inputs", "prologue_inputs", "head_tokens"]
+           "chunk_inputs", "decode_inputs", "grad_inputs", "prologue_inputs", "head_tokens",
+           "hard_reset_gate"]
 
 
 @dataclass(frozen=True)
@@ -154,6 +155,18 @@ def decode_inputs(cfg: DecodeConfig, device="cpu", seed: Optional[int] = None):
     S0 = cfg.s_sigma * torch.randn(N, H, K, V, **f32)
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), g=g,
                 beta=beta.contiguous(), S0=S0.contiguous())
+
+
+def hard_reset_gate(shape, seed: int, device="cpu") -> torch.Tensor:
+    """Scalar log-decays with hard resets: most values from -softplus(N(0,1)), about
+    one in eight drawn uniformly from [-200, -20] (alpha below e^-20 wipes the
+    state), so that a scalar-gate path sees g far below the per-channel clamp."""
+    gen = _gen(torch.device(device), seed)
+    f32 = dict(device=device, dtype=torch.float32, generator=gen)
+    g = -torch.nn.functional.softplus(torch.randn(*shape, **f32))
+    reset = torch.rand(*shape, **f32) < 0.125
+    deep = -20.0 - 180.0 * torch.rand(*shape, **f32)
+    return torch.where(reset, deep, g).contiguous()
 
 
 def grad_inputs(cfg: ChunkConfig, device="cpu", seed: Optional[int] = None):

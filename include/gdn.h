@@ -28,8 +28,8 @@
  *    row-major in the layouts given, aligned to their element size.  The
  *    streamed operands need 16 bytes: q, k, v, o and a per-channel g of
  *    gdn_chunk_fwd, and S of gdn_recurrent_step.  The library allocates nothing
- *    and keeps no state between calls (gdn_chunk_bwd takes a caller-provided
- *    workspace).
+ *    and keeps no state between calls (gdn_chunk_bwd and gdn_chunk_fwd_ws take
+ *    a caller-provided workspace).
  *  - q, k, v and o share one storage type (gdn_dtype).  g, beta and every state
  *    tensor are fp32.  Arithmetic is fp32 with fp32 accumulation; for
  *    GDN_BF16 the matrix products take bf16 operands on the MFMA units.
@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -81,7 +81,9 @@ typedef enum { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_act;
  *   S_T   [B, H, K, V]   fp32 final state, or NULL.  May equal S0 (updated in
  *                        place); must not partially overlap any other buffer.
  *
- * K and V: 64 or 128 (GDN_F32: K = 64).  chunk: 64 (tokens per chunk).  Any
+ * K and V: 64 or 128 (GDN_F32: K = 64).  chunk: 64 (tokens per chunk).  64 rows
+ * of H * max(K, V) fp32 values must stay below 2^31 bytes (H < 65536 at 128;
+ * GDN_ENOTSUP otherwise: the kernels address a chunk with 32-bit offsets).  Any
  * T >= 0: a partial last chunk behaves as if padded with identity tokens
  * (beta = 0, g = 0), whose outputs are not written.  B, T or H equal to 0 is a
  * valid call: with T = 0, S_T receives S0 (or zeros).  At least one of o, S_T
@@ -92,6 +94,47 @@ GDN_API gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v,
                          void *o, float *S_T,
                          int B, int T, int H, int K, int V, int chunk,
                          gdn_dtype dtype, gdn_gate gate, void *stream);
+
+/*
+ * Bytes of device workspace that gdn_chunk_fwd_ws uses for these sizes (written
+ * to *bytes); want_o != 0 when o will be requested.  0 means the call runs as
+ * gdn_chunk_fwd does and needs no workspace.  Same size and type rules as
+ * gdn_chunk_fwd.
+ */
+GDN_API gdn_status gdn_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, int chunk,
+                                                gdn_dtype dtype, gdn_gate gate, int want_o,
+                                                size_t *bytes);
+
+/*
+ * gdn_chunk_fwd with a caller-provided workspace, which lets a call that needs
+ * only the final state run the sequence-parallel form: each (b, h) sequence is
+ * cut into segments of whole chunks that run at the same time, every segment
+ * after the first reduced to the affine map S -> M S + N it applies to the state
+ * (each chunk is such a map and maps compose associatively: the recurrence of
+ * the Atomic-GDN2 model card, section 2.1, whose kernel benchmark, section 5.1,
+ * is against an associative scan of it), and the maps of a sequence are then
+ * applied in order to the state from the first segment (fp32).  The form is
+ * used for o == NULL with bf16 operands, GDN_GATE_CHANNEL and K = V = 128 when
+ * B * H is too small to fill the device; every other call runs as
+ * gdn_chunk_fwd.
+ *
+ *   arguments as gdn_chunk_fwd, plus
+ *   workspace        device memory of at least
+ *                    gdn_chunk_fwd_workspace_size(..., o != NULL, ...) bytes,
+ *                    256-byte aligned, owned by the caller, not overlapping any
+ *                    input or output; may be NULL when that size is 0.  Its
+ *                    contents on entry do not matter; on return they are
+ *                    unspecified.  Calls sharing one workspace must not run
+ *                    concurrently.
+ *
+ * Results equal gdn_chunk_fwd's to rounding (the segment maps add one fp32
+ * product per segment boundary), not bit for bit.  S_T may equal S0.
+ */
+GDN_API gdn_status gdn_chunk_fwd_ws(const void *q, const void *k, const void *v,
+                                    const float *g, const float *beta, const float *S0,
+                                    void *o, float *S_T, void *workspace, size_t workspace_bytes,
+                                    int B, int T, int H, int K, int V, int chunk,
+                                    gdn_dtype dtype, gdn_gate gate, void *stream);
 
 /*
  * One fused recurrent (decode) step for N sequences, updating S in place.
@@ -206,7 +249,9 @@ GDN_API gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, co
  *   cs_*_out  the raw inputs of the last three tokens (older rows from cs_* when
  *           T < 3), or NULL.  Each may be its own input exactly (updated in place).
  *
- * K and V: 64 or 128.  g_cap > 0 (+inf: no cap).  q_raw, k_raw, v_raw, q, k, v,
+ * K and V: 64 or 128.  g_cap > 0 (+inf: no cap); with GDN_GATE_CHANNEL at most 5
+ * (GDN_ENOTSUP otherwise: the per-channel chunk kernels that take these outputs
+ * need g >= -5).  q_raw, k_raw, v_raw, q, k, v,
  * the taps, the carried states and a per-channel g_raw / g need 16-byte
  * alignment; b_raw, beta and a scalar g 4 bytes.  No output may overlap an input
  * or another output, except a state output that is its own input.  B, T or H

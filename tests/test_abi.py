@@ -41,7 +41,7 @@ def test_only_declared_symbols_are_exported():
 
 
 def test_version_and_status_strings(L):
-    assert gdn.abi_version() == 4
+    assert gdn.abi_version() == 5
     assert gdn.status_str(0) == "ok"
     assert "invalid" in gdn.status_str(1)
     assert "unsupported" in gdn.status_str(2)
@@ -342,3 +342,83 @@ def test_python_binding_rejects_cpu_tensors(L):
 def test_status_error_carries_code(L):
     e = gdn.GDNError(2, "gdn_chunk_fwd")
     assert e.status == 2 and "unsupported" in str(e)
+
+
+# ---------------------------------------------------------------- chunkwise forward with workspace
+def _fws_size(L, B=1, T=262144, H=48, K=128, V=128, chunk=64, dtype=1, gate=1, want_o=0):
+    import ctypes
+    n = ctypes.c_size_t(12345)
+    rc = L.gdn_chunk_fwd_workspace_size(B, T, H, K, V, chunk, dtype, gate, want_o, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_fwd_workspace_size_values(L):
+    # final state only, bf16, per-channel gate, 48 heads of 262144 tokens: 16 segments of
+    # 256 chunks, an fp32 M (128 x 128) and N (128 x 128) for each of the 15 after the first
+    assert _fws_size(L) == (gdn.GDN_OK, 48 * 15 * 2 * 128 * 128 * 4)
+    # two heads of 2048 tokens: two segments of 16 chunks
+    assert _fws_size(L, B=1, H=2, T=2048) == (gdn.GDN_OK, 1 * 2 * 1 * 2 * 128 * 128 * 4)
+    # no sequence-parallel form: o wanted, scalar gate, fp32, K = 64, enough heads, short T
+    for kw in (dict(want_o=1), dict(gate=0), dict(dtype=0, K=64, V=64), dict(K=64),
+               dict(B=16, H=8, T=2048), dict(T=1000), dict(T=0), dict(B=0)):
+        assert _fws_size(L, **kw) == (gdn.GDN_OK, 0), kw
+
+
+def test_fwd_workspace_size_errors(L):
+    import ctypes
+    assert L.gdn_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 64, 1, 1, 0, None) == gdn.GDN_EINVAL
+    for kw in (dict(dtype=2), dict(gate=3), dict(B=-1), dict(T=-1), dict(K=0), dict(chunk=0)):
+        assert _fws_size(L, **kw)[0] == gdn.GDN_EINVAL, kw
+    for kw in (dict(K=96), dict(V=32), dict(chunk=32), dict(dtype=0, K=128), dict(H=70000)):
+        assert _fws_size(L, **kw)[0] == gdn.GDN_ENOTSUP, kw
+
+
+def _chunk_ws(L, **kw):
+    q, k, v, g, beta, S0, o, S_T, ws = _ptrs(9)
+    a = dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, o=None, S_T=S_T, ws=ws, nbytes=1 << 30,
+             B=1, T=262144, H=48, K=128, V=128, chunk=64, dtype=1, gate=1)
+    a.update(kw)
+    return L.gdn_chunk_fwd_ws(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["o"],
+                              a["S_T"], a["ws"], a["nbytes"], a["B"], a["T"], a["H"], a["K"],
+                              a["V"], a["chunk"], a["dtype"], a["gate"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ws=None),                        # the segment form needs its workspace
+    dict(nbytes=48 * 15 * 2 * 128 * 128 * 4 - 1),
+    dict(ws=BASE + 8 * SEP + 128),        # misaligned
+    dict(ws=BASE + 1 * SEP),              # over k
+    dict(ws=BASE + 7 * SEP - 4096),       # runs into S_T
+    dict(dtype=5), dict(S_T=None),        # o and S_T both absent
+    dict(q=BASE + 4),
+])
+def test_fwd_ws_rejects_invalid(L, kw):
+    assert _chunk_ws(L, **kw) == gdn.GDN_EINVAL
+
+
+def test_fwd_ws_unsupported(L):
+    assert _chunk_ws(L, K=96) == gdn.GDN_ENOTSUP
+    assert _chunk_ws(L, T=64, H=70000) == gdn.GDN_ENOTSUP
+
+
+def test_fwd_ws_empty_is_a_noop(L):
+    assert _chunk_ws(L, B=0) == gdn.GDN_OK
+    assert _chunk_ws(L, H=0, ws=None) == gdn.GDN_OK
+
+
+def test_chunk_paths_reject_shapes_past_32bit_offsets(L):
+    # 64 rows of H * 128 fp32 values past 2^31 bytes: the kernels' per-lane
+    # offsets would overflow, so the host refuses the shape
+    assert _chunk(L, B=1, T=64, H=65536) == gdn.GDN_ENOTSUP
+    import ctypes
+    n = ctypes.c_size_t(0)
+    assert L.gdn_chunk_bwd_workspace_size(1, 64, 65536, 128, 128, 64, ctypes.byref(n)) == gdn.GDN_ENOTSUP
+    assert L.gdn_chunk_bwd_workspace_size(1, 64, 65535, 128, 128, 64, ctypes.byref(n)) == gdn.GDN_OK
+
+
+def test_prologue_channel_cap_above_five_is_unsupported(L):
+    # the per-channel chunk kernels need g >= -5: a larger cap (or none) for the
+    # per-channel gate is refused; the scalar gate takes any cap
+    assert _pro(L, gate=1, cap=5.5) == gdn.GDN_ENOTSUP
+    assert _pro(L, gate=1, cap=float("inf")) == gdn.GDN_ENOTSUP
+    assert _pro(L, gate=0, cap=float("inf"), K=96) == gdn.GDN_ENOTSUP   # stops at K, not the cap

@@ -35,9 +35,10 @@ def _tol(dtype):
     return TOL_FP32 if dtype == "fp32" else TOL_BF16
 
 
-def _chunk(d, S0="from_inputs", want_o=True):
+def _chunk(d, S0="from_inputs", want_o=True, workspace=None):
     S0 = d["S0"] if isinstance(S0, str) else S0
-    o, S = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0, want_o=want_o)
+    o, S = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0, want_o=want_o,
+                         workspace=workspace)
     torch.cuda.synchronize()
     return o, S
 
@@ -182,7 +183,12 @@ def test_replicated_channel_gate_equals_scalar_gate(K, dtype):
     e = slice_rel(to_np(o_c), to_np(o_h), (0, 2))
     eS = slice_rel(to_np(S_c), to_np(S_h), (0, 1))
     _say(f"[modes] replicated vs scalar: o {e:.3e} S {eS:.3e}")
-    agree = 1e-5 if dtype == "fp32" else tol
+    # fp32: the two kernels split the decay differently (one exponent per token
+    # pair against a split at 16-token blocks), so each carries its own fp32
+    # rounding: measured on this case, each is 0.8e-6 .. 1.4e-6 (o) from the fp64
+    # oracle, so they can differ by about the sum; 5e-6 is that with a margin and
+    # still twenty times inside the 1e-4 bound
+    agree = 5e-6 if dtype == "fp32" else tol
     assert e <= agree and eS <= agree
 
 
@@ -208,7 +214,7 @@ def test_in_place_state_and_state_only(K, dtype, gate):
     d = _dev(chunk_inputs(cfg))
     _say(f"[modes] aliasing K{K} {dtype} {gate}")
     o, S = _chunk(d)
-    _, S_only = _chunk(d, want_o=False)
+    _, S_only = _chunk(d, want_o=False, workspace=False)
     assert torch.equal(S_only, S)
     B, T, H = cfg.B, cfg.T, cfg.H
     S_io = d["S0"].clone()
@@ -274,13 +280,14 @@ def test_ragged_bf16(T, K, gate):
 def test_long_prefill_48_heads_sampled():
     """T = 262144 with 48 heads of 128 x 128 fp32 state and a given S0: the GPU
     runs the whole batch; the oracle follows three heads over the whole sequence.
-    The call without o (the final state only, which skips q) gives the same state
-    bit for bit."""
+    The sequential kernels' call without o (the final state only, which skips q)
+    gives the same state bit for bit (the sequence-parallel form of the same call
+    is checked in test_gpu_seg.py)."""
     cfg = CHUNK_CONFIGS["channel_long"]
     _say(f"[modes] long prefill B{cfg.B} H{cfg.H} T{cfg.T}")
     d = chunk_inputs(cfg, device=DEV)
     o, S = _chunk(d)
-    _, S_only = _chunk(d, want_o=False)
+    _, S_only = _chunk(d, want_o=False, workspace=False)
     assert torch.equal(S_only, S)
     heads = [0, 23, cfg.H - 1]
     sel = lambda x: x[:, :, heads].cpu().contiguous()
