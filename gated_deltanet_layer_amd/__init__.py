@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
     gdn_chunk_fwd(q, k, v, g, beta, S0, o, S_T, chunk=64)
     gdn_chunk_fwd_ws(q, k, v, g, beta, S0, o, S_T, workspace, chunk=64)
     gdn_chunk_fwd_workspace_size(B, T, H, K, V, dtype, gate, want_o) -> bytes
+    gdn_chunk_fwd_noalloc(q, k, v, g, beta, S0, o, S_T, chunk=64)
     gdn_recurrent_step(q, k, v, g, beta, S, o)
     gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist)
     gdn_chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace)
@@ -37,7 +38,8 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_HEAD, GDN_GATE_CHANNEL = 0, 1
 GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
 _ACTS = {"none": GDN_ACT_NONE, "silu": GDN_ACT_SILU}
-SYMBOLS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd_ws", "gdn_recurrent_step", "gdn_recurrent_steps",
+SYMBOLS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd_ws",
+           "gdn_chunk_fwd_noalloc", "gdn_recurrent_step", "gdn_recurrent_steps",
            "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_prologue",
            "gdn_recurrent_step_prologue", "gdn_status_str", "gdn_abi_version")
 
@@ -78,6 +80,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_chunk_fwd_ws.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, sz,
                                        i, i, i, i, i, i, i, i, vp]
         L.gdn_chunk_fwd_ws.restype = i
+        L.gdn_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp,
+                                            i, i, i, i, i, i, i, i, vp]
+        L.gdn_chunk_fwd_noalloc.restype = i
         L.gdn_chunk_bwd_workspace_size.argtypes = [i, i, i, i, i, i, ctypes.POINTER(sz)]
         L.gdn_chunk_bwd_workspace_size.restype = i
         L.gdn_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp,
@@ -350,6 +355,17 @@ def chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T, want_dS0: bool = True, workspace=
     gdn_chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T, out["dq"], out["dk"], out["dv"], out["dg"],
                   out["dbeta"], out["dS0"], workspace, chunk=chunk, stream=stream)
     return out
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, S0, o, S_T, chunk: int = 64, stream=None) -> None:
+    """gdn_chunk_fwd_ws with the segment maps in the library's static device
+    buffer (no allocation in the call; calls sharing a GPU must not overlap)."""
+    B, T, H, K, V, gate = _chunk_fwd_args(q, k, v, g, beta, S0, o, S_T)
+    rc = lib().gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                                     _ptr(o), _ptr(S_T), B, T, H, K, V, int(chunk),
+                                     _dtype_code(q), gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd_noalloc")
 
 
 def chunk_fwd(q, k, v, g, beta, S0=None, want_o: bool = True, chunk: int = 64, stream=None,

@@ -40,6 +40,7 @@
 // chunk and the registers stay within the two-waves-per-SIMD budget.  One workgroup barrier per
 // chunk hands the chunk's data over; the chain's data is double-buffered.
 #include "ws_common.h"
+#include <mutex>
 #include <type_traits>
 
 namespace gdn {
@@ -638,6 +639,37 @@ unsigned long long chunk_fwd_seg_workspace(long B, long H, int nseg)
 {
     if (nseg <= 1) return 0;
     return (unsigned long long)B * H * (nseg - 1) * (2ull * SG_K * SG_K) * 4ull;
+}
+
+// Device scratch of the entry point that allocates nothing: the segment maps of
+// one call live here instead of in a caller's workspace.  Host code never
+// passes this name to a kernel: it is a host-side stand-in, so its device
+// address is looked up once per device (seg_scratch) and that pointer is used.
+constexpr unsigned long long SG_SCRATCH_BYTES = 64ull << 20;
+static __device__ __align__(256) unsigned char scratch[SG_SCRATCH_BYTES];
+
+unsigned long long chunk_fwd_seg_scratch_bytes() { return SG_SCRATCH_BYTES; }
+
+// The device address of `scratch` on the current device, looked up on the
+// first call for each device (with that device current) and kept.
+hipError_t seg_scratch(void **p)
+{
+    constexpr int MAXDEV = 64;
+    static std::mutex mu;
+    static void *addr[MAXDEV] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAXDEV) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = ptr;
+    }
+    *p = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t chunk_fwd_seg_launch(const void *k, const void *v, const float *g, const float *beta,

@@ -23,6 +23,8 @@ unsigned long long chunk_fwd_seg_workspace(long B, long H, int nseg);
 hipError_t chunk_fwd_seg_launch(const void *k, const void *v, const float *g, const float *beta,
                                 const float *S0, float *S_T, void *ws, int B, int T, int H, int nseg,
                                 hipStream_t st);
+unsigned long long chunk_fwd_seg_scratch_bytes();
+hipError_t seg_scratch(void **p);
 hipError_t recurrent_multi_launch(bool bf16, bool channel, int K, int V, const void *q,
                                   const void *k, const void *v, const float *g,
                                   const float *beta, const float *S0, void *o, float *S_T,
@@ -228,6 +230,34 @@ gdn_status gdn_chunk_fwd_ws(const void *q, const void *k, const void *v, const f
     else
         e = gdn::chunk_fwd_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL, K, q, k, v, g, beta,
                                   S0, o, S_T, B, T, H, V, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *S0, void *o, float *S_T,
+                                 int B, int T, int H, int K, int V, int chunk,
+                                 gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    const gdn_status st = chunk_fwd_check(q, k, v, g, beta, S0, o, S_T, B, T, H, K, V, chunk,
+                                          dtype, gate);
+    if (st != GDN_OK) return st;
+    unsigned long long need = 0;
+    const int nseg = chunk_fwd_plan(B, T, H, K, V, dtype, gate, o != nullptr, &need);
+    // the segment maps must fit the library's static scratch
+    if (need > gdn::chunk_fwd_seg_scratch_bytes()) return GDN_ENOTSUP;
+    if (B == 0 || H == 0) return GDN_OK;
+    if (!S_T && T == 0) return GDN_OK;
+    hipError_t e;
+    if (nseg > 1) {
+        void *ws = nullptr;
+        e = gdn::seg_scratch(&ws);
+        if (e == hipSuccess)
+            e = gdn::chunk_fwd_seg_launch(k, v, g, beta, S0, S_T, ws, B, T, H, nseg,
+                                          static_cast<hipStream_t>(stream));
+    } else {
+        e = gdn::chunk_fwd_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL, K, q, k, v, g, beta,
+                                  S0, o, S_T, B, T, H, V, static_cast<hipStream_t>(stream));
+    }
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

@@ -137,6 +137,31 @@ GDN_API gdn_status gdn_chunk_fwd_ws(const void *q, const void *k, const void *v,
                                     gdn_dtype dtype, gdn_gate gate, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): gdn_chunk_fwd_ws with
+ * the segment maps in a static device buffer that the library owns instead of a
+ * caller's workspace.  Arguments as gdn_chunk_fwd; the call runs exactly as
+ * gdn_chunk_fwd_ws does with a large enough workspace (same kernels, same
+ * segments, the same results bit for bit).
+ *
+ * The buffer holds GDN_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU the library
+ * runs on, from the module load until the process ends.  A call whose segment
+ * maps would need more (gdn_chunk_fwd_workspace_size(..., o != NULL, ...) >
+ * GDN_NOALLOC_SCRATCH_BYTES) returns GDN_ENOTSUP and enqueues nothing; use
+ * gdn_chunk_fwd_ws for it.  Every call on one GPU shares that GPU's buffer, so
+ * calls that overlap on one GPU (concurrent streams, threads) race; each call
+ * writes every map it reads, so nothing needs clearing between calls.  The
+ * stream must belong to the current device.  No hipMalloc, hipFree or other
+ * allocation happens in the call.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64ull << 20)
+GDN_API gdn_status gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                         const float *g, const float *beta, const float *S0,
+                                         void *o, float *S_T,
+                                         int B, int T, int H, int K, int V, int chunk,
+                                         gdn_dtype dtype, gdn_gate gate, void *stream);
+
+/*
  * One fused recurrent (decode) step for N sequences, updating S in place.
  *
  *   q, k  [N, H, K]   dtype          v  [N, H, V]   dtype
