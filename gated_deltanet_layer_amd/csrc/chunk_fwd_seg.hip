@@ -23,22 +23,34 @@
 //   E_bc       e^{block total}, R_b = sum of the blocks before b, gn = chunk total
 //   KL = k e^{lambda}, KI = k e^{-lambda}          (Gram operands, in range)
 //   K+ = KL e^{R_b} = k e^{gamma},  K- = KI e^{gn - R_b} = k e^{gn - gamma}  (<= 1)
-//   A_ij = diag(beta_i) KL_i (KI_j F_ij)^T,  F_ij = E_j ... E_{i-1}  (j < i)
-//   (I + A) D = diag(beta)(V - K+ S),   S' = Diag(e^{gn}) S + K-^T D
-// with V = 0 in the columns of M.
+//   G_ij = KL_i (KI_j F_ij)^T,  F_ij = E_j ... E_{i-1}  (j < i; the Gram without beta)
+//   A = diag(beta) G (strictly lower),  T_ii = (I + A_ii)^{-1},  T'_ii = T_ii diag(beta_i)
+//   D_i = T'_ii (V_i - K+_i S - sum_{j<i} G_ij D_j)   (block forward substitution of
+//         (I + A) D = diag(beta)(V - K+ S): beta moved into T')
+//   S' = Diag(e^{gn}) S + K-^T D,   with V = 0 in the columns of M.
 //
 // Work split: one workgroup of 8 waves per (head, segment).  Prep waves 4..7
 // get chunk n + 1 ready while chain waves 0..3 run chunk n.  Prep wave p owns
-// key block p (keys 32p .. 32p+31) of all 64 tokens, so the running sums, the
-// block factors and the four scaled tiles of its keys are computed without any
-// other wave; after the four prep waves have met (an LDS arrival counter), each
-// computes its share of the Gram blocks and one diagonal inverse.  Chain wave w
-// owns 64 columns of the augmented state (w = 0, 1: value columns; w = 2, 3:
-// columns of M, idle in segment 0) in MFMA accumulators for the whole segment;
-// per chunk it forms D one 16-column tile at a time and updates the state two
-// tiles (32 columns) at a time, so that the k^T fragments are read twice per
-// chunk and the registers stay within the two-waves-per-SIMD budget.  One workgroup barrier per
-// chunk hands the chunk's data over; the chain's data is double-buffered.
+// key block p (keys 32p .. 32p+31) of all 64 tokens: the running sums, the block
+// factors, the tiles K+ and K- and, on the matrix cores, its key block's share
+// of every Gram block (each an MFMA over exactly its 32 keys, operands from
+// registers); the four shares meet in LDS, and after the prep waves have met (an
+// LDS arrival counter) each sums its Gram blocks, one of them a diagonal block it
+// also inverts.  Chain wave w owns 64 columns of the augmented state (w = 0, 1:
+// value columns; w = 2, 3: columns of M, idle in segment 0) in MFMA
+// accumulators for the whole segment.  One workgroup barrier per chunk hands the
+// chunk's data over; the chain's data is double-buffered.
+//
+// LDS layouts, chosen for the matrix-core operand reads (measured on gfx950: a
+// 16-byte read by 64 lanes from one contiguous 1 KB runs at about 2.3 ns per
+// instruction per CU; 16 rows of 256 bytes read at one 16-byte chunk each, even
+// XOR-swizzled, at about 3.9 ns):
+//   K+ and V: "fragment-major": the 16 x 32 operand fragment (token block rt,
+//     32-column block kb) is 1 KB, lane l's 16 bytes at l * 16.
+//   K-: 64 rows of 256 bytes, 16-byte chunks XOR-swizzled by the row, read with
+//     the transposing ds_read_b64_tr_b16 (2.4 ns per instruction).
+//   -G blocks: four 1 KB fragments in the substitution's operand order; T':
+//     64 rows of 16 bf16.
 #include "ws_common.h"
 #include <mutex>
 #include <type_traits>
@@ -52,36 +64,37 @@ constexpr int SG_NTHR = 512;    // 4 chain waves + 4 prep waves
 constexpr int sg_al(int x) { return (x + 255) & ~255; }
 
 struct SgSmem {
-    static constexpr int RB = SG_K * 2;          // bytes per tile row
-    static constexpr int TILE = SG_T * RB;       // one 64 x 128 bf16 tile
-    static constexpr int LDC = SG_T + 8;         // row length of -A (bf16, fragment order)
-    static constexpr int LDD = 16;               // row length of T_ii
-    // prep buffer (one): KL, KI, block factors E [4][K], per-wave 16 x 16 fp32 scratch
-    static constexpr int pKL = 0, pKI = TILE, pE = 2 * TILE, pAd = pE + 4 * SG_K * 4;
+    static constexpr int TILE = SG_T * SG_K * 2;  // one 64 x 128 bf16 tile
+    static constexpr int LDD = 16;                // row length of T'
+    // prep buffer (one): each prep wave's share of the ten Gram blocks (fp32,
+    // accumulator order), beta of the chunk
+    static constexpr int pPart = 0, pBeta = 4 * 10 * 1024, pAd = pBeta + SG_T * 4;
     static constexpr int PREP = sg_al(pAd + 4 * 256 * 4);
     // hand-over buffers (two): what the chain reads for one chunk
     static constexpr int hKP = 0, hKM = TILE, hV = 2 * TILE, hAn = 3 * TILE;
-    static constexpr int hTd = hAn + 48 * LDC * 2;
-    static constexpr int hBeta = hTd + SG_T * LDD * 2;
-    static constexpr int hEgn = hBeta + SG_T * 4;
+    static constexpr int hTd = hAn + 4 * 1024;
+    static constexpr int hEgn = hTd + SG_T * LDD * 2;
     static constexpr int HBUF = sg_al(hEgn + SG_K * 4);
     static constexpr int oH = PREP;
-    static constexpr int kCtr = oH + 2 * HBUF;
+    // per prep wave 256 bytes that the L2 prefetch copies land in (never read)
+    static constexpr int kSink = oH + 2 * HBUF;
+    static constexpr int kCtr = kSink + 4 * 256;
     static constexpr int bytes = sg_al(kCtr + 16);
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-// Byte offset of the 16-byte chunk `ch` of row `row` of a 64 x 128 bf16 tile:
+// Byte offset of the 16-byte chunk `ch` of row `row` of the row-major K- tile:
 // the chunk index is XORed with the row's low four bits in swapped halves, so
-// that the 16-row fragment reads and the transposed reads hit distinct banks.
+// that the transposed reads hit distinct banks.
 __device__ __forceinline__ int sg_off(int row, int ch) {
     return row * 256 + ((ch ^ (((row & 3) << 2) | ((row >> 2) & 3))) << 4);
 }
-__device__ __forceinline__ Frag<__bf16> sg_frag(const char *M, int row0, int kb) {
-    return {*reinterpret_cast<const bf16x8 *>(M + sg_off(row0 + lane_r16(), 4 * kb + lane_gq()))};
+// Fragment-major tile: fragment (rt, kb), this lane's 16 bytes.
+__device__ __forceinline__ int fm_off(int rt, int kb) {
+    return (4 * rt + kb) * 1024 + (threadIdx.x & 63) * 16;
 }
 
-// 8 bf16 times 8 fp32 factors (fp32 arithmetic), as 8 fp32.
+// 8 bf16 as 8 fp32, and back.
 __device__ __forceinline__ void unpack8(bf16x8 x, f32x4 &lo, f32x4 &hi) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -100,6 +113,17 @@ struct SgArgs {
     int T, H, nseg, seg_len;
 };
 
+// Gram block index of (I, J), J <= I: the diagonal blocks first, then
+// (1,0) (2,0) (3,0) (2,1) (3,1) (3,2).
+__device__ __forceinline__ constexpr int gblk(int I, int J) {
+    return I == J ? I : (J == 0 ? 3 + I : (J == 1 ? 5 + I : 9));
+}
+// -G fragment (and its 8-byte half) that holds block (I, J), J < I, for the
+// substitution: F0 = G_10 | 0, F1 = G_20 | G_21, F2 = G_30 | G_31, F3 = G_32 | 0.
+__device__ __forceinline__ constexpr int gfrag_off(int I, int J) {
+    return I == 1 ? 0 : (I == 2 ? 1024 + 8 * J : (J < 2 ? 2048 + 8 * J : 3072));
+}
+
 __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
 {
     using L = SgSmem;
@@ -114,16 +138,18 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
     const int gq = lane >> 4;
 
     const int T = a.T, H = a.H;
-    const int bh = blockIdx.x / a.nseg, seg = blockIdx.x % a.nseg;
+    // segment-major order: the heads of one segment run at about the same time,
+    // so the rows of a token (all heads side by side in memory) are fetched together
+    const int nbh = gridDim.x / a.nseg;
+    const int seg = blockIdx.x / nbh, bh = blockIdx.x % nbh;
     const int b = bh / H, h = bh % H;
     const long row_base = (long)b * T * H + h;   // row of token 0 in [B*T*H]
     const int nchunks = (T + SG_T - 1) / SG_T;
     const int c0 = seg * a.seg_len, c1 = min(nchunks, c0 + a.seg_len);
 
     auto hbuf = [&](int c) { return smem + L::oH + (c & 1) * L::HBUF; };
-    char *sKL = smem + L::pKL;
-    char *sKI = smem + L::pKI;
-    float *sE = reinterpret_cast<float *>(smem + L::pE);
+    float *sPart = reinterpret_cast<float *>(smem + L::pPart);
+    float *sBeta = reinterpret_cast<float *>(smem + L::pBeta);
     unsigned *ctr = reinterpret_cast<unsigned *>(smem + L::kCtr);
     if (tid == 0) *ctr = 0u;
     lds_barrier();
@@ -137,15 +163,6 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
         for (int rt = 0; rt < 4; ++rt) {
             boff[rt] = (unsigned)((16 * rt + r16) * H);
             loff[rt] = boff[rt] * (unsigned)K + (unsigned)(32 * pw + 8 * gq);
-        }
-        // v copies: instruction i fills rows 16 pw + 4 i .. +3 (lane l: row
-        // + l / 16, physical slot l % 16, holding logical chunk slot ^ swizzle)
-        unsigned voff[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * pw + 4 * i + (lane >> 4), slot = lane & 15;
-            const int ch = slot ^ (((row & 3) << 2) | ((row >> 2) & 3));
-            voff[i] = 2u * (unsigned)(row * H * K + 8 * ch);
         }
 
         struct Raw {
@@ -175,6 +192,23 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
                 r.b[rt] = bb[bo];
             }
         };
+        // The loads of token block rt of chunk n only (same addressing as fetch).
+        auto fetch_rt = [&](int n, int rt, Raw &r) __attribute__((always_inline)) {
+            const int t0 = n * SG_T;
+            const int nlive = T - t0;
+            const long rbase = row_base + (long)t0 * H;
+            const __bf16 *kb = a.k + rbase * K;
+            const float *gb = a.g + rbase * K;
+            const float *bb = a.beta + rbase;
+            const int row = 16 * rt + r16;
+            const bool live = row < nlive;
+            const unsigned lo = live ? loff[rt] : (unsigned)((nlive - 1) * H * K + 32 * pw + 8 * gq);
+            const unsigned bo = live ? boff[rt] : (unsigned)((nlive - 1) * H);
+            r.k[rt] = *reinterpret_cast<const bf16x8 *>(kb + lo);
+            r.g[rt][0] = *reinterpret_cast<const f32x4 *>(gb + lo);
+            r.g[rt][1] = *reinterpret_cast<const f32x4 *>(gb + lo + 4);
+            r.b[rt] = bb[bo];
+        };
         auto zero_dead = [&](int n, Raw &r) __attribute__((always_inline)) {
             const int nlive = T - n * SG_T;
 #pragma unroll
@@ -187,28 +221,25 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
                 }
             }
         };
-        auto copy_v = [&](int n) __attribute__((always_inline)) {
-            char *dst = hbuf(n) + L::hV + 16 * pw * L::RB;
+        // L2 prefetch of chunk n: one 4-byte copy per 128-byte line of this
+        // wave's rows 16 pw .. +15 of g (four lines a row) and k (two lines a
+        // row) and of beta, into this wave's sink in LDS (never read); the real
+        // loads of the chunk, a period later, then find the lines in L2.
+        auto prefetch_l2 = [&](int n) __attribute__((always_inline)) {
             const int t0 = n * SG_T;
-            if (t0 + SG_T <= T) {
-                const __bf16 *vb = a.v + (row_base + (long)t0 * H) * K;   // wave-uniform
-#pragma unroll
-                for (int i = 0; i < 4; ++i) g2lds16s(vb, voff[i], dst + 4 * i * L::RB);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * pw + 4 * i + (lane >> 4), slot = lane & 15;
-                    const int ch = slot ^ (((row & 3) << 2) | ((row >> 2) & 3));
-                    const int t = min(t0 + row, T - 1);
-                    g2lds16(a.v + (row_base + (long)t * H) * K + 8 * ch, dst + 4 * i * L::RB);
-                }
-            }
+            char *sink = smem + L::kSink + pw * 256;
+            const int gr = min(t0 + 16 * pw + (lane >> 2), T - 1);         // g: 16 rows x 4 lines
+            g2lds4(a.g + (row_base + (long)gr * H) * K + 32 * (lane & 3), sink);
+            const int kr = min(t0 + 16 * pw + ((lane & 31) >> 1), T - 1);  // k: 16 rows x 2 lines
+            const float *src = lane < 32 ? reinterpret_cast<const float *>(a.k + (row_base + (long)kr * H) * K + 64 * (lane & 1))
+                                         : a.beta + row_base + (long)min(t0 + 16 * pw + (lane & 15), T - 1) * H;
+            g2lds4(src, sink);
         };
 
-        unsigned arrivals = 0;
-        // Chunk n from its raw loads r; issues the v copies of chunk n and the
-        // loads of chunk n + 1 (into nx) first.
         Raw r, nx;
+        unsigned arrivals = 0;
+        // Chunk n from its raw loads (in nx on entry); issues the v copies of
+        // chunk n and, once the tiles are out, the loads of chunk n + 1.
         auto prepare = [&](int n) __attribute__((always_inline)) {
             char *Hb = hbuf(n);
             // The loads of chunk n (issued a period ago) are complete before the
@@ -217,12 +248,12 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
             r = nx;
             zero_dead(n, r);
-            copy_v(n);
 
             // Forward over the four token blocks: lambda (4 DPP scan steps over
             // the block's 16 rows), e^{+-lambda}, the block factor E_rt (row 15),
-            // and the tiles KL, KI and K+ = KL e^{R_rt} (R_rt: the blocks before).
+            // K+ = k e^{lambda} e^{R_rt} to LDS; KL and KI kept as operands.
             f32x4 E[4][2], ki[4][2];
+            Frag<__bf16> fKL[4];
             f32x4 ER0 = {1.f, 1.f, 1.f, 1.f}, ER1 = ER0;
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
@@ -249,13 +280,17 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
                     }
                 f32x4 k0, k1;
                 unpack8(r.k[rt], k0, k1);
+                // this block's raw registers are consumed: the same block of the
+                // next chunk goes in flight (four loads per block, spread over the
+                // loop rather than issued as one burst)
+                GDN_SCHED_FENCE();
+                if (n + 1 < c1) fetch_rt(n + 1, rt, nx);
+                GDN_SCHED_FENCE();
                 const f32x4 kl0 = k0 * el[0], kl1 = k1 * el[1];
                 ki[rt][0] = k0 * ei[0];
                 ki[rt][1] = k1 * ei[1];
-                const int off = sg_off(16 * rt + r16, 4 * pw + gq);
-                *reinterpret_cast<bf16x8 *>(sKL + off) = pack8(kl0, kl1);
-                *reinterpret_cast<bf16x8 *>(sKI + off) = pack8(ki[rt][0], ki[rt][1]);
-                *reinterpret_cast<bf16x8 *>(Hb + L::hKP + off) = pack8(kl0 * ER0, kl1 * ER1);
+                fKL[rt].v = pack8(kl0, kl1);
+                *reinterpret_cast<bf16x8 *>(Hb + L::hKP + fm_off(rt, pw)) = pack8(kl0 * ER0, kl1 * ER1);
                 ER0 *= E[rt][0];
                 ER1 *= E[rt][1];
             }
@@ -275,118 +310,83 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
                     *reinterpret_cast<f32x4 *>(go + 4) = ES1;
                 }
             }
-            if (r16 == 0) {
-                float *eo = sE + 32 * pw + 8 * gq;
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    *reinterpret_cast<f32x4 *>(eo + rt * K) = E[rt][0];
-                    *reinterpret_cast<f32x4 *>(eo + rt * K + 4) = E[rt][1];
-                }
-            }
             if (pw == 0 && gq == 0) {
-                float *bo = reinterpret_cast<float *>(Hb + L::hBeta);
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) bo[16 * rt + r16] = r.b[rt];
+                for (int rt = 0; rt < 4; ++rt) sBeta[16 * rt + r16] = r.b[rt];
             }
-            // the next chunk's loads go in flight behind the v copies
-            if (n + 1 < c1) fetch(n + 1, nx);
-            arrivals += 4;
-            prep_barrier(ctr, arrivals);   // KL, KI, E and beta of every key block written
-
-            // ---- Gram blocks of chunk n: the diagonal block pw with its inverse,
-            // then off-diagonal blocks (I, J), computed transposed (rows s of
-            // block J, columns t of block I):
-            //   p0: (1,0) (3,0)   p1: (2,1) (3,1)   p2: (3,2)   p3: (2,0)
-            __bf16 *sAn = reinterpret_cast<__bf16 *>(Hb + L::hAn);
-            const float *sB = reinterpret_cast<const float *>(Hb + L::hBeta);
-            float *sAd = reinterpret_cast<float *>(smem + L::pAd) + pw * 256;
+            // This key block's share of the ten Gram blocks, G_IJ over keys
+            // 32 pw .. +31, computed transposed (rows s of block J, columns t of
+            // block I): A = KI_J F_IJ (F_IJ = E_J .. E_{I-1} per key), B = KL_I.
             {
-                Frag<__bf16> fi[NKB], fl[NKB];
+                float *mine = sPart + pw * 10 * 256 + lane * 4;
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    fi[kb] = sg_frag(sKI, 16 * pw, kb);
-                    fl[kb] = sg_frag(sKL, 16 * pw, kb);
+                for (int J = 0; J < 4; ++J) {
+                    f32x4 f0 = {1.f, 1.f, 1.f, 1.f}, f1 = f0;
+#pragma unroll
+                    for (int I = J; I < 4; ++I) {
+                        if (I > J) {
+                            f0 *= E[I - 1][0];
+                            f1 *= E[I - 1][1];
+                        }
+                        const Frag<__bf16> fa = {pack8(ki[J][0] * f0, ki[J][1] * f1)};
+                        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                        const f32x4 part = mma(z, fa, fKL[I]);
+                        *reinterpret_cast<f32x4 *>(mine + gblk(I, J) * 256) = part;
+                    }
                 }
-                f32x4 aA = {0.f, 0.f, 0.f, 0.f};
+            }
+            if (n + 2 < c1) prefetch_l2(n + 2);
+            arrivals += 4;
+            prep_barrier(ctr, arrivals);   // every share and beta written
+
+            // Sum the four shares of this wave's blocks: the diagonal block pw
+            // (then T'_pw), and -G of p0: (1,0) (3,0)   p1: (2,1) (3,1)
+            // p2: (3,2)   p3: (2,0).
+            auto sum4 = [&](int blk) __attribute__((always_inline)) {
+                f32x4 s4[4];
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) aA = mma(aA, fi[kb], fl[kb]);
-                const int t = 16 * pw + r16, s0 = 16 * pw + 4 * gq;
-                const float bt = sB[t];
+                for (int w = 0; w < 4; ++w)
+                    s4[w] = *reinterpret_cast<const f32x4 *>(sPart + (w * 10 + blk) * 256 + lane * 4);
+                return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+            };
+            auto offdiag = [&](auto ic, auto jc) __attribute__((always_inline)) {
+                constexpr int I = decltype(ic)::value, J = decltype(jc)::value;
+                const f32x4 gsum = sum4(gblk(I, J));
+                *reinterpret_cast<bf16x4 *>(Hb + L::hAn + gfrag_off(I, J) + lane * 16) = cvt4(-gsum);
+            };
+            {
+                // lane (gq, j = r16) holds G[t = 16 pw + j][s = 16 pw + 4 gq + e]:
+                // -A[t][s] = -beta_t G[t][s] (s < t) goes to this wave's scratch
+                // row-major, the row-wise inverse reads it back in order
+                const f32x4 gsum = sum4(gblk(pw, pw));
+                const float bt = sBeta[16 * pw + r16];
+                float *sAd = reinterpret_cast<float *>(smem + L::pAd) + pw * 256;
                 f32x4 na;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) na[e] = (s0 + e < t) ? -bt * aA[e] : 0.f;
+                for (int e = 0; e < 4; ++e) na[e] = (4 * gq + e < r16) ? -bt * gsum[e] : 0.f;
                 *reinterpret_cast<f32x4 *>(sAd + r16 * 16 + 4 * gq) = na;
-                const f32x4 tr = unit_lower_inverse16_rows(sAd);
-                *reinterpret_cast<bf16x4 *>(reinterpret_cast<__bf16 *>(Hb + L::hTd) +
-                                            (16 * pw + (lane >> 2)) * L::LDD + 4 * (lane & 3)) = cvt4(tr);
+                const f32x4 tr = unit_lower_inverse16_rows(sAd);   // lane 4j + p: T[j][4p .. 4p+3]
+                const f32x4 bs = *reinterpret_cast<const f32x4 *>(sBeta + 16 * pw + 4 * (lane & 3));
+                *reinterpret_cast<bf16x4 *>(Hb + L::hTd + ((16 * pw + (lane >> 2)) * L::LDD + 4 * (lane & 3)) * 2) =
+                    cvt4(tr * bs);
             }
-            auto pairs = [&](auto i1c, auto i2c, auto jc) __attribute__((always_inline)) {
-                constexpr int I1 = decltype(i1c)::value, I2 = decltype(i2c)::value, J = decltype(jc)::value;
-                constexpr int IM = I2 > 0 ? I2 : I1;       // E rows J .. IM-1 are needed
-                constexpr int NH = NKB / 2;
-                f32x4 aA1 = {0.f, 0.f, 0.f, 0.f}, aA2 = aA1;
-#pragma unroll
-                for (int hb = 0; hb < NKB; hb += NH) {
-                    Frag<__bf16> fa[NH], fk1[NH], fk2[NH];
-                    f32x4 Ef[NH][IM - J][2];
-#pragma unroll
-                    for (int i = 0; i < NH; ++i) {
-                        const int kb = hb + i;
-                        fa[i] = sg_frag(sKI, 16 * J, kb);
-                        fk1[i] = sg_frag(sKL, 16 * I1, kb);
-                        if constexpr (I2 > 0) fk2[i] = sg_frag(sKL, 16 * I2, kb);
-#pragma unroll
-                        for (int bb = J; bb < IM; ++bb) {
-                            const float *F = sE + bb * K + 32 * kb + 8 * gq;
-                            Ef[i][bb - J][0] = *reinterpret_cast<const f32x4 *>(F);
-                            Ef[i][bb - J][1] = *reinterpret_cast<const f32x4 *>(F + 4);
-                        }
-                    }
-                    GDN_SCHED_FENCE();
-#pragma unroll
-                    for (int i = 0; i < NH; ++i) {
-                        f32x4 f0 = Ef[i][0][0], f1 = Ef[i][0][1];
-#pragma unroll
-                        for (int bb = J + 1; bb < I1; ++bb) {
-                            f0 *= Ef[i][bb - J][0];
-                            f1 *= Ef[i][bb - J][1];
-                        }
-                        f32x4 x0, x1;
-                        unpack8(fa[i].v, x0, x1);
-                        aA1 = mma(aA1, Frag<__bf16>{pack8(x0 * f0, x1 * f1)}, fk1[i]);
-                        if constexpr (I2 > 0) {
-#pragma unroll
-                            for (int bb = I1; bb < I2; ++bb) {
-                                f0 *= Ef[i][bb - J][0];
-                                f1 *= Ef[i][bb - J][1];
-                            }
-                            aA2 = mma(aA2, Frag<__bf16>{pack8(x0 * f0, x1 * f1)}, fk2[i]);
-                        }
-                    }
-                }
-                const int s0 = 16 * J + 4 * gq;
-                {
-                    const int t = 16 * I1 + r16;
-                    *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * L::LDC + frag_col(s0)) = cvt4(aA1 * -sB[t]);
-                }
-                if constexpr (I2 > 0) {
-                    const int t = 16 * I2 + r16;
-                    *reinterpret_cast<bf16x4 *>(sAn + (t - 16) * L::LDC + frag_col(s0)) = cvt4(aA2 * -sB[t]);
-                }
-            };
             using std::integral_constant;
-            if (pw == 0) pairs(integral_constant<int, 1>(), integral_constant<int, 3>(), integral_constant<int, 0>());
-            else if (pw == 1) pairs(integral_constant<int, 2>(), integral_constant<int, 3>(), integral_constant<int, 1>());
-            else if (pw == 2) pairs(integral_constant<int, 3>(), integral_constant<int, 0>(), integral_constant<int, 2>());
-            else pairs(integral_constant<int, 2>(), integral_constant<int, 0>(), integral_constant<int, 0>());
-            // the v copies of chunk n landed before the hand-over barrier; the
-            // 16 loads of chunk n + 1 issued after them may stay in flight
-            if (n + 1 < c1) wait_vm<16>();
-            else wait_vm<0>();
+            if (pw == 0) {
+                offdiag(integral_constant<int, 1>(), integral_constant<int, 0>());
+                offdiag(integral_constant<int, 3>(), integral_constant<int, 0>());
+            } else if (pw == 1) {
+                offdiag(integral_constant<int, 2>(), integral_constant<int, 1>());
+                offdiag(integral_constant<int, 3>(), integral_constant<int, 1>());
+            } else if (pw == 2) {
+                offdiag(integral_constant<int, 3>(), integral_constant<int, 2>());
+            } else {
+                offdiag(integral_constant<int, 2>(), integral_constant<int, 0>());
+            }
         };
 
         if (c0 < c1) {
             fetch(c0, nx);
+            if (c0 + 1 < c1) prefetch_l2(c0 + 1);
             prepare(c0);
             lds_barrier();                      // chunk c0 is ready
         }
@@ -430,111 +430,137 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
     int k_tr[NKB];
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) k_tr[kk] = sg_off(trow, 4 * kk + tq);
+    // v in the accumulator layout from the fragment-major tile: lane 4i + a of a
+    // 16-lane group addresses token 4 gq + i, columns 16 cgv + 4 a .. +3
     int v_tr[4];
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg) v_tr[cg] = sg_off(trow, 2 * (4 * cw + cg) + (tq >> 1)) + 8 * (tq & 1);
+    for (int cg = 0; cg < 4; ++cg) {
+        const int cgv = (4 * cw + cg) & 7;
+        v_tr[cg] = (cgv >> 1) * 1024 + (16 * (2 * (cgv & 1) + (tq >> 1)) + trow) * 16 + 8 * (tq & 1);
+    }
 
-    if (c0 < c1) lds_barrier();             // chunk c0 is ready
+    // v copies: this wave fills the four fragments of token block cw of a
+    // chunk, lane (gq, r16) the 16 bytes of token 16 cw + r16, columns
+    // 32 cb + 8 gq .. +7; a chunk's copies go out a period ahead and land
+    // before the hand-over barrier
+    unsigned voff[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) voff[cb] = 2u * (unsigned)((16 * cw + r16) * H * K + 32 * cb + 8 * gq);
+    auto copy_v = [&](int n) __attribute__((always_inline)) {
+        char *dst = hbuf(n) + L::hV + 4 * cw * 1024;
+        const int t0 = n * SG_T;
+        if (t0 + SG_T <= T) {
+            const __bf16 *vb = a.v + (row_base + (long)t0 * H) * K;   // wave-uniform
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) g2lds16s(vb, voff[cb], dst + cb * 1024);
+        } else {
+            const int t = min(t0 + 16 * cw + r16, T - 1);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+                g2lds16(a.v + (row_base + (long)t * H) * K + 32 * cb + 8 * gq, dst + cb * 1024);
+        }
+    };
+    if (c0 < c1) {
+        copy_v(c0);
+        wait_vm<0>();
+        lds_barrier();                      // chunk c0 is ready
+    }
 
     for (int c = c0; c < c1; ++c) {
+        if (c + 1 < c1) copy_v(c + 1);
         if (active) {
             const char *Hb = hbuf(c);
             const char *sKP = Hb + L::hKP;
             const unsigned vbase = lds_u32(Hb + L::hV);
-            const __bf16 *sAn = reinterpret_cast<const __bf16 *>(Hb + L::hAn);
+            const char *sAn = Hb + L::hAn;
             const __bf16 *sTd = reinterpret_cast<const __bf16 *>(Hb + L::hTd);
-            const float *sBeta = reinterpret_cast<const float *>(Hb + L::hBeta);
             const float *sEgn = reinterpret_cast<const float *>(Hb + L::hEgn);
             unsigned ktr_addr[NKB];
 #pragma unroll
             for (int kk = 0; kk < NKB; ++kk) ktr_addr[kk] = opaque(lds_u32(Hb + L::hKM) + k_tr[kk]);
 
+            // Phases A and B, one 16-column tile at a time: X = V - K+ S (V = 0
+            // in the columns of M), then the block forward substitution
+            // D_i = T'_ii (X_i - sum_{j<i} G_ij D_j) (-G stored).
+            Frag<__bf16> Df[4][2];
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                // Phases A and B, one 16-column tile at a time: K+ S, then
-                // X = diag(beta)(V - K+ S) (V = 0 in the columns of M) and
-                // (I + A) D = X by block forward substitution (-A stored).
-                Frag<__bf16> Df[2][2];
+            for (int cg = 0; cg < 4; ++cg) {
+                Frag<__bf16> Sf[NKB];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int cg = 2 * half + j;
-                    Frag<__bf16> Sf[NKB];
+                for (int kb = 0; kb < NKB; ++kb) Sf[kb] = reg_frag<__bf16>(S[cg][2 * kb], S[cg][2 * kb + 1]);
+                f32x4 X[4];
 #pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) Sf[kb] = reg_frag<__bf16>(S[cg][2 * kb], S[cg][2 * kb + 1]);
-                    f32x4 X[4];
+                for (int rt = 0; rt < 4; ++rt) {
+                    Frag<__bf16> fk[NKB];
 #pragma unroll
-                    for (int rt = 0; rt < 4; ++rt) {
-                        Frag<__bf16> fk[NKB];
+                    for (int kb = 0; kb < NKB; ++kb) fk[kb] = {*reinterpret_cast<const bf16x8 *>(sKP + fm_off(rt, kb))};
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int kb = 0; kb < NKB; ++kb) fk[kb] = sg_frag(sKP, 16 * rt, kb);
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int kb = 0; kb < NKB; ++kb) acc = mma(acc, fk[kb], Sf[kb]);
-                        X[rt] = acc;
-                    }
-                    GDN_SCHED_FENCE();
-#pragma unroll
-                    for (int rt = 0; rt < 4; ++rt) {
-                        const f32x4 bt = *reinterpret_cast<const f32x4 *>(sBeta + 16 * rt + 4 * gq);
-                        if (!mcols) {
-                            const bf16x4 vv = lds_read_tr(vbase + v_tr[cg] + 16 * rt * L::RB);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) X[rt][e] = bt[e] * ((float)vv[e] - X[rt][e]);
-                        } else {
-                            X[rt] = -(bt * X[rt]);
-                        }
-                    }
-                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    f32x4 Dd[4];
-                    Dd[0] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 0, 0), reg_frag<__bf16>(X[0], z));
-                    f32x4 Y = mma_lo(X[1], lds_frag_fo_lo(sAn, L::LDC, 0, 0), reg_frag<__bf16>(Dd[0], z));
-                    Dd[1] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 16, 0), reg_frag<__bf16>(Y, z));
-                    Df[j][0] = reg_frag<__bf16>(Dd[0], Dd[1]);
-                    Y = mma(X[2], lds_frag_fo(sAn, L::LDC, 16, 0), Df[j][0]);
-                    f32x4 Y3 = mma(X[3], lds_frag_fo(sAn, L::LDC, 32, 0), Df[j][0]);
-                    Dd[2] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 32, 0), reg_frag<__bf16>(Y, z));
-                    Y3 = mma_lo(Y3, lds_frag_fo_lo(sAn, L::LDC, 32, 32), reg_frag<__bf16>(Dd[2], z));
-                    Dd[3] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 48, 0), reg_frag<__bf16>(Y3, z));
-                    Df[j][1] = reg_frag<__bf16>(Dd[2], Dd[3]);
-                    GDN_SCHED_FENCE();
-                }
-
-                // Phase D: S' = Diag(e^{gn}) S + K-^T D for the columns of this half
-#pragma unroll
-                for (int ct = 0; ct < 8; ++ct) {
-                    const unsigned pk = ktr_addr[ct >> 1] + 8 * (ct & 1);
-                    bf16x4 kt[4];
-#pragma unroll
-                    for (int kb2 = 0; kb2 < 2; ++kb2) {
-                        kt[2 * kb2] = lds_read_tr(pk + L::RB * 32 * kb2);
-                        kt[2 * kb2 + 1] = lds_read_tr(pk + L::RB * (32 * kb2 + 16));
-                    }
-                    const f32x4 eg = *reinterpret_cast<const f32x4 *>(sEgn + key_of(ct, 0));
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        f32x4 s = S[2 * half + j][ct] * eg;
-#pragma unroll
-                        for (int kb2 = 0; kb2 < 2; ++kb2)
-                            s = mma(s, Frag<__bf16>{cat8(kt[2 * kb2], kt[2 * kb2 + 1])}, Df[j][kb2]);
-                        S[2 * half + j][ct] = s;
-                    }
+                    for (int kb = 0; kb < NKB; ++kb) acc = mma(acc, fk[kb], Sf[kb]);
+                    X[rt] = acc;
                 }
                 GDN_SCHED_FENCE();
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    if (!mcols) {
+                        const bf16x4 vv = lds_read_tr(vbase + v_tr[cg] + 4096 * rt);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) X[rt][e] = (float)vv[e] - X[rt][e];
+                    } else {
+                        X[rt] = -X[rt];
+                    }
+                }
+                const bf16x4 zz = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+                auto lo_frag = [&](int off) __attribute__((always_inline)) {
+                    return Frag<__bf16>{cat8(*reinterpret_cast<const bf16x4 *>(sAn + off + lane * 16), zz)};
+                };
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                f32x4 Dd[4];
+                Dd[0] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 0, 0), reg_frag<__bf16>(X[0], z));
+                f32x4 Y = mma_lo(X[1], lo_frag(0), reg_frag<__bf16>(Dd[0], z));
+                Dd[1] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 16, 0), reg_frag<__bf16>(Y, z));
+                Df[cg][0] = reg_frag<__bf16>(Dd[0], Dd[1]);
+                Y = mma(X[2], Frag<__bf16>{*reinterpret_cast<const bf16x8 *>(sAn + 1024 + lane * 16)}, Df[cg][0]);
+                f32x4 Y3 = mma(X[3], Frag<__bf16>{*reinterpret_cast<const bf16x8 *>(sAn + 2048 + lane * 16)}, Df[cg][0]);
+                Dd[2] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 32, 0), reg_frag<__bf16>(Y, z));
+                Y3 = mma_lo(Y3, lo_frag(3072), reg_frag<__bf16>(Dd[2], z));
+                Dd[3] = mma_lo(z, lds_frag_lo(sTd, L::LDD, 48, 0), reg_frag<__bf16>(Y3, z));
+                Df[cg][1] = reg_frag<__bf16>(Dd[2], Dd[3]);
+            }
+
+            // Phase D: S' = Diag(e^{gn}) S + K-^T D for all 64 columns, the k^T
+            // fragments of each key tile read once.
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                const unsigned pk = ktr_addr[ct >> 1] + 8 * (ct & 1);
+                bf16x4 kt[4];
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2) {
+                    kt[2 * kb2] = lds_read_tr(pk + 256 * 32 * kb2);
+                    kt[2 * kb2 + 1] = lds_read_tr(pk + 256 * (32 * kb2 + 16));
+                }
+                const f32x4 eg = *reinterpret_cast<const f32x4 *>(sEgn + key_of(ct, 0));
+#pragma unroll
+                for (int cg = 0; cg < 4; ++cg) {
+                    f32x4 s = S[cg][ct] * eg;
+#pragma unroll
+                    for (int kb2 = 0; kb2 < 2; ++kb2)
+                        s = mma(s, Frag<__bf16>{cat8(kt[2 * kb2], kt[2 * kb2 + 1])}, Df[cg][kb2]);
+                    S[cg][ct] = s;
+                }
             }
         }
+        wait_vm<0>();                        // the next chunk's v landed
         lds_barrier();
     }
 
     if (!active) return;
     float *dst;
-    int ld;
     if (seg == 0) {
         dst = a.S_T + (long)bh * K * K;
-        ld = K;
     } else {
         const long slot = (long)bh * (a.nseg - 1) + (seg - 1);
         dst = (mcols ? a.mapM : a.mapN) + slot * K * K;
-        ld = K;
     }
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg) {
@@ -542,7 +568,7 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[key_of(ct, e) * ld + col] = S[cg][ct][e];
+            for (int e = 0; e < 4; ++e) dst[key_of(ct, e) * K + col] = S[cg][ct][e];
     }
 }
 
