@@ -69,6 +69,8 @@ MEASURED_TRAFFIC = {
                                                   "1fb5d0b92490e05a", 1307185835),
     "recurrent_step_prologue_kernel<bf16,128,128,channel,silu>": (("prologue.hip", "prologue.h",
                                                                   "gdn_common.h"), "1fb5d0b92490e05a", 1719304713),
+    "chunk_fwd_seg/channel_long": (("chunk_fwd_seg.hip", "ws_common.h", "gdn_common.h",
+                                    "mfma_frag.h"), "5b835b50d5c71204", 13596717888),
 }
 
 # bf16 matrix-core work per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16, units of 512
@@ -78,8 +80,6 @@ MEASURED_MFMA_MOPS = {
                                   "mfma_frag.h"),
                                  "34acdf37d6007014", 257949696),
 }
-
-SEG_SOURCES = ("chunk_fwd_seg.hip", "ws_common.h", "gdn_common.h", "mfma_frag.h")
 
 
 def _digest(files):
