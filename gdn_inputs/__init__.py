@@ -25,7 +25,7 @@ import torch
 
 __all__ = ["ChunkConfig", "DecodeConfig", "CHUNK_CONFIGS", "DECODE_CONFIG", "BWD_CONFIG",
            "chunk_inputs", "decode_inputs", "grad_inputs", "prologue_inputs", "head_tokens",
-           "hard_reset_gate"]
+           "hard_reset_gate", "decoupled_gates"]
 
 
 @dataclass(frozen=True)
@@ -167,6 +167,18 @@ def hard_reset_gate(shape, seed: int, device="cpu") -> torch.Tensor:
     reset = torch.rand(*shape, **f32) < 0.125
     deep = -20.0 - 180.0 * torch.rand(*shape, **f32)
     return torch.where(reset, deep, g).contiguous()
+
+
+def decoupled_gates(shape, seed: int, device="cpu"):
+    """Erase and write gates of the decoupled-gate variant: two independent draws
+    of sigmoid(N(0, 1)) of the given shape (beta's distribution), from a generator
+    seeded with seed + 104729 so that adding them changes none of the other inputs.
+    Returns (erase, write) fp32."""
+    gen = _gen(torch.device(device), seed + 104729)
+    f32 = dict(device=device, dtype=torch.float32, generator=gen)
+    erase = torch.sigmoid(torch.randn(*shape, **f32))
+    write = torch.sigmoid(torch.randn(*shape, **f32))
+    return erase.contiguous(), write.contiguous()
 
 
 def grad_inputs(cfg: ChunkConfig, device="cpu", seed: Optional[int] = None):
