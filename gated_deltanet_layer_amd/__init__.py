@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
     gdn_chunk_fwd_noalloc(q, k, v, g, beta, S0, o, S_T, chunk=64)
     gdn_recurrent_step(q, k, v, g, beta, S, o)
     gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist)
+    gdn_chunk_fwd_decoupled(q, k, v, g, erase, write, S0, o, S_T, chunk=64)
+    gdn_recurrent_step_decoupled(q, k, v, g, erase, write, S, o)
     gdn_chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace)
     gdn_chunk_bwd_workspace_size(B, T, H, K, V, chunk=64) -> bytes
     gdn_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, cs_q, cs_k, cs_v,
@@ -21,6 +23,8 @@ Entry points (same names as the C ABI):
 Conveniences that allocate the outputs:
     chunk_fwd(q, k, v, g, beta, S0=None, want_o=True) -> (o, S_T)
     recurrent_step_(q, k, v, g, beta, S) -> o      (S updated in place)
+    chunk_fwd_decoupled(q, k, v, g, erase, write, S0=None, want_o=True) -> (o, S_T)
+    recurrent_step_decoupled_(q, k, v, g, erase, write, S) -> o
     chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T) -> dict of dq, dk, dv, dg, dbeta, dS0
     prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, state=None) -> dict
 """
@@ -41,7 +45,8 @@ _ACTS = {"none": GDN_ACT_NONE, "silu": GDN_ACT_SILU}
 SYMBOLS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd_ws",
            "gdn_chunk_fwd_noalloc", "gdn_recurrent_step", "gdn_recurrent_steps",
            "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_prologue",
-           "gdn_recurrent_step_prologue", "gdn_status_str", "gdn_abi_version")
+           "gdn_recurrent_step_prologue", "gdn_chunk_fwd_decoupled",
+           "gdn_recurrent_step_decoupled", "gdn_status_str", "gdn_abi_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -95,6 +100,12 @@ def lib() -> ctypes.CDLL:
         L.gdn_recurrent_step_prologue.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, vp,
                                                   vp, vp, vp, fp, vp, i, i, i, i, f, i, i, i, vp]
         L.gdn_recurrent_step_prologue.restype = i
+        L.gdn_chunk_fwd_decoupled.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp,
+                                              i, i, i, i, i, i, i, i, vp]
+        L.gdn_chunk_fwd_decoupled.restype = i
+        L.gdn_recurrent_step_decoupled.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp,
+                                                   i, i, i, i, i, i, vp]
+        L.gdn_recurrent_step_decoupled.restype = i
         L.gdn_status_str.argtypes = [i]
         L.gdn_status_str.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -223,6 +234,42 @@ def gdn_recurrent_step(q, k, v, g, beta, S, o, stream=None) -> None:
 
     q, k [N,H,K], v [N,H,V] (fp32 or bf16), g [N,H] or [N,H,K] fp32, beta [N,H] fp32.
     """
+    N, H, K, V, gate = _step_args(q, k, v, g, beta, S, o)
+    rc = lib().gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S),
+                                  _ptr(o), N, H, K, V, _dtype_code(q), gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_recurrent_step")
+
+
+def gdn_recurrent_step_decoupled(q, k, v, g, erase, write, S, o, stream=None) -> None:
+    """gdn_recurrent_step with separate erase and write gates (erase, write [N,H]
+    fp32): S' = (I - e k k^T) Diag(alpha) S + w k v^T."""
+    import torch
+    N, H, K, V, gate = _step_args(q, k, v, g, erase, S, o)
+    _check(write, "write", (N, H), torch.float32, q.device)
+    rc = lib().gdn_recurrent_step_decoupled(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(erase),
+                                            _ptr(write), _ptr(S), _ptr(o), N, H, K, V,
+                                            _dtype_code(q), gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_recurrent_step_decoupled")
+
+
+def gdn_chunk_fwd_decoupled(q, k, v, g, erase, write, S0, o, S_T, chunk: int = 64,
+                            stream=None) -> None:
+    """gdn_chunk_fwd with separate erase and write gates (erase, write [B,T,H] fp32):
+    S_t = (I - e_t k_t k_t^T) Diag(alpha_t) S_{t-1} + w_t k_t v_t^T."""
+    import torch
+    B, T, H, K, V, gate = _chunk_fwd_args(q, k, v, g, erase, S0, o, S_T)
+    _check(write, "write", (B, T, H), torch.float32, q.device)
+    rc = lib().gdn_chunk_fwd_decoupled(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(erase),
+                                       _ptr(write), _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, K,
+                                       V, int(chunk), _dtype_code(q), gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd_decoupled")
+
+
+def _step_args(q, k, v, g, beta, S, o):
+    """Check the tensors of a decode step; returns (N, H, K, V, gate)."""
     import torch
     if q.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be [N, H, D]")
@@ -244,10 +291,7 @@ def gdn_recurrent_step(q, k, v, g, beta, S, o, stream=None) -> None:
     _check(beta, "beta", (N, H), torch.float32, dev)
     _check(S, "S", (N, H, K, V), torch.float32, dev)
     _check(o, "o", (N, H, V), dt, dev)
-    rc = lib().gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S),
-                                  _ptr(o), N, H, K, V, _dtype_code(q), gate, _stream(stream))
-    if rc != GDN_OK:
-        raise GDNError(rc, "gdn_recurrent_step")
+    return N, H, K, V, gate
 
 
 def gdn_recurrent_steps(q, k, v, g, beta, S0, o, S_T, S_hist=None, stream=None) -> None:
@@ -387,6 +431,28 @@ def chunk_fwd(q, k, v, g, beta, S0=None, want_o: bool = True, chunk: int = 64, s
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
     gdn_chunk_fwd_ws(q, k, v, g, beta, S0, o, S_T, workspace, chunk=chunk, stream=stream)
     return o, S_T
+
+
+def chunk_fwd_decoupled(q, k, v, g, erase, write, S0=None, want_o: bool = True,
+                        chunk: int = 64, stream=None):
+    """Allocate o (if wanted) and S_T, run gdn_chunk_fwd_decoupled, return (o, S_T)."""
+    import torch
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device) if want_o else None
+    S_T = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
+    gdn_chunk_fwd_decoupled(q, k, v, g, erase, write, S0, o, S_T, chunk=chunk, stream=stream)
+    return o, S_T
+
+
+def recurrent_step_decoupled_(q, k, v, g, erase, write, S, o=None, stream=None):
+    """One decode step with separate erase and write gates; S is updated in
+    place.  Returns o [N,H,V]."""
+    import torch
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    gdn_recurrent_step_decoupled(q, k, v, g, erase, write, S, o, stream=stream)
+    return o
 
 
 def recurrent_step_(q, k, v, g, beta, S, o=None, stream=None):

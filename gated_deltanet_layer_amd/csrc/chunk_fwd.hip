@@ -67,7 +67,8 @@ template <typename OT, int K, bool CH> struct Smem {
     static constexpr int kAd = align(kTd + CH_T * LDD * E);      // [4 waves][16][LDA] fp32
     static constexpr int kBeta = align(kAd + 4 * 16 * LDA * 4);
     static constexpr int kG = kBeta + CH_T * 4;                   // scalar g [64]
-    static constexpr int kW = kG + CH_T * 4;                      // [4 waves][3][64]
+    static constexpr int kWg = kG + CH_T * 4;                     // write gate [64]
+    static constexpr int kW = kWg + CH_T * 4;                     // [4 waves][3][64]
     static constexpr int kLam = align(kW + 4 * 3 * CH_T * 4);     // channel: [4][K]
     static constexpr int kER = kLam + (CH ? 4 * K * 4 : 0);       // [5][K] e^{R_b}
     static constexpr int kFP = kER + (CH ? 5 * K * 4 : 0);        // [6][K] e^{R_i - R_j}
@@ -81,6 +82,7 @@ __device__ __forceinline__ int pair_idx(int i, int j) { return i * (i - 1) / 2 +
 struct ChunkArgs {
     const void *q, *k, *v;
     const float *g, *beta, *S0;
+    const float *wgate;   // decoupled write gate, or nullptr (beta writes too)
     void *o;
     float *S_T;
     int B, T, H, V, nvb;
@@ -117,6 +119,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
     OT *sTd = reinterpret_cast<OT *>(smem + L::kTd);
     float *sBeta = reinterpret_cast<float *>(smem + L::kBeta);
     float *sG = reinterpret_cast<float *>(smem + L::kG);
+    float *sWg = reinterpret_cast<float *>(smem + L::kWg);
     float *sLam = reinterpret_cast<float *>(smem + L::kLam);
     float *sER = reinterpret_cast<float *>(smem + L::kER);
     float *sFP = reinterpret_cast<float *>(smem + L::kFP);
@@ -172,7 +175,8 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
     const int cg = tid % CG, rg = tid / CG;
     vec_t pk[RPT], pq[RPT], pv[NVV];
     float pgc[CH ? 16 : 1][CH ? CPT : 1];
-    float pb = 0.f, pgs = 0.f;
+    float pb = 0.f, pgs = 0.f, pw = 0.f;
+    const float *wsrc = args.wgate ? args.wgate : args.beta;
     auto load_chunk = [&](int t0) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
@@ -198,6 +202,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
         if constexpr (!CH)
             pgs = (tid < CH_T && t0 + tid < T) ? args.g[row_base + (long)(t0 + tid) * H] : 0.f;
         pb = (tid < CH_T && t0 + tid < T) ? args.beta[row_base + (long)(t0 + tid) * H] : 0.f;
+        pw = (tid < CH_T && t0 + tid < T) ? wsrc[row_base + (long)(t0 + tid) * H] : 0.f;
     };
     auto load_gate = [&](int t0) {  // per-channel gate, in the prep mapping
         if constexpr (CH) {
@@ -259,6 +264,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
         }
         if (tid < CH_T) {
             sBeta[tid] = pb;
+            sWg[tid] = pw;
             if (!CH) sG[tid] = pgs;
         }
         lds_barrier();
@@ -427,15 +433,19 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
 
         // ---- state chain (per wave, its 16 value columns) ----
         {
-            // X = diag(beta) (V - K+ S)
+            // X = diag(beta) (V - K+ S); with decoupled gates
+            // X = diag(w) V - diag(e) K+ S (e in beta's place)
             f32x4 X[4];
+            const bool dgate = args.wgate != nullptr;
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const f32x4 bt = *reinterpret_cast<const f32x4 *>(sBeta + 16 * rt + 4 * gq);
+                const f32x4 wt = *reinterpret_cast<const f32x4 *>(sWg + 16 * rt + 4 * gq);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * rt + 4 * gq + e;
-                    X[rt][e] = bt[e] * (to_f32(sV[t * L::LDC + vcol]) - KS[rt][e]);
+                    const float vv = to_f32(sV[t * L::LDC + vcol]);
+                    X[rt][e] = dgate ? wt[e] * vv - bt[e] * KS[rt][e] : bt[e] * (vv - KS[rt][e]);
                 }
             }
             // (I + A) D = X by block forward substitution (sAn holds -A)
@@ -527,6 +537,22 @@ hipError_t chunk_fwd_wsc_launch(int K, const void *q, const void *k, const void 
                                 const float *beta, const float *S0, void *o, float *S_T, int B,
                                 int T, int H, int V, hipStream_t st);
 
+static ChunkArgs chunk_args(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *wgate, const float *S0, void *o,
+                            float *S_T, int B, int T, int H, int V)
+{
+    ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = S0; a.o = o; a.S_T = S_T;
+    a.wgate = wgate;
+    a.B = B; a.T = T; a.H = H; a.V = V;
+    a.nvb = V / VBLK;
+    const long bhn = (long)B * H;
+    // The hardware hands consecutive workgroups to the 8 XCDs in turn; keep the
+    // column blocks of one head on one XCD so its q/k/g are fetched into one L2.
+    a.xcd_map = (a.nvb > 1 && bhn % 8 == 0) ? 1 : 0;
+    return a;
+}
+
 // Host entry used by the C ABI after validation.  bf16 operands take the
 // warp-specialised kernels (chunk_fwd_ws.hip for the scalar gate,
 // chunk_fwd_wsc.hip for the per-channel gate).
@@ -538,16 +564,24 @@ hipError_t chunk_fwd_launch(bool bf16, bool channel, int K, const void *q, const
         return chunk_fwd_ws_launch(K, q, k, v, g, beta, S0, o, S_T, B, T, H, V, st);
     if (bf16 && channel)
         return chunk_fwd_wsc_launch(K, q, k, v, g, beta, S0, o, S_T, B, T, H, V, st);
-    ChunkArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = S0; a.o = o; a.S_T = S_T;
-    a.B = B; a.T = T; a.H = H; a.V = V;
-    a.nvb = V / VBLK;
-    const long bhn = (long)B * H;
-    // The hardware hands consecutive workgroups to the 8 XCDs in turn; keep the
-    // column blocks of one head on one XCD so its q/k/g are fetched into one L2.
-    a.xcd_map = (a.nvb > 1 && bhn % 8 == 0) ? 1 : 0;
+    const ChunkArgs a = chunk_args(q, k, v, g, beta, nullptr, S0, o, S_T, B, T, H, V);
     // fp32 operands (K = 64)
     return channel ? launch_chunk<float, 64, true>(a, st) : launch_chunk<float, 64, false>(a, st);
+}
+
+// Decoupled erase/write gates (erase in beta's place, write gate w): every
+// storage type and K take the kernel above.
+hipError_t chunk_fwd_dg_launch(bool bf16, bool channel, int K, const void *q, const void *k,
+                               const void *v, const float *g, const float *erase,
+                               const float *write, const float *S0, void *o, float *S_T, int B,
+                               int T, int H, int V, hipStream_t st)
+{
+    const ChunkArgs a = chunk_args(q, k, v, g, erase, write, S0, o, S_T, B, T, H, V);
+    if (!bf16)
+        return channel ? launch_chunk<float, 64, true>(a, st) : launch_chunk<float, 64, false>(a, st);
+    if (K == 64)
+        return channel ? launch_chunk<__bf16, 64, true>(a, st) : launch_chunk<__bf16, 64, false>(a, st);
+    return channel ? launch_chunk<__bf16, 128, true>(a, st) : launch_chunk<__bf16, 128, false>(a, st);
 }
 
 } // namespace gdn

@@ -14,10 +14,14 @@ namespace gdn {
 hipError_t chunk_fwd_launch(bool bf16, bool channel, int K, const void *q, const void *k,
                             const void *v, const float *g, const float *beta, const float *S0,
                             void *o, float *S_T, int B, int T, int H, int V, hipStream_t st);
+hipError_t chunk_fwd_dg_launch(bool bf16, bool channel, int K, const void *q, const void *k,
+                               const void *v, const float *g, const float *erase,
+                               const float *write, const float *S0, void *o, float *S_T, int B,
+                               int T, int H, int V, hipStream_t st);
 hipError_t recurrent_step_launch(bool bf16, bool channel, int K, int V, const void *q,
                                  const void *k, const void *v, const float *g,
-                                 const float *beta, float *S, void *o, long nslices,
-                                 hipStream_t st);
+                                 const float *beta, const float *wg, float *S, void *o,
+                                 long nslices, hipStream_t st);
 int chunk_fwd_seg_count(long B, long T, long H);
 unsigned long long chunk_fwd_seg_workspace(long B, long H, int nseg);
 hipError_t chunk_fwd_seg_launch(const void *k, const void *v, const float *g, const float *beta,
@@ -261,9 +265,16 @@ gdn_status gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, co
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
-gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v, const float *g,
-                              const float *beta, float *S, void *o, int N, int H, int K,
-                              int V, gdn_dtype dtype, gdn_gate gate, void *stream)
+} // extern "C"
+
+namespace {
+
+// Checks and launch of one decode step; wg is the decoupled write gate or
+// nullptr (beta writes too).
+gdn_status recurrent_step_impl(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *wg, bool need_wg, float *S,
+                               void *o, int N, int H, int K, int V, gdn_dtype dtype,
+                               gdn_gate gate, void *stream)
 {
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_EINVAL;
     if (gate != GDN_GATE_HEAD && gate != GDN_GATE_CHANNEL) return GDN_EINVAL;
@@ -273,18 +284,20 @@ gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v, const
     if (ns < 0 || nqk < 0 || nv < 0 || nst < 0) return GDN_EINVAL;
     const long long ng = gate == GDN_GATE_CHANNEL ? nqk : ns;
     if (ns > 0 && (!q || !k || !v || !g || !beta || !S)) return GDN_EINVAL;
+    if (ns > 0 && need_wg && !wg) return GDN_EINVAL;
     // The state is streamed as 16-byte vectors; the vectors are read per element.
     if (S && !aligned16(S)) return GDN_EINVAL;
     for (const void *p : {q, k, v, (const void *)o})
         if (p && !aligned(p, (unsigned)es)) return GDN_EINVAL;
-    for (const void *p : {(const void *)g, (const void *)beta})
+    for (const void *p : {(const void *)g, (const void *)beta, (const void *)wg})
         if (p && !aligned(p, 4)) return GDN_EINVAL;
     const Range rq = range(q, nqk * es), rk = range(k, nqk * es), rv = range(v, nv * es);
     const Range rg = range(g, ng * 4), rb = range(beta, ns * 4), rs = range(S, nst * 4);
+    const Range rw = range(wg, wg ? ns * 4 : 0);
     const Range ro = range(o, o ? nv * es : 0);
-    for (Range r : {rq, rk, rv, rg, rb, rs})
+    for (Range r : {rq, rk, rv, rg, rb, rw, rs})
         if (overlap(ro, r)) return GDN_EINVAL;
-    for (Range r : {rq, rk, rv, rg, rb})
+    for (Range r : {rq, rk, rv, rg, rb, rw})
         if (overlap(rs, r)) return GDN_EINVAL;
 
     if (!kv_supported(K) || !kv_supported(V)) return GDN_ENOTSUP;
@@ -292,8 +305,52 @@ gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v, const
     if (ns == 0) return GDN_OK;
 
     const hipError_t e = gdn::recurrent_step_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL,
-                                                    K, V, q, k, v, g, beta, S, o, ns,
+                                                    K, V, q, k, v, g, beta, wg, S, o, ns,
                                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+} // namespace
+
+extern "C" {
+
+gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, float *S, void *o, int N, int H, int K,
+                              int V, gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    return recurrent_step_impl(q, k, v, g, beta, nullptr, false, S, o, N, H, K, V, dtype, gate,
+                               stream);
+}
+
+gdn_status gdn_recurrent_step_decoupled(const void *q, const void *k, const void *v,
+                                        const float *g, const float *erase, const float *write,
+                                        float *S, void *o, int N, int H, int K, int V,
+                                        gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    return recurrent_step_impl(q, k, v, g, erase, write, true, S, o, N, H, K, V, dtype, gate,
+                               stream);
+}
+
+gdn_status gdn_chunk_fwd_decoupled(const void *q, const void *k, const void *v, const float *g,
+                                   const float *erase, const float *write, const float *S0,
+                                   void *o, float *S_T, int B, int T, int H, int K, int V,
+                                   int chunk, gdn_dtype dtype, gdn_gate gate, void *stream)
+{
+    const gdn_status st = chunk_fwd_check(q, k, v, g, erase, S0, o, S_T, B, T, H, K, V, chunk,
+                                          dtype, gate);
+    if (st != GDN_OK) return st;
+    const long long ntok = prod(B, T, H);
+    if (ntok > 0 && !write) return GDN_EINVAL;
+    if (write && !aligned(write, 4)) return GDN_EINVAL;
+    const Range rw = range(write, write ? ntok * 4 : 0);
+    const long long es = dtype == GDN_BF16 ? 2 : 4;
+    if (o && overlap(range(o, prod(B, T, H, V) * es), rw)) return GDN_EINVAL;
+    if (S_T && overlap(range(S_T, prod(B, H, K, V) * 4), rw)) return GDN_EINVAL;
+    if (B == 0 || H == 0) return GDN_OK;
+    if (!S_T && T == 0) return GDN_OK;
+    const hipError_t e = gdn::chunk_fwd_dg_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL, K,
+                                                  q, k, v, g, erase, write, S0, o, S_T, B, T, H,
+                                                  V, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

@@ -8,6 +8,10 @@
 //   delta = beta (v - u)
 //   o     = y + (k . q) delta        since S'^T q = S^T(alpha*q) + delta (k^T q)
 //   S'    = Diag(alpha) S + k delta^T
+// Decoupled erase/write gates (the MindPattern page's split of beta into two
+// gates; erase e in beta's place in the removal term, write gate w in the write
+// term): S' = (I - e k k^T) Diag(alpha) S + w k v^T, so delta = w v - e u and the
+// rest is unchanged.  wg == nullptr means w = beta.
 // The step is HBM-bound: per slice it moves 2 * K * V * 4 bytes of state and a
 // few hundred bytes of vectors; it uses plain fp32 VALU work and wave-level
 // reductions, no matrix cores.
@@ -32,7 +36,7 @@ template <typename DT, int K, int V, bool CHANNEL>
 __global__ __launch_bounds__(RS_NTHR) void recurrent_step_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
-    float *__restrict__ S, DT *__restrict__ o)
+    const float *__restrict__ wg, float *__restrict__ S, DT *__restrict__ o)
 {
     constexpr int VW = V < RS_VW ? V : RS_VW;   // columns of this workgroup
     constexpr int NVW = V / VW;                 // workgroups per slice
@@ -115,11 +119,12 @@ __global__ __launch_bounds__(RS_NTHR) void recurrent_step_kernel(
             qk += s_qk[w];
         }
         const float b = beta[slice];
+        const float w = wg ? wg[slice] : 0.f;
         f32x4 d, oo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float ve = to_f32(v[slice * V + c0 + 4 * tid + e]);
-            d[e] = b * (ve - uu[e]);
+            d[e] = wg ? w * ve - b * uu[e] : b * (ve - uu[e]);
             oo[e] = yy[e] + qk * d[e];
         }
         s_delta[tid] = d;
@@ -141,38 +146,39 @@ __global__ __launch_bounds__(RS_NTHR) void recurrent_step_kernel(
 
 template <typename DT, int K, int V, bool CH>
 static hipError_t launch_step(const void *q, const void *k, const void *v, const float *g,
-                              const float *beta, float *S, void *o, long nslices,
+                              const float *beta, const float *wg, float *S, void *o, long nslices,
                               hipStream_t stream)
 {
     constexpr int NVW = V / (V < RS_VW ? V : RS_VW);
     hipLaunchKernelGGL((recurrent_step_kernel<DT, K, V, CH>), dim3((unsigned)(nslices * NVW)), dim3(RS_NTHR),
-                       0, stream, (const DT *)q, (const DT *)k, (const DT *)v, g, beta, S,
+                       0, stream, (const DT *)q, (const DT *)k, (const DT *)v, g, beta, wg, S,
                        (DT *)o);
     return hipGetLastError();
 }
 
 template <typename DT, bool CH>
 static hipError_t dispatch_kv(int K, int V, const void *q, const void *k, const void *v,
-                              const float *g, const float *beta, float *S, void *o,
-                              long nslices, hipStream_t st)
+                              const float *g, const float *beta, const float *wg, float *S,
+                              void *o, long nslices, hipStream_t st)
 {
-    if (K == 64 && V == 64) return launch_step<DT, 64, 64, CH>(q, k, v, g, beta, S, o, nslices, st);
-    if (K == 64 && V == 128) return launch_step<DT, 64, 128, CH>(q, k, v, g, beta, S, o, nslices, st);
-    if (K == 128 && V == 64) return launch_step<DT, 128, 64, CH>(q, k, v, g, beta, S, o, nslices, st);
-    return launch_step<DT, 128, 128, CH>(q, k, v, g, beta, S, o, nslices, st);
+    if (K == 64 && V == 64) return launch_step<DT, 64, 64, CH>(q, k, v, g, beta, wg, S, o, nslices, st);
+    if (K == 64 && V == 128) return launch_step<DT, 64, 128, CH>(q, k, v, g, beta, wg, S, o, nslices, st);
+    if (K == 128 && V == 64) return launch_step<DT, 128, 64, CH>(q, k, v, g, beta, wg, S, o, nslices, st);
+    return launch_step<DT, 128, 128, CH>(q, k, v, g, beta, wg, S, o, nslices, st);
 }
 
-// Host entry used by the C ABI after validation.
+// Host entry used by the C ABI after validation.  wg: the decoupled write gate,
+// or nullptr (beta both erases and writes).
 hipError_t recurrent_step_launch(bool bf16, bool channel, int K, int V, const void *q,
                                  const void *k, const void *v, const float *g,
-                                 const float *beta, float *S, void *o, long nslices,
-                                 hipStream_t st)
+                                 const float *beta, const float *wg, float *S, void *o,
+                                 long nslices, hipStream_t st)
 {
     if (bf16)
-        return channel ? dispatch_kv<__bf16, true>(K, V, q, k, v, g, beta, S, o, nslices, st)
-                       : dispatch_kv<__bf16, false>(K, V, q, k, v, g, beta, S, o, nslices, st);
-    return channel ? dispatch_kv<float, true>(K, V, q, k, v, g, beta, S, o, nslices, st)
-                   : dispatch_kv<float, false>(K, V, q, k, v, g, beta, S, o, nslices, st);
+        return channel ? dispatch_kv<__bf16, true>(K, V, q, k, v, g, beta, wg, S, o, nslices, st)
+                       : dispatch_kv<__bf16, false>(K, V, q, k, v, g, beta, wg, S, o, nslices, st);
+    return channel ? dispatch_kv<float, true>(K, V, q, k, v, g, beta, wg, S, o, nslices, st)
+                   : dispatch_kv<float, false>(K, V, q, k, v, g, beta, wg, S, o, nslices, st);
 }
 
 } // namespace gdn

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -177,6 +177,38 @@ GDN_API gdn_status gdn_recurrent_step(const void *q, const void *k, const void *
                               float *S, void *o,
                               int N, int H, int K, int V,
                               gdn_dtype dtype, gdn_gate gate, void *stream);
+
+/*
+ * Decoupled erase and write gates.  The MindPattern "Gated DeltaNet" page (its
+ * finding of 2026-05-22) names a variant that replaces the single scalar beta,
+ * which both removes the old association of k and writes the new one, by
+ * separate gates; it prints no formula.  These entry points compute the reading
+ *
+ *   S_t = (I - e_t k_t k_t^T) Diag(alpha_t) S_{t-1} + w_t k_t v_t^T,  o_t = S_t^T q_t
+ *
+ * with the erase gate e in beta's place in the removal term and the write gate
+ * w in its place in the write term; e = w = beta gives the calls above.
+ *
+ *   erase, write  [B, T, H] (prefill) or [N, H] (decode) fp32, both required
+ *                 when there is at least one token; any real values (the
+ *                 sigmoid-like range (0, 1) is the caller's choice).
+ *
+ * Every other argument, layout, check and error is that of gdn_chunk_fwd
+ * (prefill: o and S_T outputs, S_T may equal S0) and gdn_recurrent_step
+ * (decode: S updated in place); neither output may overlap `write`.  The
+ * prefill takes the sequential chunk kernel for every storage type, gate and
+ * K (fp32: K = 64), never the sequence-parallel form.
+ */
+GDN_API gdn_status gdn_chunk_fwd_decoupled(const void *q, const void *k, const void *v,
+                                           const float *g, const float *erase, const float *write,
+                                           const float *S0, void *o, float *S_T,
+                                           int B, int T, int H, int K, int V, int chunk,
+                                           gdn_dtype dtype, gdn_gate gate, void *stream);
+GDN_API gdn_status gdn_recurrent_step_decoupled(const void *q, const void *k, const void *v,
+                                                const float *g, const float *erase,
+                                                const float *write, float *S, void *o,
+                                                int N, int H, int K, int V,
+                                                gdn_dtype dtype, gdn_gate gate, void *stream);
 
 /*
  * M tokens of each of N sequences, applied in order from one state: the

@@ -41,7 +41,7 @@ def test_only_declared_symbols_are_exported():
 
 
 def test_version_and_status_strings(L):
-    assert gdn.abi_version() == 5
+    assert gdn.abi_version() == 6
     assert gdn.status_str(0) == "ok"
     assert "invalid" in gdn.status_str(1)
     assert "unsupported" in gdn.status_str(2)
@@ -422,3 +422,58 @@ def test_prologue_channel_cap_above_five_is_unsupported(L):
     assert _pro(L, gate=1, cap=5.5) == gdn.GDN_ENOTSUP
     assert _pro(L, gate=1, cap=float("inf")) == gdn.GDN_ENOTSUP
     assert _pro(L, gate=0, cap=float("inf"), K=96) == gdn.GDN_ENOTSUP   # stops at K, not the cap
+
+
+# --- decoupled erase/write gates ----------------------------------------------------
+def _chunk_dg(L, **kw):
+    q, k, v, g, e, w, S0, o, S_T = _ptrs(9)
+    a = dict(q=q, k=k, v=v, g=g, e=e, w=w, S0=S0, o=o, S_T=S_T,
+             B=2, T=100, H=3, K=128, V=128, chunk=64, dtype=1, gate=1)
+    a.update(kw)
+    return L.gdn_chunk_fwd_decoupled(a["q"], a["k"], a["v"], a["g"], a["e"], a["w"], a["S0"],
+                                     a["o"], a["S_T"], a["B"], a["T"], a["H"], a["K"], a["V"],
+                                     a["chunk"], a["dtype"], a["gate"], None)
+
+
+def _step_dg(L, **kw):
+    q, k, v, g, e, w, S, o = _ptrs(8)
+    a = dict(q=q, k=k, v=v, g=g, e=e, w=w, S=S, o=o, N=4, H=3, K=128, V=128, dtype=1, gate=1)
+    a.update(kw)
+    return L.gdn_recurrent_step_decoupled(a["q"], a["k"], a["v"], a["g"], a["e"], a["w"],
+                                          a["S"], a["o"], a["N"], a["H"], a["K"], a["V"],
+                                          a["dtype"], a["gate"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(e=None), dict(w=None), dict(w=BASE + 5 * SEP + 2), dict(e=BASE + 4 * SEP + 2),
+    dict(o=BASE + 5 * SEP),             # o aliases the write gate
+    dict(S_T=BASE + 5 * SEP + 64),      # S_T overlaps the write gate
+    dict(dtype=2), dict(gate=3), dict(T=-1), dict(o=None, S_T=None),
+])
+def test_chunk_decoupled_rejects_invalid(L, kw):
+    assert _chunk_dg(L, **kw) == gdn.GDN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(K=96), dict(chunk=32), dict(dtype=0, K=128)])
+def test_chunk_decoupled_unsupported(L, kw):
+    assert _chunk_dg(L, **kw) == gdn.GDN_ENOTSUP
+
+
+def test_chunk_decoupled_empty_is_a_noop(L):
+    assert _chunk_dg(L, B=0, q=None, k=None, v=None, g=None, e=None, w=None) == gdn.GDN_OK
+    assert _chunk_dg(L, T=0, S_T=None) == gdn.GDN_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(e=None), dict(w=None), dict(w=BASE + 5 * SEP + 1), dict(o=BASE + 5 * SEP),
+    dict(S=BASE + 5 * SEP),             # S aliases the write gate
+    dict(dtype=3), dict(N=-1),
+])
+def test_step_decoupled_rejects_invalid(L, kw):
+    assert _step_dg(L, **kw) == gdn.GDN_EINVAL
+
+
+def test_step_decoupled_unsupported_and_empty(L):
+    assert _step_dg(L, K=32) == gdn.GDN_ENOTSUP
+    assert _step_dg(L, N=0) == gdn.GDN_OK
+    assert _step_dg(L, N=0, w=None, e=None) == gdn.GDN_OK
