@@ -305,6 +305,59 @@ def bench_verify(torch, gdn, timer, M, keep_hist):
     return ent
 
 
+def bench_decoupled(torch, gdn, timer):
+    """The decoupled erase/write gates: a prefill at the per-channel workload's
+    shape through gdn_chunk_fwd_decoupled, and the decode step through
+    gdn_recurrent_step_decoupled.  Algorithmic bytes are those of the card's
+    recurrence plus the write gate (4 bytes per head-token)."""
+    from gdn_inputs import CHUNK_CONFIGS, DECODE_CONFIG, chunk_inputs, decode_inputs, decoupled_gates
+    cfg = CHUNK_CONFIGS["channel_bf16"]
+    d = chunk_inputs(cfg, device="cuda")
+    B, T, H, K, V = cfg.B, cfg.T, cfg.H, cfg.K, cfg.V
+    e, w = (x.cuda() for x in decoupled_gates((B, T, H), seed=0))
+    o = torch.empty(B, T, H, V, dtype=d["v"].dtype, device="cuda")
+    S_T = torch.empty(B, H, K, V, dtype=torch.float32, device="cuda")
+    t = timer.run(lambda: gdn.gdn_chunk_fwd_decoupled(d["q"], d["k"], d["v"], d["g"], e, w,
+                                                      d["S0"], o, S_T), max(20, timer.steps), 5)
+    nbytes = chunk_bytes(B, T, H, K, V, 2, True, True, True) + B * T * H * 4
+    s = t["ms"] / 1e3
+    pre = {"workload": f"per-key-channel-gate chunkwise forward with decoupled erase/write gates, "
+                       f"B={B} H={H} T={T} d_k=d_v={K}, bf16 q/k/v/o, fp32 g/e/w/state, "
+                       "returns o and S_T",
+           "entry": "gdn_chunk_fwd_decoupled", "kernel": "chunk_fwd_kernel<bf16,128,true>",
+           "mtok_s": B * T / s / 1e6, "gbs": nbytes / s / 1e9,
+           "frac_hbm": nbytes / s / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": nbytes}
+    pre.update(t)
+    del d, o, S_T
+    dc = DECODE_CONFIG
+    dd = decode_inputs(dc, device="cuda")
+    N, H, K, V = dc.N, dc.H, dc.K, dc.V
+    e, w = (x.cuda() for x in decoupled_gates((dc.steps, N, H), seed=0))
+    S = dd["S0"].clone()
+    o = torch.empty(dc.steps, N, H, V, dtype=torch.bfloat16, device="cuda")
+    step = [0]
+
+    def one():
+        s_ = step[0]
+        if s_ == 0:
+            S.copy_(dd["S0"])
+        gdn.gdn_recurrent_step_decoupled(dd["q"][s_], dd["k"][s_], dd["v"][s_], dd["g"][s_],
+                                         e[s_], w[s_], S, o[s_])
+        step[0] = (s_ + 1) % dc.steps
+
+    t = timer.run(one, steps=dc.steps * 2, warmup=dc.steps)
+    nbytes = decode_bytes(N, H, K, V, 2, True) + N * H * 4
+    s = t["ms_median"] / 1e3
+    dec = {"workload": f"fused recurrent decode with decoupled erase/write gates, N={N} H={H} "
+                       f"d_k=d_v={K}, per-channel gate, bf16 q/k/v/o, fp32 state in place",
+           "entry": "gdn_recurrent_step_decoupled",
+           "kernel": "recurrent_step_kernel<bf16,128,128,channel>",
+           "ms_per_step": t["ms_median"], "gbs": nbytes / s / 1e9,
+           "frac_hbm": nbytes / s / 1e9 / HBM_PEAK_GBS, "bytes_per_step": nbytes}
+    dec.update(t)
+    return {"prefill": pre, "decode": dec}
+
+
 def bwd_bytes(B, T, H, K, V, es, channel):
     """Algorithmic HBM bytes of one chunkwise backward: q, k, v, g, beta, S0, d_o and
     dS_T read once, dq, dk, dv, dg, dbeta and dS0 written once."""
@@ -382,6 +435,41 @@ def bench_prologue(torch, gdn, timer):
                     "traffic": measured_traffic("prologue_kernel<bf16,128,128,scalar,silu>"),
                     "kernel": "prologue_kernel<bf16,128,128,scalar,silu>"}
     out["chunk"].update(t)
+    # the prologue fused into the chunkwise forward, against the two launches
+    # (gdn_prologue, then gdn_chunk_fwd on its outputs), on the same raw inputs
+    fused = []
+    for gate, (Bf, Tf, Hf) in (("head", (B, T, H)), ("channel", (16, 2048, 8))):
+        if gate != "head":
+            del d, r, cso
+            d = prologue_inputs(Bf, Tf, Hf, K, V, "bf16", gate, device="cuda", seed=2)
+            r = {n: torch.empty_like(d[n]) for n in ("q_raw", "k_raw", "v_raw", "g_raw", "b_raw")}
+            cso = [torch.empty_like(d["cs_q"]), torch.empty_like(d["cs_k"]),
+                   torch.empty_like(d["cs_v"])]
+        S0 = 0.02 * torch.randn(Bf, Hf, K, V, device="cuda")
+        o = torch.empty(Bf, Tf, Hf, V, dtype=torch.bfloat16, device="cuda")
+        S_T = torch.empty_like(S0)
+        raw = [d[n] for n in ("q_raw", "k_raw", "v_raw", "g_raw", "b_raw", "w_q", "w_k", "w_v",
+                              "cs_q", "cs_k", "cs_v")]
+        one = lambda: gdn.gdn_chunk_fwd_prologue(*raw, cso[0], cso[1], cso[2], S0, o, S_T)
+
+        def two():
+            gdn.gdn_prologue(*raw, r["q_raw"], r["k_raw"], r["v_raw"], r["g_raw"], r["b_raw"],
+                             cso[0], cso[1], cso[2])
+            gdn.gdn_chunk_fwd(r["q_raw"], r["k_raw"], r["v_raw"], r["g_raw"], r["b_raw"], S0, o, S_T)
+
+        tf = timer.run(one, max(20, timer.steps), 5)
+        t2 = timer.run(two, max(20, timer.steps), 5)
+        fused.append({"workload": f"prologue + chunkwise forward from the raw projections, "
+                                  f"B={Bf} T={Tf} H={Hf} d_k=d_v={K}, "
+                                  f"{'scalar' if gate == 'head' else 'per-key-channel'} gate, bf16, "
+                                  "SiLU, carried states in and out, o and S_T",
+                      "entry": "gdn_chunk_fwd_prologue",
+                      "kernel": f"chunk_fwd_kernel<bf16,128,{'false' if gate == 'head' else 'true'},pro>",
+                      "ms_fused": tf["ms"], "ms_median_fused": tf["ms_median"],
+                      "ms_two_launches": t2["ms"], "ms_median_two_launches": t2["ms_median"],
+                      "mtok_s_fused": Bf * Tf / (tf["ms"] / 1e3) / 1e6})
+        del S0, o, S_T
+    out["chunk_fused"] = fused
     del d, r, cso
     N, H = 256, 48
     d = prologue_inputs(N, 1, H, K, V, "bf16", "channel", device="cuda", seed=1)
@@ -488,7 +576,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["all", "headline", "chunk", "decode", "verify", "bwd",
-                                       "prologue"], default="all")
+                                       "prologue", "decoupled"], default="all")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -570,6 +658,8 @@ def main():
         out["backward"] = bench_bwd(torch, gdn, timer)
     if args.only in ("all", "prologue"):
         out["prologue"] = bench_prologue(torch, gdn, timer)
+    if args.only in ("all", "decoupled"):
+        out["decoupled"] = bench_decoupled(torch, gdn, timer)
     if head_in is not None and not args.no_cpu:
         torch.cuda.synchronize()
         out["cpu_baseline"] = cpu_baseline(head_in, head_cfg)

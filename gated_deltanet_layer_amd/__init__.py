@@ -20,6 +20,8 @@ Entry points (same names as the C ABI):
                  q, k, v, g, beta, cs_q_out, cs_k_out, cs_v_out, g_cap=5.0, act="silu")
     gdn_recurrent_step_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v,
                  cs_q, cs_k, cs_v, cs_q_out, cs_k_out, cs_v_out, S, o, g_cap=5.0, act="silu")
+    gdn_chunk_fwd_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, cs_q, cs_k, cs_v,
+                 cs_q_out, cs_k_out, cs_v_out, S0, o, S_T, chunk=64, g_cap=5.0, act="silu")
 Conveniences that allocate the outputs:
     chunk_fwd(q, k, v, g, beta, S0=None, want_o=True) -> (o, S_T)
     recurrent_step_(q, k, v, g, beta, S) -> o      (S updated in place)
@@ -27,6 +29,8 @@ Conveniences that allocate the outputs:
     recurrent_step_decoupled_(q, k, v, g, erase, write, S) -> o
     chunk_bwd(q, k, v, g, beta, S0, d_o, dS_T) -> dict of dq, dk, dv, dg, dbeta, dS0
     prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, state=None) -> dict
+    chunk_fwd_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, state=None, S0=None)
+        -> (o, S_T, state)
 """
 from __future__ import annotations
 
@@ -46,7 +50,8 @@ SYMBOLS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd_ws",
            "gdn_chunk_fwd_noalloc", "gdn_recurrent_step", "gdn_recurrent_steps",
            "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_prologue",
            "gdn_recurrent_step_prologue", "gdn_chunk_fwd_decoupled",
-           "gdn_recurrent_step_decoupled", "gdn_status_str", "gdn_abi_version")
+           "gdn_recurrent_step_decoupled", "gdn_chunk_fwd_prologue", "gdn_status_str",
+           "gdn_abi_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -106,6 +111,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_recurrent_step_decoupled.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp,
                                                    i, i, i, i, i, i, vp]
         L.gdn_recurrent_step_decoupled.restype = i
+        L.gdn_chunk_fwd_prologue.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, vp, vp, vp,
+                                             vp, fp, vp, fp, i, i, i, i, i, i, f, i, i, i, vp]
+        L.gdn_chunk_fwd_prologue.restype = i
         L.gdn_status_str.argtypes = [i]
         L.gdn_status_str.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -530,6 +538,57 @@ def prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, state=None, g_cap
                  stream=stream)
     r["state"] = outs
     return r
+
+
+def gdn_chunk_fwd_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, cs_q, cs_k, cs_v,
+                           cs_q_out, cs_k_out, cs_v_out, S0, o, S_T, chunk: int = 64,
+                           g_cap: float = 5.0, act: str = "silu", stream=None) -> None:
+    """The prologue of gdn_prologue and the chunkwise forward of gdn_chunk_fwd in
+    one launch: raw projections in (layouts of gdn_prologue), o [B,T,H,V] and/or
+    S_T [B,H,K,V] out, the carried states after the sequence in cs_*_out (never
+    the incoming ones) or None."""
+    import torch
+    B, T, H, K, V, gate = _chunk_fwd_args(q_raw, k_raw, v_raw, g_raw, b_raw, S0, o, S_T)
+    dev, dt = q_raw.device, q_raw.dtype
+    for t, name, D in ((w_q, "w_q", H * K), (w_k, "w_k", H * K), (w_v, "w_v", H * V)):
+        _check(t, name, (D, 4), torch.float32, dev)
+    for t, name, D in ((cs_q, "cs_q", H * K), (cs_k, "cs_k", H * K), (cs_v, "cs_v", H * V),
+                       (cs_q_out, "cs_q_out", H * K), (cs_k_out, "cs_k_out", H * K),
+                       (cs_v_out, "cs_v_out", H * V)):
+        _check(t, name, (B, 3, D), dt, dev)
+    rc = lib().gdn_chunk_fwd_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(g_raw),
+                                      _ptr(b_raw), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(cs_q),
+                                      _ptr(cs_k), _ptr(cs_v), _ptr(cs_q_out), _ptr(cs_k_out),
+                                      _ptr(cs_v_out), _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, K, V,
+                                      int(chunk), float(g_cap), _ACTS[act], _dtype_code(q_raw),
+                                      gate, _stream(stream))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd_prologue")
+
+
+def chunk_fwd_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, state=None, S0=None,
+                       want_o: bool = True, want_state: bool = True, g_cap: float = 5.0,
+                       act: str = "silu", chunk: int = 64, stream=None):
+    """Allocate o (if wanted), S_T and the carried states after the sequence (if
+    wanted); run gdn_chunk_fwd_prologue.  ``state`` is a (cs_q, cs_k, cs_v) tuple
+    or None.  Returns (o, S_T, state)."""
+    import torch
+    B, T, H, K = q_raw.shape
+    V = v_raw.shape[-1]
+    dev, dt = q_raw.device, q_raw.dtype
+    cs = state if state is not None else (None, None, None)
+    outs = None
+    if want_state:
+        outs = (torch.empty(B, 3, H * K, dtype=dt, device=dev),
+                torch.empty(B, 3, H * K, dtype=dt, device=dev),
+                torch.empty(B, 3, H * V, dtype=dt, device=dev))
+    o3 = outs if outs is not None else (None, None, None)
+    o = torch.empty((B, T, H, V), dtype=dt, device=dev) if want_o else None
+    S_T = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+    gdn_chunk_fwd_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, cs[0], cs[1], cs[2],
+                           o3[0], o3[1], o3[2], S0, o, S_T, chunk=chunk, g_cap=g_cap, act=act,
+                           stream=stream)
+    return o, S_T, outs
 
 
 def gdn_recurrent_step_prologue(q_raw, k_raw, v_raw, g_raw, b_raw, w_q, w_k, w_v, cs_q, cs_k,

@@ -38,6 +38,8 @@
 // factor is <= 1.  This is why the gate domain is bounded (the card's
 // section 2.1 says the bound comes from the kernel, not from the model).
 #include "mfma_frag.h"
+#include "prologue_ops.h"
+#include "prologue.h"
 
 namespace gdn {
 
@@ -47,7 +49,7 @@ constexpr int NTHR = 256;
 
 // ---------------------------------------------------------------------------
 // LDS layout (bytes).  Operand arrays carry a 16-byte row pad.
-template <typename OT, int K, bool CH> struct Smem {
+template <typename OT, int K, bool CH, bool PRO = false> struct Smem {
     static constexpr int PAD = 16 / (int)sizeof(OT);
     static constexpr int LDK = K + PAD;          // [64][K] operand arrays
     static constexpr int LDC = CH_T + PAD;       // [*][64] operand arrays
@@ -72,7 +74,10 @@ template <typename OT, int K, bool CH> struct Smem {
     static constexpr int kLam = align(kW + 4 * 3 * CH_T * 4);     // channel: [4][K]
     static constexpr int kER = kLam + (CH ? 4 * K * 4 : 0);       // [5][K] e^{R_b}
     static constexpr int kFP = kER + (CH ? 5 * K * 4 : 0);        // [6][K] e^{R_i - R_j}
-    static constexpr int bytes = align(kFP + (CH ? 6 * K * 4 : 0));
+    // fused prologue: convolution taps of this head's q and k channels and of
+    // the workgroup's value columns, [K][4], [K][4], [VBLK][4] floats
+    static constexpr int kTap = align(kFP + (CH ? 6 * K * 4 : 0));
+    static constexpr int bytes = align(kTap + (PRO ? (2 * K + VBLK) * 16 : 0));
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -87,13 +92,29 @@ struct ChunkArgs {
     float *S_T;
     int B, T, H, V, nvb;
     int xcd_map;  // 1: place the column blocks of one head on one XCD
+    // Fused prologue: q, k, v, g and beta above are then the raw projections
+    // (q_raw, k_raw, v_raw, g_raw, b_raw); taps [H*K,4], [H*K,4], [H*V,4]; carried
+    // convolution states [B,3,H*K] / [B,3,H*V] in the storage type (null: zeros
+    // in, not written out; an output never overlaps an input).
+    const float *w_q, *w_k, *w_v;
+    const void *cs_q, *cs_k, *cs_v;
+    void *cs_q_out, *cs_k_out, *cs_v_out;
+    float cap;
+    int silu;
 };
 
-template <typename DT, int K, bool CH>
+// PRO: the prologue (kernel-4 causal convolution, optional SiLU, q/k L2 norm,
+// g = -min(softplus(g_raw), cap), beta = sigmoid(b_raw)) runs in the load stage:
+// each thread also loads the three raw rows before its first row (from the
+// carried state before the sequence), and transforms its registers in fp32
+// before they are staged, so the transformed q, k, v, g and beta never leave
+// the chip.  The arithmetic is that of the standalone prologue kernel, token by
+// token and in the same order.
+template <typename DT, int K, bool CH, bool PRO = false>
 __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
 {
     using OT = DT;                         // MFMA operand type
-    using L = Smem<OT, K, CH>;
+    using L = Smem<OT, K, CH, PRO>;
     constexpr int NT = K / 16;             // 16-row tiles of S
     constexpr int NKB = K / 32;            // 32-wide k blocks over the key dim
     constexpr int EPV = 16 / (int)sizeof(DT);            // elements per 16-B vector
@@ -173,19 +194,28 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
     // 16 bytes at column cg*EPV; v: NVV 16-byte vectors; channel g: thread
     // (blk = tid / 64, cp = tid % 64) loads CPT channels of its 16 tokens.
     const int cg = tid % CG, rg = tid / CG;
-    vec_t pk[RPT], pq[RPT], pv[NVV];
+    // PRO: raw rows with the three before them (index 0..2), else the rows only
+    constexpr int HQ = PRO ? 3 : 0;
+    vec_t pk[RPT + HQ], pq[RPT + HQ], pv[NVV][1 + HQ];
     float pgc[CH ? 16 : 1][CH ? CPT : 1];
     float pb = 0.f, pgs = 0.f, pw = 0.f;
     const float *wsrc = args.wgate ? args.wgate : args.beta;
+    // carried-state rows (token t < 0 of the sequence): row 3 + t of [B,3,H*D]
+    const DT *csq = static_cast<const DT *>(args.cs_q), *csk = static_cast<const DT *>(args.cs_k);
+    const DT *csv = static_cast<const DT *>(args.cs_v);
     auto load_chunk = [&](int t0) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int t = t0 + RPT * rg + i;
+        for (int i = 0; i < RPT + HQ; ++i) {
+            const int t = t0 + RPT * rg + i - HQ;
             vec_t zk = {0.f, 0.f, 0.f, 0.f}, zq = zk;
-            if (t < T) {
+            if (t >= 0 && t < T) {
                 const long off = (row_base + (long)t * H) * K + cg * EPV;
                 zk = *reinterpret_cast<const vec_t *>(kg + off);
                 zq = *reinterpret_cast<const vec_t *>(qg + off);
+            } else if (PRO && t < 0) {
+                const long off = ((long)b * 3 + 3 + t) * H * K + h * K + cg * EPV;
+                if (csk) zk = *reinterpret_cast<const vec_t *>(csk + off);
+                if (csq) zq = *reinterpret_cast<const vec_t *>(csq + off);
             }
             pk[i] = zk;
             pq[i] = zq;
@@ -193,11 +223,16 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
 #pragma unroll
         for (int j = 0; j < NVV; ++j) {
             const int idx = tid + NTHR * j, row = idx / VPRV, cv = idx % VPRV;
-            const int t = t0 + row;
-            vec_t z = {0.f, 0.f, 0.f, 0.f};
-            if (t < T)
-                z = *reinterpret_cast<const vec_t *>(vg + (row_base + (long)t * H) * V + v0 + cv * EPV);
-            pv[j] = z;
+#pragma unroll
+            for (int i = 0; i <= HQ; ++i) {
+                const int t = t0 + row + i - HQ;
+                vec_t z = {0.f, 0.f, 0.f, 0.f};
+                if (t >= 0 && t < T)
+                    z = *reinterpret_cast<const vec_t *>(vg + (row_base + (long)t * H) * V + v0 + cv * EPV);
+                else if (PRO && t < 0 && csv)
+                    z = *reinterpret_cast<const vec_t *>(csv + ((long)b * 3 + 3 + t) * H * V + h * V + v0 + cv * EPV);
+                pv[j][i] = z;
+            }
         }
         if constexpr (!CH)
             pgs = (tid < CH_T && t0 + tid < T) ? args.g[row_base + (long)(t0 + tid) * H] : 0.f;
@@ -223,6 +258,81 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
         load_gate(0);
     }
 
+    // PRO: the taps in LDS; the staged values of a chunk are the prologue's
+    // outputs, computed from the raw registers in fp32.
+    float *sTap = reinterpret_cast<float *>(smem + L::kTap);
+    if constexpr (PRO) {
+        for (int i = tid; i < 2 * K + VBLK; i += NTHR) {
+            const float *src = i < K ? args.w_q + ((long)h * K + i) * 4
+                             : i < 2 * K ? args.w_k + ((long)h * K + i - K) * 4
+                                         : args.w_v + ((long)h * V + v0 + i - 2 * K) * 4;
+            *reinterpret_cast<f32x4 *>(sTap + 4 * i) = *reinterpret_cast<const f32x4 *>(src);
+        }
+        lds_barrier();
+    }
+    const bool silu = args.silu != 0;
+    // q or k rows of this thread: convolution, activation, L2 norm over the
+    // head's K channels (the CG lanes of a row reduce with shuffles), rows past
+    // the sequence zeroed
+    auto qk_prologue = [&](const vec_t (&raw)[RPT + HQ], const float *taps, vec_t (&out)[RPT],
+                           int t0) {
+        float y[RPT][EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const f32x4 w = *reinterpret_cast<const f32x4 *>(taps + (cg * EPV + e) * 4);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const float v = pr_conv4(w, to_f32(reinterpret_cast<const DT *>(&raw[i])[e]),
+                                         to_f32(reinterpret_cast<const DT *>(&raw[i + 1])[e]),
+                                         to_f32(reinterpret_cast<const DT *>(&raw[i + 2])[e]),
+                                         to_f32(reinterpret_cast<const DT *>(&raw[i + 3])[e]));
+                y[i][e] = silu ? pr_silu(v) : v;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) ss = fmaf(y[i][e], y[i][e], ss);
+#pragma unroll
+            for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off, CG);
+            const float rn = (t0 + RPT * rg + i < T) ? pr_rnorm(ss) : 0.f;
+            DT *o = reinterpret_cast<DT *>(&out[i]);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) o[e] = from_f32<DT>(y[i][e] * rn);
+        }
+    };
+    vec_t xk[RPT], xq[RPT], xv[NVV];   // the values staged for the chunk
+    auto stage_values = [&](int t0) {
+        if constexpr (!PRO) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                xk[i] = pk[i];
+                xq[i] = pq[i];
+            }
+#pragma unroll
+            for (int j = 0; j < NVV; ++j) xv[j] = pv[j][0];
+        } else {
+            qk_prologue(pq, sTap, xq, t0);
+            qk_prologue(pk, sTap + 4 * K, xk, t0);
+#pragma unroll
+            for (int j = 0; j < NVV; ++j) {
+                const int idx = tid + NTHR * j, row = idx / VPRV, cv = idx % VPRV;
+                const bool live = t0 + row < T;
+                DT *o = reinterpret_cast<DT *>(&xv[j]);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    const f32x4 w = *reinterpret_cast<const f32x4 *>(sTap + (2 * K + cv * EPV + e) * 4);
+                    const float v = pr_conv4(w, to_f32(reinterpret_cast<const DT *>(&pv[j][0])[e]),
+                                             to_f32(reinterpret_cast<const DT *>(&pv[j][1])[e]),
+                                             to_f32(reinterpret_cast<const DT *>(&pv[j][2])[e]),
+                                             to_f32(reinterpret_cast<const DT *>(&pv[j][3])[e]));
+                    o[e] = from_f32<DT>(live ? (silu ? pr_silu(v) : v) : 0.f);
+                }
+            }
+        }
+    };
+
     // Write the staged outputs of the chunk at t0 (rows < nvalid) from sO to o.
     auto flush_o = [&](int t0, int nvalid) {
         if (!og) return;
@@ -240,10 +350,11 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
 
         // ---- stage the prefetched chunk into LDS (and flush the last outputs) ----
         if (c > 0) flush_o(t0 - CH_T, CH_T);
+        stage_values(t0);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            *reinterpret_cast<vec_t *>(sK + (RPT * rg + i) * L::LDK + cg * EPV) = pk[i];
-            *reinterpret_cast<vec_t *>(sQ + (RPT * rg + i) * L::LDK + cg * EPV) = pq[i];
+            *reinterpret_cast<vec_t *>(sK + (RPT * rg + i) * L::LDK + cg * EPV) = xk[i];
+            *reinterpret_cast<vec_t *>(sQ + (RPT * rg + i) * L::LDK + cg * EPV) = xq[i];
         }
         if constexpr (!CH) {
             // K^T (the scalar decay is applied to D instead): for each channel of
@@ -253,19 +364,21 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
                 const int ch = cg * EPV + e;
                 pack_t pk_t;
 #pragma unroll
-                for (int i = 0; i < RPT; ++i) pk_t[i] = reinterpret_cast<const DT *>(&pk[i])[e];
+                for (int i = 0; i < RPT; ++i) pk_t[i] = reinterpret_cast<const DT *>(&xk[i])[e];
                 *reinterpret_cast<pack_t *>(sKmT + ch * L::LDC + ((RPT * rg) ^ kmt_swz<EPV>(ch))) = pk_t;
             }
         }
 #pragma unroll
         for (int j = 0; j < NVV; ++j) {
             const int idx = tid + NTHR * j, row = idx / VPRV, cv = idx % VPRV;
-            *reinterpret_cast<vec_t *>(sV + row * L::LDC + cv * EPV) = pv[j];
+            *reinterpret_cast<vec_t *>(sV + row * L::LDC + cv * EPV) = xv[j];
         }
         if (tid < CH_T) {
-            sBeta[tid] = pb;
-            sWg[tid] = pw;
-            if (!CH) sG[tid] = pgs;
+            const bool live = t0 + tid < T;
+            const float bv = PRO ? (live ? pr_sigmoid(pb) : 0.f) : pb;
+            sBeta[tid] = bv;
+            sWg[tid] = PRO ? bv : pw;
+            if (!CH) sG[tid] = PRO ? (live ? pr_gate(pgs, args.cap) : 0.f) : pgs;
         }
         lds_barrier();
 
@@ -291,7 +404,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
 #pragma unroll
                 for (int tt = 0; tt < 16; ++tt) {
                     const int t = 16 * blk + tt;
-                    lam += pgc[tt][ci];
+                    lam += PRO ? (t0 + t < T ? pr_gate(pgc[tt][ci], args.cap) : 0.f) : pgc[tt][ci];
                     const float el = __expf(lam);
                     const float eil = __expf(-lam);
                     const float kv = to_f32(sK[t * L::LDK + ch]);
@@ -511,21 +624,43 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_fwd_kernel(ChunkArgs args)
 #pragma unroll
             for (int e = 0; e < 4; ++e) ST[(16 * ct + 4 * gq + e) * V + v0 + vcol] = S_acc[ct][e];
     }
+
+    if constexpr (PRO) {
+        // The carried states after the sequence: the last three raw tokens (older
+        // ones from the incoming state when T < 3).  q and k by the first column
+        // block of the head, v by every block for its columns.
+        auto state_out = [&](const DT *raw, const DT *cs, void *outp, int E, int c0, int n) {
+            DT *out = static_cast<DT *>(outp);
+            if (!out) return;
+            for (int i = tid; i < 3 * n; i += NTHR) {
+                const int r = i / n, c = c0 + i % n, t = T - 3 + r;
+                DT x = from_f32<DT>(0.f);
+                if (t >= 0) x = raw[(row_base + (long)t * H) * E + c];
+                else if (cs) x = cs[((long)b * 3 + 3 + t) * H * E + (long)h * E + c];
+                out[((long)b * 3 + r) * H * E + (long)h * E + c] = x;
+            }
+        };
+        if (vb == 0) {
+            state_out(qg, csq, args.cs_q_out, K, 0, K);
+            state_out(kg, csk, args.cs_k_out, K, 0, K);
+        }
+        state_out(vg, csv, args.cs_v_out, V, v0, VBLK);
+    }
 }
 
-template <typename DT, int K, bool CH>
+template <typename DT, int K, bool CH, bool PRO = false>
 static hipError_t launch_chunk(const ChunkArgs &a, hipStream_t stream)
 {
-    using L = Smem<DT, K, CH>;
+    using L = Smem<DT, K, CH, PRO>;
     static bool attr_set = false;  // benign race: every thread sets the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_kernel<DT, K, CH>,
+        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_kernel<DT, K, CH, PRO>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const long nwg = (long)a.B * a.H * a.nvb;
-    hipLaunchKernelGGL((chunk_fwd_kernel<DT, K, CH>), dim3((unsigned)nwg), dim3(NTHR), L::bytes,
+    hipLaunchKernelGGL((chunk_fwd_kernel<DT, K, CH, PRO>), dim3((unsigned)nwg), dim3(NTHR), L::bytes,
                        stream, a);
     return hipGetLastError();
 }
@@ -541,7 +676,7 @@ static ChunkArgs chunk_args(const void *q, const void *k, const void *v, const f
                             const float *beta, const float *wgate, const float *S0, void *o,
                             float *S_T, int B, int T, int H, int V)
 {
-    ChunkArgs a;
+    ChunkArgs a = {};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = S0; a.o = o; a.S_T = S_T;
     a.wgate = wgate;
     a.B = B; a.T = T; a.H = H; a.V = V;
@@ -582,6 +717,33 @@ hipError_t chunk_fwd_dg_launch(bool bf16, bool channel, int K, const void *q, co
     if (K == 64)
         return channel ? launch_chunk<__bf16, 64, true>(a, st) : launch_chunk<__bf16, 64, false>(a, st);
     return channel ? launch_chunk<__bf16, 128, true>(a, st) : launch_chunk<__bf16, 128, false>(a, st);
+}
+
+} // namespace gdn
+
+namespace gdn {
+
+// The prologue fused into the chunk kernel (raw projections in, o and S_T out):
+// every storage type, gate and K (fp32: K = 64).  p carries the raw inputs, the
+// taps, the carried states and the cap in the prologue's own layout.
+hipError_t chunk_fwd_pro_launch(bool bf16, bool channel, bool silu, int K, const PrArgs &p,
+                                const float *S0, void *o, float *S_T, int V, hipStream_t st)
+{
+    ChunkArgs a = chunk_args(p.q_raw, p.k_raw, p.v_raw, p.g_raw, p.b_raw, nullptr, S0, o, S_T,
+                             p.B, p.T, p.H, V);
+    a.w_q = p.w_q; a.w_k = p.w_k; a.w_v = p.w_v;
+    a.cs_q = p.cs_q; a.cs_k = p.cs_k; a.cs_v = p.cs_v;
+    a.cs_q_out = p.cs_q_out; a.cs_k_out = p.cs_k_out; a.cs_v_out = p.cs_v_out;
+    a.cap = p.cap;
+    a.silu = silu ? 1 : 0;
+    if (!bf16)
+        return channel ? launch_chunk<float, 64, true, true>(a, st)
+                       : launch_chunk<float, 64, false, true>(a, st);
+    if (K == 64)
+        return channel ? launch_chunk<__bf16, 64, true, true>(a, st)
+                       : launch_chunk<__bf16, 64, false, true>(a, st);
+    return channel ? launch_chunk<__bf16, 128, true, true>(a, st)
+                   : launch_chunk<__bf16, 128, false, true>(a, st);
 }
 
 } // namespace gdn

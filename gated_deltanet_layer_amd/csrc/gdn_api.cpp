@@ -22,6 +22,8 @@ hipError_t recurrent_step_launch(bool bf16, bool channel, int K, int V, const vo
                                  const void *k, const void *v, const float *g,
                                  const float *beta, const float *wg, float *S, void *o,
                                  long nslices, hipStream_t st);
+hipError_t chunk_fwd_pro_launch(bool bf16, bool channel, bool silu, int K, const PrArgs &p,
+                                const float *S0, void *o, float *S_T, int V, hipStream_t st);
 int chunk_fwd_seg_count(long B, long T, long H);
 unsigned long long chunk_fwd_seg_workspace(long B, long H, int nseg);
 hipError_t chunk_fwd_seg_launch(const void *k, const void *v, const float *g, const float *beta,
@@ -550,6 +552,68 @@ gdn_status gdn_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
     a.cap = g_cap; a.B = B; a.T = T; a.H = H;
     const hipError_t e = gdn::prologue_launch(dtype == GDN_BF16, ch, act == GDN_ACT_SILU, K, V, a,
                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
+                                  const float *g_raw, const float *b_raw, const float *w_q,
+                                  const float *w_k, const float *w_v, const void *cs_q,
+                                  const void *cs_k, const void *cs_v, void *cs_q_out,
+                                  void *cs_k_out, void *cs_v_out, const float *S0, void *o,
+                                  float *S_T, int B, int T, int H, int K, int V, int chunk,
+                                  float g_cap, gdn_act act, gdn_dtype dtype, gdn_gate gate,
+                                  void *stream)
+{
+    // the chunkwise forward's own checks, with the raw projections in place of
+    // q, k, v, g and beta (same shapes and alignment)
+    const gdn_status st = chunk_fwd_check(q_raw, k_raw, v_raw, g_raw, b_raw, S0, o, S_T, B, T, H,
+                                          K, V, chunk, dtype, gate);
+    if (st != GDN_OK) return st;
+    if (act != GDN_ACT_NONE && act != GDN_ACT_SILU) return GDN_EINVAL;
+    if (!(g_cap > 0.f)) return GDN_EINVAL;
+    const long long es = dtype == GDN_BF16 ? 2 : 4;
+    const long long ntok = prod(B, T, H), nqk = prod(B, T, H, K), nv = prod(B, T, H, V);
+    const long long nsk = prod(B, 3, H, K), nsv = prod(B, 3, H, V);
+    const long long nwk = prod(H, K, 4), nwv = prod(H, V, 4);
+    if (nsk < 0 || nsv < 0 || nwk < 0 || nwv < 0) return GDN_EINVAL;
+    const bool ch = gate == GDN_GATE_CHANNEL;
+    if (B > 0 && H > 0 && (!w_q || !w_k || !w_v)) return GDN_EINVAL;
+    for (const void *p : {(const void *)w_q, (const void *)w_k, (const void *)w_v, cs_q, cs_k, cs_v,
+                          (const void *)cs_q_out, (const void *)cs_k_out, (const void *)cs_v_out})
+        if (p && !aligned16(p)) return GDN_EINVAL;
+    const Range in[] = {range(q_raw, nqk * es), range(k_raw, nqk * es), range(v_raw, nv * es),
+                        range(g_raw, (ch ? nqk : ntok) * 4), range(b_raw, ntok * 4),
+                        range(w_q, nwk * 4), range(w_k, nwk * 4), range(w_v, nwv * 4),
+                        range(cs_q, cs_q ? nsk * es : 0), range(cs_k, cs_k ? nsk * es : 0),
+                        range(cs_v, cs_v ? nsv * es : 0), range(S0, S0 ? prod(B, H, K, V) * 4 : 0)};
+    // every output apart from S_T (which may be S0) touches no input and no other
+    // output; a carried state out is never its own input here, since each
+    // column block of a head reads the incoming state while another may be
+    // writing the outgoing one
+    const Range out[] = {range(cs_q_out, cs_q_out ? nsk * es : 0),
+                         range(cs_k_out, cs_k_out ? nsk * es : 0),
+                         range(cs_v_out, cs_v_out ? nsv * es : 0),
+                         range(o, o ? nv * es : 0), range(S_T, S_T ? prod(B, H, K, V) * 4 : 0)};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < (int)(sizeof(in) / sizeof(in[0])); ++j) {
+            if (i == 4 && j == 11 && (const void *)S0 == (const void *)S_T) continue;
+            if (overlap(out[i], in[j])) return GDN_EINVAL;
+        }
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(out[i], out[j])) return GDN_EINVAL;
+    }
+    // the per-channel chunk kernels take g >= -5 only (the 16-token decay split)
+    if (ch && !(g_cap <= 5.f)) return GDN_ENOTSUP;
+    if (B == 0 || H == 0) return GDN_OK;
+    if (!S_T && T == 0 && !cs_q_out && !cs_k_out && !cs_v_out) return GDN_OK;
+
+    gdn::PrArgs p = {};
+    p.q_raw = q_raw; p.k_raw = k_raw; p.v_raw = v_raw; p.g_raw = g_raw; p.b_raw = b_raw;
+    p.w_q = w_q; p.w_k = w_k; p.w_v = w_v; p.cs_q = cs_q; p.cs_k = cs_k; p.cs_v = cs_v;
+    p.cs_q_out = cs_q_out; p.cs_k_out = cs_k_out; p.cs_v_out = cs_v_out;
+    p.cap = g_cap; p.B = B; p.T = T; p.H = H;
+    const hipError_t e = gdn::chunk_fwd_pro_launch(dtype == GDN_BF16, ch, act == GDN_ACT_SILU, K, p,
+                                                   S0, o, S_T, V, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

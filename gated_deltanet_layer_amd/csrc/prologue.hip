@@ -17,26 +17,11 @@
 // that a decode token is one kernel from the raw projections to o and S'.
 #include "gdn_common.h"
 #include "prologue.h"
+#include "prologue_ops.h"
 
 namespace gdn {
 
 constexpr int PR_NTHR = 256;
-
-// The hardware reciprocal and reciprocal square root (1 ulp) rather than
-// IEEE-exact division: with exact division the chunk-mode kernel was bound by
-// its VALU work (about ten instructions per division, nine divisions per token
-// and thread), not by HBM.
-__device__ __forceinline__ float pr_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-__device__ __forceinline__ float pr_sigmoid(float x) { return pr_rcp(1.f + __expf(-x)); }
-__device__ __forceinline__ float pr_silu(float x) { return x * pr_rcp(1.f + __expf(-x)); }
-// 1 / max(sqrt(ss), 1e-12) for ss >= 0
-__device__ __forceinline__ float pr_rnorm(float ss) { return __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f)); }
-// -min(softplus(x), cap), softplus evaluated as max(x, 0) + log(1 + e^{-|x|})
-__device__ __forceinline__ float pr_gate(float x, float cap)
-{
-    const float sp = fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));
-    return -fminf(sp, cap);
-}
 
 // 8 consecutive elements of a row as fp32 (16-byte loads).
 template <typename DT> __device__ __forceinline__ void ld8(const DT *p, float (&x)[8]);
@@ -128,10 +113,7 @@ __device__ __forceinline__ void conv_run(const DT *x, const DT *cs, const float 
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float v = wt[e][0] * win[0][e];
-            v = fmaf(wt[e][1], win[1][e], v);
-            v = fmaf(wt[e][2], win[2][e], v);
-            v = fmaf(wt[e][3], xt[e], v);
+            const float v = pr_conv4(wt[e], win[0][e], win[1][e], win[2][e], xt[e]);
             o[e] = SILU ? pr_silu(v) : v;
             ss = fmaf(o[e], o[e], ss);
         }

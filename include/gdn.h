@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define GDN_API __attribute__((visibility("default")))
@@ -321,6 +321,33 @@ GDN_API gdn_status gdn_prologue(const void *q_raw, const void *k_raw, const void
                                 float *g, float *beta, void *cs_q_out, void *cs_k_out,
                                 void *cs_v_out, int B, int T, int H, int K, int V, float g_cap,
                                 gdn_act act, gdn_dtype dtype, gdn_gate gate, void *stream);
+
+/*
+ * The prologue and the chunkwise forward in one launch: the raw projections in,
+ * o and S_T out, with the transformed q, k, v, g and beta never written to HBM
+ * (the chunk kernel applies the prologue of gdn_prologue in its load stage, to
+ * each chunk's rows and the three raw rows before them).  Results are those of
+ * gdn_prologue followed by gdn_chunk_fwd, up to the rounding order of the
+ * convolution and the norm.
+ *
+ *   q_raw .. w_v, cs_q .. cs_v, g_cap, act  as gdn_prologue
+ *   cs_*_out  the carried states after the sequence as gdn_prologue writes them,
+ *             or NULL; here never the incoming state (EINVAL if any overlap)
+ *   S0, o, S_T, B .. chunk, dtype, gate      as gdn_chunk_fwd
+ *
+ * Checks and errors are those of gdn_chunk_fwd (with q_raw .. b_raw in the
+ * places of q .. beta) and of gdn_prologue.  The call takes the chunk kernel of
+ * gdn_chunk_fwd_decoupled for every storage type, gate and K (fp32: K = 64).
+ */
+GDN_API gdn_status gdn_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v_raw,
+                                          const float *g_raw, const float *b_raw,
+                                          const float *w_q, const float *w_k, const float *w_v,
+                                          const void *cs_q, const void *cs_k, const void *cs_v,
+                                          void *cs_q_out, void *cs_k_out, void *cs_v_out,
+                                          const float *S0, void *o, float *S_T,
+                                          int B, int T, int H, int K, int V, int chunk,
+                                          float g_cap, gdn_act act, gdn_dtype dtype,
+                                          gdn_gate gate, void *stream);
 
 /*
  * One decode token of N sequences from the raw projections: the prologue above

@@ -41,7 +41,7 @@ def test_only_declared_symbols_are_exported():
 
 
 def test_version_and_status_strings(L):
-    assert gdn.abi_version() == 6
+    assert gdn.abi_version() == 7
     assert gdn.status_str(0) == "ok"
     assert "invalid" in gdn.status_str(1)
     assert "unsupported" in gdn.status_str(2)
@@ -477,3 +477,42 @@ def test_step_decoupled_unsupported_and_empty(L):
     assert _step_dg(L, K=32) == gdn.GDN_ENOTSUP
     assert _step_dg(L, N=0) == gdn.GDN_OK
     assert _step_dg(L, N=0, w=None, e=None) == gdn.GDN_OK
+
+
+# --- the prologue fused into the chunkwise forward ----------------------------------------
+def _cpro(L, **kw):
+    names = ["q", "k", "v", "g", "b", "wq", "wk", "wv", "csq", "csk", "csv", "oq", "ok", "ov",
+             "S0", "o", "S_T"]
+    a = dict(zip(names, _ptrs(len(names))))
+    a.update(B=2, T=100, H=3, K=128, V=128, chunk=64, cap=5.0, act=1, dtype=1, gate=1)
+    a.update(kw)
+    return L.gdn_chunk_fwd_prologue(*(a[n] for n in names), a["B"], a["T"], a["H"], a["K"],
+                                    a["V"], a["chunk"], a["cap"], a["act"], a["dtype"], a["gate"],
+                                    None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(wq=None), dict(b=None), dict(act=2), dict(cap=0.0), dict(cap=-1.0),
+    dict(cap=float("nan")), dict(dtype=2), dict(gate=3), dict(T=-1), dict(o=None, S_T=None),
+    dict(oq=BASE + 8 * SEP),            # a carried state out that is its own input
+    dict(ov=BASE + 10 * SEP + 16),      # overlaps the incoming v state
+    dict(o=BASE + 5 * SEP),             # o overlaps the q taps
+    dict(S_T=BASE + 9 * SEP),           # S_T overlaps an incoming state
+    dict(ok=BASE + 15 * SEP),           # a carried state out overlaps o
+    dict(wk=BASE + 6 * SEP + 4), dict(csv=BASE + 10 * SEP + 8),
+])
+def test_chunk_prologue_rejects_invalid(L, kw):
+    assert _cpro(L, **kw) == gdn.GDN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(cap=5.5), dict(cap=float("inf")), dict(K=96), dict(chunk=32),
+                                dict(dtype=0, K=128)])
+def test_chunk_prologue_unsupported(L, kw):
+    assert _cpro(L, **kw) == gdn.GDN_ENOTSUP
+
+
+def test_chunk_prologue_valid_edges(L):
+    # an uncapped scalar gate passes validation (then enqueues work: not called here)
+    assert _cpro(L, B=0, gate=0, cap=float("inf")) == gdn.GDN_OK
+    assert _cpro(L, B=0, q=None, k=None, v=None, g=None, b=None, wq=None, wk=None, wv=None) == gdn.GDN_OK
+    assert _cpro(L, T=0, S_T=None, oq=None, ok=None, ov=None) == gdn.GDN_OK
