@@ -209,10 +209,12 @@ def bench_prefill(torch, gdn, timer, name, want_o, use_ws, steps=None, warmup=No
     es = 2 if cfg.dtype == "bf16" else 4
     nbytes = chunk_bytes(B, T, H, K, V, es, channel, d["S0"] is not None, want_o)
     useful, dense = chunk_flops(B, T, H, K, V, want_o)
-    nseg = 1 + (nws // (B * H * 2 * K * K * 4) if nws else 0)
+    nseg = 1 + (nws // (B * H * (3 if want_o else 2) * K * K * 4) if nws else 0)
     if nseg > 1:
         kernels = ["chunk_fwd_seg_kernel", "seg_combine_kernel"]
-        tkey = "chunk_fwd_seg/" + name
+        if want_o:
+            kernels.append("chunk_fwd_wsc_kernel<128, true>")
+        tkey = "chunk_fwd_seg/" + name + ("/o" if want_o else "")
     elif channel:
         kernels = ["chunk_fwd_wsc_kernel<128, %s>" % ("true" if want_o else "false")]
         tkey = "chunk_fwd_wsc_kernel<128>" + ("" if name == "channel_bf16" else "/" + name)

@@ -577,9 +577,12 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
 // order, starting from segment 0's final state in S_T; fp32 matrix cores
 // (16 x 16 x 4).  One workgroup of 4 waves per (head, 16 value columns): wave
 // w computes rows 32 w .. 32 w + 31; the state block lives in LDS between steps.
+// With Sb, the state entering each segment s >= 1 is also written there
+// ([B*H][nseg-1][K][V]): the incoming states of the o pass.
 struct SgCombArgs {
     const float *mapN, *mapM;
     float *S_T;
+    float *Sb;
     int nseg, xcd_map;
     long nbh;
 };
@@ -610,6 +613,10 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SgCombArgs a)
         const long slot = bh * (a.nseg - 1) + (s - 1);
         const float *Mp = a.mapM + slot * K * K;
         const float *Np = a.mapN + slot * K * V;
+        if (a.Sb) {
+            float *Bp = a.Sb + slot * K * V;
+            for (int i = tid; i < K * 16; i += 256) Bp[(i >> 4) * V + 16 * cb + (i & 15)] = sS[(i >> 4) * LDS_LD + (i & 15)];
+        }
         f32x4 acc[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -661,11 +668,17 @@ int chunk_fwd_seg_count(long B, long T, long H)
     return (int)((nch + len - 1) / len);
 }
 
-unsigned long long chunk_fwd_seg_workspace(long B, long H, int nseg)
+// The segment maps (N and M per later segment) and, for a call that also
+// writes o, the incoming state of every later segment.
+unsigned long long chunk_fwd_seg_workspace(long B, long H, int nseg, bool want_o)
 {
     if (nseg <= 1) return 0;
-    return (unsigned long long)B * H * (nseg - 1) * (2ull * SG_K * SG_K) * 4ull;
+    return (unsigned long long)B * H * (nseg - 1) * ((want_o ? 3ull : 2ull) * SG_K * SG_K) * 4ull;
 }
+
+hipError_t chunk_fwd_wsc_seg_launch(const void *q, const void *k, const void *v, const float *g,
+                                    const float *beta, const float *S0, const float *Sb, void *o,
+                                    int B, int T, int H, int nseg, int seg_len, hipStream_t st);
 
 // Device scratch of the entry point that allocates nothing: the segment maps of
 // one call live here instead of in a caller's workspace.  Host code never
@@ -698,9 +711,11 @@ hipError_t seg_scratch(void **p)
     return hipSuccess;
 }
 
-hipError_t chunk_fwd_seg_launch(const void *k, const void *v, const float *g, const float *beta,
-                                const float *S0, float *S_T, void *ws, int B, int T, int H, int nseg,
-                                hipStream_t st)
+// q and o: null for a final-state-only call; with o, a third launch runs every
+// segment's outputs from the incoming states the combine wrote.
+hipError_t chunk_fwd_seg_launch(const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const float *S0, void *o, float *S_T, void *ws,
+                                int B, int T, int H, int nseg, hipStream_t st)
 {
     using L = SgSmem;
     static bool attr_set = false;  // benign race: every thread sets the same value
@@ -725,9 +740,12 @@ hipError_t chunk_fwd_seg_launch(const void *k, const void *v, const float *g, co
     if (e != hipSuccess || nseg == 1) return e;
     SgCombArgs c;
     c.mapN = a.mapN; c.mapM = a.mapM; c.S_T = S_T; c.nseg = nseg; c.nbh = bh;
+    c.Sb = o ? a.mapM + bh * (nseg - 1) * SG_K * SG_K : nullptr;
     c.xcd_map = bh % 8 == 0 ? 1 : 0;
     hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(bh * (SG_K / 16))), dim3(256), 0, st, c);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess || !o) return e;
+    return chunk_fwd_wsc_seg_launch(q, k, v, g, beta, S0, c.Sb, o, B, T, H, nseg, a.seg_len, st);
 }
 
 } // namespace gdn

@@ -99,6 +99,12 @@ struct WcArgs {
     float *S_T;
     int T, H, V, nvb;
     int xcd_map;
+    // Segments (seg_len > 0): workgroup w runs chunks [seg seg_len, (seg + 1)
+    // seg_len) of its (b, h, column block), seg = w / nbhv, starting from S0 for
+    // segment 0 and from Sb[b h][seg - 1] ([B*H][nseg-1][K][V] fp32) after it.
+    int seg_len, nseg;
+    long nbhv;
+    const float *Sb;
 };
 
 // WO = false: the final state only (no o).  q is then not read, and QL, P, Q+ S
@@ -119,9 +125,13 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
     const int gq = lane >> 4;
 
     const int T = args.T, H = args.H, V = args.V, nvb = args.nvb;
-    int bh, vb;
+    int bh, vb, seg = 0;
     {
-        const int w = blockIdx.x;
+        int w = blockIdx.x;
+        if (args.seg_len > 0) {
+            seg = (int)(w / args.nbhv);
+            w = (int)(w % args.nbhv);
+        }
         if (args.xcd_map) {
             const int xcd = w & 7, slot = w >> 3;
             vb = slot % nvb;
@@ -134,7 +144,9 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
     const int b = bh / args.H, h = bh % args.H;
     const int v0 = vb * WC_VB;
     const long row_base = (long)b * T * H + h;   // row of token 0 in [B*T*H]
-    const int nchunks = (T + WC_T - 1) / WC_T;
+    const int nch_all = (T + WC_T - 1) / WC_T;
+    const int c0 = args.seg_len > 0 ? seg * args.seg_len : 0;                    // first chunk
+    const int c1 = args.seg_len > 0 ? min(nch_all, c0 + args.seg_len) : nch_all; // end
 
     auto cbuf = [&](int c) { return smem + L::oC + (c & 1) * L::CBUF; };
     auto dbuf = [&](int c) { return smem + L::oD + (c & 1) * L::DBUF; };
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                 fKI[kb].v = scale8(rk[kb], ei[0], ei[1]);
                 // this key block of the next chunk goes in flight (spread over the
                 // loop rather than issued as one burst)
-                if (n + 1 < nchunks) fetch_kb(n + 1, kb);
+                if (n + 1 < c1) fetch_kb(n + 1, kb);
                 const int off = wc_off<CPR>(row, 4 * kb + gq);
                 *reinterpret_cast<bf16x8 *>(C + L::cKL + off) = fKL[kb].v;
                 if constexpr (WO) *reinterpret_cast<bf16x8 *>(C + L::cQL + off) = fQL[kb].v;
@@ -225,7 +237,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                 }
             }
             if (gq == 0) reinterpret_cast<float *>(D + L::dBeta)[row] = rb;
-            if (n + 1 < nchunks) fetch_beta(n + 1);
+            if (n + 1 < c1) fetch_beta(n + 1);
             arrivals += 4;
             prep_barrier(ctr, arrivals);         // KL, QL, KI and E of all blocks written
 
@@ -278,15 +290,15 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
             else kminus(std::integral_constant<int, 3>());
         };
 
-        if (nchunks > 0) {
+        if (c0 < c1) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) fetch_kb(0, kb);
-            fetch_beta(0);
-            prepare(0);
+            for (int kb = 0; kb < NKB; ++kb) fetch_kb(c0, kb);
+            fetch_beta(c0);
+            prepare(c0);
             lds_barrier();
         }
-        for (int c = 0; c < nchunks; ++c) {
-            if (c + 1 < nchunks) prepare(c + 1);
+        for (int c = c0; c < c1; ++c) {
+            if (c + 1 < c1) prepare(c + 1);
             lds_barrier();
         }
         return;
@@ -299,7 +311,8 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
     auto key_of = [&](int ct, int e) { return 32 * (ct >> 1) + 8 * gq + 4 * (ct & 1) + e; };
     f32x4 S_acc[NT];
     {
-        const float *S0 = args.S0 ? args.S0 + (long)bh * K * V : nullptr;
+        const float *S0 = seg > 0 ? args.Sb + ((long)bh * (args.nseg - 1) + seg - 1) * K * V
+                        : args.S0 ? args.S0 + (long)bh * K * V : nullptr;
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
@@ -340,7 +353,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
     //   w0: (1,0) (3,0)   w1: (2,1) (3,1)   w2: (3,2)   w3: (2,0)
     // F_IJ = E_J ... E_{I-1} per channel.
     auto gram_pairs = [&](int n) __attribute__((always_inline)) {
-        wait_arrivals(ctr, 4u * (unsigned)(n + 1));
+        wait_arrivals(ctr, 4u * (unsigned)(n - c0 + 1));   // prepare(c0 .. n) arrived
         const char *C = cbuf(n);
         char *D = dbuf(n);
         __bf16 *sAn = reinterpret_cast<__bf16 *>(D + L::dAn);
@@ -450,10 +463,10 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         else if (cw == 2) pairs(integral_constant<int, 3>(), integral_constant<int, 0>(), integral_constant<int, 2>());
         else pairs(integral_constant<int, 2>(), integral_constant<int, 0>(), integral_constant<int, 0>());
     };
-    if (nchunks > 0) {
-        fetch_v(0);
-        gram_pairs(0);
-        lds_barrier();     // chunk 0 is ready
+    if (c0 < c1) {
+        fetch_v(c0);
+        gram_pairs(c0);
+        lds_barrier();     // chunk c0 is ready
     }
 
     const int trow = 4 * gq + (r16 >> 2), tq = r16 & 3;
@@ -461,7 +474,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) k_tr[kk] = wc_off<CPR>(trow, 4 * kk + tq);
 
-    for (int c = 0; c < nchunks; ++c) {
+    for (int c = c0; c < c1; ++c) {
         const char *C = cbuf(c);
         const char *sKL = C + L::cKL, *sQL = C + L::cQL, *sKM = C + L::cKM;
         const char *D = dbuf(c);
@@ -531,7 +544,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
             for (int e = 0; e < 4; ++e)
                 X[rt][e] = bt[e] * (__builtin_bit_cast(float, (unsigned)vr[rt][e] << 16) - KS[rt][e]);
         }
-        if (c + 1 < nchunks) fetch_v(c + 1);
+        if (c + 1 < c1) fetch_v(c + 1);
         const Frag<__bf16> fT0 = lds_frag_lo(sTd, L::LDD, 0, 0), fT1 = lds_frag_lo(sTd, L::LDD, 16, 0);
         const Frag<__bf16> fT2 = lds_frag_lo(sTd, L::LDD, 32, 0), fT3 = lds_frag_lo(sTd, L::LDD, 48, 0);
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -595,7 +608,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                 S_acc[ct] = mma(S_acc[ct], Frag<__bf16>{cat8(kt[ct][2 * kb2], kt[ct][2 * kb2 + 1])}, Ef[kb2]);
             GDN_SCHED_FENCE();
         }
-        if (c + 1 < nchunks) gram_pairs(c + 1);
+        if (c + 1 < c1) gram_pairs(c + 1);
         lds_barrier();
     }
 
@@ -628,7 +641,7 @@ hipError_t chunk_fwd_wsc_launch(int K, const void *q, const void *k, const void 
                                 const float *beta, const float *S0, void *o, float *S_T, int B,
                                 int T, int H, int V, hipStream_t st)
 {
-    WcArgs a;
+    WcArgs a = {};
     a.q = (const __bf16 *)q; a.k = (const __bf16 *)k; a.v = (const __bf16 *)v;
     a.g = g; a.beta = beta; a.S0 = S0; a.o = (__bf16 *)o; a.S_T = S_T;
     a.T = T; a.H = H; a.V = V;
@@ -639,6 +652,31 @@ hipError_t chunk_fwd_wsc_launch(int K, const void *q, const void *k, const void 
     if (o)
         return K == 64 ? launch_wsc<64, true>(a, nwg, st) : launch_wsc<128, true>(a, nwg, st);
     return K == 64 ? launch_wsc<64, false>(a, nwg, st) : launch_wsc<128, false>(a, nwg, st);
+}
+
+} // namespace gdn
+
+namespace gdn {
+
+// The o pass of the sequence-parallel forward (per-key-channel gate, K = V =
+// 128, bf16): every (b, h, column block, segment) at once, each segment from
+// its incoming state in Sb (segment 0 from S0); no final state is written.
+hipError_t chunk_fwd_wsc_seg_launch(const void *q, const void *k, const void *v, const float *g,
+                                    const float *beta, const float *S0, const float *Sb, void *o,
+                                    int B, int T, int H, int nseg, int seg_len, hipStream_t st)
+{
+    WcArgs a = {};
+    a.q = (const __bf16 *)q; a.k = (const __bf16 *)k; a.v = (const __bf16 *)v;
+    a.g = g; a.beta = beta; a.S0 = S0; a.o = (__bf16 *)o; a.S_T = nullptr;
+    a.T = T; a.H = H; a.V = 128;
+    a.nvb = 128 / WC_VB;
+    const long bhn = (long)B * H;
+    a.xcd_map = bhn % 8 == 0 ? 1 : 0;
+    a.seg_len = seg_len;
+    a.nseg = nseg;
+    a.nbhv = bhn * a.nvb;
+    a.Sb = Sb;
+    return launch_wsc<128, true>(a, a.nbhv * nseg, st);
 }
 
 } // namespace gdn

@@ -25,10 +25,10 @@ hipError_t recurrent_step_launch(bool bf16, bool channel, int K, int V, const vo
 hipError_t chunk_fwd_pro_launch(bool bf16, bool channel, bool silu, int K, const PrArgs &p,
                                 const float *S0, void *o, float *S_T, int V, hipStream_t st);
 int chunk_fwd_seg_count(long B, long T, long H);
-unsigned long long chunk_fwd_seg_workspace(long B, long H, int nseg);
-hipError_t chunk_fwd_seg_launch(const void *k, const void *v, const float *g, const float *beta,
-                                const float *S0, float *S_T, void *ws, int B, int T, int H, int nseg,
-                                hipStream_t st);
+unsigned long long chunk_fwd_seg_workspace(long B, long H, int nseg, bool want_o);
+hipError_t chunk_fwd_seg_launch(const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const float *S0, void *o, float *S_T, void *ws,
+                                int B, int T, int H, int nseg, hipStream_t st);
 unsigned long long chunk_fwd_seg_scratch_bytes();
 hipError_t seg_scratch(void **p);
 hipError_t recurrent_multi_launch(bool bf16, bool channel, int K, int V, const void *q,
@@ -122,15 +122,18 @@ gdn_status chunk_fwd_check(const void *q, const void *k, const void *v, const fl
 }
 
 // Segments of the sequence-parallel form for a chunkwise forward (1: the
-// sequential kernels) and the workspace it needs.  Only final-state calls with
-// bf16 operands, the per-key-channel gate and K = V = 128 take that form.
+// sequential kernels) and the workspace it needs.  Calls with bf16 operands,
+// the per-key-channel gate and K = V = 128 take that form (with_o: also those
+// that write o; the entry point that allocates nothing plans final-state calls
+// only).
 int chunk_fwd_plan(int B, int T, int H, int K, int V, gdn_dtype dtype, gdn_gate gate, bool want_o,
-                   unsigned long long *bytes)
+                   unsigned long long *bytes, bool with_o = true)
 {
     *bytes = 0;
-    if (want_o || dtype != GDN_BF16 || gate != GDN_GATE_CHANNEL || K != 128 || V != 128) return 1;
+    if ((want_o && !with_o) || dtype != GDN_BF16 || gate != GDN_GATE_CHANNEL || K != 128 || V != 128)
+        return 1;
     const int nseg = gdn::chunk_fwd_seg_count(B, T, H);
-    *bytes = gdn::chunk_fwd_seg_workspace(B, H, nseg);
+    *bytes = gdn::chunk_fwd_seg_workspace(B, H, nseg, want_o);
     return nseg;
 }
 
@@ -212,7 +215,7 @@ gdn_status gdn_chunk_fwd_ws(const void *q, const void *k, const void *v, const f
                                           dtype, gate);
     if (st != GDN_OK) return st;
     unsigned long long need = 0;
-    const int nseg = chunk_fwd_plan(B, T, H, K, V, dtype, gate, o != nullptr, &need);
+    int nseg = chunk_fwd_plan(B, T, H, K, V, dtype, gate, o != nullptr, &need);
     if (need > 0) {
         if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return GDN_EINVAL;
         // the workspace must not touch any input or output
@@ -229,9 +232,12 @@ gdn_status gdn_chunk_fwd_ws(const void *q, const void *k, const void *v, const f
     }
     if (B == 0 || H == 0) return GDN_OK;
     if (!S_T && T == 0) return GDN_OK;
+    // The o pass starts segment 0 from S0 after the final state is written:
+    // with S_T in place over S0 (or no S_T at all) the call runs sequentially.
+    if (o && (!S_T || (S0 && (const void *)S0 == (const void *)S_T))) nseg = 1;
     hipError_t e;
     if (nseg > 1)
-        e = gdn::chunk_fwd_seg_launch(k, v, g, beta, S0, S_T, workspace, B, T, H, nseg,
+        e = gdn::chunk_fwd_seg_launch(q, k, v, g, beta, S0, o, S_T, workspace, B, T, H, nseg,
                                       static_cast<hipStream_t>(stream));
     else
         e = gdn::chunk_fwd_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL, K, q, k, v, g, beta,
@@ -248,7 +254,7 @@ gdn_status gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, co
                                           dtype, gate);
     if (st != GDN_OK) return st;
     unsigned long long need = 0;
-    const int nseg = chunk_fwd_plan(B, T, H, K, V, dtype, gate, o != nullptr, &need);
+    const int nseg = chunk_fwd_plan(B, T, H, K, V, dtype, gate, o != nullptr, &need, false);
     // the segment maps must fit the library's static scratch
     if (need > gdn::chunk_fwd_seg_scratch_bytes()) return GDN_ENOTSUP;
     if (B == 0 || H == 0) return GDN_OK;
@@ -258,8 +264,8 @@ gdn_status gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, co
         void *ws = nullptr;
         e = gdn::seg_scratch(&ws);
         if (e == hipSuccess)
-            e = gdn::chunk_fwd_seg_launch(k, v, g, beta, S0, S_T, ws, B, T, H, nseg,
-                                          static_cast<hipStream_t>(stream));
+            e = gdn::chunk_fwd_seg_launch(nullptr, k, v, g, beta, S0, nullptr, S_T, ws, B, T, H,
+                                          nseg, static_cast<hipStream_t>(stream));
     } else {
         e = gdn::chunk_fwd_launch(dtype == GDN_BF16, gate == GDN_GATE_CHANNEL, K, q, k, v, g, beta,
                                   S0, o, S_T, B, T, H, V, static_cast<hipStream_t>(stream));

@@ -81,7 +81,9 @@ typedef enum { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_act;
  *   S_T   [B, H, K, V]   fp32 final state, or NULL.  May equal S0 (updated in
  *                        place); must not partially overlap any other buffer.
  *
- * K and V: 64 or 128 (GDN_F32: K = 64).  chunk: 64 (tokens per chunk).  64 rows
+ * K and V: 64 or 128 (GDN_F32: K = 64; fp32 with K = 128 is GDN_ENOTSUP, since one
+ * chunk's fp32 operand tiles would not fit the 160 KB of LDS a workgroup may
+ * use).  chunk: 64 (tokens per chunk).  64 rows
  * of H * max(K, V) fp32 values must stay below 2^31 bytes (H < 65536 at 128;
  * GDN_ENOTSUP otherwise: the kernels address a chunk with 32-bit offsets).  Any
  * T >= 0: a partial last chunk behaves as if padded with identity tokens
@@ -106,16 +108,19 @@ GDN_API gdn_status gdn_chunk_fwd_workspace_size(int B, int T, int H, int K, int 
                                                 size_t *bytes);
 
 /*
- * gdn_chunk_fwd with a caller-provided workspace, which lets a call that needs
- * only the final state run the sequence-parallel form: each (b, h) sequence is
- * cut into segments of whole chunks that run at the same time, every segment
- * after the first reduced to the affine map S -> M S + N it applies to the state
- * (each chunk is such a map and maps compose associatively: the recurrence of
- * the Atomic-GDN2 model card, section 2.1, whose kernel benchmark, section 5.1,
- * is against an associative scan of it), and the maps of a sequence are then
- * applied in order to the state from the first segment (fp32).  The form is
- * used for o == NULL with bf16 operands, GDN_GATE_CHANNEL and K = V = 128 when
- * B * H is too small to fill the device; every other call runs as
+ * gdn_chunk_fwd with a caller-provided workspace, which lets a long call run
+ * the sequence-parallel form: each (b, h) sequence is cut into segments of
+ * whole chunks that run at the same time, every segment after the first
+ * reduced to the affine map S -> M S + N it applies to the state (each chunk is
+ * such a map and maps compose associatively: the recurrence of the Atomic-GDN2
+ * model card, section 2.1, whose kernel benchmark, section 5.1, is against an
+ * associative scan of it), and the maps of a sequence are then applied in
+ * order to the state from the first segment (fp32).  A call that also writes o
+ * keeps the state entering each segment and then runs the chunk kernel on
+ * every segment at once from it.  The form is used with bf16 operands,
+ * GDN_GATE_CHANNEL and K = V = 128 when B * H is too small to fill the device;
+ * with o it also needs S_T non-NULL and not S0 itself (otherwise the call runs
+ * sequentially, and the workspace goes unused).  Every other call runs as
  * gdn_chunk_fwd.
  *
  *   arguments as gdn_chunk_fwd, plus

@@ -281,12 +281,12 @@ def test_long_prefill_48_heads_sampled():
     """T = 262144 with 48 heads of 128 x 128 fp32 state and a given S0: the GPU
     runs the whole batch; the oracle follows three heads over the whole sequence.
     The sequential kernels' call without o (the final state only, which skips q)
-    gives the same state bit for bit (the sequence-parallel form of the same call
+    gives the same state bit for bit (the sequence-parallel form of both calls
     is checked in test_gpu_seg.py)."""
     cfg = CHUNK_CONFIGS["channel_long"]
     _say(f"[modes] long prefill B{cfg.B} H{cfg.H} T{cfg.T}")
     d = chunk_inputs(cfg, device=DEV)
-    o, S = _chunk(d)
+    o, S = _chunk(d, workspace=False)
     _, S_only = _chunk(d, want_o=False, workspace=False)
     assert torch.equal(S_only, S)
     heads = [0, 23, cfg.H - 1]

@@ -134,3 +134,87 @@ def test_long_prefill_segments_48_heads():
     cfg = CHUNK_CONFIGS["channel_long"]
     d = chunk_inputs(cfg, device=DEV)
     _check(cfg, d, "long prefill", oracle_heads=[0, 17, 47])
+
+
+# --- the sequence-parallel form of a call that also writes o ----------------------------
+def _gpu_rel(x, ref):
+    """Per-batch-row slice_rel of one head's [B, T, V] output, on the GPU; also
+    checks that x is finite."""
+    x, ref = x.float(), ref.float()
+    assert torch.isfinite(x).all()
+    err = (x - ref).abs().amax(dim=(1, 2))
+    scale = ref.abs().amax(dim=(1, 2))
+    return float((err / torch.where(scale > 0, scale, torch.ones_like(scale))).max())
+
+
+def _with_o(d):
+    """(o, S_T) from the segment form and from the sequential kernels."""
+    o_seg, S_seg = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], want_o=True)
+    o_seq, S_seq = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], want_o=True,
+                                 workspace=False)
+    torch.cuda.synchronize()
+    return o_seg, S_seg, o_seq, S_seq
+
+
+def _check_o(cfg, d, label, oracle_heads=None):
+    n = gdn.gdn_chunk_fwd_workspace_size(cfg.B, cfg.T, cfg.H, cfg.K, cfg.V, torch.bfloat16,
+                                         gdn.GDN_GATE_CHANNEL, True)
+    nseg = 1 + n // (cfg.B * cfg.H * 3 * cfg.K * cfg.K * 4) if n else 1
+    _say(f"[seg+o] {label}: B{cfg.B} H{cfg.H} T{cfg.T}, {nseg} segments")
+    assert nseg >= 2, "case does not exercise the segment form"
+    o_seg, S_seg, o_seq, S_seq = _with_o(d)
+    # segment form against the sequential kernels on every head, reduced on the
+    # GPU (the long prefill's o is 1.6 G elements)
+    e_o = max(_gpu_rel(o_seg[:, :, h], o_seq[:, :, h]) for h in range(cfg.H))
+    assert torch.isfinite(S_seg).all()
+    e_S = slice_rel(to_np(S_seg), to_np(S_seq), (0, 1))
+    _say(f"[seg+o] {label}: vs sequential o {e_o:.3e} S_T {e_S:.3e}; oracle next")
+    heads = list(range(cfg.H)) if oracle_heads is None else oracle_heads
+    hs = lambda x: x[:, :, heads].contiguous().cpu()
+    S0 = d["S0"]
+    ro, rS = oracle.forward(hs(d["q"]), hs(d["k"]), hs(d["v"]), hs(d["g"]), hs(d["beta"]),
+                            None if S0 is None else S0[:, heads].cpu())
+    eo_or = slice_rel(to_np(o_seg[:, :, heads]), ro, (0, 2))
+    eS_or = slice_rel(to_np(S_seg[:, heads]), rS, (0, 1))
+    _say(f"[seg+o] {label}: vs oracle o {eo_or:.3e} S_T {eS_or:.3e}")
+    assert max(e_o, e_S, eo_or, eS_or) <= TOL_BF16
+
+
+@pytest.mark.parametrize("B,H,T,s0", [
+    (1, 2, 2048, 0.02),      # two segments
+    (1, 2, 4196, 0.0),       # four segments, the last one ragged, S0 absent
+    (2, 3, 8192, 0.02),      # eight segments, six sequences
+])
+def test_segments_with_o_match(B, H, T, s0):
+    cfg = _cfg(B, H, T, s0)
+    _check_o(cfg, _dev(chunk_inputs(cfg)), f"random T{T}")
+
+
+def test_segments_with_o_slow_decay():
+    cfg = _cfg(1, 2, 8192, 0.05, g_scale=0.01)
+    _check_o(cfg, _dev(chunk_inputs(cfg)), "slow decay")
+
+
+def test_segments_with_o_in_place_state_runs_sequentially():
+    """S_T = S0 with o: the o pass would need S0 after it is overwritten, so the
+    call runs the sequential kernels (bit for bit gdn_chunk_fwd)."""
+    cfg = _cfg(1, 2, 4096, 0.05)
+    d = _dev(chunk_inputs(cfg))
+    n = gdn.gdn_chunk_fwd_workspace_size(cfg.B, cfg.T, cfg.H, cfg.K, cfg.V, torch.bfloat16,
+                                         gdn.GDN_GATE_CHANNEL, True)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    S_io = d["S0"].clone()
+    o = torch.empty_like(d["v"])
+    gdn.gdn_chunk_fwd_ws(d["q"], d["k"], d["v"], d["g"], d["beta"], S_io, o, S_io, ws)
+    o2, S2 = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S_io, S2)
+
+
+@pytest.mark.timeout(600)
+def test_long_prefill_with_o_segments_48_heads():
+    """The 262,144-token, 48-head prefill writing o and S_T: every head against the
+    sequential kernels, three heads against the fp64 oracle."""
+    cfg = CHUNK_CONFIGS["channel_long"]
+    d = chunk_inputs(cfg, device=DEV)
+    _check_o(cfg, d, "long prefill", oracle_heads=[0, 17, 47])
