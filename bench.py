@@ -58,19 +58,22 @@ MEASURED_TRAFFIC = {
                                  "34acdf37d6007014", 862390784),
     "chunk_fwd_wsc_kernel<128>": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                    "mfma_frag.h"),
-                                  "4db84347cb4fcae9", 420155567),
+                                  "7f74300dedd8aaf6", 420170336),
     "recurrent_step_kernel<bf16,128,128,channel>": (("recurrent_step.hip", "gdn_common.h"),
-                                                    "1864f0aa1a777d85", 1642879983),
+                                                    "6075e5972b67aade", 1642950528),
     "recurrent_multi_kernel<bf16,128,128,channel>/final": (("recurrent_multi.hip", "gdn_common.h"),
                                                            "e96c18f898c72e85", 1739625626),
     "recurrent_multi_kernel<bf16,128,128,channel>/hist": (("recurrent_multi.hip", "gdn_common.h"),
                                                           "e96c18f898c72e85", 4158918874),
-    "prologue_kernel<bf16,128,128,scalar,silu>": (("prologue.hip", "prologue.h", "gdn_common.h"),
-                                                  "1fb5d0b92490e05a", 1307185835),
+    "prologue_kernel<bf16,128,128,scalar,silu>": (("prologue.hip", "prologue.h", "prologue_ops.h",
+                                                   "gdn_common.h"), "672309d493c963a2", 1307198496),
     "recurrent_step_prologue_kernel<bf16,128,128,channel,silu>": (("prologue.hip", "prologue.h",
-                                                                  "gdn_common.h"), "1fb5d0b92490e05a", 1719304713),
+                                                                  "prologue_ops.h", "gdn_common.h"),
+                                                                 "672309d493c963a2", 1719409472),
     "chunk_fwd_seg/channel_long": (("chunk_fwd_seg.hip", "ws_common.h", "gdn_common.h",
-                                    "mfma_frag.h"), "5b835b50d5c71204", 13596717888),
+                                    "mfma_frag.h"), "a40e09848624a8f0", 13604052000),
+    "chunk_fwd_seg/channel_long/o": (("chunk_fwd_seg.hip", "chunk_fwd_wsc.hip", "ws_common.h",
+                                      "gdn_common.h", "mfma_frag.h"), "6700ae7994480fee", 33518181008),
 }
 
 # bf16 matrix-core work per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16, units of 512
