@@ -127,21 +127,21 @@ def test_steps_zero_tokens_copies_the_state():
     assert torch.equal(S_T, S0)
 
 
-def test_steps_full_size_sampled():
+@pytest.mark.timeout(600)
+def test_steps_full_size_every_slice():
     """256 sequences x 48 heads of 128x128 fp32 state, M = 4 draft tokens with the
-    per-token states kept; the oracle follows a sample of sequences."""
+    per-token states kept; the oracle follows every (n, h) slice."""
     cfg = DECODE_CONFIG.with_(steps=4)
-    _say(f"[multi] full N{cfg.N} H{cfg.H} M{cfg.steps}")
+    _say(f"[multi] full N{cfg.N} H{cfg.H} M{cfg.steps}, every slice")
     d = decode_inputs(cfg, device=DEV)
     o, S_T, S_hist = _run(d)
-    rng = np.random.default_rng(1)
-    ns = np.unique(np.concatenate([rng.choice(cfg.N, 6, replace=False), [0, cfg.N - 1]]))
-    sel = {n: d[n][:, ns].cpu() for n in ("q", "k", "v", "g", "beta")}
-    S0 = d["S0"][ns].cpu()
+    sel = {n: d[n].cpu() for n in ("q", "k", "v", "g", "beta")}
+    S0 = d["S0"].cpu()
+    _say("[multi] full: GPU done, oracle on every slice")
     ro, rS = oracle.decode(sel["q"], sel["k"], sel["v"], sel["g"], sel["beta"], S0)
     rh = _oracle_hist(sel, S0)
-    eo = slice_rel(to_np(o[ns]).transpose(1, 0, 2, 3), ro, (0, 1, 2))
-    eS = slice_rel(to_np(S_T[ns]), rS, (0, 1))
-    eh = slice_rel(to_np(S_hist[ns]).transpose(1, 0, 2, 3, 4), rh, (0, 1, 2))
+    eo = slice_rel(to_np(o).transpose(1, 0, 2, 3), ro, (0, 1, 2))
+    eS = slice_rel(to_np(S_T), rS, (0, 1))
+    eh = slice_rel(to_np(S_hist).transpose(1, 0, 2, 3, 4), rh, (0, 1, 2))
     _say(f"[multi] full: err_o={eo:.3e} err_S={eS:.3e} err_hist={eh:.3e}")
     assert eo <= TOL_BF16 and eS <= TOL_BF16 and eh <= TOL_BF16

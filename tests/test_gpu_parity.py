@@ -76,26 +76,24 @@ def test_decode_small(K, V, gate, dtype):
     assert slice_rel(to_np(S), rS, (0, 1)) <= tol
 
 
-def test_decode_full_config_sampled():
+@pytest.mark.timeout(600)
+def test_decode_full_config_every_slice():
     """256 sequences x 48 heads of 128x128 fp32 state, 64 chained in-place steps;
-    the oracle follows a sample of (n, h) slices through all 64 steps."""
+    the oracle follows every (n, h) slice through all 64 steps."""
     cfg = DECODE_CONFIG
-    _say(f"[parity] decode full N{cfg.N} H{cfg.H} steps{cfg.steps}")
+    _say(f"[parity] decode full N{cfg.N} H{cfg.H} steps{cfg.steps}, every slice")
     d = decode_inputs(cfg, device=DEV)
     S = d["S0"].clone()
     o = torch.empty(cfg.steps, cfg.N, cfg.H, cfg.V, dtype=torch.bfloat16, device=DEV)
     for s in range(cfg.steps):
         gdn.gdn_recurrent_step(d["q"][s], d["k"][s], d["v"][s], d["g"][s], d["beta"][s], S, o[s])
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    ns = rng.choice(cfg.N, 12, replace=False)
-    ns = np.unique(np.concatenate([ns, [0, cfg.N - 1]]))
-    sel = lambda t: t[:, ns].cpu()
-    ro, rS = oracle.decode(sel(d["q"]), sel(d["k"]), sel(d["v"]), sel(d["g"]), sel(d["beta"]),
-                           d["S0"][ns].cpu())
-    eo = slice_rel(to_np(o[:, ns]), ro, (0, 1, 2))
-    eS = slice_rel(to_np(S[ns]), rS, (0, 1))
-    _say(f"[parity] decode full: err_o={eo:.3e} err_S={eS:.3e}")
+    _say("[parity] decode full: GPU done, oracle on every slice")
+    ro, rS = oracle.decode(d["q"].cpu(), d["k"].cpu(), d["v"].cpu(), d["g"].cpu(), d["beta"].cpu(),
+                           d["S0"].cpu())
+    eo = slice_rel(to_np(o), ro, (0, 1, 2))
+    eS = slice_rel(to_np(S), rS, (0, 1))
+    _say(f"[parity] decode full: err_o={eo:.3e} err_S={eS:.3e} over {cfg.N * cfg.H} slices")
     assert eo <= TOL_BF16 and eS <= TOL_BF16
 
 
