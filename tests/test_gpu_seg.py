@@ -54,15 +54,20 @@ def _check(cfg, d, label, oracle_heads=None):
     S_seg, S_seq = _state_only(d)
     assert torch.isfinite(S_seg).all()
     e_seq = slice_rel(to_np(S_seg), to_np(S_seq), (0, 1))
-    sel = (lambda x: x) if oracle_heads is None else (lambda x: x[:, :, oracle_heads].contiguous())
-    S0 = d["S0"]
-    S0h = None if S0 is None else (S0 if oracle_heads is None else S0[:, oracle_heads]).cpu()
-    _, rS = oracle.forward(sel(d["q"]).cpu(), sel(d["k"]).cpu(), sel(d["v"]).cpu(),
-                           sel(d["g"]).cpu(), sel(d["beta"]).cpu(), S0h, want_o=False)
-    got = S_seg if oracle_heads is None else S_seg[:, oracle_heads]
-    e_or = slice_rel(to_np(got), rS, (0, 1))
-    seq = S_seq if oracle_heads is None else S_seq[:, oracle_heads]
-    e_seq_or = slice_rel(to_np(seq), rS, (0, 1))
+    # the oracle in groups of at most 8 heads, a progress line after each
+    heads = list(range(cfg.H)) if oracle_heads is None else list(oracle_heads)
+    e_or = e_seq_or = 0.0
+    for i in range(0, len(heads), 8):
+        hs = heads[i:i + 8]
+        sel = lambda x: x[:, :, hs].contiguous().cpu()
+        S0 = d["S0"]
+        S0h = None if S0 is None else S0[:, hs].cpu()
+        kh = sel(d["k"])
+        # q only enters o, which a final-state call does not compute: k stands in
+        _, rS = oracle.forward(kh, kh, sel(d["v"]), sel(d["g"]), sel(d["beta"]), S0h, want_o=False)
+        e_or = max(e_or, slice_rel(to_np(S_seg[:, hs]), rS, (0, 1)))
+        e_seq_or = max(e_seq_or, slice_rel(to_np(S_seq[:, hs]), rS, (0, 1)))
+        _say(f"[seg] {label}: oracle on heads {hs[0]}..{hs[-1]} done")
     _say(f"[seg] {label}: err vs oracle {e_or:.3e} (sequential kernels {e_seq_or:.3e}), "
          f"segment form vs sequential {e_seq:.3e}")
     assert e_or <= TOL_BF16 and e_seq <= TOL_BF16
@@ -125,15 +130,14 @@ def test_segments_in_place_and_deterministic():
     assert torch.equal(S_io, S1)
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_long_prefill_segments_48_heads():
     """The 262,144-token, 48-head prefill (final state only, random S0) in the
     launch configuration the bench times: every head against the sequential
-    kernels' state, and a sample of heads against the fp64 oracle over the whole
-    sequence."""
+    kernels' state and against the fp64 oracle over the whole sequence."""
     cfg = CHUNK_CONFIGS["channel_long"]
     d = chunk_inputs(cfg, device=DEV)
-    _check(cfg, d, "long prefill", oracle_heads=[0, 17, 47])
+    _check(cfg, d, "long prefill")
 
 
 # --- the sequence-parallel form of a call that also writes o ----------------------------
