@@ -8,7 +8,7 @@
 namespace gdn {
 
 // value columns per workgroup in the two state sweeps
-constexpr int BW_VB = 16;
+constexpr int BW_VB = 32;
 
 // Intermediates, each an array over the B*H*ceil(T/64) chunks (chunk
 // ci = (b H + h) NC + c).  fp32, rows of a chunk contiguous, except where

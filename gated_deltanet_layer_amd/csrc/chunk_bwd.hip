@@ -571,7 +571,7 @@ template <int N> __device__ __forceinline__ void interleave_loads()
     }
 }
 
-// Store a K x 16 block held transposed in LDS (St[y][x], row stride ls) to
+// Store a K x BW_VB block held transposed in LDS (St[y][x], row stride ls) to
 // global rows V elements apart (dst points at column v0 of row 0), in the
 // input dtype: bf16 inputs keep the per-chunk states and their gradients as
 // bf16 (the gradient kernels read them as operands of their products, as the
@@ -579,16 +579,18 @@ template <int N> __device__ __forceinline__ void interleave_loads()
 template <int K, int V, typename ST>
 __device__ __forceinline__ void store_state_block(ST *dst, const float *St, int ls)
 {
-    for (int v = threadIdx.x; v < K * 4; v += BW_NTHR) {
-        const int x = v >> 2, y = (v & 3) * 4;
+    constexpr int NG = BW_VB / 4;   // groups of four value columns
+    for (int v = threadIdx.x; v < K * NG; v += BW_NTHR) {
+        const int x = v / NG, y = (v % NG) * 4;
         st4(dst + (long)x * V + y,
             f32x4{St[y * ls + x], St[(y + 1) * ls + x], St[(y + 2) * ls + x], St[(y + 3) * ls + x]});
     }
 }
 
-// One workgroup per (slice, block of 16 value columns), chunks in order; wave
-// w owns rows 16 w .. 16 w + 15 of the C x 16 products and K/4 rows of the
-// state block, which stays in its accumulators.  The A fragments of a chunk
+// One workgroup per (slice, block of BW_VB value columns), chunks in order;
+// wave w owns rows 16 w .. 16 w + 15 of the C x BW_VB products and K/4 rows of
+// the state block, which stays in its accumulators (one 16 x 16 tile per 16
+// value columns).  The A fragments of a chunk
 // sit in one of two register sets: all of the next chunk's loads go into the
 // other set right after this chunk's operands are in LDS, a whole chunk of
 // work before they are used (the loop is unrolled by two so that the sets keep
@@ -605,11 +607,12 @@ template <typename DT, int K, int C, int KT, int VB> struct StSet {
 template <typename DT, int K, int V>
 __device__ __forceinline__ void states_sweep(const BwArgs &a, int blk)
 {
-    constexpr int C = BW_C, VB = 16, NVB = V / VB, KT = K / 64, LK = K + 4, LC = C + 4, VP = VB + 1;
+    constexpr int C = BW_C, VB = BW_VB, NT = VB / 16, NVB = V / VB, KT = K / 64, LK = K + 4,
+                  LC = C + 4, VP = VB + 1;
     extern __shared__ __attribute__((aligned(256))) float sm[];
-    float *sSt = sm;                 // [16][LK]  S, transposed
-    float *sRt = sSt + VB * LK;      // [16][LC]  R = beta (V - Kp S), transposed
-    float *sDt = sRt + VB * LC;      // [16][LC]  Delta, transposed
+    float *sSt = sm;                 // [VB][LK]  S, transposed
+    float *sRt = sSt + VB * LK;      // [VB][LC]  R = beta (V - Kp S), transposed
+    float *sDt = sRt + VB * LC;      // [VB][LC]  Delta, transposed
     float *sV = sDt + VB * LC;       // [C][VP]   v tile
     float *sb = sV + C * VP;         // [C]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r = lane & 15;
@@ -643,14 +646,17 @@ __device__ __forceinline__ void states_sweep(const BwArgs &a, int blk)
             f.km[h].template load<0, C / 16>(reinterpret_cast<const DT *>(a.ws.KmT) + ci * (K * C) + (KT * w + h) * (16 * C));
     };
 
-    f32x4 S[KT];
+    f32x4 S[KT][NT];
 #pragma unroll
     for (int h = 0; h < KT; ++h) {
         const int x0 = 16 * (KT * w + h) + 4 * gq;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            S[h][e] = a.S0 ? a.S0[((long)sl * K + x0 + e) * V + v0 + r] : 0.f;
-        *reinterpret_cast<f32x4 *>(sSt + r * LK + x0) = S[h];
+        for (int j = 0; j < NT; ++j) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[h][j][e] = a.S0 ? a.S0[((long)sl * K + x0 + e) * V + v0 + 16 * j + r] : 0.f;
+            *reinterpret_cast<f32x4 *>(sSt + (16 * j + r) * LK + x0) = S[h][j];
+        }
     }
 
     auto chunk = [&](Set &f, Set &nf, int c) {
@@ -663,22 +669,24 @@ __device__ __forceinline__ void states_sweep(const BwArgs &a, int blk)
         // unconditional (the last chunk fetches itself again), so that the
         // compiler's waits see one straight path
         fetch(nf, min(c + 1, a.NC - 1));
-        {   // R = beta (V - Kp S)
-            const f32x4 X = mma_rows<K / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.kp, sSt, LK);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {   // R = beta (V - Kp S)
+            const f32x4 X = mma_rows<K / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.kp, sSt + 16 * j * LK, LK);
             f32x4 R;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * w + 4 * gq + e;
-                R[e] = sb[t] * (sV[t * VP + r] - X[e]);
+                R[e] = sb[t] * (sV[t * VP + 16 * j + r] - X[e]);
             }
-            *reinterpret_cast<f32x4 *>(sRt + r * LC + 16 * w + 4 * gq) = R;
+            *reinterpret_cast<f32x4 *>(sRt + (16 * j + r) * LC + 16 * w + 4 * gq) = R;
         }
         interleave_loads<KT + (K / 16 + C / 16 + KT * C / 16) / SP>();
         lds_barrier();
-        {   // Delta = T R
-            const f32x4 D = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.t, sRt, LC);
-            *reinterpret_cast<f32x4 *>(sDt + r * LC + 16 * w + 4 * gq) = D;
-            float *Dl = a.ws.Dl + ci * (C * V) + v0 + r;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {   // Delta = T R
+            const f32x4 D = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.t, sRt + 16 * j * LC, LC);
+            *reinterpret_cast<f32x4 *>(sDt + (16 * j + r) * LC + 16 * w + 4 * gq) = D;
+            float *Dl = a.ws.Dl + ci * (C * V) + v0 + 16 * j + r;
 #pragma unroll
             for (int e = 0; e < 4; ++e) Dl[(16 * w + 4 * gq + e) * V] = D[e];
         }
@@ -686,9 +694,12 @@ __device__ __forceinline__ void states_sweep(const BwArgs &a, int blk)
         // S = Diag(e^{gn}) S + Km^T Delta
 #pragma unroll
         for (int h = 0; h < KT; ++h) {
-            S[h] *= f.g[h];
-            S[h] = mma_rows<C / 16>(S[h], f.km[h], sDt, LC);
-            *reinterpret_cast<f32x4 *>(sSt + r * LK + 16 * (KT * w + h) + 4 * gq) = S[h];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                S[h][j] *= f.g[h];
+                S[h][j] = mma_rows<C / 16>(S[h][j], f.km[h], sDt + 16 * j * LC, LC);
+                *reinterpret_cast<f32x4 *>(sSt + (16 * j + r) * LK + 16 * (KT * w + h) + 4 * gq) = S[h][j];
+            }
         }
     };
 
@@ -719,12 +730,12 @@ template <typename DT, int K, int C, int KT, int VB> struct DsSet {
 template <typename DT, int K, int V>
 __device__ __forceinline__ void dstates_sweep(const BwArgs &a, int blk)
 {
-    constexpr int C = BW_C, VB = 16, NVB = V / VB, KT = K / 64;
+    constexpr int C = BW_C, VB = BW_VB, NT = VB / 16, NVB = V / VB, KT = K / 64;
     constexpr int LK = K + 4, LC = C + 4, L2 = 2 * C + 4;
     extern __shared__ __attribute__((aligned(256))) float sm[];
-    float *sdSt = sm;                // [16][LK]  dS', transposed
-    float *sOYt = sdSt + VB * LK;    // [16][L2]  columns 0..C-1: dO^T, C..2C-1: (-beta Y)^T
-    float *sdDt = sOYt + VB * L2;    // [16][LC]  dDelta, transposed
+    float *sdSt = sm;                // [VB][LK]  dS', transposed
+    float *sOYt = sdSt + VB * LK;    // [VB][L2]  columns 0..C-1: dO^T, C..2C-1: (-beta Y)^T
+    float *sdDt = sOYt + VB * L2;    // [VB][LC]  dDelta, transposed
     float *sb = sdDt + VB * LC;      // [C]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r = lane & 15;
     int sl, vb;
@@ -755,14 +766,17 @@ __device__ __forceinline__ void dstates_sweep(const BwArgs &a, int blk)
         }
     };
 
-    f32x4 dS[KT];
+    f32x4 dS[KT][NT];
 #pragma unroll
     for (int h = 0; h < KT; ++h) {
         const int x0 = 16 * (KT * w + h) + 4 * gq;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            dS[h][e] = a.dS_T ? a.dS_T[((long)sl * K + x0 + e) * V + v0 + r] : 0.f;
-        *reinterpret_cast<f32x4 *>(sdSt + r * LK + x0) = dS[h];
+        for (int j = 0; j < NT; ++j) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dS[h][j][e] = a.dS_T ? a.dS_T[((long)sl * K + x0 + e) * V + v0 + 16 * j + r] : 0.f;
+            *reinterpret_cast<f32x4 *>(sdSt + (16 * j + r) * LK + x0) = dS[h][j];
+        }
     }
 
     auto chunk = [&](Set &f, Set &nf, int c) {
@@ -784,29 +798,34 @@ __device__ __forceinline__ void dstates_sweep(const BwArgs &a, int blk)
         store_state_block<K, V>(reinterpret_cast<DT *>(a.ws.dhS) + ci * (K * V) + v0, sdSt, LK);   // dL/d(state leaving c)
         lds_barrier();
         fetch(nf, max(c - 1, 0));   // unconditional: one straight path for the compiler's waits
-        {   // dDelta = Km dS' + P^T dO
-            f32x4 dD = mma_rows<K / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.km, sdSt, LK);
-            dD = mma_rows<C / 16>(dD, f.pt, sOYt, L2);
-            *reinterpret_cast<f32x4 *>(sdDt + r * LC + 16 * w + 4 * gq) = dD;
-            float *dDl = a.ws.dDl + ci * (C * V) + v0 + r;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {   // dDelta = Km dS' + P^T dO
+            f32x4 dD = mma_rows<K / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.km, sdSt + 16 * j * LK, LK);
+            dD = mma_rows<C / 16>(dD, f.pt, sOYt + 16 * j * L2, L2);
+            *reinterpret_cast<f32x4 *>(sdDt + (16 * j + r) * LC + 16 * w + 4 * gq) = dD;
+            float *dDl = a.ws.dDl + ci * (C * V) + v0 + 16 * j + r;
 #pragma unroll
             for (int e = 0; e < 4; ++e) dDl[(16 * w + 4 * gq + e) * V] = dD[e];
         }
         interleave_loads<KT + (K / 16 + 2 * C / 16 + KT * 2 * C / 16) / SP>();
         lds_barrier();
-        {   // Y = T^T dDelta, kept as -beta Y
-            f32x4 Y = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.tt, sdDt, LC);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {   // Y = T^T dDelta, kept as -beta Y
+            f32x4 Y = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.tt, sdDt + 16 * j * LC, LC);
 #pragma unroll
             for (int e = 0; e < 4; ++e) Y[e] *= -sb[16 * w + 4 * gq + e];
-            *reinterpret_cast<f32x4 *>(sOYt + r * L2 + C + 16 * w + 4 * gq) = Y;
+            *reinterpret_cast<f32x4 *>(sOYt + (16 * j + r) * L2 + C + 16 * w + 4 * gq) = Y;
         }
         lds_barrier();
         // dS = Diag(e^{gn}) dS' + [Qp^T | Kp^T] [dO; -beta Y]
 #pragma unroll
         for (int h = 0; h < KT; ++h) {
-            dS[h] *= f.g[h];
-            dS[h] = mma_rows<2 * C / 16>(dS[h], f.qk[h], sOYt, L2);
-            *reinterpret_cast<f32x4 *>(sdSt + r * LK + 16 * (KT * w + h) + 4 * gq) = dS[h];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                dS[h][j] *= f.g[h];
+                dS[h][j] = mma_rows<2 * C / 16>(dS[h][j], f.qk[h], sOYt + 16 * j * L2, L2);
+                *reinterpret_cast<f32x4 *>(sdSt + (16 * j + r) * LK + 16 * (KT * w + h) + 4 * gq) = dS[h][j];
+            }
         }
     };
 
@@ -825,19 +844,23 @@ __device__ __forceinline__ void dstates_sweep(const BwArgs &a, int blk)
         for (int h = 0; h < KT; ++h) {
             const int x0 = 16 * (KT * w + h) + 4 * gq;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a.dS0[((long)sl * K + x0 + e) * V + v0 + r] = dS[h][e];
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a.dS0[((long)sl * K + x0 + e) * V + v0 + 16 * j + r] = dS[h][j][e];
         }
     }
 }
 
 // The two sweeps in one launch: the backward one reads only prep's operands,
 // dO and dL/dS_T, not the forward one's results, so they run side by side
-// (workgroups [0, nvb) walk forward, [nvb, 2 nvb) backward).  With both at two
-// waves per SIMD, each CU can hold one of each, and the chip's 256 CUs are no
-// longer a quarter idle as with either sweep alone.  nvb is a multiple of 8
-// whenever the XCD mapping applies, so the backward half keeps it.  fp32
-// operands need more registers than two waves per SIMD allow: that variant
-// keeps one.
+// (workgroups [0, nvb) walk forward, [nvb, 2 nvb) backward).  A sweep's period
+// per chunk is set by fetching the chunk's operands (the same for every value
+// block of a slice) and storing its state and Delta blocks, not by its
+// products: 32 value columns per workgroup (measured: 207 us for the 4 x 6 x
+// 4096 shape, against 224 us with 16) halve the operand fetches per slice and
+// leave one workgroup per CU.  nvb is a multiple of 8 whenever the XCD mapping
+// applies, so the backward half keeps it.  fp32 operands need more registers
+// than two waves per SIMD allow: that variant keeps one.
 template <typename DT, int K, int V> __device__ __forceinline__ void sweeps(const BwArgs &a)
 {
     const int nvb = a.NS * (V / BW_VB);
@@ -887,6 +910,23 @@ __device__ __forceinline__ f32x4 mma_lds(f32x4 acc, const float *A, const float 
         for (int j = 0; j < 4; ++j) acc = mfma_f32(av[j], bv[j], acc);
     }
     return acc;
+}
+
+// Eight fp32 values as two bf16 vectors, hi = bf16(x) and lo = bf16(x - hi):
+// hi + lo carries x to about 2^-17 of its size, so a product over a split
+// operand (two bf16 products, or three with both operands split) keeps close
+// to fp32 accuracy at a fraction of the fp32 matrix cores' cost.
+__device__ __forceinline__ void split8(f32x4 a, f32x4 b, bf16x8 &hi, bf16x8 &lo)
+{
+    const bf16x4 ha = cvt4(a), hb = cvt4(b);
+    f32x4 ra, rb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        ra[e] = a[e] - (float)ha[e];
+        rb[e] = b[e] - (float)hb[e];
+    }
+    hi = cat8(ha, hb);
+    lo = cat8(cvt4(ra), cvt4(rb));
 }
 
 // Sum a per-lane value over the 16 lanes of a lane group (one row of a tile).
