@@ -30,6 +30,10 @@
 //   2 sweeps   one per value block and    forward: the state entering each
 //              direction, in one launch:  chunk and Delta; backward: dL/dS' of
 //                                         each chunk, dDelta, and dS0
+//   then, for bf16 inputs,
+//   3 grad     one per chunk:             everything below in one kernel, the
+//                                         intermediates on chip
+//   and for fp32 inputs,
 //   3 vgrad    one per chunk:             every product that sums over the
 //                                         value dimension (dv), then the C x C
 //                                         part of the chain (dbeta)
@@ -47,6 +51,7 @@
 
 #include "gdn_common.h"
 #include "chunk_bwd.h"
+#include "ws_common.h"
 
 namespace gdn {
 
@@ -1484,6 +1489,571 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
     }
 }
 
+// ---------------------------------------------------------------- 3' grad (bf16 inputs)
+// The per-chunk gradients for bf16 inputs: what vgrad and kgrad2 compute for
+// fp32 inputs, in one workgroup per chunk, every intermediate (dQp, dKm, dWn,
+// dP, dT, Z, dA, dG, d gamma) kept on chip.  Wave w owns the 16 tokens
+// 16 w .. 16 w + 15: its rows of every C x K and C x C product stay in its
+// accumulators, and only the operands that other waves need pass through LDS.
+//
+//   phase 1, 32 value columns per step (bf16 16 x 16 x 32): dQp = dO S^T,
+//     dKm = Delta dS'^T, dWn = dDelta S^T, dP = dO Delta^T (its lower blocks),
+//     dT = dDelta V^T, Y = T^T dDelta (dv, dbeta), and e^{gn} rowsum(S * dS').
+//     S and dS' come straight from the workspace into a double-buffered LDS
+//     tile (global_load_lds); dO, v, Delta, dDelta through registers, Delta
+//     and dDelta split into bf16 high and low parts (split8), with a
+//     transposed copy of dDelta for Y.
+//   phase 2, the C x C chain on single-bf16 operands: dT -= dWn (beta Kp)^T,
+//     Z = -T^T dWn, M1 = T^T dT, dA = -M1 T^T (strictly lower), dG = beta dA,
+//     dbeta += rowsum(dA * G); dWn and dT pass transposed through LDS, own
+//     tiles are turned into operand layout through a per-wave 16 x 17
+//     scratch (tile_transpose).
+//   phase 3, 32 key channels per pass (bf16 16 x 16 x 16, both operands
+//     split): the token-pair sums of kgrad2 for this wave's rows, then dq,
+//     dk, d gamma per element; dg = reverse running sum of d gamma per
+//     channel.  dP and dG reach it as this wave's own rows (operand layout,
+//     pre-split) and transposed in LDS (for the sums over later rows).
+//
+// Precision: an fp64 model of this decomposition at the benchmark's
+// distributions put the C x C chain on single bf16 at 1e-4 relative error in
+// dk, dg and dbeta, but single-bf16 Delta, dDelta (1.7e-3 in dq, dk, dg), Y
+// (1.8e-3 in dv, dbeta) or scaled k and q in the pair sums (1.7e-2 in dg)
+// too coarse; those are split, which keeps them near fp32.
+//
+// LDS (bytes, K = V = 128): 72 KB at most, two workgroups per CU.
+template <int K, int V> struct GradLds {
+    static constexpr int C = BW_C, VS = 32, LT = C + 8, LP = C + 4, LW = 36;
+    static constexpr int HDR = 1024;                                    // beta [C], e^{gn} rowsum(S dS') [K]
+    // phase 1
+    static constexpr int SZ_KS = K * VS * 2, SZ_CS = C * VS * 2, SZ_T = VS * LT * 2;
+    static constexpr int S0 = HDR, DS0 = S0 + 2 * SZ_KS;              // S, dS' [2][K][VS] bf16
+    static constexpr int O1 = DS0 + 2 * SZ_KS, V1 = O1 + SZ_CS;        // dO, v [C][VS]
+    static constexpr int DH = V1 + SZ_CS, DL = DH + SZ_CS;             // Delta high / low [C][VS]
+    static constexpr int EH = DL + SZ_CS, EL = EH + SZ_CS;             // dDelta high / low [C][VS]
+    static constexpr int TH = EL + SZ_CS, TL = TH + SZ_T;              // dDelta^T high / low [VS][LT]
+    static constexpr int END1 = TL + SZ_T;
+    // phase 2 (PT and GT stay for phase 3)
+    static constexpr int SZ_PT = C * LP * 4;
+    static constexpr int PT = HDR, GT = PT + SZ_PT;                    // dP^T, dG^T [C][LP] fp32
+    static constexpr int WT = GT + SZ_PT, TT = WT + K * LT * 2;        // dWn^T [K][LT], dT^T [C][LT] bf16
+    static constexpr int SCR = TT + C * LT * 2;                        // [4][16][17] fp32
+    static constexpr int END2 = SCR + 4 * 16 * 17 * 4;
+    // phase 3
+    static constexpr int SZ_KT = C * LW * 4;
+    static constexpr int KT = GT + SZ_PT, KH = KT + SZ_KT, QH = KH + SZ_KT;   // [C][LW] fp32
+    static constexpr int GG = QH + SZ_KT;                              // gamma of the pass [C][LW]
+    static constexpr int XT = GG + SZ_KT, XP = XT + 4 * 64 * 4;        // per-wave column sums [4][64]
+    static constexpr int END3 = XP + 4 * 64 * 4;
+    static constexpr int bytes = END1 > END2 ? (END1 > END3 ? END1 : END3) : (END2 > END3 ? END2 : END3);
+    static_assert(bytes <= 80 * 1024, "two workgroups per CU");
+    static_assert(HDR >= 4 * (C + K), "header");
+};
+
+// 16 x 16 x 16 bf16 product, lane 16 g + r holding row r (A) / column r (B),
+// k = 4 g .. 4 g + 3.
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 acc)
+{
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b),
+                                                     acc, 0, 0, 0);
+}
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo)
+{
+    hi = cvt4(x);
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = x[e] - (float)hi[e];
+    lo = cvt4(r);
+}
+// Both operands split: hi hi + hi lo + lo hi.
+__device__ __forceinline__ f32x4 mfma16x3(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl, f32x4 acc)
+{
+    return mfma16(al, bh, mfma16(ah, bl, mfma16(ah, bh, acc)));
+}
+// A 16 x 16 fp32 tile in accumulator layout (lane 16 g + r: rows 4 g .. 4 g + 3
+// of column r) into operand layout (lane 16 g + r: row r, columns 4 g ..
+// 4 g + 3), through the wave's own 16 x 17 LDS scratch.  The LDS operations of
+// one wave complete in order, so no barrier is needed.
+__device__ __forceinline__ f32x4 tile_transpose(float *scr, f32x4 x)
+{
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) scr[(4 * g + e) * 17 + r] = x[e];
+    f32x4 y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = scr[r * 17 + 4 * g + j];
+    return y;
+}
+
+template <int K, int V, bool CH>
+__global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) void bwd_grad_kernel(BwArgs a)
+{
+    using L = GradLds<K, V>;
+    constexpr int C = BW_C, NXB = K / 16, VS = L::VS, NSTEP = V / VS, LT = L::LT, LP = L::LP, LW = L::LW;
+    constexpr int XW = NXB / 4;   // key blocks of e^{gn} rowsum(S dS') per wave
+    extern __shared__ __attribute__((aligned(256))) float sm[];
+    char *smc = reinterpret_cast<char *>(sm);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
+    const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
+    const int t0 = c * C, n = min(C, a.T - t0);
+    const long ci = (long)sl * a.NC + c;
+    const long H = a.H, r0 = tok_row(a, sl, t0);
+    const __bf16 *q = (const __bf16 *)a.q + r0 * K, *k = (const __bf16 *)a.k + r0 * K;
+    const __bf16 *v = (const __bf16 *)a.v + r0 * V, *dO = (const __bf16 *)a.d_o + r0 * V;
+    __bf16 *dq = (__bf16 *)a.dq + r0 * K, *dk = (__bf16 *)a.dk + r0 * K, *dv = (__bf16 *)a.dv + r0 * V;
+    const __bf16 *hS = reinterpret_cast<const __bf16 *>(a.ws.hS) + ci * (K * V);
+    const __bf16 *dhS = reinterpret_cast<const __bf16 *>(a.ws.dhS) + ci * (K * V);
+    const float *Dl = a.ws.Dl + ci * (C * V), *dDl = a.ws.dDl + ci * (C * V);
+    const float *gam = a.ws.gam + ci * (C * K);
+    float *sb = sm, *sdgn = sm + C;
+    // phase 1's first loads go out before anything waits
+    // S and dS' of step st into buffer st & 1: 16-byte pieces, piece i =
+    // (row i / 4, columns 8 (i % 4) ..), wave w moving pieces 64 w + 256 j ..
+    auto load_sds = [&](int st) {
+        char *dS = smc + L::S0 + (st & 1) * L::SZ_KS, *dD = smc + L::DS0 + (st & 1) * L::SZ_KS;
+#pragma unroll
+        for (int i0 = 64 * w; i0 < 4 * K; i0 += BW_NTHR) {   // 4 K pieces: a multiple of 256
+            const int i = i0 + lane, row = i >> 2, col = st * VS + 8 * (i & 3);
+            g2lds16(hS + row * V + col, dS + i0 * 16);
+            g2lds16(dhS + row * V + col, dD + i0 * 16);
+        }
+    };
+    // dO, v, Delta, dDelta of a step through registers: row tr, columns c8 .. c8 + 7
+    const int tr = tid >> 2, c8 = 8 * (tid & 3);
+    const bool live = tr < n;
+    uint4 so, sv;
+    f32x4 sd0, sd1, se0, se1;
+    auto load_stage = [&](int v0) {
+        const uint4 zu = {0u, 0u, 0u, 0u};
+        so = live ? *reinterpret_cast<const uint4 *>(dO + tr * H * V + v0 + c8) : zu;
+        sv = live ? *reinterpret_cast<const uint4 *>(v + tr * H * V + v0 + c8) : zu;
+        const float *dl = Dl + tr * V + v0 + c8, *dd = dDl + tr * V + v0 + c8;
+        sd0 = *reinterpret_cast<const f32x4 *>(dl);
+        sd1 = *reinterpret_cast<const f32x4 *>(dl + 4);
+        se0 = *reinterpret_cast<const f32x4 *>(dd);
+        se1 = *reinterpret_cast<const f32x4 *>(dd + 4);
+    };
+    load_sds(0);
+    load_stage(0);
+    if (tid < C) sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
+
+    // T^T rows 16 w + r16 (this wave's A operands of Y, Z and M1), k steps p of
+    // 32 tokens in the paired-block order of the fragment layout, high / low
+    bf16x8 tth[2], ttl[2];
+    {
+        const float *tt = a.ws.TT + ci * (C * C) + (4 * w) * 256 + lane * 4;
+        f32x4 f[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) f[cb] = *reinterpret_cast<const f32x4 *>(tt + cb * 256);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) split8(f[2 * p], f[2 * p + 1], tth[p], ttl[p]);
+    }
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 aQ[NXB], aKm[NXB], aWn[NXB], aP[4], aT[4];   // tiles (w, key block) and (w, token block)
+#pragma unroll
+    for (int i = 0; i < NXB; ++i) aQ[i] = aKm[i] = aWn[i] = z4;
+#pragma unroll
+    for (int J = 0; J < 4; ++J) aP[J] = aT[J] = z4;
+    float dbv[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta at rows 16 w + 4 gq + e, this lane's columns
+    float dgp[XW];                          // rowsum(S * dS') at keys 16 (XW w + i) + r16, this lane's columns
+#pragma unroll
+    for (int i = 0; i < XW; ++i) dgp[i] = 0.f;
+
+    // ----- phase 1
+    {
+        __bf16 *bO = reinterpret_cast<__bf16 *>(smc + L::O1), *bVv = reinterpret_cast<__bf16 *>(smc + L::V1);
+        __bf16 *bDh = reinterpret_cast<__bf16 *>(smc + L::DH), *bDl = reinterpret_cast<__bf16 *>(smc + L::DL);
+        __bf16 *bEh = reinterpret_cast<__bf16 *>(smc + L::EH), *bEl = reinterpret_cast<__bf16 *>(smc + L::EL);
+        __bf16 *bTh = reinterpret_cast<__bf16 *>(smc + L::TH), *bTl = reinterpret_cast<__bf16 *>(smc + L::TL);
+        auto store_stage = [&]() {
+            const int o = tr * VS + c8;
+            *reinterpret_cast<uint4 *>(bO + o) = so;
+            *reinterpret_cast<uint4 *>(bVv + o) = sv;
+            bf16x8 h, l;
+            split8(sd0, sd1, h, l);
+            *reinterpret_cast<bf16x8 *>(bDh + o) = h;
+            *reinterpret_cast<bf16x8 *>(bDl + o) = l;
+            split8(se0, se1, h, l);
+            *reinterpret_cast<bf16x8 *>(bEh + o) = h;
+            *reinterpret_cast<bf16x8 *>(bEl + o) = l;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                bTh[(c8 + j) * LT + tr] = h[j];
+                bTl[(c8 + j) * LT + tr] = l[j];
+            }
+        };
+#pragma unroll 1
+        for (int st = 0; st < NSTEP; ++st) {
+            const int v0 = st * VS;
+            wait_vm<0>();    // this step's S and dS' (and everything older) have landed
+            lds_barrier();   // every wave's copies are in; the previous step's readers are done
+            store_stage();
+            if (st + 1 < NSTEP) {
+                load_sds(st + 1);
+                load_stage(v0 + VS);
+            }
+            lds_barrier();
+            const __bf16 *bS = reinterpret_cast<const __bf16 *>(smc + L::S0 + (st & 1) * L::SZ_KS);
+            const __bf16 *bdS = reinterpret_cast<const __bf16 *>(smc + L::DS0 + (st & 1) * L::SZ_KS);
+            const int ar = (16 * w + r16) * VS + 8 * gq;   // A rows: this wave's tokens
+            const bf16x8 aO = *reinterpret_cast<const bf16x8 *>(bO + ar);
+            const bf16x8 aDh = *reinterpret_cast<const bf16x8 *>(bDh + ar);
+            const bf16x8 aDl = *reinterpret_cast<const bf16x8 *>(bDl + ar);
+            const bf16x8 aEh = *reinterpret_cast<const bf16x8 *>(bEh + ar);
+            const bf16x8 aEl = *reinterpret_cast<const bf16x8 *>(bEl + ar);
+#pragma unroll
+            for (int xb = 0; xb < NXB; ++xb) {
+                const int br = (16 * xb + r16) * VS + 8 * gq;   // B rows: key 16 xb + r16
+                const bf16x8 bs = *reinterpret_cast<const bf16x8 *>(bS + br);
+                const bf16x8 bds = *reinterpret_cast<const bf16x8 *>(bdS + br);
+                aQ[xb] = mfma_bf16(aO, bs, aQ[xb]);
+                aKm[xb] = mfma_bf16(aDl, bds, mfma_bf16(aDh, bds, aKm[xb]));
+                aWn[xb] = mfma_bf16(aEl, bs, mfma_bf16(aEh, bs, aWn[xb]));
+                if (xb / XW == w) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) dgp[xb % XW] = fmaf((float)bs[j], (float)bds[j], dgp[xb % XW]);
+                }
+            }
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                const int sr = (16 * J + r16) * VS + 8 * gq;    // B rows: token 16 J + r16
+                const bf16x8 bvv = *reinterpret_cast<const bf16x8 *>(bVv + sr);
+                aT[J] = mfma_bf16(aEl, bvv, mfma_bf16(aEh, bvv, aT[J]));
+                if (J <= w) {   // P is lower: only its blocks J <= w carry gradient
+                    const bf16x8 bdh = *reinterpret_cast<const bf16x8 *>(bDh + sr);
+                    const bf16x8 bdl = *reinterpret_cast<const bf16x8 *>(bDl + sr);
+                    aP[J] = mfma_bf16(aO, bdl, mfma_bf16(aO, bdh, aP[J]));
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < VS / 16; ++j) {   // Y = T^T dDelta: rows 16 w .., columns v0 + 16 j ..
+                f32x4 y = z4;
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const __bf16 *ph = bTh + (16 * j + r16) * LT + 32 * p + 4 * gq;
+                    const __bf16 *pl = bTl + (16 * j + r16) * LT + 32 * p + 4 * gq;
+                    const bf16x8 bh = cat8(*reinterpret_cast<const bf16x4 *>(ph),
+                                           *reinterpret_cast<const bf16x4 *>(ph + 16));
+                    const bf16x8 bl = cat8(*reinterpret_cast<const bf16x4 *>(pl),
+                                           *reinterpret_cast<const bf16x4 *>(pl + 16));
+                    y = mfma_bf16(ttl[p], bh, mfma_bf16(tth[p], bl, mfma_bf16(tth[p], bh, y)));
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * w + 4 * gq + e;
+                    dbv[e] = fmaf((float)bVv[t * VS + 16 * j + r16], y[e], dbv[e]);
+                    if (t < n) dv[t * H * V + v0 + 16 * j + r16] = (__bf16)(sb[t] * y[e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < XW; ++i) {   // e^{gn} rowsum(S * dS'), one writer per key
+            float d = dgp[i];
+            d += __shfl_xor(d, 16);
+            d += __shfl_xor(d, 32);
+            const int x = 16 * (XW * w + i) + r16;
+            if (gq == 0) sdgn[x] = a.ws.egn[ci * K + x] * d;
+        }
+    }
+    lds_barrier();   // phase 1's LDS is free
+
+    // ----- phase 2
+    float *sPT = reinterpret_cast<float *>(smc + L::PT), *sGT = reinterpret_cast<float *>(smc + L::GT);
+    float *scr = reinterpret_cast<float *>(smc + L::SCR) + w * (16 * 17);
+    __bf16 *sWT = reinterpret_cast<__bf16 *>(smc + L::WT), *sTT = reinterpret_cast<__bf16 *>(smc + L::TT);
+    f32x4 aZ[NXB];
+    bf16x4 pAh[4], pAl[4], gAh[4], gAl[4];   // this wave's dP, dG rows in operand layout, split
+    {
+        // B operands of dT -= dWn (beta Kp)^T: the bf16 copy of Kp in fragment
+        // order, segment (row block J, key pair p) = lane's 8 keys of both blocks
+        const uint4 *kps = reinterpret_cast<const uint4 *>(a.ws.Kps) + ci * (C * K / 8) + lane;
+        uint4 kf[NXB / 2][4];
+#pragma unroll
+        for (int p = 0; p < NXB / 2; ++p)
+#pragma unroll
+            for (int J = 0; J < 4; ++J) kf[p][J] = kps[(J * (NXB / 2) + p) * 64];
+#pragma unroll
+        for (int xb = 0; xb < NXB; ++xb)   // dWn^T (all rows are needed by Z)
+            *reinterpret_cast<bf16x4 *>(sWT + (16 * xb + r16) * LT + 16 * w + 4 * gq) = cvt4(aWn[xb]);
+        // dT -= dWn (beta Kp)^T on this wave's rows: A = own dWn rows, two key
+        // blocks per k step
+        f32x4 u[4] = {z4, z4, z4, z4};
+#pragma unroll
+        for (int p = 0; p < NXB / 2; ++p) {
+            const f32x4 x0 = tile_transpose(scr, aWn[2 * p]), x1 = tile_transpose(scr, aWn[2 * p + 1]);
+            const bf16x8 A = cat8(cvt4(x0), cvt4(x1));
+#pragma unroll
+            for (int J = 0; J < 4; ++J) u[J] = mfma_bf16(A, __builtin_bit_cast(bf16x8, kf[p][J]), u[J]);
+        }
+        // the operands of dA, issued now: rows of T (bf16 copy, fragment order)
+        // and G at this lane's elements
+        const uint4 *tms = reinterpret_cast<const uint4 *>(a.ws.Tms) + ci * (C * C / 8) + lane;
+        uint4 tf[4][2];
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) tf[J][p] = tms[(J * 2 + p) * 64];
+        const float *Gm = a.ws.Gm + ci * (C * C);
+        float gmv[4][4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gmv[J][e] = Gm[(16 * w + 4 * gq + e) * C + 16 * J + r16];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            const float bs = sb[16 * J + r16];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) aT[J][e] = bs * (aT[J][e] - u[J][e]);
+        }
+        lds_barrier();   // dWn^T complete
+        // Z = -T^T dWn on this wave's rows
+#pragma unroll
+        for (int xb = 0; xb < NXB; ++xb) {
+            f32x4 z = z4;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const __bf16 *pw = sWT + (16 * xb + r16) * LT + 32 * p + 4 * gq;
+                z = mfma_bf16(tth[p], cat8(*reinterpret_cast<const bf16x4 *>(pw),
+                                           *reinterpret_cast<const bf16x4 *>(pw + 16)), z);
+            }
+            aZ[xb] = -z;
+        }
+#pragma unroll
+        for (int J = 0; J < 4; ++J)   // dT^T (all rows are needed by M1)
+            *reinterpret_cast<bf16x4 *>(sTT + (16 * J + r16) * LT + 16 * w + 4 * gq) = cvt4(aT[J]);
+        lds_barrier();
+        // M1 = T^T dT on this wave's rows
+        f32x4 m1[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            f32x4 m = z4;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const __bf16 *pt = sTT + (16 * J + r16) * LT + 32 * p + 4 * gq;
+                m = mfma_bf16(tth[p], cat8(*reinterpret_cast<const bf16x4 *>(pt),
+                                           *reinterpret_cast<const bf16x4 *>(pt + 16)), m);
+            }
+            m1[J] = m;
+        }
+        // dA = -M1 T^T (strictly lower): A = own M1 rows, B = rows of T; dG =
+        // beta dA; dbeta += rowsum(dA * G)
+        bf16x8 Am[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const f32x4 x0 = tile_transpose(scr, m1[2 * p]), x1 = tile_transpose(scr, m1[2 * p + 1]);
+            Am[p] = cat8(cvt4(x0), cvt4(x1));
+        }
+        float gs[4];   // scalar gate: gamma at this lane's rows
+        if (!CH) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gs[e] = gam[(16 * w + 4 * gq + e) * K];
+        }
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            f32x4 acc = z4;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) acc = mfma_bf16(Am[p], __builtin_bit_cast(bf16x8, tf[J][p]), acc);
+            const int s = 16 * J + r16;
+            const float gsc = CH ? 0.f : gam[s * K];
+            f32x4 g4, p4 = aP[J];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * w + 4 * gq + e;
+                const float da = s < t ? -acc[e] : 0.f;
+                dbv[e] = fmaf(da, gmv[J][e], dbv[e]);
+                // scalar gate: the pair decay folded into dP and dG
+                const float f = CH ? 1.f : (s <= t ? __expf(gs[e] - gsc) : 0.f);
+                g4[e] = sb[t] * da * f;
+                p4[e] = s <= t ? p4[e] * f : 0.f;
+            }
+            if (J <= w) {   // read by the waves of later rows (sums over t >= u)
+                *reinterpret_cast<f32x4 *>(sPT + s * LP + 16 * w + 4 * gq) = p4;
+                *reinterpret_cast<f32x4 *>(sGT + s * LP + 16 * w + 4 * gq) = g4;
+            }
+            split4(tile_transpose(scr, p4), pAh[J], pAl[J]);
+            split4(tile_transpose(scr, g4), gAh[J], gAl[J]);
+        }
+    }
+
+    // ----- phase 3
+    float *sKt = reinterpret_cast<float *>(smc + L::KT), *sKh = reinterpret_cast<float *>(smc + L::KH);
+    float *sQh = reinterpret_cast<float *>(smc + L::QH), *sG = reinterpret_cast<float *>(smc + L::GG);
+    float *sXT = reinterpret_cast<float *>(smc + L::XT), *sXP = reinterpret_cast<float *>(smc + L::XP);
+    float dgs[4] = {0.f, 0.f, 0.f, 0.f};   // scalar gate: dg at this lane's rows, this lane's channels
+#pragma unroll
+    for (int pp = 0; pp < K / 32; ++pp) {
+        lds_barrier();   // phase 2 / the previous pass is done with this space
+        {   // the pass's scaled k and q and gamma, rows = tokens: thread (token tr, channels c8 ..)
+            const int x = 32 * pp + c8;
+            bf16x8 kr8 = {}, qr8 = {};
+            if (live) {
+                kr8 = *reinterpret_cast<const bf16x8 *>(k + tr * H * K + x);
+                qr8 = *reinterpret_cast<const bf16x8 *>(q + tr * H * K + x);
+            }
+            const float *gr = gam + tr * K + x;
+            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gr), g1 = *reinterpret_cast<const f32x4 *>(gr + 4);
+            f32x4 kt[2], kh[2], qh[2];
+            if (CH) {
+                const float *gp = gam + (16 * (tr >> 4) + 8) * K + x;
+                const f32x4 p0 = *reinterpret_cast<const f32x4 *>(gp), p1 = *reinterpret_cast<const f32x4 *>(gp + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float gv = e < 4 ? g0[e] : g1[e - 4], gpv = e < 4 ? p0[e] : p1[e - 4];
+                    const float up = __expf(gpv - gv), dn = __expf(gv - gpv);
+                    const float kk = (float)kr8[e], qq = (float)qr8[e];
+                    kt[e >> 2][e & 3] = kk * up;
+                    kh[e >> 2][e & 3] = kk * dn;
+                    qh[e >> 2][e & 3] = qq * dn;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    kt[e >> 2][e & 3] = kh[e >> 2][e & 3] = (float)kr8[e];
+                    qh[e >> 2][e & 3] = (float)qr8[e];
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                *reinterpret_cast<f32x4 *>(sKt + tr * LW + c8 + 4 * h) = kt[h];
+                *reinterpret_cast<f32x4 *>(sKh + tr * LW + c8 + 4 * h) = kh[h];
+                *reinterpret_cast<f32x4 *>(sQh + tr * LW + c8 + 4 * h) = qh[h];
+            }
+            *reinterpret_cast<f32x4 *>(sG + tr * LW + c8) = g0;
+            *reinterpret_cast<f32x4 *>(sG + tr * LW + c8 + 4) = g1;
+        }
+        lds_barrier();
+        float loc[2][4];   // d gamma summed over the later rows of this lane's tile column
+#pragma unroll
+        for (int xi = 0; xi < 2; ++xi) {
+            const int xb = 2 * pp + xi, xl = 16 * xi + r16, x = 16 * xb + r16;
+            float gv[4], grho[4], fw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gv[e] = sG[(16 * w + 4 * gq + e) * LW + xl];
+            if (CH) {
+#pragma unroll
+                for (int J = 0; J < 4; ++J) grho[J] = sG[(16 * J + 8) * LW + xl];
+            }
+            f32x4 aq = z4, ak = z4, as = z4;
+            // rows r of this wave, s <= r:  sum_J e^{gamma_r - gamma_rho(J)} (dP_rJ, dG_rJ) Kt_J
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                if (J <= w) {
+                    f32x4 b;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) b[j] = sKt[(16 * J + 4 * gq + j) * LW + xl];
+                    bf16x4 bh, bl;
+                    split4(b, bh, bl);
+                    const f32x4 pq = mfma16x3(pAh[J], pAl[J], bh, bl, z4);
+                    const f32x4 pk = mfma16x3(gAh[J], gAl[J], bh, bl, z4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float f = CH ? __expf(gv[e] - grho[J]) : 1.f;
+                        aq[e] = fmaf(f, pq[e], aq[e]);
+                        ak[e] = fmaf(f, pk[e], ak[e]);
+                    }
+                }
+            }
+            // rows u of this wave, t >= u:  sum_I e^{gamma_rho(I) - gamma_u} (dG^T Kh_I + dP^T Qh_I)
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                if (I >= w) {
+                    const f32x4 ag = *reinterpret_cast<const f32x4 *>(sGT + (16 * w + r16) * LP + 16 * I + 4 * gq);
+                    const f32x4 ap = *reinterpret_cast<const f32x4 *>(sPT + (16 * w + r16) * LP + 16 * I + 4 * gq);
+                    f32x4 bk, bq;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        bk[j] = sKh[(16 * I + 4 * gq + j) * LW + xl];
+                        bq[j] = sQh[(16 * I + 4 * gq + j) * LW + xl];
+                    }
+                    bf16x4 agh, agl, aph, apl, bkh, bkl, bqh, bql;
+                    split4(ag, agh, agl);
+                    split4(ap, aph, apl);
+                    split4(bk, bkh, bkl);
+                    split4(bq, bqh, bql);
+                    const f32x4 ps = mfma16x3(aph, apl, bqh, bql, mfma16x3(agh, agl, bkh, bkl, z4));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float f = CH ? __expf(grho[I] - gv[e]) : 1.f;
+                        if (I == w) fw[e] = f;   // also turns Kh, Qh of this wave's rows back into k, q
+                        as[e] = fmaf(f, ps[e], as[e]);
+                    }
+                }
+            }
+            // per element: dq, dk, d gamma; the gn terms of this channel
+            const float gn = sG[(C - 1) * LW + xl];
+            float dgn = 0.f, dga[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 16 * w + 4 * gq + e;
+                const float kh = sKh[rr * LW + xl], qh = sQh[rr * LW + xl];
+                const float kr = CH ? kh * fw[e] : kh, qr = CH ? qh * fw[e] : qh;   // 0 past the end
+                const float eg = __expf(gv[e]), em = __expf(gn - gv[e]);
+                const float dqp = aQ[xb][e], dkm = aKm[xb][e], zr = aZ[xb][e], z = zr * sb[rr];
+                dga[e] = qr * aq[e] + kr * (ak[e] - as[e]) + (dqp * qr + z * kr) * eg - dkm * kr * em;
+                dgn = fmaf(dkm * kr, em, dgn);
+                dbv[e] = fmaf(kr * eg, zr, dbv[e]);   // rowsum(Kp * Z)
+                if (rr < n) {
+                    dq[rr * H * K + x] = (__bf16)fmaf(dqp, eg, aq[e]);
+                    dk[rr * H * K + x] = (__bf16)(ak[e] + as[e] + z * eg + dkm * em);
+                }
+            }
+            // reverse running sums down this tile column: the lane's own rows, then
+            // the lanes of later row groups (same column); tile totals and the gn
+            // terms go to LDS for the other waves
+            const float l3 = dga[3], l2 = l3 + dga[2], l1 = l2 + dga[1], l0 = l1 + dga[0];
+            const float n1 = __shfl(l0, (lane + 16) & 63), n2 = __shfl(l0, (lane + 32) & 63),
+                        n3 = __shfl(l0, (lane + 48) & 63);
+            const float after = (gq < 3 ? n1 : 0.f) + (gq < 2 ? n2 : 0.f) + (gq < 1 ? n3 : 0.f);
+            loc[xi][0] = l0 + after;
+            loc[xi][1] = l1 + after;
+            loc[xi][2] = l2 + after;
+            loc[xi][3] = l3 + after;
+            float tot = l0;
+            tot += __shfl_xor(tot, 16);
+            tot += __shfl_xor(tot, 32);
+            dgn += __shfl_xor(dgn, 16);
+            dgn += __shfl_xor(dgn, 32);
+            if (gq == 0) {
+                sXT[w * 64 + xl] = tot;
+                sXP[w * 64 + xl] = dgn;
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int xi = 0; xi < 2; ++xi) {   // dg = reverse running sum of d gamma plus the gn terms
+            const int xl = 16 * xi + r16, x = 32 * pp + xl;
+            float later = sdgn[x] + ((sXP[xl] + sXP[64 + xl]) + (sXP[128 + xl] + sXP[192 + xl]));
+#pragma unroll
+            for (int w2 = 1; w2 < 4; ++w2) later += w2 > w ? sXT[w2 * 64 + xl] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 16 * w + 4 * gq + e;
+                const float dgv = loc[xi][e] + later;
+                if (CH) {
+                    if (rr < n) a.dg[(r0 + rr * H) * K + x] = dgv;
+                } else {
+                    dgs[e] += dgv;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        dbv[e] = sum16(dbv[e]);
+        if (!CH) dgs[e] = sum16(dgs[e]);
+    }
+    if (r16 == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * w + 4 * gq + e;
+            if (t < n) {
+                a.dbeta[r0 + t * H] = dbv[e];
+                if (!CH) a.dg[r0 + t * H] = dgs[e];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- host side
 template <int K, int V> struct BwLds {
     static constexpr int C = BW_C, KP = K + 1, CP = C + 1, VB = BW_VB, VP = VB + 1;
@@ -1524,8 +2094,13 @@ static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
     else
         sweeps_kern = bwd_sweeps_kernel<DT, K, V>;
     if ((e = set_lds(sweeps_kern, lds_sweeps, s2)) != hipSuccess) return e;
-    if ((e = set_lds(bwd_vgrad_kernel<DT, K, V>, L::vgrad, s4)) != hipSuccess) return e;
-    if ((e = set_lds(bwd_kgrad2_kernel<DT, K, CH>, L::kgrad2, s6)) != hipSuccess) return e;
+    if constexpr (F32) {
+        if ((e = set_lds(bwd_vgrad_kernel<DT, K, V>, L::vgrad, s4)) != hipSuccess) return e;
+        if ((e = set_lds(bwd_kgrad2_kernel<DT, K, CH>, L::kgrad2, s6)) != hipSuccess) return e;
+    } else {
+        constexpr int lds_grad = GradLds<K, V>::bytes;
+        if ((e = set_lds(bwd_grad_kernel<K, V, CH>, lds_grad, s4)) != hipSuccess) return e;
+    }
     const unsigned nch = (unsigned)(nslices * a.NC), nvb = (unsigned)(nslices * (V / L::VB));
     if (nch > 0)
         hipLaunchKernelGGL((bwd_prep_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::prep, st, a);
@@ -1533,8 +2108,13 @@ static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
     // passes dL/dS_T to dS0
     hipLaunchKernelGGL(sweeps_kern, dim3(2 * nvb), dim3(BW_NTHR), lds_sweeps, st, a);
     if (nch > 0) {
-        hipLaunchKernelGGL((bwd_vgrad_kernel<DT, K, V>), dim3(nch), dim3(BW_NTHR), L::vgrad, st, a);
-        hipLaunchKernelGGL((bwd_kgrad2_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::kgrad2, st, a);
+        if constexpr (F32) {
+            hipLaunchKernelGGL((bwd_vgrad_kernel<DT, K, V>), dim3(nch), dim3(BW_NTHR), L::vgrad, st, a);
+            hipLaunchKernelGGL((bwd_kgrad2_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::kgrad2, st, a);
+        } else {
+            constexpr int lds_grad = GradLds<K, V>::bytes;
+            hipLaunchKernelGGL((bwd_grad_kernel<K, V, CH>), dim3(nch), dim3(BW_NTHR), lds_grad, st, a);
+        }
     }
     return hipGetLastError();
 }
