@@ -101,6 +101,15 @@ template <typename T, int R, int W> struct TileRegs {
                 r[i] = vec{};
         }
     }
+    // the vectors as loaded, in the storage type (row stride ls elements, 16-byte aligned rows)
+    __device__ __forceinline__ void store_raw(T *dst, int ls) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int v = threadIdx.x + i * BW_NTHR;
+            if (NV % BW_NTHR == 0 || v < NV)
+                *reinterpret_cast<vec *>(dst + (v / VPR) * ls + (v % VPR) * VE) = r[i];
+        }
+    }
     // LOWER: keep the entries with column <= row, zero the rest
     template <bool LOWER = false> __device__ __forceinline__ void store(float *dst, int ls) const {
 #pragma unroll
@@ -257,15 +266,37 @@ template <> struct Raw8<__bf16> {
     }
 };
 
+// Four consecutive LDS elements as fp32.
+__device__ __forceinline__ f32x4 ld4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 ld4f(const __bf16 *p)
+{
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+
+// LDS of prep: gamma [C][K + 4] fp32, then k and q [C][KQ] in the input dtype
+// (exact), whose space A and T ([C][C + 1] fp32 each) take over once the Gram
+// blocks are done, then beta and the scalar gate.  bf16 inputs fit two
+// workgroups per CU (69 KB at K = 128).
+template <typename DT, int K> struct PrepLds {
+    static constexpr int C = BW_C, KP = K + 4, KQ = std::is_same<DT, float>::value ? K + 4 : K + 8, CP = C + 1;
+    static constexpr int KQB = 2 * C * KQ * (int)sizeof(DT), ATB = 2 * C * CP * 4;
+    static constexpr int U = KQB > ATB ? KQB : ATB;
+    static constexpr int bytes = 4 * C * KP + U + 4 * 2 * C;
+};
+
 // ---------------------------------------------------------------- 1 prep
 template <typename DT, int K, bool CH>
 __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
 {
     using OT = DT;   // storage of the sweeps' operands
-    constexpr int C = BW_C, KP = K + 4, CP = C + 1;   // rows of k, q, gamma 16-byte aligned
+    using PL = PrepLds<DT, K>;
+    constexpr int C = BW_C, KP = PL::KP, KQ = PL::KQ, CP = PL::CP;   // rows 16-byte aligned
     extern __shared__ __attribute__((aligned(256))) float sm[];
-    float *sk = sm, *sq = sk + C * KP, *sg = sq + C * KP, *sA = sg + C * KP, *sT = sA + C * CP;
-    float *sb = sT + C * CP, *sgs = sb + C;
+    float *sg = sm;
+    DT *sk = reinterpret_cast<DT *>(sg + C * KP), *sq = sk + C * KQ;
+    float *sA = reinterpret_cast<float *>(sk), *sT = sA + C * CP;   // after the Gram blocks
+    float *sb = reinterpret_cast<float *>(reinterpret_cast<char *>(sk) + PL::U), *sgs = sb + C;
     const int tid = threadIdx.x;
     const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
     const int t0 = c * C, n = min(C, a.T - t0);
@@ -283,8 +314,8 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
             sgs[tid] = tid < n ? a.g[r0 + tid * H] : 0.f;
         }
         if (tid < C) sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
-        tk.store(sk, KP);
-        tq.store(sq, KP);
+        tk.store_raw(sk, KQ);
+        tq.store_raw(sq, KQ);
     }
     lds_barrier();
     if (tid < K) {   // gamma: running sum over the chunk, one channel per thread
@@ -304,7 +335,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
         }
         // by rows: element (t, x), four channels x .. x + 3
         auto kp_row = [&](int t, int x) {
-            const f32x4 k4 = *reinterpret_cast<const f32x4 *>(sk + t * KP + x);
+            const f32x4 k4 = ld4f(sk + t * KQ + x);
             const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sg + t * KP + x);
             f32x4 o;
 #pragma unroll
@@ -312,7 +343,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
             return o;
         };
         auto km_row = [&](int t, int x) {
-            const f32x4 k4 = *reinterpret_cast<const f32x4 *>(sk + t * KP + x);
+            const f32x4 k4 = ld4f(sk + t * KQ + x);
             const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sg + t * KP + x);
             const f32x4 n4 = *reinterpret_cast<const f32x4 *>(sg + (C - 1) * KP + x);
             f32x4 o;
@@ -324,24 +355,25 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
         auto kp_col = [&](int x, int t) {
             f32x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = sk[(t + e) * KP + x] * __expf(sg[(t + e) * KP + x]);
+            for (int e = 0; e < 4; ++e) o[e] = to_f32(sk[(t + e) * KQ + x]) * __expf(sg[(t + e) * KP + x]);
             return o;
         };
         auto qp_col = [&](int x, int t) {
             f32x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = sq[(t + e) * KP + x] * __expf(sg[(t + e) * KP + x]);
+            for (int e = 0; e < 4; ++e) o[e] = to_f32(sq[(t + e) * KQ + x]) * __expf(sg[(t + e) * KP + x]);
             return o;
         };
         auto km_col = [&](int x, int t) {
             const float gn = sg[(C - 1) * KP + x];
             f32x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = sk[(t + e) * KP + x] * __expf(gn - sg[(t + e) * KP + x]);
+            for (int e = 0; e < 4; ++e) o[e] = to_f32(sk[(t + e) * KQ + x]) * __expf(gn - sg[(t + e) * KP + x]);
             return o;
         };
-        write_frag<float, C, K>(a.ws.Kp + ci * (C * K), kp_row);   // fp32 for the gradient kernels
-        if constexpr (!std::is_same<OT, float>::value)
+        if constexpr (std::is_same<OT, float>::value)   // fp32 for the fp32 gradient kernels
+            write_frag<float, C, K>(a.ws.Kp + ci * (C * K), kp_row);
+        else
             write_frag<OT, C, K>(reinterpret_cast<OT *>(a.ws.Kps) + ci * (C * K), kp_row);
         write_frag<OT, C, K>(reinterpret_cast<OT *>(a.ws.Km) + ci * (C * K), km_row);
         write_frag<OT, K, C>(reinterpret_cast<OT *>(a.ws.KpT) + ci * (K * C), kp_col);
@@ -357,22 +389,29 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
     // k_s e^{gamma_rho - gamma_s}.  With g >= -5 per token no factor exceeds
     // e^{8 * 5}; for s in an earlier block the B factor is at most 1.  Scalar
     // gate: the plain products, scaled by e^{gamma_t - gamma_s} afterwards.
+    // A = diag(beta) G goes to LDS only after every wave is done with k and q
+    // (A and T take their space): each wave keeps its (at most three) blocks.
     float *Gm = a.ws.Gm + ci * (C * C);
     OT *PT = reinterpret_cast<OT *>(a.ws.PT) + ci * (C * C);
+    f32x4 akeep[3];
     {
         const int lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
-        for (int p = w; p < 10; p += 4) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int p = w + 4 * i;
+            if (p >= 10) break;
             const int I = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0, J = p - I * (I + 1) / 2;
-            const float *ka = sk + (16 * I + r16) * KP, *qa = sq + (16 * I + r16) * KP;
+            const DT *ka = sk + (16 * I + r16) * KQ, *qa = sq + (16 * I + r16) * KQ;
             const float *ga = sg + (16 * I + r16) * KP, *gr = sg + (16 * I + 8) * KP;
-            const float *kb = sk + (16 * J + r16) * KP, *gb = sg + (16 * J + r16) * KP;
+            const DT *kb = sk + (16 * J + r16) * KQ;
+            const float *gb = sg + (16 * J + r16) * KP;
             f32x4 gacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
             // four channels c .. c + 3 of the A rows (k and q) and the B row (k),
             // decay-scaled for the per-channel gate
             auto operands = [&](int c, f32x4 &kA, f32x4 &qA, f32x4 &kB) {
-                kA = *reinterpret_cast<const f32x4 *>(ka + c);
-                qA = *reinterpret_cast<const f32x4 *>(qa + c);
-                kB = *reinterpret_cast<const f32x4 *>(kb + c);
+                kA = ld4f(ka + c);
+                qA = ld4f(qa + c);
+                kB = ld4f(kb + c);
                 if (CH) {
                     const f32x4 gA = *reinterpret_cast<const f32x4 *>(ga + c);
                     const f32x4 gR = *reinterpret_cast<const f32x4 *>(gr + c);
@@ -427,7 +466,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
                 gv = s < t ? gv : 0.f;
                 p4[e] = s <= t ? pv : 0.f;
                 Gm[t * C + s] = gv;
-                sA[t * CP + s] = sb[t] * gv;
+                akeep[i][e] = sb[t] * gv;
             }
             st4(PT + frag_idx<OT, C>(16 * J + r16, 16 * I + 4 * gq), p4);
         }
@@ -437,7 +476,22 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
         if (s / 16 > t / 16) {
             Gm[idx] = 0.f;
             PT[frag_idx<OT, C>(s, t)] = OT(0.f);
-            sA[t * CP + s] = 0.f;
+        }
+    }
+    lds_barrier();   // k and q are no longer read
+    {
+        const int lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int p = w + 4 * i;
+            if (p >= 10) break;
+            const int I = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0, J = p - I * (I + 1) / 2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sA[(16 * I + 4 * gq + e) * CP + 16 * J + r16] = akeep[i][e];
+        }
+        for (int idx = tid; idx < C * C; idx += BW_NTHR) {
+            const int t = idx / C, s = idx % C;
+            if (s / 16 > t / 16) sA[t * CP + s] = 0.f;
         }
     }
     lds_barrier();
@@ -497,7 +551,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
     write_frag<float, C, C>(a.ws.TT + ci * (C * C), tt_val);
     if constexpr (!std::is_same<OT, float>::value)
         write_frag<OT, C, C>(reinterpret_cast<OT *>(a.ws.TTs) + ci * (C * C), tt_val);
-    store_frag<float, C, C>(a.ws.Tm + ci * (C * C), sT, CP);
+    if constexpr (std::is_same<OT, float>::value) store_frag<float, C, C>(a.ws.Tm + ci * (C * C), sT, CP);
     if constexpr (!std::is_same<OT, float>::value)
         store_frag<OT, C, C>(reinterpret_cast<OT *>(a.ws.Tms) + ci * (C * C), sT, CP);
 }
@@ -2058,7 +2112,7 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
 template <int K, int V> struct BwLds {
     static constexpr int C = BW_C, KP = K + 1, CP = C + 1, VB = BW_VB, VP = VB + 1;
     static constexpr int LK = K + 4, LC = C + 4, L2 = 2 * C + 4;
-    static constexpr int prep = 4 * (3 * C * (K + 4) + 2 * C * CP + 2 * C);
+    static constexpr int prep = PrepLds<float, K>::bytes;
     static constexpr int states = 4 * (VB * LK + 2 * VB * LC + C * VP + C);
     static constexpr int dstates = 4 * (VB * LK + VB * L2 + VB * LC + C);
     static constexpr int vgrad1 = 4 * (2 * K * 20 + 4 * C * 20 + C * LC + C);   // part 1
@@ -2086,7 +2140,8 @@ static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
     static bool s1 = false, s2 = false, s4 = false, s6 = false;
     constexpr int lds_sweeps = L::states > L::dstates ? L::states : L::dstates;
     hipError_t e;
-    if ((e = set_lds(bwd_prep_kernel<DT, K, CH>, L::prep, s1)) != hipSuccess) return e;
+    constexpr int lds_prep = PrepLds<DT, K>::bytes;
+    if ((e = set_lds(bwd_prep_kernel<DT, K, CH>, lds_prep, s1)) != hipSuccess) return e;
     constexpr bool F32 = std::is_same<DT, float>::value;
     void (*sweeps_kern)(BwArgs);
     if constexpr (F32)
@@ -2103,7 +2158,7 @@ static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
     }
     const unsigned nch = (unsigned)(nslices * a.NC), nvb = (unsigned)(nslices * (V / L::VB));
     if (nch > 0)
-        hipLaunchKernelGGL((bwd_prep_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::prep, st, a);
+        hipLaunchKernelGGL((bwd_prep_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), lds_prep, st, a);
     // with no chunks the forward sweep returns at once and the backward one
     // passes dL/dS_T to dS0
     hipLaunchKernelGGL(sweeps_kern, dim3(2 * nvb), dim3(BW_NTHR), lds_sweeps, st, a);
