@@ -638,11 +638,30 @@ template <int N> __device__ __forceinline__ void interleave_loads()
 template <int K, int V, typename ST>
 __device__ __forceinline__ void store_state_block(ST *dst, const float *St, int ls)
 {
-    constexpr int NG = BW_VB / 4;   // groups of four value columns
+    constexpr int W = 16 / (int)sizeof(ST), NG = BW_VB / W;   // one 16-byte piece: W value columns
     for (int v = threadIdx.x; v < K * NG; v += BW_NTHR) {
-        const int x = v / NG, y = (v % NG) * 4;
-        st4(dst + (long)x * V + y,
-            f32x4{St[y * ls + x], St[(y + 1) * ls + x], St[(y + 2) * ls + x], St[(y + 3) * ls + x]});
+        const int x = v / NG, y = (v % NG) * W;
+        const f32x4 a = {St[y * ls + x], St[(y + 1) * ls + x], St[(y + 2) * ls + x], St[(y + 3) * ls + x]};
+        if constexpr (W == 4) {
+            st4(dst + (long)x * V + y, a);
+        } else {
+            const f32x4 b = {St[(y + 4) * ls + x], St[(y + 5) * ls + x], St[(y + 6) * ls + x],
+                             St[(y + 7) * ls + x]};
+            *reinterpret_cast<bf16x8 *>(dst + (long)x * V + y) = cat8(cvt4(a), cvt4(b));
+        }
+    }
+}
+
+// Store a C x BW_VB fp32 block held transposed in LDS (Dt[y][t], row stride
+// ls) to global rows V floats apart (dst at column v0 of row 0), four value
+// columns (16 bytes) per piece; a wave's pieces are 64 consecutive rows of the
+// same columns, so its LDS reads are conflict-free.
+template <int V> __device__ __forceinline__ void store_rows_block(float *dst, const float *Dt, int ls)
+{
+    for (int v = threadIdx.x; v < BW_C * BW_VB / 4; v += BW_NTHR) {
+        const int t = v % BW_C, y = (v / BW_C) * 4;
+        *reinterpret_cast<f32x4 *>(dst + (long)t * V + y) =
+            f32x4{Dt[y * ls + t], Dt[(y + 1) * ls + t], Dt[(y + 2) * ls + t], Dt[(y + 3) * ls + t]};
     }
 }
 
@@ -745,11 +764,9 @@ __device__ __forceinline__ void states_sweep(const BwArgs &a, int blk)
         for (int j = 0; j < NT; ++j) {   // Delta = T R
             const f32x4 D = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.t, sRt + 16 * j * LC, LC);
             *reinterpret_cast<f32x4 *>(sDt + (16 * j + r) * LC + 16 * w + 4 * gq) = D;
-            float *Dl = a.ws.Dl + ci * (C * V) + v0 + 16 * j + r;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Dl[(16 * w + 4 * gq + e) * V] = D[e];
         }
         lds_barrier();
+        store_rows_block<V>(a.ws.Dl + ci * (C * V) + v0, sDt, LC);
         // S = Diag(e^{gn}) S + Km^T Delta
 #pragma unroll
         for (int h = 0; h < KT; ++h) {
@@ -862,12 +879,10 @@ __device__ __forceinline__ void dstates_sweep(const BwArgs &a, int blk)
             f32x4 dD = mma_rows<K / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.km, sdSt + 16 * j * LK, LK);
             dD = mma_rows<C / 16>(dD, f.pt, sOYt + 16 * j * L2, L2);
             *reinterpret_cast<f32x4 *>(sdDt + (16 * j + r) * LC + 16 * w + 4 * gq) = dD;
-            float *dDl = a.ws.dDl + ci * (C * V) + v0 + 16 * j + r;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dDl[(16 * w + 4 * gq + e) * V] = dD[e];
         }
         interleave_loads<KT + (K / 16 + 2 * C / 16 + KT * 2 * C / 16) / SP>();
         lds_barrier();
+        store_rows_block<V>(a.ws.dDl + ci * (C * V) + v0, sdDt, LC);
 #pragma unroll
         for (int j = 0; j < NT; ++j) {   // Y = T^T dDelta, kept as -beta Y
             f32x4 Y = mma_rows<C / 16>(f32x4{0.f, 0.f, 0.f, 0.f}, f.tt, sdDt + 16 * j * LC, LC);
