@@ -1831,7 +1831,6 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
     float *scr = reinterpret_cast<float *>(smc + L::SCR) + w * (16 * 17);
     __bf16 *sWT = reinterpret_cast<__bf16 *>(smc + L::WT), *sTT = reinterpret_cast<__bf16 *>(smc + L::TT);
     f32x4 aZ[NXB];
-    bf16x4 pAh[4], pAl[4], gAh[4], gAl[4];   // this wave's dP, dG rows in operand layout, split
     {
         // B operands of dT -= dWn (beta Kp)^T: the bf16 copy of Kp in fragment
         // order, segment (row block J, key pair p) = lane's 8 keys of both blocks
@@ -1935,12 +1934,10 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
                 g4[e] = sb[t] * da * f;
                 p4[e] = s <= t ? p4[e] * f : 0.f;
             }
-            if (J <= w) {   // read by the waves of later rows (sums over t >= u)
+            if (J <= w) {   // the tiles that carry gradient: this wave's rows, transposed
                 *reinterpret_cast<f32x4 *>(sPT + s * LP + 16 * w + 4 * gq) = p4;
                 *reinterpret_cast<f32x4 *>(sGT + s * LP + 16 * w + 4 * gq) = g4;
             }
-            split4(tile_transpose(scr, p4), pAh[J], pAl[J]);
-            split4(tile_transpose(scr, g4), gAh[J], gAl[J]);
         }
     }
 
@@ -2007,13 +2004,20 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
                 if (J <= w) {
-                    f32x4 b;
+                    // A: this wave's rows of dP and dG (its own transposed tiles), B: Kt
+                    f32x4 b, pa, ga;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) b[j] = sKt[(16 * J + 4 * gq + j) * LW + xl];
-                    bf16x4 bh, bl;
+                    for (int j = 0; j < 4; ++j) {
+                        b[j] = sKt[(16 * J + 4 * gq + j) * LW + xl];
+                        pa[j] = sPT[(16 * J + 4 * gq + j) * LP + 16 * w + r16];
+                        ga[j] = sGT[(16 * J + 4 * gq + j) * LP + 16 * w + r16];
+                    }
+                    bf16x4 bh, bl, pah, pal, gah, gal;
                     split4(b, bh, bl);
-                    const f32x4 pq = mfma16x3(pAh[J], pAl[J], bh, bl, z4);
-                    const f32x4 pk = mfma16x3(gAh[J], gAl[J], bh, bl, z4);
+                    split4(pa, pah, pal);
+                    split4(ga, gah, gal);
+                    const f32x4 pq = mfma16x3(pah, pal, bh, bl, z4);
+                    const f32x4 pk = mfma16x3(gah, gal, bh, bl, z4);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float f = CH ? __expf(gv[e] - grho[J]) : 1.f;
