@@ -74,6 +74,9 @@ MEASURED_TRAFFIC = {
                                     "mfma_frag.h"), "a40e09848624a8f0", 13604052000),
     "chunk_fwd_seg/channel_long/o": (("chunk_fwd_seg.hip", "chunk_fwd_wsc.hip", "ws_common.h",
                                       "gdn_common.h", "mfma_frag.h"), "6700ae7994480fee", 33518181008),
+    # the whole backward call (prep, sweeps, grad) at B4 H6 T4096, per-channel gate, bf16
+    "chunk_bwd/channel_bf16": (("chunk_bwd.hip", "chunk_bwd.h", "ws_common.h", "gdn_common.h",
+                                "mfma_frag.h"), "08727da811cf16c0", 1606155328),
 }
 
 # bf16 matrix-core work per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16, units of 512
@@ -391,21 +394,31 @@ def bench_bwd(torch, gdn, timer):
     bwd = lambda: gdn.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], gr["d_o"],
                                     gr["dS_T"], g["dq"], g["dk"], g["dv"], g["dg"], g["dbeta"],
                                     g["dS0"], ws)
-    fwd = lambda: gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o, S_T)
+    # the forward with its workspace: at this shape (24 slices of 64 chunks) the
+    # sequence-parallel form with o
+    nwf = gdn.gdn_chunk_fwd_workspace_size(B, T, H, K, V, torch.bfloat16, gdn.GDN_GATE_CHANNEL, True)
+    wsf = torch.empty(nwf, dtype=torch.uint8, device="cuda") if nwf else None
+    fwd = lambda: gdn.gdn_chunk_fwd_ws(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o, S_T,
+                                       wsf)
     tb = timer.run(bwd, steps=max(10, timer.steps), warmup=5)
+    tf = timer.run(fwd, steps=max(10, timer.steps), warmup=5)
     tfb = timer.run(lambda: (fwd(), bwd()), steps=max(10, timer.steps), warmup=5)
     nbytes = bwd_bytes(B, T, H, K, V, 2, True)
     s = tb["ms"] / 1e3
+    traffic = measured_traffic("chunk_bwd/channel_bf16")
     return {"workload": f"chunkwise backward, B={B} H={H} T={T} d_k=d_v={K} chunk=64, per-channel "
                         f"gate, bf16 q/k/v/do and dq/dk/dv, fp32 g/beta/states and their gradients, "
                         f"dL/do and dL/dS_T ~ N(0, 1)",
-            "ms": tb["ms"], "ms_median": tb["ms_median"], "ms_fwd_bwd": tfb["ms"],
+            "ms": tb["ms"], "ms_median": tb["ms_median"], "ms_fwd": tf["ms"], "ms_fwd_bwd": tfb["ms"],
             "mtok_s_fwd_bwd": B * T / (tfb["ms"] / 1e3) / 1e6,
             "gbs": nbytes / s / 1e9, "frac_hbm": nbytes / s / 1e9 / HBM_PEAK_GBS,
-            "bytes_per_call": nbytes, "workspace_bytes": nws, "steps": tb["steps"],
+            "bytes_per_call": nbytes, "traffic_bytes": traffic,
+            "traffic_x_algorithmic": None if traffic is None else traffic / nbytes,
+            "workspace_bytes": nws, "fwd_workspace_bytes": nwf, "steps": tb["steps"],
             "warmup_performed": tb["warmup_performed"],
-            "kernels": ["bwd_prep_kernel", "bwd_sweeps_kernel", "bwd_vgrad_kernel",
-                        "bwd_kgrad2_kernel"]}
+            "kernels": ["bwd_prep_kernel", "bwd_sweeps_kernel", "bwd_grad_kernel"],
+            "forward": "gdn_chunk_fwd_ws: chunk_fwd_seg_kernel, seg_combine_kernel, "
+                       "chunk_fwd_wsc_kernel<128, true> per segment"}
 
 
 def prologue_bytes(B, T, H, K, V, es, channel):

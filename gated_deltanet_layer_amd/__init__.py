@@ -224,8 +224,8 @@ def gdn_chunk_fwd_workspace_size(B: int, T: int, H: int, K: int, V: int, dtype, 
 def gdn_chunk_fwd_ws(q, k, v, g, beta, S0, o, S_T, workspace, chunk: int = 64,
                      stream=None) -> None:
     """gdn_chunk_fwd with a workspace (a uint8 device tensor, or None when
-    gdn_chunk_fwd_workspace_size is 0): a final-state-only call may then run
-    the sequence-parallel form."""
+    gdn_chunk_fwd_workspace_size is 0): a call may then run the
+    sequence-parallel form (with o as well, unless S_T is S0)."""
     B, T, H, K, V, gate = _chunk_fwd_args(q, k, v, g, beta, S0, o, S_T)
     if workspace is not None:
         _check(workspace, "workspace", device=q.device)

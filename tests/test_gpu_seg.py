@@ -188,6 +188,7 @@ def _check_o(cfg, d, label, oracle_heads=None):
     (1, 2, 2048, 0.02),      # two segments
     (1, 2, 4196, 0.0),       # four segments, the last one ragged, S0 absent
     (2, 3, 8192, 0.02),      # eight segments, six sequences
+    (4, 6, 4096, 0.02),      # the backward benchmark's forward: four segments, 24 sequences
 ])
 def test_segments_with_o_match(B, H, T, s0):
     cfg = _cfg(B, H, T, s0)
