@@ -652,7 +652,8 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SgCombArgs a)
 // Segments per (b, h) for the sequence-parallel form, or 1 when the call should
 // run the sequential kernel: long sequences with too few heads to fill the
 // chip.  Enough segments for about three workgroups per CU of a 256-CU part,
-// at least 16 chunks per segment, at most 64 segments (the combine walks them
+// at least 8 chunks per segment (shorter ones would spend more on the maps and
+// their combine than they save), at most 64 segments (the combine walks them
 // in order).
 int chunk_fwd_seg_count(long B, long T, long H)
 {
@@ -660,7 +661,7 @@ int chunk_fwd_seg_count(long B, long T, long H)
     const long bh = B * H;
     if (bh <= 0 || nch <= 0 || bh * 2 >= 256) return 1;
     long nseg = (768 + bh - 1) / bh;
-    nseg = nseg < nch / 16 ? nseg : nch / 16;
+    nseg = nseg < nch / 8 ? nseg : nch / 8;
     nseg = nseg < 64 ? nseg : 64;
     if (nseg < 2) return 1;
     // equal whole-chunk segments, none empty

@@ -80,9 +80,9 @@ def _cfg(B, H, T, s0=0.02, **kw):
 
 
 @pytest.mark.parametrize("B,H,T,s0", [
-    (1, 2, 2048, 0.02),      # two segments of 16 chunks
-    (1, 2, 4196, 0.0),       # four segments, the last one ragged (a partial last chunk), S0 absent
-    (2, 3, 8192, 0.02),      # eight segments, six sequences
+    (1, 2, 2048, 0.02),      # four segments of 8 chunks
+    (1, 2, 4196, 0.0),       # eight segments, the last one ragged (a partial last chunk), S0 absent
+    (2, 3, 8192, 0.02),      # sixteen segments, six sequences
     (1, 1, 4096 + 1, 0.1),   # one head, one token in the last chunk
 ])
 def test_segments_match_oracle(B, H, T, s0):
@@ -185,10 +185,10 @@ def _check_o(cfg, d, label, oracle_heads=None):
 
 
 @pytest.mark.parametrize("B,H,T,s0", [
-    (1, 2, 2048, 0.02),      # two segments
-    (1, 2, 4196, 0.0),       # four segments, the last one ragged, S0 absent
-    (2, 3, 8192, 0.02),      # eight segments, six sequences
-    (4, 6, 4096, 0.02),      # the backward benchmark's forward: four segments, 24 sequences
+    (1, 2, 2048, 0.02),      # four segments
+    (1, 2, 4196, 0.0),       # eight segments, the last one ragged, S0 absent
+    (2, 3, 8192, 0.02),      # sixteen segments, six sequences
+    (4, 6, 4096, 0.02),      # the backward benchmark's forward: eight segments, 24 sequences
 ])
 def test_segments_with_o_match(B, H, T, s0):
     cfg = _cfg(B, H, T, s0)
