@@ -71,9 +71,9 @@ MEASURED_TRAFFIC = {
                                                                   "prologue_ops.h", "gdn_common.h"),
                                                                  "672309d493c963a2", 1719409472),
     "chunk_fwd_seg/channel_long": (("chunk_fwd_seg.hip", "ws_common.h", "gdn_common.h",
-                                    "mfma_frag.h"), "a40e09848624a8f0", 13604052000),
+                                    "mfma_frag.h"), "64ac46ed9b65d47a", 13592231008),
     "chunk_fwd_seg/channel_long/o": (("chunk_fwd_seg.hip", "chunk_fwd_wsc.hip", "ws_common.h",
-                                      "gdn_common.h", "mfma_frag.h"), "6700ae7994480fee", 33518181008),
+                                      "gdn_common.h", "mfma_frag.h"), "bef54b1936a85dd7", 33505080592),
     # the whole backward call (prep, sweeps, grad) at B4 H6 T4096, per-channel gate, bf16
     "chunk_bwd/channel_bf16": (("chunk_bwd.hip", "chunk_bwd.h", "ws_common.h", "gdn_common.h",
                                 "mfma_frag.h"), "08727da811cf16c0", 1606155328),
