@@ -1561,27 +1561,34 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
 // ---------------------------------------------------------------- 3' grad (bf16 inputs)
 // The per-chunk gradients for bf16 inputs: what vgrad and kgrad2 compute for
 // fp32 inputs, in one workgroup per chunk, every intermediate (dQp, dKm, dWn,
-// dP, dT, Z, dA, dG, d gamma) kept on chip.  Wave w owns the 16 tokens
-// 16 w .. 16 w + 15: its rows of every C x K and C x C product stay in its
-// accumulators, and only the operands that other waves need pass through LDS.
+// dP, dT, Z, dA, dG, d gamma) kept on chip.  Eight waves: wave (rb, hf) owns
+// the 16 tokens 16 rb .. 16 rb + 15 together with its partner (rb, 1 - hf);
+// of the products on those rows it keeps in its accumulators the key blocks
+// 4 i + 2 hf, 4 i + 2 hf + 1 of the C x K ones and the token blocks 2 hf,
+// 2 hf + 1 of the C x C ones.  Only the operands that other waves need pass
+// through LDS.
 //
 //   phase 1, 32 value columns per step (bf16 16 x 16 x 32): dQp = dO S^T,
 //     dKm = Delta dS'^T, dWn = dDelta S^T, dP = dO Delta^T (its lower blocks),
-//     dT = dDelta V^T, Y = T^T dDelta (dv, dbeta), and e^{gn} rowsum(S * dS').
-//     S and dS' come straight from the workspace into a double-buffered LDS
-//     tile (global_load_lds); dO, v, Delta, dDelta through registers, Delta
-//     and dDelta split into bf16 high and low parts (split8), with a
-//     transposed copy of dDelta for Y.
+//     dT = dDelta V^T, Y = T^T dDelta (dv, dbeta; value tile hf of the step),
+//     and e^{gn} rowsum(S * dS').  S and dS' come straight from the workspace
+//     into a double-buffered LDS tile (global_load_lds); dO, v, Delta, dDelta
+//     through registers, Delta and dDelta split into bf16 high and low parts
+//     (split8), with a transposed copy of dDelta for Y.
 //   phase 2, the C x C chain on single-bf16 operands: dT -= dWn (beta Kp)^T,
 //     Z = -T^T dWn, M1 = T^T dT, dA = -M1 T^T (strictly lower), dG = beta dA,
-//     dbeta += rowsum(dA * G); dWn and dT pass transposed through LDS, own
-//     tiles are turned into operand layout through a per-wave 16 x 17
-//     scratch (tile_transpose).
-//   phase 3, 32 key channels per pass (bf16 16 x 16 x 16, both operands
-//     split): the token-pair sums of kgrad2 for this wave's rows, then dq,
-//     dk, d gamma per element; dg = reverse running sum of d gamma per
-//     channel.  dP and dG reach it as this wave's own rows (operand layout,
-//     pre-split) and transposed in LDS (for the sums over later rows).
+//     dbeta += rowsum(dA * G); dWn and dT pass transposed through LDS, and the
+//     rows of dWn and M1 that a product takes as its A operand pass in operand
+//     layout (turned through a per-wave 16 x 17 scratch, tile_transpose).
+//   phase 3, 64 key channels per pass (bf16 16 x 16 x 16, both operands
+//     split): the token-pair sums of kgrad2 for the wave's rows and key
+//     blocks, then dq, dk, d gamma per element; dg = reverse running sum of
+//     d gamma per channel, in registers down each tile column plus one
+//     exchange of per-row-block column totals.  dP and dG come transposed
+//     from LDS (written in phase 2), gamma and the scaled k and q from LDS
+//     tiles built once per pass.
+//   dbeta (and the scalar gate's dg) are summed over a row's columns per wave
+//   and then over the two waves of the row block.
 //
 // Precision: an fp64 model of this decomposition at the benchmark's
 // distributions put the C x C chain on single bf16 at 1e-4 relative error in
@@ -1589,10 +1596,13 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
 // (1.8e-3 in dv, dbeta) or scaled k and q in the pair sums (1.7e-2 in dg)
 // too coarse; those are split, which keeps them near fp32.
 //
-// LDS (bytes, K = V = 128): 72 KB at most, two workgroups per CU.
+// LDS (bytes, K = V = 128): 105 KB at most, one workgroup of eight waves per CU.
+constexpr int GR_NTHR = 512;
+
 template <int K, int V> struct GradLds {
-    static constexpr int C = BW_C, VS = 32, LT = C + 8, LP = C + 4, LW = 36;
-    static constexpr int HDR = 1024;                                    // beta [C], e^{gn} rowsum(S dS') [K]
+    static constexpr int C = BW_C, VS = 32, LT = C + 8, LP = C + 4, PC = 64, LW = PC + 4;
+    static constexpr int NXB = K / 16;
+    static constexpr int HDR = 2048;   // beta [C], e^{gn} rowsum(S dS') [K], pair sums [2][2][C]
     // phase 1
     static constexpr int SZ_KS = K * VS * 2, SZ_CS = C * VS * 2, SZ_T = VS * LT * 2;
     static constexpr int S0 = HDR, DS0 = S0 + 2 * SZ_KS;              // S, dS' [2][K][VS] bf16
@@ -1605,17 +1615,19 @@ template <int K, int V> struct GradLds {
     static constexpr int SZ_PT = C * LP * 4;
     static constexpr int PT = HDR, GT = PT + SZ_PT;                    // dP^T, dG^T [C][LP] fp32
     static constexpr int WT = GT + SZ_PT, TT = WT + K * LT * 2;        // dWn^T [K][LT], dT^T [C][LT] bf16
-    static constexpr int SCR = TT + C * LT * 2;                        // [4][16][17] fp32
-    static constexpr int END2 = SCR + 4 * 16 * 17 * 4;
+    static constexpr int SCR = TT + C * LT * 2;                        // [8][16][17] fp32
+    static constexpr int WA = SCR + 8 * 16 * 17 * 4;                   // dWn rows, operand layout [4][NXB][64] bf16x4
+    static constexpr int MA = WA + 4 * NXB * 64 * 8;                   // M1 rows, operand layout [4][4][64] bf16x4
+    static constexpr int END2 = MA + 4 * 4 * 64 * 8;
     // phase 3
     static constexpr int SZ_KT = C * LW * 4;
     static constexpr int KT = GT + SZ_PT, KH = KT + SZ_KT, QH = KH + SZ_KT;   // [C][LW] fp32
     static constexpr int GG = QH + SZ_KT;                              // gamma of the pass [C][LW]
-    static constexpr int XT = GG + SZ_KT, XP = XT + 4 * 64 * 4;        // per-wave column sums [4][64]
-    static constexpr int END3 = XP + 4 * 64 * 4;
+    static constexpr int XT = GG + SZ_KT, XP = XT + 4 * PC * 4;        // per-row-block column sums [4][PC]
+    static constexpr int END3 = XP + 4 * PC * 4;
     static constexpr int bytes = END1 > END2 ? (END1 > END3 ? END1 : END3) : (END2 > END3 ? END2 : END3);
-    static_assert(bytes <= 80 * 1024, "two workgroups per CU");
-    static_assert(HDR >= 4 * (C + K), "header");
+    static_assert(bytes <= 160 * 1024, "LDS budget");
+    static_assert(HDR >= 4 * (C + K + 4 * C), "header");
 };
 
 // 16 x 16 x 16 bf16 product, lane 16 g + r holding row r (A) / column r (B),
@@ -1655,14 +1667,17 @@ __device__ __forceinline__ f32x4 tile_transpose(float *scr, f32x4 x)
 }
 
 template <int K, int V, bool CH>
-__global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) void bwd_grad_kernel(BwArgs a)
+__global__ __launch_bounds__(GR_NTHR) void bwd_grad_kernel(BwArgs a)
 {
     using L = GradLds<K, V>;
-    constexpr int C = BW_C, NXB = K / 16, VS = L::VS, NSTEP = V / VS, LT = L::LT, LP = L::LP, LW = L::LW;
-    constexpr int XW = NXB / 4;   // key blocks of e^{gn} rowsum(S dS') per wave
+    constexpr int C = BW_C, NXB = K / 16, NXH = NXB / 2, VS = L::VS, NSTEP = V / VS, LT = L::LT, LP = L::LP;
+    constexpr int PC = L::PC, LW = L::LW;
     extern __shared__ __attribute__((aligned(256))) float sm[];
     char *smc = reinterpret_cast<char *>(sm);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, r16 = lane & 15;
+    const int rb = w & 3, hf = w >> 2;   // row block, half of the pair
+    // this wave's key blocks: 4 (i / 2) + 2 hf + (i % 2), i < NXH
+    auto xb_of = [&](int i) { return 4 * (i >> 1) + 2 * hf + (i & 1); };
     const int c = blockIdx.x % a.NC, sl = blockIdx.x / a.NC;
     const int t0 = c * C, n = min(C, a.T - t0);
     const long ci = (long)sl * a.NC + c;
@@ -1674,43 +1689,42 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
     const __bf16 *dhS = reinterpret_cast<const __bf16 *>(a.ws.dhS) + ci * (K * V);
     const float *Dl = a.ws.Dl + ci * (C * V), *dDl = a.ws.dDl + ci * (C * V);
     const float *gam = a.ws.gam + ci * (C * K);
-    float *sb = sm, *sdgn = sm + C;
+    float *sb = sm, *sdgn = sm + C, *spair = sdgn + K;   // spair [2 quantities][2 halves][C]
     // phase 1's first loads go out before anything waits
     // S and dS' of step st into buffer st & 1: 16-byte pieces, piece i =
-    // (row i / 4, columns 8 (i % 4) ..), wave w moving pieces 64 w + 256 j ..
+    // (row i / 4, columns 8 (i % 4) ..), wave w moving pieces 64 w + 512 j ..
     auto load_sds = [&](int st) {
         char *dS = smc + L::S0 + (st & 1) * L::SZ_KS, *dD = smc + L::DS0 + (st & 1) * L::SZ_KS;
 #pragma unroll
-        for (int i0 = 64 * w; i0 < 4 * K; i0 += BW_NTHR) {   // 4 K pieces: a multiple of 256
+        for (int i0 = 64 * w; i0 < 4 * K; i0 += GR_NTHR) {
             const int i = i0 + lane, row = i >> 2, col = st * VS + 8 * (i & 3);
             g2lds16(hS + row * V + col, dS + i0 * 16);
             g2lds16(dhS + row * V + col, dD + i0 * 16);
         }
     };
-    // dO, v, Delta, dDelta of a step through registers: row tr, columns c8 .. c8 + 7
-    const int tr = tid >> 2, c8 = 8 * (tid & 3);
+    // dO and Delta (first half of the workgroup) or v and dDelta (second) of a
+    // step through registers: row tr, columns c8 .. c8 + 7
+    const int tr = (tid & 255) >> 2, c8 = 8 * (tid & 3);
     const bool live = tr < n;
-    uint4 so, sv;
-    f32x4 sd0, sd1, se0, se1;
+    uint4 sv;      // dO or v
+    f32x4 s0, s1;  // Delta or dDelta
     auto load_stage = [&](int v0) {
         const uint4 zu = {0u, 0u, 0u, 0u};
-        so = live ? *reinterpret_cast<const uint4 *>(dO + tr * H * V + v0 + c8) : zu;
-        sv = live ? *reinterpret_cast<const uint4 *>(v + tr * H * V + v0 + c8) : zu;
-        const float *dl = Dl + tr * V + v0 + c8, *dd = dDl + tr * V + v0 + c8;
-        sd0 = *reinterpret_cast<const f32x4 *>(dl);
-        sd1 = *reinterpret_cast<const f32x4 *>(dl + 4);
-        se0 = *reinterpret_cast<const f32x4 *>(dd);
-        se1 = *reinterpret_cast<const f32x4 *>(dd + 4);
+        const __bf16 *src = hf == 0 ? dO : v;
+        const float *fs = (hf == 0 ? Dl : dDl) + tr * V + v0 + c8;
+        sv = live ? *reinterpret_cast<const uint4 *>(src + tr * H * V + v0 + c8) : zu;
+        s0 = *reinterpret_cast<const f32x4 *>(fs);
+        s1 = *reinterpret_cast<const f32x4 *>(fs + 4);
     };
     load_sds(0);
     load_stage(0);
     if (tid < C) sb[tid] = tid < n ? a.beta[r0 + tid * H] : 0.f;
 
-    // T^T rows 16 w + r16 (this wave's A operands of Y, Z and M1), k steps p of
-    // 32 tokens in the paired-block order of the fragment layout, high / low
+    // T^T rows 16 rb + r16 (A operands of Y, Z and M1), k steps p of 32
+    // tokens in the paired-block order of the fragment layout, high / low
     bf16x8 tth[2], ttl[2];
     {
-        const float *tt = a.ws.TT + ci * (C * C) + (4 * w) * 256 + lane * 4;
+        const float *tt = a.ws.TT + ci * (C * C) + (4 * rb) * 256 + lane * 4;
         f32x4 f[4];
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) f[cb] = *reinterpret_cast<const f32x4 *>(tt + cb * 256);
@@ -1718,15 +1732,13 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int p = 0; p < 2; ++p) split8(f[2 * p], f[2 * p + 1], tth[p], ttl[p]);
     }
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 aQ[NXB], aKm[NXB], aWn[NXB], aP[4], aT[4];   // tiles (w, key block) and (w, token block)
+    f32x4 aQ[NXH], aKm[NXH], aWn[NXH], aP[2], aT[2];   // tiles (rb, xb_of(i)) and (rb, 2 hf + jj)
 #pragma unroll
-    for (int i = 0; i < NXB; ++i) aQ[i] = aKm[i] = aWn[i] = z4;
+    for (int i = 0; i < NXH; ++i) aQ[i] = aKm[i] = aWn[i] = z4;
 #pragma unroll
-    for (int J = 0; J < 4; ++J) aP[J] = aT[J] = z4;
-    float dbv[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta at rows 16 w + 4 gq + e, this lane's columns
-    float dgp[XW];                          // rowsum(S * dS') at keys 16 (XW w + i) + r16, this lane's columns
-#pragma unroll
-    for (int i = 0; i < XW; ++i) dgp[i] = 0.f;
+    for (int jj = 0; jj < 2; ++jj) aP[jj] = aT[jj] = z4;
+    float dbv[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta at rows 16 rb + 4 gq + e, this lane's columns
+    float dgp = 0.f;                        // rowsum(S * dS') at key block xb_of(rb) (rb < NXH)
 
     // ----- phase 1
     {
@@ -1736,19 +1748,21 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
         __bf16 *bTh = reinterpret_cast<__bf16 *>(smc + L::TH), *bTl = reinterpret_cast<__bf16 *>(smc + L::TL);
         auto store_stage = [&]() {
             const int o = tr * VS + c8;
-            *reinterpret_cast<uint4 *>(bO + o) = so;
-            *reinterpret_cast<uint4 *>(bVv + o) = sv;
             bf16x8 h, l;
-            split8(sd0, sd1, h, l);
-            *reinterpret_cast<bf16x8 *>(bDh + o) = h;
-            *reinterpret_cast<bf16x8 *>(bDl + o) = l;
-            split8(se0, se1, h, l);
-            *reinterpret_cast<bf16x8 *>(bEh + o) = h;
-            *reinterpret_cast<bf16x8 *>(bEl + o) = l;
+            split8(s0, s1, h, l);
+            if (hf == 0) {
+                *reinterpret_cast<uint4 *>(bO + o) = sv;
+                *reinterpret_cast<bf16x8 *>(bDh + o) = h;
+                *reinterpret_cast<bf16x8 *>(bDl + o) = l;
+            } else {
+                *reinterpret_cast<uint4 *>(bVv + o) = sv;
+                *reinterpret_cast<bf16x8 *>(bEh + o) = h;
+                *reinterpret_cast<bf16x8 *>(bEl + o) = l;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                bTh[(c8 + j) * LT + tr] = h[j];
-                bTl[(c8 + j) * LT + tr] = l[j];
+                for (int j = 0; j < 8; ++j) {
+                    bTh[(c8 + j) * LT + tr] = h[j];
+                    bTl[(c8 + j) * LT + tr] = l[j];
+                }
             }
         };
 #pragma unroll 1
@@ -1764,43 +1778,42 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
             lds_barrier();
             const __bf16 *bS = reinterpret_cast<const __bf16 *>(smc + L::S0 + (st & 1) * L::SZ_KS);
             const __bf16 *bdS = reinterpret_cast<const __bf16 *>(smc + L::DS0 + (st & 1) * L::SZ_KS);
-            const int ar = (16 * w + r16) * VS + 8 * gq;   // A rows: this wave's tokens
+            const int ar = (16 * rb + r16) * VS + 8 * gq;   // A rows: this row block's tokens
             const bf16x8 aO = *reinterpret_cast<const bf16x8 *>(bO + ar);
             const bf16x8 aDh = *reinterpret_cast<const bf16x8 *>(bDh + ar);
             const bf16x8 aDl = *reinterpret_cast<const bf16x8 *>(bDl + ar);
             const bf16x8 aEh = *reinterpret_cast<const bf16x8 *>(bEh + ar);
             const bf16x8 aEl = *reinterpret_cast<const bf16x8 *>(bEl + ar);
 #pragma unroll
-            for (int xb = 0; xb < NXB; ++xb) {
-                const int br = (16 * xb + r16) * VS + 8 * gq;   // B rows: key 16 xb + r16
+            for (int i = 0; i < NXH; ++i) {
+                const int br = (16 * xb_of(i) + r16) * VS + 8 * gq;   // B rows: key 16 xb + r16
                 const bf16x8 bs = *reinterpret_cast<const bf16x8 *>(bS + br);
                 const bf16x8 bds = *reinterpret_cast<const bf16x8 *>(bdS + br);
-                aQ[xb] = mfma_bf16(aO, bs, aQ[xb]);
-                aKm[xb] = mfma_bf16(aDl, bds, mfma_bf16(aDh, bds, aKm[xb]));
-                aWn[xb] = mfma_bf16(aEl, bs, mfma_bf16(aEh, bs, aWn[xb]));
-                if (xb / XW == w) {
+                aQ[i] = mfma_bf16(aO, bs, aQ[i]);
+                aKm[i] = mfma_bf16(aDl, bds, mfma_bf16(aDh, bds, aKm[i]));
+                aWn[i] = mfma_bf16(aEl, bs, mfma_bf16(aEh, bs, aWn[i]));
+                if (i == rb) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) dgp[xb % XW] = fmaf((float)bs[j], (float)bds[j], dgp[xb % XW]);
+                    for (int j = 0; j < 8; ++j) dgp = fmaf((float)bs[j], (float)bds[j], dgp);
                 }
             }
 #pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                const int sr = (16 * J + r16) * VS + 8 * gq;    // B rows: token 16 J + r16
+            for (int jj = 0; jj < 2; ++jj) {
+                const int J = 2 * hf + jj, sr = (16 * J + r16) * VS + 8 * gq;   // B rows: token 16 J + r16
                 const bf16x8 bvv = *reinterpret_cast<const bf16x8 *>(bVv + sr);
-                aT[J] = mfma_bf16(aEl, bvv, mfma_bf16(aEh, bvv, aT[J]));
-                if (J <= w) {   // P is lower: only its blocks J <= w carry gradient
+                aT[jj] = mfma_bf16(aEl, bvv, mfma_bf16(aEh, bvv, aT[jj]));
+                if (J <= rb) {   // P is lower: only its blocks J <= rb carry gradient
                     const bf16x8 bdh = *reinterpret_cast<const bf16x8 *>(bDh + sr);
                     const bf16x8 bdl = *reinterpret_cast<const bf16x8 *>(bDl + sr);
-                    aP[J] = mfma_bf16(aO, bdl, mfma_bf16(aO, bdh, aP[J]));
+                    aP[jj] = mfma_bf16(aO, bdl, mfma_bf16(aO, bdh, aP[jj]));
                 }
             }
-#pragma unroll
-            for (int j = 0; j < VS / 16; ++j) {   // Y = T^T dDelta: rows 16 w .., columns v0 + 16 j ..
+            {   // Y = T^T dDelta: rows 16 rb .., value columns v0 + 16 hf ..
                 f32x4 y = z4;
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
-                    const __bf16 *ph = bTh + (16 * j + r16) * LT + 32 * p + 4 * gq;
-                    const __bf16 *pl = bTl + (16 * j + r16) * LT + 32 * p + 4 * gq;
+                    const __bf16 *ph = bTh + (16 * hf + r16) * LT + 32 * p + 4 * gq;
+                    const __bf16 *pl = bTl + (16 * hf + r16) * LT + 32 * p + 4 * gq;
                     const bf16x8 bh = cat8(*reinterpret_cast<const bf16x4 *>(ph),
                                            *reinterpret_cast<const bf16x4 *>(ph + 16));
                     const bf16x8 bl = cat8(*reinterpret_cast<const bf16x4 *>(pl),
@@ -1809,18 +1822,17 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * w + 4 * gq + e;
-                    dbv[e] = fmaf((float)bVv[t * VS + 16 * j + r16], y[e], dbv[e]);
-                    if (t < n) dv[t * H * V + v0 + 16 * j + r16] = (__bf16)(sb[t] * y[e]);
+                    const int t = 16 * rb + 4 * gq + e;
+                    dbv[e] = fmaf((float)bVv[t * VS + 16 * hf + r16], y[e], dbv[e]);
+                    if (t < n) dv[t * H * V + v0 + 16 * hf + r16] = (__bf16)(sb[t] * y[e]);
                 }
             }
         }
-#pragma unroll
-        for (int i = 0; i < XW; ++i) {   // e^{gn} rowsum(S * dS'), one writer per key
-            float d = dgp[i];
+        if (rb < NXH) {   // e^{gn} rowsum(S * dS'), one wave per key block
+            float d = dgp;
             d += __shfl_xor(d, 16);
             d += __shfl_xor(d, 32);
-            const int x = 16 * (XW * w + i) + r16;
+            const int x = 16 * xb_of(rb) + r16;
             if (gq == 0) sdgn[x] = a.ws.egn[ci * K + x] * d;
         }
     }
@@ -1830,53 +1842,44 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
     float *sPT = reinterpret_cast<float *>(smc + L::PT), *sGT = reinterpret_cast<float *>(smc + L::GT);
     float *scr = reinterpret_cast<float *>(smc + L::SCR) + w * (16 * 17);
     __bf16 *sWT = reinterpret_cast<__bf16 *>(smc + L::WT), *sTT = reinterpret_cast<__bf16 *>(smc + L::TT);
-    f32x4 aZ[NXB];
+    bf16x4 *sWA = reinterpret_cast<bf16x4 *>(smc + L::WA), *sMA = reinterpret_cast<bf16x4 *>(smc + L::MA);
+    f32x4 aZ[NXH];
     {
         // B operands of dT -= dWn (beta Kp)^T: the bf16 copy of Kp in fragment
-        // order, segment (row block J, key pair p) = lane's 8 keys of both blocks
+        // order, segment (row block J, key pair p) = the lane's 8 keys of both blocks
         const uint4 *kps = reinterpret_cast<const uint4 *>(a.ws.Kps) + ci * (C * K / 8) + lane;
-        uint4 kf[NXB / 2][4];
+        uint4 kf[NXB / 2][2];
 #pragma unroll
         for (int p = 0; p < NXB / 2; ++p)
 #pragma unroll
-            for (int J = 0; J < 4; ++J) kf[p][J] = kps[(J * (NXB / 2) + p) * 64];
+            for (int jj = 0; jj < 2; ++jj) kf[p][jj] = kps[((2 * hf + jj) * (NXB / 2) + p) * 64];
+        // dWn^T (all rows: the B operand of Z) and this row block's dWn rows in
+        // operand layout (the A operand of the dT update, both waves' blocks)
 #pragma unroll
-        for (int xb = 0; xb < NXB; ++xb)   // dWn^T (all rows are needed by Z)
-            *reinterpret_cast<bf16x4 *>(sWT + (16 * xb + r16) * LT + 16 * w + 4 * gq) = cvt4(aWn[xb]);
-        // dT -= dWn (beta Kp)^T on this wave's rows: A = own dWn rows, two key
-        // blocks per k step
-        f32x4 u[4] = {z4, z4, z4, z4};
+        for (int i = 0; i < NXH; ++i) {
+            const int xb = xb_of(i);
+            *reinterpret_cast<bf16x4 *>(sWT + (16 * xb + r16) * LT + 16 * rb + 4 * gq) = cvt4(aWn[i]);
+            sWA[(rb * NXB + xb) * 64 + lane] = cvt4(tile_transpose(scr, aWn[i]));
+        }
+        lds_barrier();
+        // dT -= dWn (beta Kp)^T on this wave's tiles (rb, 2 hf + jj), over all keys
+        f32x4 u[2] = {z4, z4};
 #pragma unroll
         for (int p = 0; p < NXB / 2; ++p) {
-            const f32x4 x0 = tile_transpose(scr, aWn[2 * p]), x1 = tile_transpose(scr, aWn[2 * p + 1]);
-            const bf16x8 A = cat8(cvt4(x0), cvt4(x1));
+            const bf16x8 A = cat8(sWA[(rb * NXB + 2 * p) * 64 + lane], sWA[(rb * NXB + 2 * p + 1) * 64 + lane]);
 #pragma unroll
-            for (int J = 0; J < 4; ++J) u[J] = mfma_bf16(A, __builtin_bit_cast(bf16x8, kf[p][J]), u[J]);
+            for (int jj = 0; jj < 2; ++jj) u[jj] = mfma_bf16(A, __builtin_bit_cast(bf16x8, kf[p][jj]), u[jj]);
         }
-        // the operands of dA, issued now: rows of T (bf16 copy, fragment order)
-        // and G at this lane's elements
-        const uint4 *tms = reinterpret_cast<const uint4 *>(a.ws.Tms) + ci * (C * C / 8) + lane;
-        uint4 tf[4][2];
 #pragma unroll
-        for (int J = 0; J < 4; ++J)
+        for (int jj = 0; jj < 2; ++jj) {
+            const float bs = sb[16 * (2 * hf + jj) + r16];
 #pragma unroll
-            for (int p = 0; p < 2; ++p) tf[J][p] = tms[(J * 2 + p) * 64];
-        const float *Gm = a.ws.Gm + ci * (C * C);
-        float gmv[4][4];
-#pragma unroll
-        for (int J = 0; J < 4; ++J)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) gmv[J][e] = Gm[(16 * w + 4 * gq + e) * C + 16 * J + r16];
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            const float bs = sb[16 * J + r16];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) aT[J][e] = bs * (aT[J][e] - u[J][e]);
+            for (int e = 0; e < 4; ++e) aT[jj][e] = bs * (aT[jj][e] - u[jj][e]);
         }
-        lds_barrier();   // dWn^T complete
-        // Z = -T^T dWn on this wave's rows
+        // Z = -T^T dWn on this wave's tiles
 #pragma unroll
-        for (int xb = 0; xb < NXB; ++xb) {
+        for (int i = 0; i < NXH; ++i) {
+            const int xb = xb_of(i);
             f32x4 z = z4;
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
@@ -1884,16 +1887,23 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
                 z = mfma_bf16(tth[p], cat8(*reinterpret_cast<const bf16x4 *>(pw),
                                            *reinterpret_cast<const bf16x4 *>(pw + 16)), z);
             }
-            aZ[xb] = -z;
+            aZ[i] = -z;
         }
+        // dA's B operands, issued now: T (bf16 copy, fragment order), segment (J, p)
+        const uint4 *tms = reinterpret_cast<const uint4 *>(a.ws.Tms) + ci * (C * C / 8) + lane;
+        uint4 tf[2][2];
 #pragma unroll
-        for (int J = 0; J < 4; ++J)   // dT^T (all rows are needed by M1)
-            *reinterpret_cast<bf16x4 *>(sTT + (16 * J + r16) * LT + 16 * w + 4 * gq) = cvt4(aT[J]);
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) tf[jj][p] = tms[((2 * hf + jj) * 2 + p) * 64];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)   // dT^T (all rows: the B operand of M1)
+            *reinterpret_cast<bf16x4 *>(sTT + (16 * (2 * hf + jj) + r16) * LT + 16 * rb + 4 * gq) = cvt4(aT[jj]);
         lds_barrier();
-        // M1 = T^T dT on this wave's rows
-        f32x4 m1[4];
+        // M1 = T^T dT on this wave's tiles, then in operand layout for the pair
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
+        for (int jj = 0; jj < 2; ++jj) {
+            const int J = 2 * hf + jj;
             f32x4 m = z4;
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
@@ -1901,42 +1911,46 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
                 m = mfma_bf16(tth[p], cat8(*reinterpret_cast<const bf16x4 *>(pt),
                                            *reinterpret_cast<const bf16x4 *>(pt + 16)), m);
             }
-            m1[J] = m;
+            sMA[(rb * 4 + J) * 64 + lane] = cvt4(tile_transpose(scr, m));
         }
-        // dA = -M1 T^T (strictly lower): A = own M1 rows, B = rows of T; dG =
-        // beta dA; dbeta += rowsum(dA * G)
-        bf16x8 Am[2];
+        const float *Gm = a.ws.Gm + ci * (C * C);   // G at this lane's elements, for dbeta
+        float gmv[2][4];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const f32x4 x0 = tile_transpose(scr, m1[2 * p]), x1 = tile_transpose(scr, m1[2 * p + 1]);
-            Am[p] = cat8(cvt4(x0), cvt4(x1));
-        }
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gmv[jj][e] = Gm[(16 * rb + 4 * gq + e) * C + 16 * (2 * hf + jj) + r16];
         float gs[4];   // scalar gate: gamma at this lane's rows
         if (!CH) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gs[e] = gam[(16 * w + 4 * gq + e) * K];
+            for (int e = 0; e < 4; ++e) gs[e] = gam[(16 * rb + 4 * gq + e) * K];
         }
+        lds_barrier();
+        // dA = -M1 T^T (strictly lower) on this wave's tiles: A = the row block's
+        // M1 rows, B = rows of T; dG = beta dA; dbeta += rowsum(dA * G)
+        bf16x8 Am[2];
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
+        for (int p = 0; p < 2; ++p) Am[p] = cat8(sMA[(rb * 4 + 2 * p) * 64 + lane], sMA[(rb * 4 + 2 * p + 1) * 64 + lane]);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int J = 2 * hf + jj, s = 16 * J + r16;
             f32x4 acc = z4;
 #pragma unroll
-            for (int p = 0; p < 2; ++p) acc = mfma_bf16(Am[p], __builtin_bit_cast(bf16x8, tf[J][p]), acc);
-            const int s = 16 * J + r16;
+            for (int p = 0; p < 2; ++p) acc = mfma_bf16(Am[p], __builtin_bit_cast(bf16x8, tf[jj][p]), acc);
             const float gsc = CH ? 0.f : gam[s * K];
-            f32x4 g4, p4 = aP[J];
+            f32x4 g4, p4 = aP[jj];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t = 16 * w + 4 * gq + e;
+                const int t = 16 * rb + 4 * gq + e;
                 const float da = s < t ? -acc[e] : 0.f;
-                dbv[e] = fmaf(da, gmv[J][e], dbv[e]);
+                dbv[e] = fmaf(da, gmv[jj][e], dbv[e]);
                 // scalar gate: the pair decay folded into dP and dG
                 const float f = CH ? 1.f : (s <= t ? __expf(gs[e] - gsc) : 0.f);
                 g4[e] = sb[t] * da * f;
                 p4[e] = s <= t ? p4[e] * f : 0.f;
             }
-            if (J <= w) {   // the tiles that carry gradient: this wave's rows, transposed
-                *reinterpret_cast<f32x4 *>(sPT + s * LP + 16 * w + 4 * gq) = p4;
-                *reinterpret_cast<f32x4 *>(sGT + s * LP + 16 * w + 4 * gq) = g4;
+            if (J <= rb) {   // the tiles that carry gradient, transposed
+                *reinterpret_cast<f32x4 *>(sPT + s * LP + 16 * rb + 4 * gq) = p4;
+                *reinterpret_cast<f32x4 *>(sGT + s * LP + 16 * rb + 4 * gq) = g4;
             }
         }
     }
@@ -1947,20 +1961,20 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
     float *sXT = reinterpret_cast<float *>(smc + L::XT), *sXP = reinterpret_cast<float *>(smc + L::XP);
     float dgs[4] = {0.f, 0.f, 0.f, 0.f};   // scalar gate: dg at this lane's rows, this lane's channels
 #pragma unroll
-    for (int pp = 0; pp < K / 32; ++pp) {
+    for (int pp = 0; pp < K / PC; ++pp) {
         lds_barrier();   // phase 2 / the previous pass is done with this space
-        {   // the pass's scaled k and q and gamma, rows = tokens: thread (token tr, channels c8 ..)
-            const int x = 32 * pp + c8;
+        {   // the pass's scaled k and q and gamma, rows = tokens: thread (token tb, channels cb ..)
+            const int tb = tid >> 3, cb = 8 * (tid & 7), x = PC * pp + cb;
             bf16x8 kr8 = {}, qr8 = {};
-            if (live) {
-                kr8 = *reinterpret_cast<const bf16x8 *>(k + tr * H * K + x);
-                qr8 = *reinterpret_cast<const bf16x8 *>(q + tr * H * K + x);
+            if (tb < n) {
+                kr8 = *reinterpret_cast<const bf16x8 *>(k + tb * H * K + x);
+                qr8 = *reinterpret_cast<const bf16x8 *>(q + tb * H * K + x);
             }
-            const float *gr = gam + tr * K + x;
+            const float *gr = gam + tb * K + x;
             const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gr), g1 = *reinterpret_cast<const f32x4 *>(gr + 4);
             f32x4 kt[2], kh[2], qh[2];
             if (CH) {
-                const float *gp = gam + (16 * (tr >> 4) + 8) * K + x;
+                const float *gp = gam + (16 * (tb >> 4) + 8) * K + x;
                 const f32x4 p0 = *reinterpret_cast<const f32x4 *>(gp), p1 = *reinterpret_cast<const f32x4 *>(gp + 4);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -1980,37 +1994,37 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                *reinterpret_cast<f32x4 *>(sKt + tr * LW + c8 + 4 * h) = kt[h];
-                *reinterpret_cast<f32x4 *>(sKh + tr * LW + c8 + 4 * h) = kh[h];
-                *reinterpret_cast<f32x4 *>(sQh + tr * LW + c8 + 4 * h) = qh[h];
+                *reinterpret_cast<f32x4 *>(sKt + tb * LW + cb + 4 * h) = kt[h];
+                *reinterpret_cast<f32x4 *>(sKh + tb * LW + cb + 4 * h) = kh[h];
+                *reinterpret_cast<f32x4 *>(sQh + tb * LW + cb + 4 * h) = qh[h];
             }
-            *reinterpret_cast<f32x4 *>(sG + tr * LW + c8) = g0;
-            *reinterpret_cast<f32x4 *>(sG + tr * LW + c8 + 4) = g1;
+            *reinterpret_cast<f32x4 *>(sG + tb * LW + cb) = g0;
+            *reinterpret_cast<f32x4 *>(sG + tb * LW + cb + 4) = g1;
         }
         lds_barrier();
         float loc[2][4];   // d gamma summed over the later rows of this lane's tile column
 #pragma unroll
         for (int xi = 0; xi < 2; ++xi) {
-            const int xb = 2 * pp + xi, xl = 16 * xi + r16, x = 16 * xb + r16;
+            const int i = 2 * pp + xi, xl = 16 * (2 * hf + xi) + r16, x = PC * pp + xl;
             float gv[4], grho[4], fw[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gv[e] = sG[(16 * w + 4 * gq + e) * LW + xl];
+            for (int e = 0; e < 4; ++e) gv[e] = sG[(16 * rb + 4 * gq + e) * LW + xl];
             if (CH) {
 #pragma unroll
                 for (int J = 0; J < 4; ++J) grho[J] = sG[(16 * J + 8) * LW + xl];
             }
             f32x4 aq = z4, ak = z4, as = z4;
-            // rows r of this wave, s <= r:  sum_J e^{gamma_r - gamma_rho(J)} (dP_rJ, dG_rJ) Kt_J
+            // rows r of this block, s <= r:  sum_J e^{gamma_r - gamma_rho(J)} (dP_rJ, dG_rJ) Kt_J
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
-                if (J <= w) {
-                    // A: this wave's rows of dP and dG (its own transposed tiles), B: Kt
+                if (J <= rb) {
+                    // A: this block's rows of dP and dG (the transposed tiles), B: Kt
                     f32x4 b, pa, ga;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         b[j] = sKt[(16 * J + 4 * gq + j) * LW + xl];
-                        pa[j] = sPT[(16 * J + 4 * gq + j) * LP + 16 * w + r16];
-                        ga[j] = sGT[(16 * J + 4 * gq + j) * LP + 16 * w + r16];
+                        pa[j] = sPT[(16 * J + 4 * gq + j) * LP + 16 * rb + r16];
+                        ga[j] = sGT[(16 * J + 4 * gq + j) * LP + 16 * rb + r16];
                     }
                     bf16x4 bh, bl, pah, pal, gah, gal;
                     split4(b, bh, bl);
@@ -2026,12 +2040,12 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
                     }
                 }
             }
-            // rows u of this wave, t >= u:  sum_I e^{gamma_rho(I) - gamma_u} (dG^T Kh_I + dP^T Qh_I)
+            // rows u of this block, t >= u:  sum_I e^{gamma_rho(I) - gamma_u} (dG^T Kh_I + dP^T Qh_I)
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                if (I >= w) {
-                    const f32x4 ag = *reinterpret_cast<const f32x4 *>(sGT + (16 * w + r16) * LP + 16 * I + 4 * gq);
-                    const f32x4 ap = *reinterpret_cast<const f32x4 *>(sPT + (16 * w + r16) * LP + 16 * I + 4 * gq);
+                if (I >= rb) {
+                    const f32x4 ag = *reinterpret_cast<const f32x4 *>(sGT + (16 * rb + r16) * LP + 16 * I + 4 * gq);
+                    const f32x4 ap = *reinterpret_cast<const f32x4 *>(sPT + (16 * rb + r16) * LP + 16 * I + 4 * gq);
                     f32x4 bk, bq;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -2047,7 +2061,7 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float f = CH ? __expf(grho[I] - gv[e]) : 1.f;
-                        if (I == w) fw[e] = f;   // also turns Kh, Qh of this wave's rows back into k, q
+                        if (I == rb) fw[e] = f;   // also turns Kh, Qh of this block's rows back into k, q
                         as[e] = fmaf(f, ps[e], as[e]);
                     }
                 }
@@ -2057,11 +2071,11 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
             float dgn = 0.f, dga[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * w + 4 * gq + e;
+                const int rr = 16 * rb + 4 * gq + e;
                 const float kh = sKh[rr * LW + xl], qh = sQh[rr * LW + xl];
                 const float kr = CH ? kh * fw[e] : kh, qr = CH ? qh * fw[e] : qh;   // 0 past the end
                 const float eg = __expf(gv[e]), em = __expf(gn - gv[e]);
-                const float dqp = aQ[xb][e], dkm = aKm[xb][e], zr = aZ[xb][e], z = zr * sb[rr];
+                const float dqp = aQ[i][e], dkm = aKm[i][e], zr = aZ[i][e], z = zr * sb[rr];
                 dga[e] = qr * aq[e] + kr * (ak[e] - as[e]) + (dqp * qr + z * kr) * eg - dkm * kr * em;
                 dgn = fmaf(dkm * kr, em, dgn);
                 dbv[e] = fmaf(kr * eg, zr, dbv[e]);   // rowsum(Kp * Z)
@@ -2072,7 +2086,7 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
             // reverse running sums down this tile column: the lane's own rows, then
             // the lanes of later row groups (same column); tile totals and the gn
-            // terms go to LDS for the other waves
+            // terms go to LDS for the other row blocks
             const float l3 = dga[3], l2 = l3 + dga[2], l1 = l2 + dga[1], l0 = l1 + dga[0];
             const float n1 = __shfl(l0, (lane + 16) & 63), n2 = __shfl(l0, (lane + 32) & 63),
                         n3 = __shfl(l0, (lane + 48) & 63);
@@ -2087,20 +2101,20 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
             dgn += __shfl_xor(dgn, 16);
             dgn += __shfl_xor(dgn, 32);
             if (gq == 0) {
-                sXT[w * 64 + xl] = tot;
-                sXP[w * 64 + xl] = dgn;
+                sXT[rb * PC + xl] = tot;
+                sXP[rb * PC + xl] = dgn;
             }
         }
         lds_barrier();
 #pragma unroll
         for (int xi = 0; xi < 2; ++xi) {   // dg = reverse running sum of d gamma plus the gn terms
-            const int xl = 16 * xi + r16, x = 32 * pp + xl;
-            float later = sdgn[x] + ((sXP[xl] + sXP[64 + xl]) + (sXP[128 + xl] + sXP[192 + xl]));
+            const int xl = 16 * (2 * hf + xi) + r16, x = PC * pp + xl;
+            float later = sdgn[x] + ((sXP[xl] + sXP[PC + xl]) + (sXP[2 * PC + xl] + sXP[3 * PC + xl]));
 #pragma unroll
-            for (int w2 = 1; w2 < 4; ++w2) later += w2 > w ? sXT[w2 * 64 + xl] : 0.f;
+            for (int b2 = 1; b2 < 4; ++b2) later += b2 > rb ? sXT[b2 * PC + xl] : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * w + 4 * gq + e;
+                const int rr = 16 * rb + 4 * gq + e;
                 const float dgv = loc[xi][e] + later;
                 if (CH) {
                     if (rr < n) a.dg[(r0 + rr * H) * K + x] = dgv;
@@ -2110,6 +2124,7 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
         }
     }
+    // dbeta (and the scalar gate's dg): this wave's columns, then the pair's
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         dbv[e] = sum16(dbv[e]);
@@ -2118,12 +2133,15 @@ __global__ __launch_bounds__(BW_NTHR) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (r16 == 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int t = 16 * w + 4 * gq + e;
-            if (t < n) {
-                a.dbeta[r0 + t * H] = dbv[e];
-                if (!CH) a.dg[r0 + t * H] = dgs[e];
-            }
+            const int t = 16 * rb + 4 * gq + e;
+            spair[hf * C + t] = dbv[e];
+            if (!CH) spair[2 * C + hf * C + t] = dgs[e];
         }
+    }
+    lds_barrier();
+    if (tid < n) {
+        a.dbeta[r0 + tid * H] = spair[tid] + spair[C + tid];
+        if (!CH) a.dg[r0 + tid * H] = spair[2 * C + tid] + spair[3 * C + tid];
     }
 }
 
@@ -2187,7 +2205,7 @@ static hipError_t launch_bwd(const BwArgs &a, long nslices, hipStream_t st)
             hipLaunchKernelGGL((bwd_kgrad2_kernel<DT, K, CH>), dim3(nch), dim3(BW_NTHR), L::kgrad2, st, a);
         } else {
             constexpr int lds_grad = GradLds<K, V>::bytes;
-            hipLaunchKernelGGL((bwd_grad_kernel<K, V, CH>), dim3(nch), dim3(BW_NTHR), lds_grad, st, a);
+            hipLaunchKernelGGL((bwd_grad_kernel<K, V, CH>), dim3(nch), dim3(GR_NTHR), lds_grad, st, a);
         }
     }
     return hipGetLastError();

@@ -148,8 +148,9 @@ gdn_status bwd_sizes(int B, int T, int H, int K, int V, int chunk, long long *nc
     if (!chunk_offsets_fit(H, K, V)) return GDN_ENOTSUP;
     const long long n = prod(B, H, (T + 63) / 64);
     const long long nvb = prod(B, H, V / gdn::BW_VB);
-    // one 256-thread workgroup per chunk / per value block: grid x * 256 < 2^32
-    if (n < 0 || nvb < 0 || n >= (1LL << 24) || nvb >= (1LL << 24)) return GDN_ENOTSUP;
+    // one workgroup of at most 512 threads per chunk, of 256 per value block:
+    // grid x * threads < 2^32
+    if (n < 0 || nvb < 0 || n >= (1LL << 23) || nvb >= (1LL << 24)) return GDN_ENOTSUP;
     *nch = n;
     return GDN_OK;
 }
