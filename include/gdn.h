@@ -279,7 +279,8 @@ GDN_API gdn_status gdn_chunk_bwd_workspace_size(int B, int T, int H, int K, int 
  * alignment, every other pointer its element alignment.  No output may
  * overlap an input, another output or the workspace.  B, T or H equal to 0 is a
  * valid call (T = 0: dS0 receives dS_T, or zeros).  Calls that share one
- * workspace must not run concurrently.
+ * workspace must not run concurrently.  B H ceil(T / 64) must stay below 2^23
+ * chunks (one workgroup of up to 512 threads per chunk; GDN_ENOTSUP beyond).
  */
 GDN_API gdn_status gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *g,
                                  const float *beta, const float *S0, const void *d_o,

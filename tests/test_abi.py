@@ -420,6 +420,15 @@ def test_chunk_paths_reject_shapes_past_32bit_offsets(L):
     assert L.gdn_chunk_bwd_workspace_size(1, 64, 65535, 128, 128, 64, ctypes.byref(n)) == gdn.GDN_OK
 
 
+def test_chunk_bwd_rejects_grids_past_2_23_chunks(L):
+    # one 512-thread workgroup per 64-token chunk: 2^23 chunks would make the
+    # grid 2^32 threads
+    import ctypes
+    n = ctypes.c_size_t(0)
+    assert L.gdn_chunk_bwd_workspace_size(1, 64 * (1 << 23), 1, 128, 128, 64, ctypes.byref(n)) == gdn.GDN_ENOTSUP
+    assert L.gdn_chunk_bwd_workspace_size(1, 64 * ((1 << 23) - 1), 1, 128, 128, 64, ctypes.byref(n)) == gdn.GDN_OK
+
+
 def test_prologue_channel_cap_above_five_is_unsupported(L):
     # the per-channel chunk kernels need g >= -5: a larger cap (or none) for the
     # per-channel gate is refused; the scalar gate takes any cap
