@@ -20,7 +20,7 @@ struct BwWs {
     float *gam;   // [64][K]  in-chunk cumulative log-decay
     float *Tm;    // [64][64] (I + diag(beta) G)^{-1}                          F
     float *TT;    // [64][64] its transpose                                     F
-    float *Gm;    // [64][64] G, strictly lower
+    float *Gm;    // [64][64] G, strictly lower (bf16 for bf16 inputs)
     float *PT;    // [64][64] P^T (P lower with the diagonal)                     S
     float *hS;    // [K][V]   state entering the chunk                      (input dtype)
     float *dhS;   // [K][V]   dL/d(state leaving the chunk)                 (input dtype)

@@ -391,7 +391,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
     // gate: the plain products, scaled by e^{gamma_t - gamma_s} afterwards.
     // A = diag(beta) G goes to LDS only after every wave is done with k and q
     // (A and T take their space): each wave keeps its (at most three) blocks.
-    float *Gm = a.ws.Gm + ci * (C * C);
+    OT *Gm = reinterpret_cast<OT *>(a.ws.Gm) + ci * (C * C);   // bf16 inputs: read for dbeta only
     OT *PT = reinterpret_cast<OT *>(a.ws.PT) + ci * (C * C);
     f32x4 akeep[3];
     {
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
                 }
                 gv = s < t ? gv : 0.f;
                 p4[e] = s <= t ? pv : 0.f;
-                Gm[t * C + s] = gv;
+                Gm[t * C + s] = OT(gv);
                 akeep[i][e] = sb[t] * gv;
             }
             st4(PT + frag_idx<OT, C>(16 * J + r16, 16 * I + 4 * gq), p4);
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_prep_kernel(BwArgs a)
     for (int idx = tid; idx < C * C; idx += BW_NTHR) {   // the blocks above the diagonal
         const int t = idx / C, s = idx % C;
         if (s / 16 > t / 16) {
-            Gm[idx] = 0.f;
+            Gm[idx] = OT(0.f);
             PT[frag_idx<OT, C>(s, t)] = OT(0.f);
         }
     }
@@ -1913,12 +1913,12 @@ __global__ __launch_bounds__(GR_NTHR) void bwd_grad_kernel(BwArgs a)
             }
             sMA[(rb * 4 + J) * 64 + lane] = cvt4(tile_transpose(scr, m));
         }
-        const float *Gm = a.ws.Gm + ci * (C * C);   // G at this lane's elements, for dbeta
+        const __bf16 *Gm = reinterpret_cast<const __bf16 *>(a.ws.Gm) + ci * (C * C);   // G, for dbeta
         float gmv[2][4];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gmv[jj][e] = Gm[(16 * rb + 4 * gq + e) * C + 16 * (2 * hf + jj) + r16];
+            for (int e = 0; e < 4; ++e) gmv[jj][e] = (float)Gm[(16 * rb + 4 * gq + e) * C + 16 * (2 * hf + jj) + r16];
         float gs[4];   // scalar gate: gamma at this lane's rows
         if (!CH) {
 #pragma unroll
