@@ -62,9 +62,9 @@ MEASURED_TRAFFIC = {
     "recurrent_step_kernel<bf16,128,128,channel>": (("recurrent_step.hip", "gdn_common.h"),
                                                     "6075e5972b67aade", 1642950528),
     "recurrent_multi_kernel<bf16,128,128,channel>/final": (("recurrent_multi.hip", "gdn_common.h"),
-                                                           "e96c18f898c72e85", 1739625626),
+                                                           "67d516fbad7f5b32", 1739688128),
     "recurrent_multi_kernel<bf16,128,128,channel>/hist": (("recurrent_multi.hip", "gdn_common.h"),
-                                                          "e96c18f898c72e85", 4158918874),
+                                                          "67d516fbad7f5b32", 4159179904),
     "prologue_kernel<bf16,128,128,scalar,silu>": (("prologue.hip", "prologue.h", "prologue_ops.h",
                                                    "gdn_common.h"), "672309d493c963a2", 1307198496),
     "recurrent_step_prologue_kernel<bf16,128,128,channel,silu>": (("prologue.hip", "prologue.h",

@@ -19,6 +19,11 @@
 // (alpha k, alpha q, alpha, k) are double-buffered in LDS by token parity, so
 // that a token's vectors can be written while the previous token's state update
 // still reads its own.
+//
+// Occupancy: the kernel is bound by the state's round trip to HBM, and more
+// workgroups in flight keep more of it moving.  It is compiled for five waves
+// per SIMD (at most 96 VGPRs; d_k = d_v = 128 needs 92 then, with no spills,
+// against 99 and four waves without the bound).
 #include "gdn_common.h"
 
 namespace gdn {
@@ -28,7 +33,7 @@ constexpr int RM_NWAVE = RM_NTHR / 64;
 constexpr int RM_VW = 64;             // value columns per workgroup (at most)
 
 template <typename DT, int K, int V, bool CHANNEL>
-__global__ __launch_bounds__(RM_NTHR) void recurrent_multi_kernel(
+__global__ __launch_bounds__(RM_NTHR) __attribute__((amdgpu_waves_per_eu(5))) void recurrent_multi_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const float *S0,
     DT *__restrict__ o, float *S_T, float *__restrict__ S_hist, int M, int H)
