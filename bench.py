@@ -58,7 +58,7 @@ MEASURED_TRAFFIC = {
                                  "34acdf37d6007014", 862390784),
     "chunk_fwd_wsc_kernel<128>": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                    "mfma_frag.h"),
-                                  "7f74300dedd8aaf6", 420170336),
+                                  "919f74973a0c28f3", 420173184),
     "recurrent_step_kernel<bf16,128,128,channel>": (("recurrent_step.hip", "gdn_common.h"),
                                                     "6075e5972b67aade", 1642950528),
     "recurrent_multi_kernel<bf16,128,128,channel>/final": (("recurrent_multi.hip", "gdn_common.h"),
@@ -73,7 +73,7 @@ MEASURED_TRAFFIC = {
     "chunk_fwd_seg/channel_long": (("chunk_fwd_seg.hip", "ws_common.h", "gdn_common.h",
                                     "mfma_frag.h"), "64ac46ed9b65d47a", 13592231008),
     "chunk_fwd_seg/channel_long/o": (("chunk_fwd_seg.hip", "chunk_fwd_wsc.hip", "ws_common.h",
-                                      "gdn_common.h", "mfma_frag.h"), "bef54b1936a85dd7", 33505080592),
+                                      "gdn_common.h", "mfma_frag.h"), "7be8db47e2f9a32b", 33514739872),
     # the whole backward call (prep, sweeps, grad) at B4 H6 T4096, per-channel gate, bf16
     "chunk_bwd/channel_bf16": (("chunk_bwd.hip", "chunk_bwd.h", "ws_common.h", "gdn_common.h",
                                 "mfma_frag.h"), "366716605ada2129", 1350506336),
@@ -219,10 +219,10 @@ def bench_prefill(torch, gdn, timer, name, want_o, use_ws, steps=None, warmup=No
     if nseg > 1:
         kernels = ["chunk_fwd_seg_kernel", "seg_combine_kernel"]
         if want_o:
-            kernels.append("chunk_fwd_wsc_kernel<128, true>")
+            kernels.append("chunk_fwd_wsc_kernel<128, true, false>")
         tkey = "chunk_fwd_seg/" + name + ("/o" if want_o else "")
     elif channel:
-        kernels = ["chunk_fwd_wsc_kernel<128, %s>" % ("true" if want_o else "false")]
+        kernels = ["chunk_fwd_wsc_kernel<128, %s, false>" % ("true" if want_o else "false")]
         tkey = "chunk_fwd_wsc_kernel<128>" + ("" if name == "channel_bf16" else "/" + name)
     else:
         kernels = ["chunk_fwd_ws_kernel<128>"]
@@ -332,7 +332,7 @@ def bench_decoupled(torch, gdn, timer):
     pre = {"workload": f"per-key-channel-gate chunkwise forward with decoupled erase/write gates, "
                        f"B={B} H={H} T={T} d_k=d_v={K}, bf16 q/k/v/o, fp32 g/e/w/state, "
                        "returns o and S_T",
-           "entry": "gdn_chunk_fwd_decoupled", "kernel": "chunk_fwd_kernel<bf16,128,true>",
+           "entry": "gdn_chunk_fwd_decoupled", "kernel": "chunk_fwd_wsc_kernel<128, true, true>",
            "mtok_s": B * T / s / 1e6, "gbs": nbytes / s / 1e9,
            "frac_hbm": nbytes / s / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": nbytes}
     pre.update(t)
@@ -418,7 +418,7 @@ def bench_bwd(torch, gdn, timer):
             "warmup_performed": tb["warmup_performed"],
             "kernels": ["bwd_prep_kernel", "bwd_sweeps_kernel", "bwd_grad_kernel"],
             "forward": "gdn_chunk_fwd_ws: chunk_fwd_seg_kernel, seg_combine_kernel, "
-                       "chunk_fwd_wsc_kernel<128, true> per segment"}
+                       "chunk_fwd_wsc_kernel<128, true, false> per segment"}
 
 
 def prologue_bytes(B, T, H, K, V, es, channel):

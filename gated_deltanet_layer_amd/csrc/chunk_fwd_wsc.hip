@@ -36,7 +36,8 @@ constexpr int WC_T = 64;       // tokens per chunk
 constexpr int WC_VB = 64;      // value columns per workgroup
 constexpr int WC_NTHR = 512;   // 4 chain waves + 4 prep waves
 
-template <int K> struct WcSmem {
+// DEC: decoupled erase/write gates (the derived buffer also holds w_t).
+template <int K, bool DEC = false> struct WcSmem {
     static constexpr int al(int x) { return (x + 255) & ~255; }
     static constexpr int RB = K * 2;              // bytes per tile row
     static constexpr int CPR = RB / 16;           // 16-byte chunks per row
@@ -55,8 +56,9 @@ template <int K> struct WcSmem {
     static constexpr int dAn = 0;                           // [48][LDC] rows 16..63 of -A
     static constexpr int dP = dAn + (WC_T - 16) * LDC * 2;  // [64][LDC] P
     static constexpr int dTd = dP + WC_T * LDC * 2;         // [64][16] T_ii
-    static constexpr int dBeta = dTd + WC_T * LDD * 2;      // beta_t
-    static constexpr int dCF = dBeta + WC_T * 4;            // [4][K]: e^{R_1}, e^{R_2}, e^{R_3}, e^{gn}
+    static constexpr int dBeta = dTd + WC_T * LDD * 2;      // beta_t (decoupled gates: e_t)
+    static constexpr int dW = dBeta + WC_T * 4;             // decoupled gates: w_t
+    static constexpr int dCF = dW + (DEC ? WC_T * 4 : 0);   // [4][K]: e^{R_1}, e^{R_2}, e^{R_3}, e^{gn}
     static constexpr int DBUF = al(dCF + 4 * K * 4);
     static constexpr int kE = oD + 2 * DBUF;                // [4][K] E_b of the chunk being prepared
     static constexpr int kAd = kE + 4 * K * 4;              // [4][16][16] fp32 -A of diagonal blocks
@@ -105,14 +107,21 @@ struct WcArgs {
     int seg_len, nseg;
     long nbhv;
     const float *Sb;
+    // Decoupled erase/write gates (reading of the MindPattern "Gated DeltaNet"
+    // page, finding of 2026-05-22): beta carries the erase gate e and wgate the
+    // write gate w; only the DEC instantiations read it.
+    const float *wgate;
 };
 
 // WO = false: the final state only (no o).  q is then not read, and QL, P, Q+ S
 // and O are not formed: the state update needs none of them.
-template <int K, bool WO>
+// DEC = true: decoupled gates, S_t = (I - e_t k k^T) Diag(alpha_t) S + w_t k v^T.
+// The chunk algebra is the same with e in beta's place in (I + A) and on the
+// right side X = diag(w) V - diag(e) K+ S.
+template <int K, bool WO, bool DEC>
 __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
 {
-    using L = WcSmem<K>;
+    using L = WcSmem<K, DEC>;
     constexpr int NT = K / 16;          // 16-row tiles of S
     constexpr int NKB = K / 32;         // 32-key blocks
     constexpr int CPR = L::CPR;
@@ -163,7 +172,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         // raw q, k, g of this lane's row, fragment layout: keys 32 kb + 8 gq .. +7
         bf16x8 rk[NKB], rq[NKB];
         f32x4 rg[NKB][2];
-        float rb = 0.f;
+        float rb = 0.f, rw = 0.f;
         // Loads of one key block (k, q, g) or of beta for chunk n; rows past T
         // read as zero (g = beta = 0: they change nothing).
         auto fetch_kb = [&](int n, int kb) __attribute__((always_inline)) {
@@ -184,6 +193,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         auto fetch_beta = [&](int n) __attribute__((always_inline)) {
             const int t = n * WC_T + row;
             rb = t < T ? args.beta[row_base + (long)t * H] : 0.f;
+            if constexpr (DEC) rw = t < T ? args.wgate[row_base + (long)t * H] : 0.f;
         };
 
         unsigned arrivals = 0;
@@ -236,7 +246,10 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
                     *reinterpret_cast<f32x4 *>(eb + 4) = el[1];
                 }
             }
-            if (gq == 0) reinterpret_cast<float *>(D + L::dBeta)[row] = rb;
+            if (gq == 0) {
+                reinterpret_cast<float *>(D + L::dBeta)[row] = rb;
+                if constexpr (DEC) reinterpret_cast<float *>(D + L::dW)[row] = rw;
+            }
             if (n + 1 < c1) fetch_beta(n + 1);
             arrivals += 4;
             prep_barrier(ctr, arrivals);         // KL, QL, KI and E of all blocks written
@@ -482,6 +495,7 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
         const __bf16 *sP = reinterpret_cast<const __bf16 *>(D + L::dP);
         const __bf16 *sTd = reinterpret_cast<const __bf16 *>(D + L::dTd);
         const float *sBeta = reinterpret_cast<const float *>(D + L::dBeta);
+        const float *sW = reinterpret_cast<const float *>(D + L::dW);   // decoupled gates only
         const float *sCF = reinterpret_cast<const float *>(D + L::dCF);
         unsigned ktr_addr[NKB];
 #pragma unroll
@@ -540,9 +554,16 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             const f32x4 bt = *reinterpret_cast<const f32x4 *>(sBeta + 16 * rt + 4 * gq);
+            if constexpr (DEC) {   // w v - e K+ S
+                const f32x4 wt = *reinterpret_cast<const f32x4 *>(sW + 16 * rt + 4 * gq);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                X[rt][e] = bt[e] * (__builtin_bit_cast(float, (unsigned)vr[rt][e] << 16) - KS[rt][e]);
+                for (int e = 0; e < 4; ++e)
+                    X[rt][e] = wt[e] * __builtin_bit_cast(float, (unsigned)vr[rt][e] << 16) - bt[e] * KS[rt][e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    X[rt][e] = bt[e] * (__builtin_bit_cast(float, (unsigned)vr[rt][e] << 16) - KS[rt][e]);
+            }
         }
         if (c + 1 < c1) fetch_v(c + 1);
         const Frag<__bf16> fT0 = lds_frag_lo(sTd, L::LDD, 0, 0), fT1 = lds_frag_lo(sTd, L::LDD, 16, 0);
@@ -621,18 +642,18 @@ __global__ __launch_bounds__(WC_NTHR, 1) void chunk_fwd_wsc_kernel(WcArgs args)
     }
 }
 
-template <int K, bool WO>
+template <int K, bool WO, bool DEC = false>
 static hipError_t launch_wsc(const WcArgs &a, long nwg, hipStream_t stream)
 {
-    using L = WcSmem<K>;
+    using L = WcSmem<K, DEC>;
     static bool attr_set = false;  // benign race: every thread sets the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_wsc_kernel<K, WO>,
+        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_wsc_kernel<K, WO, DEC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((chunk_fwd_wsc_kernel<K, WO>), dim3((unsigned)nwg), dim3(WC_NTHR), L::bytes, stream, a);
+    hipLaunchKernelGGL((chunk_fwd_wsc_kernel<K, WO, DEC>), dim3((unsigned)nwg), dim3(WC_NTHR), L::bytes, stream, a);
     return hipGetLastError();
 }
 
@@ -652,6 +673,24 @@ hipError_t chunk_fwd_wsc_launch(int K, const void *q, const void *k, const void 
     if (o)
         return K == 64 ? launch_wsc<64, true>(a, nwg, st) : launch_wsc<128, true>(a, nwg, st);
     return K == 64 ? launch_wsc<64, false>(a, nwg, st) : launch_wsc<128, false>(a, nwg, st);
+}
+
+// The same for decoupled erase/write gates (erase in beta's place).
+hipError_t chunk_fwd_wsc_dg_launch(int K, const void *q, const void *k, const void *v, const float *g,
+                                   const float *erase, const float *write, const float *S0, void *o,
+                                   float *S_T, int B, int T, int H, int V, hipStream_t st)
+{
+    WcArgs a = {};
+    a.q = (const __bf16 *)q; a.k = (const __bf16 *)k; a.v = (const __bf16 *)v;
+    a.g = g; a.beta = erase; a.wgate = write; a.S0 = S0; a.o = (__bf16 *)o; a.S_T = S_T;
+    a.T = T; a.H = H; a.V = V;
+    a.nvb = V / WC_VB;
+    const long bhn = (long)B * H;
+    a.xcd_map = (a.nvb > 1 && bhn % 8 == 0) ? 1 : 0;
+    const long nwg = bhn * a.nvb;
+    if (o)
+        return K == 64 ? launch_wsc<64, true, true>(a, nwg, st) : launch_wsc<128, true, true>(a, nwg, st);
+    return K == 64 ? launch_wsc<64, false, true>(a, nwg, st) : launch_wsc<128, false, true>(a, nwg, st);
 }
 
 } // namespace gdn
