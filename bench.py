@@ -55,7 +55,7 @@ FLUSH_BYTES = 512 << 20        # twice the 256 MB last-level cache
 MEASURED_TRAFFIC = {
     "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
                                   "mfma_frag.h"),
-                                 "34acdf37d6007014", 862390784),
+                                 "5df1a38c069ce213", 862547296),
     "chunk_fwd_wsc_kernel<128>": (("chunk_fwd_wsc.hip", "ws_common.h", "gdn_common.h",
                                    "mfma_frag.h"),
                                   "919f74973a0c28f3", 420173184),
@@ -84,7 +84,7 @@ MEASURED_TRAFFIC = {
 MEASURED_MFMA_MOPS = {
     "chunk_fwd_ws_kernel<128>": (("chunk_fwd_ws.hip", "ws_common.h", "gdn_common.h",
                                   "mfma_frag.h"),
-                                 "34acdf37d6007014", 257949696),
+                                 "5df1a38c069ce213", 257949696),
 }
 
 
@@ -225,7 +225,7 @@ def bench_prefill(torch, gdn, timer, name, want_o, use_ws, steps=None, warmup=No
         kernels = ["chunk_fwd_wsc_kernel<128, %s, false>" % ("true" if want_o else "false")]
         tkey = "chunk_fwd_wsc_kernel<128>" + ("" if name == "channel_bf16" else "/" + name)
     else:
-        kernels = ["chunk_fwd_ws_kernel<128>"]
+        kernels = ["chunk_fwd_ws_kernel<128, false>"]
         tkey = "chunk_fwd_ws_kernel<128>"
     s = t["ms"] / 1e3
     gbs = nbytes / s / 1e9

@@ -674,6 +674,9 @@ hipError_t chunk_fwd_wsc_launch(int K, const void *q, const void *k, const void 
 hipError_t chunk_fwd_wsc_dg_launch(int K, const void *q, const void *k, const void *v, const float *g,
                                    const float *erase, const float *write, const float *S0, void *o,
                                    float *S_T, int B, int T, int H, int V, hipStream_t st);
+hipError_t chunk_fwd_ws_dg_launch(int K, const void *q, const void *k, const void *v, const float *g,
+                                  const float *erase, const float *write, const float *S0, void *o,
+                                  float *S_T, int B, int T, int H, int V, hipStream_t st);
 
 static ChunkArgs chunk_args(const void *q, const void *k, const void *v, const float *g,
                             const float *beta, const float *wgate, const float *S0, void *o,
@@ -707,9 +710,9 @@ hipError_t chunk_fwd_launch(bool bf16, bool channel, int K, const void *q, const
     return channel ? launch_chunk<float, 64, true>(a, st) : launch_chunk<float, 64, false>(a, st);
 }
 
-// Decoupled erase/write gates (erase in beta's place, write gate w): bf16 with
-// the per-channel gate takes the warp-specialised kernel's decoupled
-// instantiation; every other storage type, gate and K the kernel above.
+// Decoupled erase/write gates (erase in beta's place, write gate w): bf16
+// takes the warp-specialised kernels' decoupled instantiations; fp32 the
+// kernel above.
 hipError_t chunk_fwd_dg_launch(bool bf16, bool channel, int K, const void *q, const void *k,
                                const void *v, const float *g, const float *erase,
                                const float *write, const float *S0, void *o, float *S_T, int B,
@@ -717,6 +720,8 @@ hipError_t chunk_fwd_dg_launch(bool bf16, bool channel, int K, const void *q, co
 {
     if (bf16 && channel)
         return chunk_fwd_wsc_dg_launch(K, q, k, v, g, erase, write, S0, o, S_T, B, T, H, V, st);
+    if (bf16)
+        return chunk_fwd_ws_dg_launch(K, q, k, v, g, erase, write, S0, o, S_T, B, T, H, V, st);
     const ChunkArgs a = chunk_args(q, k, v, g, erase, write, S0, o, S_T, B, T, H, V);
     if (!bf16)
         return channel ? launch_chunk<float, 64, true>(a, st) : launch_chunk<float, 64, false>(a, st);

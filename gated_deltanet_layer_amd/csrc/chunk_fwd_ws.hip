@@ -39,7 +39,8 @@ constexpr int WS_T = 64;       // tokens per chunk
 constexpr int WS_VB = 64;      // value columns per workgroup
 constexpr int WS_NTHR = 512;   // 4 chain waves + 4 prep waves
 
-template <int K> struct WsSmem {
+// DEC: decoupled erase/write gates (each q/k stage also holds w of its chunk).
+template <int K, bool DEC = false> struct WsSmem {
     static constexpr int al(int x) { return (x + 255) & ~255; }
     static constexpr int RB = K * 2;              // bytes per q/k row
     static constexpr int CPR = RB / 16;           // 16-byte chunks per q/k row
@@ -50,8 +51,8 @@ template <int K> struct WsSmem {
     static constexpr int LDC = WS_T + PAD;        // rows of -A and P (fragment order)
     static constexpr int LDD = 16;                // rows of T_ii
     // q/k: a ring of three stages (k at +0, q at +TILE, then g and beta of the
-    // chunk, 64 floats each); v: a ring of two
-    static constexpr int STAGE = 2 * TILE + 2 * WS_T * 4;
+    // chunk, 64 floats each, and with decoupled gates w); v: a ring of two
+    static constexpr int STAGE = 2 * TILE + (DEC ? 3 : 2) * WS_T * 4;
     static constexpr int oKQ = 0;
     static constexpr int oV = oKQ + 3 * STAGE;
     static constexpr int oD = oV + 2 * VTILE;
@@ -59,8 +60,8 @@ template <int K> struct WsSmem {
     static constexpr int dAn = 0;                           // [48][LDC] rows 16..63 of -A
     static constexpr int dP = dAn + (WS_T - 16) * LDC * 2;  // [64][LDC] P
     static constexpr int dTd = dP + WS_T * LDC * 2;         // [64][16] T_ii
-    static constexpr int dBeta = dTd + WS_T * LDD * 2;      // beta_t
-    static constexpr int dBeg = dBeta + WS_T * 4;           // beta_t e^{gamma_t}
+    static constexpr int dBeta = dTd + WS_T * LDD * 2;      // beta_t (decoupled gates: w_t)
+    static constexpr int dBeg = dBeta + WS_T * 4;           // beta_t e^{gamma_t} (decoupled: e_t e^{gamma_t})
     static constexpr int dEg = dBeg + WS_T * 4;             // e^{gamma_t}
     static constexpr int dEgn = dEg + WS_T * 4;             // e^{gamma_n - gamma_t}
     static constexpr int dEgN = dEgn + WS_T * 4;            // e^{gamma_n}
@@ -172,12 +173,20 @@ struct WsArgs {
     float *S_T;
     int T, H, V, nvb;
     int xcd_map;
+    // Decoupled erase/write gates (reading of the MindPattern "Gated DeltaNet"
+    // page, finding of 2026-05-22): beta carries the erase gate e and wgate the
+    // write gate w; only the DEC instantiations read it.
+    const float *wgate;
 };
 
-template <int K>
+// DEC = true: decoupled gates, S_t = (I - e_t k k^T) Diag(alpha_t) S + w_t k v^T:
+// e takes beta's place in (I + A) and in the K S term of the right side, w in
+// its V term, X = diag(w) V - diag(e e^{gamma}) K S.  Only the prep waves'
+// staging differs.
+template <int K, bool DEC>
 __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
 {
-    using L = WsSmem<K>;
+    using L = WsSmem<K, DEC>;
     constexpr int NT = K / 16;          // 16-row tiles of S
     constexpr int NKB = K / 32;         // 32-key blocks
     constexpr int CPR = L::CPR;
@@ -251,6 +260,7 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 const long r = row_base + (long)min(t0 + lane, T - 1) * H;
                 g2lds4(args.g + r, st + 2 * L::TILE);
                 g2lds4(args.beta + r, st + 2 * L::TILE + WS_T * 4);
+                if constexpr (DEC) g2lds4(args.wgate + r, st + 2 * L::TILE + 2 * WS_T * 4);
             }
             const __bf16 *src = which == 0 ? args.k : args.q;
             char *tile = st + (which == 0 ? 0 : L::TILE);
@@ -312,7 +322,10 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
                 const float eg = __expf(x);
                 reinterpret_cast<float *>(D + L::dEg)[lane] = eg;
                 reinterpret_cast<float *>(D + L::dBeg)[lane] = pb * eg;
-                reinterpret_cast<float *>(D + L::dBeta)[lane] = pb;
+                if constexpr (DEC)   // the write gate scales V
+                    reinterpret_cast<float *>(D + L::dBeta)[lane] = live ? gb[2 * WS_T + lane] : 0.f;
+                else
+                    reinterpret_cast<float *>(D + L::dBeta)[lane] = pb;
             } else if (pw == 3) {
                 const float gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
                 reinterpret_cast<float *>(D + L::dEgn)[lane] = __expf(gn - x);
@@ -558,18 +571,18 @@ __global__ __launch_bounds__(WS_NTHR, 1) void chunk_fwd_ws_kernel(WsArgs args)
     }
 }
 
-template <int K>
+template <int K, bool DEC = false>
 static hipError_t launch_ws(const WsArgs &a, long nwg, hipStream_t stream)
 {
-    using L = WsSmem<K>;
+    using L = WsSmem<K, DEC>;
     static bool attr_set = false;  // benign race: every thread sets the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_ws_kernel<K>,
+        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_ws_kernel<K, DEC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(chunk_fwd_ws_kernel<K>, dim3((unsigned)nwg), dim3(WS_NTHR), L::bytes, stream, a);
+    hipLaunchKernelGGL((chunk_fwd_ws_kernel<K, DEC>), dim3((unsigned)nwg), dim3(WS_NTHR), L::bytes, stream, a);
     return hipGetLastError();
 }
 
@@ -578,7 +591,7 @@ hipError_t chunk_fwd_ws_launch(int K, const void *q, const void *k, const void *
                                const float *beta, const float *S0, void *o, float *S_T, int B,
                                int T, int H, int V, hipStream_t st)
 {
-    WsArgs a;
+    WsArgs a = {};
     a.q = (const __bf16 *)q; a.k = (const __bf16 *)k; a.v = (const __bf16 *)v;
     a.g = g; a.beta = beta; a.S0 = S0; a.o = (__bf16 *)o; a.S_T = S_T;
     a.T = T; a.H = H; a.V = V;
@@ -587,6 +600,22 @@ hipError_t chunk_fwd_ws_launch(int K, const void *q, const void *k, const void *
     a.xcd_map = (a.nvb > 1 && bhn % 8 == 0) ? 1 : 0;
     const long nwg = bhn * a.nvb;
     return K == 64 ? launch_ws<64>(a, nwg, st) : launch_ws<128>(a, nwg, st);
+}
+
+// The same for decoupled erase/write gates (erase in beta's place).
+hipError_t chunk_fwd_ws_dg_launch(int K, const void *q, const void *k, const void *v, const float *g,
+                                  const float *erase, const float *write, const float *S0, void *o,
+                                  float *S_T, int B, int T, int H, int V, hipStream_t st)
+{
+    WsArgs a = {};
+    a.q = (const __bf16 *)q; a.k = (const __bf16 *)k; a.v = (const __bf16 *)v;
+    a.g = g; a.beta = erase; a.wgate = write; a.S0 = S0; a.o = (__bf16 *)o; a.S_T = S_T;
+    a.T = T; a.H = H; a.V = V;
+    a.nvb = V / WS_VB;
+    const long bhn = (long)B * H;
+    a.xcd_map = (a.nvb > 1 && bhn % 8 == 0) ? 1 : 0;
+    const long nwg = bhn * a.nvb;
+    return K == 64 ? launch_ws<64, true>(a, nwg, st) : launch_ws<128, true>(a, nwg, st);
 }
 
 } // namespace gdn

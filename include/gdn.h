@@ -202,9 +202,8 @@ GDN_API gdn_status gdn_recurrent_step(const void *q, const void *k, const void *
  * (prefill: o and S_T outputs, S_T may equal S0) and gdn_recurrent_step
  * (decode: S updated in place); neither output may overlap `write`.  The
  * prefill runs the sequential chunk kernels for every storage type, gate and
- * K (fp32: K = 64), never the sequence-parallel form: bf16 with the
- * per-key-channel gate on the warp-specialised kernel, the rest on the plain
- * chunk kernel.
+ * K (fp32: K = 64), never the sequence-parallel form: bf16 on the
+ * warp-specialised kernels, fp32 on the plain chunk kernel.
  */
 GDN_API gdn_status gdn_chunk_fwd_decoupled(const void *q, const void *k, const void *v,
                                            const float *g, const float *erase, const float *write,

@@ -56,6 +56,8 @@ CASES = [
     (2, 2, 257, 128, 128, "bf16", "head", 0.0),        # one token in the last chunk, no S0
     (1, 3, 200, 64, 128, "bf16", "channel", 0.05),
     (1, 2, 190, 128, 64, "bf16", "head", 0.05),
+    (1, 2, 150, 64, 64, "bf16", "head", 0.05),         # the scalar-gate kernel at K = 64
+    (2, 1, 200, 64, 128, "bf16", "head", 0.0),
     (1, 2, 130, 64, 64, "fp32", "head", 0.05),
     (2, 1, 129, 64, 64, "fp32", "channel", 0.0),
 ]
@@ -70,12 +72,14 @@ def test_chunk_decoupled_matches_oracle(B, H, T, K, V, dtype, gate, s0):
     _chunk_case(cfg, e, w, label="random gates")
 
 
-@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("fp32", 64)])
-def test_chunk_equal_gates_is_the_card_recurrence(dtype, K):
+@pytest.mark.parametrize("dtype,K,gate", [("bf16", 128, "channel"), ("bf16", 128, "head"),
+                                          ("fp32", 64, "channel")])
+def test_chunk_equal_gates_is_the_card_recurrence(dtype, K, gate):
     """e = w = beta: the same results as gdn_chunk_fwd, within the rounding of
     w v - e K+S against beta (v - K+S)."""
-    cfg = ChunkConfig("dg", B=1, H=2, T=333, K=K, V=K, dtype=dtype, gate="channel",
-                      g_sigma=2.0, g_cap=5.0, s0_sigma=0.05)
+    cfg = ChunkConfig("dg", B=1, H=2, T=333, K=K, V=K, dtype=dtype, gate=gate,
+                      g_sigma=2.0 if gate == "channel" else 1.0,
+                      g_cap=5.0 if gate == "channel" else None, s0_sigma=0.05)
     d = _dev(chunk_inputs(cfg))
     _, o, S = _chunk_case(cfg, d["beta"], d["beta"], d=d, label="e = w = beta")
     ro, rS = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], workspace=False)
