@@ -1604,13 +1604,12 @@ template <int K, int V> struct GradLds {
     static constexpr int NXB = K / 16;
     static constexpr int HDR = 2048;   // beta [C], e^{gn} rowsum(S dS') [K], pair sums [2][2][C]
     // phase 1
-    static constexpr int SZ_KS = K * VS * 2, SZ_CS = C * VS * 2, SZ_T = VS * LT * 2;
+    static constexpr int SZ_KS = K * VS * 2, SZ_CS = C * VS * 2;
     static constexpr int S0 = HDR, DS0 = S0 + 2 * SZ_KS;              // S, dS' [2][K][VS] bf16
     static constexpr int O1 = DS0 + 2 * SZ_KS, V1 = O1 + SZ_CS;        // dO, v [C][VS]
     static constexpr int DH = V1 + SZ_CS, DL = DH + SZ_CS;             // Delta high / low [C][VS]
     static constexpr int EH = DL + SZ_CS, EL = EH + SZ_CS;             // dDelta high / low [C][VS]
-    static constexpr int TH = EL + SZ_CS, TL = TH + SZ_T;              // dDelta^T high / low [VS][LT]
-    static constexpr int END1 = TL + SZ_T;
+    static constexpr int END1 = EL + SZ_CS;
     // phase 2 (PT and GT stay for phase 3)
     static constexpr int SZ_PT = C * LP * 4;
     static constexpr int PT = HDR, GT = PT + SZ_PT;                    // dP^T, dG^T [C][LP] fp32
@@ -1745,7 +1744,6 @@ __global__ __launch_bounds__(GR_NTHR) void bwd_grad_kernel(BwArgs a)
         __bf16 *bO = reinterpret_cast<__bf16 *>(smc + L::O1), *bVv = reinterpret_cast<__bf16 *>(smc + L::V1);
         __bf16 *bDh = reinterpret_cast<__bf16 *>(smc + L::DH), *bDl = reinterpret_cast<__bf16 *>(smc + L::DL);
         __bf16 *bEh = reinterpret_cast<__bf16 *>(smc + L::EH), *bEl = reinterpret_cast<__bf16 *>(smc + L::EL);
-        __bf16 *bTh = reinterpret_cast<__bf16 *>(smc + L::TH), *bTl = reinterpret_cast<__bf16 *>(smc + L::TL);
         auto store_stage = [&]() {
             const int o = tr * VS + c8;
             bf16x8 h, l;
@@ -1758,11 +1756,6 @@ __global__ __launch_bounds__(GR_NTHR) void bwd_grad_kernel(BwArgs a)
                 *reinterpret_cast<uint4 *>(bVv + o) = sv;
                 *reinterpret_cast<bf16x8 *>(bEh + o) = h;
                 *reinterpret_cast<bf16x8 *>(bEl + o) = l;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    bTh[(c8 + j) * LT + tr] = h[j];
-                    bTl[(c8 + j) * LT + tr] = l[j];
-                }
             }
         };
 #pragma unroll 1
@@ -1809,15 +1802,20 @@ __global__ __launch_bounds__(GR_NTHR) void bwd_grad_kernel(BwArgs a)
                 }
             }
             {   // Y = T^T dDelta: rows 16 rb .., value columns v0 + 16 hf ..
+                // The B operand (four consecutive tokens of one column per
+                // lane) by the transposing read from the row-major dDelta tile:
+                // lane 4 i + a of a 16-lane group addresses token t0 + i,
+                // columns 16 hf + 4 a .. + 3; lane r then receives tokens
+                // t0 .. t0 + 3 of column 16 hf + r.
                 f32x4 y = z4;
+                const unsigned eh = lds_u32(reinterpret_cast<const char *>(bEh)),
+                               el = lds_u32(reinterpret_cast<const char *>(bEl));
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
-                    const __bf16 *ph = bTh + (16 * hf + r16) * LT + 32 * p + 4 * gq;
-                    const __bf16 *pl = bTl + (16 * hf + r16) * LT + 32 * p + 4 * gq;
-                    const bf16x8 bh = cat8(*reinterpret_cast<const bf16x4 *>(ph),
-                                           *reinterpret_cast<const bf16x4 *>(ph + 16));
-                    const bf16x8 bl = cat8(*reinterpret_cast<const bf16x4 *>(pl),
-                                           *reinterpret_cast<const bf16x4 *>(pl + 16));
+                    const unsigned o0 = 2u * ((32 * p + 4 * gq + (r16 >> 2)) * VS + 16 * hf + 4 * (r16 & 3));
+                    const unsigned o1 = o0 + 2u * 16 * VS;   // tokens + 16
+                    const bf16x8 bh = cat8(lds_read_tr(eh + o0), lds_read_tr(eh + o1));
+                    const bf16x8 bl = cat8(lds_read_tr(el + o0), lds_read_tr(el + o1));
                     y = mfma_bf16(ttl[p], bh, mfma_bf16(tth[p], bl, mfma_bf16(tth[p], bh, y)));
                 }
 #pragma unroll
@@ -1844,6 +1842,30 @@ __global__ __launch_bounds__(GR_NTHR) void bwd_grad_kernel(BwArgs a)
     __bf16 *sWT = reinterpret_cast<__bf16 *>(smc + L::WT), *sTT = reinterpret_cast<__bf16 *>(smc + L::TT);
     bf16x4 *sWA = reinterpret_cast<bf16x4 *>(smc + L::WA), *sMA = reinterpret_cast<bf16x4 *>(smc + L::MA);
     f32x4 aZ[NXH];
+    // phase 3's k, q and gamma rows of a pass, loaded a pass ahead (pass 0's
+    // during phase 2): thread (token tb, channels PC pp + cb .. + 7); k and q
+    // zero past the end
+    const int tb = tid >> 3, cb = 8 * (tid & 7);
+    bf16x8 kr8, qr8;
+    f32x4 g0, g1, p0, p1;   // gamma of row tb and (channel gate) of its reference row
+    auto load_pass = [&](int pp) {
+        const int x = PC * pp + cb;
+        kr8 = bf16x8{};
+        qr8 = bf16x8{};
+        if (tb < n) {
+            kr8 = *reinterpret_cast<const bf16x8 *>(k + tb * H * K + x);
+            qr8 = *reinterpret_cast<const bf16x8 *>(q + tb * H * K + x);
+        }
+        const float *gr = gam + tb * K + x;
+        g0 = *reinterpret_cast<const f32x4 *>(gr);
+        g1 = *reinterpret_cast<const f32x4 *>(gr + 4);
+        if (CH) {
+            const float *gp = gam + (16 * (tb >> 4) + 8) * K + x;
+            p0 = *reinterpret_cast<const f32x4 *>(gp);
+            p1 = *reinterpret_cast<const f32x4 *>(gp + 4);
+        }
+    };
+    load_pass(0);
     {
         // B operands of dT -= dWn (beta Kp)^T: the bf16 copy of Kp in fragment
         // order, segment (row block J, key pair p) = the lane's 8 keys of both blocks
@@ -1963,19 +1985,9 @@ __global__ __launch_bounds__(GR_NTHR) void bwd_grad_kernel(BwArgs a)
 #pragma unroll
     for (int pp = 0; pp < K / PC; ++pp) {
         lds_barrier();   // phase 2 / the previous pass is done with this space
-        {   // the pass's scaled k and q and gamma, rows = tokens: thread (token tb, channels cb ..)
-            const int tb = tid >> 3, cb = 8 * (tid & 7), x = PC * pp + cb;
-            bf16x8 kr8 = {}, qr8 = {};
-            if (tb < n) {
-                kr8 = *reinterpret_cast<const bf16x8 *>(k + tb * H * K + x);
-                qr8 = *reinterpret_cast<const bf16x8 *>(q + tb * H * K + x);
-            }
-            const float *gr = gam + tb * K + x;
-            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gr), g1 = *reinterpret_cast<const f32x4 *>(gr + 4);
+        {   // the pass's scaled k and q and gamma, rows = tokens (loaded a pass ahead)
             f32x4 kt[2], kh[2], qh[2];
             if (CH) {
-                const float *gp = gam + (16 * (tb >> 4) + 8) * K + x;
-                const f32x4 p0 = *reinterpret_cast<const f32x4 *>(gp), p1 = *reinterpret_cast<const f32x4 *>(gp + 4);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float gv = e < 4 ? g0[e] : g1[e - 4], gpv = e < 4 ? p0[e] : p1[e - 4];
@@ -2001,71 +2013,93 @@ __global__ __launch_bounds__(GR_NTHR) void bwd_grad_kernel(BwArgs a)
             *reinterpret_cast<f32x4 *>(sG + tb * LW + cb) = g0;
             *reinterpret_cast<f32x4 *>(sG + tb * LW + cb + 4) = g1;
         }
+        if (pp + 1 < K / PC) load_pass(pp + 1);
         lds_barrier();
         float loc[2][4];   // d gamma summed over the later rows of this lane's tile column
+        // The dP and dG operands of a block do not depend on the channel tile:
+        // each is read and split once and serves both tiles xi of the pass.
+        float gv2[2][4], grho2[2][4], fw2[2][4];
+        f32x4 aq2[2], ak2[2], as2[2];
 #pragma unroll
         for (int xi = 0; xi < 2; ++xi) {
-            const int i = 2 * pp + xi, xl = 16 * (2 * hf + xi) + r16, x = PC * pp + xl;
-            float gv[4], grho[4], fw[4];
+            const int xl = 16 * (2 * hf + xi) + r16;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gv[e] = sG[(16 * rb + 4 * gq + e) * LW + xl];
+            for (int e = 0; e < 4; ++e) gv2[xi][e] = sG[(16 * rb + 4 * gq + e) * LW + xl];
             if (CH) {
 #pragma unroll
-                for (int J = 0; J < 4; ++J) grho[J] = sG[(16 * J + 8) * LW + xl];
+                for (int J = 0; J < 4; ++J) grho2[xi][J] = sG[(16 * J + 8) * LW + xl];
             }
-            f32x4 aq = z4, ak = z4, as = z4;
-            // rows r of this block, s <= r:  sum_J e^{gamma_r - gamma_rho(J)} (dP_rJ, dG_rJ) Kt_J
+            aq2[xi] = ak2[xi] = as2[xi] = z4;
+        }
+        // rows r of this block, s <= r:  sum_J e^{gamma_r - gamma_rho(J)} (dP_rJ, dG_rJ) Kt_J
 #pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                if (J <= rb) {
-                    // A: this block's rows of dP and dG (the transposed tiles), B: Kt
-                    f32x4 b, pa, ga;
+        for (int J = 0; J < 4; ++J) {
+            if (J <= rb) {
+                // A: this block's rows of dP and dG (the transposed tiles), B: Kt
+                f32x4 pa, ga;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        b[j] = sKt[(16 * J + 4 * gq + j) * LW + xl];
-                        pa[j] = sPT[(16 * J + 4 * gq + j) * LP + 16 * rb + r16];
-                        ga[j] = sGT[(16 * J + 4 * gq + j) * LP + 16 * rb + r16];
-                    }
-                    bf16x4 bh, bl, pah, pal, gah, gal;
+                for (int j = 0; j < 4; ++j) {
+                    pa[j] = sPT[(16 * J + 4 * gq + j) * LP + 16 * rb + r16];
+                    ga[j] = sGT[(16 * J + 4 * gq + j) * LP + 16 * rb + r16];
+                }
+                bf16x4 pah, pal, gah, gal;
+                split4(pa, pah, pal);
+                split4(ga, gah, gal);
+#pragma unroll
+                for (int xi = 0; xi < 2; ++xi) {
+                    const int xl = 16 * (2 * hf + xi) + r16;
+                    f32x4 b;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) b[j] = sKt[(16 * J + 4 * gq + j) * LW + xl];
+                    bf16x4 bh, bl;
                     split4(b, bh, bl);
-                    split4(pa, pah, pal);
-                    split4(ga, gah, gal);
                     const f32x4 pq = mfma16x3(pah, pal, bh, bl, z4);
                     const f32x4 pk = mfma16x3(gah, gal, bh, bl, z4);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float f = CH ? __expf(gv[e] - grho[J]) : 1.f;
-                        aq[e] = fmaf(f, pq[e], aq[e]);
-                        ak[e] = fmaf(f, pk[e], ak[e]);
+                        const float f = CH ? __expf(gv2[xi][e] - grho2[xi][J]) : 1.f;
+                        aq2[xi][e] = fmaf(f, pq[e], aq2[xi][e]);
+                        ak2[xi][e] = fmaf(f, pk[e], ak2[xi][e]);
                     }
                 }
             }
-            // rows u of this block, t >= u:  sum_I e^{gamma_rho(I) - gamma_u} (dG^T Kh_I + dP^T Qh_I)
+        }
+        // rows u of this block, t >= u:  sum_I e^{gamma_rho(I) - gamma_u} (dG^T Kh_I + dP^T Qh_I)
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                if (I >= rb) {
-                    const f32x4 ag = *reinterpret_cast<const f32x4 *>(sGT + (16 * rb + r16) * LP + 16 * I + 4 * gq);
-                    const f32x4 ap = *reinterpret_cast<const f32x4 *>(sPT + (16 * rb + r16) * LP + 16 * I + 4 * gq);
+        for (int I = 0; I < 4; ++I) {
+            if (I >= rb) {
+                const f32x4 ag = *reinterpret_cast<const f32x4 *>(sGT + (16 * rb + r16) * LP + 16 * I + 4 * gq);
+                const f32x4 ap = *reinterpret_cast<const f32x4 *>(sPT + (16 * rb + r16) * LP + 16 * I + 4 * gq);
+                bf16x4 agh, agl, aph, apl;
+                split4(ag, agh, agl);
+                split4(ap, aph, apl);
+#pragma unroll
+                for (int xi = 0; xi < 2; ++xi) {
+                    const int xl = 16 * (2 * hf + xi) + r16;
                     f32x4 bk, bq;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         bk[j] = sKh[(16 * I + 4 * gq + j) * LW + xl];
                         bq[j] = sQh[(16 * I + 4 * gq + j) * LW + xl];
                     }
-                    bf16x4 agh, agl, aph, apl, bkh, bkl, bqh, bql;
-                    split4(ag, agh, agl);
-                    split4(ap, aph, apl);
+                    bf16x4 bkh, bkl, bqh, bql;
                     split4(bk, bkh, bkl);
                     split4(bq, bqh, bql);
                     const f32x4 ps = mfma16x3(aph, apl, bqh, bql, mfma16x3(agh, agl, bkh, bkl, z4));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float f = CH ? __expf(grho[I] - gv[e]) : 1.f;
-                        if (I == rb) fw[e] = f;   // also turns Kh, Qh of this block's rows back into k, q
-                        as[e] = fmaf(f, ps[e], as[e]);
+                        const float f = CH ? __expf(grho2[xi][I] - gv2[xi][e]) : 1.f;
+                        if (I == rb) fw2[xi][e] = f;   // also turns Kh, Qh of this block's rows back into k, q
+                        as2[xi][e] = fmaf(f, ps[e], as2[xi][e]);
                     }
                 }
             }
+        }
+#pragma unroll
+        for (int xi = 0; xi < 2; ++xi) {
+            const int i = 2 * pp + xi, xl = 16 * (2 * hf + xi) + r16, x = PC * pp + xl;
+            const float *gv = gv2[xi], *fw = fw2[xi];
+            const f32x4 aq = aq2[xi], ak = ak2[xi], as = as2[xi];
             // per element: dq, dk, d gamma; the gn terms of this channel
             const float gn = sG[(C - 1) * LW + xl];
             float dgn = 0.f, dga[4];
