@@ -648,8 +648,8 @@ def main():
                                     steps=max(5, min(args.steps, 20)) if name == "channel_long"
                                     else max(20, args.steps))
             if want_o:
-                e["mfma_note"] = ("useful per head-token C(3K+2V) + 6KV + C^2/3 (the survey's "
-                                  "count); dense doubles the C-terms")
+                e["mfma_note"] = ("useful per head-token C(3K+2V) + 6KV + C^2/3 (the triangular "
+                                  "blocks counted at half); dense doubles the C-terms")
                 if name == "scalar_bf16":
                     cfl = measured_mfma_flops("chunk_fwd_ws_kernel<128>")
                     e["counter_mfma_flops_per_launch"] = cfl
