@@ -76,7 +76,7 @@ MEASURED_TRAFFIC = {
                                       "gdn_common.h", "mfma_frag.h"), "7be8db47e2f9a32b", 33514739872),
     # the whole backward call (prep, sweeps, grad) at B4 H6 T4096, per-channel gate, bf16
     "chunk_bwd/channel_bf16": (("chunk_bwd.hip", "chunk_bwd.h", "ws_common.h", "gdn_common.h",
-                                "mfma_frag.h"), "5ae791e1d36b7d08", 1350448320),
+                                "mfma_frag.h"), "909863fa64a1af75", 1350448320),
 }
 
 # bf16 matrix-core work per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16, units of 512

@@ -1596,7 +1596,7 @@ __global__ __launch_bounds__(BW_NTHR) void bwd_kgrad2_kernel(BwArgs a)
 // (1.8e-3 in dv, dbeta) or scaled k and q in the pair sums (1.7e-2 in dg)
 // too coarse; those are split, which keeps them near fp32.
 //
-// LDS (bytes, K = V = 128): 105 KB at most, one workgroup of eight waves per CU.
+// LDS (bytes, K = V = 128): 106 KB at most (phase 3), one workgroup of eight waves per CU.
 constexpr int GR_NTHR = 512;
 
 template <int K, int V> struct GradLds {
