@@ -76,9 +76,7 @@ struct SgSmem {
     static constexpr int hEgn = hTd + SG_T * LDD * 2;
     static constexpr int HBUF = sg_al(hEgn + SG_K * 4);
     static constexpr int oH = PREP;
-    // per prep wave 256 bytes that the L2 prefetch copies land in (never read)
-    static constexpr int kSink = oH + 2 * HBUF;
-    static constexpr int kCtr = kSink + 4 * 256;
+    static constexpr int kCtr = oH + 2 * HBUF;
     static constexpr int bytes = sg_al(kCtr + 16);
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
@@ -221,20 +219,6 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
                 }
             }
         };
-        // L2 prefetch of chunk n: one 4-byte copy per 128-byte line of this
-        // wave's rows 16 pw .. +15 of g (four lines a row) and k (two lines a
-        // row) and of beta, into this wave's sink in LDS (never read); the real
-        // loads of the chunk, a period later, then find the lines in L2.
-        auto prefetch_l2 = [&](int n) __attribute__((always_inline)) {
-            const int t0 = n * SG_T;
-            char *sink = smem + L::kSink + pw * 256;
-            const int gr = min(t0 + 16 * pw + (lane >> 2), T - 1);         // g: 16 rows x 4 lines
-            g2lds4(a.g + (row_base + (long)gr * H) * K + 32 * (lane & 3), sink);
-            const int kr = min(t0 + 16 * pw + ((lane & 31) >> 1), T - 1);  // k: 16 rows x 2 lines
-            const float *src = lane < 32 ? reinterpret_cast<const float *>(a.k + (row_base + (long)kr * H) * K + 64 * (lane & 1))
-                                         : a.beta + row_base + (long)min(t0 + 16 * pw + (lane & 15), T - 1) * H;
-            g2lds4(src, sink);
-        };
 
         Raw r, nx;
         unsigned arrivals = 0;
@@ -335,7 +319,6 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
                     }
                 }
             }
-            if (n + 2 < c1) prefetch_l2(n + 2);
             arrivals += 4;
             prep_barrier(ctr, arrivals);   // every share and beta written
 
@@ -386,7 +369,6 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
 
         if (c0 < c1) {
             fetch(c0, nx);
-            if (c0 + 1 < c1) prefetch_l2(c0 + 1);
             prepare(c0);
             lds_barrier();                      // chunk c0 is ready
         }
