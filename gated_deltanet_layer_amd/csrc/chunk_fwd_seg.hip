@@ -187,7 +187,7 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
                 r.k[rt] = *reinterpret_cast<const bf16x8 *>(kb + lo);
                 r.g[rt][0] = *reinterpret_cast<const f32x4 *>(gb + lo);
                 r.g[rt][1] = *reinterpret_cast<const f32x4 *>(gb + lo + 4);
-                r.b[rt] = bb[bo];
+                r.b[rt] = pw == 0 ? bb[bo] : 0.f;   // beta: only wave 0 stages it
             }
         };
         // The loads of token block rt of chunk n only (same addressing as fetch).
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
             r.k[rt] = *reinterpret_cast<const bf16x8 *>(kb + lo);
             r.g[rt][0] = *reinterpret_cast<const f32x4 *>(gb + lo);
             r.g[rt][1] = *reinterpret_cast<const f32x4 *>(gb + lo + 4);
-            r.b[rt] = bb[bo];
+            r.b[rt] = pw == 0 ? bb[bo] : 0.f;
         };
         auto zero_dead = [&](int n, Raw &r) __attribute__((always_inline)) {
             const int nlive = T - n * SG_T;
