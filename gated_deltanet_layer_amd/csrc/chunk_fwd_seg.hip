@@ -36,9 +36,10 @@
 // of every Gram block (each an MFMA over exactly its 32 keys, operands from
 // registers); the four shares meet in LDS, and after the prep waves have met (an
 // LDS arrival counter) each sums its Gram blocks, one of them a diagonal block it
-// also inverts.  Chain wave w owns 64 columns of the augmented state (w = 0, 1:
-// value columns; w = 2, 3: columns of M, idle in segment 0) in MFMA
-// accumulators for the whole segment.  One workgroup barrier per chunk hands the
+// also inverts.  Chain wave w owns 64 columns of the augmented state in MFMA
+// accumulators for the whole segment: value columns 32w .. 32w+31 and the same
+// columns of M (none in segment 0; skipped once they have decayed to exactly
+// zero).  One workgroup barrier per chunk hands the
 // chunk's data over; the chain's data is double-buffered.
 //
 // LDS layouts, chosen for the matrix-core operand reads (measured on gfx950: a
@@ -381,27 +382,31 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
     }
 
     // ============================= chain waves =============================
-    // Column group cg (16 columns) of this wave: augmented column 64 wave +
-    // 16 cg + r16 (below 128: value columns; from 128: columns of M).
-    // Accumulator S[cg][ct], ct = 2 kb + hh, element e holds the row of key
-    // 32 kb + 8 gq + 4 hh + e.
+    // Column groups (16 columns each) of this wave: groups 0 and 1 hold columns
+    // 32 wave + 16 cg + r16 of N (of the state itself in segment 0), groups 2 and
+    // 3 the same columns of M (later segments only).  Accumulator S[cg][ct],
+    // ct = 2 kb + hh, element e holds the row of key 32 kb + 8 gq + 4 hh + e.
     const int cw = wave;
-    const bool mcols = cw >= 2;
-    const bool active = seg > 0 || !mcols;
     auto key_of = [&](int ct, int e) { return 32 * (ct >> 1) + 8 * gq + 4 * (ct & 1) + e; };
+    auto col_of = [&](int cg) { return 32 * cw + 16 * (cg & 1) + r16; };
+    // M' = Diag(e^{gn}) M - K-^T D(K+ M) is exactly zero once M is (every product
+    // and sum is of zeros), so a wave skips its M columns from the chunk after
+    // they are all seen to be zero; the decay gets them there within a few
+    // chunks unless the gates stay close to 1.
+    bool mlive = seg > 0;
     f32x4 S[4][8];
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg) {
-        const int col = 64 * cw + 16 * cg + r16;
+        const int col = col_of(cg);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float x = 0.f;
-                if (seg == 0) {
-                    if (!mcols && a.S0) x = a.S0[((long)bh * K + key_of(ct, e)) * K + col];
-                } else if (mcols) {
-                    x = key_of(ct, e) == col - K ? 1.f : 0.f;
+                if (cg < 2) {
+                    if (seg == 0 && a.S0) x = a.S0[((long)bh * K + key_of(ct, e)) * K + col];
+                } else if (seg > 0) {
+                    x = key_of(ct, e) == col ? 1.f : 0.f;
                 }
                 S[cg][ct][e] = x;
             }
@@ -417,7 +422,7 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
     int v_tr[4];
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg) {
-        const int cgv = (4 * cw + cg) & 7;
+        const int cgv = 2 * cw + (cg & 1);   // groups 2 and 3 (M) read no v
         v_tr[cg] = (cgv >> 1) * 1024 + (16 * (2 * (cgv & 1) + (tq >> 1)) + trow) * 16 + 8 * (tq & 1);
     }
 
@@ -450,7 +455,7 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
 
     for (int c = c0; c < c1; ++c) {
         if (c + 1 < c1) copy_v(c + 1);
-        if (active) {
+        {
             const char *Hb = hbuf(c);
             const char *sKP = Hb + L::hKP;
             const unsigned vbase = lds_u32(Hb + L::hV);
@@ -467,6 +472,7 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
             Frag<__bf16> Df[4][2];
 #pragma unroll
             for (int cg = 0; cg < 4; ++cg) {
+                if (cg >= 2 && !mlive) continue;
                 Frag<__bf16> Sf[NKB];
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) Sf[kb] = reg_frag<__bf16>(S[cg][2 * kb], S[cg][2 * kb + 1]);
@@ -484,7 +490,7 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
                 GDN_SCHED_FENCE();
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
-                    if (!mcols) {
+                    if (cg < 2) {
                         const bf16x4 vv = lds_read_tr(vbase + v_tr[cg] + 4096 * rt);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) X[rt][e] = (float)vv[e] - X[rt][e];
@@ -524,6 +530,7 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
                 const f32x4 eg = *reinterpret_cast<const f32x4 *>(sEgn + key_of(ct, 0));
 #pragma unroll
                 for (int cg = 0; cg < 4; ++cg) {
+                    if (cg >= 2 && !mlive) continue;
                     f32x4 s = S[cg][ct] * eg;
 #pragma unroll
                     for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -531,22 +538,34 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
                     S[cg][ct] = s;
                 }
             }
+            if (mlive && (c & 3) == 3) {     // every fourth chunk: are the M columns all zero?
+                unsigned bits = 0u;
+#pragma unroll
+                for (int cg = 2; cg < 4; ++cg)
+#pragma unroll
+                    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) bits |= __float_as_uint(S[cg][ct][e]) & 0x7fffffffu;
+                mlive = __builtin_amdgcn_ballot_w64(bits != 0u) != 0ull;
+            }
         }
         wait_vm<0>();                        // the next chunk's v landed
         lds_barrier();
     }
 
-    if (!active) return;
-    float *dst;
+    float *dN, *dM = nullptr;
     if (seg == 0) {
-        dst = a.S_T + (long)bh * K * K;
+        dN = a.S_T + (long)bh * K * K;
     } else {
         const long slot = (long)bh * (a.nseg - 1) + (seg - 1);
-        dst = (mcols ? a.mapM : a.mapN) + slot * K * K;
+        dN = a.mapN + slot * K * K;
+        dM = a.mapM + slot * K * K;
     }
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg) {
-        const int col = (64 * cw + 16 * cg + r16) & (K - 1);
+        if (cg >= 2 && seg == 0) continue;
+        float *dst = cg < 2 ? dN : dM;
+        const int col = col_of(cg);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
