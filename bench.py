@@ -626,7 +626,10 @@ def main():
         out["config"] = {"workload": head["workload"] + " (gdn_chunk_fwd_ws, "
                          f"{head['segments']} segments per sequence)",
                          "global_batch": head_cfg.B, "seq_len": head_cfg.T, "heads": head_cfg.H,
-                         "d_k": head_cfg.K, "d_v": head_cfg.V, "parallelism": "single GPU"}
+                         "d_k": head_cfg.K, "d_v": head_cfg.V, "parallelism": "single GPU",
+                         "note": ("later segments stop carrying the M part of their map once it "
+                                  "has decayed to exactly zero (same result bit for bit; how soon "
+                                  "depends on the gates: within a few chunks for these)")}
         out["timing"] = {k: head[k] for k in ("ms", "ms_median", "ms_min", "ms_max", "steps",
                                               "warmup_requested", "warmup_performed")}
         out["roofline"] = {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS,
