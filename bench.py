@@ -71,9 +71,9 @@ MEASURED_TRAFFIC = {
                                                                   "prologue_ops.h", "gdn_common.h"),
                                                                  "672309d493c963a2", 1719409472),
     "chunk_fwd_seg/channel_long": (("chunk_fwd_seg.hip", "ws_common.h", "gdn_common.h",
-                                    "mfma_frag.h"), "67702618b290d962", 13548338496),
+                                    "mfma_frag.h"), "db896b910e4d7fd9", 13454399872),
     "chunk_fwd_seg/channel_long/o": (("chunk_fwd_seg.hip", "chunk_fwd_wsc.hip", "ws_common.h",
-                                      "gdn_common.h", "mfma_frag.h"), "b5b9f70bf581edc0", 33483738816),
+                                      "gdn_common.h", "mfma_frag.h"), "0980df048bf9396b", 33386495168),
     # the whole backward call (prep, sweeps, grad) at B4 H6 T4096, per-channel gate, bf16
     "chunk_bwd/channel_bf16": (("chunk_bwd.hip", "chunk_bwd.h", "ws_common.h", "gdn_common.h",
                                 "mfma_frag.h"), "909863fa64a1af75", 1350448320),

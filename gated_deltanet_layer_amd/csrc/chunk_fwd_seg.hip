@@ -109,6 +109,7 @@ struct SgArgs {
     float *S_T;       // segment 0 leaves its final state here
     float *mapN;      // [B*H][nseg-1][K][V]
     float *mapM;      // [B*H][nseg-1][K][K]
+    int *mflag;       // [B*H][nseg-1][4]: 0 where chain wave w's M columns are all zero
     int T, H, nseg, seg_len;
 };
 
@@ -560,10 +561,12 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
         const long slot = (long)bh * (a.nseg - 1) + (seg - 1);
         dN = a.mapN + slot * K * K;
         dM = a.mapM + slot * K * K;
+        // M columns seen to be all zero are not written; the combine skips them
+        if (lane == 0) a.mflag[slot * 4 + cw] = mlive ? 1 : 0;
     }
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg) {
-        if (cg >= 2 && seg == 0) continue;
+        if (cg >= 2 && (seg == 0 || !mlive)) continue;
         float *dst = cg < 2 ? dN : dM;
         const int col = col_of(cg);
 #pragma unroll
@@ -582,6 +585,7 @@ __global__ __launch_bounds__(SG_NTHR, 1) void chunk_fwd_seg_kernel(SgArgs a)
 // ([B*H][nseg-1][K][V]): the incoming states of the o pass.
 struct SgCombArgs {
     const float *mapN, *mapM;
+    const int *mflag;   // [nbh][nseg-1][4]: 0 where columns 32 w .. 32 w + 31 of M_s are all zero (not written)
     float *S_T;
     float *Sb;
     int nseg, xcd_map;
@@ -623,20 +627,29 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SgCombArgs a)
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[rt][e] = Np[(32 * wave + 16 * rt + 4 * gq + e) * V + col];
+        // columns 16 m .. 16 m + 15 of M_s: skipped where the segment kernel found
+        // them all zero (they contribute nothing and were not written)
+        int live[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) live[w] = __builtin_amdgcn_readfirstlane(a.mflag[slot * 4 + w]);
         f32x4 am[8][2];
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 8; ++m) {
+            if (!live[m >> 1]) continue;
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
                 am[m][rt] = *reinterpret_cast<const f32x4 *>(Mp + (32 * wave + 16 * rt + r16) * K + 16 * m + 4 * gq);
+        }
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 8; ++m) {
+            if (!live[m >> 1]) continue;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float bv = sS[(16 * m + 4 * gq + e) * LDS_LD + r16];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) acc[rt] = mfma_f32(am[m][rt][e], bv, acc[rt]);
             }
+        }
         __syncthreads();
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -675,7 +688,8 @@ int chunk_fwd_seg_count(long B, long T, long H)
 unsigned long long chunk_fwd_seg_workspace(long B, long H, int nseg, bool want_o)
 {
     if (nseg <= 1) return 0;
-    return (unsigned long long)B * H * (nseg - 1) * ((want_o ? 3ull : 2ull) * SG_K * SG_K) * 4ull;
+    // N and M (and the incoming states) in fp32, then four int flags per map
+    return (unsigned long long)B * H * (nseg - 1) * ((want_o ? 3ull : 2ull) * SG_K * SG_K + 4ull) * 4ull;
 }
 
 hipError_t chunk_fwd_wsc_seg_launch(const void *q, const void *k, const void *v, const float *g,
@@ -736,12 +750,13 @@ hipError_t chunk_fwd_seg_launch(const void *q, const void *k, const void *v, con
     a.nseg = nseg;
     a.mapN = (float *)ws;
     a.mapM = a.mapN + bh * (nseg - 1) * SG_K * SG_K;
+    a.mflag = (int *)(a.mapM + bh * (nseg - 1) * SG_K * SG_K * (o ? 2 : 1));   // after M (and Sb)
     a.T = T; a.H = H;
     hipLaunchKernelGGL(chunk_fwd_seg_kernel, dim3((unsigned)(bh * nseg)), dim3(SG_NTHR), L::bytes, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nseg == 1) return e;
     SgCombArgs c;
-    c.mapN = a.mapN; c.mapM = a.mapM; c.S_T = S_T; c.nseg = nseg; c.nbh = bh;
+    c.mapN = a.mapN; c.mapM = a.mapM; c.mflag = a.mflag; c.S_T = S_T; c.nseg = nseg; c.nbh = bh;
     c.Sb = o ? a.mapM + bh * (nseg - 1) * SG_K * SG_K : nullptr;
     c.xcd_map = bh % 8 == 0 ? 1 : 0;
     hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(bh * (SG_K / 16))), dim3(256), 0, st, c);

@@ -354,14 +354,15 @@ def _fws_size(L, B=1, T=262144, H=48, K=128, V=128, chunk=64, dtype=1, gate=1, w
 
 def test_fwd_workspace_size_values(L):
     # final state only, bf16, per-channel gate, 48 heads of 262144 tokens: 16 segments of
-    # 256 chunks, an fp32 M (128 x 128) and N (128 x 128) for each of the 15 after the first
-    assert _fws_size(L) == (gdn.GDN_OK, 48 * 15 * 2 * 128 * 128 * 4)
+    # 256 chunks, an fp32 M (128 x 128) and N (128 x 128) and four int flags (which
+    # column blocks of M are all zero) for each of the 15 after the first
+    assert _fws_size(L) == (gdn.GDN_OK, 48 * 15 * (2 * 128 * 128 + 4) * 4)
     # two heads of 2048 tokens: four segments of 8 chunks
-    assert _fws_size(L, B=1, H=2, T=2048) == (gdn.GDN_OK, 1 * 2 * 3 * 2 * 128 * 128 * 4)
+    assert _fws_size(L, B=1, H=2, T=2048) == (gdn.GDN_OK, 1 * 2 * 3 * (2 * 128 * 128 + 4) * 4)
     # 48 heads of 16 chunks: two segments of 8
-    assert _fws_size(L, T=1000) == (gdn.GDN_OK, 48 * 1 * 2 * 128 * 128 * 4)
+    assert _fws_size(L, T=1000) == (gdn.GDN_OK, 48 * 1 * (2 * 128 * 128 + 4) * 4)
     # with o: the incoming state of each later segment as well
-    assert _fws_size(L, want_o=1) == (gdn.GDN_OK, 48 * 15 * 3 * 128 * 128 * 4)
+    assert _fws_size(L, want_o=1) == (gdn.GDN_OK, 48 * 15 * (3 * 128 * 128 + 4) * 4)
     # no sequence-parallel form: scalar gate, fp32, K = 64, enough heads, short T
     for kw in (dict(gate=0), dict(dtype=0, K=64, V=64), dict(K=64), dict(K=64, want_o=1),
                dict(B=16, H=8, T=2048), dict(T=500), dict(T=0), dict(B=0)):
